@@ -1,0 +1,282 @@
+/*
+ * CPU oracle for the BitNet b1.58 BitLinear layer (W1.58A8).
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may link, load or
+ * call this file: only the test suite, the smoke check and the CPU-baseline
+ * leg of the benchmark use it.  It shares no code, header, table or helper
+ * with the HIP library; the two are written independently from the same
+ * definitions, so that agreement between them means something.
+ *
+ * Style: plain scalar C, one obvious loop per definition, no SIMD, no
+ * blocking, no fusion.  Built with -O2 -fno-fast-math -ffp-contract=off so
+ * that every fp32 operation is a single IEEE-754 rounding in the default
+ * round-to-nearest-even mode.
+ *
+ * Sources (page title, section):
+ *  [AN]  anthology note-168 on arXiv 2402.17764 (dmarx.github.io),
+ *        "What it does" and "The part that is a bet rather than a measurement".
+ *  [YT]  BitNet b1.58 2B4T video transcript (yousumm.com), "Transcription".
+ *  [BH]  "Bit Happens: How Tiny Weights Are Shaking It Off"
+ *        (michaelmallari.bitbucket.io), "From High-Precision Bloat to Elegant
+ *        Bit-Level Efficiency".
+ *
+ * Readings taken where the pages are silent (each is listed in the design doc):
+ *  R1  absmean scale = mean of |W| over the whole matrix (one scale per
+ *      tensor), accumulated in fp64, divided by N*K in fp64, rounded once to
+ *      fp32, then floored at 1e-5.
+ *  R2  ternary code = clamp(rintf(w / gamma), -1, 1), fp32 IEEE division,
+ *      round-half-to-even (so |w| == gamma/2 gives 0).
+ *  R3  activation scale = per-token max |x|, floored at 1e-5;
+ *      q = clamp(rintf(x * (127 / a)), -127, 127), the multiplier computed
+ *      once per token by an fp32 IEEE division.
+ *  R4  output y = (float)acc * c with c = (gamma * a) / 127 in fp32
+ *      (multiply, then divide).
+ *  R5  the 2-bit packed format "BL2-T64" defined at oracle_pack below.
+ *
+ * Parity pins: every function below is pinned by tests/test_oracle_pins.py
+ * against closed forms, hand-derived fixtures (tests/golden/), library
+ * routines or brute force.  The exact last bit of the absmean scale for a
+ * random matrix depends on the fp64 summation order and is the one value
+ * that is "parity unpinned" beyond a 1e-6 relative bound.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "oracle.h"
+
+/* ------------------------------------------------------------------------ */
+/* Weight side: absmean scale and ternary codes.   [AN] "What it does";      */
+/* [YT] the absmean quantizer chooses -1, 0 or +1 for every weight.          */
+/* ------------------------------------------------------------------------ */
+
+float oracle_absmean_scale(const float *W, int64_t N, int64_t K)
+{
+    double s = 0.0;
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k)
+            s += fabs((double)W[n * K + k]);
+    double mean = s / ((double)N * (double)K);
+    float gamma = (float)mean;
+    if (!(gamma >= 1e-5f)) gamma = 1e-5f;
+    return gamma;
+}
+
+void oracle_ternarize(const float *W, int64_t N, int64_t K, float gamma, int8_t *T)
+{
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t k = 0; k < K; ++k) {
+            float r = rintf(W[n * K + k] / gamma);
+            int8_t t = 0;
+            if (r >= 1.0f) t = 1;
+            else if (r <= -1.0f) t = -1;
+            T[n * K + k] = t;
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Packed format BL2-T64: four ternary codes per byte ([YT]: four codes are  */
+/* bundled into one byte, moved to the compute unit and unpacked there).     */
+/*                                                                           */
+/* Field value = code + 1, so {-1, 0, +1} -> {0, 1, 2}; the value 3 is never */
+/* written and a byte of four zero codes is 0x55.                            */
+/*                                                                           */
+/* The N x K matrix is cut into row tiles of 64 rows and K units of 64       */
+/* codes (K is padded up to a multiple of 64 and N up to a multiple of 64    */
+/* with zero codes).  Tile t, unit u is a 1024-byte block at byte            */
+/* (t * KU + u) * 1024, KU = ceil(K / 64).  The block is 64 slots of 16      */
+/* bytes; slot L holds four little-endian 32-bit words d = 0..3.  With       */
+/* d = 2*s + h, word d of slot L holds row 64*t + 32*s + (L mod 32) and      */
+/* codes k = 64*u + 32*h + 16*(L div 32) + c for c = 0..15, code c in byte   */
+/* (c mod 4) at bit 2*(c div 4) of the word.                                 */
+/* ------------------------------------------------------------------------ */
+
+int64_t oracle_packed_bytes(int64_t N, int64_t K)
+{
+    int64_t tiles = (N + 63) / 64;
+    int64_t units = (K + 63) / 64;
+    return tiles * units * 1024;
+}
+
+/* Position of code (n, k): byte index into the packed buffer and the bit
+ * shift of its 2-bit field inside that byte.                                */
+static void bl2_position(int64_t n, int64_t k, int64_t K, int64_t *byte, int *shift)
+{
+    int64_t units = (K + 63) / 64;
+    int64_t t = n / 64, r = n % 64;
+    int64_t u = k / 64, kk = k % 64;
+    int64_t s = r / 32, row_in_half = r % 32;
+    int64_t h = kk / 32, g = (kk % 32) / 16, c = kk % 16;
+    int64_t slot = row_in_half + 32 * g;
+    int64_t word = 2 * s + h;
+    *byte = (t * units + u) * 1024 + 16 * slot + 4 * word + (c % 4);
+    *shift = (int)(2 * (c / 4));
+}
+
+void oracle_pack(const int8_t *T, int64_t N, int64_t K, uint8_t *P)
+{
+    int64_t bytes = oracle_packed_bytes(N, K);
+    for (int64_t i = 0; i < bytes; ++i) P[i] = 0x55; /* every field = zero code */
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t k = 0; k < K; ++k) {
+            int64_t b; int sh;
+            bl2_position(n, k, K, &b, &sh);
+            uint8_t field = (uint8_t)(T[n * K + k] + 1);
+            P[b] = (uint8_t)((P[b] & ~(3u << sh)) | ((unsigned)field << sh));
+        }
+    }
+}
+
+/* Returns the number of fields holding the forbidden value 3 among the N*K
+ * real positions, plus the number of padding fields that are not the zero
+ * code; T receives the decoded codes (a forbidden field decodes as 0).      */
+int64_t oracle_unpack(const uint8_t *P, int64_t N, int64_t K, int8_t *T)
+{
+    int64_t bad = 0;
+    int64_t tiles = (N + 63) / 64, units = (K + 63) / 64;
+    for (int64_t n = 0; n < tiles * 64; ++n) {
+        for (int64_t k = 0; k < units * 64; ++k) {
+            int64_t b; int sh;
+            bl2_position(n, k, K, &b, &sh);
+            int field = (P[b] >> sh) & 3;
+            if (n < N && k < K) {
+                if (field == 3) { ++bad; field = 1; }
+                T[n * K + k] = (int8_t)(field - 1);
+            } else if (field != 1) {
+                ++bad;
+            }
+        }
+    }
+    return bad;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Activation side: per-token absmax to int8 ([AN] "What it does":           */
+/* activations at 8 bits; [YT]: values are squeezed into eight-bit numbers). */
+/* ------------------------------------------------------------------------ */
+
+void oracle_quant_act(const float *X, int64_t M, int64_t K,
+                      int8_t *Q, float *absmax, int32_t *rowsum)
+{
+    for (int64_t m = 0; m < M; ++m) {
+        float a = 0.0f;
+        for (int64_t k = 0; k < K; ++k) {
+            float v = fabsf(X[m * K + k]);
+            if (v > a) a = v;
+        }
+        if (!(a >= 1e-5f)) a = 1e-5f;
+        float s = 127.0f / a;
+        int32_t sum = 0;
+        for (int64_t k = 0; k < K; ++k) {
+            float r = rintf(X[m * K + k] * s);
+            if (r > 127.0f) r = 127.0f;
+            if (r < -127.0f) r = -127.0f;
+            int8_t q = (int8_t)r;
+            Q[m * K + k] = q;
+            sum += q;
+        }
+        absmax[m] = a;
+        if (rowsum) rowsum[m] = sum;
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Contraction ([AN] "The part that is a bet...": with ternary weights the   */
+/* product needs only integer additions).  acc[m][n] = sum_k T[n][k]Q[m][k]. */
+/* ------------------------------------------------------------------------ */
+
+void oracle_matmul(const int8_t *Q, const int8_t *T, int64_t M, int64_t N, int64_t K,
+                   int32_t *acc)
+{
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n) {
+            int32_t s = 0;
+            for (int64_t k = 0; k < K; ++k)
+                s += (int32_t)T[n * K + k] * (int32_t)Q[m * K + k];
+            acc[m * N + n] = s;
+        }
+}
+
+/* The same result written as the pages phrase it: additions of the          */
+/* activations where the weight is +1, subtractions where it is -1, nothing  */
+/* where it is 0.  No multiplication is used.                                */
+void oracle_matmul_addsub(const int8_t *Q, const int8_t *T, int64_t M, int64_t N, int64_t K,
+                          int32_t *acc)
+{
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n) {
+            int32_t plus = 0, minus = 0;
+            for (int64_t k = 0; k < K; ++k) {
+                int8_t t = T[n * K + k];
+                if (t == 1) plus += Q[m * K + k];
+                else if (t == -1) minus += Q[m * K + k];
+            }
+            acc[m * N + n] = plus - minus;
+        }
+}
+
+/* Contraction straight from the packed buffer for a chosen list of output
+ * rows (used for sampled checks at full model sizes).  acc is M x nrows.    */
+void oracle_matmul_packed_rows(const int8_t *Q, const uint8_t *P, int64_t M, int64_t N,
+                               int64_t K, const int64_t *rows, int64_t nrows, int32_t *acc)
+{
+    (void)N;
+    for (int64_t i = 0; i < nrows; ++i) {
+        int64_t n = rows[i];
+        for (int64_t m = 0; m < M; ++m) {
+            int32_t s = 0;
+            for (int64_t k = 0; k < K; ++k) {
+                int64_t b; int sh;
+                bl2_position(n, k, K, &b, &sh);
+                int t = ((P[b] >> sh) & 3) - 1;
+                s += t * (int32_t)Q[m * K + k];
+            }
+            acc[m * nrows + i] = s;
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Rescale back to real values (BitLinear replaces nn.Linear, [AN] "What it  */
+/* does", so the layer returns real numbers).                                */
+/* ------------------------------------------------------------------------ */
+
+void oracle_epilogue(const int32_t *acc, int64_t M, int64_t N, float gamma,
+                     const float *absmax, float *Y)
+{
+    for (int64_t m = 0; m < M; ++m) {
+        float c = (gamma * absmax[m]) / 127.0f;
+        for (int64_t n = 0; n < N; ++n)
+            Y[m * N + n] = (float)acc[m * N + n] * c;
+    }
+}
+
+/* Tolerance reference: the same rescale carried out in fp64.                */
+void oracle_epilogue_f64(const int32_t *acc, int64_t M, int64_t N, float gamma,
+                         const float *absmax, double *Y)
+{
+    for (int64_t m = 0; m < M; ++m) {
+        double c = ((double)gamma * (double)absmax[m]) / 127.0;
+        for (int64_t n = 0; n < N; ++n)
+            Y[m * N + n] = (double)acc[m * N + n] * c;
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Whole layer from fp32 activations and packed weights: unpack, quantize    */
+/* the activations, contract, rescale.  Q/T/acc are caller scratch           */
+/* (M*K, N*K, M*N).  Returns the number of bad packed fields.                */
+/* ------------------------------------------------------------------------ */
+int64_t oracle_forward_packed(const float *X, int64_t M, int64_t K, const uint8_t *P,
+                              float gamma, int64_t N, float *Y,
+                              int8_t *Q, float *absmax, int32_t *rowsum,
+                              int8_t *T, int32_t *acc)
+{
+    int64_t bad = oracle_unpack(P, N, K, T);
+    oracle_quant_act(X, M, K, Q, absmax, rowsum);
+    oracle_matmul(Q, T, M, N, K, acc);
+    oracle_epilogue(acc, M, N, gamma, absmax, Y);
+    return bad;
+}

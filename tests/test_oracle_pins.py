@@ -1,0 +1,430 @@
+"""Pins of the CPU oracle to things other than itself (closed forms, hand-
+derived fixtures, library routines, brute force, statistics with known
+expectations).  CPU only.
+
+Pages cited (title, section):
+  [AN] anthology note-168 on arXiv 2402.17764 (dmarx.github.io)
+  [YT] BitNet b1.58 2B4T video transcript (yousumm.com), "Transcription"
+  [PI] "BitNet: Microsoft's AI Revolution Shows Why Precision May be
+       Overrated" (promptinjection.net)
+"""
+import math
+import os
+import subprocess
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle as O
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+# ---------------------------------------------------------------- helpers --
+
+def _golden(name):
+    with open(os.path.join(ROOT, "tests", "golden", name)) as f:
+        return [ln.strip() for ln in f if ln.strip() and not ln.startswith("#")]
+
+
+def _frac_round_half_even(x: Fraction) -> int:
+    fl = math.floor(x)
+    rem = x - fl
+    if rem > Fraction(1, 2):
+        return fl + 1
+    if rem < Fraction(1, 2):
+        return fl
+    return fl if fl % 2 == 0 else fl + 1
+
+
+def _exact_ternary(w: float, gamma: float) -> int:
+    """Nearest of {-1, 0, +1} to w/gamma in exact arithmetic, ties to 0."""
+    r = Fraction(w) / Fraction(gamma)
+    best = None
+    for v in (0, 1, -1):  # 0 first: it wins every tie it takes part in
+        d = abs(r - v)
+        if best is None or d < best[0]:
+            best = (d, v)
+    return best[1]
+
+
+# ------------------------------------------------------- P-A closed forms --
+
+def test_bits_per_weight_is_log2_3():
+    # [YT] prints 1.58496 bits per weight; [AN] "What it does" prints 1.58.
+    # Three equiprobable codes carry -sum p log2 p = log2 3 bits.
+    h = -sum((1 / 3) * math.log2(1 / 3) for _ in range(3))
+    assert round(h, 5) == 1.58496
+    assert round(h, 2) == 1.58
+
+
+@pytest.mark.parametrize("N,K", [(64, 64), (256, 256), (2560, 2560), (640, 2560), (2560, 6912)])
+def test_packed_size_is_two_bits_per_weight(N, K):
+    # Four codes per byte ([YT]); with N and K multiples of 64 there is no
+    # padding, so the buffer is exactly N*K/4 bytes = 2 bits per weight.
+    assert O.packed_bytes(N, K) * 8 == 2 * N * K
+    assert abs(2 / math.log2(3) - 1.2619) < 1e-4  # storage overhead vs log2 3
+
+
+def test_packed_size_of_2b_stack():
+    # A 2B-class model's BitLinear weights (30 layers of q,k,v,o,gate,up,down)
+    # hold 2.084e9 weights: 0.521 GB at 2 bits, 0.413 GB at log2(3) bits --
+    # the ~0.4 GB the pages quote ([YT]; [PI] "3. Benchmarks") is the log2(3)
+    # figure, which a 2-bit layout cannot reach.
+    n_weights = 30 * sum(K * N for _, K, N in synth.SHAPES_2B)
+    assert n_weights == 2_084_044_800
+    total = 30 * sum(O.packed_bytes(N, K) for _, K, N in synth.SHAPES_2B)
+    assert total == n_weights // 4 == 521_011_200
+    assert abs(n_weights * math.log2(3) / 8 / 1e9 - 0.4129) < 1e-3
+
+
+def test_padding_rounds_up_to_64():
+    assert O.packed_bytes(1, 1) == 1024
+    assert O.packed_bytes(65, 64) == 2048
+    assert O.packed_bytes(130, 200) == 3 * 4 * 1024
+    assert O.packed_bytes(0, 64) == 0
+
+
+# ------------------------------------------------- P-B format and invariants --
+
+def test_pack_golden_single_codes():
+    rows = [ln.split() for ln in _golden("bl2_t64_fixtures.txt") if ln.startswith("single")]
+    assert len(rows) == 7
+    for _, N, K, n, k, code, byte_idx, byte_hex in rows:
+        N, K, n, k, code, byte_idx = map(int, (N, K, n, k, code, byte_idx))
+        T = np.zeros((N, K), np.int8)
+        T[n, k] = code
+        P = O.pack(T)
+        expect = np.full(O.packed_bytes(N, K), 0x55, np.uint8)
+        expect[byte_idx] = int(byte_hex, 16)
+        np.testing.assert_array_equal(P, expect)
+        T2, bad = O.unpack(P, N, K)
+        assert bad == 0
+        np.testing.assert_array_equal(T2, T)
+
+
+def test_pack_golden_word():
+    rows = [ln.split() for ln in _golden("bl2_t64_fixtures.txt") if ln.startswith("word")]
+    assert len(rows) == 1
+    _, N, K, n, codes, first, bytes_hex = rows[0]
+    N, K, n, first = map(int, (N, K, n, first))
+    codes = [int(c) for c in codes.split(",")]
+    T = np.zeros((N, K), np.int8)
+    T[n, :16] = codes
+    P = O.pack(T)
+    want = [int(b, 16) for b in bytes_hex.split(",")]
+    assert list(P[first:first + 4]) == want
+    word = int.from_bytes(bytes(P[first:first + 4]), "little")
+    # each plane j of the word yields the fields of codes 4j..4j+3 in byte order
+    for j in range(4):
+        plane = (word >> (2 * j)) & 0x03030303
+        fields = [(plane >> (8 * b)) & 0xFF for b in range(4)]
+        assert fields == [c + 1 for c in codes[4 * j:4 * j + 4]]
+
+
+def test_zero_matrix_packs_to_0x55():
+    P = O.pack(np.zeros((100, 130), np.int8))
+    assert P.size == O.packed_bytes(100, 130)
+    assert np.all(P == 0x55)
+
+
+@pytest.mark.parametrize("N,K", [(1, 1), (3, 17), (64, 64), (65, 129), (130, 200), (200, 640)])
+def test_pack_roundtrip_and_fields(N, K):
+    T = synth.random_ternary(N, K, seed=N * 1000 + K)
+    P = O.pack(T)
+    fields = np.stack([(P >> s) & 3 for s in (0, 2, 4, 6)])
+    assert not np.any(fields == 3)  # 0b11 is never written
+    T2, bad = O.unpack(P, N, K)
+    assert bad == 0
+    np.testing.assert_array_equal(T2, T)
+    # number of nonzero fields == number of nonzero codes (zero survives)
+    assert int(np.sum(fields != 1)) == int(np.count_nonzero(T))
+
+
+def test_unpack_reports_malformed_fields():
+    P = O.pack(np.zeros((64, 64), np.int8))
+    P[7] = 0xFF  # four fields of value 3
+    _, bad = O.unpack(P, 64, 64)
+    assert bad == 4
+    P = O.pack(np.zeros((3, 10), np.int8))
+    P[-1] = 0x00  # padding region no longer zero codes
+    _, bad = O.unpack(P, 3, 10)
+    assert bad == 4
+
+
+def test_ternary_codes_only_in_set():
+    # [AN] "What it does": weights in {-1, 0, +1}; zero is a real state.
+    rng = np.random.default_rng(5)
+    W = (rng.standard_normal((300, 200)) * rng.choice([1e-3, 1.0, 50.0], (300, 1))).astype(np.float32)
+    T, g = O.quantize_weights(W)
+    assert set(np.unique(T)).issubset({-1, 0, 1})
+    assert np.any(T == 0) and np.any(T == 1) and np.any(T == -1)
+
+
+# ------------------------------------------------- quantizer fixtures/ties --
+
+def test_weight_quantizer_golden_ties():
+    rows = {ln.split()[1]: ln.split()[2:] for ln in _golden("quant_fixtures.txt")
+            if ln.startswith("weights")}
+    W = np.array([float(v) for v in rows["W"]], np.float32).reshape(4, 4)
+    gamma = O.absmean_scale(W)
+    assert gamma == float(rows["gamma"][0])
+    T = O.ternarize(W, gamma)
+    np.testing.assert_array_equal(T.ravel(), np.array([int(v) for v in rows["T"]], np.int8))
+
+
+def test_weight_quantizer_is_nearest_code_with_ties_to_zero():
+    # exact-arithmetic argmin over {-1,0,1}, ties to 0, on random values and
+    # on constructed exact ties |w| = gamma/2 and |w| = 3*gamma/2
+    rng = np.random.default_rng(11)
+    gammas = np.float32(2.0) ** rng.integers(-12, 3, 64).astype(np.float32)
+    for g in gammas:
+        g = float(g)
+        ws = list(rng.standard_normal(40).astype(np.float32) * np.float32(g))
+        ws += [g / 2, -g / 2, 1.5 * g, -1.5 * g, g, -g, 0.0, -0.0, 3 * g, -3 * g]
+        W = np.array(ws, np.float32).reshape(1, -1)
+        T = O.ternarize(W, g)
+        want = [_exact_ternary(float(w), g) for w in W.ravel()]
+        assert list(T.ravel()) == want
+
+
+def test_absmean_scale_matches_exact_mean():
+    # gamma = mean |W| in exact arithmetic, rounded once to fp32
+    rng = np.random.default_rng(3)
+    for shape in [(4, 4), (7, 13), (64, 96)]:
+        W = (rng.standard_normal(shape) * 0.02).astype(np.float32)
+        exact = sum(Fraction(float(abs(w))) for w in W.ravel()) / W.size
+        want = np.float32(float(exact))
+        got = O.absmean_scale(W)
+        # the fp64 running sum may differ from the exact mean in the last
+        # fp64 bits; after rounding to fp32 the two agree to 1 ulp
+        assert abs(got - float(want)) <= float(np.spacing(want))
+        assert abs(got - float(exact)) / float(exact) < 1e-6
+    assert O.absmean_scale(np.zeros((3, 5), np.float32)) == np.float32(1e-5)
+
+
+def test_activation_quantizer_golden():
+    acts = [ln for ln in _golden("quant_fixtures.txt") if ln.startswith("act ")]
+    assert len(acts) == 3
+    for ln in acts:
+        x, q, tail = ln[4:].split("|")
+        X = np.array([float(v) for v in x.split()], np.float32).reshape(1, -1)
+        Q, a, rs = O.quant_act(X)
+        assert list(Q.ravel()) == [int(v) for v in q.split()]
+        amax, rsum = tail.split()
+        assert a[0] == np.float32(float(amax))
+        assert rs[0] == int(rsum)
+
+
+def test_activation_quantizer_exact_rounding_power_of_two_scales():
+    # with a = 127 * 2^e the multiplier 127/a = 2^-e is exact, so x*s is
+    # exact and q must be the half-to-even rounding of the exact product
+    rng = np.random.default_rng(17)
+    for e in range(-6, 7):
+        a = 127.0 * 2.0 ** e
+        x = (rng.integers(-254, 255, 200) / 2.0 * 2.0 ** e).astype(np.float32)
+        x[0] = a
+        X = x.reshape(1, -1)
+        Q, am, rs = O.quant_act(X)
+        assert am[0] == np.float32(a)
+        want = [max(-127, min(127, _frac_round_half_even(Fraction(float(v)) / Fraction(2.0 ** e))))
+                for v in x]
+        assert list(Q.ravel()) == want
+        assert rs[0] == sum(want)
+
+
+def test_epilogue_golden():
+    for ln in (ln for ln in _golden("quant_fixtures.txt") if ln.startswith("epi ")):
+        head, acc, y = ln[4:].split("|")
+        gamma, amax = (float(v) for v in head.split())
+        acc = np.array([int(v) for v in acc.split()], np.int32).reshape(1, -1)
+        Y = O.epilogue(acc, gamma, np.array([amax], np.float32))
+        np.testing.assert_array_equal(Y.ravel(), np.array([float(v) for v in y.split()], np.float32))
+
+
+# ------------------------------------------ P-C identity and library check --
+
+@pytest.mark.parametrize("M,N,K", [(1, 7, 5), (4, 256, 256), (9, 65, 130)])
+def test_matmul_identity_and_library(M, N, K):
+    T = synth.random_ternary(N, K, seed=M + N + K)
+    Q = synth.random_int8(M, K, seed=M * N)
+    acc = O.matmul(Q, T)
+    # [AN]: with ternary weights the product is additions and subtractions
+    np.testing.assert_array_equal(acc, O.matmul_addsub(Q, T))
+    # library routine, int64 so nothing can wrap
+    np.testing.assert_array_equal(acc, Q.astype(np.int64) @ T.astype(np.int64).T)
+    # straight from the packed buffer, every row
+    P = O.pack(T)
+    np.testing.assert_array_equal(O.matmul_packed_rows(Q, P, N, K, np.arange(N)), acc)
+
+
+def test_matmul_catches_transposed_operand():
+    # a non-symmetric case where Q @ T.T and Q @ T differ
+    T = np.array([[1, 0], [0, 0]], np.int8)
+    Q = np.array([[0, 5]], np.int8)
+    acc = O.matmul(Q, T)
+    assert acc.tolist() == [[0, 0]]
+    T = np.array([[0, 1], [0, 0]], np.int8)
+    assert O.matmul(Q, T).tolist() == [[5, 0]]
+
+
+# ---------------------------------------------------- P-D brute force 4x4 --
+
+def test_bruteforce_all_ternary_4x4_small_block():
+    # all 81 ternary 1x4 rows against a set of int8 rows, in Python
+    import itertools
+    Q = np.array([[127, -127, 0, 1], [-1, 2, -3, 4], [100, -50, 25, -12]], np.int8)
+    rows = np.array(list(itertools.product((-1, 0, 1), repeat=4)), np.int8)
+    acc = O.matmul(Q, rows)
+    for m in range(3):
+        for n in range(81):
+            assert acc[m, n] == sum(int(Q[m, k]) * int(rows[n, k]) for k in range(4))
+
+
+@pytest.mark.slow
+def test_bruteforce_all_3pow16_ternary_4x4(tmp_path):
+    # every one of the 3^16 ternary 4x4 matrices, in C (about 20 s)
+    O.lib()
+    exe = tmp_path / "bruteforce_4x4"
+    src = os.path.join(ROOT, "tests", "csrc", "bruteforce_4x4.c")
+    odir = os.path.join(ROOT, "oracle")
+    subprocess.run(["gcc", "-O2", "-o", str(exe), src, f"-L{odir}", "-loracle",
+                    f"-Wl,-rpath,{odir}"], check=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout
+    assert out.strip() == "ok 43046721"
+
+
+# ------------------------------------------------------- P-E fixed points --
+
+def test_fixed_points():
+    rng = np.random.default_rng(23)
+    # quantize(g0 * T) == T for a ternary T with at least one nonzero
+    T = synth.random_ternary(37, 91, seed=4)
+    for g0 in (0.02, 1.0, 3.5):
+        W = (T.astype(np.float32) * np.float32(g0))
+        T2, g = O.quantize_weights(W)
+        np.testing.assert_array_equal(T2, T)
+        assert g <= np.float32(g0) * (1 + 1e-6)
+    # integer rows with max |x| = 127 quantize to themselves
+    X = rng.integers(-127, 128, (5, 64)).astype(np.float32)
+    X[:, 3] = 127
+    Q, a, rs = O.quant_act(X)
+    np.testing.assert_array_equal(Q, X.astype(np.int8))
+    assert np.all(a == 127) and np.all(rs == X.sum(1))
+    # T = I gives acc = Q; all +1 gives rowsum; all -1 gives -rowsum
+    Qi = synth.random_int8(3, 50, seed=9)
+    np.testing.assert_array_equal(O.matmul(Qi, np.eye(50, dtype=np.int8)), Qi.astype(np.int32))
+    rsum = Qi.astype(np.int32).sum(1)
+    np.testing.assert_array_equal(O.matmul(Qi, np.ones((4, 50), np.int8)), np.repeat(rsum[:, None], 4, 1))
+    np.testing.assert_array_equal(O.matmul(Qi, -np.ones((4, 50), np.int8)), -np.repeat(rsum[:, None], 4, 1))
+
+
+def test_all_zero_token_and_matrix():
+    X = np.zeros((2, 64), np.float32)
+    X[1] = 0.5
+    W = np.zeros((8, 64), np.float32)
+    T, g = O.quantize_weights(W)
+    assert g == np.float32(1e-5) and not T.any()
+    out = O.forward(X, T, g)
+    assert out["absmax"][0] == np.float32(1e-5)
+    assert not out["Q"][0].any() and not out["Y"].any()
+
+
+# ------------------------------------------------ P-F / P-G statistics ------
+
+def _p_zero_gaussian():
+    # w ~ N(0, s^2): gamma = E|w| = s sqrt(2/pi); t = 0 iff |w| <= gamma/2
+    return math.erf(0.5 * math.sqrt(2 / math.pi) / math.sqrt(2))
+
+
+def test_zero_fraction_closed_form_config1():
+    p0 = _p_zero_gaussian()
+    assert abs(p0 - 0.31006) < 1e-5  # "about one-third zeros"
+    W, _ = synth.config1()
+    T, g = O.quantize_weights(W)
+    n = T.size
+    sd = math.sqrt(p0 * (1 - p0) / n)
+    frac0 = np.mean(T == 0)
+    assert abs(frac0 - p0) < 5 * sd
+    # the +1 and -1 halves are symmetric
+    assert abs(np.mean(T == 1) - np.mean(T == -1)) < 5 * math.sqrt(0.5 / n)
+
+
+@pytest.mark.slow
+def test_zero_fraction_closed_form_2560():
+    p0 = _p_zero_gaussian()
+    W = synth.weights_np(2560, 2560, 0.02, seed=1000)
+    T, g = O.quantize_weights(W)
+    sd = math.sqrt(p0 * (1 - p0) / T.size)
+    assert abs(np.mean(T == 0) - p0) < 5 * sd
+    assert abs(g - 0.02 * math.sqrt(2 / math.pi)) / g < 2e-3
+
+
+def test_output_cosine_closed_form():
+    # weight-level correlation of t with w for Gaussian w:
+    # 2 phi(a) / sqrt(1 - p0) with a = sqrt(2/pi)/2  (= 0.8871)
+    a = 0.5 * math.sqrt(2 / math.pi)
+    rho = 2 * math.exp(-a * a / 2) / math.sqrt(2 * math.pi) / math.sqrt(1 - _p_zero_gaussian())
+    assert abs(rho - 0.8871) < 1e-4
+    W = synth.weights_np(1024, 1024, 0.02, seed=77)
+    X = synth.activations_np(16, 1024, seed=78)
+    T, g = O.quantize_weights(W)
+    Y = O.forward(X, T, g)["Y"].astype(np.float64)
+    Yr = X.astype(np.float64) @ W.astype(np.float64).T
+    cos = np.sum(Y * Yr) / math.sqrt(np.sum(Y * Y) * np.sum(Yr * Yr))
+    assert abs(cos - rho) < 0.03
+    # the scale is pinned too, not only the direction.  Regressing the real
+    # output on the quantized one gives E[t w] / (gamma E[t^2])
+    # = 2 phi(a) / (sqrt(2/pi) (1 - p0)) = 1.3385 for Gaussian w: absmean is
+    # not the least-squares scale, and a lost or doubled factor shows here.
+    gain_cf = 2 * math.exp(-a * a / 2) / math.sqrt(2 * math.pi) / (
+        math.sqrt(2 / math.pi) * (1 - _p_zero_gaussian()))
+    assert abs(gain_cf - 1.3385) < 1e-3
+    gain = np.sum(Y * Yr) / np.sum(Y * Y)
+    assert abs(gain - gain_cf) < 0.03
+
+
+# ---------------------------------------------------- P-H bounds -------------
+
+def test_bounds_and_fp64_reference():
+    W, X = synth.config1()
+    T, g = O.quantize_weights(W)
+    out = O.forward(X, T, g)
+    K = X.shape[1]
+    assert np.all(np.abs(out["acc"]) <= 127 * K)
+    y, y64 = out["Y"].astype(np.float64), out["Y64"]
+    nz = y64 != 0
+    assert np.all(np.abs(y[nz] - y64[nz]) <= 1e-5 * np.abs(y64[nz]))
+    assert np.all(y[~nz] == 0)
+    # and acc == 0 gives exactly 0
+    assert np.all(out["Y"][out["acc"] == 0] == 0)
+
+
+# ------------------------------------------------ P-I per-token outliers -----
+
+def test_outlier_channels_raise_only_their_token_scale():
+    K = 2560
+    X = synth.activations_np(64, K, seed=5, outlier_frac=0.01)
+    Xc = synth.activations_np(64, K, seed=5)
+    Q, a, _ = O.quant_act(X)
+    Qc, ac, _ = O.quant_act(Xc)
+    ch = synth.outlier_channels(K, 5)
+    assert ch.size == 26
+    assert np.all(a > 4 * ac)           # the scale follows the outliers
+    assert 30 < np.median(a) < 60       # ~20 x the max of ~26 |N(0,1)| draws
+    # zero fraction of ordinary channels per token is 2 Phi(a/254) - 1
+    mask = np.ones(K, bool)
+    mask[ch] = False
+    z = np.mean(Q[:, mask] == 0, axis=1)
+    expect = np.array([math.erf((float(t) / 254) / math.sqrt(2)) for t in a])
+    sd = np.sqrt(expect * (1 - expect) / mask.sum())
+    assert np.all(np.abs(z - expect) < 5 * sd + 1e-3)
+    assert 0.10 < float(np.mean(z)) < 0.20
+    # one token's outlier scale does not touch another's: token-wise scales
+    X2 = Xc.copy()
+    X2[0, 0] = 1000.0
+    Q2, a2, _ = O.quant_act(X2)
+    np.testing.assert_array_equal(Q2[1:], Qc[1:])
+    np.testing.assert_array_equal(a2[1:], ac[1:])
