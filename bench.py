@@ -1,0 +1,251 @@
+"""Benchmark of the BitLinear W1.58A8 hot path on one MI355X.
+
+Default workload (one step): the 2B-class decode GEMV set -- 30 layers x
+{q, k, v, o, gate, up, down} = 210 BitLinear matrices held in HBM as 2-bit
+packed ternary codes (521.0 MB), one token (M = 1) of fresh fp32
+activations per matrix.  A step quantizes every activation vector per token
+(absmax -> int8) and contracts it with its packed matrix, rescaling to fp32
+(grouped launches: one activation-quantization kernel, one contraction
+kernel for all 210 problems).  Weights are quantized and packed once, before
+timing, like loading an inference-ready checkpoint.
+
+Printed: one JSON line.  value = packed weight bytes per step / step time.
+roofline = the contraction kernel's algorithmic bytes (packed weights + int8
+activations + fp32 outputs) over its average duration (HIP events on the
+launch stream), against 8 TB/s.  prefill = the same 210 matrices at
+M = 512 (int8 TOP/s against 5.0 POP/s dense int8).  cpu_baseline = the CPU
+oracle (single thread) on a bounded sample of the same workload.
+
+Inputs are synthetic: weights ~ N(0, 0.02) drawn on the device per matrix,
+activations ~ N(0, 1) (prefill: 1% of channels x20), seeded.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+import synth  # noqa: E402
+
+METRIC = "BitLinear packed-weight GB/s at M=1 (HBM roofline %) + int8 TOPS at M=512"
+HBM_PEAK_GBS = 8000.0
+INT8_PEAK_TOPS = 5000.0
+KERNEL_SOURCES = ["ternary_weight_w1_amd/csrc/gemv_stream.hip", "ternary_weight_w1_amd/csrc/gemm_tile.hip",
+                  "ternary_weight_w1_amd/csrc/mm_common.hpp", "ternary_weight_w1_amd/csrc/common.hpp"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def build_stack(B, torch, model: str, layers: int, dev):
+    """Quantize and pack every matrix of the stack on the device."""
+    spec = synth.MODELS[model]
+    mats = []
+    for layer in range(layers):
+        for j, (name, K, N) in enumerate(spec["shapes"]):
+            W = synth.weights_torch(N, K, spec["sigma"], synth.matrix_seed(layer, j), dev)
+            T, g = B.quantize_weights(W)
+            del W
+            P = B.pack(T)
+            del T
+            mats.append(dict(layer=layer, name=name, K=K, N=N, P=P, gamma=g))
+    torch.cuda.synchronize()
+    return mats
+
+
+def make_plan(B, torch, mats, M, dev, outliers=0.0, seed0=7):
+    probs = []
+    for i, m in enumerate(mats):
+        X = synth.activations_torch(M, m["K"], seed0 + i, dev, outlier_frac=outliers)
+        Y = torch.empty((M, m["N"]), dtype=torch.float32, device=dev)
+        probs.append(dict(X=X, P=m["P"], gamma=m["gamma"], Y=Y, N=m["N"]))
+    plan = B.GroupPlan(probs, device=dev)
+    torch.cuda.synchronize()
+    return plan, probs
+
+
+def time_plan(torch, plan, steps, warmup):
+    """Wall time of `steps` steps, and HIP-event durations of each step's
+    contraction launch (events recorded on the launch stream)."""
+    for _ in range(warmup):
+        plan.quant_act()
+        plan.matmul()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    t0 = time.perf_counter()
+    for a, b in evs:
+        plan.quant_act()
+        a.record()
+        plan.matmul()
+        b.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern_ms = [a.elapsed_time(b) for a, b in evs]
+    return wall / steps * 1e3, float(np.mean(kern_ms)), float(np.median(kern_ms))
+
+
+def load_traffic(name):
+    """HBM traffic of the dominant kernel from the committed rocprofv3 PMC
+    summary, if it was taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = d.get(name)
+    if not e or e.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    return e.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(model: str, seconds: float = 10.0):
+    """The oracle, untuned, single thread: unpack + activation quantization +
+    triple-loop contraction + rescale on one layer of the stack (7 matrices,
+    M = 1), repeated until about `seconds` of CPU time."""
+    import oracle as O
+    spec = synth.MODELS[model]
+    work = []
+    for j, (name, K, N) in enumerate(spec["shapes"]):
+        W = synth.weights_np(N, K, spec["sigma"], synth.matrix_seed(0, j))
+        T, g = O.quantize_weights(W)
+        work.append((synth.activations_np(1, K, 7 + j), O.pack(T), g, N, N * K // 4))
+        del W, T
+    reps, t, nbytes = 0, 0.0, 0
+    while t < seconds:
+        t0 = time.perf_counter()
+        for X, P, g, N, b in work:
+            O.forward_packed(X, P, g, N)
+            nbytes += b
+        t += time.perf_counter() - t0
+        reps += 1
+    return {"value": nbytes / t / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"layer 0 of the {model.upper()} stack (7 matrices, M=1) x {reps} passes, "
+                      f"{t:.1f} s single-thread: unpack + act quant + int32 triple loop + rescale"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--model", default="2b", choices=sorted(synth.MODELS))
+    ap.add_argument("--layers", type=int, default=None)
+    ap.add_argument("--M", type=int, default=1)
+    ap.add_argument("--prefill-M", type=int, default=512)
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="run only a plain device copy of known size (PMC calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import ternary_weight_w1_amd as B
+    B.lib()
+    dev = torch.device("cuda:0")
+
+    if args.copy_probe:
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy probe: 3 x {n} bytes")
+        return
+
+    spec = synth.MODELS[args.model]
+    layers = args.layers or spec["layers"]
+    log(f"building {args.model} stack: {layers} layers")
+    mats = build_stack(B, torch, args.model, layers, dev)
+    packed = sum(m["N"] * m["K"] // 4 for m in mats)
+    assert packed == sum(B.packed_bytes(m["N"], m["K"]) for m in mats)
+
+    M = args.M
+    plan, probs = make_plan(B, torch, mats, M, dev)
+    log(f"timing decode sweep: {len(mats)} matrices, M={M}, {packed / 1e6:.1f} MB packed")
+    ms, kern_ms, kern_med = time_plan(torch, plan, args.steps, args.warmup)
+    value = packed / (ms * 1e-3) / 1e9
+    act_bytes = sum(M * B.q_stride(m["K"]) + 8 * M for m in mats)
+    out_bytes = sum(4 * M * m["N"] for m in mats)
+    alg_bytes = packed + act_bytes + out_bytes
+    achieved = alg_bytes / (kern_ms * 1e-3) / 1e9
+    traffic = load_traffic(f"stream_{args.model}_m{M}")
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i8",
+        "data": "synthetic (seeded N(0,0.02) weights quantized+packed on device; N(0,1) activations)",
+        "config": {"workload": f"{args.model.upper()}-class decode GEMV set: {layers} layers x "
+                               f"q,k,v,o,gate,up,down BitLinear, M={M}, packed ternary resident in HBM",
+                   "matrices": len(mats), "M": M, "packed_bytes": packed},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic,
+                     "kernel": "stream contraction (grouped, one launch per step)",
+                     "kernel_ms_mean": round(kern_ms, 5), "kernel_ms_median": round(kern_med, 5),
+                     "bytes_per_launch": alg_bytes},
+    }
+    del plan, probs
+    torch.cuda.empty_cache()
+
+    if not args.no_prefill:
+        PM = args.prefill_M
+        plan, probs = make_plan(B, torch, mats, PM, dev, outliers=0.01)
+        log(f"timing prefill sweep: M={PM}")
+        steps = max(3, args.steps // 5)
+        pms, pkern, pmed = time_plan(torch, plan, steps, max(1, args.warmup // 2))
+        ops = sum(2 * PM * m["N"] * m["K"] for m in mats)
+        result["prefill"] = {
+            "M": PM, "ms_per_step": round(pms, 4), "value": round(ops / (pms * 1e-3) / 1e12, 2),
+            "unit": "TOP/s",
+            "roofline": {"bound": "mfma", "achieved": round(ops / (pkern * 1e-3) / 1e12, 2),
+                         "peak": INT8_PEAK_TOPS, "unit": "TOP/s",
+                         "frac": round(ops / (pkern * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4),
+                         "traffic": load_traffic(f"tile_{args.model}_m{PM}"),
+                         "kernel": "tile contraction (grouped)", "kernel_ms_mean": round(pkern, 4),
+                         "ops_per_launch": ops},
+        }
+        del plan, probs
+        torch.cuda.empty_cache()
+
+    if not args.no_cpu:
+        log("timing CPU oracle baseline")
+        result["cpu_baseline"] = cpu_baseline(args.model)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,217 @@
+/*
+ * bitlinear.h -- C ABI of the MI355X (gfx950) BitLinear W1.58A8 library.
+ *
+ * The layer (anthology note-168 on arXiv 2402.17764, "What it does"):
+ * BitLinear stands in for nn.Linear; its weights are ternary {-1, 0, +1},
+ * chosen by an absmean quantizer, and its activations are 8-bit.  The
+ * product of ternary weights with integer activations needs only integer
+ * additions (same note, "The part that is a bet rather than a measurement").
+ * For inference the weights are quantized once and stored packed, four
+ * codes to a byte, then streamed to the compute units and unpacked there
+ * next to the 8-bit multiply (BitNet b1.58 2B4T video transcript,
+ * yousumm.com, "Transcription").
+ *
+ * Definitions implemented (readings of the pages; they print no formula):
+ *   gamma  = max(1e-5, fp32(mean |W|))        mean over all N*K, fp64 sum
+ *   T[n,k] = clamp(rint(W[n,k] / gamma), -1, 1)   fp32 IEEE divide, half-even
+ *   a[m]   = max(1e-5, max_k |X[m,k]|)
+ *   Q[m,k] = clamp(rint(X[m,k] * (127 / a[m])), -127, 127)
+ *   acc[m,n] = sum_k T[n,k] * Q[m,k]           exact int32
+ *   Y[m,n] = float(acc[m,n]) * ((gamma * a[m]) / 127)
+ *
+ * Conventions for every call
+ *   - Matrices are row-major.  W and T are N x K (N = out features, K = in
+ *     features); X and Q are M x K (M tokens); Y and acc are M x N.
+ *   - Every buffer pointer is DEVICE memory allocated and owned by the
+ *     caller.  The library never allocates, frees or synchronizes; every
+ *     call only enqueues kernels on `stream` (a hipStream_t; NULL = the
+ *     default stream) and returns.  Results are ready when the stream is.
+ *   - Every device buffer must be 16-byte aligned (BITLINEAR_ERR_ALIGN).
+ *   - Return value: BITLINEAR_OK (0) or a negative status.  On a
+ *     validation error nothing is enqueued.  bitlinear_strerror() names a
+ *     status; bitlinear_last_error() gives the calling thread's last
+ *     detailed message (including the HIP error text on BITLINEAR_ERR_HIP).
+ *   - Sizes: 1 <= M, N <= 2^24 and 1 <= K <= 131072, so |acc| <= 127*K
+ *     < 2^24 is exact in int32 and converts to fp32 exactly.  Any M, N, K
+ *     in range is accepted (no multiple-of-64 requirement); internally K
+ *     is padded to a multiple of 64 with zero codes / zero activations.
+ *   - NaN or infinite inputs give unspecified (but memory-safe) results.
+ *   - Calls are reentrant; the library holds no mutable global state.  Two
+ *     calls that share a workspace must not run concurrently.
+ *
+ * Packed weight format "BL2-T64" (the buffer bitlinear_pack writes and the
+ * matmul calls read; bitlinear_packed_bytes(N, K) bytes):
+ *   field = code + 1 in 2 bits, so {-1, 0, +1} -> {0, 1, 2}; 3 never occurs;
+ *   0x55 is four zero codes.  Rows are grouped in tiles of 64 (t = n / 64),
+ *   K in units of 64 codes (u = k / 64), KU = ceil(K / 64) units per row.
+ *   Tile t, unit u is a 1024-byte block at (t * KU + u) * 1024 made of 64
+ *   slots of 16 bytes; 32-bit little-endian word d = 2*s + h of slot L
+ *   holds row 64*t + 32*s + (L % 32), codes k = 64*u + 32*h + 16*(L / 32)
+ *   + c for c = 0..15, code c at bit 8*(c % 4) + 2*(c / 4).  Rows >= N and
+ *   codes >= K are padding and hold zero codes.
+ *   Why this order: one 16-byte load per lane gives a 64-row x 64-code
+ *   block; (word >> 2j) & 0x03030303 yields four consecutive codes as
+ *   bytes, ready for a 4-way int8 dot product, and the four planes of one
+ *   word are exactly the 16-byte int8 operand of one lane of the gfx950
+ *   32x32x32 int8 matrix instruction.
+ */
+#ifndef BITLINEAR_H
+#define BITLINEAR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BITLINEAR_ABI_VERSION 1
+
+enum bitlinear_status {
+    BITLINEAR_OK = 0,
+    BITLINEAR_ERR_NULL = -1,      /* a required pointer is NULL                 */
+    BITLINEAR_ERR_SHAPE = -2,     /* a size is out of range or inconsistent     */
+    BITLINEAR_ERR_ALIGN = -3,     /* a buffer or stride is not 16-byte aligned  */
+    BITLINEAR_ERR_WORKSPACE = -4, /* workspace missing or smaller than needed   */
+    BITLINEAR_ERR_HIP = -5,       /* the HIP runtime refused a launch           */
+    BITLINEAR_ERR_ARG = -6        /* any other bad argument (op code, table)    */
+};
+
+/* Workspace kinds for bitlinear_workspace_bytes. */
+enum bitlinear_ws_op {
+    BITLINEAR_WS_QUANTIZE_WEIGHTS = 1,
+    BITLINEAR_WS_MATMUL = 2,
+    BITLINEAR_WS_FORWARD = 3
+};
+
+/* Library ABI version (BITLINEAR_ABI_VERSION of the build). */
+int bitlinear_abi_version(void);
+
+/* Static text for a status code. */
+const char *bitlinear_strerror(int status);
+
+/* The calling thread's last detailed error message ("" if none). */
+const char *bitlinear_last_error(void);
+
+/* Bytes of the BL2-T64 buffer for an N x K matrix:
+ * ceil(N/64) * ceil(K/64) * 1024 (= N*K/4 when 64 divides N and K).
+ * Returns 0 for sizes out of range. */
+size_t bitlinear_packed_bytes(int64_t N, int64_t K);
+
+/* Smallest row stride (bytes) of an int8 activation matrix that the matmul
+ * calls accept: K rounded up to a multiple of 64. */
+int64_t bitlinear_q_stride(int64_t K);
+
+/* Workspace bytes that `op` needs for these sizes (0 if none; SIZE_MAX if
+ * the sizes are invalid).  M is ignored for BITLINEAR_WS_QUANTIZE_WEIGHTS. */
+size_t bitlinear_workspace_bytes(int op, int64_t M, int64_t N, int64_t K);
+
+/*
+ * Weight quantization (absmean -> ternary), once per weight matrix.
+ *   W         [in]  N x K fp32.
+ *   gamma_in  [in]  NULL: compute gamma = absmean of W (deterministic fp64
+ *                   two-stage reduction, rounded once to fp32).  Non-NULL:
+ *                   device pointer to one fp32 used as gamma instead.
+ *   T_out     [out] N x K int8 codes in {-1, 0, +1}.
+ *   gamma_out [out] one fp32: the scale used.
+ *   ws        workspace of bitlinear_workspace_bytes(BITLINEAR_WS_QUANTIZE_
+ *             WEIGHTS, 0, N, K) bytes (may be NULL when that is 0).
+ */
+int bitlinear_quantize_weights(const float *W, int64_t N, int64_t K, const float *gamma_in,
+                               int8_t *T_out, float *gamma_out, void *ws, size_t ws_bytes,
+                               void *stream);
+
+/*
+ * Pack ternary codes into BL2-T64 (four codes per byte).
+ *   T      [in]  N x K int8 codes; values outside {-1, 0, +1} are clamped.
+ *   P_out  [out] bitlinear_packed_bytes(N, K) bytes; padding is written too.
+ */
+int bitlinear_pack(const int8_t *T, int64_t N, int64_t K, uint8_t *P_out, void *stream);
+
+/*
+ * Unpack BL2-T64 back to N x K int8 codes (inverse of bitlinear_pack; a
+ * malformed field 3 decodes as 0).
+ */
+int bitlinear_unpack(const uint8_t *P, int64_t N, int64_t K, int8_t *T_out, void *stream);
+
+/*
+ * Per-token absmax int8 activation quantization.
+ *   X          [in]  M x K fp32.
+ *   Q_out      [out] M rows of ldq bytes: K int8 codes, then zeros up to ldq.
+ *   ldq        row stride of Q_out in bytes, ldq >= K, ldq % 16 == 0.
+ *   absmax_out [out] M fp32 scales a[m].
+ *   rowsum_out [out] M int32 sums of each row of Q (nullable).
+ */
+int bitlinear_quant_act(const float *X, int64_t M, int64_t K, int8_t *Q_out, int64_t ldq,
+                        float *absmax_out, int32_t *rowsum_out, void *stream);
+
+/*
+ * Ternary x int8 contraction and rescale from already-quantized activations
+ * (lets a caller supply Q, a and the row sums itself).
+ *   Q       [in]  M rows of ldq bytes, ldq >= bitlinear_q_stride(K),
+ *                 ldq % 16 == 0; bytes K..ldq-1 of each row must be 0.
+ *   absmax  [in]  M fp32 activation scales.
+ *   rowsum  [in]  M int32, rowsum[m] = sum_k Q[m,k].
+ *   P       [in]  BL2-T64 weights of an N x K matrix.
+ *   gamma   [in]  one fp32 weight scale (device).
+ *   Y_out   [out] M x N fp32.
+ *   acc_out [out] M x N int32 exact accumulators (nullable; for checking).
+ *   ws      bitlinear_workspace_bytes(BITLINEAR_WS_MATMUL, M, N, K) bytes.
+ */
+int bitlinear_matmul(const int8_t *Q, int64_t ldq, const float *absmax, const int32_t *rowsum,
+                     int64_t M, int64_t K, const uint8_t *P, const float *gamma, int64_t N,
+                     float *Y_out, int32_t *acc_out, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * The whole BitLinear forward: quantize X per token, contract with the
+ * packed ternary weights, rescale.
+ *   X       [in]  M x K fp32.          P, gamma as for bitlinear_matmul.
+ *   Y_out   [out] M x N fp32.          acc_out as for bitlinear_matmul.
+ *   ws      bitlinear_workspace_bytes(BITLINEAR_WS_FORWARD, M, N, K) bytes;
+ *           it receives Q, a and the row sums (layout private).
+ */
+int bitlinear_forward(const float *X, int64_t M, int64_t K, const uint8_t *P,
+                      const float *gamma, int64_t N, float *Y_out, int32_t *acc_out,
+                      void *ws, size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------------- */
+/* Grouped forward: many independent BitLinear layers in one launch per    */
+/* stage (e.g. every weight matrix of a model, or q|k|v sharing an input). */
+/* ---------------------------------------------------------------------- */
+
+typedef struct bitlinear_problem {
+    const float *X;     /* M x K fp32 activations (device)                  */
+    const uint8_t *P;   /* BL2-T64 weights of the N x K matrix (device)     */
+    const float *gamma; /* one fp32 weight scale (device)                   */
+    float *Y;           /* M x N fp32 output (device)                       */
+    int32_t *acc;       /* M x N int32 accumulators (device, nullable)      */
+    int64_t M, N, K;
+} bitlinear_problem;
+
+/* Host bytes of the plan table for these problems (0 on invalid input),
+ * and the device workspace bytes the group needs. */
+size_t bitlinear_group_table_bytes(const bitlinear_problem *probs, int count);
+size_t bitlinear_group_workspace_bytes(const bitlinear_problem *probs, int count);
+
+/*
+ * Validate the problems and write the plan table into HOST memory
+ * (table_host, table_bytes >= bitlinear_group_table_bytes).  The plan binds
+ * the problems' buffers and the device workspace `ws` (ws_bytes >=
+ * bitlinear_group_workspace_bytes).  The caller copies the table byte for
+ * byte to a 16-byte aligned device buffer and passes both copies to the
+ * calls below; host copy gives launch sizes, device copy feeds the kernels.
+ */
+int bitlinear_group_plan(const bitlinear_problem *probs, int count, void *ws, size_t ws_bytes,
+                         void *table_host, size_t table_bytes);
+
+/* Stage 1 of the grouped forward: quantize every problem's activations. */
+int bitlinear_group_quant_act(const void *table_host, const void *table_dev, void *stream);
+/* Stage 2: contract and rescale every problem (reads stage 1's results). */
+int bitlinear_group_matmul(const void *table_host, const void *table_dev, void *stream);
+/* Both stages. */
+int bitlinear_group_forward(const void *table_host, const void *table_dev, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* BITLINEAR_H */

@@ -1,0 +1,246 @@
+"""Python binding of libbitlinear.so (include/bitlinear.h), the gfx950 HIP
+BitLinear W1.58A8 library.
+
+Argument marshalling only: every step of the layer runs in the library's HIP
+kernels.  torch supplies device memory and the current stream.  There is no
+fallback: if the shared library is missing, importing works but the first
+call raises.
+
+Functions carry the C names without the ``bitlinear_`` prefix:
+quantize_weights, pack, unpack, quant_act, matmul, forward, plus the
+grouped forward (GroupPlan).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libbitlinear.so")
+
+OK = 0
+WS_QUANTIZE_WEIGHTS = 1
+WS_MATMUL = 2
+WS_FORWARD = 3
+
+_vp = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_sz = ctypes.c_size_t
+_int = ctypes.c_int
+
+
+class Problem(ctypes.Structure):
+    """ctypes mirror of struct bitlinear_problem."""
+    _fields_ = [("X", _vp), ("P", _vp), ("gamma", _vp), ("Y", _vp), ("acc", _vp),
+                ("M", _i64), ("N", _i64), ("K", _i64)]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libbitlinear.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python ternary_weight_w1_amd/build.py` (or __graft_entry__.build())")
+        L = ctypes.CDLL(LIB_PATH)
+        sig = {
+            "bitlinear_abi_version": (_int, []),
+            "bitlinear_strerror": (ctypes.c_char_p, [_int]),
+            "bitlinear_last_error": (ctypes.c_char_p, []),
+            "bitlinear_packed_bytes": (_sz, [_i64, _i64]),
+            "bitlinear_q_stride": (_i64, [_i64]),
+            "bitlinear_workspace_bytes": (_sz, [_int, _i64, _i64, _i64]),
+            "bitlinear_quantize_weights": (_int, [_vp, _i64, _i64, _vp, _vp, _vp, _vp, _sz, _vp]),
+            "bitlinear_pack": (_int, [_vp, _i64, _i64, _vp, _vp]),
+            "bitlinear_unpack": (_int, [_vp, _i64, _i64, _vp, _vp]),
+            "bitlinear_quant_act": (_int, [_vp, _i64, _i64, _vp, _i64, _vp, _vp, _vp]),
+            "bitlinear_matmul": (_int, [_vp, _i64, _vp, _vp, _i64, _i64, _vp, _vp, _i64, _vp, _vp,
+                                        _vp, _sz, _vp]),
+            "bitlinear_forward": (_int, [_vp, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _vp, _sz, _vp]),
+            "bitlinear_group_table_bytes": (_sz, [ctypes.POINTER(Problem), _int]),
+            "bitlinear_group_workspace_bytes": (_sz, [ctypes.POINTER(Problem), _int]),
+            "bitlinear_group_plan": (_int, [ctypes.POINTER(Problem), _int, _vp, _sz, _vp, _sz]),
+            "bitlinear_group_quant_act": (_int, [_vp, _vp, _vp]),
+            "bitlinear_group_matmul": (_int, [_vp, _vp, _vp]),
+            "bitlinear_group_forward": (_int, [_vp, _vp, _vp]),
+        }
+        for name, (res, args) in sig.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(status: int, what: str):
+    if status != OK:
+        L = lib()
+        raise RuntimeError(f"{what}: {L.bitlinear_strerror(status).decode()} "
+                           f"({L.bitlinear_last_error().decode()})")
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _dev_tensor(t, dtype, name):
+    if not (isinstance(t, torch.Tensor) and t.is_cuda and t.dtype == dtype and t.is_contiguous()):
+        raise TypeError(f"{name} must be a contiguous {dtype} CUDA tensor")
+    return t
+
+
+def packed_bytes(N: int, K: int) -> int:
+    return int(lib().bitlinear_packed_bytes(N, K))
+
+
+def q_stride(K: int) -> int:
+    return int(lib().bitlinear_q_stride(K))
+
+
+def workspace_bytes(op: int, M: int, N: int, K: int) -> int:
+    return int(lib().bitlinear_workspace_bytes(op, M, N, K))
+
+
+def _workspace(nbytes, device):
+    if nbytes == 0:
+        return None
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def quantize_weights(W, gamma_in=None, stream=None):
+    """(T int8 N x K, gamma fp32 [1]) for fp32 N x K weights."""
+    _dev_tensor(W, torch.float32, "W")
+    N, K = W.shape
+    T = torch.empty((N, K), dtype=torch.int8, device=W.device)
+    gamma = torch.empty(1, dtype=torch.float32, device=W.device)
+    ws = _workspace(workspace_bytes(WS_QUANTIZE_WEIGHTS, 0, N, K), W.device)
+    _check(lib().bitlinear_quantize_weights(_ptr(W), N, K, _ptr(gamma_in), _ptr(T), _ptr(gamma),
+                                            _ptr(ws), 0 if ws is None else ws.numel(),
+                                            _stream(stream)), "quantize_weights")
+    return T, gamma
+
+
+def pack(T, stream=None):
+    """BL2-T64 packed bytes (uint8, packed_bytes(N, K)) of int8 codes."""
+    _dev_tensor(T, torch.int8, "T")
+    N, K = T.shape
+    P = torch.empty(packed_bytes(N, K), dtype=torch.uint8, device=T.device)
+    _check(lib().bitlinear_pack(_ptr(T), N, K, _ptr(P), _stream(stream)), "pack")
+    return P
+
+
+def unpack(P, N: int, K: int, stream=None):
+    _dev_tensor(P, torch.uint8, "P")
+    T = torch.empty((N, K), dtype=torch.int8, device=P.device)
+    _check(lib().bitlinear_unpack(_ptr(P), N, K, _ptr(T), _stream(stream)), "unpack")
+    return T
+
+
+def quant_act(X, ldq: int | None = None, stream=None):
+    """(Q int8 M x ldq, absmax fp32 [M], rowsum int32 [M]); ldq defaults to
+    q_stride(K), the stride the matmul call accepts."""
+    _dev_tensor(X, torch.float32, "X")
+    M, K = X.shape
+    ldq = q_stride(K) if ldq is None else ldq
+    Q = torch.empty((M, ldq), dtype=torch.int8, device=X.device)
+    a = torch.empty(M, dtype=torch.float32, device=X.device)
+    rs = torch.empty(M, dtype=torch.int32, device=X.device)
+    _check(lib().bitlinear_quant_act(_ptr(X), M, K, _ptr(Q), ldq, _ptr(a), _ptr(rs),
+                                     _stream(stream)), "quant_act")
+    return Q, a, rs
+
+
+def matmul(Q, absmax, rowsum, P, gamma, N: int, K: int, with_acc: bool = False, stream=None):
+    """Y (and acc) from already-quantized activations Q (M rows, stride
+    Q.shape[1] >= q_stride(K), zero beyond K)."""
+    _dev_tensor(Q, torch.int8, "Q")
+    _dev_tensor(absmax, torch.float32, "absmax")
+    _dev_tensor(rowsum, torch.int32, "rowsum")
+    _dev_tensor(P, torch.uint8, "P")
+    _dev_tensor(gamma, torch.float32, "gamma")
+    M, ldq = Q.shape
+    Y = torch.empty((M, N), dtype=torch.float32, device=Q.device)
+    acc = torch.empty((M, N), dtype=torch.int32, device=Q.device) if with_acc else None
+    ws = _workspace(workspace_bytes(WS_MATMUL, M, N, K), Q.device)
+    _check(lib().bitlinear_matmul(_ptr(Q), ldq, _ptr(absmax), _ptr(rowsum), M, K, _ptr(P),
+                                  _ptr(gamma), N, _ptr(Y), _ptr(acc), _ptr(ws),
+                                  0 if ws is None else ws.numel(), _stream(stream)), "matmul")
+    return (Y, acc) if with_acc else Y
+
+
+def forward(X, P, gamma, N: int, with_acc: bool = False, ws=None, out=None, stream=None):
+    """BitLinear forward: Y = rescale(ternary(P) x int8(X)), M x N fp32."""
+    _dev_tensor(X, torch.float32, "X")
+    _dev_tensor(P, torch.uint8, "P")
+    _dev_tensor(gamma, torch.float32, "gamma")
+    M, K = X.shape
+    Y = torch.empty((M, N), dtype=torch.float32, device=X.device) if out is None else out
+    acc = torch.empty((M, N), dtype=torch.int32, device=X.device) if with_acc else None
+    if ws is None:
+        ws = _workspace(workspace_bytes(WS_FORWARD, M, N, K), X.device)
+    _check(lib().bitlinear_forward(_ptr(X), M, K, _ptr(P), _ptr(gamma), N, _ptr(Y), _ptr(acc),
+                                   _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)),
+           "forward")
+    return (Y, acc) if with_acc else Y
+
+
+class GroupPlan:
+    """A grouped forward over independent BitLinear problems.
+
+    problems: sequence of dicts with keys X, P, gamma, Y (torch CUDA
+    tensors), N, and optionally acc.  M and K come from X.  The plan binds
+    these tensors and its own workspace; run it with forward() (both stages)
+    or quant_act() then matmul().
+    """
+
+    def __init__(self, problems, device=None):
+        L = lib()
+        n = len(problems)
+        arr = (Problem * n)()
+        keep = []
+        for i, p in enumerate(problems):
+            X, P, g, Y = p["X"], p["P"], p["gamma"], p["Y"]
+            acc = p.get("acc")
+            _dev_tensor(X, torch.float32, "X")
+            _dev_tensor(P, torch.uint8, "P")
+            _dev_tensor(g, torch.float32, "gamma")
+            _dev_tensor(Y, torch.float32, "Y")
+            M, K = X.shape
+            arr[i] = Problem(X.data_ptr(), P.data_ptr(), g.data_ptr(), Y.data_ptr(),
+                             _ptr(acc), M, int(p["N"]), K)
+            keep.append((X, P, g, Y, acc))
+        device = device or problems[0]["X"].device
+        ws_bytes = L.bitlinear_group_workspace_bytes(arr, n)
+        tb = L.bitlinear_group_table_bytes(arr, n)
+        if tb == 0:
+            _check(-2, "group_table_bytes")
+        self.ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=device)
+        self.table_host = torch.empty(tb, dtype=torch.uint8)
+        _check(L.bitlinear_group_plan(arr, n, self.ws.data_ptr(), self.ws.numel(),
+                                      self.table_host.data_ptr(), tb), "group_plan")
+        self.table_dev = self.table_host.to(device)
+        self._keep = keep
+        self.count = n
+
+    def quant_act(self, stream=None):
+        _check(lib().bitlinear_group_quant_act(self.table_host.data_ptr(), self.table_dev.data_ptr(),
+                                               _stream(stream)), "group_quant_act")
+
+    def matmul(self, stream=None):
+        _check(lib().bitlinear_group_matmul(self.table_host.data_ptr(), self.table_dev.data_ptr(),
+                                            _stream(stream)), "group_matmul")
+
+    def forward(self, stream=None):
+        _check(lib().bitlinear_group_forward(self.table_host.data_ptr(), self.table_dev.data_ptr(),
+                                             _stream(stream)), "group_forward")

@@ -1,0 +1,537 @@
+// Host side of the C ABI declared in include/bitlinear.h: argument
+// validation, workspace layout, kernel selection and launches.  No call
+// allocates, frees, copies or synchronizes; validation happens before the
+// first launch, so a rejected call enqueues nothing.
+#include <bitlinear.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "common.hpp"
+
+using bl::Problem;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char *fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return status;
+}
+
+int hip_fail(hipError_t e, const char *what)
+{
+    return fail(BITLINEAR_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr int64_t kMaxMN = int64_t(1) << 24;
+constexpr int64_t kMaxK = 131072;
+constexpr int kStreamMaxM = 32;  // larger token counts take the tile kernel
+
+bool a16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+bool a4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3) == 0; }
+int64_t up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+int check_nk(int64_t N, int64_t K)
+{
+    if (N < 1 || N > kMaxMN) return fail(BITLINEAR_ERR_SHAPE, "N=%lld out of range [1, 2^24]", (long long)N);
+    if (K < 1 || K > kMaxK) return fail(BITLINEAR_ERR_SHAPE, "K=%lld out of range [1, 131072]", (long long)K);
+    return BITLINEAR_OK;
+}
+
+int check_mnk(int64_t M, int64_t N, int64_t K)
+{
+    if (M < 1 || M > kMaxMN) return fail(BITLINEAR_ERR_SHAPE, "M=%lld out of range [1, 2^24]", (long long)M);
+    return check_nk(N, K);
+}
+
+// Tuning knobs, read once from the environment (immutable afterwards).
+struct Knobs {
+    int dot4_max_m = 1;          // M <= this takes the packed-dot4 kernel
+    int split_target = 1024;     // aim for at least this many workgroups
+};
+const Knobs &knobs()
+{
+    static const Knobs k = [] {
+        Knobs v;
+        if (const char *s = getenv("BITLINEAR_DOT4_MAX_M")) v.dot4_max_m = atoi(s) > 0 ? 1 : 0;
+        if (const char *s = getenv("BITLINEAR_SPLIT_TARGET")) v.split_target = atoi(s) > 0 ? atoi(s) : 1;
+        return v;
+    }();
+    return k;
+}
+
+// Kernel kind and decomposition of one problem.  `base_items` is the number
+// of streaming work items the whole launch has without K splits; splits are
+// added only while the launch is short of workgroups.
+void decompose(Problem &p, int64_t base_items)
+{
+    p.KU = (int32_t)((p.K + 63) / 64);
+    p.NT = (int32_t)((p.N + 63) / 64);
+    p.ks = 1;
+    p.upsplit = p.KU;
+    p.mt = p.ntt = p.mtile = p.ntile = 0;
+    if (p.M <= kStreamMaxM) {
+        p.kind = 0;
+        const int64_t target = knobs().split_target;
+        if (base_items < target) {
+            int64_t ks = (target + base_items - 1) / base_items;
+            int64_t cap = p.KU / 8;  // keep >= 8 units (2 per wave) per split
+            if (cap < 1) cap = 1;
+            if (ks > cap) ks = cap;
+            const int64_t upsplit = (p.KU + ks - 1) / ks;
+            p.upsplit = (int32_t)upsplit;
+            p.ks = (int32_t)((p.KU + upsplit - 1) / upsplit);
+        }
+    } else {
+        p.kind = 1;
+        p.mtile = p.M > 64 ? 128 : 64;
+        p.ntile = 256;
+        p.mt = (int32_t)((p.M + p.mtile - 1) / p.mtile);
+        p.ntt = (p.NT + 3) / 4;
+    }
+}
+
+int64_t items_of(const Problem &p)
+{
+    return p.kind == 0 ? (int64_t)p.NT * p.ks : (int64_t)p.mt * p.ntt;
+}
+
+int stream_variant_for(int64_t M) { return (M <= knobs().dot4_max_m) ? 0 : 1; }
+int tile_variant_for(int64_t M) { return M > 64 ? 1 : 0; }
+
+// Workspace layout of one problem: [Q][absmax][rowsum][partials][tickets],
+// each region 256-byte aligned.  with_act = false leaves out the first three.
+struct WsLayout {
+    int64_t q = 0, absmax = 0, rowsum = 0, part = 0, tick = 0, total = 0;
+};
+WsLayout ws_layout(const Problem &p, bool with_act)
+{
+    WsLayout L;
+    int64_t off = 0;
+    const int64_t ldq = 64 * (int64_t)p.KU;
+    if (with_act) {
+        L.q = off;
+        off = up(off + (int64_t)p.M * ldq, 256);
+        L.absmax = off;
+        off = up(off + 4 * (int64_t)p.M, 256);
+        L.rowsum = off;
+        off = up(off + 4 * (int64_t)p.M, 256);
+    }
+    if (p.kind == 0 && p.ks > 1) {
+        L.part = off;
+        off = up(off + 4 * (int64_t)p.ks * p.M * p.NT * 64, 256);
+        L.tick = off;
+        off = up(off + 4 * (int64_t)p.NT, 256);
+    }
+    L.total = off;
+    return L;
+}
+
+int quant_weight_blocks(int64_t count)
+{
+    int64_t b = (count + 65535) / 65536;
+    if (b < 1) b = 1;
+    if (b > 1024) b = 1024;
+    return (int)b;
+}
+
+Problem make_problem(int64_t M, int64_t N, int64_t K)
+{
+    Problem p;
+    memset(&p, 0, sizeof p);
+    p.M = (int32_t)M;
+    p.N = (int32_t)N;
+    p.K = (int32_t)K;
+    return p;
+}
+
+hipError_t launch_contraction(const Problem &p, hipStream_t s)
+{
+    if (p.kind == 0) return bl::launch_stream_single(p, stream_variant_for(p.M), s);
+    return bl::launch_tile_single(p, tile_variant_for(p.M), s);
+}
+
+}  // namespace
+
+extern "C" {
+
+int bitlinear_abi_version(void) { return BITLINEAR_ABI_VERSION; }
+
+const char *bitlinear_strerror(int status)
+{
+    switch (status) {
+    case BITLINEAR_OK: return "ok";
+    case BITLINEAR_ERR_NULL: return "a required pointer is NULL";
+    case BITLINEAR_ERR_SHAPE: return "a size is out of range or inconsistent";
+    case BITLINEAR_ERR_ALIGN: return "a buffer or stride is not aligned";
+    case BITLINEAR_ERR_WORKSPACE: return "workspace missing or too small";
+    case BITLINEAR_ERR_HIP: return "HIP runtime error";
+    case BITLINEAR_ERR_ARG: return "invalid argument";
+    default: return "unknown status";
+    }
+}
+
+const char *bitlinear_last_error(void) { return g_last_error.c_str(); }
+
+size_t bitlinear_packed_bytes(int64_t N, int64_t K)
+{
+    if (N < 1 || N > kMaxMN || K < 1 || K > kMaxK) return 0;
+    return (size_t)((N + 63) / 64) * (size_t)((K + 63) / 64) * 1024u;
+}
+
+int64_t bitlinear_q_stride(int64_t K) { return (K < 1 || K > kMaxK) ? 0 : up(K, 64); }
+
+size_t bitlinear_workspace_bytes(int op, int64_t M, int64_t N, int64_t K)
+{
+    if (op == BITLINEAR_WS_QUANTIZE_WEIGHTS) {
+        if (check_nk(N, K) != BITLINEAR_OK) return SIZE_MAX;
+        return (size_t)quant_weight_blocks(N * K) * sizeof(double);
+    }
+    if (op != BITLINEAR_WS_MATMUL && op != BITLINEAR_WS_FORWARD) return SIZE_MAX;
+    if (check_mnk(M, N, K) != BITLINEAR_OK) return SIZE_MAX;
+    Problem p = make_problem(M, N, K);
+    decompose(p, (N + 63) / 64);
+    return (size_t)ws_layout(p, op == BITLINEAR_WS_FORWARD).total;
+}
+
+int bitlinear_quantize_weights(const float *W, int64_t N, int64_t K, const float *gamma_in,
+                               int8_t *T_out, float *gamma_out, void *ws, size_t ws_bytes,
+                               void *stream)
+{
+    if (!W || !T_out || !gamma_out) return fail(BITLINEAR_ERR_NULL, "quantize_weights: W, T_out and gamma_out are required");
+    if (int st = check_nk(N, K)) return st;
+    if (!a16(W) || !a16(T_out) || !a4(gamma_out) || (gamma_in && !a4(gamma_in)))
+        return fail(BITLINEAR_ERR_ALIGN, "quantize_weights: W/T_out need 16-byte, gamma 4-byte alignment");
+    const int64_t count = N * K;
+    const int nb = quant_weight_blocks(count);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (!gamma_in) {
+        if (!ws || ws_bytes < (size_t)nb * sizeof(double) || !a16(ws))
+            return fail(BITLINEAR_ERR_WORKSPACE, "quantize_weights: needs %zu workspace bytes (16-byte aligned)",
+                        (size_t)nb * sizeof(double));
+        double *partial = static_cast<double *>(ws);
+        if (hipError_t e = bl::launch_absmean_partial(W, count, partial, nb, s)) return hip_fail(e, "absmean_partial");
+        if (hipError_t e = bl::launch_absmean_final(partial, nb, count, nullptr, gamma_out, s)) return hip_fail(e, "absmean_final");
+    } else {
+        if (hipError_t e = bl::launch_absmean_final(nullptr, 0, count, gamma_in, gamma_out, s)) return hip_fail(e, "absmean_final");
+    }
+    if (hipError_t e = bl::launch_ternarize(W, count, gamma_out, T_out, s)) return hip_fail(e, "ternarize");
+    return BITLINEAR_OK;
+}
+
+int bitlinear_pack(const int8_t *T, int64_t N, int64_t K, uint8_t *P_out, void *stream)
+{
+    if (!T || !P_out) return fail(BITLINEAR_ERR_NULL, "pack: T and P_out are required");
+    if (int st = check_nk(N, K)) return st;
+    if (!a16(T) || !a16(P_out)) return fail(BITLINEAR_ERR_ALIGN, "pack: buffers need 16-byte alignment");
+    if (hipError_t e = bl::launch_pack(T, N, K, P_out, static_cast<hipStream_t>(stream))) return hip_fail(e, "pack");
+    return BITLINEAR_OK;
+}
+
+int bitlinear_unpack(const uint8_t *P, int64_t N, int64_t K, int8_t *T_out, void *stream)
+{
+    if (!P || !T_out) return fail(BITLINEAR_ERR_NULL, "unpack: P and T_out are required");
+    if (int st = check_nk(N, K)) return st;
+    if (!a16(P) || !a16(T_out)) return fail(BITLINEAR_ERR_ALIGN, "unpack: buffers need 16-byte alignment");
+    if (hipError_t e = bl::launch_unpack(P, N, K, T_out, static_cast<hipStream_t>(stream))) return hip_fail(e, "unpack");
+    return BITLINEAR_OK;
+}
+
+int bitlinear_quant_act(const float *X, int64_t M, int64_t K, int8_t *Q_out, int64_t ldq,
+                        float *absmax_out, int32_t *rowsum_out, void *stream)
+{
+    if (!X || !Q_out || !absmax_out) return fail(BITLINEAR_ERR_NULL, "quant_act: X, Q_out and absmax_out are required");
+    if (int st = check_mnk(M, 1, K)) return st;
+    if (ldq < K || ldq % 16 != 0) return fail(BITLINEAR_ERR_SHAPE, "quant_act: ldq=%lld must be >= K and a multiple of 16", (long long)ldq);
+    if (!a16(X) || !a16(Q_out) || !a4(absmax_out) || (rowsum_out && !a4(rowsum_out)))
+        return fail(BITLINEAR_ERR_ALIGN, "quant_act: X/Q_out need 16-byte, absmax/rowsum 4-byte alignment");
+    if (hipError_t e = bl::launch_quant_act(X, M, K, Q_out, ldq, absmax_out, rowsum_out, nullptr, 0,
+                                            static_cast<hipStream_t>(stream)))
+        return hip_fail(e, "quant_act");
+    return BITLINEAR_OK;
+}
+
+int bitlinear_matmul(const int8_t *Q, int64_t ldq, const float *absmax, const int32_t *rowsum,
+                     int64_t M, int64_t K, const uint8_t *P, const float *gamma, int64_t N,
+                     float *Y_out, int32_t *acc_out, void *ws, size_t ws_bytes, void *stream)
+{
+    if (!Q || !absmax || !rowsum || !P || !gamma || !Y_out)
+        return fail(BITLINEAR_ERR_NULL, "matmul: Q, absmax, rowsum, P, gamma and Y_out are required");
+    if (int st = check_mnk(M, N, K)) return st;
+    if (ldq < up(K, 64) || ldq % 16 != 0)
+        return fail(BITLINEAR_ERR_SHAPE, "matmul: ldq=%lld must be >= %lld and a multiple of 16", (long long)ldq, (long long)up(K, 64));
+    if (!a16(Q) || !a16(P) || !a16(Y_out) || (acc_out && !a16(acc_out)) || !a4(absmax) || !a4(rowsum) || !a4(gamma))
+        return fail(BITLINEAR_ERR_ALIGN, "matmul: arrays need 16-byte, scalars 4-byte alignment");
+    Problem p = make_problem(M, N, K);
+    decompose(p, (N + 63) / 64);
+    const WsLayout L = ws_layout(p, false);
+    if (L.total > 0 && (!ws || ws_bytes < (size_t)L.total || !a16(ws)))
+        return fail(BITLINEAR_ERR_WORKSPACE, "matmul: needs %lld workspace bytes (16-byte aligned)", (long long)L.total);
+    if (p.kind == 1 && (int64_t)p.mt * p.ntt >= (int64_t(1) << 31))
+        return fail(BITLINEAR_ERR_SHAPE, "matmul: grid too large");
+    p.Q = const_cast<int8_t *>(Q);
+    p.ldq = ldq;
+    p.absmax = const_cast<float *>(absmax);
+    p.rowsum = const_cast<int32_t *>(rowsum);
+    p.P = P;
+    p.gamma = gamma;
+    p.Y = Y_out;
+    p.acc_out = acc_out;
+    char *base = static_cast<char *>(ws);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (p.kind == 0 && p.ks > 1) {
+        p.acc_ws = reinterpret_cast<int32_t *>(base + L.part);
+        p.tickets = reinterpret_cast<uint32_t *>(base + L.tick);
+        if (hipError_t e = bl::launch_zero_words(p.tickets, p.NT, s)) return hip_fail(e, "zero tickets");
+    }
+    if (hipError_t e = launch_contraction(p, s)) return hip_fail(e, "matmul");
+    return BITLINEAR_OK;
+}
+
+int bitlinear_forward(const float *X, int64_t M, int64_t K, const uint8_t *P,
+                      const float *gamma, int64_t N, float *Y_out, int32_t *acc_out,
+                      void *ws, size_t ws_bytes, void *stream)
+{
+    if (!X || !P || !gamma || !Y_out) return fail(BITLINEAR_ERR_NULL, "forward: X, P, gamma and Y_out are required");
+    if (int st = check_mnk(M, N, K)) return st;
+    if (!a16(X) || !a16(P) || !a16(Y_out) || (acc_out && !a16(acc_out)) || !a4(gamma))
+        return fail(BITLINEAR_ERR_ALIGN, "forward: arrays need 16-byte, gamma 4-byte alignment");
+    Problem p = make_problem(M, N, K);
+    decompose(p, (N + 63) / 64);
+    const WsLayout L = ws_layout(p, true);
+    if (!ws || ws_bytes < (size_t)L.total || !a16(ws))
+        return fail(BITLINEAR_ERR_WORKSPACE, "forward: needs %lld workspace bytes (16-byte aligned)", (long long)L.total);
+    if (p.kind == 1 && (int64_t)p.mt * p.ntt >= (int64_t(1) << 31))
+        return fail(BITLINEAR_ERR_SHAPE, "forward: grid too large");
+    char *base = static_cast<char *>(ws);
+    p.X = X;
+    p.P = P;
+    p.gamma = gamma;
+    p.Y = Y_out;
+    p.acc_out = acc_out;
+    p.ldq = 64 * (int64_t)p.KU;
+    p.Q = reinterpret_cast<int8_t *>(base + L.q);
+    p.absmax = reinterpret_cast<float *>(base + L.absmax);
+    p.rowsum = reinterpret_cast<int32_t *>(base + L.rowsum);
+    if (p.kind == 0 && p.ks > 1) {
+        p.acc_ws = reinterpret_cast<int32_t *>(base + L.part);
+        p.tickets = reinterpret_cast<uint32_t *>(base + L.tick);
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (hipError_t e = bl::launch_quant_act(X, M, K, p.Q, p.ldq, p.absmax, p.rowsum, p.tickets,
+                                            p.tickets ? p.NT : 0, s))
+        return hip_fail(e, "forward: quant_act");
+    if (hipError_t e = launch_contraction(p, s)) return hip_fail(e, "forward: matmul");
+    return BITLINEAR_OK;
+}
+
+}  // extern "C"
+
+// --------------------------------------------------------------------------
+// Grouped forward: plan table construction.
+// --------------------------------------------------------------------------
+namespace {
+
+struct GroupPlan {
+    std::vector<Problem> probs;
+    bl::GroupHeader h;
+};
+
+// Validates the problems and computes the whole plan.  With ws == nullptr
+// the problems' workspace pointers are left null (sizing only).
+int build_group(const bitlinear_problem *in, int count, char *ws, GroupPlan &out)
+{
+    if (!in) return fail(BITLINEAR_ERR_NULL, "group: problem array is NULL");
+    if (count < 1 || count > (1 << 20)) return fail(BITLINEAR_ERR_SHAPE, "group: count=%d out of range", count);
+    memset(&out.h, 0, sizeof out.h);
+    out.probs.assign(count, make_problem(1, 1, 1));
+    int64_t base_items = 0;
+    for (int i = 0; i < count; ++i) {
+        const bitlinear_problem &q = in[i];
+        if (!q.X || !q.P || !q.gamma || !q.Y) return fail(BITLINEAR_ERR_NULL, "group: problem %d lacks X, P, gamma or Y", i);
+        if (int st = check_mnk(q.M, q.N, q.K)) return st;
+        if (!a16(q.X) || !a16(q.P) || !a16(q.Y) || (q.acc && !a16(q.acc)) || !a4(q.gamma))
+            return fail(BITLINEAR_ERR_ALIGN, "group: problem %d buffers misaligned", i);
+        if (q.M <= kStreamMaxM) base_items += (q.N + 63) / 64;
+    }
+    if (base_items < 1) base_items = 1;
+    int64_t tokens = 0, items_s = 0, items_t = 0, off = 0;
+    bool all_m1 = true, any_big = false;
+    for (int i = 0; i < count; ++i) {
+        const bitlinear_problem &q = in[i];
+        Problem &p = out.probs[i];
+        p = make_problem(q.M, q.N, q.K);
+        decompose(p, base_items);
+        p.X = q.X;
+        p.P = q.P;
+        p.gamma = q.gamma;
+        p.Y = q.Y;
+        p.acc_out = q.acc;
+        p.ldq = 64 * (int64_t)p.KU;
+        const WsLayout L = ws_layout(p, true);
+        if (ws) {
+            char *b = ws + off;
+            p.Q = reinterpret_cast<int8_t *>(b + L.q);
+            p.absmax = reinterpret_cast<float *>(b + L.absmax);
+            p.rowsum = reinterpret_cast<int32_t *>(b + L.rowsum);
+            if (p.kind == 0 && p.ks > 1) {
+                p.acc_ws = reinterpret_cast<int32_t *>(b + L.part);
+                p.tickets = reinterpret_cast<uint32_t *>(b + L.tick);
+            }
+        }
+        off += L.total;
+        p.tok_begin = (int32_t)tokens;
+        tokens += p.M;
+        if (p.kind == 0) {
+            p.item_begin = (int32_t)items_s;
+            items_s += items_of(p);
+            all_m1 = all_m1 && p.M <= knobs().dot4_max_m;
+        } else {
+            p.item_begin = (int32_t)items_t;
+            items_t += items_of(p);
+            any_big = any_big || p.M > 64;
+        }
+        if (tokens >= (int64_t(1) << 31) || items_s >= (int64_t(1) << 31) || items_t >= (int64_t(1) << 31))
+            return fail(BITLINEAR_ERR_SHAPE, "group: too many tokens or work items");
+    }
+    // a mixed launch takes one instantiation per kernel: tile kernel with
+    // 128-token tiles if any problem needs them, streaming kernel with MFMA
+    // unless every streaming problem has a single token
+    for (Problem &p : out.probs)
+        if (p.kind == 1 && any_big && p.mtile != 128) {
+            p.mtile = 128;
+            p.mt = (p.M + 127) / 128;
+        }
+    items_t = 0;
+    for (Problem &p : out.probs)
+        if (p.kind == 1) {
+            p.item_begin = (int32_t)items_t;
+            items_t += items_of(p);
+        }
+    bl::GroupHeader &h = out.h;
+    h.magic = bl::kGroupMagic;
+    h.count = count;
+    h.n_tokens = (int32_t)tokens;
+    h.n_items_stream = (int32_t)items_s;
+    h.n_items_tile = (int32_t)items_t;
+    h.stream_variant = all_m1 ? 0 : 1;
+    h.tile_variant = any_big ? 1 : 0;
+    h.ws_bytes = off;
+    int64_t t = up(sizeof(bl::GroupHeader), 16);
+    h.off_probs = t;
+    t = up(t + (int64_t)count * sizeof(Problem), 16);
+    h.off_tok_map = t;
+    t = up(t + 4 * tokens, 16);
+    h.off_stream_map = t;
+    t = up(t + 4 * items_s, 16);
+    h.off_tile_map = t;
+    t = up(t + 4 * items_t, 16);
+    h.total_bytes = t;
+    return BITLINEAR_OK;
+}
+
+int read_header(const void *table_host, const void *table_dev, bl::GroupHeader &h)
+{
+    if (!table_host || !table_dev) return fail(BITLINEAR_ERR_NULL, "group: table pointers are required");
+    if (!a16(table_dev) || !a16(table_host)) return fail(BITLINEAR_ERR_ALIGN, "group: tables need 16-byte alignment");
+    memcpy(&h, table_host, sizeof h);
+    if (h.magic != bl::kGroupMagic || h.count < 1) return fail(BITLINEAR_ERR_ARG, "group: not a plan table");
+    return BITLINEAR_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t bitlinear_group_table_bytes(const bitlinear_problem *probs, int count)
+{
+    GroupPlan g;
+    if (build_group(probs, count, nullptr, g) != BITLINEAR_OK) return 0;
+    return (size_t)g.h.total_bytes;
+}
+
+size_t bitlinear_group_workspace_bytes(const bitlinear_problem *probs, int count)
+{
+    GroupPlan g;
+    if (build_group(probs, count, nullptr, g) != BITLINEAR_OK) return SIZE_MAX;
+    return (size_t)g.h.ws_bytes;
+}
+
+int bitlinear_group_plan(const bitlinear_problem *probs, int count, void *ws, size_t ws_bytes,
+                         void *table_host, size_t table_bytes)
+{
+    if (!table_host) return fail(BITLINEAR_ERR_NULL, "group_plan: table_host is required");
+    if (!a16(table_host)) return fail(BITLINEAR_ERR_ALIGN, "group_plan: table_host needs 16-byte alignment");
+    GroupPlan g;
+    if (int st = build_group(probs, count, nullptr, g)) return st;
+    if (g.h.ws_bytes > 0 && (!ws || ws_bytes < (size_t)g.h.ws_bytes || !a16(ws)))
+        return fail(BITLINEAR_ERR_WORKSPACE, "group_plan: needs %lld workspace bytes (16-byte aligned)", (long long)g.h.ws_bytes);
+    if (table_bytes < (size_t)g.h.total_bytes)
+        return fail(BITLINEAR_ERR_ARG, "group_plan: table needs %lld bytes", (long long)g.h.total_bytes);
+    if (int st = build_group(probs, count, static_cast<char *>(ws), g)) return st;
+    char *t = static_cast<char *>(table_host);
+    memset(t, 0, (size_t)g.h.total_bytes);
+    memcpy(t, &g.h, sizeof g.h);
+    memcpy(t + g.h.off_probs, g.probs.data(), g.probs.size() * sizeof(Problem));
+    uint32_t *tok = reinterpret_cast<uint32_t *>(t + g.h.off_tok_map);
+    uint32_t *sm = reinterpret_cast<uint32_t *>(t + g.h.off_stream_map);
+    uint32_t *tm = reinterpret_cast<uint32_t *>(t + g.h.off_tile_map);
+    for (int i = 0; i < count; ++i) {
+        const Problem &p = g.probs[i];
+        for (int m = 0; m < p.M; ++m) tok[p.tok_begin + m] = (uint32_t)i;
+        const int64_t n = items_of(p);
+        uint32_t *map = p.kind == 0 ? sm : tm;
+        for (int64_t j = 0; j < n; ++j) map[p.item_begin + j] = (uint32_t)i;
+    }
+    return BITLINEAR_OK;
+}
+
+int bitlinear_group_quant_act(const void *table_host, const void *table_dev, void *stream)
+{
+    bl::GroupHeader h;
+    if (int st = read_header(table_host, table_dev, h)) return st;
+    const char *d = static_cast<const char *>(table_dev);
+    if (hipError_t e = bl::launch_quant_act_group(reinterpret_cast<const Problem *>(d + h.off_probs),
+                                                  reinterpret_cast<const uint32_t *>(d + h.off_tok_map),
+                                                  h.n_tokens, static_cast<hipStream_t>(stream)))
+        return hip_fail(e, "group quant_act");
+    return BITLINEAR_OK;
+}
+
+int bitlinear_group_matmul(const void *table_host, const void *table_dev, void *stream)
+{
+    bl::GroupHeader h;
+    if (int st = read_header(table_host, table_dev, h)) return st;
+    const char *d = static_cast<const char *>(table_dev);
+    const Problem *probs = reinterpret_cast<const Problem *>(d + h.off_probs);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (h.n_items_stream > 0)
+        if (hipError_t e = bl::launch_stream_group(probs, reinterpret_cast<const uint32_t *>(d + h.off_stream_map),
+                                                   h.n_items_stream, h.stream_variant, s))
+            return hip_fail(e, "group stream kernel");
+    if (h.n_items_tile > 0)
+        if (hipError_t e = bl::launch_tile_group(probs, reinterpret_cast<const uint32_t *>(d + h.off_tile_map),
+                                                 h.n_items_tile, h.tile_variant, s))
+            return hip_fail(e, "group tile kernel");
+    return BITLINEAR_OK;
+}
+
+int bitlinear_group_forward(const void *table_host, const void *table_dev, void *stream)
+{
+    if (int st = bitlinear_group_quant_act(table_host, table_dev, stream)) return st;
+    return bitlinear_group_matmul(table_host, table_dev, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,89 @@
+// Shared definitions of the BitLinear HIP library (device and host side).
+// Everything here is private to the library; the public contract is
+// include/bitlinear.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bl {
+
+// BL2-T64 geometry: 64-row tiles, 64-code units, 1 KiB blocks.
+constexpr int kTileRows = 64;
+constexpr int kUnitCodes = 64;
+constexpr int kBlockBytes = 1024;
+
+// Everything the contraction kernels need to know about one BitLinear
+// problem.  Single calls pass one of these by value; the grouped path keeps
+// an array of them in device memory (the plan table).
+struct Problem {
+    const float *X;        // fp32 activations, M x K (quantization input)
+    const uint8_t *P;      // BL2-T64 packed weights
+    const float *gamma;    // device scalar
+    float *Y;              // M x N fp32 output
+    int32_t *acc_out;      // optional M x N int32 accumulators
+    int8_t *Q;             // int8 activations, M rows of ldq bytes
+    float *absmax;         // [M]
+    int32_t *rowsum;       // [M]
+    int32_t *acc_ws;       // split-K partial sums, M x (NT*64), or null
+    uint32_t *tickets;     // split-K arrival counters, [NT], or null
+    int64_t ldq;           // row stride of Q in bytes (>= 64*KU, % 16 == 0)
+    int32_t M, N, K;
+    int32_t KU;            // ceil(K/64)
+    int32_t NT;            // ceil(N/64)
+    int32_t ks;            // K splits of the streaming kernel (1 = none)
+    int32_t upsplit;       // units per split (last split may be shorter)
+    int32_t kind;          // 0 = streaming kernel (small M), 1 = tile kernel
+    int32_t mtile;         // rows of M per tile-kernel work item
+    int32_t ntile;         // rows of N per tile-kernel work item
+    int32_t mt;            // M tiles of the tile kernel
+    int32_t ntt;           // N tiles of the tile kernel
+    int32_t tok_begin;     // first row of this problem in the grouped quant grid
+    int32_t item_begin;    // first work item of this problem in its kernel's grid
+};
+static_assert(sizeof(Problem) == 144, "Problem layout is shared by host and device");
+
+// Plan table header (first bytes of the grouped-forward table).
+struct GroupHeader {
+    uint32_t magic;
+    int32_t count;          // problems
+    int32_t n_tokens;       // total rows over all problems (quant grid)
+    int32_t n_items_stream; // work items of the streaming kernel
+    int32_t n_items_tile;   // work items of the tile kernel
+    int32_t n_zero;         // problems whose split-K scratch must be zeroed
+    int32_t dot4_items;     // unused by the kernels (diagnostics)
+    int32_t stream_variant; // streaming kernel instantiation (see api.hip)
+    int32_t tile_variant;   // tile kernel instantiation
+    int32_t pad_[3];
+    int64_t ws_bytes;       // workspace the plan was built for
+    int64_t off_probs;      // byte offsets inside the table
+    int64_t off_tok_map;    // uint32 per token:  problem index
+    int64_t off_stream_map; // uint32 per item:   problem index
+    int64_t off_tile_map;   // uint32 per item:   problem index
+    int64_t total_bytes;
+};
+constexpr uint32_t kGroupMagic = 0xB17E0001u;
+
+// Kernel launchers (each defined next to its kernels).
+hipError_t launch_absmean_partial(const float *W, int64_t count, double *partial, int nblocks,
+                                  hipStream_t s);
+hipError_t launch_absmean_final(const double *partial, int nblocks, int64_t count,
+                                const float *gamma_in, float *gamma_out, hipStream_t s);
+hipError_t launch_ternarize(const float *W, int64_t count, const float *gamma, int8_t *T,
+                            hipStream_t s);
+hipError_t launch_pack(const int8_t *T, int64_t N, int64_t K, uint8_t *P, hipStream_t s);
+hipError_t launch_unpack(const uint8_t *P, int64_t N, int64_t K, int8_t *T, hipStream_t s);
+hipError_t launch_quant_act(const float *X, int64_t M, int64_t K, int8_t *Q, int64_t ldq,
+                            float *absmax, int32_t *rowsum, uint32_t *zero_ptr, int zero_n,
+                            hipStream_t s);
+hipError_t launch_quant_act_group(const Problem *probs, const uint32_t *tok_map, int n_tokens,
+                                  hipStream_t s);
+hipError_t launch_zero_words(uint32_t *p, int64_t n, hipStream_t s);
+hipError_t launch_stream_single(const Problem &p, int variant, hipStream_t s);
+hipError_t launch_stream_group(const Problem *probs, const uint32_t *item_map, int n_items,
+                               int variant, hipStream_t s);
+hipError_t launch_tile_single(const Problem &p, int variant, hipStream_t s);
+hipError_t launch_tile_group(const Problem *probs, const uint32_t *item_map, int n_items,
+                             int variant, hipStream_t s);
+
+}  // namespace bl

@@ -1,0 +1,256 @@
+// Streaming contraction for small token counts (decode): M = 1 with packed
+// int8 dot products, 2 <= M <= 32 with int8 matrix instructions.
+//
+// The pages describe the decode kernel as: weights packed four codes per
+// byte are streamed across the GPU and unpacked next to the math units,
+// then multiplied with 8-bit activations (BitNet b1.58 2B4T video
+// transcript, yousumm.com, "Transcription"); the product needs only
+// integer additions (anthology note-168 on arXiv 2402.17764, "The part that
+// is a bet rather than a measurement").  On gfx950 this regime is bound by
+// HBM: every packed byte is read once and carries 4 codes, so the kernel is
+// built to keep many 16-byte non-temporal loads in flight and to spend as
+// few VALU operations per code as possible.
+//
+// Work item = (problem, 64-row weight tile, K split).  A 256-thread
+// workgroup owns one item; its four waves take every fourth 64-code unit of
+// the split, so together they stream 4 KiB of contiguous packed weights per
+// step.  Each lane loads one 16-byte slot of the unit's 1 KiB block: words
+// (s, h) hold 16 codes of rows r and 32 + r (r = lane % 32) for code chunk
+// lane / 32 of half h.
+//
+// M = 1 (dot4):   plane j of a word times the matching 4 activation bytes
+//                 with v_dot4c_i32_i8: per 16 codes 7 bit operations + 4
+//                 dot products.  The (t+1) fields make the sum exceed the
+//                 ternary dot product by the activation row sum, which the
+//                 epilogue subtracts once.
+// M <= 32 (mfma): the four planes of a word are exactly one lane's B operand
+//                 of v_mfma_i32_32x32x32_i8 (A = 32 token rows of int8
+//                 activations, zero beyond M), so per 1 KiB unit a wave
+//                 issues 4 MFMAs after 28 bit operations, whatever M is.
+//
+// Partial sums of the four waves meet in LDS; with K split over several
+// workgroups the last one to arrive (atomic ticket) adds the splits.
+// Integer addition is associative, so every order gives the same bits.
+#include "mm_common.hpp"
+
+namespace bl {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = 4;
+
+__device__ inline int dot16(unsigned w, v4i q, int acc)
+{
+    acc = __builtin_amdgcn_sdot4((int)(w & 0x03030303u), q.x, acc, false);
+    acc = __builtin_amdgcn_sdot4((int)((w >> 2) & 0x03030303u), q.y, acc, false);
+    acc = __builtin_amdgcn_sdot4((int)((w >> 4) & 0x03030303u), q.z, acc, false);
+    acc = __builtin_amdgcn_sdot4((int)((w >> 6) & 0x03030303u), q.w, acc, false);
+    return acc;
+}
+
+template <int UNROLL>
+__device__ void stream_dot4(const Problem &p, int local)
+{
+    __shared__ int red[kWaves][64];
+    const int tile = local / p.ks, split = local - tile * p.ks;
+    const int u0 = split * p.upsplit;
+    const int u1 = min(p.KU, u0 + p.upsplit);
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 5;
+    const v4u *blk = reinterpret_cast<const v4u *>(p.P + (int64_t)tile * p.KU * kBlockBytes) + lane;
+    const int8_t *q = p.Q + 16 * g;  // token 0; chunk g of each 32-code half
+
+    int acc0 = 0, acc1 = 0;  // rows r and 32 + r of the tile
+    int u = u0 + wave;
+    for (; u + kWaves * (UNROLL - 1) < u1; u += kWaves * UNROLL) {
+        v4u w[UNROLL];
+        v4i qa[UNROLL], qb[UNROLL];
+#pragma unroll
+        for (int j = 0; j < UNROLL; ++j) w[j] = load_packed(blk + (int64_t)(u + kWaves * j) * 64);
+#pragma unroll
+        for (int j = 0; j < UNROLL; ++j) {
+            const int8_t *qu = q + 64 * (u + kWaves * j);
+            qa[j] = *reinterpret_cast<const v4i *>(qu);
+            qb[j] = *reinterpret_cast<const v4i *>(qu + 32);
+        }
+#pragma unroll
+        for (int j = 0; j < UNROLL; ++j) {
+            acc0 = dot16(w[j].x, qa[j], acc0);
+            acc0 = dot16(w[j].y, qb[j], acc0);
+            acc1 = dot16(w[j].z, qa[j], acc1);
+            acc1 = dot16(w[j].w, qb[j], acc1);
+        }
+    }
+    for (; u < u1; u += kWaves) {
+        const v4u w = load_packed(blk + (int64_t)u * 64);
+        const int8_t *qu = q + 64 * u;
+        const v4i qa = *reinterpret_cast<const v4i *>(qu);
+        const v4i qb = *reinterpret_cast<const v4i *>(qu + 32);
+        acc0 = dot16(w.x, qa, acc0);
+        acc0 = dot16(w.y, qb, acc0);
+        acc1 = dot16(w.z, qa, acc1);
+        acc1 = dot16(w.w, qb, acc1);
+    }
+    // lanes r and r + 32 hold the two code chunks of the same rows
+    acc0 += __shfl_xor(acc0, 32, 64);
+    acc1 += __shfl_xor(acc1, 32, 64);
+    if (lane < 32) {
+        red[wave][lane] = acc0;
+        red[wave][32 + lane] = acc1;
+    }
+    __syncthreads();
+
+    const int t = threadIdx.x;
+    const int n = 64 * tile + t;
+    const float gamma = *p.gamma;
+    int total = 0;
+    if (t < 64) total = red[0][t] + red[1][t] + red[2][t] + red[3][t];
+    if (p.ks == 1) {
+        if (t < 64 && n < p.N) finish_output(p, gamma, 0, n, total);
+        return;
+    }
+    const int64_t ldp = (int64_t)p.NT * 64;  // partial row stride
+    if (t < 64) p.acc_ws[(int64_t)split * p.M * ldp + n] = total;
+    if (!arrive_last(p, tile)) return;
+    if (t < 64 && n < p.N) {
+        int sum = 0;
+        for (int j = 0; j < p.ks; ++j) sum += p.acc_ws[(int64_t)j * p.M * ldp + n];
+        finish_output(p, gamma, 0, n, sum);
+    }
+}
+
+template <int UNROLL>
+__device__ void stream_mfma(const Problem &p, int local)
+{
+    // per wave, per 32-row half s, per accumulator element e, per lane
+    __shared__ int red[kWaves][2][16][64];
+    const int tile = local / p.ks, split = local - tile * p.ks;
+    const int u0 = split * p.upsplit;
+    const int u1 = min(p.KU, u0 + p.upsplit);
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 5, r = lane & 31;
+    const v4u *blk = reinterpret_cast<const v4u *>(p.P + (int64_t)tile * p.KU * kBlockBytes) + lane;
+    const bool rv = r < p.M;
+    const int8_t *qrow = p.Q + (int64_t)(rv ? r : 0) * p.ldq + 16 * g;
+    const v4i zero = {0, 0, 0, 0};
+
+    v16i acc0 = {}, acc1 = {};
+    int u = u0 + wave;
+    for (; u + kWaves * (UNROLL - 1) < u1; u += kWaves * UNROLL) {
+        v4u w[UNROLL];
+        v4i qa[UNROLL], qb[UNROLL];
+#pragma unroll
+        for (int j = 0; j < UNROLL; ++j) w[j] = load_packed(blk + (int64_t)(u + kWaves * j) * 64);
+#pragma unroll
+        for (int j = 0; j < UNROLL; ++j) {
+            const int8_t *qu = qrow + 64 * (u + kWaves * j);
+            qa[j] = rv ? *reinterpret_cast<const v4i *>(qu) : zero;
+            qb[j] = rv ? *reinterpret_cast<const v4i *>(qu + 32) : zero;
+        }
+#pragma unroll
+        for (int j = 0; j < UNROLL; ++j) {
+            acc0 = mfma_i8(qa[j], planes(w[j].x), acc0);
+            acc0 = mfma_i8(qb[j], planes(w[j].y), acc0);
+            acc1 = mfma_i8(qa[j], planes(w[j].z), acc1);
+            acc1 = mfma_i8(qb[j], planes(w[j].w), acc1);
+        }
+    }
+    for (; u < u1; u += kWaves) {
+        const v4u w = load_packed(blk + (int64_t)u * 64);
+        const int8_t *qu = qrow + 64 * u;
+        const v4i qa = rv ? *reinterpret_cast<const v4i *>(qu) : zero;
+        const v4i qb = rv ? *reinterpret_cast<const v4i *>(qu + 32) : zero;
+        acc0 = mfma_i8(qa, planes(w.x), acc0);
+        acc0 = mfma_i8(qb, planes(w.y), acc0);
+        acc1 = mfma_i8(qa, planes(w.z), acc1);
+        acc1 = mfma_i8(qb, planes(w.w), acc1);
+    }
+    // element e of lane l is token 8*(e/4) + 4*(l/32) + e%4, row 32*s + l%32;
+    // only element groups that hold real tokens are exchanged
+    const int eg = (p.M + 7) >> 3;  // 1..4
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+        if ((e >> 2) < eg) {
+            red[wave][0][e][lane] = acc0[e];
+            red[wave][1][e][lane] = acc1[e];
+        }
+    }
+    __syncthreads();
+
+    const float gamma = *p.gamma;
+    const int64_t ldp = (int64_t)p.NT * 64;
+    const int entries = 2 * 4 * eg * 64;
+    int *flat = &red[0][0][0][0];
+    constexpr int kWaveStride = 2 * 16 * 64;
+    for (int idx = threadIdx.x; idx < entries; idx += kThreads) {
+        const int s = idx / (4 * eg * 64);
+        const int e = (idx >> 6) % (4 * eg);
+        const int l = idx & 63;
+        const int m = 8 * (e >> 2) + 4 * (l >> 5) + (e & 3);
+        const int n = 64 * tile + 32 * s + (l & 31);
+        if (m >= p.M || n >= p.N) continue;
+        const int off = (s * 16 + e) * 64 + l;
+        const int total = flat[off] + flat[kWaveStride + off] + flat[2 * kWaveStride + off] +
+                          flat[3 * kWaveStride + off];
+        if (p.ks == 1)
+            finish_output(p, gamma, m, n, total);
+        else
+            p.acc_ws[((int64_t)split * p.M + m) * ldp + n] = total;
+    }
+    if (p.ks == 1) return;
+    if (!arrive_last(p, tile)) return;
+    for (int idx = threadIdx.x; idx < p.M * 64; idx += kThreads) {
+        const int m = idx >> 6;
+        const int n = 64 * tile + (idx & 63);
+        if (n >= p.N) continue;
+        int sum = 0;
+        for (int j = 0; j < p.ks; ++j) sum += p.acc_ws[((int64_t)j * p.M + m) * ldp + n];
+        finish_output(p, gamma, m, n, sum);
+    }
+}
+
+template <int V>
+__device__ inline void stream_body(const Problem &p, int local)
+{
+    if constexpr (V == 0)
+        stream_dot4<4>(p, local);
+    else
+        stream_mfma<2>(p, local);
+}
+
+template <int V>
+__global__ __launch_bounds__(kThreads) void stream_single_kernel(Problem p)
+{
+    stream_body<V>(p, blockIdx.x);
+}
+
+template <int V>
+__global__ __launch_bounds__(kThreads) void stream_group_kernel(const Problem *__restrict__ probs,
+                                                                const uint32_t *__restrict__ item_map)
+{
+    const Problem &p = probs[item_map[blockIdx.x]];
+    stream_body<V>(p, (int)blockIdx.x - p.item_begin);
+}
+
+}  // namespace
+
+hipError_t launch_stream_single(const Problem &p, int variant, hipStream_t s)
+{
+    const dim3 grid((unsigned)(p.NT * p.ks)), block(kThreads);
+    if (variant == 0)
+        hipLaunchKernelGGL(stream_single_kernel<0>, grid, block, 0, s, p);
+    else
+        hipLaunchKernelGGL(stream_single_kernel<1>, grid, block, 0, s, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_stream_group(const Problem *probs, const uint32_t *item_map, int n_items,
+                               int variant, hipStream_t s)
+{
+    const dim3 grid((unsigned)n_items), block(kThreads);
+    if (variant == 0)
+        hipLaunchKernelGGL(stream_group_kernel<0>, grid, block, 0, s, probs, item_map);
+    else
+        hipLaunchKernelGGL(stream_group_kernel<1>, grid, block, 0, s, probs, item_map);
+    return hipGetLastError();
+}
+
+}  // namespace bl

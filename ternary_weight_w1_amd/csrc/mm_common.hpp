@@ -1,0 +1,64 @@
+// Device helpers shared by the two contraction kernels.
+#pragma once
+
+#include "common.hpp"
+
+namespace bl {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+
+// The four 2-bit planes of a packed word as four int8x4 words: plane j holds
+// the (code + 1) fields of codes 4j..4j+3 as bytes.  Together they are the
+// 16 consecutive fields of the word, in code order.
+__device__ inline v4i planes(unsigned w)
+{
+    v4i r;
+    r.x = (int)(w & 0x03030303u);
+    r.y = (int)((w >> 2) & 0x03030303u);
+    r.z = (int)((w >> 4) & 0x03030303u);
+    r.w = (int)((w >> 6) & 0x03030303u);
+    return r;
+}
+
+// Streaming read of one 16-byte slot of the packed weights (read once, so
+// marked non-temporal).
+__device__ inline v4u load_packed(const v4u *p) { return __builtin_nontemporal_load(p); }
+
+__device__ inline v16i mfma_i8(v4i a, v4i b, v16i c)
+{
+    return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
+}
+
+// Rescale epilogue (anthology note-168 on arXiv 2402.17764, "What it does":
+// the layer replaces nn.Linear, so it returns real values).  The kernels
+// accumulate sum_k (t+1) q = acc + rowsum; the exact integer acc is
+// recovered here, then y = float(acc) * ((gamma * a) / 127) in fp32.
+__device__ inline void finish_output(const Problem &p, float gamma, int m, int n, int32_t fields)
+{
+    const int32_t acc = fields - p.rowsum[m];
+    const float c = (gamma * p.absmax[m]) / 127.0f;
+    const int64_t o = (int64_t)m * p.N + n;
+    p.Y[o] = (float)acc * c;
+    if (p.acc_out) p.acc_out[o] = acc;
+}
+
+// Split-K arrival: every workgroup of a 64-row tile publishes its partial
+// sums, then takes a ticket; the one that takes the last ticket sums the
+// partials.  The fences order the partial stores before the ticket and the
+// ticket before the reads of the other workgroups' partials.
+__device__ inline bool arrive_last(const Problem &p, int tile)
+{
+    __shared__ int s_last;
+    __threadfence();
+    __syncthreads();
+    if (threadIdx.x == 0)
+        s_last = (atomicAdd(&p.tickets[tile], 1u) == (unsigned)(p.ks - 1)) ? 1 : 0;
+    __syncthreads();
+    const bool last = s_last != 0;
+    if (last) __threadfence();
+    return last;
+}
+
+}  // namespace bl

@@ -1,0 +1,361 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Bar: bit-exact ternary codes, packed bytes, int8 codes, absmax, row sums and
+int32 accumulators given identical scales; fp32 outputs within 1e-5
+relative of the fp64 rescale of the same accumulators (and, since both sides
+run the same IEEE fp32 operations, equal to the oracle's fp32 outputs);
+the absmean scale within 1e-6 relative of the oracle's.
+
+Every expected value comes from the oracle on the same seeded inputs; no
+input of the oracle comes from the HIP path.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synth
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print("[case]", *a, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module")
+def B():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import ternary_weight_w1_amd as B
+    B.lib()
+    return B
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def gamma_dev(g):
+    return dev(np.array([g], np.float32))
+
+
+def check_outputs(Y, acc, ref_acc, gamma, absmax, what=""):
+    np.testing.assert_array_equal(acc, ref_acc, err_msg=f"acc {what}")
+    y64 = O.epilogue_f64(ref_acc, gamma, absmax)
+    y = Y.astype(np.float64)
+    nz = y64 != 0
+    rel = np.abs(y[nz] - y64[nz]) / np.abs(y64[nz])
+    assert rel.size == 0 or rel.max() <= 1e-5, f"Y rel err {rel.max()} {what}"
+    assert np.all(Y[~nz] == 0), what
+    np.testing.assert_array_equal(Y, O.epilogue(ref_acc, gamma, absmax), err_msg=f"Y {what}")
+
+
+# --------------------------------------------------------------- config 1 --
+
+def test_config1_end_to_end(B):
+    say("config1 K=N=256 M=4")
+    W, X = synth.config1()
+    T, g = O.quantize_weights(W)
+    P = O.pack(T)
+    ref = O.forward(X, T, g)
+
+    Tg, gg = B.quantize_weights(dev(W))
+    gg = float(host(gg)[0])
+    assert abs(gg - g) / g <= 1e-6
+    T2, g2 = B.quantize_weights(dev(W), gamma_in=gamma_dev(g))
+    assert float(host(g2)[0]) == g
+    np.testing.assert_array_equal(host(T2), T)
+    Pg = B.pack(T2)
+    np.testing.assert_array_equal(host(Pg), P)
+
+    Q, a, rs = B.quant_act(dev(X))
+    Q = host(Q)
+    np.testing.assert_array_equal(Q[:, :256], ref["Q"])
+    np.testing.assert_array_equal(host(a), ref["absmax"])
+    np.testing.assert_array_equal(host(rs), ref["rowsum"])
+
+    Y, acc = B.forward(dev(X), Pg, gamma_dev(g), 256, with_acc=True)
+    check_outputs(host(Y), host(acc), ref["acc"], g, ref["absmax"], "config1")
+
+
+# ---------------------------------------------------- activation quantizer --
+
+@pytest.mark.parametrize("M,K,outliers", [(1, 1, 0), (1, 5, 0), (3, 64, 0), (4, 100, 0),
+                                          (7, 256, 0.01), (2, 2560, 0.01), (5, 6912, 0.01),
+                                          (1, 28672, 0), (33, 130, 0), (512, 2560, 0.01)])
+def test_quant_act_parity(B, M, K, outliers):
+    say("quant_act", M, K, outliers)
+    X = synth.activations_np(M, K, seed=M * 31 + K, outlier_frac=outliers)
+    if M > 2:
+        X[1] = 0.0                      # an all-zero token
+        X[2, : min(K, 8)] = [127, 63.5, -0.5, 1.5, 2.5, -2.5, 0.49, -127][: min(K, 8)]
+    Q, a, rs = O.quant_act(X)
+    for ldq in (B.q_stride(K), B.q_stride(K) + 64):
+        Qg, ag, rsg = B.quant_act(dev(X), ldq=ldq)
+        Qg = host(Qg)
+        np.testing.assert_array_equal(Qg[:, :K], Q)
+        assert not Qg[:, K:].any()
+        np.testing.assert_array_equal(host(ag), a)
+        np.testing.assert_array_equal(host(rsg), rs)
+
+
+def test_quant_act_unaligned_stride_rows(B):
+    # K not a multiple of 4 takes the scalar path; ldq = K rounded to 16
+    say("quant_act scalar path")
+    X = synth.activations_np(6, 37, seed=9)
+    Q, a, rs = O.quant_act(X)
+    Qg, ag, rsg = B.quant_act(dev(X), ldq=48)
+    np.testing.assert_array_equal(host(Qg)[:, :37], Q)
+    np.testing.assert_array_equal(host(ag), a)
+    np.testing.assert_array_equal(host(rsg), rs)
+
+
+# -------------------------------------------------------- weight quantizer --
+
+@pytest.mark.parametrize("N,K,sigma", [(1, 1, 0.02), (3, 17, 0.02), (64, 64, 0.02),
+                                       (130, 200, 1.0), (640, 2560, 0.02), (2560, 6912, 0.02)])
+def test_weight_quant_parity(B, N, K, sigma):
+    say("quantize_weights", N, K)
+    W = synth.weights_np(N, K, sigma, seed=N + K)
+    T, g = O.quantize_weights(W)
+    Tg, gg = B.quantize_weights(dev(W))
+    gg = float(host(gg)[0])
+    assert abs(gg - g) / g <= 1e-6
+    # codes from the GPU's own scale match the oracle's codes for that scale
+    np.testing.assert_array_equal(host(Tg), O.ternarize(W, gg))
+    # and with the oracle's scale injected they match the oracle exactly
+    T2, _ = B.quantize_weights(dev(W), gamma_in=gamma_dev(g))
+    np.testing.assert_array_equal(host(T2), T)
+
+
+def test_weight_quant_ties_and_zero(B):
+    say("quantize_weights ties")
+    rows = [ln.split() for ln in open("tests/golden/quant_fixtures.txt") if ln.startswith("weights")]
+    d = {r[1]: r[2:] for r in rows}
+    W = np.array([float(v) for v in d["W"]], np.float32).reshape(4, 4)
+    Tg, gg = B.quantize_weights(dev(W))
+    assert float(host(gg)[0]) == float(d["gamma"][0])
+    np.testing.assert_array_equal(host(Tg).ravel(), np.array([int(v) for v in d["T"]], np.int8))
+    Tz, gz = B.quantize_weights(dev(np.zeros((5, 70), np.float32)))
+    assert float(host(gz)[0]) == np.float32(1e-5)
+    assert not host(Tz).any()
+
+
+# ------------------------------------------------------------------ packing --
+
+@pytest.mark.parametrize("N,K", [(1, 1), (3, 17), (64, 64), (65, 129), (130, 200), (200, 640),
+                                 (640, 2560), (64, 131072)])
+def test_pack_parity(B, N, K):
+    say("pack", N, K)
+    T = synth.random_ternary(N, K, seed=N * 7 + K)
+    P = O.pack(T)
+    Pg = B.pack(dev(T))
+    np.testing.assert_array_equal(host(Pg), P)
+    np.testing.assert_array_equal(host(B.unpack(Pg, N, K)), T)
+
+
+def test_pack_golden_single_codes(B):
+    say("pack golden")
+    for ln in open("tests/golden/bl2_t64_fixtures.txt"):
+        if not ln.startswith("single"):
+            continue
+        _, N, K, n, k, code, idx, val = ln.split()
+        N, K, n, k, code, idx = map(int, (N, K, n, k, code, idx))
+        T = np.zeros((N, K), np.int8)
+        T[n, k] = code
+        P = host(B.pack(dev(T)))
+        want = np.full(P.size, 0x55, np.uint8)
+        want[idx] = int(val, 16)
+        np.testing.assert_array_equal(P, want)
+
+
+# ---------------------------------------------------------- contraction ------
+
+MM_CASES = [
+    # (M, N, K): dot4 (M=1), streaming MFMA (2..32), tile MFMA (33..64 -> 64-token
+    # tiles, > 64 -> 128-token tiles); ragged N and K tails throughout
+    (1, 64, 64), (1, 100, 200), (1, 257, 640), (1, 640, 2560),
+    (2, 64, 64), (3, 100, 200), (8, 257, 640), (17, 640, 2560), (32, 130, 1000),
+    (33, 64, 64), (40, 100, 200), (64, 257, 640), (65, 130, 1000), (128, 640, 2560),
+    (176, 300, 700), (200, 513, 129), (512, 256, 256),
+]
+
+
+@pytest.mark.parametrize("M,N,K", MM_CASES)
+def test_matmul_parity_injected_scales(B, M, N, K):
+    say("matmul", M, N, K)
+    T = synth.random_ternary(N, K, seed=M + 3 * N + 7 * K)
+    X = synth.activations_np(M, K, seed=M * 13 + K, outlier_frac=0.01)
+    Q, a, rs = O.quant_act(X)
+    g = 0.0123
+    ref = O.matmul(Q, T)
+    ldq = B.q_stride(K)
+    Qp = np.zeros((M, ldq), np.int8)
+    Qp[:, :K] = Q
+    Y, acc = B.matmul(dev(Qp), dev(a), dev(rs), dev(O.pack(T)), gamma_dev(g), N, K, with_acc=True)
+    check_outputs(host(Y), host(acc), ref, g, a, f"M={M} N={N} K={K}")
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 64, 8192), (5, 64, 8192), (1, 200, 4000), (3, 130, 131072)])
+def test_matmul_split_k(B, M, N, K):
+    # few row tiles and a long K: the streaming kernel splits K over
+    # workgroups and the last one to arrive adds the partial sums
+    say("matmul split-K", M, N, K)
+    assert B.workspace_bytes(B.WS_MATMUL, M, N, K) > 0
+    T = synth.random_ternary(N, K, seed=K)
+    Q = synth.random_int8(M, K, seed=M + K)
+    a = np.full(M, 3.0, np.float32)
+    rs = Q.astype(np.int32).sum(1).astype(np.int32)
+    ldq = B.q_stride(K)
+    Qp = np.zeros((M, ldq), np.int8)
+    Qp[:, :K] = Q
+    Qd, Pd = dev(Qp), dev(O.pack(T))
+    ref = O.matmul(Q, T)
+    for _ in range(2):  # twice: the arrival counters must be reset between calls
+        Y, acc = B.matmul(Qd, dev(a), dev(rs), Pd, gamma_dev(0.5), N, K, with_acc=True)
+        check_outputs(host(Y), host(acc), ref, 0.5, a, "split-K")
+
+
+def test_extreme_values_exact(B):
+    # |acc| = 127*K: every code +1 against every activation 127, and the
+    # mirrored case; exercises the int32 path at its bound for this K
+    say("extremes")
+    M, N, K = 3, 64, 4096
+    T = np.ones((N, K), np.int8)
+    T[1::2] = -1
+    X = np.full((M, K), 2.0, np.float32)
+    X[1] = -2.0
+    X[2, ::2] = 0.0
+    Q, a, rs = O.quant_act(X)
+    ref = O.matmul(Q, T)
+    assert abs(ref).max() == 127 * K
+    Y, acc = B.forward(dev(X), dev(O.pack(T)), gamma_dev(1.0), N, with_acc=True)
+    check_outputs(host(Y), host(acc), ref, 1.0, a, "extremes")
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 640, 2560), (4, 100, 200), (16, 257, 640), (96, 300, 700)])
+def test_forward_parity_and_determinism(B, M, N, K):
+    say("forward", M, N, K)
+    W = synth.weights_np(N, K, 0.02, seed=M + N + K)
+    X = synth.activations_np(M, K, seed=M + 2 * N + K, outlier_frac=0.01)
+    T, g = O.quantize_weights(W)
+    ref = O.forward(X, T, g)
+    Xd, Pd, gd = dev(X), dev(O.pack(T)), gamma_dev(g)
+    Y1, acc1 = B.forward(Xd, Pd, gd, N, with_acc=True)
+    check_outputs(host(Y1), host(acc1), ref["acc"], g, ref["absmax"], "forward")
+    Y2, acc2 = B.forward(Xd, Pd, gd, N, with_acc=True)
+    assert torch.equal(Y1, Y2) and torch.equal(acc1, acc2)
+
+
+def test_forward_rejects_small_workspace(B):
+    Xd = dev(np.zeros((2, 64), np.float32))
+    Pd = dev(np.full(B.packed_bytes(64, 64), 0x55, np.uint8))
+    with pytest.raises(RuntimeError, match="workspace"):
+        B.forward(Xd, Pd, gamma_dev(1.0), 64, ws=torch.empty(16, dtype=torch.uint8, device="cuda"))
+
+
+# ------------------------------------------------------------------ groups ---
+
+def _group_run(B, specs, seed0):
+    probs, refs = [], []
+    for i, (M, N, K) in enumerate(specs):
+        T = synth.random_ternary(N, K, seed=seed0 + i)
+        X = synth.activations_np(M, K, seed=seed0 + 100 + i, outlier_frac=0.01)
+        g = 0.01 * (i + 1)
+        refs.append((O.forward(X, T, np.float32(g)), np.float32(g)))
+        probs.append(dict(X=dev(X), P=dev(O.pack(T)), gamma=gamma_dev(g),
+                          Y=torch.empty((M, N), dtype=torch.float32, device="cuda"),
+                          acc=torch.empty((M, N), dtype=torch.int32, device="cuda"), N=N))
+    plan = B.GroupPlan(probs)
+    plan.forward()
+    first = [(host(p["Y"]).copy(), host(p["acc"]).copy()) for p in probs]
+    for (Y, acc), (ref, g) in zip(first, refs):
+        check_outputs(Y, acc, ref["acc"], float(g), ref["absmax"], "group")
+    plan.quant_act()
+    plan.matmul()
+    for p, (Y, acc) in zip(probs, first):
+        np.testing.assert_array_equal(host(p["Y"]), Y)
+        np.testing.assert_array_equal(host(p["acc"]), acc)
+
+
+def test_group_all_single_token(B):
+    say("group M=1")
+    _group_run(B, [(1, 640, 2560), (1, 100, 200), (1, 2560, 640), (1, 64, 64)], 500)
+
+
+def test_group_mixed(B):
+    say("group mixed")
+    _group_run(B, [(1, 640, 2560), (4, 100, 200), (40, 257, 640), (130, 300, 700), (17, 64, 64)], 600)
+
+
+# ------------------------------------------------- full model shapes, sampled --
+
+_WEIGHTS = {}
+
+
+def _layer_weights(B, name, N, K, sigma, seed):
+    """Oracle codes/scale/packing of one seeded matrix, and the GPU's packing
+    of the same codes (checked bit-exact); cached across token counts."""
+    key = (name, N, K, sigma, seed)
+    if key not in _WEIGHTS:
+        W = synth.weights_np(N, K, sigma, seed=seed)
+        T, g = O.quantize_weights(W)
+        P = O.pack(T)
+        del T
+        Tg, gg = B.quantize_weights(dev(W), gamma_in=gamma_dev(g))
+        del W
+        Pg = B.pack(Tg)
+        del Tg
+        np.testing.assert_array_equal(host(Pg), P, err_msg=name)
+        _WEIGHTS[key] = (P, g, Pg)
+    return _WEIGHTS[key]
+
+
+def _layer_group(B, shapes, M, sigma, seed_layer, outliers):
+    """One layer of model-shaped BitLinears through the grouped forward (the
+    launch configuration the benchmark times); oracle on 48 sampled rows."""
+    rng = np.random.default_rng(seed_layer)
+    probs, refs = [], []
+    for j, (name, K, N) in enumerate(shapes):
+        P, g, Pg = _layer_weights(B, name, N, K, sigma, synth.matrix_seed(seed_layer, j))
+        X = synth.activations_np(M, K, seed=7 + j, outlier_frac=outliers)
+        Q, a, rs = O.quant_act(X)
+        rows = np.sort(rng.choice(N, size=48, replace=False))
+        rows[-1] = N - 1
+        refs.append((name, rows, O.matmul_packed_rows(Q, P, N, K, rows), g, a))
+        probs.append(dict(X=dev(X), P=Pg, gamma=gamma_dev(g),
+                          Y=torch.empty((M, N), dtype=torch.float32, device="cuda"),
+                          acc=torch.empty((M, N), dtype=torch.int32, device="cuda"), N=N))
+    plan = B.GroupPlan(probs)
+    plan.forward()
+    for p, (name, rows, ref_acc, g, a) in zip(probs, refs):
+        Y = host(p["Y"])[:, rows]
+        acc = host(p["acc"])[:, rows]
+        check_outputs(Y, acc, ref_acc, g, a, f"{name} M={M}")
+
+
+@pytest.mark.parametrize("M", [1, 8, 512])
+def test_2b_layer_sampled(B, M):
+    say("2B layer", M)
+    _layer_group(B, synth.SHAPES_2B, M, 0.02, 0, 0.01 if M == 512 else 0.0)
+
+
+@pytest.mark.parametrize("M", [1, 64, 256])
+def test_3b_layer_sampled(B, M):
+    say("3B layer", M)
+    _layer_group(B, synth.SHAPES_3B, M, 0.02, 1, 0.0)
+
+
+@pytest.mark.parametrize("M", [1, 16, 176])
+def test_70b_layer_sampled(B, M):
+    say("70B layer", M)
+    shapes = [s for s in synth.SHAPES_70B if s[0] in ("q", "k", "gate", "down")]
+    _layer_group(B, shapes, M, 0.01, 2, 0.0)
