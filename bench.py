@@ -83,24 +83,27 @@ def make_plan(B, torch, mats, M, dev, outliers=0.0, seed0=7):
 
 
 def time_plan(torch, plan, steps, warmup):
-    """Wall time of `steps` steps, and HIP-event durations of each step's
-    contraction launch (events recorded on the launch stream)."""
+    """Wall time per step over `steps` steps (quantize + contract), then the
+    contraction kernel alone: `steps` back-to-back launches between one pair
+    of HIP events on the launch stream (torch's current stream), giving its
+    average launch duration without per-launch event overhead."""
     for _ in range(warmup):
         plan.quant_act()
         plan.matmul()
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(steps)]
     t0 = time.perf_counter()
-    for a, b in evs:
+    for _ in range(steps):
         plan.quant_act()
-        a.record()
         plan.matmul()
-        b.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    kern_ms = [a.elapsed_time(b) for a, b in evs]
-    return wall / steps * 1e3, float(np.mean(kern_ms)), float(np.median(kern_ms))
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        plan.matmul()
+    b.record()
+    torch.cuda.synchronize()
+    return wall / steps * 1e3, a.elapsed_time(b) / steps
 
 
 def load_traffic(name):
@@ -188,7 +191,7 @@ def main():
     M = args.M
     plan, probs = make_plan(B, torch, mats, M, dev)
     log(f"timing decode sweep: {len(mats)} matrices, M={M}, {packed / 1e6:.1f} MB packed")
-    ms, kern_ms, kern_med = time_plan(torch, plan, args.steps, args.warmup)
+    ms, kern_ms = time_plan(torch, plan, args.steps, args.warmup)
     value = packed / (ms * 1e-3) / 1e9
     act_bytes = sum(M * B.q_stride(m["K"]) + 8 * M for m in mats)
     out_bytes = sum(4 * M * m["N"] for m in mats)
@@ -215,8 +218,7 @@ def main():
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
                      "kernel": "stream contraction (grouped, one launch per step)",
-                     "kernel_ms_mean": round(kern_ms, 5), "kernel_ms_median": round(kern_med, 5),
-                     "bytes_per_launch": alg_bytes},
+                     "kernel_ms_mean": round(kern_ms, 5), "bytes_per_launch": alg_bytes},
     }
     del plan, probs
     torch.cuda.empty_cache()
@@ -226,7 +228,7 @@ def main():
         plan, probs = make_plan(B, torch, mats, PM, dev, outliers=0.01)
         log(f"timing prefill sweep: M={PM}")
         steps = max(3, args.steps // 5)
-        pms, pkern, pmed = time_plan(torch, plan, steps, max(1, args.warmup // 2))
+        pms, pkern = time_plan(torch, plan, steps, max(1, args.warmup // 2))
         ops = sum(2 * PM * m["N"] * m["K"] for m in mats)
         result["prefill"] = {
             "M": PM, "ms_per_step": round(pms, 4), "value": round(ops / (pms * 1e-3) / 1e12, 2),

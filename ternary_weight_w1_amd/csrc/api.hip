@@ -60,6 +60,8 @@ int check_mnk(int64_t M, int64_t N, int64_t K)
 struct Knobs {
     int dot4_max_m = 1;          // M <= this takes the packed-dot4 kernel
     int split_target = 1024;     // aim for at least this many workgroups
+    int xcd_order = 2;           // bit 0: streaming kernel, bit 1: tile kernel
+    int tile_bm = 0;             // 64 or 128 forces the tile kernel's token tile
 };
 const Knobs &knobs()
 {
@@ -67,6 +69,8 @@ const Knobs &knobs()
         Knobs v;
         if (const char *s = getenv("BITLINEAR_DOT4_MAX_M")) v.dot4_max_m = atoi(s) > 0 ? 1 : 0;
         if (const char *s = getenv("BITLINEAR_SPLIT_TARGET")) v.split_target = atoi(s) > 0 ? atoi(s) : 1;
+        if (const char *s = getenv("BITLINEAR_XCD_ORDER")) v.xcd_order = atoi(s) & 3;
+        if (const char *s = getenv("BITLINEAR_TILE_BM")) v.tile_bm = (atoi(s) == 64 || atoi(s) == 128) ? atoi(s) : 0;
         return v;
     }();
     return k;
@@ -96,7 +100,7 @@ void decompose(Problem &p, int64_t base_items)
         }
     } else {
         p.kind = 1;
-        p.mtile = p.M > 64 ? 128 : 64;
+        p.mtile = knobs().tile_bm ? knobs().tile_bm : (p.M > 64 ? 128 : 64);
         p.ntile = 256;
         p.mt = (int32_t)((p.M + p.mtile - 1) / p.mtile);
         p.ntt = (p.NT + 3) / 4;
@@ -109,7 +113,7 @@ int64_t items_of(const Problem &p)
 }
 
 int stream_variant_for(int64_t M) { return (M <= knobs().dot4_max_m) ? 0 : 1; }
-int tile_variant_for(int64_t M) { return M > 64 ? 1 : 0; }
+int tile_variant_for(const Problem &p) { return p.mtile == 128 ? 1 : 0; }
 
 // Workspace layout of one problem: [Q][absmax][rowsum][partials][tickets],
 // each region 256-byte aligned.  with_act = false leaves out the first three.
@@ -160,7 +164,7 @@ Problem make_problem(int64_t M, int64_t N, int64_t K)
 hipError_t launch_contraction(const Problem &p, hipStream_t s)
 {
     if (p.kind == 0) return bl::launch_stream_single(p, stream_variant_for(p.M), s);
-    return bl::launch_tile_single(p, tile_variant_for(p.M), s);
+    return bl::launch_tile_single(p, tile_variant_for(p), s);
 }
 
 }  // namespace
@@ -347,7 +351,33 @@ namespace {
 struct GroupPlan {
     std::vector<Problem> probs;
     bl::GroupHeader h;
+    int64_t items_s = 0, items_t = 0;  // logical work items before XCD padding
 };
+
+// Work-item map of one kernel: logical items in problem order; with
+// xcd = true, workgroup b takes logical item (b % 8) * per + b / 8, so each
+// of the eight XCDs walks a contiguous slice of the list.
+void fill_map(const std::vector<Problem> &probs, int kind, int64_t logical, int64_t slots,
+              bool xcd, uint32_t *map)
+{
+    std::vector<uint32_t> pi, li;
+    pi.reserve(logical);
+    li.reserve(logical);
+    for (size_t i = 0; i < probs.size(); ++i) {
+        if (probs[i].kind != kind) continue;
+        const int64_t n = items_of(probs[i]);
+        for (int64_t j = 0; j < n; ++j) {
+            pi.push_back((uint32_t)i);
+            li.push_back((uint32_t)j);
+        }
+    }
+    const int64_t per = xcd ? slots / 8 : slots;
+    for (int64_t b = 0; b < slots; ++b) {
+        const int64_t j = xcd ? (b % 8) * per + b / 8 : b;
+        map[2 * b] = j < logical ? pi[j] : 0xFFFFFFFFu;
+        map[2 * b + 1] = j < logical ? li[j] : 0u;
+    }
+}
 
 // Validates the problems and computes the whole plan.  With ws == nullptr
 // the problems' workspace pointers are left null (sizing only).
@@ -401,7 +431,7 @@ int build_group(const bitlinear_problem *in, int count, char *ws, GroupPlan &out
         } else {
             p.item_begin = (int32_t)items_t;
             items_t += items_of(p);
-            any_big = any_big || p.M > 64;
+            any_big = any_big || p.mtile == 128;
         }
         if (tokens >= (int64_t(1) << 31) || items_s >= (int64_t(1) << 31) || items_t >= (int64_t(1) << 31))
             return fail(BITLINEAR_ERR_SHAPE, "group: too many tokens or work items");
@@ -424,6 +454,10 @@ int build_group(const bitlinear_problem *in, int count, char *ws, GroupPlan &out
     h.magic = bl::kGroupMagic;
     h.count = count;
     h.n_tokens = (int32_t)tokens;
+    out.items_s = items_s;
+    out.items_t = items_t;
+    if (knobs().xcd_order & 1) items_s = up(items_s, 8);
+    if (knobs().xcd_order & 2) items_t = up(items_t, 8);
     h.n_items_stream = (int32_t)items_s;
     h.n_items_tile = (int32_t)items_t;
     h.stream_variant = all_m1 ? 0 : 1;
@@ -435,9 +469,9 @@ int build_group(const bitlinear_problem *in, int count, char *ws, GroupPlan &out
     h.off_tok_map = t;
     t = up(t + 4 * tokens, 16);
     h.off_stream_map = t;
-    t = up(t + 4 * items_s, 16);
+    t = up(t + 8 * items_s, 16);
     h.off_tile_map = t;
-    t = up(t + 4 * items_t, 16);
+    t = up(t + 8 * items_t, 16);
     h.total_bytes = t;
     return BITLINEAR_OK;
 }
@@ -486,15 +520,14 @@ int bitlinear_group_plan(const bitlinear_problem *probs, int count, void *ws, si
     memcpy(t, &g.h, sizeof g.h);
     memcpy(t + g.h.off_probs, g.probs.data(), g.probs.size() * sizeof(Problem));
     uint32_t *tok = reinterpret_cast<uint32_t *>(t + g.h.off_tok_map);
-    uint32_t *sm = reinterpret_cast<uint32_t *>(t + g.h.off_stream_map);
-    uint32_t *tm = reinterpret_cast<uint32_t *>(t + g.h.off_tile_map);
     for (int i = 0; i < count; ++i) {
         const Problem &p = g.probs[i];
         for (int m = 0; m < p.M; ++m) tok[p.tok_begin + m] = (uint32_t)i;
-        const int64_t n = items_of(p);
-        uint32_t *map = p.kind == 0 ? sm : tm;
-        for (int64_t j = 0; j < n; ++j) map[p.item_begin + j] = (uint32_t)i;
     }
+    fill_map(g.probs, 0, g.items_s, g.h.n_items_stream, knobs().xcd_order & 1,
+             reinterpret_cast<uint32_t *>(t + g.h.off_stream_map));
+    fill_map(g.probs, 1, g.items_t, g.h.n_items_tile, (knobs().xcd_order & 2) != 0,
+             reinterpret_cast<uint32_t *>(t + g.h.off_tile_map));
     return BITLINEAR_OK;
 }
 
@@ -518,11 +551,11 @@ int bitlinear_group_matmul(const void *table_host, const void *table_dev, void *
     const Problem *probs = reinterpret_cast<const Problem *>(d + h.off_probs);
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (h.n_items_stream > 0)
-        if (hipError_t e = bl::launch_stream_group(probs, reinterpret_cast<const uint32_t *>(d + h.off_stream_map),
+        if (hipError_t e = bl::launch_stream_group(probs, reinterpret_cast<const uint2 *>(d + h.off_stream_map),
                                                    h.n_items_stream, h.stream_variant, s))
             return hip_fail(e, "group stream kernel");
     if (h.n_items_tile > 0)
-        if (hipError_t e = bl::launch_tile_group(probs, reinterpret_cast<const uint32_t *>(d + h.off_tile_map),
+        if (hipError_t e = bl::launch_tile_group(probs, reinterpret_cast<const uint2 *>(d + h.off_tile_map),
                                                  h.n_items_tile, h.tile_variant, s))
             return hip_fail(e, "group tile kernel");
     return BITLINEAR_OK;

@@ -57,9 +57,9 @@ struct GroupHeader {
     int32_t pad_[3];
     int64_t ws_bytes;       // workspace the plan was built for
     int64_t off_probs;      // byte offsets inside the table
-    int64_t off_tok_map;    // uint32 per token:  problem index
-    int64_t off_stream_map; // uint32 per item:   problem index
-    int64_t off_tile_map;   // uint32 per item:   problem index
+    int64_t off_tok_map;    // uint32 per token: problem index
+    int64_t off_stream_map; // uint2 per workgroup: {problem, local item} ({~0u, 0} = idle)
+    int64_t off_tile_map;   // uint2 per workgroup: {problem, local item}
     int64_t total_bytes;
 };
 constexpr uint32_t kGroupMagic = 0xB17E0001u;
@@ -80,10 +80,10 @@ hipError_t launch_quant_act_group(const Problem *probs, const uint32_t *tok_map,
                                   hipStream_t s);
 hipError_t launch_zero_words(uint32_t *p, int64_t n, hipStream_t s);
 hipError_t launch_stream_single(const Problem &p, int variant, hipStream_t s);
-hipError_t launch_stream_group(const Problem *probs, const uint32_t *item_map, int n_items,
+hipError_t launch_stream_group(const Problem *probs, const uint2 *item_map, int n_items,
                                int variant, hipStream_t s);
 hipError_t launch_tile_single(const Problem &p, int variant, hipStream_t s);
-hipError_t launch_tile_group(const Problem *probs, const uint32_t *item_map, int n_items,
+hipError_t launch_tile_group(const Problem *probs, const uint2 *item_map, int n_items,
                              int variant, hipStream_t s);
 
 }  // namespace bl

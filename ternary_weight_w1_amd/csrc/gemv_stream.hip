@@ -224,10 +224,11 @@ __global__ __launch_bounds__(kThreads) void stream_single_kernel(Problem p)
 
 template <int V>
 __global__ __launch_bounds__(kThreads) void stream_group_kernel(const Problem *__restrict__ probs,
-                                                                const uint32_t *__restrict__ item_map)
+                                                                const uint2 *__restrict__ item_map)
 {
-    const Problem &p = probs[item_map[blockIdx.x]];
-    stream_body<V>(p, (int)blockIdx.x - p.item_begin);
+    const uint2 it = item_map[blockIdx.x];
+    if (it.x == 0xFFFFFFFFu) return;
+    stream_body<V>(probs[it.x], (int)it.y);
 }
 
 }  // namespace
@@ -242,7 +243,7 @@ hipError_t launch_stream_single(const Problem &p, int variant, hipStream_t s)
     return hipGetLastError();
 }
 
-hipError_t launch_stream_group(const Problem *probs, const uint32_t *item_map, int n_items,
+hipError_t launch_stream_group(const Problem *probs, const uint2 *item_map, int n_items,
                                int variant, hipStream_t s)
 {
     const dim3 grid((unsigned)n_items), block(kThreads);

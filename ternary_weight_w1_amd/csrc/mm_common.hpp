@@ -46,15 +46,20 @@ __device__ inline void finish_output(const Problem &p, float gamma, int m, int n
 
 // Split-K arrival: every workgroup of a 64-row tile publishes its partial
 // sums, then takes a ticket; the one that takes the last ticket sums the
-// partials.  The fences order the partial stores before the ticket and the
-// ticket before the reads of the other workgroups' partials.
+// partials and puts the counter back to zero (every other workgroup of the
+// tile has already taken its ticket), so the counters are clean for the
+// next launch.  The fences order the partial stores before the ticket and
+// the ticket before the reads of the other workgroups' partials.
 __device__ inline bool arrive_last(const Problem &p, int tile)
 {
     __shared__ int s_last;
     __threadfence();
     __syncthreads();
-    if (threadIdx.x == 0)
-        s_last = (atomicAdd(&p.tickets[tile], 1u) == (unsigned)(p.ks - 1)) ? 1 : 0;
+    if (threadIdx.x == 0) {
+        const bool last = atomicAdd(&p.tickets[tile], 1u) == (unsigned)(p.ks - 1);
+        if (last) atomicExch(&p.tickets[tile], 0u);
+        s_last = last ? 1 : 0;
+    }
     __syncthreads();
     const bool last = s_last != 0;
     if (last) __threadfence();
