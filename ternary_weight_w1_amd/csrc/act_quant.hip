@@ -7,10 +7,10 @@
 // of q is produced too: the contraction kernels multiply by (code + 1)
 // fields and subtract it once per output.
 //
-// One 256-thread workgroup per token: pass 1 reads the row with 16-byte
-// loads and reduces |x| with wave butterflies, then across the four waves
-// through LDS; pass 2 re-reads the row (L1/L2 resident) and writes four
-// codes per 32-bit store.  The max is order-free and the row sum is an
+// One 256-thread workgroup per token: the row is read with 16-byte loads
+// (kept in registers up to 8192 values), |x| is reduced with wave
+// butterflies and then across the four waves through LDS, and the codes are
+// written 16 per 16-byte store.  The max is order-free and the row sum is an
 // integer sum, so both are exact whatever the reduction order.
 #include "common.hpp"
 
@@ -18,6 +18,8 @@ namespace bl {
 namespace {
 
 constexpr int kThreads = 256;
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 
 __device__ inline float block_max(float v, float *lds)
 {
@@ -47,21 +49,58 @@ __device__ inline int8_t quant_code(float x, float s)
     return (int8_t)(int)r;
 }
 
-__device__ void quant_row(const float *__restrict__ x, int K, int8_t *__restrict__ q, int64_t ldq,
-                          float *__restrict__ absmax, int32_t *__restrict__ rowsum)
+// Where code k of the row goes: row-major (Q + m*ldq + k) or fragment order.
+// In both layouts each aligned 16-code chunk is 16 contiguous bytes.
+struct QDest {
+    int8_t *Q;
+    int64_t ldq;  // row-major stride; unused in fragment order
+    int64_t m;
+    int64_t KU;
+    int tiled;
+    __device__ int64_t at(int64_t k) const { return tiled ? qf32_offset(m, k, KU) : m * ldq + k; }
+    __device__ int64_t fill_end() const { return tiled ? 64 * KU : ldq; }
+};
+
+// One token row.  Each thread owns 16-code chunks (four 16-byte loads, one
+// 16-byte store); rows of up to kRegChunks * 16 * 256 values stay in
+// registers between the max and the rounding pass, so X is read from HBM
+// once; longer rows read it twice (the second pass mostly from L2).
+constexpr int kRegChunks = 2;
+
+__device__ void quant_row(const float *x_, int K, const QDest &dst, float *absmax_,
+                          int32_t *rowsum_)
 {
     __shared__ float fl[4];
     __shared__ int il[4];
+    const BL_GLOBAL float *x = gload_ptr<float>(x_);
+    BL_GLOBAL int8_t *q = gstore_ptr<int8_t>(dst.Q);
     const int tid = threadIdx.x;
-    const bool vec = ((K & 3) == 0) && ((reinterpret_cast<uintptr_t>(x) & 15) == 0);
+    // chunk path: K a multiple of 16 and X rows 16-byte aligned
+    const bool vec = ((K & 15) == 0) && ((reinterpret_cast<uintptr_t>(x_) & 15) == 0);
+    const int nc = K >> 4;
+    const BL_GLOBAL v4f *x4 = reinterpret_cast<const BL_GLOBAL v4f *>(x);
+    const bool in_regs = vec && nc <= kRegChunks * kThreads;
+    const v4f zero4 = {0.f, 0.f, 0.f, 0.f};
 
+    auto amax4 = [](v4f w) {
+        return fmaxf(fmaxf(fabsf(w.x), fabsf(w.y)), fmaxf(fabsf(w.z), fabsf(w.w)));
+    };
+    v4f v[kRegChunks][4];
     float a = 0.0f;
-    if (vec) {
-        const float4 *x4 = reinterpret_cast<const float4 *>(x);
-        for (int i = tid; i < (K >> 2); i += kThreads) {
-            const float4 v = x4[i];
-            a = fmaxf(a, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+    if (in_regs) {
+#pragma unroll
+        for (int j = 0; j < kRegChunks; ++j) {
+            const int c = tid + j * kThreads;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                v[j][t] = c < nc ? x4[4 * c + t] : zero4;
+                a = fmaxf(a, amax4(v[j][t]));
+            }
         }
+    } else if (vec) {
+        for (int c = tid; c < nc; c += kThreads)
+#pragma unroll
+            for (int t = 0; t < 4; ++t) a = fmaxf(a, amax4(x4[4 * c + t]));
     } else {
         for (int i = tid; i < K; i += kThreads) a = fmaxf(a, fabsf(x[i]));
     }
@@ -70,34 +109,52 @@ __device__ void quant_row(const float *__restrict__ x, int K, int8_t *__restrict
     const float s = 127.0f / a;
 
     int sum = 0;
-    if (vec) {
-        const float4 *x4 = reinterpret_cast<const float4 *>(x);
-        uint32_t *q4 = reinterpret_cast<uint32_t *>(q);
-        for (int i = tid; i < (K >> 2); i += kThreads) {
-            const float4 v = x4[i];
-            const int8_t c0 = quant_code(v.x, s), c1 = quant_code(v.y, s);
-            const int8_t c2 = quant_code(v.z, s), c3 = quant_code(v.w, s);
-            sum += (int)c0 + (int)c1 + (int)c2 + (int)c3;
-            q4[i] = (uint32_t)(uint8_t)c0 | ((uint32_t)(uint8_t)c1 << 8) |
-                    ((uint32_t)(uint8_t)c2 << 16) | ((uint32_t)(uint8_t)c3 << 24);
+    auto pack4 = [&](v4f w) {
+        const int8_t c0 = quant_code(w.x, s), c1 = quant_code(w.y, s);
+        const int8_t c2 = quant_code(w.z, s), c3 = quant_code(w.w, s);
+        sum += (int)c0 + (int)c1 + (int)c2 + (int)c3;
+        return (uint32_t)(uint8_t)c0 | ((uint32_t)(uint8_t)c1 << 8) | ((uint32_t)(uint8_t)c2 << 16) |
+               ((uint32_t)(uint8_t)c3 << 24);
+    };
+    auto put16 = [&](int c, const v4f *w) {
+        v4u o;
+        o.x = pack4(w[0]);
+        o.y = pack4(w[1]);
+        o.z = pack4(w[2]);
+        o.w = pack4(w[3]);
+        *reinterpret_cast<BL_GLOBAL v4u *>(q + dst.at(16 * c)) = o;
+    };
+    if (in_regs) {
+#pragma unroll
+        for (int j = 0; j < kRegChunks; ++j) {
+            const int c = tid + j * kThreads;
+            if (c < nc) put16(c, v[j]);
+        }
+    } else if (vec) {
+        for (int c = tid; c < nc; c += kThreads) {
+            v4f w[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) w[t] = x4[4 * c + t];
+            put16(c, w);
         }
     } else {
         for (int i = tid; i < K; i += kThreads) {
             const int8_t c = quant_code(x[i], s);
             sum += c;
-            q[i] = c;
+            q[dst.at(i)] = c;
         }
     }
-    for (int64_t i = K + tid; i < ldq; i += kThreads) q[i] = 0;
+    for (int64_t i = K + tid; i < dst.fill_end(); i += kThreads) q[dst.at(i)] = 0;
     sum = block_sum_i32(sum, il);
     if (tid == 0) {
-        *absmax = a;
-        if (rowsum) *rowsum = sum;
+        *gstore_ptr<float>(absmax_) = a;
+        if (rowsum_) *gstore_ptr<int32_t>(rowsum_) = sum;
     }
 }
 
 __global__ __launch_bounds__(kThreads) void quant_act_kernel(const float *__restrict__ X, int K,
                                                              int8_t *__restrict__ Q, int64_t ldq,
+                                                             int qtiled,
                                                              float *__restrict__ absmax,
                                                              int32_t *__restrict__ rowsum,
                                                              uint32_t *__restrict__ zero_ptr,
@@ -106,7 +163,8 @@ __global__ __launch_bounds__(kThreads) void quant_act_kernel(const float *__rest
     const int64_t m = blockIdx.x;
     if (m == 0 && zero_ptr)
         for (int i = threadIdx.x; i < zero_n; i += kThreads) zero_ptr[i] = 0u;
-    quant_row(X + m * K, K, Q + m * ldq, ldq, absmax + m, rowsum ? rowsum + m : nullptr);
+    const QDest dst{Q, ldq, m, (K + 63) / 64, qtiled};
+    quant_row(X + m * K, K, dst, absmax + m, rowsum ? rowsum + m : nullptr);
 }
 
 __global__ __launch_bounds__(kThreads) void quant_act_group_kernel(const Problem *__restrict__ probs,
@@ -117,7 +175,8 @@ __global__ __launch_bounds__(kThreads) void quant_act_group_kernel(const Problem
     const int64_t m = tok - p.tok_begin;
     if (m == 0 && p.tickets)
         for (int i = threadIdx.x; i < p.NT; i += kThreads) p.tickets[i] = 0u;
-    quant_row(p.X + m * p.K, p.K, p.Q + m * p.ldq, p.ldq, p.absmax + m, p.rowsum + m);
+    const QDest dst{p.Q, p.ldq, m, p.KU, p.qtiled};
+    quant_row(p.X + m * p.K, p.K, dst, p.absmax + m, p.rowsum + m);
 }
 
 __global__ __launch_bounds__(kThreads) void zero_words_kernel(uint32_t *__restrict__ p, int64_t n)
@@ -129,11 +188,11 @@ __global__ __launch_bounds__(kThreads) void zero_words_kernel(uint32_t *__restri
 }  // namespace
 
 hipError_t launch_quant_act(const float *X, int64_t M, int64_t K, int8_t *Q, int64_t ldq,
-                            float *absmax, int32_t *rowsum, uint32_t *zero_ptr, int zero_n,
-                            hipStream_t s)
+                            int qtiled, float *absmax, int32_t *rowsum, uint32_t *zero_ptr,
+                            int zero_n, hipStream_t s)
 {
     hipLaunchKernelGGL(quant_act_kernel, dim3((unsigned)M), dim3(kThreads), 0, s, X, (int)K, Q, ldq,
-                       absmax, rowsum, zero_ptr, zero_n);
+                       qtiled, absmax, rowsum, zero_ptr, zero_n);
     return hipGetLastError();
 }
 

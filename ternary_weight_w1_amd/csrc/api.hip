@@ -61,7 +61,7 @@ struct Knobs {
     int dot4_max_m = 1;          // M <= this takes the packed-dot4 kernel
     int split_target = 1024;     // aim for at least this many workgroups
     int xcd_order = 2;           // bit 0: streaming kernel, bit 1: tile kernel
-    int tile_bm = 0;             // 64 or 128 forces the tile kernel's token tile
+    int tile_variant = -1;       // force a tile-kernel instantiation (0..7)
 };
 const Knobs &knobs()
 {
@@ -70,22 +70,43 @@ const Knobs &knobs()
         if (const char *s = getenv("BITLINEAR_DOT4_MAX_M")) v.dot4_max_m = atoi(s) > 0 ? 1 : 0;
         if (const char *s = getenv("BITLINEAR_SPLIT_TARGET")) v.split_target = atoi(s) > 0 ? atoi(s) : 1;
         if (const char *s = getenv("BITLINEAR_XCD_ORDER")) v.xcd_order = atoi(s) & 3;
-        if (const char *s = getenv("BITLINEAR_TILE_BM")) v.tile_bm = (atoi(s) == 64 || atoi(s) == 128) ? atoi(s) : 0;
+        if (const char *s = getenv("BITLINEAR_TILE_VARIANT")) v.tile_variant = (atoi(s) >= 0 && atoi(s) <= 7) ? atoi(s) : -1;
         return v;
     }();
     return k;
 }
 
+// Tile-kernel instantiation: 0..2 are the LDS-staged variants on row-major
+// activations (64-token tiles; 128-token 2x2 waves; 128-token 4x1 waves),
+// 3/4 the barrier-free direct-load variants (fragment-ordered / row-major).
+// 5..7 are the LDS-staged variants on fragment-ordered activations (as 2,
+// 0, 1).
+int tile_variant(bool own_q)
+{
+    int v = knobs().tile_variant;
+    if (v < 0) v = 2;
+    if (!own_q) {  // caller-supplied activations are row-major
+        if (v == 3) return 4;
+        if (v == 5) return 2;
+        if (v == 6) return 0;
+        if (v == 7) return 1;
+    }
+    return v;
+}
+int tile_bm(int variant) { return (variant == 0 || variant == 6) ? 64 : 128; }
+bool tile_frag(int variant) { return variant == 3 || variant >= 5; }
+
 // Kernel kind and decomposition of one problem.  `base_items` is the number
 // of streaming work items the whole launch has without K splits; splits are
-// added only while the launch is short of workgroups.
-void decompose(Problem &p, int64_t base_items)
+// added only while the launch is short of workgroups.  own_q: the library
+// quantizes the activations itself and may choose their layout.
+void decompose(Problem &p, int64_t base_items, bool own_q)
 {
     p.KU = (int32_t)((p.K + 63) / 64);
     p.NT = (int32_t)((p.N + 63) / 64);
     p.ks = 1;
     p.upsplit = p.KU;
-    p.mt = p.ntt = p.mtile = p.ntile = 0;
+    p.mt = p.ntt = p.mtile = p.qtiled = 0;
     if (p.M <= kStreamMaxM) {
         p.kind = 0;
         const int64_t target = knobs().split_target;
@@ -100,8 +121,9 @@ void decompose(Problem &p, int64_t base_items)
         }
     } else {
         p.kind = 1;
-        p.mtile = knobs().tile_bm ? knobs().tile_bm : (p.M > 64 ? 128 : 64);
-        p.ntile = 256;
+        const int v = tile_variant(own_q);
+        p.mtile = tile_bm(v);
+        p.qtiled = tile_frag(v) ? 1 : 0;
         p.mt = (int32_t)((p.M + p.mtile - 1) / p.mtile);
         p.ntt = (p.NT + 3) / 4;
     }
@@ -113,7 +135,7 @@ int64_t items_of(const Problem &p)
 }
 
 int stream_variant_for(int64_t M) { return (M <= knobs().dot4_max_m) ? 0 : 1; }
-int tile_variant_for(const Problem &p) { return p.mtile == 128 ? 1 : 0; }
+
 
 // Workspace layout of one problem: [Q][absmax][rowsum][partials][tickets],
 // each region 256-byte aligned.  with_act = false leaves out the first three.
@@ -127,7 +149,7 @@ WsLayout ws_layout(const Problem &p, bool with_act)
     const int64_t ldq = 64 * (int64_t)p.KU;
     if (with_act) {
         L.q = off;
-        off = up(off + (int64_t)p.M * ldq, 256);
+        off = up(off + (p.qtiled ? up(p.M, 32) : (int64_t)p.M) * ldq, 256);
         L.absmax = off;
         off = up(off + 4 * (int64_t)p.M, 256);
         L.rowsum = off;
@@ -161,10 +183,10 @@ Problem make_problem(int64_t M, int64_t N, int64_t K)
     return p;
 }
 
-hipError_t launch_contraction(const Problem &p, hipStream_t s)
+hipError_t launch_contraction(const Problem &p, bool own_q, hipStream_t s)
 {
     if (p.kind == 0) return bl::launch_stream_single(p, stream_variant_for(p.M), s);
-    return bl::launch_tile_single(p, tile_variant_for(p), s);
+    return bl::launch_tile_single(p, tile_variant(own_q), s);
 }
 
 }  // namespace
@@ -206,7 +228,7 @@ size_t bitlinear_workspace_bytes(int op, int64_t M, int64_t N, int64_t K)
     if (op != BITLINEAR_WS_MATMUL && op != BITLINEAR_WS_FORWARD) return SIZE_MAX;
     if (check_mnk(M, N, K) != BITLINEAR_OK) return SIZE_MAX;
     Problem p = make_problem(M, N, K);
-    decompose(p, (N + 63) / 64);
+    decompose(p, (N + 63) / 64, op == BITLINEAR_WS_FORWARD);
     return (size_t)ws_layout(p, op == BITLINEAR_WS_FORWARD).total;
 }
 
@@ -261,7 +283,7 @@ int bitlinear_quant_act(const float *X, int64_t M, int64_t K, int8_t *Q_out, int
     if (ldq < K || ldq % 16 != 0) return fail(BITLINEAR_ERR_SHAPE, "quant_act: ldq=%lld must be >= K and a multiple of 16", (long long)ldq);
     if (!a16(X) || !a16(Q_out) || !a4(absmax_out) || (rowsum_out && !a4(rowsum_out)))
         return fail(BITLINEAR_ERR_ALIGN, "quant_act: X/Q_out need 16-byte, absmax/rowsum 4-byte alignment");
-    if (hipError_t e = bl::launch_quant_act(X, M, K, Q_out, ldq, absmax_out, rowsum_out, nullptr, 0,
+    if (hipError_t e = bl::launch_quant_act(X, M, K, Q_out, ldq, 0, absmax_out, rowsum_out, nullptr, 0,
                                             static_cast<hipStream_t>(stream)))
         return hip_fail(e, "quant_act");
     return BITLINEAR_OK;
@@ -279,7 +301,7 @@ int bitlinear_matmul(const int8_t *Q, int64_t ldq, const float *absmax, const in
     if (!a16(Q) || !a16(P) || !a16(Y_out) || (acc_out && !a16(acc_out)) || !a4(absmax) || !a4(rowsum) || !a4(gamma))
         return fail(BITLINEAR_ERR_ALIGN, "matmul: arrays need 16-byte, scalars 4-byte alignment");
     Problem p = make_problem(M, N, K);
-    decompose(p, (N + 63) / 64);
+    decompose(p, (N + 63) / 64, false);
     const WsLayout L = ws_layout(p, false);
     if (L.total > 0 && (!ws || ws_bytes < (size_t)L.total || !a16(ws)))
         return fail(BITLINEAR_ERR_WORKSPACE, "matmul: needs %lld workspace bytes (16-byte aligned)", (long long)L.total);
@@ -300,7 +322,7 @@ int bitlinear_matmul(const int8_t *Q, int64_t ldq, const float *absmax, const in
         p.tickets = reinterpret_cast<uint32_t *>(base + L.tick);
         if (hipError_t e = bl::launch_zero_words(p.tickets, p.NT, s)) return hip_fail(e, "zero tickets");
     }
-    if (hipError_t e = launch_contraction(p, s)) return hip_fail(e, "matmul");
+    if (hipError_t e = launch_contraction(p, false, s)) return hip_fail(e, "matmul");
     return BITLINEAR_OK;
 }
 
@@ -313,7 +335,7 @@ int bitlinear_forward(const float *X, int64_t M, int64_t K, const uint8_t *P,
     if (!a16(X) || !a16(P) || !a16(Y_out) || (acc_out && !a16(acc_out)) || !a4(gamma))
         return fail(BITLINEAR_ERR_ALIGN, "forward: arrays need 16-byte, gamma 4-byte alignment");
     Problem p = make_problem(M, N, K);
-    decompose(p, (N + 63) / 64);
+    decompose(p, (N + 63) / 64, true);
     const WsLayout L = ws_layout(p, true);
     if (!ws || ws_bytes < (size_t)L.total || !a16(ws))
         return fail(BITLINEAR_ERR_WORKSPACE, "forward: needs %lld workspace bytes (16-byte aligned)", (long long)L.total);
@@ -334,10 +356,10 @@ int bitlinear_forward(const float *X, int64_t M, int64_t K, const uint8_t *P,
         p.tickets = reinterpret_cast<uint32_t *>(base + L.tick);
     }
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (hipError_t e = bl::launch_quant_act(X, M, K, p.Q, p.ldq, p.absmax, p.rowsum, p.tickets,
-                                            p.tickets ? p.NT : 0, s))
+    if (hipError_t e = bl::launch_quant_act(X, M, K, p.Q, p.ldq, p.qtiled, p.absmax, p.rowsum,
+                                            p.tickets, p.tickets ? p.NT : 0, s))
         return hip_fail(e, "forward: quant_act");
-    if (hipError_t e = launch_contraction(p, s)) return hip_fail(e, "forward: matmul");
+    if (hipError_t e = launch_contraction(p, true, s)) return hip_fail(e, "forward: matmul");
     return BITLINEAR_OK;
 }
 
@@ -398,12 +420,12 @@ int build_group(const bitlinear_problem *in, int count, char *ws, GroupPlan &out
     }
     if (base_items < 1) base_items = 1;
     int64_t tokens = 0, items_s = 0, items_t = 0, off = 0;
-    bool all_m1 = true, any_big = false;
+    bool all_m1 = true;
     for (int i = 0; i < count; ++i) {
         const bitlinear_problem &q = in[i];
         Problem &p = out.probs[i];
         p = make_problem(q.M, q.N, q.K);
-        decompose(p, base_items);
+        decompose(p, base_items, true);
         p.X = q.X;
         p.P = q.P;
         p.gamma = q.gamma;
@@ -431,25 +453,14 @@ int build_group(const bitlinear_problem *in, int count, char *ws, GroupPlan &out
         } else {
             p.item_begin = (int32_t)items_t;
             items_t += items_of(p);
-            any_big = any_big || p.mtile == 128;
         }
         if (tokens >= (int64_t(1) << 31) || items_s >= (int64_t(1) << 31) || items_t >= (int64_t(1) << 31))
             return fail(BITLINEAR_ERR_SHAPE, "group: too many tokens or work items");
     }
-    // a mixed launch takes one instantiation per kernel: tile kernel with
-    // 128-token tiles if any problem needs them, streaming kernel with MFMA
-    // unless every streaming problem has a single token
-    for (Problem &p : out.probs)
-        if (p.kind == 1 && any_big && p.mtile != 128) {
-            p.mtile = 128;
-            p.mt = (p.M + 127) / 128;
-        }
-    items_t = 0;
-    for (Problem &p : out.probs)
-        if (p.kind == 1) {
-            p.item_begin = (int32_t)items_t;
-            items_t += items_of(p);
-        }
+    // one instantiation per kernel and launch: every tile problem of a group
+    // takes the same tile variant (decompose picks it from the knobs alone);
+    // the streaming kernel runs MFMA unless every streaming problem has a
+    // single token
     bl::GroupHeader &h = out.h;
     h.magic = bl::kGroupMagic;
     h.count = count;
@@ -461,7 +472,7 @@ int build_group(const bitlinear_problem *in, int count, char *ws, GroupPlan &out
     h.n_items_stream = (int32_t)items_s;
     h.n_items_tile = (int32_t)items_t;
     h.stream_variant = all_m1 ? 0 : 1;
-    h.tile_variant = any_big ? 1 : 0;
+    h.tile_variant = tile_variant(true);
     h.ws_bytes = off;
     int64_t t = up(sizeof(bl::GroupHeader), 16);
     h.off_probs = t;

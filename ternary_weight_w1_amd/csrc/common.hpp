@@ -8,6 +8,22 @@
 
 namespace bl {
 
+// Global-memory views of the problem's buffers.  Pointers read from a
+// problem descriptor are generic; the explicit address space makes every
+// access a global_load/global_store (flat accesses would also count against
+// the LDS wait counter and serialize LDS waits behind in-flight loads).
+#define BL_GLOBAL __attribute__((address_space(1)))
+template <typename T>
+__device__ inline const BL_GLOBAL T *gload_ptr(const void *p)
+{
+    return (const BL_GLOBAL T *)p;
+}
+template <typename T>
+__device__ inline BL_GLOBAL T *gstore_ptr(void *p)
+{
+    return (BL_GLOBAL T *)p;
+}
+
 // BL2-T64 geometry: 64-row tiles, 64-code units, 1 KiB blocks.
 constexpr int kTileRows = 64;
 constexpr int kUnitCodes = 64;
@@ -35,13 +51,26 @@ struct Problem {
     int32_t upsplit;       // units per split (last split may be shorter)
     int32_t kind;          // 0 = streaming kernel (small M), 1 = tile kernel
     int32_t mtile;         // rows of M per tile-kernel work item
-    int32_t ntile;         // rows of N per tile-kernel work item
+    int32_t qtiled;        // 1: Q is stored in MFMA fragment order (see below)
     int32_t mt;            // M tiles of the tile kernel
     int32_t ntt;           // N tiles of the tile kernel
     int32_t tok_begin;     // first row of this problem in the grouped quant grid
     int32_t item_begin;    // first work item of this problem in its kernel's grid
 };
 static_assert(sizeof(Problem) == 144, "Problem layout is shared by host and device");
+
+// Fragment order of the int8 activations ("QF32"), used by the tile kernel
+// so that each wave reads an MFMA A operand with one contiguous 1 KiB load:
+// for 32-row block b = m / 32, 64-code unit u and half h, a 1 KiB block at
+// ((b * KU + u) * 2 + h) * 1024 holds, at byte 16 * l + c (lane l = 0..63,
+// c = 0..15), Q[32 b + l % 32][64 u + 32 h + 16 (l / 32) + c].  Rows past M
+// in the last block are never written and never stored from.
+__host__ __device__ inline int64_t qf32_offset(int64_t m, int64_t k, int64_t KU)
+{
+    const int64_t b = m >> 5;
+    const int64_t u = k >> 6, h = (k >> 5) & 1, g = (k >> 4) & 1;
+    return ((b * KU + u) * 2 + h) * 1024 + 16 * ((m & 31) + 32 * g) + (k & 15);
+}
 
 // Plan table header (first bytes of the grouped-forward table).
 struct GroupHeader {
@@ -74,8 +103,8 @@ hipError_t launch_ternarize(const float *W, int64_t count, const float *gamma, i
 hipError_t launch_pack(const int8_t *T, int64_t N, int64_t K, uint8_t *P, hipStream_t s);
 hipError_t launch_unpack(const uint8_t *P, int64_t N, int64_t K, int8_t *T, hipStream_t s);
 hipError_t launch_quant_act(const float *X, int64_t M, int64_t K, int8_t *Q, int64_t ldq,
-                            float *absmax, int32_t *rowsum, uint32_t *zero_ptr, int zero_n,
-                            hipStream_t s);
+                            int qtiled, float *absmax, int32_t *rowsum, uint32_t *zero_ptr,
+                            int zero_n, hipStream_t s);
 hipError_t launch_quant_act_group(const Problem *probs, const uint32_t *tok_map, int n_tokens,
                                   hipStream_t s);
 hipError_t launch_zero_words(uint32_t *p, int64_t n, hipStream_t s);

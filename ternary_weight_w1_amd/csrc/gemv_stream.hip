@@ -56,8 +56,8 @@ __device__ void stream_dot4(const Problem &p, int local)
     const int u0 = split * p.upsplit;
     const int u1 = min(p.KU, u0 + p.upsplit);
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 5;
-    const v4u *blk = reinterpret_cast<const v4u *>(p.P + (int64_t)tile * p.KU * kBlockBytes) + lane;
-    const int8_t *q = p.Q + 16 * g;  // token 0; chunk g of each 32-code half
+    const BL_GLOBAL v4u *blk = gload_ptr<v4u>(p.P + (int64_t)tile * p.KU * kBlockBytes) + lane;
+    const BL_GLOBAL int8_t *q = gload_ptr<int8_t>(p.Q) + 16 * g;  // token 0; chunk g of each 32-code half
 
     int acc0 = 0, acc1 = 0;  // rows r and 32 + r of the tile
     int u = u0 + wave;
@@ -68,9 +68,9 @@ __device__ void stream_dot4(const Problem &p, int local)
         for (int j = 0; j < UNROLL; ++j) w[j] = load_packed(blk + (int64_t)(u + kWaves * j) * 64);
 #pragma unroll
         for (int j = 0; j < UNROLL; ++j) {
-            const int8_t *qu = q + 64 * (u + kWaves * j);
-            qa[j] = *reinterpret_cast<const v4i *>(qu);
-            qb[j] = *reinterpret_cast<const v4i *>(qu + 32);
+            const BL_GLOBAL int8_t *qu = q + 64 * (u + kWaves * j);
+            qa[j] = *reinterpret_cast<const BL_GLOBAL v4i *>(qu);
+            qb[j] = *reinterpret_cast<const BL_GLOBAL v4i *>(qu + 32);
         }
 #pragma unroll
         for (int j = 0; j < UNROLL; ++j) {
@@ -82,9 +82,9 @@ __device__ void stream_dot4(const Problem &p, int local)
     }
     for (; u < u1; u += kWaves) {
         const v4u w = load_packed(blk + (int64_t)u * 64);
-        const int8_t *qu = q + 64 * u;
-        const v4i qa = *reinterpret_cast<const v4i *>(qu);
-        const v4i qb = *reinterpret_cast<const v4i *>(qu + 32);
+        const BL_GLOBAL int8_t *qu = q + 64 * u;
+        const v4i qa = *reinterpret_cast<const BL_GLOBAL v4i *>(qu);
+        const v4i qb = *reinterpret_cast<const BL_GLOBAL v4i *>(qu + 32);
         acc0 = dot16(w.x, qa, acc0);
         acc0 = dot16(w.y, qb, acc0);
         acc1 = dot16(w.z, qa, acc1);
@@ -109,11 +109,11 @@ __device__ void stream_dot4(const Problem &p, int local)
         return;
     }
     const int64_t ldp = (int64_t)p.NT * 64;  // partial row stride
-    if (t < 64) p.acc_ws[(int64_t)split * p.M * ldp + n] = total;
+    if (t < 64) gstore_ptr<int32_t>(p.acc_ws)[(int64_t)split * p.M * ldp + n] = total;
     if (!arrive_last(p, tile)) return;
     if (t < 64 && n < p.N) {
         int sum = 0;
-        for (int j = 0; j < p.ks; ++j) sum += p.acc_ws[(int64_t)j * p.M * ldp + n];
+        for (int j = 0; j < p.ks; ++j) sum += gload_ptr<int32_t>(p.acc_ws)[(int64_t)j * p.M * ldp + n];
         finish_output(p, gamma, 0, n, sum);
     }
 }
@@ -127,9 +127,9 @@ __device__ void stream_mfma(const Problem &p, int local)
     const int u0 = split * p.upsplit;
     const int u1 = min(p.KU, u0 + p.upsplit);
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 5, r = lane & 31;
-    const v4u *blk = reinterpret_cast<const v4u *>(p.P + (int64_t)tile * p.KU * kBlockBytes) + lane;
+    const BL_GLOBAL v4u *blk = gload_ptr<v4u>(p.P + (int64_t)tile * p.KU * kBlockBytes) + lane;
     const bool rv = r < p.M;
-    const int8_t *qrow = p.Q + (int64_t)(rv ? r : 0) * p.ldq + 16 * g;
+    const BL_GLOBAL int8_t *qrow = gload_ptr<int8_t>(p.Q + (int64_t)(rv ? r : 0) * p.ldq + 16 * g);
     const v4i zero = {0, 0, 0, 0};
 
     v16i acc0 = {}, acc1 = {};
@@ -141,9 +141,9 @@ __device__ void stream_mfma(const Problem &p, int local)
         for (int j = 0; j < UNROLL; ++j) w[j] = load_packed(blk + (int64_t)(u + kWaves * j) * 64);
 #pragma unroll
         for (int j = 0; j < UNROLL; ++j) {
-            const int8_t *qu = qrow + 64 * (u + kWaves * j);
-            qa[j] = rv ? *reinterpret_cast<const v4i *>(qu) : zero;
-            qb[j] = rv ? *reinterpret_cast<const v4i *>(qu + 32) : zero;
+            const BL_GLOBAL int8_t *qu = qrow + 64 * (u + kWaves * j);
+            qa[j] = rv ? *reinterpret_cast<const BL_GLOBAL v4i *>(qu) : zero;
+            qb[j] = rv ? *reinterpret_cast<const BL_GLOBAL v4i *>(qu + 32) : zero;
         }
 #pragma unroll
         for (int j = 0; j < UNROLL; ++j) {
@@ -155,9 +155,9 @@ __device__ void stream_mfma(const Problem &p, int local)
     }
     for (; u < u1; u += kWaves) {
         const v4u w = load_packed(blk + (int64_t)u * 64);
-        const int8_t *qu = qrow + 64 * u;
-        const v4i qa = rv ? *reinterpret_cast<const v4i *>(qu) : zero;
-        const v4i qb = rv ? *reinterpret_cast<const v4i *>(qu + 32) : zero;
+        const BL_GLOBAL int8_t *qu = qrow + 64 * u;
+        const v4i qa = rv ? *reinterpret_cast<const BL_GLOBAL v4i *>(qu) : zero;
+        const v4i qb = rv ? *reinterpret_cast<const BL_GLOBAL v4i *>(qu + 32) : zero;
         acc0 = mfma_i8(qa, planes(w.x), acc0);
         acc0 = mfma_i8(qb, planes(w.y), acc0);
         acc1 = mfma_i8(qa, planes(w.z), acc1);
@@ -193,7 +193,7 @@ __device__ void stream_mfma(const Problem &p, int local)
         if (p.ks == 1)
             finish_output(p, gamma, m, n, total);
         else
-            p.acc_ws[((int64_t)split * p.M + m) * ldp + n] = total;
+            gstore_ptr<int32_t>(p.acc_ws)[((int64_t)split * p.M + m) * ldp + n] = total;
     }
     if (p.ks == 1) return;
     if (!arrive_last(p, tile)) return;
@@ -202,7 +202,7 @@ __device__ void stream_mfma(const Problem &p, int local)
         const int n = 64 * tile + (idx & 63);
         if (n >= p.N) continue;
         int sum = 0;
-        for (int j = 0; j < p.ks; ++j) sum += p.acc_ws[((int64_t)j * p.M + m) * ldp + n];
+        for (int j = 0; j < p.ks; ++j) sum += gload_ptr<int32_t>(p.acc_ws)[((int64_t)j * p.M + m) * ldp + n];
         finish_output(p, gamma, m, n, sum);
     }
 }

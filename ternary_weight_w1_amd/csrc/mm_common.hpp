@@ -9,6 +9,7 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 
+
 // The four 2-bit planes of a packed word as four int8x4 words: plane j holds
 // the (code + 1) fields of codes 4j..4j+3 as bytes.  Together they are the
 // 16 consecutive fields of the word, in code order.
@@ -24,7 +25,7 @@ __device__ inline v4i planes(unsigned w)
 
 // Streaming read of one 16-byte slot of the packed weights (read once, so
 // marked non-temporal).
-__device__ inline v4u load_packed(const v4u *p) { return __builtin_nontemporal_load(p); }
+__device__ inline v4u load_packed(const BL_GLOBAL v4u *p) { return __builtin_nontemporal_load(p); }
 
 __device__ inline v16i mfma_i8(v4i a, v4i b, v16i c)
 {
@@ -37,11 +38,11 @@ __device__ inline v16i mfma_i8(v4i a, v4i b, v16i c)
 // recovered here, then y = float(acc) * ((gamma * a) / 127) in fp32.
 __device__ inline void finish_output(const Problem &p, float gamma, int m, int n, int32_t fields)
 {
-    const int32_t acc = fields - p.rowsum[m];
-    const float c = (gamma * p.absmax[m]) / 127.0f;
+    const int32_t acc = fields - gload_ptr<int32_t>(p.rowsum)[m];
+    const float c = (gamma * gload_ptr<float>(p.absmax)[m]) / 127.0f;
     const int64_t o = (int64_t)m * p.N + n;
-    p.Y[o] = (float)acc * c;
-    if (p.acc_out) p.acc_out[o] = acc;
+    gstore_ptr<float>(p.Y)[o] = (float)acc * c;
+    if (p.acc_out) gstore_ptr<int32_t>(p.acc_out)[o] = acc;
 }
 
 // Split-K arrival: every workgroup of a 64-row tile publishes its partial
