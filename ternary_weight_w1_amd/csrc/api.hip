@@ -59,8 +59,9 @@ int check_mnk(int64_t M, int64_t N, int64_t K)
 // Tuning knobs, read once from the environment (immutable afterwards).
 struct Knobs {
     int dot4_max_m = 1;          // M <= this takes the packed-dot4 kernel
+    int dot4_variant = 3;        // 0: global activations, 2/3: LDS-staged (unroll 4/8)
     int split_target = 1024;     // aim for at least this many workgroups
-    int xcd_order = 2;           // bit 0: streaming kernel, bit 1: tile kernel
+    int xcd_order = 3;           // bit 0: streaming kernel, bit 1: tile kernel
     int tile_variant = -1;       // force a tile-kernel instantiation (0..7)
 };
 const Knobs &knobs()
@@ -69,6 +70,7 @@ const Knobs &knobs()
         Knobs v;
         if (const char *s = getenv("BITLINEAR_DOT4_MAX_M")) v.dot4_max_m = atoi(s) > 0 ? 1 : 0;
         if (const char *s = getenv("BITLINEAR_SPLIT_TARGET")) v.split_target = atoi(s) > 0 ? atoi(s) : 1;
+        if (const char *s = getenv("BITLINEAR_DOT4_VARIANT")) v.dot4_variant = (atoi(s) == 0 || atoi(s) == 2) ? atoi(s) : 3;
         if (const char *s = getenv("BITLINEAR_XCD_ORDER")) v.xcd_order = atoi(s) & 3;
         if (const char *s = getenv("BITLINEAR_TILE_VARIANT")) v.tile_variant = (atoi(s) >= 0 && atoi(s) <= 7) ? atoi(s) : -1;
         return v;
@@ -134,7 +136,15 @@ int64_t items_of(const Problem &p)
     return p.kind == 0 ? (int64_t)p.NT * p.ks : (int64_t)p.mt * p.ntt;
 }
 
-int stream_variant_for(int64_t M) { return (M <= knobs().dot4_max_m) ? 0 : 1; }
+// The LDS-staged dot4 variants hold 64 bytes of activations per unit of
+// the workgroup's K range; longer ranges fall back to global activations.
+constexpr int kStreamLdsMax = 64 * 1024;
+int stream_variant_for(int64_t M, int64_t upsplit)
+{
+    if (M > knobs().dot4_max_m) return 1;
+    const int v = knobs().dot4_variant;
+    return (v != 0 && 64 * upsplit <= kStreamLdsMax) ? v : 0;
+}
 
 
 // Workspace layout of one problem: [Q][absmax][rowsum][partials][tickets],
@@ -185,7 +195,7 @@ Problem make_problem(int64_t M, int64_t N, int64_t K)
 
 hipError_t launch_contraction(const Problem &p, bool own_q, hipStream_t s)
 {
-    if (p.kind == 0) return bl::launch_stream_single(p, stream_variant_for(p.M), s);
+    if (p.kind == 0) return bl::launch_stream_single(p, stream_variant_for(p.M, p.upsplit), s);
     return bl::launch_tile_single(p, tile_variant(own_q), s);
 }
 
@@ -421,6 +431,7 @@ int build_group(const bitlinear_problem *in, int count, char *ws, GroupPlan &out
     if (base_items < 1) base_items = 1;
     int64_t tokens = 0, items_s = 0, items_t = 0, off = 0;
     bool all_m1 = true;
+    int64_t max_upsplit = 0;
     for (int i = 0; i < count; ++i) {
         const bitlinear_problem &q = in[i];
         Problem &p = out.probs[i];
@@ -450,6 +461,7 @@ int build_group(const bitlinear_problem *in, int count, char *ws, GroupPlan &out
             p.item_begin = (int32_t)items_s;
             items_s += items_of(p);
             all_m1 = all_m1 && p.M <= knobs().dot4_max_m;
+            max_upsplit = max_upsplit > p.upsplit ? max_upsplit : p.upsplit;
         } else {
             p.item_begin = (int32_t)items_t;
             items_t += items_of(p);
@@ -471,7 +483,8 @@ int build_group(const bitlinear_problem *in, int count, char *ws, GroupPlan &out
     if (knobs().xcd_order & 2) items_t = up(items_t, 8);
     h.n_items_stream = (int32_t)items_s;
     h.n_items_tile = (int32_t)items_t;
-    h.stream_variant = all_m1 ? 0 : 1;
+    h.stream_variant = all_m1 ? stream_variant_for(1, max_upsplit) : 1;
+    h.stream_lds = h.stream_variant >= 2 ? (int32_t)(64 * max_upsplit) : 0;
     h.tile_variant = tile_variant(true);
     h.ws_bytes = off;
     int64_t t = up(sizeof(bl::GroupHeader), 16);
@@ -563,7 +576,7 @@ int bitlinear_group_matmul(const void *table_host, const void *table_dev, void *
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (h.n_items_stream > 0)
         if (hipError_t e = bl::launch_stream_group(probs, reinterpret_cast<const uint2 *>(d + h.off_stream_map),
-                                                   h.n_items_stream, h.stream_variant, s))
+                                                   h.n_items_stream, h.stream_variant, h.stream_lds, s))
             return hip_fail(e, "group stream kernel");
     if (h.n_items_tile > 0)
         if (hipError_t e = bl::launch_tile_group(probs, reinterpret_cast<const uint2 *>(d + h.off_tile_map),

@@ -83,7 +83,8 @@ struct GroupHeader {
     int32_t dot4_items;     // unused by the kernels (diagnostics)
     int32_t stream_variant; // streaming kernel instantiation (see api.hip)
     int32_t tile_variant;   // tile kernel instantiation
-    int32_t pad_[3];
+    int32_t stream_lds;     // dynamic LDS bytes of the streaming kernel
+    int32_t pad_[2];
     int64_t ws_bytes;       // workspace the plan was built for
     int64_t off_probs;      // byte offsets inside the table
     int64_t off_tok_map;    // uint32 per token: problem index
@@ -110,7 +111,7 @@ hipError_t launch_quant_act_group(const Problem *probs, const uint32_t *tok_map,
 hipError_t launch_zero_words(uint32_t *p, int64_t n, hipStream_t s);
 hipError_t launch_stream_single(const Problem &p, int variant, hipStream_t s);
 hipError_t launch_stream_group(const Problem *probs, const uint2 *item_map, int n_items,
-                               int variant, hipStream_t s);
+                               int variant, int lds_bytes, hipStream_t s);
 hipError_t launch_tile_single(const Problem &p, int variant, hipStream_t s);
 hipError_t launch_tile_group(const Problem *probs, const uint2 *item_map, int n_items,
                              int variant, hipStream_t s);

@@ -48,7 +48,14 @@ __device__ inline int dot16(unsigned w, v4i q, int acc)
     return acc;
 }
 
-template <int UNROLL>
+// Activations of the workgroup's K range, staged once per workgroup when
+// the dot4 kernel runs with QLDS (dynamic LDS, 64 bytes per unit).
+extern __shared__ __attribute__((aligned(16))) int8_t stream_q_lds[];
+
+// QLDS: read the activations with broadcast LDS reads (2 distinct 16-byte
+// addresses per half wave) instead of two 16-byte global loads per lane per
+// unit, which would triple the vector-memory instructions of the stream.
+template <int UNROLL, bool QLDS>
 __device__ void stream_dot4(const Problem &p, int local)
 {
     __shared__ int red[kWaves][64];
@@ -57,7 +64,20 @@ __device__ void stream_dot4(const Problem &p, int local)
     const int u1 = min(p.KU, u0 + p.upsplit);
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 5;
     const BL_GLOBAL v4u *blk = gload_ptr<v4u>(p.P + (int64_t)tile * p.KU * kBlockBytes) + lane;
-    const BL_GLOBAL int8_t *q = gload_ptr<int8_t>(p.Q) + 16 * g;  // token 0; chunk g of each 32-code half
+    const BL_GLOBAL int8_t *qg = gload_ptr<int8_t>(p.Q) + 16 * g;  // token 0; chunk g of each 32-code half
+    if constexpr (QLDS) {
+        const BL_GLOBAL v4i *src = gload_ptr<v4i>(p.Q + 64 * u0);
+        v4i *dst = reinterpret_cast<v4i *>(stream_q_lds);
+        for (int i = threadIdx.x; i < 4 * (u1 - u0); i += kThreads) dst[i] = src[i];
+        __syncthreads();
+    }
+    // activation bytes 64*u + 16*g (+32 for the second half) of unit u
+    auto qload = [&](int u, int off) -> v4i {
+        if constexpr (QLDS)
+            return *reinterpret_cast<const v4i *>(stream_q_lds + 64 * (u - u0) + 16 * g + off);
+        else
+            return *reinterpret_cast<const BL_GLOBAL v4i *>(qg + 64 * u + off);
+    };
 
     int acc0 = 0, acc1 = 0;  // rows r and 32 + r of the tile
     int u = u0 + wave;
@@ -68,9 +88,8 @@ __device__ void stream_dot4(const Problem &p, int local)
         for (int j = 0; j < UNROLL; ++j) w[j] = load_packed(blk + (int64_t)(u + kWaves * j) * 64);
 #pragma unroll
         for (int j = 0; j < UNROLL; ++j) {
-            const BL_GLOBAL int8_t *qu = q + 64 * (u + kWaves * j);
-            qa[j] = *reinterpret_cast<const BL_GLOBAL v4i *>(qu);
-            qb[j] = *reinterpret_cast<const BL_GLOBAL v4i *>(qu + 32);
+            qa[j] = qload(u + kWaves * j, 0);
+            qb[j] = qload(u + kWaves * j, 32);
         }
 #pragma unroll
         for (int j = 0; j < UNROLL; ++j) {
@@ -82,9 +101,8 @@ __device__ void stream_dot4(const Problem &p, int local)
     }
     for (; u < u1; u += kWaves) {
         const v4u w = load_packed(blk + (int64_t)u * 64);
-        const BL_GLOBAL int8_t *qu = q + 64 * u;
-        const v4i qa = *reinterpret_cast<const BL_GLOBAL v4i *>(qu);
-        const v4i qb = *reinterpret_cast<const BL_GLOBAL v4i *>(qu + 32);
+        const v4i qa = qload(u, 0);
+        const v4i qb = qload(u, 32);
         acc0 = dot16(w.x, qa, acc0);
         acc0 = dot16(w.y, qb, acc0);
         acc1 = dot16(w.z, qa, acc1);
@@ -207,13 +225,19 @@ __device__ void stream_mfma(const Problem &p, int local)
     }
 }
 
+// 0: dot4, activations from global; 1: MFMA (2..32 tokens); 2: dot4 with
+// LDS-staged activations; 3: as 2 with 8 units in flight per wave.
 template <int V>
 __device__ inline void stream_body(const Problem &p, int local)
 {
     if constexpr (V == 0)
-        stream_dot4<4>(p, local);
-    else
+        stream_dot4<4, false>(p, local);
+    else if constexpr (V == 1)
         stream_mfma<2>(p, local);
+    else if constexpr (V == 2)
+        stream_dot4<4, true>(p, local);
+    else
+        stream_dot4<8, true>(p, local);
 }
 
 template <int V>
@@ -236,21 +260,27 @@ __global__ __launch_bounds__(kThreads) void stream_group_kernel(const Problem *_
 hipError_t launch_stream_single(const Problem &p, int variant, hipStream_t s)
 {
     const dim3 grid((unsigned)(p.NT * p.ks)), block(kThreads);
-    if (variant == 0)
-        hipLaunchKernelGGL(stream_single_kernel<0>, grid, block, 0, s, p);
-    else
-        hipLaunchKernelGGL(stream_single_kernel<1>, grid, block, 0, s, p);
+    const unsigned lds = variant >= 2 ? 64u * (unsigned)p.upsplit : 0u;
+    switch (variant) {
+    case 0: hipLaunchKernelGGL(stream_single_kernel<0>, grid, block, 0, s, p); break;
+    case 1: hipLaunchKernelGGL(stream_single_kernel<1>, grid, block, 0, s, p); break;
+    case 2: hipLaunchKernelGGL(stream_single_kernel<2>, grid, block, lds, s, p); break;
+    default: hipLaunchKernelGGL(stream_single_kernel<3>, grid, block, lds, s, p); break;
+    }
     return hipGetLastError();
 }
 
 hipError_t launch_stream_group(const Problem *probs, const uint2 *item_map, int n_items,
-                               int variant, hipStream_t s)
+                               int variant, int lds_bytes, hipStream_t s)
 {
     const dim3 grid((unsigned)n_items), block(kThreads);
-    if (variant == 0)
-        hipLaunchKernelGGL(stream_group_kernel<0>, grid, block, 0, s, probs, item_map);
-    else
-        hipLaunchKernelGGL(stream_group_kernel<1>, grid, block, 0, s, probs, item_map);
+    const unsigned lds = variant >= 2 ? (unsigned)lds_bytes : 0u;
+    switch (variant) {
+    case 0: hipLaunchKernelGGL(stream_group_kernel<0>, grid, block, 0, s, probs, item_map); break;
+    case 1: hipLaunchKernelGGL(stream_group_kernel<1>, grid, block, 0, s, probs, item_map); break;
+    case 2: hipLaunchKernelGGL(stream_group_kernel<2>, grid, block, lds, s, probs, item_map); break;
+    default: hipLaunchKernelGGL(stream_group_kernel<3>, grid, block, lds, s, probs, item_map); break;
+    }
     return hipGetLastError();
 }
 
