@@ -41,14 +41,6 @@ __device__ inline int block_sum_i32(int v, int *lds)
     return lds[0] + lds[1] + lds[2] + lds[3];
 }
 
-__device__ inline int8_t quant_code(float x, float s)
-{
-    float r = rintf(x * s);
-    r = r > 127.0f ? 127.0f : r;
-    r = r < -127.0f ? -127.0f : r;
-    return (int8_t)(int)r;
-}
-
 // Where code k of the row goes: row-major (Q + m*ldq + k) or fragment order.
 // In both layouts each aligned 16-code chunk is 16 contiguous bytes.
 struct QDest {

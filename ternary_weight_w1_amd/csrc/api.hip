@@ -60,6 +60,7 @@ int check_mnk(int64_t M, int64_t N, int64_t K)
 struct Knobs {
     int dot4_max_m = 1;          // M <= this takes the packed-dot4 kernel
     int dot4_variant = 3;        // 0: global activations, 2/3: LDS-staged (unroll 4/8)
+    int fuse_quant = 0;          // single-token problems quantize in the dot4 prologue
     int split_target = 1024;     // aim for at least this many workgroups
     int xcd_order = 3;           // bit 0: streaming kernel, bit 1: tile kernel
     int tile_variant = -1;       // force a tile-kernel instantiation (0..7)
@@ -71,6 +72,7 @@ const Knobs &knobs()
         if (const char *s = getenv("BITLINEAR_DOT4_MAX_M")) v.dot4_max_m = atoi(s) > 0 ? 1 : 0;
         if (const char *s = getenv("BITLINEAR_SPLIT_TARGET")) v.split_target = atoi(s) > 0 ? atoi(s) : 1;
         if (const char *s = getenv("BITLINEAR_DOT4_VARIANT")) v.dot4_variant = (atoi(s) == 0 || atoi(s) == 2) ? atoi(s) : 3;
+        if (const char *s = getenv("BITLINEAR_FUSE_QUANT")) v.fuse_quant = atoi(s) != 0;
         if (const char *s = getenv("BITLINEAR_XCD_ORDER")) v.xcd_order = atoi(s) & 3;
         if (const char *s = getenv("BITLINEAR_TILE_VARIANT")) v.tile_variant = (atoi(s) >= 0 && atoi(s) <= 7) ? atoi(s) : -1;
         return v;
@@ -366,6 +368,13 @@ int bitlinear_forward(const float *X, int64_t M, int64_t K, const uint8_t *P,
         p.tickets = reinterpret_cast<uint32_t *>(base + L.tick);
     }
     hipStream_t s = static_cast<hipStream_t>(stream);
+    if (p.kind == 0 && knobs().fuse_quant && stream_variant_for(p.M, p.upsplit) == 3) {
+        // one token: the dot4 kernel quantizes it in its prologue
+        if (p.tickets)
+            if (hipError_t e = bl::launch_zero_words(p.tickets, p.NT, s)) return hip_fail(e, "forward: zero tickets");
+        if (hipError_t e = bl::launch_stream_single(p, 4, s)) return hip_fail(e, "forward: fused matmul");
+        return BITLINEAR_OK;
+    }
     if (hipError_t e = bl::launch_quant_act(X, M, K, p.Q, p.ldq, p.qtiled, p.absmax, p.rowsum,
                                             p.tickets, p.tickets ? p.NT : 0, s))
         return hip_fail(e, "forward: quant_act");
@@ -430,8 +439,21 @@ int build_group(const bitlinear_problem *in, int count, char *ws, GroupPlan &out
     }
     if (base_items < 1) base_items = 1;
     int64_t tokens = 0, items_s = 0, items_t = 0, off = 0;
-    bool all_m1 = true;
+    // streaming instantiation for the whole launch: LDS-staged dot4 when every
+    // streaming problem has a single token (fused with the quantization when
+    // none of them splits K), MFMA otherwise
+    bool all_m1 = true, any_split = false;
     int64_t max_upsplit = 0;
+    for (int i = 0; i < count; ++i) {
+        Problem p = make_problem(in[i].M, in[i].N, in[i].K);
+        decompose(p, base_items, true);
+        if (p.kind != 0) continue;
+        all_m1 = all_m1 && p.M <= knobs().dot4_max_m;
+        any_split = any_split || p.ks > 1;
+        max_upsplit = max_upsplit > p.upsplit ? max_upsplit : p.upsplit;
+    }
+    int stream_variant = all_m1 ? stream_variant_for(1, max_upsplit) : 1;
+    if (stream_variant == 3 && knobs().fuse_quant && !any_split) stream_variant = 4;
     for (int i = 0; i < count; ++i) {
         const bitlinear_problem &q = in[i];
         Problem &p = out.probs[i];
@@ -455,13 +477,16 @@ int build_group(const bitlinear_problem *in, int count, char *ws, GroupPlan &out
             }
         }
         off += L.total;
-        p.tok_begin = (int32_t)tokens;
-        tokens += p.M;
+        // rows quantized by the separate kernel (fused problems do it inline)
+        if (!(p.kind == 0 && stream_variant == 4)) {
+            p.tok_begin = (int32_t)tokens;
+            tokens += p.M;
+        } else {
+            p.tok_begin = -1;
+        }
         if (p.kind == 0) {
             p.item_begin = (int32_t)items_s;
             items_s += items_of(p);
-            all_m1 = all_m1 && p.M <= knobs().dot4_max_m;
-            max_upsplit = max_upsplit > p.upsplit ? max_upsplit : p.upsplit;
         } else {
             p.item_begin = (int32_t)items_t;
             items_t += items_of(p);
@@ -469,10 +494,8 @@ int build_group(const bitlinear_problem *in, int count, char *ws, GroupPlan &out
         if (tokens >= (int64_t(1) << 31) || items_s >= (int64_t(1) << 31) || items_t >= (int64_t(1) << 31))
             return fail(BITLINEAR_ERR_SHAPE, "group: too many tokens or work items");
     }
-    // one instantiation per kernel and launch: every tile problem of a group
-    // takes the same tile variant (decompose picks it from the knobs alone);
-    // the streaming kernel runs MFMA unless every streaming problem has a
-    // single token
+    // every tile problem of a group takes the same tile variant (decompose
+    // picks it from the knobs alone)
     bl::GroupHeader &h = out.h;
     h.magic = bl::kGroupMagic;
     h.count = count;
@@ -483,7 +506,7 @@ int build_group(const bitlinear_problem *in, int count, char *ws, GroupPlan &out
     if (knobs().xcd_order & 2) items_t = up(items_t, 8);
     h.n_items_stream = (int32_t)items_s;
     h.n_items_tile = (int32_t)items_t;
-    h.stream_variant = all_m1 ? stream_variant_for(1, max_upsplit) : 1;
+    h.stream_variant = stream_variant;
     h.stream_lds = h.stream_variant >= 2 ? (int32_t)(64 * max_upsplit) : 0;
     h.tile_variant = tile_variant(true);
     h.ws_bytes = off;
@@ -546,7 +569,8 @@ int bitlinear_group_plan(const bitlinear_problem *probs, int count, void *ws, si
     uint32_t *tok = reinterpret_cast<uint32_t *>(t + g.h.off_tok_map);
     for (int i = 0; i < count; ++i) {
         const Problem &p = g.probs[i];
-        for (int m = 0; m < p.M; ++m) tok[p.tok_begin + m] = (uint32_t)i;
+        if (p.tok_begin >= 0)
+            for (int m = 0; m < p.M; ++m) tok[p.tok_begin + m] = (uint32_t)i;
     }
     fill_map(g.probs, 0, g.items_s, g.h.n_items_stream, knobs().xcd_order & 1,
              reinterpret_cast<uint32_t *>(t + g.h.off_stream_map));
@@ -560,6 +584,7 @@ int bitlinear_group_quant_act(const void *table_host, const void *table_dev, voi
     bl::GroupHeader h;
     if (int st = read_header(table_host, table_dev, h)) return st;
     const char *d = static_cast<const char *>(table_dev);
+    if (h.n_tokens == 0) return BITLINEAR_OK;  // every problem quantizes in its contraction kernel
     if (hipError_t e = bl::launch_quant_act_group(reinterpret_cast<const Problem *>(d + h.off_probs),
                                                   reinterpret_cast<const uint32_t *>(d + h.off_tok_map),
                                                   h.n_tokens, static_cast<hipStream_t>(stream)))

@@ -24,6 +24,19 @@ __device__ inline BL_GLOBAL T *gstore_ptr(void *p)
     return (BL_GLOBAL T *)p;
 }
 
+// int8 code of one activation: clamp(rint(x * s), -127, 127) with s = 127 / a
+// computed once per token (anthology note-168 on arXiv 2402.17764, "What it
+// does": 8-bit activations; per-token absmax scaling is the reading taken).
+// The only definition in the library: the quantization kernel and the fused
+// decode prologue both call it.
+__device__ inline int8_t quant_code(float x, float s)
+{
+    float r = rintf(x * s);
+    r = r > 127.0f ? 127.0f : r;
+    r = r < -127.0f ? -127.0f : r;
+    return (int8_t)(int)r;
+}
+
 // BL2-T64 geometry: 64-row tiles, 64-code units, 1 KiB blocks.
 constexpr int kTileRows = 64;
 constexpr int kUnitCodes = 64;

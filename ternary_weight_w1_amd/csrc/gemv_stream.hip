@@ -52,12 +52,73 @@ __device__ inline int dot16(unsigned w, v4i q, int acc)
 // the dot4 kernel runs with QLDS (dynamic LDS, 64 bytes per unit).
 extern __shared__ __attribute__((aligned(16))) int8_t stream_q_lds[];
 
+// Fused prologue (decode, one token): quantize the token's fp32 activations
+// straight into LDS -- absmax over the whole row (block reduction), then
+// the same per-element code as the quantization kernel -- keeping the codes
+// of units [u0, u1) and the row sum of all of them.  Replaces a separate
+// quantization launch; the row is re-read from L1/L2 in the second pass.
+__device__ void fused_quant_token(const Problem &p, int u0, int u1, float &absmax, int &rowsum)
+{
+    __shared__ float fmax_l[kWaves];
+    __shared__ int isum_l[kWaves];
+    const int tid = threadIdx.x, K = p.K;
+    const BL_GLOBAL float *x = gload_ptr<float>(p.X);
+    typedef float v4f __attribute__((ext_vector_type(4)));
+    const bool vec = ((K & 3) == 0) && ((reinterpret_cast<uintptr_t>(p.X) & 15) == 0);
+    const BL_GLOBAL v4f *x4 = reinterpret_cast<const BL_GLOBAL v4f *>(x);
+    float a = 0.0f;
+    if (vec) {
+        for (int i = tid; i < (K >> 2); i += kThreads) {
+            const v4f w = x4[i];
+            a = fmaxf(a, fmaxf(fmaxf(fabsf(w.x), fabsf(w.y)), fmaxf(fabsf(w.z), fabsf(w.w))));
+        }
+    } else {
+        for (int i = tid; i < K; i += kThreads) a = fmaxf(a, fabsf(x[i]));
+    }
+    for (int off = 32; off > 0; off >>= 1) a = fmaxf(a, __shfl_xor(a, off, 64));
+    if ((tid & 63) == 0) fmax_l[tid >> 6] = a;
+    __syncthreads();
+    a = fmaxf(fmaxf(fmax_l[0], fmax_l[1]), fmaxf(fmax_l[2], fmax_l[3]));
+    if (!(a >= 1e-5f)) a = 1e-5f;
+    const float s = 127.0f / a;
+
+    const int k0 = 64 * u0, k1 = 64 * u1;  // LDS holds codes k0 .. k1-1
+    int sum = 0;
+    if (vec) {
+        for (int i = tid; i < (K >> 2); i += kThreads) {
+            const v4f w = x4[i];
+            const int8_t c0 = quant_code(w.x, s), c1 = quant_code(w.y, s);
+            const int8_t c2 = quant_code(w.z, s), c3 = quant_code(w.w, s);
+            sum += (int)c0 + (int)c1 + (int)c2 + (int)c3;
+            const int k = 4 * i;
+            if (k >= k0 && k < k1)
+                *reinterpret_cast<uint32_t *>(stream_q_lds + (k - k0)) =
+                    (uint32_t)(uint8_t)c0 | ((uint32_t)(uint8_t)c1 << 8) |
+                    ((uint32_t)(uint8_t)c2 << 16) | ((uint32_t)(uint8_t)c3 << 24);
+        }
+    } else {
+        for (int k = tid; k < K; k += kThreads) {
+            const int8_t c = quant_code(x[k], s);
+            sum += c;
+            if (k >= k0 && k < k1) stream_q_lds[k - k0] = c;
+        }
+    }
+    for (int k = (K > k0 ? K : k0) + tid; k < k1; k += kThreads) stream_q_lds[k - k0] = 0;
+    for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off, 64);
+    if ((tid & 63) == 0) isum_l[tid >> 6] = sum;
+    __syncthreads();
+    absmax = a;
+    rowsum = isum_l[0] + isum_l[1] + isum_l[2] + isum_l[3];
+}
+
 // QLDS: read the activations with broadcast LDS reads (2 distinct 16-byte
 // addresses per half wave) instead of two 16-byte global loads per lane per
 // unit, which would triple the vector-memory instructions of the stream.
-template <int UNROLL, bool QLDS>
+// FUSED: the activations are quantized in the prologue (implies QLDS).
+template <int UNROLL, bool QLDS, bool FUSED = false>
 __device__ void stream_dot4(const Problem &p, int local)
 {
+    static_assert(!FUSED || QLDS, "the fused prologue writes the LDS activations");
     __shared__ int red[kWaves][64];
     const int tile = local / p.ks, split = local - tile * p.ks;
     const int u0 = split * p.upsplit;
@@ -65,12 +126,22 @@ __device__ void stream_dot4(const Problem &p, int local)
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 5;
     const BL_GLOBAL v4u *blk = gload_ptr<v4u>(p.P + (int64_t)tile * p.KU * kBlockBytes) + lane;
     const BL_GLOBAL int8_t *qg = gload_ptr<int8_t>(p.Q) + 16 * g;  // token 0; chunk g of each 32-code half
-    if constexpr (QLDS) {
+    float tok_absmax = 0.0f;
+    int tok_rowsum = 0;
+    if constexpr (FUSED) {
+        fused_quant_token(p, u0, u1, tok_absmax, tok_rowsum);
+    } else if constexpr (QLDS) {
         const BL_GLOBAL v4i *src = gload_ptr<v4i>(p.Q + 64 * u0);
         v4i *dst = reinterpret_cast<v4i *>(stream_q_lds);
         for (int i = threadIdx.x; i < 4 * (u1 - u0); i += kThreads) dst[i] = src[i];
         __syncthreads();
     }
+    auto finish = [&](int n, int32_t fields, float gamma) {
+        if constexpr (FUSED)
+            finish_output_with(p, gamma, 0, n, fields, tok_rowsum, tok_absmax);
+        else
+            finish_output(p, gamma, 0, n, fields);
+    };
     // activation bytes 64*u + 16*g (+32 for the second half) of unit u
     auto qload = [&](int u, int off) -> v4i {
         if constexpr (QLDS)
@@ -123,7 +194,7 @@ __device__ void stream_dot4(const Problem &p, int local)
     int total = 0;
     if (t < 64) total = red[0][t] + red[1][t] + red[2][t] + red[3][t];
     if (p.ks == 1) {
-        if (t < 64 && n < p.N) finish_output(p, gamma, 0, n, total);
+        if (t < 64 && n < p.N) finish(n, total, gamma);
         return;
     }
     const int64_t ldp = (int64_t)p.NT * 64;  // partial row stride
@@ -132,7 +203,7 @@ __device__ void stream_dot4(const Problem &p, int local)
     if (t < 64 && n < p.N) {
         int sum = 0;
         for (int j = 0; j < p.ks; ++j) sum += gload_ptr<int32_t>(p.acc_ws)[(int64_t)j * p.M * ldp + n];
-        finish_output(p, gamma, 0, n, sum);
+        finish(n, sum, gamma);
     }
 }
 
@@ -226,7 +297,8 @@ __device__ void stream_mfma(const Problem &p, int local)
 }
 
 // 0: dot4, activations from global; 1: MFMA (2..32 tokens); 2: dot4 with
-// LDS-staged activations; 3: as 2 with 8 units in flight per wave.
+// LDS-staged activations; 3: as 2 with 8 units in flight per wave; 4: as 3
+// with the activation quantization fused into the prologue.
 template <int V>
 __device__ inline void stream_body(const Problem &p, int local)
 {
@@ -236,8 +308,10 @@ __device__ inline void stream_body(const Problem &p, int local)
         stream_mfma<2>(p, local);
     else if constexpr (V == 2)
         stream_dot4<4, true>(p, local);
-    else
+    else if constexpr (V == 3)
         stream_dot4<8, true>(p, local);
+    else
+        stream_dot4<8, true, true>(p, local);
 }
 
 template <int V>
@@ -265,7 +339,8 @@ hipError_t launch_stream_single(const Problem &p, int variant, hipStream_t s)
     case 0: hipLaunchKernelGGL(stream_single_kernel<0>, grid, block, 0, s, p); break;
     case 1: hipLaunchKernelGGL(stream_single_kernel<1>, grid, block, 0, s, p); break;
     case 2: hipLaunchKernelGGL(stream_single_kernel<2>, grid, block, lds, s, p); break;
-    default: hipLaunchKernelGGL(stream_single_kernel<3>, grid, block, lds, s, p); break;
+    case 3: hipLaunchKernelGGL(stream_single_kernel<3>, grid, block, lds, s, p); break;
+    default: hipLaunchKernelGGL(stream_single_kernel<4>, grid, block, lds, s, p); break;
     }
     return hipGetLastError();
 }
@@ -279,7 +354,8 @@ hipError_t launch_stream_group(const Problem *probs, const uint2 *item_map, int 
     case 0: hipLaunchKernelGGL(stream_group_kernel<0>, grid, block, 0, s, probs, item_map); break;
     case 1: hipLaunchKernelGGL(stream_group_kernel<1>, grid, block, 0, s, probs, item_map); break;
     case 2: hipLaunchKernelGGL(stream_group_kernel<2>, grid, block, lds, s, probs, item_map); break;
-    default: hipLaunchKernelGGL(stream_group_kernel<3>, grid, block, lds, s, probs, item_map); break;
+    case 3: hipLaunchKernelGGL(stream_group_kernel<3>, grid, block, lds, s, probs, item_map); break;
+    default: hipLaunchKernelGGL(stream_group_kernel<4>, grid, block, lds, s, probs, item_map); break;
     }
     return hipGetLastError();
 }

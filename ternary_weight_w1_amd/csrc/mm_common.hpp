@@ -36,13 +36,20 @@ __device__ inline v16i mfma_i8(v4i a, v4i b, v16i c)
 // the layer replaces nn.Linear, so it returns real values).  The kernels
 // accumulate sum_k (t+1) q = acc + rowsum; the exact integer acc is
 // recovered here, then y = float(acc) * ((gamma * a) / 127) in fp32.
-__device__ inline void finish_output(const Problem &p, float gamma, int m, int n, int32_t fields)
+__device__ inline void finish_output_with(const Problem &p, float gamma, int m, int n, int32_t fields,
+                                          int32_t rowsum, float absmax)
 {
-    const int32_t acc = fields - gload_ptr<int32_t>(p.rowsum)[m];
-    const float c = (gamma * gload_ptr<float>(p.absmax)[m]) / 127.0f;
+    const int32_t acc = fields - rowsum;
+    const float c = (gamma * absmax) / 127.0f;
     const int64_t o = (int64_t)m * p.N + n;
     gstore_ptr<float>(p.Y)[o] = (float)acc * c;
     if (p.acc_out) gstore_ptr<int32_t>(p.acc_out)[o] = acc;
+}
+
+__device__ inline void finish_output(const Problem &p, float gamma, int m, int n, int32_t fields)
+{
+    finish_output_with(p, gamma, m, n, fields, gload_ptr<int32_t>(p.rowsum)[m],
+                       gload_ptr<float>(p.absmax)[m]);
 }
 
 // Split-K arrival: every workgroup of a 64-row tile publishes its partial

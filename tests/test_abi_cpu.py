@@ -136,7 +136,7 @@ def test_group_plan_table_on_host():
     hdr = np.frombuffer(host[:48].tobytes(), np.int32)
     assert hdr[0] == np.int32(np.uint32(0xB17E0001).astype(np.int32))
     assert hdr[1] == 4            # problems
-    assert hdr[2] == 4            # tokens (M = 1 each)
+    assert hdr[2] in (0, 4)       # tokens quantized by the separate kernel (0 when fused)
     items = sum((N + 63) // 64 for _, N, _ in specs)
     assert hdr[3] >= items        # streaming work items (K splits may add more)
     assert hdr[4] == 0            # no tile-kernel items at M = 1
@@ -148,6 +148,32 @@ def test_group_plan_table_on_host():
     bad = _problems(specs + [(1, 0, 64)])
     assert L.bitlinear_group_table_bytes(bad, 5) == 0
     assert L.bitlinear_group_plan(bad, 5, FAKE, wsb, host.ctypes.data, tb) == -2
+
+
+def test_group_plan_single_token_quantization():
+    # 16 single-token problems with 64 row tiles each (no K split): every
+    # token goes to the quantization kernel and the dot4 kernel reads LDS-
+    # staged activations (3), or -- with BITLINEAR_FUSE_QUANT=1 -- the dot4
+    # kernel quantizes in its prologue (4) and no token is left over; a
+    # 2-token problem switches the streaming kernel to MFMA (1)
+    L = B.lib()
+    fused = os.environ.get("BITLINEAR_FUSE_QUANT", "0") not in ("", "0")
+    specs = [(1, 4096, 256)] * 16
+    arr = _problems(specs)
+    tb = L.bitlinear_group_table_bytes(arr, 16)
+    host = np.zeros(tb, np.uint8)
+    wsb = L.bitlinear_group_workspace_bytes(arr, 16)
+    assert L.bitlinear_group_plan(arr, 16, FAKE, wsb, host.ctypes.data, tb) == 0
+    hdr = np.frombuffer(host[:48].tobytes(), np.int32)
+    assert hdr[3] == 16 * 64
+    assert (hdr[2], hdr[7]) == ((0, 4) if fused else (16, 3))
+    arr2 = _problems(specs + [(2, 64, 64)])
+    tb2 = L.bitlinear_group_table_bytes(arr2, 17)
+    host2 = np.zeros(tb2, np.uint8)
+    wsb2 = L.bitlinear_group_workspace_bytes(arr2, 17)
+    assert L.bitlinear_group_plan(arr2, 17, FAKE, wsb2, host2.ctypes.data, tb2) == 0
+    hdr2 = np.frombuffer(host2[:48].tobytes(), np.int32)
+    assert hdr2[2] == 18 and hdr2[7] == 1
 
 
 def test_group_calls_reject_foreign_tables():

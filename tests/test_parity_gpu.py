@@ -255,6 +255,17 @@ def test_forward_parity_and_determinism(B, M, N, K):
     assert torch.equal(Y1, Y2) and torch.equal(acc1, acc2)
 
 
+@pytest.mark.parametrize("N,K", [(640, 512), (100, 37), (300, 130), (2560, 6912)])
+def test_forward_single_token(B, N, K):
+    # one token through the dot4 kernel, with and without K splits
+    say("forward M=1", N, K)
+    T = synth.random_ternary(N, K, seed=N + K)
+    X = synth.activations_np(1, K, seed=K, outlier_frac=0.01)
+    ref = O.forward(X, T, np.float32(0.031))
+    Y, acc = B.forward(dev(X), dev(O.pack(T)), gamma_dev(0.031), N, with_acc=True)
+    check_outputs(host(Y), host(acc), ref["acc"], 0.031, ref["absmax"], "fused")
+
+
 def test_forward_rejects_small_workspace(B):
     Xd = dev(np.zeros((2, 64), np.float32))
     Pd = dev(np.full(B.packed_bytes(64, 64), 0x55, np.uint8))
@@ -289,6 +300,52 @@ def _group_run(B, specs, seed0):
 def test_group_all_single_token(B):
     say("group M=1")
     _group_run(B, [(1, 640, 2560), (1, 100, 200), (1, 2560, 640), (1, 64, 64)], 500)
+
+
+def test_group_single_token_no_split(B):
+    # enough row tiles that no problem splits K (the benchmark's regime)
+    say("group M=1 no split")
+    specs = [(1, 4096, 256)] * 14 + [(1, 4100, 200), (1, 4000, 37)]
+    _group_run(B, specs, 700)
+
+
+FUSED_SCRIPT = r'''
+import numpy as np, torch, sys
+sys.path.insert(0, ".")
+import oracle as O, synth, ternary_weight_w1_amd as B
+dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+def check(Y, acc, ref):
+    assert np.array_equal(acc, ref["acc"]) and np.array_equal(Y, ref["Y"])
+for N, K in [(640, 512), (100, 37), (2560, 6912)]:
+    T = synth.random_ternary(N, K, seed=N + K); X = synth.activations_np(1, K, seed=K, outlier_frac=0.01)
+    ref = O.forward(X, T, np.float32(0.031))
+    Y, acc = B.forward(dev(X), dev(O.pack(T)), dev(np.array([0.031], np.float32)), N, with_acc=True)
+    torch.cuda.synchronize(); check(Y.cpu().numpy(), acc.cpu().numpy(), ref)
+probs, refs = [], []
+for i, (M, N, K) in enumerate([(1, 4096, 256)] * 14 + [(1, 4100, 200), (1, 4000, 37)]):
+    T = synth.random_ternary(N, K, seed=800 + i); X = synth.activations_np(M, K, seed=900 + i)
+    refs.append(O.forward(X, T, np.float32(0.02)))
+    probs.append(dict(X=dev(X), P=dev(O.pack(T)), gamma=dev(np.array([0.02], np.float32)),
+                      Y=torch.empty((M, N), device="cuda"), acc=torch.empty((M, N), dtype=torch.int32, device="cuda"), N=N))
+plan = B.GroupPlan(probs)
+assert int(np.frombuffer(plan.table_host.numpy()[:48].tobytes(), np.int32)[7]) == 4
+plan.forward(); torch.cuda.synchronize()
+for p, ref in zip(probs, refs):
+    check(p["Y"].cpu().numpy(), p["acc"].cpu().numpy(), ref)
+print("fused ok")
+'''
+
+
+def test_fused_quant_prologue_subprocess(B):
+    # the dot4 kernel variant that quantizes the token in its prologue
+    # (BITLINEAR_FUSE_QUANT=1, a process-wide knob, hence one child process)
+    say("fused-quant prologue (child process)")
+    import os
+    import subprocess
+    env = dict(os.environ, BITLINEAR_FUSE_QUANT="1")
+    r = subprocess.run([sys.executable, "-c", FUSED_SCRIPT], env=env, capture_output=True,
+                       text=True, timeout=110)
+    assert r.returncode == 0 and "fused ok" in r.stdout, r.stdout + r.stderr
 
 
 def test_group_mixed(B):
