@@ -63,7 +63,7 @@ struct Knobs {
     int fuse_quant = 0;          // single-token problems quantize in the dot4 prologue
     int split_target = 1024;     // aim for at least this many workgroups
     int xcd_order = 3;           // bit 0: streaming kernel, bit 1: tile kernel
-    int tile_variant = -1;       // force a tile-kernel instantiation (0..7)
+    int tile_variant = -1;       // force a tile-kernel instantiation (0..9)
 };
 const Knobs &knobs()
 {
@@ -74,7 +74,7 @@ const Knobs &knobs()
         if (const char *s = getenv("BITLINEAR_DOT4_VARIANT")) v.dot4_variant = (atoi(s) == 0 || atoi(s) == 2) ? atoi(s) : 3;
         if (const char *s = getenv("BITLINEAR_FUSE_QUANT")) v.fuse_quant = atoi(s) != 0;
         if (const char *s = getenv("BITLINEAR_XCD_ORDER")) v.xcd_order = atoi(s) & 3;
-        if (const char *s = getenv("BITLINEAR_TILE_VARIANT")) v.tile_variant = (atoi(s) >= 0 && atoi(s) <= 7) ? atoi(s) : -1;
+        if (const char *s = getenv("BITLINEAR_TILE_VARIANT")) v.tile_variant = (atoi(s) >= 0 && atoi(s) <= 13) ? atoi(s) : -1;
         return v;
     }();
     return k;
@@ -88,7 +88,7 @@ const Knobs &knobs()
 int tile_variant(bool own_q)
 {
     int v = knobs().tile_variant;
-    if (v < 0) v = 2;
+    if (v < 0) v = 11;
     if (!own_q) {  // caller-supplied activations are row-major
         if (v == 3) return 4;
         if (v == 5) return 2;
@@ -97,8 +97,8 @@ int tile_variant(bool own_q)
     }
     return v;
 }
-int tile_bm(int variant) { return (variant == 0 || variant == 6) ? 64 : 128; }
-bool tile_frag(int variant) { return variant == 3 || variant >= 5; }
+int tile_bm(int variant) { return (variant == 0 || variant == 6 || variant == 8) ? 64 : 128; }
+bool tile_frag(int variant) { return variant == 3 || (variant >= 5 && variant <= 7); }
 
 // Kernel kind and decomposition of one problem.  `base_items` is the number
 // of streaming work items the whole launch has without K splits; splits are

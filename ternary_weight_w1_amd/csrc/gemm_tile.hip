@@ -30,25 +30,43 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kLda = 80;  // padded LDS row stride of the activation tile
+typedef float v4f_t __attribute__((ext_vector_type(4)));
 constexpr int kDepth = 3; // units of global-load lookahead
 
 // WMS: 32-token subtiles per wave; WNT: 64-row weight tiles per wave;
 // WAVES_M x (4 / WAVES_M) waves.  The workgroup covers BM = WAVES_M*WMS*32
 // tokens and always 256 weight rows.
-// FRAG: the activations arrive in fragment order (see qf32_offset) and are
-// staged into LDS unchanged, so the global loads are whole 1 KiB blocks and
-// both the LDS writes and the operand reads are linear (conflict-free,
-// unpadded); otherwise row-major activations are staged into padded rows.
-template <int WMS, int WNT, int WAVES_M, bool FRAG>
+// Activation staging (ALAY):
+//   0  row-major activations -> LDS rows padded to 80 bytes;
+//   1  fragment-ordered activations (see qf32_offset) -> LDS unchanged: the
+//      global loads are whole 1 KiB blocks;
+//   2  row-major activations -> LDS in fragment order: each wave instruction
+//      fills one 1 KiB operand fragment (32 rows x 32 bytes from global).
+// In 1 and 2 the LDS writes and the operand reads are linear (conflict-free,
+// no padding).
+// EPI: the rescaled outputs go through LDS, 32 rows at a time per wave, so
+// that Y is written with 16-byte stores covering whole 256-byte row pieces
+// instead of one 4-byte store per accumulator element.
+// Output stores are non-temporal: the fp32 result (M*N*4 bytes, the largest
+// stream of the kernel) is written once and must not evict the activation
+// and weight tiles that other workgroups still reuse from L2.
+constexpr int kEpiStride = 72;  // floats per LDS row of the epilogue transpose
+
+template <int WMS, int WNT, int WAVES_M, int ALAY, bool EPI = false>
 __device__ void tile_body(const Problem &p, int local)
 {
+    constexpr bool FRAG = ALAY != 0;
     constexpr int WAVES_N = 4 / WAVES_M;
     static_assert(WAVES_N * WNT == 4, "a workgroup spans 256 weight rows");
     constexpr int BM = WAVES_M * WMS * 32;
     constexpr int CH = BM * 4 / kThreads;  // 16-byte activation chunks per thread per unit
     static_assert(CH >= 1, "tile too small for the staging pattern");
     constexpr int kRowBytes = FRAG ? 64 : kLda;
-    __shared__ __attribute__((aligned(16))) int8_t As[2][BM * kRowBytes];
+    constexpr int kStageBytes = BM * kRowBytes;
+    constexpr int kEpiBytes = EPI ? 4 * 32 * kEpiStride * 4 : 0;
+    constexpr int kSmem = 2 * kStageBytes > kEpiBytes ? 2 * kStageBytes : kEpiBytes;
+    __shared__ __attribute__((aligned(16))) int8_t smem[kSmem];
+    int8_t (*As)[kStageBytes] = reinterpret_cast<int8_t (*)[kStageBytes]>(smem);
     __shared__ float cs[BM];
     __shared__ int rsum[BM];
 
@@ -83,9 +101,16 @@ __device__ void tile_body(const Problem &p, int local)
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
         const int c = tid + kThreads * i;
-        if constexpr (FRAG) {
+        if constexpr (ALAY == 1) {
             const int64_t b = min((m0 >> 5) + (c >> 7), ((p.M + 31) >> 5) - 1);
             asrc[i] = gload_ptr<int8_t>(p.Q + b * KU * 2048 + 16 * (c & 127));
+            adst[i] = 16 * c;
+        } else if constexpr (ALAY == 2) {
+            // fragment f = c / 64 = (32-row block, half), lane l = c % 64:
+            // row 32*(f/2) + l%32, 16 bytes at 32*(f%2) + 16*(l/32) of the unit
+            const int f = c >> 6, l = c & 63;
+            const int m = min(m0 + 32 * (f >> 1) + (l & 31), p.M - 1);
+            asrc[i] = gload_ptr<int8_t>(p.Q + (int64_t)m * p.ldq + 32 * (f & 1) + 16 * (l >> 5));
             adst[i] = 16 * c;
         } else {
             const int m = min(m0 + (c >> 2), p.M - 1);
@@ -93,7 +118,7 @@ __device__ void tile_body(const Problem &p, int local)
             adst[i] = (c >> 2) * kLda + 16 * (c & 3);
         }
     }
-    astep = FRAG ? 2048 : 64;
+    astep = ALAY == 1 ? 2048 : 64;
 
     __syncthreads();  // the previous work item of this workgroup may still read LDS
     if (tid < BM) {
@@ -178,6 +203,46 @@ __device__ void tile_body(const Problem &p, int local)
     for (int s = 0; s < kDepth - 1; ++s)
         if (u0 + s < KU) step(s, u0 + s);
 
+    if constexpr (EPI) {
+        __syncthreads();  // every wave is done with the activation stages
+        float *ep = reinterpret_cast<float *>(smem) + wave * (32 * kEpiStride);
+        const bool vec_ok = (p.N & 3) == 0;  // 16-byte aligned output rows
+        BL_GLOBAL float *Y = gstore_ptr<float>(p.Y);
+#pragma unroll
+        for (int j = 0; j < WNT; ++j) {
+#pragma unroll
+            for (int i = 0; i < WMS; ++i) {
+#pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        const int row = 8 * (e >> 2) + 4 * g + (e & 3);
+                        const int rr = arow0 + 32 * i + row;
+                        ep[row * kEpiStride + 32 * s2 + r] = (float)(acc[i][2 * j + s2][e] - rsum[rr]) * cs[rr];
+                    }
+                // 16 lanes per 64-float row piece, 4 rows per pass, 8 passes
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    const int row = (lane >> 4) + 4 * k;
+                    const int c4 = 4 * (lane & 15);
+                    const int m = m0 + arow0 + 32 * i + row;
+                    const int n = 64 * tile[j] + c4;
+                    const v4f_t v = *reinterpret_cast<const v4f_t *>(&ep[row * kEpiStride + c4]);
+                    if (tv[j] && m < p.M) {
+                        const int64_t o = (int64_t)m * p.N + n;
+                        if (vec_ok && n + 3 < p.N) {
+                            __builtin_nontemporal_store(v, reinterpret_cast<BL_GLOBAL v4f_t *>(Y + o));
+                        } else {
+                            if (n < p.N) __builtin_nontemporal_store(v.x, Y + o);
+                            if (n + 1 < p.N) __builtin_nontemporal_store(v.y, Y + o + 1);
+                            if (n + 2 < p.N) __builtin_nontemporal_store(v.z, Y + o + 2);
+                            if (n + 3 < p.N) __builtin_nontemporal_store(v.w, Y + o + 3);
+                        }
+                    }
+                }
+            }
+        }
+    }
 #pragma unroll
     for (int j = 0; j < WNT; ++j) {
         if (!tv[j]) continue;
@@ -194,13 +259,362 @@ __device__ void tile_body(const Problem &p, int local)
                     if (m < p.M) {
                         const int32_t a = acc[i][2 * j + s2][e] - rsum[row];
                         const int64_t o = (int64_t)m * p.N + n;
-                        gstore_ptr<float>(p.Y)[o] = (float)a * cs[row];
+                        if constexpr (!EPI)
+                            __builtin_nontemporal_store((float)a * cs[row], gstore_ptr<float>(p.Y) + o);
                         if (p.acc_out) gstore_ptr<int32_t>(p.acc_out)[o] = a;
                     }
                 }
             }
         }
     }
+}
+
+// Software-pipelined variant (row-major activations, four waves along N,
+// WMS 32-token subtiles per wave).  The activation tile goes through a
+// three-stage LDS ring: while the MFMAs of unit u run, each wave already
+// reads unit u+1's operands from LDS and unpacks its weight planes, stores
+// unit u+2's activations into the third stage, and issues the global loads
+// of unit u+4 (activations) and u+3 (weights).  One barrier per unit.
+template <int WMS>
+__device__ void tile_pipe_body(const Problem &p, int local)
+{
+    constexpr int BM = 32 * WMS;
+    constexpr int CH = BM * 4 / kThreads;
+    static_assert(CH >= 1, "tile too small for the staging pattern");
+    __shared__ __attribute__((aligned(16))) int8_t As[3][BM * kLda];
+    __shared__ float cs[BM];
+    __shared__ int rsum[BM];
+
+    const int mtile = local % p.mt;
+    const int nt = local / p.mt;
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63, g = lane >> 5, r = lane & 31;
+    const int m0 = mtile * BM;
+    const int KU = p.KU;
+    const int tile = 4 * nt + wave;
+    const bool tv = tile < p.NT;
+    const BL_GLOBAL v4u *blk = gload_ptr<v4u>(p.P + (int64_t)min(tile, p.NT - 1) * KU * kBlockBytes) + lane;
+
+    const BL_GLOBAL int8_t *asrc[CH];
+    int adst[CH];
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+        const int c = tid + kThreads * i;
+        const int m = min(m0 + (c >> 2), p.M - 1);
+        asrc[i] = gload_ptr<int8_t>(p.Q + (int64_t)m * p.ldq + 16 * (c & 3));
+        adst[i] = (c >> 2) * kLda + 16 * (c & 3);
+    }
+    if (tid < BM) {
+        const int m = min(m0 + tid, p.M - 1);
+        cs[tid] = (*gload_ptr<float>(p.gamma) * gload_ptr<float>(p.absmax)[m]) / 127.0f;
+        rsum[tid] = gload_ptr<int32_t>(p.rowsum)[m];
+    }
+
+    // register rings (slot = unit % 3): activation chunks of units u+2..u+4,
+    // packed weights of units u+1..u+3
+    v4i ar[3][CH];
+    v4u br[3];
+    auto load_a = [&](int slot, int u) {
+        const int uc = min(u, KU - 1);
+#pragma unroll
+        for (int i = 0; i < CH; ++i) ar[slot][i] = *reinterpret_cast<const BL_GLOBAL v4i *>(asrc[i] + 64 * uc);
+    };
+    auto load_b = [&](int slot, int u) { br[slot] = blk[(int64_t)min(u, KU - 1) * 64]; };
+    auto store_a = [&](int stage, int slot) {
+#pragma unroll
+        for (int i = 0; i < CH; ++i) *reinterpret_cast<v4i *>(&As[stage][adst[i]]) = ar[slot][i];
+    };
+    v4i fa[2][WMS][2];  // activation operands of the current / next unit
+    v4i fb[2][4];       // weight planes of the current / next unit
+    auto read_a = [&](int buf, int stage) {
+#pragma unroll
+        for (int i = 0; i < WMS; ++i) {
+            const int8_t *arow = &As[stage][(32 * i + r) * kLda + 16 * g];
+            fa[buf][i][0] = *reinterpret_cast<const v4i *>(arow);
+            fa[buf][i][1] = *reinterpret_cast<const v4i *>(arow + 32);
+        }
+    };
+    auto unpack_b = [&](int buf, int slot) {
+        const v4u w = br[slot];
+        fb[buf][0] = planes(w.x);
+        fb[buf][1] = planes(w.y);
+        fb[buf][2] = planes(w.z);
+        fb[buf][3] = planes(w.w);
+    };
+
+    // prologue: units 0 and 1 staged, unit 0's operands in registers
+    load_a(0, 0);
+    load_a(1, 1);
+    load_a(2, 2);
+    load_b(0, 0);
+    load_b(1, 1);
+    load_b(2, 2);
+    store_a(0, 0);
+    store_a(1, 1);
+    load_a(0, 3);
+    load_a(1, 4);
+    __syncthreads();
+    read_a(0, 0);
+    unpack_b(0, 0);
+    load_b(0, 3);
+
+    v16i acc[WMS][2];
+#pragma unroll
+    for (int i = 0; i < WMS; ++i) acc[i][0] = acc[i][1] = (v16i){};
+
+    // unit u (cur = u & 1 operand buffer, u % 3 ring slot and LDS stage)
+    auto step = [&](int u, int cur, int s3) {
+        const int s1 = (s3 + 1) % 3, s2 = (s3 + 2) % 3;
+        read_a(cur ^ 1, s1);    // unit u+1 (staged one unit ago)
+        unpack_b(cur ^ 1, s1);  // unit u+1
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int i = 0; i < WMS; ++i) {
+                acc[i][0] = mfma_i8(fa[cur][i][h], fb[cur][h], acc[i][0]);
+                acc[i][1] = mfma_i8(fa[cur][i][h], fb[cur][2 + h], acc[i][1]);
+            }
+        store_a(s2, s2);        // unit u+2 into the free stage
+        load_a(s2, u + 5);      // that ring slot now takes unit u+5
+        load_b(s1, u + 4);      // unit u+1's weights are unpacked: slot takes u+4
+        __syncthreads();
+    };
+    int u = 0;
+    for (; u + 6 <= KU; u += 6) {
+        step(u + 0, 0, 0);
+        step(u + 1, 1, 1);
+        step(u + 2, 0, 2);
+        step(u + 3, 1, 0);
+        step(u + 4, 0, 1);
+        step(u + 5, 1, 2);
+    }
+#pragma unroll
+    for (int t = 0; t < 5; ++t)
+        if (u + t < KU) step(u + t, t & 1, t % 3);
+
+    if (!tv) return;
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+        const int n = 64 * tile + 32 * s2 + r;
+        if (n >= p.N) continue;
+#pragma unroll
+        for (int i = 0; i < WMS; ++i) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int row = 32 * i + 8 * (e >> 2) + 4 * g + (e & 3);
+                const int m = m0 + row;
+                if (m < p.M) {
+                    const int32_t a = acc[i][s2][e] - rsum[row];
+                    const int64_t o = (int64_t)m * p.N + n;
+                    gstore_ptr<float>(p.Y)[o] = (float)a * cs[row];
+                    if (p.acc_out) gstore_ptr<int32_t>(p.acc_out)[o] = a;
+                }
+            }
+        }
+    }
+}
+
+// Persistent variant of the 128-token x 64-row-per-wave tile (row-major
+// activations, padded LDS rows).  The grid holds the resident workgroups;
+// each walks its XCD slice of work items.  At the end of a tile's K loop it
+// first issues the NEXT tile's first kDepth units of loads, then the
+// current tile's output stores: on gfx9 loads and stores share one in-order
+// completion counter, so stores issued before the next tile's loads would
+// stall its first wait; issued after them, the fp32 output drains while the
+// next tile's loop runs instead of in a separate burst.
+// Work cursor of a persistent workgroup: slots b, b + stride, ...; a slot
+// names a logical item through the XCD-slice order (single problem) or the
+// plan's slot map (grouped launch).
+struct TileCursor {
+    int b;
+    int stride;
+    int n_slots;
+    const Problem *single;
+    const Problem *probs;
+    const uint2 *item_map;
+    int single_items, single_per;  // single-problem cursors (unused by the grouped launch)
+};
+
+__device__ inline bool cursor_fetch(TileCursor &c, const Problem *&pp, int &local)
+{
+    for (; c.b < c.n_slots; c.b += c.stride) {
+        if (c.single) {
+            const int j = (c.b & 7) * c.single_per + (c.b >> 3);
+            if (j < c.single_items) {
+                pp = c.single;
+                local = j;
+                return true;
+            }
+        } else {
+            const uint2 it = c.item_map[c.b];
+            if (it.x != 0xFFFFFFFFu) {
+                pp = c.probs + it.x;
+                local = (int)it.y;
+                return true;
+            }
+        }
+    }
+    return false;
+}
+
+__device__ void tile_persist_body(TileCursor cur)
+{
+    constexpr int WMS = 4, BM = 128, CH = 2;
+    __shared__ __attribute__((aligned(16))) int8_t As[2][BM * kLda];
+    __shared__ float cs[BM];
+    __shared__ int rsum[BM];
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63, g = lane >> 5, r = lane & 31;
+
+    const Problem *pp = nullptr;
+    int local = 0;
+    if (!cursor_fetch(cur, pp, local)) return;
+
+    // per-tile state
+    int KU = 0, m0 = 0, tile = 0;
+    const BL_GLOBAL v4u *blk = nullptr;
+    const BL_GLOBAL int8_t *asrc[CH];
+    int adst[CH];
+    v4i ar[kDepth][CH];
+    v4u br[kDepth];
+
+    auto setup = [&](const Problem &p, int loc) {
+        const int mtile = loc % p.mt, nt = loc / p.mt;
+        KU = p.KU;
+        m0 = mtile * BM;
+        tile = 4 * nt + wave;
+        blk = gload_ptr<v4u>(p.P + (int64_t)min(tile, p.NT - 1) * KU * kBlockBytes) + lane;
+#pragma unroll
+        for (int i = 0; i < CH; ++i) {
+            const int c = tid + kThreads * i;
+            const int m = min(m0 + (c >> 2), p.M - 1);
+            asrc[i] = gload_ptr<int8_t>(p.Q + (int64_t)m * p.ldq + 16 * (c & 3));
+            adst[i] = (c >> 2) * kLda + 16 * (c & 3);
+        }
+    };
+    auto load_unit = [&](int slot, int u) {
+        const int uc = min(u, KU - 1);
+#pragma unroll
+        for (int i = 0; i < CH; ++i) ar[slot][i] = *reinterpret_cast<const BL_GLOBAL v4i *>(asrc[i] + 64 * uc);
+        br[slot] = blk[(int64_t)uc * 64];
+    };
+    auto begin_tile = [&](const Problem &p) {
+        if (tid < BM) {
+            const int m = min(m0 + tid, p.M - 1);
+            cs[tid] = (*gload_ptr<float>(p.gamma) * gload_ptr<float>(p.absmax)[m]) / 127.0f;
+            rsum[tid] = gload_ptr<int32_t>(p.rowsum)[m];
+        }
+#pragma unroll
+        for (int i = 0; i < CH; ++i) *reinterpret_cast<v4i *>(&As[0][adst[i]]) = ar[0][i];
+        __syncthreads();
+    };
+
+    v16i acc[WMS][2];
+    auto step = [&](int s, int u) {
+        const int buf = u & 1;
+        const v4u w = br[s];
+        const v4i b0 = planes(w.x), b1 = planes(w.y), b2 = planes(w.z), b3 = planes(w.w);
+        v4i a[WMS][2];
+#pragma unroll
+        for (int i = 0; i < WMS; ++i) {
+            const int8_t *arow = &As[buf][(32 * i + r) * kLda + 16 * g];
+            a[i][0] = *reinterpret_cast<const v4i *>(arow);
+            a[i][1] = *reinterpret_cast<const v4i *>(arow + 32);
+        }
+        load_unit(s, u + kDepth);
+#pragma unroll
+        for (int i = 0; i < WMS; ++i) {
+            acc[i][0] = mfma_i8(a[i][0], b0, acc[i][0]);
+            acc[i][1] = mfma_i8(a[i][0], b2, acc[i][1]);
+        }
+#pragma unroll
+        for (int i = 0; i < WMS; ++i) {
+            acc[i][0] = mfma_i8(a[i][1], b1, acc[i][0]);
+            acc[i][1] = mfma_i8(a[i][1], b3, acc[i][1]);
+        }
+        const int ns = (s + 1) % kDepth;
+#pragma unroll
+        for (int i = 0; i < CH; ++i) *reinterpret_cast<v4i *>(&As[buf ^ 1][adst[i]]) = ar[ns][i];
+        __syncthreads();
+    };
+
+    setup(*pp, local);
+#pragma unroll
+    for (int d = 0; d < kDepth; ++d) load_unit(d, d);
+    begin_tile(*pp);
+
+    bool more = true;
+    while (more) {
+#pragma unroll
+        for (int i = 0; i < WMS; ++i) acc[i][0] = acc[i][1] = (v16i){};
+        int u0 = 0;
+        for (; u0 + kDepth <= KU; u0 += kDepth) {
+#pragma unroll
+            for (int s = 0; s < kDepth; ++s) step(s, u0 + s);
+        }
+#pragma unroll
+        for (int s = 0; s < kDepth - 1; ++s)
+            if (u0 + s < KU) step(s, u0 + s);
+
+        // this tile's output coordinates, then the next tile's first loads
+        const Problem *pc = pp;
+        const int c_m0 = m0, c_tile = tile;
+        cur.b += cur.stride;
+        more = cursor_fetch(cur, pp, local);
+        if (more) {
+            setup(*pp, local);
+#pragma unroll
+            for (int d = 0; d < kDepth; ++d) load_unit(d, d);
+        }
+        // epilogue of the finished tile (its scales are still in LDS)
+        const int M = pc->M, N = pc->N;
+        if (c_tile < pc->NT) {
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) {
+                const int n = 64 * c_tile + 32 * s2 + r;
+                if (n >= N) continue;
+#pragma unroll
+                for (int i = 0; i < WMS; ++i) {
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        const int row = 32 * i + 8 * (e >> 2) + 4 * g + (e & 3);
+                        const int m = c_m0 + row;
+                        if (m < M) {
+                            const int32_t a = acc[i][s2][e] - rsum[row];
+                            const int64_t o = (int64_t)m * N + n;
+                            gstore_ptr<float>(pc->Y)[o] = (float)a * cs[row];
+                            if (pc->acc_out) gstore_ptr<int32_t>(pc->acc_out)[o] = a;
+                        }
+                    }
+                }
+            }
+        }
+        if (more) {
+            __syncthreads();  // every wave has read this tile's scales
+            begin_tile(*pp);
+        }
+    }
+}
+
+template <int V>
+__global__ __launch_bounds__(kThreads, 2) void tile_persist_group_kernel(const Problem *__restrict__ probs,
+                                                                         const uint2 *__restrict__ item_map,
+                                                                         int n_slots)
+{
+    TileCursor c{(int)blockIdx.x, (int)gridDim.x, n_slots, nullptr, probs, item_map, 0, 0};
+    tile_persist_body(c);
+}
+
+// resident workgroups of a kernel on the current device, a multiple of 8
+template <typename Kern>
+int resident_grid(Kern kernel)
+{
+    int dev = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 8;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 8;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kThreads, 0) != hipSuccess) return 8;
+    const int g = (cus * per_cu) & ~7;
+    return g < 8 ? 8 : g;
 }
 
 // Barrier-free variant: every wave loads its own MFMA A operands straight
@@ -336,27 +750,37 @@ template <int V>
 __device__ inline void tile_dispatch(const Problem &p, int local)
 {
     if constexpr (V == 0)
-        tile_body<2, 1, 1, false>(p, local);
+        tile_body<2, 1, 1, 0>(p, local);
     else if constexpr (V == 1)
-        tile_body<2, 2, 2, false>(p, local);
+        tile_body<2, 2, 2, 0>(p, local);
     else if constexpr (V == 2)
-        tile_body<4, 1, 1, false>(p, local);
+        tile_body<4, 1, 1, 0>(p, local);
     else if constexpr (V == 3)
         tile_direct_body<true>(p, local);
     else if constexpr (V == 4)
         tile_direct_body<false>(p, local);
     else if constexpr (V == 5)
-        tile_body<4, 1, 1, true>(p, local);
+        tile_body<4, 1, 1, 1>(p, local);
     else if constexpr (V == 6)
-        tile_body<2, 1, 1, true>(p, local);
+        tile_body<2, 1, 1, 1>(p, local);
+    else if constexpr (V == 7)
+        tile_body<2, 2, 2, 1>(p, local);
+    else if constexpr (V == 8)
+        tile_pipe_body<2>(p, local);
+    else if constexpr (V == 9)
+        tile_pipe_body<4>(p, local);
+    else if constexpr (V == 10)
+        tile_body<4, 1, 1, 2, true>(p, local);
+    else if constexpr (V == 11)
+        tile_body<4, 1, 1, 0, true>(p, local);
     else
-        tile_body<2, 2, 2, true>(p, local);
+        tile_body<4, 1, 1, 2, false>(p, local);
 }
 
 template <int V>
 constexpr int tile_min_waves()
 {
-    return (V == 3 || V == 4) ? 1 : 2;
+    return (V == 3 || V == 4 || V == 9) ? 1 : 2;
 }
 
 // Workgroup b runs on XCD b % 8; the logical item order is split into eight
@@ -390,6 +814,7 @@ hipError_t launch_tile_single(const Problem &p, int variant, hipStream_t s)
     const int items = p.mt * p.ntt;
     const int per = (items + 7) / 8;
     const dim3 grid((unsigned)(8 * per)), block(kThreads);
+    if (variant == 13) variant = 2;  // the persistent variant walks device-side plans only
     switch (variant) {
     case 0: hipLaunchKernelGGL(tile_single_kernel<0>, grid, block, 0, s, p, items, per); break;
     case 1: hipLaunchKernelGGL(tile_single_kernel<1>, grid, block, 0, s, p, items, per); break;
@@ -398,7 +823,12 @@ hipError_t launch_tile_single(const Problem &p, int variant, hipStream_t s)
     case 4: hipLaunchKernelGGL(tile_single_kernel<4>, grid, block, 0, s, p, items, per); break;
     case 5: hipLaunchKernelGGL(tile_single_kernel<5>, grid, block, 0, s, p, items, per); break;
     case 6: hipLaunchKernelGGL(tile_single_kernel<6>, grid, block, 0, s, p, items, per); break;
-    default: hipLaunchKernelGGL(tile_single_kernel<7>, grid, block, 0, s, p, items, per); break;
+    case 7: hipLaunchKernelGGL(tile_single_kernel<7>, grid, block, 0, s, p, items, per); break;
+    case 8: hipLaunchKernelGGL(tile_single_kernel<8>, grid, block, 0, s, p, items, per); break;
+    case 9: hipLaunchKernelGGL(tile_single_kernel<9>, grid, block, 0, s, p, items, per); break;
+    case 10: hipLaunchKernelGGL(tile_single_kernel<10>, grid, block, 0, s, p, items, per); break;
+    case 11: hipLaunchKernelGGL(tile_single_kernel<11>, grid, block, 0, s, p, items, per); break;
+    default: hipLaunchKernelGGL(tile_single_kernel<12>, grid, block, 0, s, p, items, per); break;
     }
     return hipGetLastError();
 }
@@ -407,6 +837,12 @@ hipError_t launch_tile_group(const Problem *probs, const uint2 *item_map, int n_
                              int variant, hipStream_t s)
 {
     const dim3 grid((unsigned)n_items), block(kThreads);
+    if (variant == 13) {
+        const int g = resident_grid(tile_persist_group_kernel<13>);
+        const dim3 pg((unsigned)(n_items < g ? n_items : g));
+        hipLaunchKernelGGL(tile_persist_group_kernel<13>, pg, block, 0, s, probs, item_map, n_items);
+        return hipGetLastError();
+    }
     switch (variant) {
     case 0: hipLaunchKernelGGL(tile_group_kernel<0>, grid, block, 0, s, probs, item_map); break;
     case 1: hipLaunchKernelGGL(tile_group_kernel<1>, grid, block, 0, s, probs, item_map); break;
@@ -415,7 +851,12 @@ hipError_t launch_tile_group(const Problem *probs, const uint2 *item_map, int n_
     case 4: hipLaunchKernelGGL(tile_group_kernel<4>, grid, block, 0, s, probs, item_map); break;
     case 5: hipLaunchKernelGGL(tile_group_kernel<5>, grid, block, 0, s, probs, item_map); break;
     case 6: hipLaunchKernelGGL(tile_group_kernel<6>, grid, block, 0, s, probs, item_map); break;
-    default: hipLaunchKernelGGL(tile_group_kernel<7>, grid, block, 0, s, probs, item_map); break;
+    case 7: hipLaunchKernelGGL(tile_group_kernel<7>, grid, block, 0, s, probs, item_map); break;
+    case 8: hipLaunchKernelGGL(tile_group_kernel<8>, grid, block, 0, s, probs, item_map); break;
+    case 9: hipLaunchKernelGGL(tile_group_kernel<9>, grid, block, 0, s, probs, item_map); break;
+    case 10: hipLaunchKernelGGL(tile_group_kernel<10>, grid, block, 0, s, probs, item_map); break;
+    case 11: hipLaunchKernelGGL(tile_group_kernel<11>, grid, block, 0, s, probs, item_map); break;
+    default: hipLaunchKernelGGL(tile_group_kernel<12>, grid, block, 0, s, probs, item_map); break;
     }
     return hipGetLastError();
 }

@@ -90,7 +90,10 @@ def test_config1_end_to_end(B):
 
 @pytest.mark.parametrize("M,K,outliers", [(1, 1, 0), (1, 5, 0), (3, 64, 0), (4, 100, 0),
                                           (7, 256, 0.01), (2, 2560, 0.01), (5, 6912, 0.01),
-                                          (1, 28672, 0), (33, 130, 0), (512, 2560, 0.01)])
+                                          (1, 28672, 0), (33, 130, 0), (512, 2560, 0.01),
+                                          # many tokens: one wave per token (register, re-read
+                                          # and scalar paths)
+                                          (2048, 2560, 0.01), (2049, 10004, 0), (2050, 37, 0)])
 def test_quant_act_parity(B, M, K, outliers):
     say("quant_act", M, K, outliers)
     X = synth.activations_np(M, K, seed=M * 31 + K, outlier_frac=outliers)
