@@ -74,7 +74,7 @@ const Knobs &knobs()
         if (const char *s = getenv("BITLINEAR_DOT4_VARIANT")) v.dot4_variant = (atoi(s) == 0 || atoi(s) == 2) ? atoi(s) : 3;
         if (const char *s = getenv("BITLINEAR_FUSE_QUANT")) v.fuse_quant = atoi(s) != 0;
         if (const char *s = getenv("BITLINEAR_XCD_ORDER")) v.xcd_order = atoi(s) & 3;
-        if (const char *s = getenv("BITLINEAR_TILE_VARIANT")) v.tile_variant = (atoi(s) >= 0 && atoi(s) <= 13) ? atoi(s) : -1;
+        if (const char *s = getenv("BITLINEAR_TILE_VARIANT")) v.tile_variant = (atoi(s) >= 0 && atoi(s) <= 18) ? atoi(s) : -1;
         return v;
     }();
     return k;
@@ -88,7 +88,7 @@ const Knobs &knobs()
 int tile_variant(bool own_q)
 {
     int v = knobs().tile_variant;
-    if (v < 0) v = 11;
+    if (v < 0) v = 18;
     if (!own_q) {  // caller-supplied activations are row-major
         if (v == 3) return 4;
         if (v == 5) return 2;
@@ -97,7 +97,7 @@ int tile_variant(bool own_q)
     }
     return v;
 }
-int tile_bm(int variant) { return (variant == 0 || variant == 6 || variant == 8) ? 64 : 128; }
+int tile_bm(int variant) { return (variant == 0 || variant == 6 || variant == 8 || variant == 14 || variant == 15) ? 64 : 128; }
 bool tile_frag(int variant) { return variant == 3 || (variant >= 5 && variant <= 7); }
 
 // Kernel kind and decomposition of one problem.  `base_items` is the number

@@ -25,6 +25,8 @@
 // separates the two LDS buffers.
 #include "mm_common.hpp"
 
+#include <cstdlib>
+
 namespace bl {
 namespace {
 
@@ -53,7 +55,7 @@ constexpr int kDepth = 3; // units of global-load lookahead
 constexpr int kEpiStride = 72;  // floats per LDS row of the epilogue transpose
 
 template <int WMS, int WNT, int WAVES_M, int ALAY, bool EPI = false>
-__device__ void tile_body(const Problem &p, int local)
+__device__ __forceinline__ void tile_body(const Problem &p, int local)
 {
     constexpr bool FRAG = ALAY != 0;
     constexpr int WAVES_N = 4 / WAVES_M;
@@ -265,6 +267,182 @@ __device__ void tile_body(const Problem &p, int local)
                     }
                 }
             }
+        }
+    }
+}
+
+// 128-token x 64-row-per-wave tile (as tile_body<4, 1, 1, 0, true>) with
+// UPS units of K per LDS stage and barrier: the fixed cost of a barrier
+// round (the wait itself and the LDS read latency before the first MFMA)
+// is paid once per UPS units.  A stage's unit past KU gets an all-zero
+// packed word -- zero fields add nothing -- so odd unit counts need no
+// branch; its activation chunk re-reads unit KU-1 (valid memory).
+constexpr int kLda2 = 144;  // 128 bytes + 16 of padding: 8 lanes on distinct banks
+
+template <int UPS>
+__device__ __forceinline__ void tile_body_ups(const Problem &p, int local)
+{
+    constexpr int WMS = 4, BM = 128, CH = 2;  // CH: 16-byte chunks per thread per unit
+    constexpr int kRow = 64 * UPS + 16;
+    static_assert(UPS == 2 && kRow == kLda2, "stage rows are 128 bytes + padding");
+    constexpr int kStageBytes = BM * kRow;
+    constexpr int kEpiBytes = 4 * 32 * kEpiStride * 4;
+    constexpr int kSmem = 2 * kStageBytes > kEpiBytes ? 2 * kStageBytes : kEpiBytes;
+    constexpr int kD = 2;  // stages of global-load lookahead
+    __shared__ __attribute__((aligned(16))) int8_t smem[kSmem];
+    int8_t (*As)[kStageBytes] = reinterpret_cast<int8_t (*)[kStageBytes]>(smem);
+    __shared__ float cs[BM];
+    __shared__ int rsum[BM];
+
+    const int mtile = local % p.mt;
+    const int nt = local / p.mt;
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63, g = lane >> 5, r = lane & 31;
+    const int m0 = mtile * BM;
+    const int KU = p.KU;
+    const int KS = (KU + UPS - 1) / UPS;
+    const int tile = 4 * nt + wave;
+    const bool tv = tile < p.NT;
+    const BL_GLOBAL v4u *blk = gload_ptr<v4u>(p.P + (int64_t)min(tile, p.NT - 1) * KU * kBlockBytes) + lane;
+
+    const BL_GLOBAL int8_t *asrc[CH];
+    int adst[CH];
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+        const int c = tid + kThreads * i;
+        const int m = min(m0 + (c >> 2), p.M - 1);
+        asrc[i] = gload_ptr<int8_t>(p.Q + (int64_t)m * p.ldq + 16 * (c & 3));
+        adst[i] = (c >> 2) * kRow + 16 * (c & 3);
+    }
+
+    __syncthreads();  // the previous work item of this workgroup may still read LDS
+    if (tid < BM) {
+        const int m = min(m0 + tid, p.M - 1);
+        cs[tid] = (*gload_ptr<float>(p.gamma) * gload_ptr<float>(p.absmax)[m]) / 127.0f;
+        rsum[tid] = gload_ptr<int32_t>(p.rowsum)[m];
+    }
+
+    v4i ar[kD][UPS][CH];
+    v4u br[kD][UPS];
+    auto load_stage = [&](int slot, int st) {
+#pragma unroll
+        for (int h = 0; h < UPS; ++h) {
+            const int u = st * UPS + h;
+            const int uc = min(u, KU - 1);
+#pragma unroll
+            for (int i = 0; i < CH; ++i) ar[slot][h][i] = *reinterpret_cast<const BL_GLOBAL v4i *>(asrc[i] + 64 * uc);
+            br[slot][h] = blk[(int64_t)uc * 64];
+        }
+    };
+    auto stage_lds = [&](int buf, int slot) {
+#pragma unroll
+        for (int h = 0; h < UPS; ++h)
+#pragma unroll
+            for (int i = 0; i < CH; ++i) *reinterpret_cast<v4i *>(&As[buf][adst[i] + 64 * h]) = ar[slot][h][i];
+    };
+#pragma unroll
+    for (int d = 0; d < kD; ++d) load_stage(d, d);
+    stage_lds(0, 0);
+    __syncthreads();
+
+    v16i acc[WMS][2];
+#pragma unroll
+    for (int i = 0; i < WMS; ++i) acc[i][0] = acc[i][1] = (v16i){};
+
+    auto step = [&](int s, int st) {
+        __builtin_amdgcn_sched_barrier(0);
+        const int buf = st & 1;
+        v4u w[UPS];
+        const v4u z = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int h = 0; h < UPS; ++h) w[h] = st * UPS + h < KU ? br[s][h] : z;
+        const int8_t *abase = &As[buf][r * kRow + 16 * g];
+#pragma unroll
+        for (int h = 0; h < UPS; ++h) {
+            v4i a[WMS][2];
+#pragma unroll
+            for (int i = 0; i < WMS; ++i) {
+                const int8_t *arow = abase + 32 * i * kRow + 64 * h;
+                a[i][0] = *reinterpret_cast<const v4i *>(arow);
+                a[i][1] = *reinterpret_cast<const v4i *>(arow + 32);
+            }
+            const v4i b0 = planes(w[h].x), b1 = planes(w[h].y), b2 = planes(w[h].z), b3 = planes(w[h].w);
+            if (h == UPS - 1) {
+                // every word of slot s has become planes: refill it
+                __builtin_amdgcn_sched_barrier(0);
+                load_stage(s, st + kD);
+            }
+#pragma unroll
+            for (int i = 0; i < WMS; ++i) {
+                acc[i][0] = mfma_i8(a[i][0], b0, acc[i][0]);
+                acc[i][1] = mfma_i8(a[i][0], b2, acc[i][1]);
+            }
+#pragma unroll
+            for (int i = 0; i < WMS; ++i) {
+                acc[i][0] = mfma_i8(a[i][1], b1, acc[i][0]);
+                acc[i][1] = mfma_i8(a[i][1], b3, acc[i][1]);
+            }
+        }
+        stage_lds(buf ^ 1, (s + 1) % kD);
+        __syncthreads();
+    };
+    int s0 = 0;
+    for (; s0 + kD <= KS; s0 += kD) {
+#pragma unroll
+        for (int s = 0; s < kD; ++s) step(s, s0 + s);
+    }
+#pragma unroll
+    for (int s = 0; s < kD - 1; ++s)
+        if (s0 + s < KS) step(s, s0 + s);
+
+    // epilogue: rescale, transpose through LDS, 16-byte non-temporal stores
+    __syncthreads();  // every wave is done with the activation stages
+    float *ep = reinterpret_cast<float *>(smem) + wave * (32 * kEpiStride);
+    const bool vec_ok = (p.N & 3) == 0;
+    BL_GLOBAL float *Y = gstore_ptr<float>(p.Y);
+#pragma unroll
+    for (int i = 0; i < WMS; ++i) {
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int row = 8 * (e >> 2) + 4 * g + (e & 3);
+                const int rr = 32 * i + row;
+                ep[row * kEpiStride + 32 * s2 + r] = (float)(acc[i][s2][e] - rsum[rr]) * cs[rr];
+            }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int row = (lane >> 4) + 4 * k;
+            const int c4 = 4 * (lane & 15);
+            const int m = m0 + 32 * i + row;
+            const int n = 64 * tile + c4;
+            const v4f_t v = *reinterpret_cast<const v4f_t *>(&ep[row * kEpiStride + c4]);
+            if (tv && m < p.M) {
+                const int64_t o = (int64_t)m * p.N + n;
+                if (vec_ok && n + 3 < p.N) {
+                    __builtin_nontemporal_store(v, reinterpret_cast<BL_GLOBAL v4f_t *>(Y + o));
+                } else {
+                    if (n < p.N) __builtin_nontemporal_store(v.x, Y + o);
+                    if (n + 1 < p.N) __builtin_nontemporal_store(v.y, Y + o + 1);
+                    if (n + 2 < p.N) __builtin_nontemporal_store(v.z, Y + o + 2);
+                    if (n + 3 < p.N) __builtin_nontemporal_store(v.w, Y + o + 3);
+                }
+            }
+        }
+    }
+    if (p.acc_out && tv) {
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+            const int n = 64 * tile + 32 * s2 + r;
+            if (n >= p.N) continue;
+#pragma unroll
+            for (int i = 0; i < WMS; ++i)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int row = 32 * i + 8 * (e >> 2) + 4 * g + (e & 3);
+                    const int m = m0 + row;
+                    if (m < p.M) gstore_ptr<int32_t>(p.acc_out)[(int64_t)m * p.N + n] = acc[i][s2][e] - rsum[row];
+                }
         }
     }
 }
@@ -605,6 +783,620 @@ __global__ __launch_bounds__(kThreads, 2) void tile_persist_group_kernel(const P
     tile_persist_body(c);
 }
 
+// Persistent tile kernel whose fp32 outputs leave during the next tile's
+// K loop.  Tile = 64 tokens x 256 weight rows (four waves, 64 rows each).
+// At the end of a tile's K loop the rescaled outputs are written to an LDS
+// staging tile (64 x 256 fp32); during the next tile's loop each wave sends
+// one 1 KiB staged row to Y per unit (16 rows per wave), so the output
+// stream, the largest HBM stream of a prefill contraction, runs under the
+// MFMAs instead of in a burst after them.  The drain stores are buffer
+// stores whose record count is 0 when there is nothing to send (the
+// hardware drops out-of-range lanes), so every unit issues the same memory
+// instructions and the load ring keeps static wait counts.  LDS: 10 KiB
+// activation stages + 66 KiB output stage per workgroup, two per CU.
+constexpr int kDrainBM = 64;
+constexpr int kYsStride = 264;  // floats per staged row: rows 4 apart land 32 banks apart
+constexpr int kDrainRows = kDrainBM / 4;  // rows each wave sends per tile
+
+// the staged tile still to be sent (wave-uniform values)
+struct DrainState {
+    float *Y;
+    int64_t N;
+    int m0, rows, n0, bytes;  // rows == 0: nothing staged
+};
+
+__device__ __forceinline__ void tile_drain_body(TileCursor cur)
+{
+    constexpr int WMS = 2, BM = kDrainBM, CH = 1;
+    __shared__ __attribute__((aligned(16))) int8_t As[2][BM * kLda];
+    __shared__ __attribute__((aligned(16))) float Ys[BM * kYsStride];
+    __shared__ float cs[BM];
+    __shared__ int rsum[BM];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, g = lane >> 5, r = lane & 31;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+    const Problem *pp = nullptr;
+    int local = 0;
+    if (!cursor_fetch(cur, pp, local)) return;
+
+    int KU = 0, m0 = 0, tile = 0;
+    const BL_GLOBAL v4u *blk = nullptr;
+    const BL_GLOBAL int8_t *asrc[CH];
+    int adst[CH];
+    v4i ar[kDepth][CH];
+    v4u br[kDepth];
+    DrainState d{nullptr, 0, 0, 0, 0, 0};
+
+    auto setup = [&](const Problem &p, int loc) {
+        const int mtile = loc % p.mt, nt = loc / p.mt;
+        KU = p.KU;
+        m0 = mtile * BM;
+        tile = 4 * nt + wave;
+        blk = gload_ptr<v4u>(p.P + (int64_t)min(tile, p.NT - 1) * KU * kBlockBytes) + lane;
+#pragma unroll
+        for (int i = 0; i < CH; ++i) {
+            const int c = tid + kThreads * i;
+            const int m = min(m0 + (c >> 2), p.M - 1);
+            asrc[i] = gload_ptr<int8_t>(p.Q + (int64_t)m * p.ldq + 16 * (c & 3));
+            adst[i] = (c >> 2) * kLda + 16 * (c & 3);
+        }
+    };
+    auto load_unit = [&](int slot, int u) {
+        const int uc = min(u, KU - 1);
+#pragma unroll
+        for (int i = 0; i < CH; ++i) ar[slot][i] = *reinterpret_cast<const BL_GLOBAL v4i *>(asrc[i] + 64 * uc);
+        br[slot] = blk[(int64_t)uc * 64];
+    };
+    auto begin_tile = [&](const Problem &p) {
+        if (tid < BM) {
+            const int m = min(m0 + tid, p.M - 1);
+            cs[tid] = (*gload_ptr<float>(p.gamma) * gload_ptr<float>(p.absmax)[m]) / 127.0f;
+            rsum[tid] = gload_ptr<int32_t>(p.rowsum)[m];
+        }
+#pragma unroll
+        for (int i = 0; i < CH; ++i) *reinterpret_cast<v4i *>(&As[0][adst[i]]) = ar[0][i];
+        __syncthreads();
+    };
+    // staged row j (< kDrainRows) of this wave -> Y; j >= kDrainRows sends nothing
+    auto drain_row = [&](int j) {
+        const int jr = min(j, kDrainRows - 1);
+        const int rt = 4 * jr + wave;
+        const v4u v = *reinterpret_cast<const v4u *>(&Ys[rt * kYsStride + 4 * lane]);
+        const bool ok = j < kDrainRows && rt < d.rows;
+        float *base = d.Y + ((int64_t)d.m0 + (ok ? rt : 0)) * d.N + d.n0;
+        const __amdgpu_buffer_rsrc_t rs =
+            __builtin_amdgcn_make_buffer_rsrc(base, (short)0, ok ? d.bytes : 0, 0x00020000);
+        __builtin_amdgcn_raw_buffer_store_b128(v, rs, 16 * lane, 0, 2 /* non-temporal */);
+    };
+
+    v16i acc[WMS][2];
+    auto step = [&](int s, int u) {
+        // keep each unit's work inside its own step: hoisting a later unit's
+        // plane extraction would wait on loads that are still in flight
+        __builtin_amdgcn_sched_barrier(0);
+        const int buf = u & 1;
+        const v4u w = br[s];
+        const v4i b0 = planes(w.x), b1 = planes(w.y), b2 = planes(w.z), b3 = planes(w.w);
+        v4i a[WMS][2];
+#pragma unroll
+        for (int i = 0; i < WMS; ++i) {
+            const int8_t *arow = &As[buf][(32 * i + r) * kLda + 16 * g];
+            a[i][0] = *reinterpret_cast<const v4i *>(arow);
+            a[i][1] = *reinterpret_cast<const v4i *>(arow + 32);
+        }
+        // slot s is refilled only after its previous contents became planes,
+        // so the ring slots keep fixed registers across iterations
+        __builtin_amdgcn_sched_barrier(0);
+        load_unit(s, u + kDepth);
+#pragma unroll
+        for (int i = 0; i < WMS; ++i) {
+            acc[i][0] = mfma_i8(a[i][0], b0, acc[i][0]);
+            acc[i][1] = mfma_i8(a[i][0], b2, acc[i][1]);
+        }
+#pragma unroll
+        for (int i = 0; i < WMS; ++i) {
+            acc[i][0] = mfma_i8(a[i][1], b1, acc[i][0]);
+            acc[i][1] = mfma_i8(a[i][1], b3, acc[i][1]);
+        }
+        const int ns = (s + 1) % kDepth;
+#pragma unroll
+        for (int i = 0; i < CH; ++i) *reinterpret_cast<v4i *>(&As[buf ^ 1][adst[i]]) = ar[ns][i];
+        // the drain goes last: its LDS read shares the barrier's wait, and
+        // placed between the MFMAs it made the compiler copy ring registers
+        // that still had loads in flight
+        drain_row(u);
+        __syncthreads();
+    };
+
+    // The ring registers are filled and drained within one pass of the tile
+    // loop (nothing in flight crosses its back-edge), which keeps them in
+    // fixed registers; the previous tile's staged outputs are what carries
+    // over.
+    do {
+        setup(*pp, local);
+#pragma unroll
+        for (int d0 = 0; d0 < kDepth; ++d0) load_unit(d0, d0);
+        begin_tile(*pp);
+#pragma unroll
+        for (int i = 0; i < WMS; ++i) acc[i][0] = acc[i][1] = (v16i){};
+        int u0 = 0;
+        for (; u0 + kDepth <= KU; u0 += kDepth) {
+#pragma unroll
+            for (int s = 0; s < kDepth; ++s) step(s, u0 + s);
+        }
+#pragma unroll
+        for (int s = 0; s < kDepth - 1; ++s)
+            if (u0 + s < KU) step(s, u0 + s);
+        // a loop shorter than kDrainRows units leaves staged rows behind
+        for (int j = KU; j < kDrainRows; ++j) drain_row(j);
+        __syncthreads();  // every staged row has been read
+
+        // this tile's outputs -> LDS stage (or straight to Y when its rows are
+        // not 16-byte aligned pieces)
+        const Problem &pc = *pp;
+        const int M = pc.M, N = pc.N;
+        const bool staged = (N & 3) == 0 && (reinterpret_cast<uintptr_t>(pc.Y) & 15) == 0;
+        const int n0 = 256 * (tile >> 2);
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+            const int col = 64 * wave + 32 * s2 + r;
+            const int n = n0 + col;
+#pragma unroll
+            for (int i = 0; i < WMS; ++i) {
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int row = 32 * i + 8 * (e >> 2) + 4 * g + (e & 3);
+                    const int32_t a = acc[i][s2][e] - rsum[row];
+                    const float y = (float)a * cs[row];
+                    Ys[row * kYsStride + col] = y;
+                    const int m = m0 + row;
+                    if (m < M && n < N) {
+                        const int64_t o = (int64_t)m * N + n;
+                        if (!staged) gstore_ptr<float>(pc.Y)[o] = y;
+                        if (pc.acc_out) gstore_ptr<int32_t>(pc.acc_out)[o] = a;
+                    }
+                }
+            }
+        }
+        d.Y = pc.Y;
+        d.N = N;
+        d.m0 = m0;
+        d.n0 = n0;
+        d.rows = staged ? min(BM, M - m0) : 0;
+        d.bytes = 4 * min(256, N - n0);
+        __syncthreads();  // the stage is complete and every wave has read the scales
+        cur.b += cur.stride;
+    } while (cursor_fetch(cur, pp, local));
+    for (int j = 0; j < kDrainRows; ++j) drain_row(j);
+}
+
+template <int V>
+__global__ __launch_bounds__(kThreads, 2) void tile_drain_group_kernel(const Problem *__restrict__ probs,
+                                                                       const uint2 *__restrict__ item_map,
+                                                                       int n_slots)
+{
+    TileCursor c{(int)blockIdx.x, (int)gridDim.x, n_slots, nullptr, probs, item_map, 0, 0};
+    tile_drain_body(c);
+}
+
+// Wave-specialized persistent tile kernel: 320-thread workgroups, two per
+// CU.  Waves 0-3 compute 64-token x 256-row tiles exactly like the 64-token
+// LDS-staged kernel, but end each tile by writing the rescaled outputs to an
+// LDS stage instead of storing them; wave 4 sends the previous tile's staged
+// rows (1 KiB each) to Y while the compute waves run the next tile's K loop,
+// and takes part in every barrier of that loop.  The output stream
+// thus runs under the MFMAs, and since the store waves issue no loads, the
+// single in-order memory counter never makes a compute wave wait for a
+// store.  LDS per workgroup: 10 KiB activation stages + 66 KiB output stage.
+constexpr int kWsThreads = 320;
+// The kernel is declared for up to 512 threads so that the compiler budgets
+// registers for four waves per SIMD (<= 128 VGPRs): the first and fifth wave
+// of a 5-wave workgroup share a SIMD, so two co-resident workgroups put four
+// waves on it.
+
+template <int V>
+__global__ __launch_bounds__(512, 4) void tile_ws_group_kernel(const Problem *__restrict__ probs,
+                                                                      const uint2 *__restrict__ item_map,
+                                                                      int n_slots)
+{
+    constexpr int WMS = 2, BM = kDrainBM, CH = 1;
+    __shared__ __attribute__((aligned(16))) int8_t As[2][BM * kLda];
+    __shared__ __attribute__((aligned(16))) float Ys[BM * kYsStride];
+    __shared__ float cs[BM];
+    __shared__ int rsum[BM];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, g = lane >> 5, r = lane & 31;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool compute = wave < 4;
+    const int cw = wave & 3;  // compute wave index
+
+    TileCursor cur{(int)blockIdx.x, (int)gridDim.x, n_slots, nullptr, probs, item_map, 0, 0};
+    const Problem *pp = nullptr;
+    int local = 0;
+    if (!cursor_fetch(cur, pp, local)) return;
+
+    int KU = 0, m0 = 0, tile = 0;
+    const BL_GLOBAL v4u *blk = nullptr;
+    const BL_GLOBAL int8_t *asrc = nullptr;
+    int adst = 0;
+    v4i ar[kDepth];
+    v4u br[kDepth];
+    DrainState d{nullptr, 0, 0, 0, 0, 0};
+
+    auto setup = [&](const Problem &p, int loc) {
+        const int mtile = loc % p.mt, nt = loc / p.mt;
+        KU = p.KU;
+        m0 = mtile * BM;
+        tile = 4 * nt + cw;
+        blk = gload_ptr<v4u>(p.P + (int64_t)min(tile, p.NT - 1) * KU * kBlockBytes) + lane;
+        const int c = tid & 255;
+        const int m = min(m0 + (c >> 2), p.M - 1);
+        asrc = gload_ptr<int8_t>(p.Q + (int64_t)m * p.ldq + 16 * (c & 3));
+        adst = (c >> 2) * kLda + 16 * (c & 3);
+    };
+    auto load_unit = [&](int slot, int u) {
+        const int uc = min(u, KU - 1);
+        ar[slot] = *reinterpret_cast<const BL_GLOBAL v4i *>(asrc + 64 * uc);
+        br[slot] = blk[(int64_t)uc * 64];
+    };
+    // the store wave sends staged rows [j0, j1)
+    auto drain_rows = [&](int j0, int j1) {
+        for (int rt = j0; rt < j1; ++rt) {
+            if (rt < d.rows && 16 * lane < d.bytes) {
+                const v4f_t v = *reinterpret_cast<const v4f_t *>(&Ys[rt * kYsStride + 4 * lane]);
+                __builtin_nontemporal_store(
+                    v, reinterpret_cast<BL_GLOBAL v4f_t *>(gstore_ptr<float>(d.Y) + ((int64_t)d.m0 + rt) * d.N + d.n0) +
+                           lane);
+            }
+        }
+    };
+
+    v16i acc[WMS][2];
+    // Register budget (two 5-wave workgroups per CU need <= 128 VGPRs): the
+    // planes of each half unit are extracted right before its MFMAs and the
+    // activation operands are read one half at a time.
+    auto step = [&](int s, int u) {
+        __builtin_amdgcn_sched_barrier(0);
+        const int buf = u & 1;
+        const v4u w = br[s];
+        const int8_t *arow = &As[buf][r * kLda + 16 * g];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            v4i a[WMS];
+#pragma unroll
+            for (int i = 0; i < WMS; ++i) a[i] = *reinterpret_cast<const v4i *>(arow + 32 * i * kLda + 32 * h);
+            const v4i bl = planes(h ? w.y : w.x), bh = planes(h ? w.w : w.z);
+            __builtin_amdgcn_sched_barrier(0);
+            if (h == 0) load_unit(s, u + kDepth);  // slot s is free once w is read
+#pragma unroll
+            for (int i = 0; i < WMS; ++i) {
+                acc[i][0] = mfma_i8(a[i], bl, acc[i][0]);
+                acc[i][1] = mfma_i8(a[i], bh, acc[i][1]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        const int ns = (s + 1) % kDepth;
+        *reinterpret_cast<v4i *>(&As[buf ^ 1][adst]) = ar[ns];
+        __syncthreads();
+    };
+
+    // The two roles walk the same work list and meet at the same barriers:
+    // one at a tile's start, one per unit of its K loop, two at its end.
+    if (!compute) {
+        do {
+            const int ku = pp->KU;
+            __syncthreads();  // tile start
+            // the previous tile's BM rows, spread over this tile's loop
+            for (int u = 0; u < ku; ++u) {
+                drain_rows((u * BM + ku - 1) / ku, ((u + 1) * BM + ku - 1) / ku);
+                __syncthreads();
+            }
+            __syncthreads();  // the stage has been read
+            const Problem &pc = *pp;
+            const bool staged = (pc.N & 3) == 0 && (reinterpret_cast<uintptr_t>(pc.Y) & 15) == 0;
+            d.Y = pc.Y;
+            d.N = pc.N;
+            d.m0 = (local % pc.mt) * BM;
+            d.n0 = 256 * (local / pc.mt);
+            d.rows = staged ? min(BM, pc.M - d.m0) : 0;
+            d.bytes = 4 * min(256, pc.N - d.n0);
+            __syncthreads();  // the stage holds this tile
+            cur.b += cur.stride;
+        } while (cursor_fetch(cur, pp, local));
+        drain_rows(0, BM);
+        return;
+    }
+
+    do {
+        setup(*pp, local);
+#pragma unroll
+        for (int d0 = 0; d0 < kDepth; ++d0) load_unit(d0, d0);
+        if (tid < BM) {
+            const int m = min(m0 + tid, pp->M - 1);
+            cs[tid] = (*gload_ptr<float>(pp->gamma) * gload_ptr<float>(pp->absmax)[m]) / 127.0f;
+            rsum[tid] = gload_ptr<int32_t>(pp->rowsum)[m];
+        }
+        *reinterpret_cast<v4i *>(&As[0][adst]) = ar[0];
+        __syncthreads();  // tile start
+
+#pragma unroll
+        for (int i = 0; i < WMS; ++i) acc[i][0] = acc[i][1] = (v16i){};
+        int u0 = 0;
+        for (; u0 + kDepth <= KU; u0 += kDepth) {
+#pragma unroll
+            for (int s = 0; s < kDepth; ++s) step(s, u0 + s);
+        }
+#pragma unroll
+        for (int s = 0; s < kDepth - 1; ++s)
+            if (u0 + s < KU) step(s, u0 + s);
+        __syncthreads();  // the stage has been read
+
+        const Problem &pc = *pp;
+        const int M = pc.M, N = pc.N;
+        const bool staged = (N & 3) == 0 && (reinterpret_cast<uintptr_t>(pc.Y) & 15) == 0;
+        const int n0 = 256 * (tile >> 2);
+        // one 32-row block at a time: its 16 scales and row sums per lane
+        // plus the accumulators fit the register budget
+#pragma unroll
+        for (int i = 0; i < WMS; ++i) {
+            __builtin_amdgcn_sched_barrier(0);
+            float csv[16];
+            int rsv[16];
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int row = 32 * i + 8 * (e >> 2) + 4 * g + (e & 3);
+                csv[e] = cs[row];
+                rsv[e] = rsum[row];
+            }
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) {
+                const int col = 64 * cw + 32 * s2 + r;
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int row = 32 * i + 8 * (e >> 2) + 4 * g + (e & 3);
+                    Ys[row * kYsStride + col] = (float)(acc[i][s2][e] - rsv[e]) * csv[e];
+                }
+            }
+        }
+        if (!staged || pc.acc_out) {
+            // rows that are not 16-byte pieces, and the optional int32 sums
+            for (int i = 0; i < WMS; ++i)
+                for (int s2 = 0; s2 < 2; ++s2)
+                    for (int e = 0; e < 16; ++e) {
+                        const int row = 32 * i + 8 * (e >> 2) + 4 * g + (e & 3);
+                        const int n = n0 + 64 * cw + 32 * s2 + r;
+                        const int m = m0 + row;
+                        if (m < M && n < N) {
+                            const int32_t a = acc[i][s2][e] - rsum[row];
+                            const int64_t o = (int64_t)m * N + n;
+                            if (!staged) gstore_ptr<float>(pc.Y)[o] = (float)a * cs[row];
+                            if (pc.acc_out) gstore_ptr<int32_t>(pc.acc_out)[o] = a;
+                        }
+                    }
+        }
+        __syncthreads();  // the stage holds this tile; the scales are free
+        cur.b += cur.stride;
+    } while (cursor_fetch(cur, pp, local));
+}
+
+// Wave-specialized persistent tile kernel, one 576-thread workgroup per CU:
+// tile = 128 tokens x 256 weight rows.  Waves 0-7 compute (two per SIMD,
+// each 64 tokens x 64 rows: two 64-token halves x four 64-row weight
+// tiles) and end each tile by writing the rescaled outputs to an LDS stage;
+// wave 8 sends the previous tile's staged rows to Y during the next tile's
+// K loop and meets the compute waves at every barrier.  LDS: 20 KiB
+// activation stages + 132 KiB output stage.
+constexpr int kWs2Threads = 576;
+
+template <int V>
+__global__ __launch_bounds__(kWs2Threads) void tile_ws2_group_kernel(const Problem *__restrict__ probs,
+                                                                      const uint2 *__restrict__ item_map,
+                                                                      int n_slots)
+{
+    constexpr int WMS = 2, BM = 2 * kDrainBM, CH = 1;
+    __shared__ __attribute__((aligned(16))) int8_t As[2][BM * kLda];
+    __shared__ __attribute__((aligned(16))) float Ys[BM * kYsStride];
+    __shared__ float cs[BM];
+    __shared__ int rsum[BM];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, g = lane >> 5, r = lane & 31;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool compute = wave < 8;
+    const int cw = wave & 3;  // weight tile of a compute wave
+    const int wm = (wave >> 2) & 1;  // 64-token half of a compute wave
+
+    TileCursor cur{(int)blockIdx.x, (int)gridDim.x, n_slots, nullptr, probs, item_map, 0, 0};
+    const Problem *pp = nullptr;
+    int local = 0;
+    if (!cursor_fetch(cur, pp, local)) return;
+
+    int KU = 0, m0 = 0, tile = 0;
+    const BL_GLOBAL v4u *blk = nullptr;
+    const BL_GLOBAL int8_t *asrc = nullptr;
+    int adst = 0;
+    v4i ar[kDepth];
+    v4u br[kDepth];
+    DrainState d{nullptr, 0, 0, 0, 0, 0};
+
+    auto setup = [&](const Problem &p, int loc) {
+        const int mtile = loc % p.mt, nt = loc / p.mt;
+        KU = p.KU;
+        m0 = mtile * BM;
+        tile = 4 * nt + cw;
+        blk = gload_ptr<v4u>(p.P + (int64_t)min(tile, p.NT - 1) * KU * kBlockBytes) + lane;
+        const int c = tid & 511;
+        const int m = min(m0 + (c >> 2), p.M - 1);
+        asrc = gload_ptr<int8_t>(p.Q + (int64_t)m * p.ldq + 16 * (c & 3));
+        adst = (c >> 2) * kLda + 16 * (c & 3);
+    };
+    auto load_unit = [&](int slot, int u) {
+        const int uc = min(u, KU - 1);
+        ar[slot] = *reinterpret_cast<const BL_GLOBAL v4i *>(asrc + 64 * uc);
+        br[slot] = blk[(int64_t)uc * 64];
+    };
+    // the store wave sends staged rows [j0, j1)
+    auto drain_rows = [&](int j0, int j1) {
+        for (int rt = j0; rt < j1; ++rt) {
+            if (rt < d.rows && 16 * lane < d.bytes) {
+                const v4f_t v = *reinterpret_cast<const v4f_t *>(&Ys[rt * kYsStride + 4 * lane]);
+                __builtin_nontemporal_store(
+                    v, reinterpret_cast<BL_GLOBAL v4f_t *>(gstore_ptr<float>(d.Y) + ((int64_t)d.m0 + rt) * d.N + d.n0) +
+                           lane);
+            }
+        }
+    };
+
+    v16i acc[WMS][2];
+    // Register budget (two 5-wave workgroups per CU need <= 128 VGPRs): the
+    // planes of each half unit are extracted right before its MFMAs and the
+    // activation operands are read one half at a time.
+    auto step = [&](int s, int u) {
+        __builtin_amdgcn_sched_barrier(0);
+        const int buf = u & 1;
+        const v4u w = br[s];
+        const int8_t *arow = &As[buf][(64 * wm + r) * kLda + 16 * g];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            v4i a[WMS];
+#pragma unroll
+            for (int i = 0; i < WMS; ++i) a[i] = *reinterpret_cast<const v4i *>(arow + 32 * i * kLda + 32 * h);
+            const v4i bl = planes(h ? w.y : w.x), bh = planes(h ? w.w : w.z);
+            __builtin_amdgcn_sched_barrier(0);
+            if (h == 0) load_unit(s, u + kDepth);  // slot s is free once w is read
+#pragma unroll
+            for (int i = 0; i < WMS; ++i) {
+                acc[i][0] = mfma_i8(a[i], bl, acc[i][0]);
+                acc[i][1] = mfma_i8(a[i], bh, acc[i][1]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        const int ns = (s + 1) % kDepth;
+        *reinterpret_cast<v4i *>(&As[buf ^ 1][adst]) = ar[ns];
+        __syncthreads();
+    };
+
+    // The two roles walk the same work list and meet at the same barriers:
+    // one at a tile's start, one per unit of its K loop, two at its end.
+    if (!compute) {
+        do {
+            const int ku = pp->KU;
+            __syncthreads();  // tile start
+            // the previous tile's BM rows, spread over this tile's loop
+            for (int u = 0; u < ku; ++u) {
+                drain_rows((u * BM + ku - 1) / ku, ((u + 1) * BM + ku - 1) / ku);
+                __syncthreads();
+            }
+            __syncthreads();  // the stage has been read
+            const Problem &pc = *pp;
+            const bool staged = (pc.N & 3) == 0 && (reinterpret_cast<uintptr_t>(pc.Y) & 15) == 0;
+            d.Y = pc.Y;
+            d.N = pc.N;
+            d.m0 = (local % pc.mt) * BM;
+            d.n0 = 256 * (local / pc.mt);
+            d.rows = staged ? min(BM, pc.M - d.m0) : 0;
+            d.bytes = 4 * min(256, pc.N - d.n0);
+            __syncthreads();  // the stage holds this tile
+            cur.b += cur.stride;
+        } while (cursor_fetch(cur, pp, local));
+        drain_rows(0, BM);
+        return;
+    }
+
+    do {
+        setup(*pp, local);
+#pragma unroll
+        for (int d0 = 0; d0 < kDepth; ++d0) load_unit(d0, d0);
+        if (tid < BM) {
+            const int m = min(m0 + tid, pp->M - 1);
+            cs[tid] = (*gload_ptr<float>(pp->gamma) * gload_ptr<float>(pp->absmax)[m]) / 127.0f;
+            rsum[tid] = gload_ptr<int32_t>(pp->rowsum)[m];
+        }
+        *reinterpret_cast<v4i *>(&As[0][adst]) = ar[0];
+        __syncthreads();  // tile start
+
+#pragma unroll
+        for (int i = 0; i < WMS; ++i) acc[i][0] = acc[i][1] = (v16i){};
+        int u0 = 0;
+        for (; u0 + kDepth <= KU; u0 += kDepth) {
+#pragma unroll
+            for (int s = 0; s < kDepth; ++s) step(s, u0 + s);
+        }
+#pragma unroll
+        for (int s = 0; s < kDepth - 1; ++s)
+            if (u0 + s < KU) step(s, u0 + s);
+        __syncthreads();  // the stage has been read
+
+        const Problem &pc = *pp;
+        const int M = pc.M, N = pc.N;
+        const bool staged = (N & 3) == 0 && (reinterpret_cast<uintptr_t>(pc.Y) & 15) == 0;
+        const int n0 = 256 * (tile >> 2);
+        // one 32-row block at a time: its 16 scales and row sums per lane
+        // plus the accumulators fit the register budget
+#pragma unroll
+        for (int i = 0; i < WMS; ++i) {
+            __builtin_amdgcn_sched_barrier(0);
+            float csv[16];
+            int rsv[16];
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int row = 64 * wm + 32 * i + 8 * (e >> 2) + 4 * g + (e & 3);
+                csv[e] = cs[row];
+                rsv[e] = rsum[row];
+            }
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) {
+                const int col = 64 * cw + 32 * s2 + r;
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int row = 64 * wm + 32 * i + 8 * (e >> 2) + 4 * g + (e & 3);
+                    Ys[row * kYsStride + col] = (float)(acc[i][s2][e] - rsv[e]) * csv[e];
+                }
+            }
+        }
+        if (!staged || pc.acc_out) {
+            // rows that are not 16-byte pieces, and the optional int32 sums
+            for (int i = 0; i < WMS; ++i)
+                for (int s2 = 0; s2 < 2; ++s2)
+                    for (int e = 0; e < 16; ++e) {
+                        const int row = 64 * wm + 32 * i + 8 * (e >> 2) + 4 * g + (e & 3);
+                        const int n = n0 + 64 * cw + 32 * s2 + r;
+                        const int m = m0 + row;
+                        if (m < M && n < N) {
+                            const int32_t a = acc[i][s2][e] - rsum[row];
+                            const int64_t o = (int64_t)m * N + n;
+                            if (!staged) gstore_ptr<float>(pc.Y)[o] = (float)a * cs[row];
+                            if (pc.acc_out) gstore_ptr<int32_t>(pc.acc_out)[o] = a;
+                        }
+                    }
+        }
+        __syncthreads();  // the stage holds this tile; the scales are free
+        cur.b += cur.stride;
+    } while (cursor_fetch(cur, pp, local));
+}
+
+// Persistent form of the 128-token tile with the LDS-transposed epilogue:
+// the resident workgroups walk the work list, one tile body per item (its
+// load ring lives within the item).  Two workgroups share each CU; started
+// together they would reach their epilogues together, every CU storing at
+// once while its matrix cores idle.  The second half of the grid therefore
+// starts `stagger` ticks of the 100 MHz real-time counter late, so that on
+// each CU one workgroup's output burst falls inside the other's K loop.
+template <int V>
+__global__ __launch_bounds__(kThreads, 2) void tile_persist_epi_kernel(const Problem *__restrict__ probs,
+                                                                       const uint2 *__restrict__ item_map,
+                                                                       int n_slots, int stagger)
+{
+    if (stagger > 0 && blockIdx.x >= gridDim.x / 2) {
+        const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+        while (__builtin_amdgcn_s_memrealtime() - t0 < (uint64_t)stagger) __builtin_amdgcn_s_sleep(8);
+    }
+    for (int b = blockIdx.x; b < n_slots; b += gridDim.x) {
+        const uint2 it = item_map[b];
+        if (it.x != 0xFFFFFFFFu) tile_body<4, 1, 1, 0, true>(probs[it.x], (int)it.y);
+    }
+}
+
 // resident workgroups of a kernel on the current device, a multiple of 8
 template <typename Kern>
 int resident_grid(Kern kernel)
@@ -773,6 +1565,8 @@ __device__ inline void tile_dispatch(const Problem &p, int local)
         tile_body<4, 1, 1, 2, true>(p, local);
     else if constexpr (V == 11)
         tile_body<4, 1, 1, 0, true>(p, local);
+    else if constexpr (V == 18)
+        tile_body_ups<2>(p, local);
     else
         tile_body<4, 1, 1, 2, false>(p, local);
 }
@@ -814,7 +1608,10 @@ hipError_t launch_tile_single(const Problem &p, int variant, hipStream_t s)
     const int items = p.mt * p.ntt;
     const int per = (items + 7) / 8;
     const dim3 grid((unsigned)(8 * per)), block(kThreads);
-    if (variant == 13) variant = 2;  // the persistent variant walks device-side plans only
+    // the persistent variants walk device-side plans only
+    if (variant == 13) variant = 2;
+    if (variant == 14 || variant == 15) variant = 0;   // same 64-token tile, not persistent
+    if (variant == 16 || variant == 17) variant = 11;
     switch (variant) {
     case 0: hipLaunchKernelGGL(tile_single_kernel<0>, grid, block, 0, s, p, items, per); break;
     case 1: hipLaunchKernelGGL(tile_single_kernel<1>, grid, block, 0, s, p, items, per); break;
@@ -828,6 +1625,7 @@ hipError_t launch_tile_single(const Problem &p, int variant, hipStream_t s)
     case 9: hipLaunchKernelGGL(tile_single_kernel<9>, grid, block, 0, s, p, items, per); break;
     case 10: hipLaunchKernelGGL(tile_single_kernel<10>, grid, block, 0, s, p, items, per); break;
     case 11: hipLaunchKernelGGL(tile_single_kernel<11>, grid, block, 0, s, p, items, per); break;
+    case 18: hipLaunchKernelGGL(tile_single_kernel<18>, grid, block, 0, s, p, items, per); break;
     default: hipLaunchKernelGGL(tile_single_kernel<12>, grid, block, 0, s, p, items, per); break;
     }
     return hipGetLastError();
@@ -843,6 +1641,44 @@ hipError_t launch_tile_group(const Problem *probs, const uint2 *item_map, int n_
         hipLaunchKernelGGL(tile_persist_group_kernel<13>, pg, block, 0, s, probs, item_map, n_items);
         return hipGetLastError();
     }
+    if (variant == 17) {
+        int dev = 0, cus = 0, per_cu = 0;
+        hipGetDevice(&dev);
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, tile_ws2_group_kernel<17>, kWs2Threads, 0);
+        int g = (cus * per_cu) & ~7;
+        if (g < 8) g = 8;
+        const dim3 pg((unsigned)(n_items < g ? n_items : g));
+        hipLaunchKernelGGL(tile_ws2_group_kernel<17>, pg, dim3(kWs2Threads), 0, s, probs, item_map, n_items);
+        return hipGetLastError();
+    }
+    if (variant == 16) {
+        static const int stagger = [] {
+            const char *e = getenv("BITLINEAR_TILE_STAGGER");
+            return e ? atoi(e) : 2000;
+        }();
+        const int g = resident_grid(tile_persist_epi_kernel<16>);
+        const dim3 pg((unsigned)(n_items < g ? n_items : g));
+        hipLaunchKernelGGL(tile_persist_epi_kernel<16>, pg, block, 0, s, probs, item_map, n_items, stagger);
+        return hipGetLastError();
+    }
+    if (variant == 15) {
+        int dev = 0, cus = 0, per_cu = 0;
+        hipGetDevice(&dev);
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, tile_ws_group_kernel<15>, kWsThreads, 0);
+        int g = (cus * per_cu) & ~7;
+        if (g < 8) g = 8;
+        const dim3 pg((unsigned)(n_items < g ? n_items : g));
+        hipLaunchKernelGGL(tile_ws_group_kernel<15>, pg, dim3(kWsThreads), 0, s, probs, item_map, n_items);
+        return hipGetLastError();
+    }
+    if (variant == 14) {
+        const int g = resident_grid(tile_drain_group_kernel<14>);
+        const dim3 pg((unsigned)(n_items < g ? n_items : g));
+        hipLaunchKernelGGL(tile_drain_group_kernel<14>, pg, block, 0, s, probs, item_map, n_items);
+        return hipGetLastError();
+    }
     switch (variant) {
     case 0: hipLaunchKernelGGL(tile_group_kernel<0>, grid, block, 0, s, probs, item_map); break;
     case 1: hipLaunchKernelGGL(tile_group_kernel<1>, grid, block, 0, s, probs, item_map); break;
@@ -856,6 +1692,7 @@ hipError_t launch_tile_group(const Problem *probs, const uint2 *item_map, int n_
     case 9: hipLaunchKernelGGL(tile_group_kernel<9>, grid, block, 0, s, probs, item_map); break;
     case 10: hipLaunchKernelGGL(tile_group_kernel<10>, grid, block, 0, s, probs, item_map); break;
     case 11: hipLaunchKernelGGL(tile_group_kernel<11>, grid, block, 0, s, probs, item_map); break;
+    case 18: hipLaunchKernelGGL(tile_group_kernel<18>, grid, block, 0, s, probs, item_map); break;
     default: hipLaunchKernelGGL(tile_group_kernel<12>, grid, block, 0, s, probs, item_map); break;
     }
     return hipGetLastError();
