@@ -63,7 +63,7 @@ struct Knobs {
     int fuse_quant = 0;          // single-token problems quantize in the dot4 prologue
     int split_target = 1024;     // aim for at least this many workgroups
     int xcd_order = 3;           // bit 0: streaming kernel, bit 1: tile kernel
-    int tile_variant = -1;       // force a tile-kernel instantiation (0..9)
+    int tile_variant = -1;       // force a tile-kernel instantiation (see tile_variant())
 };
 const Knobs &knobs()
 {
@@ -74,31 +74,30 @@ const Knobs &knobs()
         if (const char *s = getenv("BITLINEAR_DOT4_VARIANT")) v.dot4_variant = (atoi(s) == 0 || atoi(s) == 2) ? atoi(s) : 3;
         if (const char *s = getenv("BITLINEAR_FUSE_QUANT")) v.fuse_quant = atoi(s) != 0;
         if (const char *s = getenv("BITLINEAR_XCD_ORDER")) v.xcd_order = atoi(s) & 3;
-        if (const char *s = getenv("BITLINEAR_TILE_VARIANT")) v.tile_variant = (atoi(s) >= 0 && atoi(s) <= 18) ? atoi(s) : -1;
+        if (const char *s = getenv("BITLINEAR_TILE_VARIANT")) v.tile_variant = atoi(s);
         return v;
     }();
     return k;
 }
 
-// Tile-kernel instantiation: 0..2 are the LDS-staged variants on row-major
-// activations (64-token tiles; 128-token 2x2 waves; 128-token 4x1 waves),
-// 3/4 the barrier-free direct-load variants (fragment-ordered / row-major).
-// 5..7 are the LDS-staged variants on fragment-ordered activations (as 2,
-// 0, 1).
+// Tile-kernel instantiation (the list is next to the tile kernels): 18 by
+// default; 5..7 read fragment-ordered activations that only the library's
+// own quantizer writes, so caller-supplied activations map them to their
+// row-major twins 2, 0, 1.
+bool tile_variant_known(int v) { return v == 0 || v == 1 || v == 2 || (v >= 5 && v <= 7) || (v >= 10 && v <= 12) || v == 18; }
 int tile_variant(bool own_q)
 {
     int v = knobs().tile_variant;
-    if (v < 0) v = 18;
+    if (!tile_variant_known(v)) v = 18;
     if (!own_q) {  // caller-supplied activations are row-major
-        if (v == 3) return 4;
         if (v == 5) return 2;
         if (v == 6) return 0;
         if (v == 7) return 1;
     }
     return v;
 }
-int tile_bm(int variant) { return (variant == 0 || variant == 6 || variant == 8 || variant == 14 || variant == 15) ? 64 : 128; }
-bool tile_frag(int variant) { return variant == 3 || (variant >= 5 && variant <= 7); }
+int tile_bm(int variant) { return (variant == 0 || variant == 6) ? 64 : 128; }
+bool tile_frag(int variant) { return variant >= 5 && variant <= 7; }
 
 // Kernel kind and decomposition of one problem.  `base_items` is the number
 // of streaming work items the whole launch has without K splits; splits are
