@@ -13,8 +13,11 @@ Printed: one JSON line.  value = packed weight bytes per step / step time.
 roofline = the contraction kernel's algorithmic bytes (packed weights + int8
 activations + fp32 outputs) over its average duration (HIP events on the
 launch stream), against 8 TB/s.  prefill = the same 210 matrices at
-M = 512 (int8 TOP/s against 5.0 POP/s dense int8).  cpu_baseline = the CPU
-oracle (single thread) on a bounded sample of the same workload.
+M = 512 (int8 TOP/s against 5.0 POP/s dense int8).  graph = the decode
+step captured once in a HIP graph and replayed.  curves = latency of a full
+sweep over the 3B-class stack at M in {1, 8, 64, 256} (and, on request, the
+70B-class stack at M in {1, 16, 176}).  cpu_baseline = the CPU oracle
+(single thread) on a bounded sample of the same workload.
 
 Inputs are synthetic: weights ~ N(0, 0.02) drawn on the device per matrix,
 activations ~ N(0, 1) (prefill: 1% of channels x20), seeded.
@@ -106,6 +109,53 @@ def time_plan(torch, plan, steps, warmup):
     return wall / steps * 1e3, a.elapsed_time(b) / steps
 
 
+def time_graph(torch, plan, steps, warmup):
+    """The same step captured once into a HIP graph (torch.cuda.CUDAGraph on
+    a default-priority side stream) and replayed `steps` times: wall time
+    per replay."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(2):
+            plan.quant_act()
+            plan.matmul()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        plan.quant_act()
+        plan.matmul()
+    for _ in range(warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        graph.replay()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps * 1e3
+
+
+def curve(B, torch, model, Ms, dev, steps, warmup):
+    """Latency of one full sweep over a model's BitLinear stack at each token
+    count M (quantize + contract every matrix, grouped launches)."""
+    spec = synth.MODELS[model]
+    log(f"building {model} stack: {spec['layers']} layers")
+    mats = build_stack(B, torch, model, spec["layers"], dev)
+    packed = sum(m["N"] * m["K"] // 4 for m in mats)
+    out = {"matrices": len(mats), "packed_bytes": packed, "points": []}
+    for M in Ms:
+        plan, probs = make_plan(B, torch, mats, M, dev)
+        ms, kern = time_plan(torch, plan, steps, warmup)
+        ops = sum(2 * M * m["N"] * m["K"] for m in mats)
+        out["points"].append({"M": M, "ms_per_sweep": round(ms, 4), "contraction_ms": round(kern, 4),
+                              "packed_GBps": round(packed / (ms * 1e-3) / 1e9, 1),
+                              "TOPs": round(ops / (ms * 1e-3) / 1e12, 1)})
+        log(f"  {model} M={M}: {ms:.3f} ms per sweep")
+        del plan, probs
+    del mats
+    torch.cuda.empty_cache()
+    return out
+
+
 def load_traffic(name):
     """HBM traffic of the dominant kernel from the committed rocprofv3 PMC
     summary, if it was taken on the current kernel sources."""
@@ -157,6 +207,10 @@ def main():
     ap.add_argument("--prefill-M", type=int, default=512)
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--curves", default="3b",
+                    help="comma list of latency-vs-M curves to add: 3b (M 1,8,64,256), 70b (M 1,16,176); "
+                         "'none' to skip")
+    ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run only a plain device copy of known size (PMC calibration)")
     args = ap.parse_args()
@@ -197,6 +251,7 @@ def main():
     out_bytes = sum(4 * M * m["N"] for m in mats)
     alg_bytes = packed + act_bytes + out_bytes
     achieved = alg_bytes / (kern_ms * 1e-3) / 1e9
+    gms = None if args.no_graph else time_graph(torch, plan, args.steps, args.warmup)
     traffic = load_traffic(f"stream_{args.model}_m{M}")
     result = {
         "metric": METRIC,
@@ -220,6 +275,9 @@ def main():
                      "kernel": "stream contraction (grouped, one launch per step)",
                      "kernel_ms_mean": round(kern_ms, 5), "bytes_per_launch": alg_bytes},
     }
+    if gms is not None:
+        result["graph"] = {"ms_per_step": round(gms, 5), "GBps": round(packed / (gms * 1e-3) / 1e9, 2),
+                           "note": "the same step captured once in a HIP graph and replayed"}
     del plan, probs
     torch.cuda.empty_cache()
 
@@ -242,6 +300,14 @@ def main():
         }
         del plan, probs
         torch.cuda.empty_cache()
+
+    curves = [c for c in args.curves.split(",") if c and c != "none"]
+    if curves:
+        del mats
+        torch.cuda.empty_cache()
+        points = {"3b": [1, 8, 64, 256], "70b": [1, 16, 176]}
+        result["curves"] = {c: curve(B, torch, c, points[c], dev, max(5, args.steps // 5),
+                                     max(1, args.warmup // 2)) for c in curves}
 
     if not args.no_cpu:
         log("timing CPU oracle baseline")

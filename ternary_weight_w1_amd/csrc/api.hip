@@ -37,7 +37,8 @@ int hip_fail(hipError_t e, const char *what)
 
 constexpr int64_t kMaxMN = int64_t(1) << 24;
 constexpr int64_t kMaxK = 131072;
-constexpr int kStreamMaxM = 32;  // larger token counts take the tile kernel
+constexpr int kStreamMaxM = bl::kStreamMaxTokens;
+constexpr int kGroupTiles = 4 * bl::kStreamMfmaTiles;  // tiles per streaming MFMA workgroup
 
 bool a16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 bool a4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3) == 0; }
@@ -102,8 +103,10 @@ bool tile_frag(int variant) { return variant >= 5 && variant <= 7; }
 // Kernel kind and decomposition of one problem.  `base_items` is the number
 // of streaming work items the whole launch has without K splits; splits are
 // added only while the launch is short of workgroups.  own_q: the library
-// quantizes the activations itself and may choose their layout.
-void decompose(Problem &p, int64_t base_items, bool own_q)
+// quantizes the activations itself and may choose their layout.  groups4:
+// the launch runs the streaming MFMA kernel, whose work items are groups of
+// kGroupTiles 64-row tiles (p.ntt of them).
+void decompose(Problem &p, int64_t base_items, bool own_q, bool groups4 = false)
 {
     p.KU = (int32_t)((p.K + 63) / 64);
     p.NT = (int32_t)((p.N + 63) / 64);
@@ -112,6 +115,12 @@ void decompose(Problem &p, int64_t base_items, bool own_q)
     p.mt = p.ntt = p.mtile = p.qtiled = 0;
     if (p.M <= kStreamMaxM) {
         p.kind = 0;
+        if (groups4) {
+            p.ntt = (p.NT + kGroupTiles - 1) / kGroupTiles;
+            // past 16 tokens the MFMA kernel reads each A operand as one
+            // 1 KiB block when the library lays the activations out itself
+            p.qtiled = own_q && p.M > bl::kStreamFragTokens ? 1 : 0;
+        }
         const int64_t target = knobs().split_target;
         if (base_items < target) {
             int64_t ks = (target + base_items - 1) / base_items;
@@ -134,7 +143,17 @@ void decompose(Problem &p, int64_t base_items, bool own_q)
 
 int64_t items_of(const Problem &p)
 {
-    return p.kind == 0 ? (int64_t)p.NT * p.ks : (int64_t)p.mt * p.ntt;
+    if (p.kind == 0) return (int64_t)(p.ntt > 0 ? p.ntt : p.NT) * p.ks;
+    return (int64_t)p.mt * p.ntt;
+}
+
+// Decomposition of a problem launched alone: the streaming MFMA kernel (more
+// tokens than the dot4 kernel takes) works on tile groups.
+void decompose_single(Problem &p, bool own_q)
+{
+    const int64_t nt = (p.N + 63) / 64;
+    const bool g4 = p.M <= kStreamMaxM && p.M > knobs().dot4_max_m;
+    decompose(p, g4 ? (nt + kGroupTiles - 1) / kGroupTiles : nt, own_q, g4);
 }
 
 // The LDS-staged dot4 variants hold 64 bytes of activations per unit of
@@ -239,7 +258,7 @@ size_t bitlinear_workspace_bytes(int op, int64_t M, int64_t N, int64_t K)
     if (op != BITLINEAR_WS_MATMUL && op != BITLINEAR_WS_FORWARD) return SIZE_MAX;
     if (check_mnk(M, N, K) != BITLINEAR_OK) return SIZE_MAX;
     Problem p = make_problem(M, N, K);
-    decompose(p, (N + 63) / 64, op == BITLINEAR_WS_FORWARD);
+    decompose_single(p, op == BITLINEAR_WS_FORWARD);
     return (size_t)ws_layout(p, op == BITLINEAR_WS_FORWARD).total;
 }
 
@@ -312,7 +331,7 @@ int bitlinear_matmul(const int8_t *Q, int64_t ldq, const float *absmax, const in
     if (!a16(Q) || !a16(P) || !a16(Y_out) || (acc_out && !a16(acc_out)) || !a4(absmax) || !a4(rowsum) || !a4(gamma))
         return fail(BITLINEAR_ERR_ALIGN, "matmul: arrays need 16-byte, scalars 4-byte alignment");
     Problem p = make_problem(M, N, K);
-    decompose(p, (N + 63) / 64, false);
+    decompose_single(p, false);
     const WsLayout L = ws_layout(p, false);
     if (L.total > 0 && (!ws || ws_bytes < (size_t)L.total || !a16(ws)))
         return fail(BITLINEAR_ERR_WORKSPACE, "matmul: needs %lld workspace bytes (16-byte aligned)", (long long)L.total);
@@ -346,7 +365,7 @@ int bitlinear_forward(const float *X, int64_t M, int64_t K, const uint8_t *P,
     if (!a16(X) || !a16(P) || !a16(Y_out) || (acc_out && !a16(acc_out)) || !a4(gamma))
         return fail(BITLINEAR_ERR_ALIGN, "forward: arrays need 16-byte, gamma 4-byte alignment");
     Problem p = make_problem(M, N, K);
-    decompose(p, (N + 63) / 64, true);
+    decompose_single(p, true);
     const WsLayout L = ws_layout(p, true);
     if (!ws || ws_bytes < (size_t)L.total || !a16(ws))
         return fail(BITLINEAR_ERR_WORKSPACE, "forward: needs %lld workspace bytes (16-byte aligned)", (long long)L.total);
@@ -453,11 +472,19 @@ int build_group(const bitlinear_problem *in, int count, char *ws, GroupPlan &out
     }
     int stream_variant = all_m1 ? stream_variant_for(1, max_upsplit) : 1;
     if (stream_variant == 3 && knobs().fuse_quant && !any_split) stream_variant = 4;
+    const bool groups4 = stream_variant == 1;
+    if (groups4) {
+        // the MFMA kernel's work items are tile groups
+        base_items = 0;
+        for (int i = 0; i < count; ++i)
+            if (in[i].M <= kStreamMaxM) base_items += ((in[i].N + 63) / 64 + kGroupTiles - 1) / kGroupTiles;
+        if (base_items < 1) base_items = 1;
+    }
     for (int i = 0; i < count; ++i) {
         const bitlinear_problem &q = in[i];
         Problem &p = out.probs[i];
         p = make_problem(q.M, q.N, q.K);
-        decompose(p, base_items, true);
+        decompose(p, base_items, true, groups4);
         p.X = q.X;
         p.P = q.P;
         p.gamma = q.gamma;

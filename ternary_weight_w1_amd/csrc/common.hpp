@@ -41,6 +41,12 @@ __device__ inline int8_t quant_code(float x, float s)
 constexpr int kTileRows = 64;
 constexpr int kUnitCodes = 64;
 constexpr int kBlockBytes = 1024;
+// token counts the streaming kernels take; larger ones take the tile kernel
+constexpr int kStreamMaxTokens = 32;
+// 64-row tiles per wave of the streaming MFMA kernel (a workgroup takes 4x)
+constexpr int kStreamMfmaTiles = 2;
+// token counts above which that kernel reads fragment-ordered activations
+constexpr int kStreamFragTokens = 16;
 
 // Everything the contraction kernels need to know about one BitLinear
 // problem.  Single calls pass one of these by value; the grouped path keeps

@@ -207,88 +207,133 @@ __device__ void stream_dot4(const Problem &p, int local)
     }
 }
 
+// 2..32 tokens: the same packed stream feeds v_mfma_i32_32x32x32_i8 with the
+// token rows as the A operand.  A workgroup covers 4 * kStreamMfmaTiles
+// 64-row tiles over one K range: each wave owns kStreamMfmaTiles tiles and
+// every wave walks the same units in the same order, so a wave streams its
+// tiles' blocks contiguously, one activation fragment serves all its tiles,
+// the four waves fetch that fragment at about the same time (one L2 read,
+// three L1 hits), and each wave ends with complete sums -- no cross-wave
+// reduction, no LDS, no barrier.  Loads run one group of UNROLL units ahead
+// of the MFMAs through a two-slot register ring (branch-free: unit indices
+// clamp to the range end and surplus units get zero weights, which add
+// nothing).
 template <int UNROLL>
 __device__ void stream_mfma(const Problem &p, int local)
 {
-    // per wave, per 32-row half s, per accumulator element e, per lane
-    __shared__ int red[kWaves][2][16][64];
-    const int tile = local / p.ks, split = local - tile * p.ks;
+    constexpr int TPW = kStreamMfmaTiles;
+    const int grp = local / p.ks, split = local - grp * p.ks;
     const int u0 = split * p.upsplit;
     const int u1 = min(p.KU, u0 + p.upsplit);
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 5, r = lane & 31;
-    const BL_GLOBAL v4u *blk = gload_ptr<v4u>(p.P + (int64_t)tile * p.KU * kBlockBytes) + lane;
-    const bool rv = r < p.M;
-    const BL_GLOBAL int8_t *qrow = gload_ptr<int8_t>(p.Q + (int64_t)(rv ? r : 0) * p.ldq + 16 * g);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63, g = lane >> 5, r = lane & 31;
+    const int tile0 = 4 * TPW * grp + TPW * wave;
+    // tiles past NT stream tile NT-1 (valid memory); their sums are dropped
+    const BL_GLOBAL v4u *blk[TPW];
+#pragma unroll
+    for (int t = 0; t < TPW; ++t)
+        blk[t] = gload_ptr<v4u>(p.P + (int64_t)min(tile0 + t, p.NT - 1) * p.KU * kBlockBytes) + lane;
+    // A operand of unit u, half h: fragment-ordered activations hold it as one
+    // contiguous 1 KiB block (16 bytes per lane); row-major activations give
+    // each lane 16 bytes of its token row (lanes of rows past M load nothing).
+    const bool rv = p.qtiled || r < p.M;
+    const BL_GLOBAL int8_t *qbase;
+    int64_t ustride, hoff;
+    if (p.qtiled) {
+        qbase = gload_ptr<int8_t>(p.Q) + 16 * lane;
+        ustride = 2048;
+        hoff = 1024;
+    } else {
+        qbase = gload_ptr<int8_t>(p.Q) + (int64_t)min(r, p.M - 1) * p.ldq + 16 * g;
+        ustride = 64;
+        hoff = 32;
+    }
     const v4i zero = {0, 0, 0, 0};
+    const v4u zw = {0u, 0u, 0u, 0u};
+    // the tokens' row sums and absmax, fetched now so that their latency
+    // hides under the stream (read per output element at the end)
+    __shared__ int s_rowsum[kStreamMaxTokens];
+    __shared__ float s_absmax[kStreamMaxTokens];
+    if (threadIdx.x < p.M) {
+        s_rowsum[threadIdx.x] = gload_ptr<int32_t>(p.rowsum)[threadIdx.x];
+        s_absmax[threadIdx.x] = gload_ptr<float>(p.absmax)[threadIdx.x];
+    }
 
-    v16i acc0 = {}, acc1 = {};
-    int u = u0 + wave;
-    for (; u + kWaves * (UNROLL - 1) < u1; u += kWaves * UNROLL) {
-        v4u w[UNROLL];
-        v4i qa[UNROLL], qb[UNROLL];
-#pragma unroll
-        for (int j = 0; j < UNROLL; ++j) w[j] = load_packed(blk + (int64_t)(u + kWaves * j) * 64);
+    const int n_units = u1 - u0;
+    const int groups = (n_units + UNROLL - 1) / UNROLL;
+    v4u w[2][UNROLL][TPW];
+    v4i qa[2][UNROLL], qb[2][UNROLL];
+    auto load_group = [&](int slot, int i) {
 #pragma unroll
         for (int j = 0; j < UNROLL; ++j) {
-            const BL_GLOBAL int8_t *qu = qrow + 64 * (u + kWaves * j);
-            qa[j] = rv ? *reinterpret_cast<const BL_GLOBAL v4i *>(qu) : zero;
-            qb[j] = rv ? *reinterpret_cast<const BL_GLOBAL v4i *>(qu + 32) : zero;
-        }
+            const int u = min(u0 + UNROLL * i + j, u1 - 1);
 #pragma unroll
-        for (int j = 0; j < UNROLL; ++j) {
-            acc0 = mfma_i8(qa[j], planes(w[j].x), acc0);
-            acc0 = mfma_i8(qb[j], planes(w[j].y), acc0);
-            acc1 = mfma_i8(qa[j], planes(w[j].z), acc1);
-            acc1 = mfma_i8(qb[j], planes(w[j].w), acc1);
+            for (int t = 0; t < TPW; ++t) w[slot][j][t] = load_packed(blk[t] + (int64_t)u * 64);
+            const BL_GLOBAL int8_t *qu = qbase + ustride * u;
+            qa[slot][j] = rv ? *reinterpret_cast<const BL_GLOBAL v4i *>(qu) : zero;
+            qb[slot][j] = rv ? *reinterpret_cast<const BL_GLOBAL v4i *>(qu + hoff) : zero;
         }
-    }
-    for (; u < u1; u += kWaves) {
-        const v4u w = load_packed(blk + (int64_t)u * 64);
-        const BL_GLOBAL int8_t *qu = qrow + 64 * u;
-        const v4i qa = rv ? *reinterpret_cast<const BL_GLOBAL v4i *>(qu) : zero;
-        const v4i qb = rv ? *reinterpret_cast<const BL_GLOBAL v4i *>(qu + 32) : zero;
-        acc0 = mfma_i8(qa, planes(w.x), acc0);
-        acc0 = mfma_i8(qb, planes(w.y), acc0);
-        acc1 = mfma_i8(qa, planes(w.z), acc1);
-        acc1 = mfma_i8(qb, planes(w.w), acc1);
-    }
-    // element e of lane l is token 8*(e/4) + 4*(l/32) + e%4, row 32*s + l%32;
-    // only element groups that hold real tokens are exchanged
-    const int eg = (p.M + 7) >> 3;  // 1..4
+    };
+    v16i acc[TPW][2];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-        if ((e >> 2) < eg) {
-            red[wave][0][e][lane] = acc0[e];
-            red[wave][1][e][lane] = acc1[e];
-        }
+    for (int t = 0; t < TPW; ++t) acc[t][0] = acc[t][1] = (v16i){};
+    // Both halves of every unit of the group, first half first: consecutive
+    // updates of one accumulator are 2 * TPW MFMAs apart, so the matrix pipe
+    // never waits on its own previous result.
+    auto run_group = [&](int slot, int i) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int j = 0; j < UNROLL; ++j) {
+                const bool live = UNROLL * i + j < n_units;
+                const v4i a = h ? qb[slot][j] : qa[slot][j];
+#pragma unroll
+                for (int t = 0; t < TPW; ++t) {
+                    const v4u wj = live ? w[slot][j][t] : zw;
+                    acc[t][0] = mfma_i8(a, planes(h ? wj.y : wj.x), acc[t][0]);
+                    acc[t][1] = mfma_i8(a, planes(h ? wj.w : wj.z), acc[t][1]);
+                }
+            }
+    };
+    load_group(0, 0);
+    int i = 0;
+    for (; i + 2 <= groups; i += 2) {
+        load_group(1, i + 1);
+        run_group(0, i);
+        load_group(0, i + 2);
+        run_group(1, i + 1);
     }
-    __syncthreads();
+    if (i < groups) run_group(0, i);
 
+    // element e of lane l is token 8*(e/4) + 4*(l/32) + e%4, row 32*s + l%32
     const float gamma = *p.gamma;
     const int64_t ldp = (int64_t)p.NT * 64;
-    const int entries = 2 * 4 * eg * 64;
-    int *flat = &red[0][0][0][0];
-    constexpr int kWaveStride = 2 * 16 * 64;
-    for (int idx = threadIdx.x; idx < entries; idx += kThreads) {
-        const int s = idx / (4 * eg * 64);
-        const int e = (idx >> 6) % (4 * eg);
-        const int l = idx & 63;
-        const int m = 8 * (e >> 2) + 4 * (l >> 5) + (e & 3);
-        const int n = 64 * tile + 32 * s + (l & 31);
-        if (m >= p.M || n >= p.N) continue;
-        const int off = (s * 16 + e) * 64 + l;
-        const int total = flat[off] + flat[kWaveStride + off] + flat[2 * kWaveStride + off] +
-                          flat[3 * kWaveStride + off];
-        if (p.ks == 1)
-            finish_output(p, gamma, m, n, total);
-        else
-            gstore_ptr<int32_t>(p.acc_ws)[((int64_t)split * p.M + m) * ldp + n] = total;
+    __syncthreads();  // the token scales are in LDS
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+        if (tile0 + t >= p.NT) continue;
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+            const int n = 64 * (tile0 + t) + 32 * s2 + r;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int m = 8 * (e >> 2) + 4 * g + (e & 3);
+                if (m < p.M && n < p.N) {
+                    if (p.ks == 1)
+                        finish_output_with(p, gamma, m, n, acc[t][s2][e], s_rowsum[m], s_absmax[m]);
+                    else
+                        gstore_ptr<int32_t>(p.acc_ws)[((int64_t)split * p.M + m) * ldp + n] = acc[t][s2][e];
+                }
+            }
+        }
     }
     if (p.ks == 1) return;
-    if (!arrive_last(p, tile)) return;
-    for (int idx = threadIdx.x; idx < p.M * 64; idx += kThreads) {
-        const int m = idx >> 6;
-        const int n = 64 * tile + (idx & 63);
+    // split K: the last workgroup of the tile group sums its tiles
+    constexpr int kRows = 256 * TPW;
+    if (!arrive_last(p, 4 * TPW * grp)) return;
+    for (int idx = threadIdx.x; idx < p.M * kRows; idx += kThreads) {
+        const int m = idx / kRows;
+        const int n = kRows * grp + idx % kRows;
         if (n >= p.N) continue;
         int sum = 0;
         for (int j = 0; j < p.ks; ++j) sum += gload_ptr<int32_t>(p.acc_ws)[((int64_t)j * p.M + m) * ldp + n];
@@ -296,7 +341,8 @@ __device__ void stream_mfma(const Problem &p, int local)
     }
 }
 
-// 0: dot4, activations from global; 1: MFMA (2..32 tokens); 2: dot4 with
+// 0: dot4, activations from global; 1: MFMA (2..32 tokens, tile groups per
+// workgroup); 2: dot4 with
 // LDS-staged activations; 3: as 2 with 8 units in flight per wave; 4: as 3
 // with the activation quantization fused into the prologue.
 template <int V>
@@ -333,7 +379,9 @@ __global__ __launch_bounds__(kThreads) void stream_group_kernel(const Problem *_
 
 hipError_t launch_stream_single(const Problem &p, int variant, hipStream_t s)
 {
-    const dim3 grid((unsigned)(p.NT * p.ks)), block(kThreads);
+    // the MFMA variant's work items are tile groups (p.ntt of them)
+    const int64_t tiles = variant == 1 ? (int64_t)p.ntt : (int64_t)p.NT;
+    const dim3 grid((unsigned)(tiles * p.ks)), block(kThreads);
     const unsigned lds = variant >= 2 ? 64u * (unsigned)p.upsplit : 0u;
     switch (variant) {
     case 0: hipLaunchKernelGGL(stream_single_kernel<0>, grid, block, 0, s, p); break;

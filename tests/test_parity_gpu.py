@@ -312,6 +312,52 @@ def test_group_single_token_no_split(B):
     _group_run(B, specs, 700)
 
 
+def test_group_graph_replay(B):
+    # The grouped step (quantize, then contract) captured once in a HIP graph:
+    # every replay -- with eager library work and synchronizations between
+    # replays -- matches the oracle and the eager result bit for bit.  The mix
+    # has a split-K problem (arrival tickets must be re-armed on every
+    # replay), a streaming MFMA problem and a tile-kernel problem.
+    say("group graph replay")
+    specs = [(1, 640, 2560), (1, 64, 8192), (5, 257, 640), (96, 300, 700)]
+    probs, refs = [], []
+    for i, (M, N, K) in enumerate(specs):
+        T = synth.random_ternary(N, K, seed=900 + i)
+        X = synth.activations_np(M, K, seed=950 + i, outlier_frac=0.01)
+        g = np.float32(0.02 * (i + 1))
+        refs.append((O.forward(X, T, g), g))
+        probs.append(dict(X=dev(X), P=dev(O.pack(T)), gamma=gamma_dev(float(g)),
+                          Y=torch.empty((M, N), dtype=torch.float32, device="cuda"),
+                          acc=torch.empty((M, N), dtype=torch.int32, device="cuda"), N=N))
+    plan = B.GroupPlan(probs)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        plan.quant_act()
+        plan.matmul()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    eager = [(host(p["Y"]).copy(), host(p["acc"]).copy()) for p in probs]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        plan.quant_act()
+        plan.matmul()
+    Xo = dev(synth.activations_np(7, 300, seed=999))
+    for rep in range(4):
+        for p in probs:
+            p["Y"].fill_(-1.0)
+            p["acc"].fill_(-1)
+        B.quant_act(Xo)  # unrelated eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for p, (Y, acc), (ref, g) in zip(probs, eager, refs):
+            np.testing.assert_array_equal(host(p["Y"]), Y, err_msg=f"replay {rep}")
+            np.testing.assert_array_equal(host(p["acc"]), acc, err_msg=f"replay {rep}")
+            check_outputs(host(p["Y"]), host(p["acc"]), ref["acc"], float(g), ref["absmax"],
+                          f"graph replay {rep}")
+
+
 FUSED_SCRIPT = r'''
 import numpy as np, torch, sys
 sys.path.insert(0, ".")
