@@ -40,6 +40,8 @@ def lib():
         L.oracle_unpack.argtypes = [_vp, _i64, _i64, _vp]
         L.oracle_quant_act.restype = None
         L.oracle_quant_act.argtypes = [_vp, _i64, _i64, _vp, _vp, _vp]
+        L.oracle_rmsnorm_quant_act.restype = None
+        L.oracle_rmsnorm_quant_act.argtypes = [_vp, _i64, _i64, _vp, _f32, _vp, _vp, _vp, _vp, _vp]
         for name in ("oracle_matmul", "oracle_matmul_addsub"):
             f = getattr(L, name)
             f.restype = None
@@ -118,6 +120,23 @@ def quant_act(X):
     rs = np.empty(M, np.int32)
     lib().oracle_quant_act(_p(X), M, K, _p(Q), _p(a), _p(rs))
     return Q, a, rs
+
+
+def rmsnorm_quant_act(X, g=None, eps=1e-5):
+    """RMSNorm (gain g, all ones when None) then the absmax int8 cast:
+    (Q int8 M x K, absmax fp32 [M], rowsum int32 [M], Xn fp32 M x K,
+    inv fp32 [M])."""
+    X = _c(X, np.float32)
+    M, K = X.shape
+    gp = None if g is None else _c(g, np.float32)
+    Q = np.empty((M, K), np.int8)
+    a = np.empty(M, np.float32)
+    rs = np.empty(M, np.int32)
+    Xn = np.empty((M, K), np.float32)
+    inv = np.empty(M, np.float32)
+    lib().oracle_rmsnorm_quant_act(_p(X), M, K, None if gp is None else _p(gp), eps, _p(Xn),
+                                   _p(inv), _p(Q), _p(a), _p(rs))
+    return Q, a, rs, Xn, inv
 
 
 def matmul(Q, T):

@@ -32,6 +32,8 @@
  *  R4  output y = (float)acc * c with c = (gamma * a) / 127 in fp32
  *      (multiply, then divide).
  *  R5  the 2-bit packed format "BL2-T64" defined at oracle_pack below.
+ *  R13 the sub-layer norm before the activation cast is RMSNorm with a
+ *      per-channel gain (oracle_rmsnorm_quant_act).
  *
  * Parity pins: every function below is pinned by tests/test_oracle_pins.py
  * against closed forms, hand-derived fixtures (tests/golden/), library
@@ -180,6 +182,39 @@ void oracle_quant_act(const float *X, int64_t M, int64_t K,
         absmax[m] = a;
         if (rowsum) rowsum[m] = sum;
     }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Sub-layer norm before the activation cast ([YT] "Transcription": BitNet   */
+/* adds a sub-layer norm for stability; the pages give no formula).          */
+/* Reading R13: RMSNorm with a per-channel gain g (all ones when absent):    */
+/*   inv = (float)(1 / sqrt(sum_k x_k^2 / K + eps)), fp64 throughout, one     */
+/*         rounding to fp32 at the end;                                      */
+/*   xn_k = (x_k * inv) * g_k, two fp32 roundings in that order;             */
+/* then the absmax int8 cast of xn (R3).  Xn (nullable) receives xn.         */
+/* ------------------------------------------------------------------------ */
+
+void oracle_rmsnorm_quant_act(const float *X, int64_t M, int64_t K, const float *g, float eps,
+                              float *Xn, float *inv_out, int8_t *Q, float *absmax,
+                              int32_t *rowsum)
+{
+    float *row = (float *)malloc((size_t)K * sizeof(float));
+    for (int64_t m = 0; m < M; ++m) {
+        double s2 = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            double v = (double)X[m * K + k];
+            s2 += v * v;
+        }
+        float inv = (float)(1.0 / sqrt(s2 / (double)K + (double)eps));
+        for (int64_t k = 0; k < K; ++k) {
+            float v = X[m * K + k] * inv;
+            row[k] = v * (g ? g[k] : 1.0f);
+            if (Xn) Xn[m * K + k] = row[k];
+        }
+        if (inv_out) inv_out[m] = inv;
+        oracle_quant_act(row, 1, K, Q + m * K, absmax + m, rowsum ? rowsum + m : NULL);
+    }
+    free(row);
 }
 
 /* ------------------------------------------------------------------------ */

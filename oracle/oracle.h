@@ -19,6 +19,9 @@ void    oracle_pack(const int8_t *T, int64_t N, int64_t K, uint8_t *P);
 int64_t oracle_unpack(const uint8_t *P, int64_t N, int64_t K, int8_t *T);
 void    oracle_quant_act(const float *X, int64_t M, int64_t K,
                          int8_t *Q, float *absmax, int32_t *rowsum);
+void    oracle_rmsnorm_quant_act(const float *X, int64_t M, int64_t K, const float *g,
+                                 float eps, float *Xn, float *inv_out, int8_t *Q,
+                                 float *absmax, int32_t *rowsum);
 void    oracle_matmul(const int8_t *Q, const int8_t *T, int64_t M, int64_t N, int64_t K,
                       int32_t *acc);
 void    oracle_matmul_addsub(const int8_t *Q, const int8_t *T, int64_t M, int64_t N,

@@ -428,3 +428,86 @@ def test_outlier_channels_raise_only_their_token_scale():
     Q2, a2, _ = O.quant_act(X2)
     np.testing.assert_array_equal(Q2[1:], Qc[1:])
     np.testing.assert_array_equal(a2[1:], ac[1:])
+
+
+# ------------------------------------------ RMSNorm + int8 cast (NEXT-1) --
+
+def _rms_fixtures():
+    rows = []
+    for line in _golden("rmsnorm_fixtures.txt"):
+        if not line.strip() or line.startswith("#"):
+            continue
+        head, x, q, rs = [f.strip() for f in line.split("|")]
+        K, eps, g = head.split()
+        g = None if g == "1" else np.array([float(v) for v in g.split(",")], np.float32)
+        rows.append((int(K), float(eps), g, np.array([float(v) for v in x.split(",")], np.float32),
+                     np.array([int(v) for v in q.split(",")]), int(rs)))
+    return rows
+
+
+def test_rmsnorm_golden_fixtures():
+    # hand-derived worked examples (tests/golden/rmsnorm_fixtures.txt)
+    for K, eps, g, x, q, rs in _rms_fixtures():
+        Q, a, r, Xn, inv = O.rmsnorm_quant_act(x[None, :], g, eps)
+        np.testing.assert_array_equal(Q[0], q)
+        assert r[0] == rs
+
+
+def test_rmsnorm_matches_float64_definition():
+    # x_hat against the definition evaluated in float64 (three fp32 roundings
+    # separate them: inv, x*inv, *g), and the codes against the plain int8
+    # cast of the oracle's own x_hat (the composition the reading states)
+    rng = np.random.default_rng(11)
+    for M, K, eps in [(3, 37, 1e-5), (4, 1000, 1e-5), (2, 4096, 1e-6), (2, 300, 10.0)]:
+        X = (rng.standard_normal((M, K)) * rng.uniform(0.1, 10)).astype(np.float32)
+        g = rng.standard_normal(K).astype(np.float32)
+        Q, a, rs, Xn, inv = O.rmsnorm_quant_act(X, g, eps)
+        x64 = X.astype(np.float64)
+        want = x64 / np.sqrt((x64 * x64).mean(axis=1, keepdims=True) + eps) * g.astype(np.float64)
+        rel = np.abs(Xn - want) / np.maximum(np.abs(want), 1e-30)
+        assert rel.max() <= 4e-7, rel.max()
+        inv64 = 1.0 / np.sqrt((x64 * x64).mean(axis=1) + eps)
+        assert np.all(np.abs(inv - inv64) / inv64 <= 6e-8)
+        Q2, a2, rs2 = O.quant_act(Xn)
+        np.testing.assert_array_equal(Q, Q2)
+        np.testing.assert_array_equal(a, a2)
+        np.testing.assert_array_equal(rs, rs2)
+
+
+def test_rmsnorm_power_of_two_invariance():
+    # with eps = 0 RMSNorm is scale-free, and scaling x by 2^j is exact in
+    # floating point at every step: identical x_hat and codes, inv scaled by
+    # 2^-j exactly; scaling g by 2 doubles x_hat exactly and keeps the codes
+    rng = np.random.default_rng(12)
+    X = rng.standard_normal((6, 777)).astype(np.float32)
+    g = rng.uniform(-2, 2, 777).astype(np.float32)
+    Q, a, rs, Xn, inv = O.rmsnorm_quant_act(X, g, 0.0)
+    for j in (-3, 5):
+        Qj, aj, rsj, Xnj, invj = O.rmsnorm_quant_act(X * np.float32(2.0 ** j), g, 0.0)
+        np.testing.assert_array_equal(Qj, Q)
+        np.testing.assert_array_equal(Xnj, Xn)
+        np.testing.assert_array_equal(invj, inv * np.float32(2.0 ** -j))
+    Q2, a2, rs2, Xn2, _ = O.rmsnorm_quant_act(X, g * np.float32(2), 0.0)
+    np.testing.assert_array_equal(Q2, Q)
+    np.testing.assert_array_equal(Xn2, Xn * 2)
+    np.testing.assert_array_equal(a2, a * 2)
+
+
+def test_rmsnorm_special_cases():
+    # no gain == unit gain; a zero row stays zero (inv = 1/sqrt(eps), codes 0,
+    # absmax at its floor); a constant row normalizes to +-1 -> +-127
+    rng = np.random.default_rng(13)
+    X = rng.standard_normal((3, 64)).astype(np.float32)
+    A = O.rmsnorm_quant_act(X, None, 1e-5)
+    B = O.rmsnorm_quant_act(X, np.ones(64, np.float32), 1e-5)
+    for u, v in zip(A, B):
+        np.testing.assert_array_equal(u, v)
+    Z = np.zeros((1, 64), np.float32)
+    Q, a, rs, Xn, inv = O.rmsnorm_quant_act(Z, None, 1e-4)
+    assert not Q.any() and a[0] == np.float32(1e-5) and rs[0] == 0
+    assert inv[0] == np.float32(100.0)
+    C = np.full((1, 64), -0.25, np.float32)
+    C[0, 1::2] = 0.25
+    Q, a, rs, Xn, inv = O.rmsnorm_quant_act(C, None, 0.0)
+    np.testing.assert_array_equal(np.abs(Q), 127)
+    assert rs[0] == 0

@@ -183,8 +183,8 @@ def test_pack_golden_single_codes(B):
 # ---------------------------------------------------------- contraction ------
 
 MM_CASES = [
-    # (M, N, K): dot4 (M=1), streaming MFMA (2..32), tile MFMA (33..64 -> 64-token
-    # tiles, > 64 -> 128-token tiles); ragged N and K tails throughout
+    # (M, N, K): dot4 (M=1), streaming MFMA (2..32), tile MFMA (64- or 128-token
+    # tiles, whichever pads less); ragged N and K tails throughout
     (1, 64, 64), (1, 100, 200), (1, 257, 640), (1, 640, 2560),
     (2, 64, 64), (3, 100, 200), (8, 257, 640), (17, 640, 2560), (32, 130, 1000),
     (33, 64, 64), (40, 100, 200), (64, 257, 640), (65, 130, 1000), (128, 640, 2560),
@@ -225,6 +225,22 @@ def test_matmul_split_k(B, M, N, K):
     for _ in range(2):  # twice: the arrival counters must be reset between calls
         Y, acc = B.matmul(Qd, dev(a), dev(rs), Pd, gamma_dev(0.5), N, K, with_acc=True)
         check_outputs(host(Y), host(acc), ref, 0.5, a, "split-K")
+
+
+@pytest.mark.parametrize("M,N,K", [(24, 64, 8192), (32, 520, 4000), (17, 64, 131072), (2, 64, 131072)])
+def test_forward_split_k(B, M, N, K):
+    # the forward call quantizes itself: above 16 tokens the streaming MFMA
+    # kernel reads fragment-ordered activations; few tile groups and a long K
+    # split it over workgroups (partial sums + arrival tickets); twice, so the
+    # tickets must come back to zero
+    say("forward split-K", M, N, K)
+    T = synth.random_ternary(N, K, seed=N + K)
+    X = synth.activations_np(M, K, seed=M + K, outlier_frac=0.01)
+    ref = O.forward(X, T, np.float32(0.03))
+    Xd, Pd = dev(X), dev(O.pack(T))
+    for _ in range(2):
+        Y, acc = B.forward(Xd, Pd, gamma_dev(0.03), N, with_acc=True)
+        check_outputs(host(Y), host(acc), ref["acc"], 0.03, ref["absmax"], "forward split-K")
 
 
 def test_extreme_values_exact(B):
