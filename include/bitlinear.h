@@ -146,6 +146,22 @@ int bitlinear_quant_act(const float *X, int64_t M, int64_t K, int8_t *Q_out, int
                         float *absmax_out, int32_t *rowsum_out, void *stream);
 
 /*
+ * Sub-layer norm, then the per-token absmax int8 cast, in one pass over X
+ * (BitNet b1.58 2B4T video transcript, yousumm.com, "Transcription": a
+ * sub-layer norm sits before the quantized layers; the formula is not
+ * given -- the reading taken is RMSNorm with a per-channel gain):
+ *   inv[m]   = (float)(1 / sqrt(sum_k X[m][k]^2 / K + eps)), fp64 inside;
+ *   Xhat[m][k] = (X[m][k] * inv[m]) * norm_weight[k] (two fp32 roundings);
+ *   then exactly bitlinear_quant_act on Xhat (absmax_out is max |Xhat|).
+ *   norm_weight [in] K fp32 gains, 4-byte aligned; NULL means all ones.
+ *   eps          >= 0 and finite, else BITLINEAR_ERR_ARG.
+ *   Other arguments, layouts and errors as bitlinear_quant_act.
+ */
+int bitlinear_quant_act_rmsnorm(const float *X, int64_t M, int64_t K, const float *norm_weight,
+                                float eps, int8_t *Q_out, int64_t ldq, float *absmax_out,
+                                int32_t *rowsum_out, void *stream);
+
+/*
  * Ternary x int8 contraction and rescale from already-quantized activations
  * (lets a caller supply Q, a and the row sums itself).
  *   Q       [in]  M rows of ldq bytes, ldq >= bitlinear_q_stride(K),

@@ -59,6 +59,8 @@ def lib():
             "bitlinear_pack": (_int, [_vp, _i64, _i64, _vp, _vp]),
             "bitlinear_unpack": (_int, [_vp, _i64, _i64, _vp, _vp]),
             "bitlinear_quant_act": (_int, [_vp, _i64, _i64, _vp, _i64, _vp, _vp, _vp]),
+            "bitlinear_quant_act_rmsnorm": (_int, [_vp, _i64, _i64, _vp, ctypes.c_float, _vp, _i64, _vp,
+                                                   _vp, _vp]),
             "bitlinear_matmul": (_int, [_vp, _i64, _vp, _vp, _i64, _i64, _vp, _vp, _i64, _vp, _vp,
                                         _vp, _sz, _vp]),
             "bitlinear_forward": (_int, [_vp, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _vp, _sz, _vp]),
@@ -158,6 +160,23 @@ def quant_act(X, ldq: int | None = None, stream=None):
     rs = torch.empty(M, dtype=torch.int32, device=X.device)
     _check(lib().bitlinear_quant_act(_ptr(X), M, K, _ptr(Q), ldq, _ptr(a), _ptr(rs),
                                      _stream(stream)), "quant_act")
+    return Q, a, rs
+
+
+def quant_act_rmsnorm(X, norm_weight=None, eps: float = 1e-5, ldq: int | None = None, stream=None):
+    """RMSNorm (gain norm_weight, all ones when None) then the absmax int8
+    cast: (Q int8 M x ldq, absmax fp32 [M] of the normalized rows, rowsum
+    int32 [M])."""
+    _dev_tensor(X, torch.float32, "X")
+    if norm_weight is not None:
+        _dev_tensor(norm_weight, torch.float32, "norm_weight")
+    M, K = X.shape
+    ldq = q_stride(K) if ldq is None else ldq
+    Q = torch.empty((M, ldq), dtype=torch.int8, device=X.device)
+    a = torch.empty(M, dtype=torch.float32, device=X.device)
+    rs = torch.empty(M, dtype=torch.int32, device=X.device)
+    _check(lib().bitlinear_quant_act_rmsnorm(_ptr(X), M, K, _ptr(norm_weight), float(eps), _ptr(Q), ldq,
+                                             _ptr(a), _ptr(rs), _stream(stream)), "quant_act_rmsnorm")
     return Q, a, rs
 
 

@@ -10,7 +10,8 @@
 // One workgroup per token (one wave when there are many tokens, four for
 // few): the row is read with 16-byte loads (kept in registers up to 8192
 // values), |x| and the code sum are reduced with wave butterflies, and the
-// codes are written four per 4-byte store.  The max is order-free and the row sum is an
+// codes are written four per 4-byte store.  A variant applies the sub-layer
+// norm (RMSNorm) to the row first, in the same pass over X.  The max is order-free and the row sum is an
 // integer sum, so both are exact whatever the reduction order.
 #include "common.hpp"
 
@@ -38,47 +39,117 @@ struct QDest {
 // groups t, t + 64 * WAVES, ... of the row, so each 16-byte load of a wave
 // reads 1 KiB of contiguous X and each 4-byte code store writes 256
 // contiguous bytes of Q.  Rows of up to kRegF4 * 64 * 4 values stay in
-// registers between the max and the rounding pass, so X is read from HBM
-// once (longer rows are read twice, the second time mostly from L2).  The
-// reductions are wave butterflies, joined through LDS when WAVES > 1.  Many
-// tokens: one wave each (no barrier); few tokens (decode): four waves each,
-// so the loads of one row are spread over more lanes.
+// registers between the passes, so X is read from HBM once (longer rows are
+// read again, mostly from L2).  The reductions are wave butterflies, joined
+// through LDS when WAVES > 1.  Many tokens: one wave each (no barrier); few
+// tokens (decode): four waves each, so the loads of one row are spread over
+// more lanes.
+//
+// NORM: the sub-layer norm first ([YT] "Transcription" names it; the
+// reading taken is RMSNorm with a per-channel gain g):
+// inv = (float)(1 / sqrt(sum x^2 / K + eps)) with the sum and the square
+// root in fp64, then x_hat = (x * inv) * g in fp32, and the cast below runs
+// on x_hat.  The fp64 sum runs per thread, then across lanes, then across
+// waves in a fixed order, so it is deterministic.
 constexpr int kRegF4 = 32;
 constexpr int kFewTokens = 2048;
 
-template <int WAVES>
-__device__ void quant_row(const float *x_, int K, const QDest &dst, float *absmax_, int32_t *rowsum_)
+template <int WAVES, bool NORM>
+__device__ void quant_row(const float *x_, int K, const QDest &dst, float *absmax_, int32_t *rowsum_,
+                          const float *g_, float eps)
 {
     constexpr int kThr = 64 * WAVES;
     constexpr int kRegs = kRegF4 / WAVES;
     __shared__ float red_a[WAVES];
     __shared__ int red_s[WAVES];
+    __shared__ double red_d[WAVES];
     const int t = threadIdx.x, lane = t & 63, w = t >> 6;
     const BL_GLOBAL float *x = gload_ptr<float>(x_);
+    const BL_GLOBAL float *gw = gload_ptr<float>(g_);
     BL_GLOBAL int8_t *q = gstore_ptr<int8_t>(dst.Q);
-    // float4 path: K a multiple of 4 and the row 16-byte aligned
-    const bool vec = ((K & 3) == 0) && ((reinterpret_cast<uintptr_t>(x_) & 15) == 0);
+    // float4 path: K a multiple of 4 and the rows (and gains) 16-byte aligned
+    const bool vec = ((K & 3) == 0) && ((reinterpret_cast<uintptr_t>(x_) & 15) == 0) &&
+                     (!NORM || !g_ || (reinterpret_cast<uintptr_t>(g_) & 15) == 0);
     const int nf = K >> 2;
     const BL_GLOBAL v4f *x4 = reinterpret_cast<const BL_GLOBAL v4f *>(x);
+    const BL_GLOBAL v4f *g4 = reinterpret_cast<const BL_GLOBAL v4f *>(gw);
     const bool in_regs = vec && nf <= kRegs * kThr;
     const v4f zero4 = {0.f, 0.f, 0.f, 0.f};
 
-    auto amax4 = [](v4f v) {
-        return fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
-    };
     v4f v[kRegs];
-    float a = 0.0f;
     if (in_regs) {
 #pragma unroll
         for (int j = 0; j < kRegs; ++j) {
             const int f = t + kThr * j;
             v[j] = f < nf ? __builtin_nontemporal_load(x4 + f) : zero4;
-            a = fmaxf(a, amax4(v[j]));
         }
+    }
+
+    float inv = 1.0f;
+    if constexpr (NORM) {
+        auto sq4 = [](v4f u) {
+            double d = (double)u.x * (double)u.x;
+            d += (double)u.y * (double)u.y;
+            d += (double)u.z * (double)u.z;
+            d += (double)u.w * (double)u.w;
+            return d;
+        };
+        double s2 = 0.0;
+        if (in_regs) {
+#pragma unroll
+            for (int j = 0; j < kRegs; ++j) s2 += sq4(v[j]);
+        } else if (vec) {
+            for (int f = t; f < nf; f += kThr) s2 += sq4(x4[f]);
+        } else {
+            for (int i = t; i < K; i += kThr) s2 += (double)x[i] * (double)x[i];
+        }
+        for (int off = 32; off > 0; off >>= 1) s2 += __shfl_xor(s2, off, 64);
+        if constexpr (WAVES > 1) {
+            if (lane == 0) red_d[w] = s2;
+            __syncthreads();
+            s2 = red_d[0];
+#pragma unroll
+            for (int i = 1; i < WAVES; ++i) s2 += red_d[i];
+        }
+        inv = (float)(1.0 / sqrt(s2 / (double)K + (double)eps));
+    }
+    // x_hat of float4 group f / element i (x itself without the norm)
+    auto norm4 = [&](v4f u, int f) {
+        if constexpr (NORM) {
+            u = u * inv;
+            if (g_) u = u * g4[f];
+        }
+        return u;
+    };
+    auto norm1 = [&](int i) {
+        float u = x[i];
+        if constexpr (NORM) {
+            u = u * inv;
+            if (g_) u = u * gw[i];
+        }
+        return u;
+    };
+    if constexpr (NORM) {
+        if (in_regs) {
+#pragma unroll
+            for (int j = 0; j < kRegs; ++j) {
+                const int f = t + kThr * j;
+                if (f < nf) v[j] = norm4(v[j], f);
+            }
+        }
+    }
+
+    auto amax4 = [](v4f u) {
+        return fmaxf(fmaxf(fabsf(u.x), fabsf(u.y)), fmaxf(fabsf(u.z), fabsf(u.w)));
+    };
+    float a = 0.0f;
+    if (in_regs) {
+#pragma unroll
+        for (int j = 0; j < kRegs; ++j) a = fmaxf(a, amax4(v[j]));
     } else if (vec) {
-        for (int f = t; f < nf; f += kThr) a = fmaxf(a, amax4(x4[f]));
+        for (int f = t; f < nf; f += kThr) a = fmaxf(a, amax4(norm4(x4[f], f)));
     } else {
-        for (int i = t; i < K; i += kThr) a = fmaxf(a, fabsf(x[i]));
+        for (int i = t; i < K; i += kThr) a = fmaxf(a, fabsf(norm1(i)));
     }
     for (int off = 32; off > 0; off >>= 1) a = fmaxf(a, __shfl_xor(a, off, 64));
     if constexpr (WAVES > 1) {
@@ -107,10 +178,10 @@ __device__ void quant_row(const float *x_, int K, const QDest &dst, float *absma
             if (f < nf) put4(f, v[j]);
         }
     } else if (vec) {
-        for (int f = t; f < nf; f += kThr) put4(f, x4[f]);
+        for (int f = t; f < nf; f += kThr) put4(f, norm4(x4[f], f));
     } else {
         for (int i = t; i < K; i += kThr) {
-            const int8_t c = quant_code(x[i], s);
+            const int8_t c = quant_code(norm1(i), s);
             sum += c;
             q[dst.at(i)] = c;
         }
@@ -131,19 +202,20 @@ __device__ void quant_row(const float *x_, int K, const QDest &dst, float *absma
 }
 
 // One workgroup per token.
-template <int WAVES>
+template <int WAVES, bool NORM>
 __global__ __launch_bounds__(64 * WAVES) void quant_act_kernel(const float *__restrict__ X, int K,
                                                                int8_t *__restrict__ Q, int64_t ldq,
                                                                int qtiled, float *__restrict__ absmax,
                                                                int32_t *__restrict__ rowsum,
                                                                uint32_t *__restrict__ zero_ptr,
-                                                               int zero_n)
+                                                               int zero_n, const float *__restrict__ g,
+                                                               float eps)
 {
     const int64_t m = blockIdx.x;
     if (m == 0 && zero_ptr)
         for (int i = threadIdx.x; i < zero_n; i += 64 * WAVES) zero_ptr[i] = 0u;
     const QDest dst{Q, ldq, m, (K + 63) / 64, qtiled};
-    quant_row<WAVES>(X + m * K, K, dst, absmax + m, rowsum ? rowsum + m : nullptr);
+    quant_row<WAVES, NORM>(X + m * K, K, dst, absmax + m, rowsum ? rowsum + m : nullptr, g, eps);
 }
 
 template <int WAVES>
@@ -156,7 +228,7 @@ __global__ __launch_bounds__(64 * WAVES) void quant_act_group_kernel(const Probl
     if (m == 0 && p.tickets)
         for (int i = threadIdx.x; i < p.NT; i += 64 * WAVES) p.tickets[i] = 0u;
     const QDest dst{p.Q, p.ldq, m, p.KU, p.qtiled};
-    quant_row<WAVES>(p.X + m * p.K, p.K, dst, p.absmax + m, p.rowsum + m);
+    quant_row<WAVES, false>(p.X + m * p.K, p.K, dst, p.absmax + m, p.rowsum + m, nullptr, 0.0f);
 }
 
 __global__ __launch_bounds__(kThreads) void zero_words_kernel(uint32_t *__restrict__ p, int64_t n)
@@ -172,11 +244,24 @@ hipError_t launch_quant_act(const float *X, int64_t M, int64_t K, int8_t *Q, int
                             int zero_n, hipStream_t s)
 {
     if (M < kFewTokens)
-        hipLaunchKernelGGL(quant_act_kernel<4>, dim3((unsigned)M), dim3(256), 0, s, X, (int)K, Q, ldq,
-                           qtiled, absmax, rowsum, zero_ptr, zero_n);
+        hipLaunchKernelGGL((quant_act_kernel<4, false>), dim3((unsigned)M), dim3(256), 0, s, X, (int)K, Q,
+                           ldq, qtiled, absmax, rowsum, zero_ptr, zero_n, nullptr, 0.0f);
     else
-        hipLaunchKernelGGL(quant_act_kernel<1>, dim3((unsigned)M), dim3(64), 0, s, X, (int)K, Q, ldq,
-                           qtiled, absmax, rowsum, zero_ptr, zero_n);
+        hipLaunchKernelGGL((quant_act_kernel<1, false>), dim3((unsigned)M), dim3(64), 0, s, X, (int)K, Q,
+                           ldq, qtiled, absmax, rowsum, zero_ptr, zero_n, nullptr, 0.0f);
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_act_rmsnorm(const float *X, int64_t M, int64_t K, const float *g, float eps,
+                                    int8_t *Q, int64_t ldq, float *absmax, int32_t *rowsum,
+                                    hipStream_t s)
+{
+    if (M < kFewTokens)
+        hipLaunchKernelGGL((quant_act_kernel<4, true>), dim3((unsigned)M), dim3(256), 0, s, X, (int)K, Q,
+                           ldq, 0, absmax, rowsum, nullptr, 0, g, eps);
+    else
+        hipLaunchKernelGGL((quant_act_kernel<1, true>), dim3((unsigned)M), dim3(64), 0, s, X, (int)K, Q,
+                           ldq, 0, absmax, rowsum, nullptr, 0, g, eps);
     return hipGetLastError();
 }
 

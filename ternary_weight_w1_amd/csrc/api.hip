@@ -329,6 +329,26 @@ int bitlinear_quant_act(const float *X, int64_t M, int64_t K, int8_t *Q_out, int
     return BITLINEAR_OK;
 }
 
+int bitlinear_quant_act_rmsnorm(const float *X, int64_t M, int64_t K, const float *norm_weight, float eps,
+                                int8_t *Q_out, int64_t ldq, float *absmax_out, int32_t *rowsum_out,
+                                void *stream)
+{
+    if (!X || !Q_out || !absmax_out)
+        return fail(BITLINEAR_ERR_NULL, "quant_act_rmsnorm: X, Q_out and absmax_out are required");
+    if (int st = check_mnk(M, 1, K)) return st;
+    if (ldq < K || ldq % 16 != 0)
+        return fail(BITLINEAR_ERR_SHAPE, "quant_act_rmsnorm: ldq=%lld must be >= K and a multiple of 16", (long long)ldq);
+    if (!(eps >= 0.0f) || !(eps <= 3.0e38f))
+        return fail(BITLINEAR_ERR_ARG, "quant_act_rmsnorm: eps must be finite and >= 0");
+    if (!a16(X) || !a16(Q_out) || !a4(absmax_out) || (rowsum_out && !a4(rowsum_out)) ||
+        (norm_weight && !a4(norm_weight)))
+        return fail(BITLINEAR_ERR_ALIGN, "quant_act_rmsnorm: X/Q_out need 16-byte, absmax/rowsum/norm_weight 4-byte alignment");
+    if (hipError_t e = bl::launch_quant_act_rmsnorm(X, M, K, norm_weight, eps, Q_out, ldq, absmax_out,
+                                                    rowsum_out, static_cast<hipStream_t>(stream)))
+        return hip_fail(e, "quant_act_rmsnorm");
+    return BITLINEAR_OK;
+}
+
 int bitlinear_matmul(const int8_t *Q, int64_t ldq, const float *absmax, const int32_t *rowsum,
                      int64_t M, int64_t K, const uint8_t *P, const float *gamma, int64_t N,
                      float *Y_out, int32_t *acc_out, void *ws, size_t ws_bytes, void *stream)

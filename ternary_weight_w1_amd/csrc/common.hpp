@@ -125,6 +125,9 @@ hipError_t launch_unpack(const uint8_t *P, int64_t N, int64_t K, int8_t *T, hipS
 hipError_t launch_quant_act(const float *X, int64_t M, int64_t K, int8_t *Q, int64_t ldq,
                             int qtiled, float *absmax, int32_t *rowsum, uint32_t *zero_ptr,
                             int zero_n, hipStream_t s);
+hipError_t launch_quant_act_rmsnorm(const float *X, int64_t M, int64_t K, const float *g, float eps,
+                                    int8_t *Q, int64_t ldq, float *absmax, int32_t *rowsum,
+                                    hipStream_t s);
 hipError_t launch_quant_act_group(const Problem *probs, const uint32_t *tok_map, int n_tokens,
                                   hipStream_t s);
 hipError_t launch_zero_words(uint32_t *p, int64_t n, hipStream_t s);

@@ -110,6 +110,43 @@ def test_quant_act_parity(B, M, K, outliers):
         np.testing.assert_array_equal(host(rsg), rs)
 
 
+@pytest.mark.parametrize("M,K,gain,eps", [(1, 2560, True, 1e-5), (3, 37, True, 1e-6), (4, 100, False, 0.0),
+                                          (7, 6912, True, 1e-5), (1, 28672, True, 1e-5),
+                                          (2049, 2560, True, 1e-5), (2050, 10004, False, 1e-6),
+                                          (2048, 37, True, 1e-5), (5, 64, True, 10.0)])
+def test_quant_act_rmsnorm_parity(B, M, K, gain, eps):
+    # sub-layer norm + cast in one pass: every path of the kernel (4-wave and
+    # 1-wave workgroups; registers, re-read and scalar rows) against the
+    # oracle -- codes, scales and row sums bit-exact
+    say("quant_act_rmsnorm", M, K, gain, eps)
+    X = synth.activations_np(M, K, seed=M * 17 + K, outlier_frac=0.01)
+    if M > 2:
+        X[1] = 0.0                      # an all-zero token
+    g = synth.activations_np(1, K, seed=K + 5)[0] if gain else None
+    Q, a, rs, Xn, inv = O.rmsnorm_quant_act(X, g, eps)
+    Qg, ag, rsg = B.quant_act_rmsnorm(dev(X), None if g is None else dev(g), eps)
+    Qg = host(Qg)
+    np.testing.assert_array_equal(Qg[:, :K], Q)
+    assert not Qg[:, K:].any()
+    np.testing.assert_array_equal(host(ag), a)
+    np.testing.assert_array_equal(host(rsg), rs)
+
+
+def test_rmsnorm_then_contraction(B):
+    # norm + cast, then the contraction on the library's own codes, equals the
+    # oracle's whole layer on the normalized rows
+    say("rmsnorm -> matmul")
+    M, N, K = 6, 257, 2560
+    X = synth.activations_np(M, K, seed=41, outlier_frac=0.01)
+    g = synth.activations_np(1, K, seed=42)[0]
+    T = synth.random_ternary(N, K, seed=43)
+    Q, a, rs, Xn, inv = O.rmsnorm_quant_act(X, g, 1e-5)
+    ref = O.matmul(Q, T)
+    Qg, ag, rsg = B.quant_act_rmsnorm(dev(X), dev(g), 1e-5)
+    Y, acc = B.matmul(Qg, ag, rsg, dev(O.pack(T)), gamma_dev(0.02), N, K, with_acc=True)
+    check_outputs(host(Y), host(acc), ref, 0.02, a, "rmsnorm -> matmul")
+
+
 def test_quant_act_unaligned_stride_rows(B):
     # K not a multiple of 4 takes the scalar path; ldq = K rounded to 16
     say("quant_act scalar path")
