@@ -40,6 +40,8 @@ def lib():
         L.oracle_unpack.argtypes = [_vp, _i64, _i64, _vp]
         L.oracle_quant_act.restype = None
         L.oracle_quant_act.argtypes = [_vp, _i64, _i64, _vp, _vp, _vp]
+        L.oracle_relu2_gate_quant_act.restype = None
+        L.oracle_relu2_gate_quant_act.argtypes = [_vp, _vp, _i64, _i64, _vp, _vp, _vp, _vp]
         L.oracle_rmsnorm_quant_act.restype = None
         L.oracle_rmsnorm_quant_act.argtypes = [_vp, _i64, _i64, _vp, _f32, _vp, _vp, _vp, _vp, _vp]
         for name in ("oracle_matmul", "oracle_matmul_addsub"):
@@ -137,6 +139,21 @@ def rmsnorm_quant_act(X, g=None, eps=1e-5):
     lib().oracle_rmsnorm_quant_act(_p(X), M, K, None if gp is None else _p(gp), eps, _p(Xn),
                                    _p(inv), _p(Q), _p(a), _p(rs))
     return Q, a, rs, Xn, inv
+
+
+def relu2_gate_quant_act(G, U):
+    """Gated squared-ReLU h = relu(G)^2 * U, then the absmax int8 cast:
+    (Q int8 M x N, absmax fp32 [M], rowsum int32 [M], H fp32 M x N)."""
+    G = _c(G, np.float32)
+    U = _c(U, np.float32)
+    assert G.shape == U.shape
+    M, N = G.shape
+    Q = np.empty((M, N), np.int8)
+    a = np.empty(M, np.float32)
+    rs = np.empty(M, np.int32)
+    H = np.empty((M, N), np.float32)
+    lib().oracle_relu2_gate_quant_act(_p(G), _p(U), M, N, _p(H), _p(Q), _p(a), _p(rs))
+    return Q, a, rs, H
 
 
 def matmul(Q, T):

@@ -34,6 +34,8 @@
  *  R5  the 2-bit packed format "BL2-T64" defined at oracle_pack below.
  *  R13 the sub-layer norm before the activation cast is RMSNorm with a
  *      per-channel gain (oracle_rmsnorm_quant_act).
+ *  R14 the squared-ReLU feed-forward is gated: h = relu(gate)^2 * up
+ *      (oracle_relu2_gate_quant_act).
  *
  * Parity pins: every function below is pinned by tests/test_oracle_pins.py
  * against closed forms, hand-derived fixtures (tests/golden/), library
@@ -213,6 +215,32 @@ void oracle_rmsnorm_quant_act(const float *X, int64_t M, int64_t K, const float 
         }
         if (inv_out) inv_out[m] = inv;
         oracle_quant_act(row, 1, K, Q + m * K, absmax + m, rowsum ? rowsum + m : NULL);
+    }
+    free(row);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Gated squared-ReLU feed-forward activation before the down projection's  */
+/* int8 cast ([YT] "Transcription": BitNet swaps its activation function for */
+/* a squared ReLU; the pages give no formula).  Reading R14: the FFN hidden  */
+/* value is h = relu(g)^2 * u from the gate and up projections' outputs,     */
+/* evaluated in fp32 as r = max(g, 0); h = (r * r) * u (two roundings in     */
+/* that order); then the absmax int8 cast of h (R3).  H (nullable) gets h.   */
+/* ------------------------------------------------------------------------ */
+
+void oracle_relu2_gate_quant_act(const float *G, const float *U, int64_t M, int64_t N, float *H,
+                                 int8_t *Q, float *absmax, int32_t *rowsum)
+{
+    float *row = (float *)malloc((size_t)N * sizeof(float));
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t n = 0; n < N; ++n) {
+            float g = G[m * N + n];
+            float r = g > 0.0f ? g : 0.0f;
+            float sq = r * r;
+            row[n] = sq * U[m * N + n];
+            if (H) H[m * N + n] = row[n];
+        }
+        oracle_quant_act(row, 1, N, Q + m * N, absmax + m, rowsum ? rowsum + m : NULL);
     }
     free(row);
 }

@@ -22,6 +22,8 @@ void    oracle_quant_act(const float *X, int64_t M, int64_t K,
 void    oracle_rmsnorm_quant_act(const float *X, int64_t M, int64_t K, const float *g,
                                  float eps, float *Xn, float *inv_out, int8_t *Q,
                                  float *absmax, int32_t *rowsum);
+void    oracle_relu2_gate_quant_act(const float *G, const float *U, int64_t M, int64_t N,
+                                    float *H, int8_t *Q, float *absmax, int32_t *rowsum);
 void    oracle_matmul(const int8_t *Q, const int8_t *T, int64_t M, int64_t N, int64_t K,
                       int32_t *acc);
 void    oracle_matmul_addsub(const int8_t *Q, const int8_t *T, int64_t M, int64_t N,

@@ -511,3 +511,54 @@ def test_rmsnorm_special_cases():
     Q, a, rs, Xn, inv = O.rmsnorm_quant_act(C, None, 0.0)
     np.testing.assert_array_equal(np.abs(Q), 127)
     assert rs[0] == 0
+
+
+# ------------------------------- gated squared-ReLU + int8 cast (NEXT-2) --
+
+def test_relu2_gate_hand_values():
+    # h = relu(g)^2 * u by hand: g = (-2, 0, 0.5, 3), u = (5, 5, -4, 2)
+    #   -> h = (0, 0, -1, 18); a = 18; q = rint(h * 127/18) = (0, 0, -7, 127)
+    #   (-127/18 = -7.0555... -> -7); rowsum 120
+    G = np.array([[-2, 0, 0.5, 3]], np.float32)
+    U = np.array([[5, 5, -4, 2]], np.float32)
+    Q, a, rs, H = O.relu2_gate_quant_act(G, U)
+    np.testing.assert_array_equal(H[0], [0, 0, -1, 18])
+    np.testing.assert_array_equal(Q[0], [0, 0, -7, 127])
+    assert a[0] == 18 and rs[0] == 120
+
+
+def test_relu2_gate_matches_float64_definition():
+    # h against the definition in float64 (two fp32 roundings apart), and the
+    # codes against the plain int8 cast of the oracle's own h
+    rng = np.random.default_rng(21)
+    for M, N in [(3, 37), (4, 6912), (2, 1000)]:
+        G = (rng.standard_normal((M, N)) * 3).astype(np.float32)
+        U = rng.standard_normal((M, N)).astype(np.float32)
+        Q, a, rs, H = O.relu2_gate_quant_act(G, U)
+        want = np.maximum(G.astype(np.float64), 0) ** 2 * U.astype(np.float64)
+        nz = want != 0
+        assert np.all(H[~nz] == 0)
+        rel = np.abs(H[nz] - want[nz]) / np.abs(want[nz])
+        assert rel.max() <= 2.5e-7, rel.max()
+        Q2, a2, rs2 = O.quant_act(H)
+        np.testing.assert_array_equal(Q, Q2)
+        np.testing.assert_array_equal(rs, rs2)
+
+
+def test_relu2_gate_special_cases():
+    # gate <= 0 everywhere -> zero codes, absmax at its floor; gate = 1 -> the
+    # plain cast of u; negating u negates h and the codes exactly
+    rng = np.random.default_rng(22)
+    U = rng.standard_normal((3, 500)).astype(np.float32)
+    Q, a, rs, H = O.relu2_gate_quant_act(-np.abs(U), U)
+    assert not Q.any() and np.all(a == np.float32(1e-5))
+    Q, a, rs, H = O.relu2_gate_quant_act(np.ones_like(U), U)
+    Q2, a2, rs2 = O.quant_act(U)
+    np.testing.assert_array_equal(Q, Q2)
+    np.testing.assert_array_equal(a, a2)
+    G = rng.standard_normal((3, 500)).astype(np.float32)
+    Qa, aa, rsa, Ha = O.relu2_gate_quant_act(G, U)
+    Qb, ab, rsb, Hb = O.relu2_gate_quant_act(G, -U)
+    np.testing.assert_array_equal(Qb, -Qa)
+    np.testing.assert_array_equal(ab, aa)
+    np.testing.assert_array_equal(rsb, -rsa)
