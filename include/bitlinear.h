@@ -162,6 +162,22 @@ int bitlinear_quant_act_rmsnorm(const float *X, int64_t M, int64_t K, const floa
                                 int32_t *rowsum_out, void *stream);
 
 /*
+ * Gated squared-ReLU feed-forward activation, then the per-token absmax
+ * int8 cast, in one pass: the input of a feed-forward block's down
+ * projection (BitNet b1.58 2B4T video transcript, yousumm.com,
+ * "Transcription": the activation function is a squared ReLU; the formula
+ * is not given -- the reading taken is the gated form
+ *   H[m][n] = (r * r) * U[m][n],  r = max(G[m][n], 0), in fp32),
+ * then exactly bitlinear_quant_act on H (absmax_out is max |H|).
+ *   G, U      [in]  M x N fp32: the gate and up projections' outputs
+ *                   (row-major, 16-byte aligned).
+ *   Q_out, ldq, absmax_out, rowsum_out: as bitlinear_quant_act with K = N.
+ */
+int bitlinear_quant_act_relu2_gate(const float *G, const float *U, int64_t M, int64_t N,
+                                   int8_t *Q_out, int64_t ldq, float *absmax_out,
+                                   int32_t *rowsum_out, void *stream);
+
+/*
  * Ternary x int8 contraction and rescale from already-quantized activations
  * (lets a caller supply Q, a and the row sums itself).
  *   Q       [in]  M rows of ldq bytes, ldq >= bitlinear_q_stride(K),

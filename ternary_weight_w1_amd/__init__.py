@@ -61,6 +61,7 @@ def lib():
             "bitlinear_quant_act": (_int, [_vp, _i64, _i64, _vp, _i64, _vp, _vp, _vp]),
             "bitlinear_quant_act_rmsnorm": (_int, [_vp, _i64, _i64, _vp, ctypes.c_float, _vp, _i64, _vp,
                                                    _vp, _vp]),
+            "bitlinear_quant_act_relu2_gate": (_int, [_vp, _vp, _i64, _i64, _vp, _i64, _vp, _vp, _vp]),
             "bitlinear_matmul": (_int, [_vp, _i64, _vp, _vp, _i64, _i64, _vp, _vp, _i64, _vp, _vp,
                                         _vp, _sz, _vp]),
             "bitlinear_forward": (_int, [_vp, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _vp, _sz, _vp]),
@@ -177,6 +178,24 @@ def quant_act_rmsnorm(X, norm_weight=None, eps: float = 1e-5, ldq: int | None = 
     rs = torch.empty(M, dtype=torch.int32, device=X.device)
     _check(lib().bitlinear_quant_act_rmsnorm(_ptr(X), M, K, _ptr(norm_weight), float(eps), _ptr(Q), ldq,
                                              _ptr(a), _ptr(rs), _stream(stream)), "quant_act_rmsnorm")
+    return Q, a, rs
+
+
+def quant_act_relu2_gate(G, U, ldq: int | None = None, stream=None):
+    """Gated squared-ReLU H = relu(G)^2 * U of the gate and up projections'
+    outputs (M x N fp32 each), then the absmax int8 cast: (Q int8 M x ldq,
+    absmax fp32 [M] of H, rowsum int32 [M])."""
+    _dev_tensor(G, torch.float32, "G")
+    _dev_tensor(U, torch.float32, "U")
+    if G.shape != U.shape:
+        raise ValueError("G and U must have the same shape")
+    M, N = G.shape
+    ldq = q_stride(N) if ldq is None else ldq
+    Q = torch.empty((M, ldq), dtype=torch.int8, device=G.device)
+    a = torch.empty(M, dtype=torch.float32, device=G.device)
+    rs = torch.empty(M, dtype=torch.int32, device=G.device)
+    _check(lib().bitlinear_quant_act_relu2_gate(_ptr(G), _ptr(U), M, N, _ptr(Q), ldq, _ptr(a), _ptr(rs),
+                                                _stream(stream)), "quant_act_relu2_gate")
     return Q, a, rs
 
 

@@ -10,8 +10,10 @@
 // One workgroup per token (one wave when there are many tokens, four for
 // few): the row is read with 16-byte loads (kept in registers up to 8192
 // values), |x| and the code sum are reduced with wave butterflies, and the
-// codes are written four per 4-byte store.  A variant applies the sub-layer
-// norm (RMSNorm) to the row first, in the same pass over X.  The max is order-free and the row sum is an
+// codes are written four per 4-byte store.  Variants cast the RMSNorm of
+// the row (the sub-layer norm before a BitLinear) or the gated squared-ReLU
+// of two rows (the feed-forward hidden value before the down projection),
+// computed in the same pass over the inputs.  The max is order-free and the row sum is an
 // integer sum, so both are exact whatever the reduction order.
 #include "common.hpp"
 
@@ -45,19 +47,25 @@ struct QDest {
 // tokens (decode): four waves each, so the loads of one row are spread over
 // more lanes.
 //
-// NORM: the sub-layer norm first ([YT] "Transcription" names it; the
-// reading taken is RMSNorm with a per-channel gain g):
-// inv = (float)(1 / sqrt(sum x^2 / K + eps)) with the sum and the square
-// root in fp64, then x_hat = (x * inv) * g in fp32, and the cast below runs
-// on x_hat.  The fp64 sum runs per thread, then across lanes, then across
-// waves in a fixed order, so it is deterministic.
+// MODE (what is cast; BitNet b1.58 2B4T video transcript, yousumm.com,
+// "Transcription", names a sub-layer norm and a squared ReLU but gives no
+// formulas -- the readings taken are these):
+//   kPlain     x itself;
+//   kRmsNorm   x_hat = (x * inv) * g with inv = (float)(1 / sqrt(sum x^2 /
+//              K + eps)), the sum and the square root in fp64 (aux = g,
+//              NULL = all ones).  The fp64 sum runs per thread, then across
+//              lanes, then across waves in a fixed order: deterministic;
+//   kRelu2Gate h = (r * r) * u with r = max(x, 0), x the gate projection's
+//              output and u the up projection's (aux = u).
 constexpr int kRegF4 = 32;
 constexpr int kFewTokens = 2048;
+enum { kPlain = 0, kRmsNorm = 1, kRelu2Gate = 2 };
 
-template <int WAVES, bool NORM>
+template <int WAVES, int MODE>
 __device__ void quant_row(const float *x_, int K, const QDest &dst, float *absmax_, int32_t *rowsum_,
                           const float *g_, float eps)
 {
+    constexpr bool NORM = MODE == kRmsNorm;
     constexpr int kThr = 64 * WAVES;
     constexpr int kRegs = kRegF4 / WAVES;
     __shared__ float red_a[WAVES];
@@ -69,19 +77,33 @@ __device__ void quant_row(const float *x_, int K, const QDest &dst, float *absma
     BL_GLOBAL int8_t *q = gstore_ptr<int8_t>(dst.Q);
     // float4 path: K a multiple of 4 and the rows (and gains) 16-byte aligned
     const bool vec = ((K & 3) == 0) && ((reinterpret_cast<uintptr_t>(x_) & 15) == 0) &&
-                     (!NORM || !g_ || (reinterpret_cast<uintptr_t>(g_) & 15) == 0);
+                     (MODE == kPlain || !g_ || (reinterpret_cast<uintptr_t>(g_) & 15) == 0);
     const int nf = K >> 2;
     const BL_GLOBAL v4f *x4 = reinterpret_cast<const BL_GLOBAL v4f *>(x);
     const BL_GLOBAL v4f *g4 = reinterpret_cast<const BL_GLOBAL v4f *>(gw);
     const bool in_regs = vec && nf <= kRegs * kThr;
     const v4f zero4 = {0.f, 0.f, 0.f, 0.f};
 
+    auto relu2 = [](float gv, float uv) {
+        const float r = gv > 0.0f ? gv : 0.0f;
+        return (r * r) * uv;
+    };
+    auto relu2_4 = [&](v4f gv, v4f uv) {
+        v4f h;
+        h.x = relu2(gv.x, uv.x);
+        h.y = relu2(gv.y, uv.y);
+        h.z = relu2(gv.z, uv.z);
+        h.w = relu2(gv.w, uv.w);
+        return h;
+    };
     v4f v[kRegs];
     if (in_regs) {
 #pragma unroll
         for (int j = 0; j < kRegs; ++j) {
             const int f = t + kThr * j;
             v[j] = f < nf ? __builtin_nontemporal_load(x4 + f) : zero4;
+            if constexpr (MODE == kRelu2Gate)
+                if (f < nf) v[j] = relu2_4(v[j], __builtin_nontemporal_load(g4 + f));
         }
     }
 
@@ -113,11 +135,13 @@ __device__ void quant_row(const float *x_, int K, const QDest &dst, float *absma
         }
         inv = (float)(1.0 / sqrt(s2 / (double)K + (double)eps));
     }
-    // x_hat of float4 group f / element i (x itself without the norm)
+    // the value cast, for float4 group f (given x's group) / element i
     auto norm4 = [&](v4f u, int f) {
         if constexpr (NORM) {
             u = u * inv;
             if (g_) u = u * g4[f];
+        } else if constexpr (MODE == kRelu2Gate) {
+            u = relu2_4(u, g4[f]);
         }
         return u;
     };
@@ -126,6 +150,8 @@ __device__ void quant_row(const float *x_, int K, const QDest &dst, float *absma
         if constexpr (NORM) {
             u = u * inv;
             if (g_) u = u * gw[i];
+        } else if constexpr (MODE == kRelu2Gate) {
+            u = relu2(u, gw[i]);
         }
         return u;
     };
@@ -202,7 +228,7 @@ __device__ void quant_row(const float *x_, int K, const QDest &dst, float *absma
 }
 
 // One workgroup per token.
-template <int WAVES, bool NORM>
+template <int WAVES, int MODE>
 __global__ __launch_bounds__(64 * WAVES) void quant_act_kernel(const float *__restrict__ X, int K,
                                                                int8_t *__restrict__ Q, int64_t ldq,
                                                                int qtiled, float *__restrict__ absmax,
@@ -215,7 +241,9 @@ __global__ __launch_bounds__(64 * WAVES) void quant_act_kernel(const float *__re
     if (m == 0 && zero_ptr)
         for (int i = threadIdx.x; i < zero_n; i += 64 * WAVES) zero_ptr[i] = 0u;
     const QDest dst{Q, ldq, m, (K + 63) / 64, qtiled};
-    quant_row<WAVES, NORM>(X + m * K, K, dst, absmax + m, rowsum ? rowsum + m : nullptr, g, eps);
+    // the gate/up mode reads a second M x K array (g) row by row
+    const float *aux = MODE == kRelu2Gate ? g + m * K : g;
+    quant_row<WAVES, MODE>(X + m * K, K, dst, absmax + m, rowsum ? rowsum + m : nullptr, aux, eps);
 }
 
 template <int WAVES>
@@ -228,7 +256,7 @@ __global__ __launch_bounds__(64 * WAVES) void quant_act_group_kernel(const Probl
     if (m == 0 && p.tickets)
         for (int i = threadIdx.x; i < p.NT; i += 64 * WAVES) p.tickets[i] = 0u;
     const QDest dst{p.Q, p.ldq, m, p.KU, p.qtiled};
-    quant_row<WAVES, false>(p.X + m * p.K, p.K, dst, p.absmax + m, p.rowsum + m, nullptr, 0.0f);
+    quant_row<WAVES, kPlain>(p.X + m * p.K, p.K, dst, p.absmax + m, p.rowsum + m, nullptr, 0.0f);
 }
 
 __global__ __launch_bounds__(kThreads) void zero_words_kernel(uint32_t *__restrict__ p, int64_t n)
@@ -244,10 +272,10 @@ hipError_t launch_quant_act(const float *X, int64_t M, int64_t K, int8_t *Q, int
                             int zero_n, hipStream_t s)
 {
     if (M < kFewTokens)
-        hipLaunchKernelGGL((quant_act_kernel<4, false>), dim3((unsigned)M), dim3(256), 0, s, X, (int)K, Q,
+        hipLaunchKernelGGL((quant_act_kernel<4, kPlain>), dim3((unsigned)M), dim3(256), 0, s, X, (int)K, Q,
                            ldq, qtiled, absmax, rowsum, zero_ptr, zero_n, nullptr, 0.0f);
     else
-        hipLaunchKernelGGL((quant_act_kernel<1, false>), dim3((unsigned)M), dim3(64), 0, s, X, (int)K, Q,
+        hipLaunchKernelGGL((quant_act_kernel<1, kPlain>), dim3((unsigned)M), dim3(64), 0, s, X, (int)K, Q,
                            ldq, qtiled, absmax, rowsum, zero_ptr, zero_n, nullptr, 0.0f);
     return hipGetLastError();
 }
@@ -257,11 +285,23 @@ hipError_t launch_quant_act_rmsnorm(const float *X, int64_t M, int64_t K, const 
                                     hipStream_t s)
 {
     if (M < kFewTokens)
-        hipLaunchKernelGGL((quant_act_kernel<4, true>), dim3((unsigned)M), dim3(256), 0, s, X, (int)K, Q,
+        hipLaunchKernelGGL((quant_act_kernel<4, kRmsNorm>), dim3((unsigned)M), dim3(256), 0, s, X, (int)K, Q,
                            ldq, 0, absmax, rowsum, nullptr, 0, g, eps);
     else
-        hipLaunchKernelGGL((quant_act_kernel<1, true>), dim3((unsigned)M), dim3(64), 0, s, X, (int)K, Q,
+        hipLaunchKernelGGL((quant_act_kernel<1, kRmsNorm>), dim3((unsigned)M), dim3(64), 0, s, X, (int)K, Q,
                            ldq, 0, absmax, rowsum, nullptr, 0, g, eps);
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_act_relu2_gate(const float *G, const float *U, int64_t M, int64_t N, int8_t *Q,
+                                       int64_t ldq, float *absmax, int32_t *rowsum, hipStream_t s)
+{
+    if (M < kFewTokens)
+        hipLaunchKernelGGL((quant_act_kernel<4, kRelu2Gate>), dim3((unsigned)M), dim3(256), 0, s, G, (int)N,
+                           Q, ldq, 0, absmax, rowsum, nullptr, 0, U, 0.0f);
+    else
+        hipLaunchKernelGGL((quant_act_kernel<1, kRelu2Gate>), dim3((unsigned)M), dim3(64), 0, s, G, (int)N,
+                           Q, ldq, 0, absmax, rowsum, nullptr, 0, U, 0.0f);
     return hipGetLastError();
 }
 

@@ -349,6 +349,22 @@ int bitlinear_quant_act_rmsnorm(const float *X, int64_t M, int64_t K, const floa
     return BITLINEAR_OK;
 }
 
+int bitlinear_quant_act_relu2_gate(const float *G, const float *U, int64_t M, int64_t N, int8_t *Q_out,
+                                   int64_t ldq, float *absmax_out, int32_t *rowsum_out, void *stream)
+{
+    if (!G || !U || !Q_out || !absmax_out)
+        return fail(BITLINEAR_ERR_NULL, "quant_act_relu2_gate: G, U, Q_out and absmax_out are required");
+    if (int st = check_mnk(M, 1, N)) return st;
+    if (ldq < N || ldq % 16 != 0)
+        return fail(BITLINEAR_ERR_SHAPE, "quant_act_relu2_gate: ldq=%lld must be >= N and a multiple of 16", (long long)ldq);
+    if (!a16(G) || !a16(U) || !a16(Q_out) || !a4(absmax_out) || (rowsum_out && !a4(rowsum_out)))
+        return fail(BITLINEAR_ERR_ALIGN, "quant_act_relu2_gate: G/U/Q_out need 16-byte, absmax/rowsum 4-byte alignment");
+    if (hipError_t e = bl::launch_quant_act_relu2_gate(G, U, M, N, Q_out, ldq, absmax_out, rowsum_out,
+                                                       static_cast<hipStream_t>(stream)))
+        return hip_fail(e, "quant_act_relu2_gate");
+    return BITLINEAR_OK;
+}
+
 int bitlinear_matmul(const int8_t *Q, int64_t ldq, const float *absmax, const int32_t *rowsum,
                      int64_t M, int64_t K, const uint8_t *P, const float *gamma, int64_t N,
                      float *Y_out, int32_t *acc_out, void *ws, size_t ws_bytes, void *stream)

@@ -29,7 +29,7 @@ def _declared():
 
 def test_every_declared_symbol_is_exported():
     names = _declared()
-    assert len(names) == 19, names
+    assert len(names) == 20, names
     out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r"\bT (bitlinear_\w+)", out))
@@ -108,6 +108,12 @@ def test_pack_quant_matmul_forward_validation():
     assert q(FAKE, 2, 100, None, -1.0, FAKE, 112, FAKE, FAKE, None) == -6
     assert q(FAKE, 2, 100, None, float("nan"), FAKE, 112, FAKE, FAKE, None) == -6
     assert q(FAKE, 2, 100, FAKE + 2, 1e-5, FAKE, 112, FAKE, FAKE, None) == -3
+    # gated squared-ReLU + cast
+    r = L.bitlinear_quant_act_relu2_gate
+    assert r(FAKE, None, 2, 100, FAKE, 112, FAKE, FAKE, None) == -1
+    assert r(FAKE, FAKE, 2, 0, FAKE, 112, FAKE, FAKE, None) == -2
+    assert r(FAKE, FAKE, 2, 100, FAKE, 104, FAKE, FAKE, None) == -2
+    assert r(FAKE, FAKE + 4, 2, 100, FAKE, 112, FAKE, FAKE, None) == -3
     # matmul: ldq must cover K rounded up to 64
     assert _st("bitlinear_matmul", FAKE, 112, FAKE, FAKE, 2, 100, FAKE, FAKE, 64, FAKE, None,
                None, 0, None)[0] == -2

@@ -147,6 +147,54 @@ def test_rmsnorm_then_contraction(B):
     check_outputs(host(Y), host(acc), ref, 0.02, a, "rmsnorm -> matmul")
 
 
+@pytest.mark.parametrize("M,N", [(1, 6912), (3, 37), (7, 8640), (1, 28672), (2049, 6912), (2050, 10004),
+                                 (2048, 37)])
+def test_quant_act_relu2_gate_parity(B, M, N):
+    # gated squared-ReLU + cast: every kernel path against the oracle
+    say("quant_act_relu2_gate", M, N)
+    G = synth.activations_np(M, N, seed=M * 19 + N) * np.float32(3)
+    U = synth.activations_np(M, N, seed=M * 23 + N, outlier_frac=0.01)
+    if M > 2:
+        G[1] = -1.0                     # a token whose gate is closed everywhere
+    Q, a, rs, H = O.relu2_gate_quant_act(G, U)
+    Qg, ag, rsg = B.quant_act_relu2_gate(dev(G), dev(U))
+    Qg = host(Qg)
+    np.testing.assert_array_equal(Qg[:, :N], Q)
+    assert not Qg[:, N:].any()
+    np.testing.assert_array_equal(host(ag), a)
+    np.testing.assert_array_equal(host(rsg), rs)
+
+
+@pytest.mark.parametrize("M", [1, 5, 80])
+def test_ffn_block_chain(B, M):
+    # a BitLinear feed-forward block end to end on the GPU: RMSNorm + cast,
+    # gate and up projections (one grouped launch), gated squared-ReLU +
+    # cast, down projection -- every stage bit-exact against the oracle chain
+    say("ffn block", M)
+    D, F = 640, 1728
+    X = synth.activations_np(M, D, seed=300 + M, outlier_frac=0.01)
+    g = synth.activations_np(1, D, seed=301)[0]
+    Tg, Tu, Td = (synth.random_ternary(*s_, seed=302 + i) for i, s_ in enumerate([(F, D), (F, D), (D, F)]))
+    gg, gu, gd = np.float32(0.021), np.float32(0.017), np.float32(0.013)
+    # oracle chain
+    Q1, a1, r1, _, _ = O.rmsnorm_quant_act(X, g, 1e-5)
+    Gr = O.epilogue(O.matmul(Q1, Tg), gg, a1)
+    Ur = O.epilogue(O.matmul(Q1, Tu), gu, a1)
+    Q2, a2, r2, _ = O.relu2_gate_quant_act(Gr, Ur)
+    acc_d = O.matmul(Q2, Td)
+    # GPU chain
+    Q1g, a1g, r1g = B.quant_act_rmsnorm(dev(X), dev(g), 1e-5)
+    np.testing.assert_array_equal(host(Q1g)[:, :D], Q1)
+    Gg = B.matmul(Q1g, a1g, r1g, dev(O.pack(Tg)), gamma_dev(float(gg)), F, D)
+    Ug = B.matmul(Q1g, a1g, r1g, dev(O.pack(Tu)), gamma_dev(float(gu)), F, D)
+    np.testing.assert_array_equal(host(Gg), Gr)
+    np.testing.assert_array_equal(host(Ug), Ur)
+    Q2g, a2g, r2g = B.quant_act_relu2_gate(Gg, Ug)
+    np.testing.assert_array_equal(host(Q2g)[:, :F], Q2)
+    Yg, accg = B.matmul(Q2g, a2g, r2g, dev(O.pack(Td)), gamma_dev(float(gd)), D, F, with_acc=True)
+    check_outputs(host(Yg), host(accg), acc_d, float(gd), a2, "ffn down")
+
+
 def test_quant_act_unaligned_stride_rows(B):
     # K not a multiple of 4 takes the scalar path; ldq = K rounded to 16
     say("quant_act scalar path")
