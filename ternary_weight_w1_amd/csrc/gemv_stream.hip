@@ -198,11 +198,11 @@ __device__ void stream_dot4(const Problem &p, int local)
         return;
     }
     const int64_t ldp = (int64_t)p.NT * 64;  // partial row stride
-    if (t < 64) gstore_ptr<int32_t>(p.acc_ws)[(int64_t)split * p.M * ldp + n] = total;
+    if (t < 64) put_partial(p.acc_ws + ((int64_t)split * p.M * ldp + n), total);
     if (!arrive_last(p, tile)) return;
     if (t < 64 && n < p.N) {
         int sum = 0;
-        for (int j = 0; j < p.ks; ++j) sum += gload_ptr<int32_t>(p.acc_ws)[(int64_t)j * p.M * ldp + n];
+        for (int j = 0; j < p.ks; ++j) sum += get_partial(p.acc_ws + ((int64_t)j * p.M * ldp + n));
         finish(n, sum, gamma);
     }
 }
@@ -322,7 +322,7 @@ __device__ void stream_mfma(const Problem &p, int local)
                     if (p.ks == 1)
                         finish_output_with(p, gamma, m, n, acc[t][s2][e], s_rowsum[m], s_absmax[m]);
                     else
-                        gstore_ptr<int32_t>(p.acc_ws)[((int64_t)split * p.M + m) * ldp + n] = acc[t][s2][e];
+                        put_partial(p.acc_ws + (((int64_t)split * p.M + m) * ldp + n), acc[t][s2][e]);
                 }
             }
         }
@@ -336,7 +336,7 @@ __device__ void stream_mfma(const Problem &p, int local)
         const int n = kRows * grp + idx % kRows;
         if (n >= p.N) continue;
         int sum = 0;
-        for (int j = 0; j < p.ks; ++j) sum += gload_ptr<int32_t>(p.acc_ws)[((int64_t)j * p.M + m) * ldp + n];
+        for (int j = 0; j < p.ks; ++j) sum += get_partial(p.acc_ws + (((int64_t)j * p.M + m) * ldp + n));
         finish_output(p, gamma, m, n, sum);
     }
 }

@@ -52,26 +52,40 @@ __device__ inline void finish_output(const Problem &p, float gamma, int m, int n
                        gload_ptr<float>(p.absmax)[m]);
 }
 
-// Split-K arrival: every workgroup of a 64-row tile publishes its partial
-// sums, then takes a ticket; the one that takes the last ticket sums the
-// partials and puts the counter back to zero (every other workgroup of the
-// tile has already taken its ticket), so the counters are clean for the
-// next launch.  The fences order the partial stores before the ticket and
-// the ticket before the reads of the other workgroups' partials.
+// Split-K exchange.  The workgroups of one tile may run on different XCDs,
+// each with its own L2, so their int32 partial sums travel as device-scope
+// relaxed atomic stores and loads (written through to, and read from, the
+// device's coherence point) instead of through fences: a device-scope fence
+// writes back and invalidates the whole local L2 in every workgroup.
+__device__ inline void put_partial(int32_t *p, int32_t v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline int32_t get_partial(const int32_t *p)
+{
+    return __hip_atomic_load(const_cast<int32_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Split-K arrival: every workgroup of a tile publishes its partial sums
+// (put_partial), waits until those stores have completed, then takes a
+// ticket; the one that takes the last ticket reads every partial
+// (get_partial, issued only after its ticket came back) and puts the
+// counter back to zero (every other workgroup of the tile has already taken
+// its ticket), so the counters are clean for the next launch.
 __device__ inline bool arrive_last(const Problem &p, int tile)
 {
     __shared__ int s_last;
-    __threadfence();
+    __builtin_amdgcn_s_waitcnt(0);  // this thread's partial stores are complete
     __syncthreads();
     if (threadIdx.x == 0) {
-        const bool last = atomicAdd(&p.tickets[tile], 1u) == (unsigned)(p.ks - 1);
-        if (last) atomicExch(&p.tickets[tile], 0u);
+        const unsigned old =
+            __hip_atomic_fetch_add(&p.tickets[tile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const bool last = old == (unsigned)(p.ks - 1);
+        if (last) __hip_atomic_store(&p.tickets[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         s_last = last ? 1 : 0;
     }
     __syncthreads();
-    const bool last = s_last != 0;
-    if (last) __threadfence();
-    return last;
+    return s_last != 0;
 }
 
 }  // namespace bl
