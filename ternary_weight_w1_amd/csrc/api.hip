@@ -81,19 +81,18 @@ const Knobs &knobs()
     return k;
 }
 
-// Tile-kernel instantiation (the list is next to the tile kernels).  With
-// the knob unset a launch takes the 128-token tile (18) or, when its token
-// counts pad to clearly fewer rows that way, the 64-token tile (0): per
-// padded row the 128-token tile is about 5% faster (64 tokens: the 64-token
-// tile is 27% faster; 176: 13%; 256: the 128-token tile is 5% faster).
-// 5..7 read fragment-ordered activations that only the library's own
-// quantizer writes, so caller-supplied activations map them to their
+// Tile-kernel instantiation (the list is next to the tile kernels): 19 (64
+// token rows per tile, two units per stage) unless the knob picks another.
+// Against the 128-token tile it is as fast at M = 256 and 512 and pads
+// less elsewhere (M = 64: 0.27 vs 0.40 ms; 176: 0.40 vs 0.49 ms on 3B/2B
+// stacks).  5..7 read fragment-ordered activations that only the library's
+// own quantizer writes, so caller-supplied activations map them to their
 // row-major twins 2, 0, 1.
-bool tile_variant_known(int v) { return v == 0 || v == 1 || v == 2 || (v >= 5 && v <= 7) || (v >= 10 && v <= 12) || v == 18; }
-int tile_variant(bool own_q, int auto_bm = 128)
+bool tile_variant_known(int v) { return v == 0 || v == 1 || v == 2 || (v >= 5 && v <= 7) || (v >= 10 && v <= 12) || v == 18 || v == 19; }
+int tile_variant(bool own_q)
 {
     int v = knobs().tile_variant;
-    if (!tile_variant_known(v)) return auto_bm == 64 ? 0 : 18;
+    if (!tile_variant_known(v)) return 19;
     if (!own_q) {  // caller-supplied activations are row-major
         if (v == 5) return 2;
         if (v == 6) return 0;
@@ -101,11 +100,7 @@ int tile_variant(bool own_q, int auto_bm = 128)
     }
     return v;
 }
-// 64 or 128: the tile height whose padding costs less for this work
-// (token rows rounded up to each height, weighted by N*K)
-int auto_tile_bm(double work64, double work128) { return work64 * 1.05 < work128 ? 64 : 128; }
-double padded_work(int64_t M, int64_t N, int64_t K, int64_t bm) { return (double)((M + bm - 1) / bm * bm) * N * K; }
-int tile_bm(int variant) { return (variant == 0 || variant == 6) ? 64 : 128; }
+int tile_bm(int variant) { return (variant == 0 || variant == 6 || variant == 19) ? 64 : 128; }
 bool tile_frag(int variant) { return variant >= 5 && variant <= 7; }
 
 // Kernel kind and decomposition of one problem.  `base_items` is the number
@@ -114,7 +109,7 @@ bool tile_frag(int variant) { return variant >= 5 && variant <= 7; }
 // quantizes the activations itself and may choose their layout.  groups4:
 // the launch runs the streaming MFMA kernel, whose work items are groups of
 // kGroupTiles 64-row tiles (p.ntt of them).
-void decompose(Problem &p, int64_t base_items, bool own_q, bool groups4 = false, int auto_bm = 0)
+void decompose(Problem &p, int64_t base_items, bool own_q, bool groups4 = false)
 {
     p.KU = (int32_t)((p.K + 63) / 64);
     p.NT = (int32_t)((p.N + 63) / 64);
@@ -141,9 +136,7 @@ void decompose(Problem &p, int64_t base_items, bool own_q, bool groups4 = false,
         }
     } else {
         p.kind = 1;
-        if (auto_bm == 0)
-            auto_bm = auto_tile_bm(padded_work(p.M, p.N, p.K, 64), padded_work(p.M, p.N, p.K, 128));
-        const int v = tile_variant(own_q, auto_bm);
+        const int v = tile_variant(own_q);
         p.mtile = tile_bm(v);
         p.qtiled = tile_frag(v) ? 1 : 0;
         p.mt = (int32_t)((p.M + p.mtile - 1) / p.mtile);
@@ -226,7 +219,7 @@ Problem make_problem(int64_t M, int64_t N, int64_t K)
 hipError_t launch_contraction(const Problem &p, bool own_q, hipStream_t s)
 {
     if (p.kind == 0) return bl::launch_stream_single(p, stream_variant_for(p.M, p.upsplit), s);
-    return bl::launch_tile_single(p, tile_variant(own_q, p.mtile), s);
+    return bl::launch_tile_single(p, tile_variant(own_q), s);
 }
 
 }  // namespace
@@ -502,14 +495,6 @@ int build_group(const bitlinear_problem *in, int count, char *ws, GroupPlan &out
         if (q.M <= kStreamMaxM) base_items += (q.N + 63) / 64;
     }
     if (base_items < 1) base_items = 1;
-    // one tile height for every tile problem of the launch
-    double work64 = 0, work128 = 0;
-    for (int i = 0; i < count; ++i)
-        if (in[i].M > kStreamMaxM) {
-            work64 += padded_work(in[i].M, in[i].N, in[i].K, 64);
-            work128 += padded_work(in[i].M, in[i].N, in[i].K, 128);
-        }
-    const int group_bm = auto_tile_bm(work64, work128);
     int64_t tokens = 0, items_s = 0, items_t = 0, off = 0;
     // streaming instantiation for the whole launch: LDS-staged dot4 when every
     // streaming problem has a single token (fused with the quantization when
@@ -518,7 +503,7 @@ int build_group(const bitlinear_problem *in, int count, char *ws, GroupPlan &out
     int64_t max_upsplit = 0;
     for (int i = 0; i < count; ++i) {
         Problem p = make_problem(in[i].M, in[i].N, in[i].K);
-        decompose(p, base_items, true, false, group_bm);
+        decompose(p, base_items, true);
         if (p.kind != 0) continue;
         all_m1 = all_m1 && p.M <= knobs().dot4_max_m;
         any_split = any_split || p.ks > 1;
@@ -538,7 +523,7 @@ int build_group(const bitlinear_problem *in, int count, char *ws, GroupPlan &out
         const bitlinear_problem &q = in[i];
         Problem &p = out.probs[i];
         p = make_problem(q.M, q.N, q.K);
-        decompose(p, base_items, true, groups4, group_bm);
+        decompose(p, base_items, true, groups4);
         p.X = q.X;
         p.P = q.P;
         p.gamma = q.gamma;
@@ -588,7 +573,7 @@ int build_group(const bitlinear_problem *in, int count, char *ws, GroupPlan &out
     h.n_items_tile = (int32_t)items_t;
     h.stream_variant = stream_variant;
     h.stream_lds = h.stream_variant >= 2 ? (int32_t)(64 * max_upsplit) : 0;
-    h.tile_variant = tile_variant(true, group_bm);
+    h.tile_variant = tile_variant(true);
     h.ws_bytes = off;
     int64_t t = up(sizeof(bl::GroupHeader), 16);
     h.off_probs = t;

@@ -269,7 +269,7 @@ __device__ __forceinline__ void tile_body(const Problem &p, int local)
     }
 }
 
-// 128-token x 64-row-per-wave tile (as tile_body<4, 1, 1, 0, true>) with
+// WMS*32-token x 64-row-per-wave tile (as tile_body<WMS, 1, 1, 0, true>) with
 // UPS units of K per LDS stage and barrier: the fixed cost of a barrier
 // round (the wait itself and the LDS read latency before the first MFMA)
 // is paid once per UPS units.  A stage's unit past KU gets an all-zero
@@ -277,10 +277,10 @@ __device__ __forceinline__ void tile_body(const Problem &p, int local)
 // branch; its activation chunk re-reads unit KU-1 (valid memory).
 constexpr int kLda2 = 144;  // 128 bytes + 16 of padding: 8 lanes on distinct banks
 
-template <int UPS>
+template <int UPS, int WMS>
 __device__ __forceinline__ void tile_body_ups(const Problem &p, int local)
 {
-    constexpr int WMS = 4, BM = 128, CH = 2;  // CH: 16-byte chunks per thread per unit
+    constexpr int BM = 32 * WMS, CH = BM / 64;  // CH: 16-byte chunks per thread per unit
     constexpr int kRow = 64 * UPS + 16;
     static_assert(UPS == 2 && kRow == kLda2, "stage rows are 128 bytes + padding");
     constexpr int kStageBytes = BM * kRow;
@@ -454,7 +454,8 @@ __device__ __forceinline__ void tile_body_ups(const Problem &p, int local)
 //   10, 12  as 2 with activations staged in fragment order (10 with the
 //      LDS-transposed epilogue);
 //   11  as 2 with the LDS-transposed epilogue;
-//   18  as 11 with two 64-code units per LDS stage (the default).
+//   18  as 11 with two 64-code units per LDS stage;
+//   19  as 18 with 64-token tiles (64 x 64 per wave; the default).
 template <int V>
 __device__ inline void tile_dispatch(const Problem &p, int local)
 {
@@ -476,8 +477,10 @@ __device__ inline void tile_dispatch(const Problem &p, int local)
         tile_body<4, 1, 1, 0, true>(p, local);
     else if constexpr (V == 12)
         tile_body<4, 1, 1, 2, false>(p, local);
+    else if constexpr (V == 19)
+        tile_body_ups<2, 2>(p, local);
     else
-        tile_body_ups<2>(p, local);
+        tile_body_ups<2, 4>(p, local);
 }
 
 // Workgroup b runs on XCD b % 8; the logical item order is split into eight
@@ -506,7 +509,7 @@ __global__ __launch_bounds__(kThreads, 2) void tile_group_kernel(const Problem *
 
 }  // namespace
 
-// one case per instantiation; unknown values take the default (18)
+// one case per instantiation; unknown values take 18
 #define BL_TILE_CASES(KERNEL, ...)                                                         \
     switch (variant) {                                                                     \
     case 0: hipLaunchKernelGGL(KERNEL<0>, __VA_ARGS__); break;                             \
@@ -518,6 +521,7 @@ __global__ __launch_bounds__(kThreads, 2) void tile_group_kernel(const Problem *
     case 10: hipLaunchKernelGGL(KERNEL<10>, __VA_ARGS__); break;                           \
     case 11: hipLaunchKernelGGL(KERNEL<11>, __VA_ARGS__); break;                           \
     case 12: hipLaunchKernelGGL(KERNEL<12>, __VA_ARGS__); break;                           \
+    case 19: hipLaunchKernelGGL(KERNEL<19>, __VA_ARGS__); break;                           \
     default: hipLaunchKernelGGL(KERNEL<18>, __VA_ARGS__); break;                           \
     }
 

@@ -268,8 +268,8 @@ def test_pack_golden_single_codes(B):
 # ---------------------------------------------------------- contraction ------
 
 MM_CASES = [
-    # (M, N, K): dot4 (M=1), streaming MFMA (2..32), tile MFMA (64- or 128-token
-    # tiles, whichever pads less); ragged N and K tails throughout
+    # (M, N, K): dot4 (M=1), streaming MFMA (2..32), tile MFMA (33 and up);
+    # ragged N and K tails throughout
     (1, 64, 64), (1, 100, 200), (1, 257, 640), (1, 640, 2560),
     (2, 64, 64), (3, 100, 200), (8, 257, 640), (17, 640, 2560), (32, 130, 1000),
     (33, 64, 64), (40, 100, 200), (64, 257, 640), (65, 130, 1000), (128, 640, 2560),
