@@ -38,6 +38,14 @@ def lib():
         L.oracle_pack.argtypes = [_vp, _i64, _i64, _vp]
         L.oracle_unpack.restype = _i64
         L.oracle_unpack.argtypes = [_vp, _i64, _i64, _vp]
+        L.oracle_packed5_bytes.restype = _i64
+        L.oracle_packed5_bytes.argtypes = [_i64, _i64]
+        L.oracle_pack5.restype = None
+        L.oracle_pack5.argtypes = [_vp, _i64, _i64, _vp]
+        L.oracle_unpack5.restype = _i64
+        L.oracle_unpack5.argtypes = [_vp, _i64, _i64, _vp]
+        L.oracle_matmul_packed5_rows.restype = None
+        L.oracle_matmul_packed5_rows.argtypes = [_vp, _vp, _i64, _i64, _i64, _vp, _i64, _vp]
         L.oracle_quant_act.restype = None
         L.oracle_quant_act.argtypes = [_vp, _i64, _i64, _vp, _vp, _vp]
         L.oracle_relu2_gate_quant_act.restype = None
@@ -111,6 +119,42 @@ def unpack(P, N, K):
     T = np.empty((N, K), np.int8)
     bad = lib().oracle_unpack(_p(P), N, K, _p(T))
     return T, int(bad)
+
+
+def packed5_bytes(N, K):
+    return int(lib().oracle_packed5_bytes(N, K))
+
+
+def pack5(T):
+    """BT5-T32 bytes of the N x K codes T (five codes per byte, base 3)."""
+    T = _c(T, np.int8)
+    N, K = T.shape
+    P = np.empty(packed5_bytes(N, K), np.uint8)
+    lib().oracle_pack5(_p(T), N, K, _p(P))
+    return P
+
+
+def unpack5(P, N, K):
+    """(T, bad): decoded N x K codes and the count of malformed bytes/padding."""
+    P = _c(P, np.uint8)
+    if P.size != packed5_bytes(N, K):
+        raise ValueError("packed buffer has the wrong size")
+    T = np.empty((N, K), np.int8)
+    bad = lib().oracle_unpack5(_p(P), N, K, _p(T))
+    return T, int(bad)
+
+
+def matmul_packed5_rows(Q, P, N, K, rows):
+    """acc[:, i] for output row rows[i], read straight from a BT5-T32 buffer."""
+    Q = _c(Q, np.int8)
+    P = _c(P, np.uint8)
+    rows = _c(rows, np.int64)
+    M = Q.shape[0]
+    assert Q.shape[1] == K and P.size == packed5_bytes(N, K)
+    assert rows.size == 0 or (rows.min() >= 0 and rows.max() < N)
+    acc = np.empty((M, rows.size), np.int32)
+    lib().oracle_matmul_packed5_rows(_p(Q), _p(P), M, N, K, _p(rows), rows.size, _p(acc))
+    return acc
 
 
 def quant_act(X):

@@ -32,6 +32,8 @@
  *  R4  output y = (float)acc * c with c = (gamma * a) / 127 in fp32
  *      (multiply, then divide).
  *  R5  the 2-bit packed format "BL2-T64" defined at oracle_pack below.
+ *  R15 the ~0.4 GB footprint of the 2B model read as five codes per byte:
+ *      the base-3 format "BT5-T32" defined at oracle_pack5 below.
  *  R13 the sub-layer norm before the activation cast is RMSNorm with a
  *      per-channel gain (oracle_rmsnorm_quant_act).
  *  R14 the squared-ReLU feed-forward is gated: h = relu(gate)^2 * up
@@ -154,6 +156,114 @@ int64_t oracle_unpack(const uint8_t *P, int64_t N, int64_t K, int8_t *T)
         }
     }
     return bad;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Packed format BT5-T32: five ternary codes per byte.  [YT] "Transcription" */
+/* puts the 2B model at about 0.4 GB; four codes per byte gives 0.52 GB for  */
+/* its 2.08 G BitLinear weights, five per byte (1.6 bits) gives 0.42 GB, so  */
+/* the figure is read as base-3 packing (reading R15).                       */
+/*                                                                           */
+/* Byte value: the five codes of a byte, digit i = 0..4 (0 most significant) */
+/* with digit value code + 1, form b = sum_i (code_i + 1) * 3^(4-i), an      */
+/* integer in [0, 242].  The stored byte is s = ceil(256 * b / 243), so that */
+/* s / 256 is b / 243 rounded up; b comes back as floor(243 * s / 256).     */
+/* Five zero codes give b = 121, s = 128.                                    */
+/*                                                                           */
+/* Layout: row tiles of 32 rows, K units of 160 codes (K padded to a        */
+/* multiple of 160 and N to a multiple of 32 with zero codes), KU5 =         */
+/* ceil(K / 160).  Tile t, unit u is a 1024-byte block at byte               */
+/* (t * KU5 + u) * 1024, made of 64 slots of 16 bytes.  Byte p (0..15) of    */
+/* slot L holds row 32*t + (L mod 32) and, as digit i, the code              */
+/* k = 160*u + 32*i + 16*(L div 32) + p.                                     */
+/* ------------------------------------------------------------------------ */
+
+int64_t oracle_packed5_bytes(int64_t N, int64_t K)
+{
+    int64_t tiles = (N + 31) / 32;
+    int64_t units = (K + 159) / 160;
+    return tiles * units * 1024;
+}
+
+/* Byte of the packed buffer that holds row n, unit u, slot half g (= L div
+ * 32) and byte p of the slot.                                               */
+static int64_t bt5_byte(int64_t n, int64_t u, int64_t g, int64_t p, int64_t units)
+{
+    int64_t t = n / 32, slot = n % 32 + 32 * g;
+    return (t * units + u) * 1024 + 16 * slot + p;
+}
+
+void oracle_pack5(const int8_t *T, int64_t N, int64_t K, uint8_t *P)
+{
+    int64_t units = (K + 159) / 160, rows = (N + 31) / 32 * 32;
+    for (int64_t n = 0; n < rows; ++n) {
+        for (int64_t u = 0; u < units; ++u) {
+            for (int64_t g = 0; g < 2; ++g) {
+                for (int64_t p = 0; p < 16; ++p) {
+                    int64_t b = 0;
+                    for (int64_t i = 0; i < 5; ++i) {
+                        int64_t k = 160 * u + 32 * i + 16 * g + p;
+                        int code = (n < N && k < K) ? T[n * K + k] : 0;
+                        b = 3 * b + (code + 1);          /* base-3 digit, most significant first */
+                    }
+                    int64_t s = (256 * b + 242) / 243;   /* ceil(256 b / 243) */
+                    P[bt5_byte(n, u, g, p, units)] = (uint8_t)s;
+                }
+            }
+        }
+    }
+}
+
+/* Returns the number of bytes that are not the image of any five codes
+ * (s != ceil(256 b / 243) for b = floor(243 s / 256)), plus the number of
+ * padding positions that do not hold the zero code; T receives the decoded
+ * codes.                                                                    */
+int64_t oracle_unpack5(const uint8_t *P, int64_t N, int64_t K, int8_t *T)
+{
+    int64_t bad = 0;
+    int64_t units = (K + 159) / 160, rows = (N + 31) / 32 * 32;
+    for (int64_t n = 0; n < rows; ++n) {
+        for (int64_t u = 0; u < units; ++u) {
+            for (int64_t g = 0; g < 2; ++g) {
+                for (int64_t p = 0; p < 16; ++p) {
+                    int64_t s = P[bt5_byte(n, u, g, p, units)];
+                    int64_t b = (243 * s) / 256;
+                    if ((256 * b + 242) / 243 != s) ++bad;
+                    for (int64_t i = 4; i >= 0; --i) {   /* least significant digit first */
+                        int code = (int)(b % 3) - 1;
+                        b /= 3;
+                        int64_t k = 160 * u + 32 * i + 16 * g + p;
+                        if (n < N && k < K) T[n * K + k] = (int8_t)code;
+                        else if (code != 0) ++bad;
+                    }
+                }
+            }
+        }
+    }
+    return bad;
+}
+
+/* acc[m * nrows + r] = sum_k T[rows[r], k] * Q[m, k] with the codes read
+ * straight from a BT5-T32 buffer (one byte decoded per code visit).         */
+void oracle_matmul_packed5_rows(const int8_t *Q, const uint8_t *P, int64_t M, int64_t N,
+                                int64_t K, const int64_t *rows, int64_t nrows, int32_t *acc)
+{
+    (void)N;
+    int64_t units = (K + 159) / 160;
+    for (int64_t r = 0; r < nrows; ++r) {
+        int64_t n = rows[r];
+        for (int64_t m = 0; m < M; ++m) {
+            int32_t sum = 0;
+            for (int64_t k = 0; k < K; ++k) {
+                int64_t u = k / 160, i = (k % 160) / 32, g = (k % 32) / 16, p = k % 16;
+                int64_t b = (243 * (int64_t)P[bt5_byte(n, u, g, p, units)]) / 256;
+                for (int64_t j = 4; j > i; --j) b /= 3;  /* drop the digits below digit i */
+                int t = (int)(b % 3) - 1;
+                sum += t * (int32_t)Q[m * K + k];
+            }
+            acc[m * nrows + r] = sum;
+        }
+    }
 }
 
 /* ------------------------------------------------------------------------ */

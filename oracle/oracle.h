@@ -17,6 +17,12 @@ void    oracle_ternarize(const float *W, int64_t N, int64_t K, float gamma, int8
 int64_t oracle_packed_bytes(int64_t N, int64_t K);
 void    oracle_pack(const int8_t *T, int64_t N, int64_t K, uint8_t *P);
 int64_t oracle_unpack(const uint8_t *P, int64_t N, int64_t K, int8_t *T);
+int64_t oracle_packed5_bytes(int64_t N, int64_t K);
+void    oracle_pack5(const int8_t *T, int64_t N, int64_t K, uint8_t *P);
+int64_t oracle_unpack5(const uint8_t *P, int64_t N, int64_t K, int8_t *T);
+void    oracle_matmul_packed5_rows(const int8_t *Q, const uint8_t *P, int64_t M, int64_t N,
+                                   int64_t K, const int64_t *rows, int64_t nrows,
+                                   int32_t *acc);
 void    oracle_quant_act(const float *X, int64_t M, int64_t K,
                          int8_t *Q, float *absmax, int32_t *rowsum);
 void    oracle_rmsnorm_quant_act(const float *X, int64_t M, int64_t K, const float *g,

@@ -154,6 +154,145 @@ def test_unpack_reports_malformed_fields():
     assert bad == 4
 
 
+# ------------------------------------------- BT5-T32 (five codes per byte) --
+
+def _bt5_value(codes):
+    """Stored byte of five codes, digit 0 most significant (the format's
+    definition, evaluated with exact rationals)."""
+    b = 0
+    for c in codes:
+        b = 3 * b + (c + 1)
+    return math.ceil(Fraction(256 * b, 243))
+
+
+def test_bt5_golden_bytes():
+    rows = [ln.split() for ln in _golden("bt5_t32_fixtures.txt") if ln.startswith("byte")]
+    assert len(rows) == 7
+    for _, codes, value in rows:
+        codes = [int(c) for c in codes.split(",")]
+        T = np.zeros((1, 160), np.int8)
+        for i, c in enumerate(codes):
+            T[0, 32 * i] = c  # digit i of byte 0 (g = 0, p = 0)
+        P = O.pack5(T)
+        assert P[0] == int(value, 16)
+        assert _bt5_value(codes) == int(value, 16)
+
+
+def test_bt5_golden_single_codes():
+    rows = [ln.split() for ln in _golden("bt5_t32_fixtures.txt") if ln.startswith("single")]
+    assert len(rows) == 7
+    for _, N, K, n, k, code, byte_idx, byte_hex in rows:
+        N, K, n, k, code, byte_idx = map(int, (N, K, n, k, code, byte_idx))
+        T = np.zeros((N, K), np.int8)
+        T[n, k] = code
+        P = O.pack5(T)
+        expect = np.full(O.packed5_bytes(N, K), 0x80, np.uint8)
+        expect[byte_idx] = int(byte_hex, 16)
+        np.testing.assert_array_equal(P, expect)
+        T2, bad = O.unpack5(P, N, K)
+        assert bad == 0
+        np.testing.assert_array_equal(T2, T)
+
+
+def test_bt5_all_243_byte_values():
+    # every five-code combination: distinct stored bytes, increasing with the
+    # base-3 value b, and b = floor(243 s / 256) recovers it
+    import itertools
+    seen = []
+    for b, codes in enumerate(itertools.product((-1, 0, 1), repeat=5)):
+        s = _bt5_value(codes)
+        assert 0 <= s <= 255
+        assert (243 * s) // 256 == b
+        seen.append(s)
+    assert seen == sorted(seen) and len(set(seen)) == 243
+    # the same through the oracle, 243 combinations in the 16 x 2 bytes x 8 rows
+    T = np.zeros((8, 160), np.int8)
+    combos = list(itertools.product((-1, 0, 1), repeat=5))
+    for j, codes in enumerate(combos):
+        n, g, pp = j // 32, (j % 32) // 16, j % 16
+        for i, c in enumerate(codes):
+            T[n, 32 * i + 16 * g + pp] = c
+    P = O.pack5(T)
+    got = [P[16 * (j // 32 + 32 * ((j % 32) // 16)) + j % 16] for j in range(243)]
+    assert got == seen
+
+
+def test_bt5_prefix_digits_by_multiply_shift():
+    # The format's reason for storing ceil(256 b / 243): floor(s * 3^j / 256)
+    # is the integer formed by the top j base-3 digits of b, exactly, for
+    # every byte and j = 0..5 (243 < 256 keeps the rounding error below one
+    # digit).
+    for b in range(243):
+        s = math.ceil(Fraction(256 * b, 243))
+        for j in range(6):
+            assert (s * 3 ** j) >> 8 == b // 3 ** (5 - j)
+
+
+def test_bt5_size_is_1_6_bits_and_2b_stack_is_0_4_gb():
+    # 32 | N and 160 | K: no padding, 8 bits per 5 codes
+    for N, K in ((32, 160), (2560, 2560), (6912, 2560)):
+        assert O.packed5_bytes(N, K) * 8 * 5 == 8 * N * K
+    # [YT] "Transcription": about 0.4 GB for the 2B model; the 6912-wide down
+    # projection pads K to 7040
+    total = 30 * sum(O.packed5_bytes(N, K) for _, K, N in synth.SHAPES_2B)
+    assert total == 418_775_040
+    assert 0.40 < total / 1e9 < 0.42
+
+
+@pytest.mark.parametrize("N,K", [(1, 1), (32, 160), (33, 161), (37, 333), (64, 320), (70, 2560)])
+def test_bt5_roundtrip(N, K):
+    T = synth.random_ternary(N, K, seed=N * 7 + K)
+    P = O.pack5(T)
+    assert P.size == O.packed5_bytes(N, K)
+    T2, bad = O.unpack5(P, N, K)
+    assert bad == 0
+    np.testing.assert_array_equal(T2, T)
+    # only the 243 images occur
+    allowed = {math.ceil(Fraction(256 * b, 243)) for b in range(243)}
+    assert set(np.unique(P).tolist()) <= allowed
+
+
+def test_bt5_unpack_reports_malformed():
+    P = O.pack5(np.zeros((32, 160), np.int8))
+    P[3] = 1  # no five codes map to 1 (b = 0 -> 0, b = 1 -> 2)
+    _, bad = O.unpack5(P, 32, 160)
+    assert bad == 1
+    P = O.pack5(np.zeros((3, 10), np.int8))
+    P[-1] = 0xFF  # a padding byte holding five +1 codes
+    _, bad = O.unpack5(P, 3, 10)
+    assert bad == 5
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 33, 161), (3, 40, 480), (5, 64, 1000)])
+def test_bt5_packed_rows_matmul(M, N, K):
+    T = synth.random_ternary(N, K, seed=M + 3 * N + K)
+    Q = synth.random_int8(M, K, seed=M * N + 1)
+    P = O.pack5(T)
+    rows = np.array([0, N // 2, N - 1], np.int64)
+    got = O.matmul_packed5_rows(Q, P, N, K, rows)
+    want = Q.astype(np.int64) @ T[rows].astype(np.int64).T  # numpy integer product
+    np.testing.assert_array_equal(got, want)
+
+
+def test_bt5_prefix_plane_identity():
+    # The contraction over one byte's five codes written with the prefix
+    # integers H_j = floor(s 3^j / 256) (j = 1..5) and the digits d_i = code_i
+    # + 1: sum_i d_i q_i = sum_{j=1..3} H_j (q_{j-1} - 3 q_j) + H_4 q_3
+    # + (H_5 - 3 H_4) q_4.  Checked for every byte against random activations.
+    rng = np.random.default_rng(5)
+    import itertools
+    for codes in itertools.product((-1, 0, 1), repeat=5):
+        s = _bt5_value(codes)
+        H = [(s * 3 ** j) >> 8 for j in range(6)]
+        d = [c + 1 for c in codes]
+        for q in rng.integers(-127, 128, size=(4, 5)):
+            lhs = sum(d[i] * int(q[i]) for i in range(5))
+            rhs = sum(H[j] * (int(q[j - 1]) - 3 * int(q[j])) for j in (1, 2, 3))
+            rhs += H[4] * int(q[3]) + (H[5] - 3 * H[4]) * int(q[4])
+            assert lhs == rhs
+            assert 0 <= H[5] - 3 * H[4] <= 2 and max(H[1:5]) <= 80
+
+
 def test_ternary_codes_only_in_set():
     # [AN] "What it does": weights in {-1, 0, +1}; zero is a real state.
     rng = np.random.default_rng(5)
