@@ -16,7 +16,9 @@ launch stream), against 8 TB/s.  prefill = the same 210 matrices at
 M = 512 (int8 TOP/s against 5.0 POP/s dense int8).  graph = the decode
 step captured once in a HIP graph and replayed.  curves = latency of a full
 sweep over the 3B-class stack at M in {1, 8, 64, 256} (and, on request, the
-70B-class stack at M in {1, 16, 176}).  cpu_baseline = the CPU oracle
+70B-class stack at M in {1, 16, 176}).  bt5 = the same 2B stack packed
+five codes per byte (BT5-T32, 1.6 bits per weight) at M in {1, 8, 16},
+next to the 2-bit path at the same M.  cpu_baseline = the CPU oracle
 (single thread) on a bounded sample of the same workload.
 
 Inputs are synthetic: weights ~ N(0, 0.02) drawn on the device per matrix,
@@ -43,7 +45,8 @@ METRIC = "BitLinear packed-weight GB/s at M=1 (HBM roofline %) + int8 TOPS at M=
 HBM_PEAK_GBS = 8000.0
 INT8_PEAK_TOPS = 5000.0
 KERNEL_SOURCES = ["ternary_weight_w1_amd/csrc/gemv_stream.hip", "ternary_weight_w1_amd/csrc/gemm_tile.hip",
-                  "ternary_weight_w1_amd/csrc/mm_common.hpp", "ternary_weight_w1_amd/csrc/common.hpp"]
+                  "ternary_weight_w1_amd/csrc/mm_common.hpp", "ternary_weight_w1_amd/csrc/common.hpp",
+                  "ternary_weight_w1_amd/csrc/gemv5.hip", "ternary_weight_w1_amd/csrc/bt5.hpp"]
 
 
 def log(*a):
@@ -58,8 +61,9 @@ def kernel_source_sha() -> str:
     return h.hexdigest()[:16]
 
 
-def build_stack(B, torch, model: str, layers: int, dev):
-    """Quantize and pack every matrix of the stack on the device."""
+def build_stack(B, torch, model: str, layers: int, dev, bt5: bool = False):
+    """Quantize and pack every matrix of the stack on the device (with
+    bt5, also in the five-codes-per-byte format)."""
     spec = synth.MODELS[model]
     mats = []
     for layer in range(layers):
@@ -68,18 +72,20 @@ def build_stack(B, torch, model: str, layers: int, dev):
             T, g = B.quantize_weights(W)
             del W
             P = B.pack(T)
+            P5 = B.pack5(T) if bt5 else None
             del T
-            mats.append(dict(layer=layer, name=name, K=K, N=N, P=P, gamma=g))
+            mats.append(dict(layer=layer, name=name, K=K, N=N, P=P, P5=P5, gamma=g))
     torch.cuda.synchronize()
     return mats
 
 
-def make_plan(B, torch, mats, M, dev, outliers=0.0, seed0=7):
+def make_plan(B, torch, mats, M, dev, outliers=0.0, seed0=7, fmt=0):
     probs = []
     for i, m in enumerate(mats):
         X = synth.activations_torch(M, m["K"], seed0 + i, dev, outlier_frac=outliers)
         Y = torch.empty((M, m["N"]), dtype=torch.float32, device=dev)
-        probs.append(dict(X=X, P=m["P"], gamma=m["gamma"], Y=Y, N=m["N"]))
+        probs.append(dict(X=X, P=m["P5"] if fmt else m["P"], gamma=m["gamma"], Y=Y, N=m["N"],
+                          format=fmt))
     plan = B.GroupPlan(probs, device=dev)
     torch.cuda.synchronize()
     return plan, probs
@@ -156,6 +162,34 @@ def curve(B, torch, model, Ms, dev, steps, warmup):
     return out
 
 
+def bt5_section(B, torch, mats, dev, Ms, steps, warmup):
+    """The stack in BT5-T32 (five codes per byte) against the 2-bit path at
+    each M: step time (quantize + contract) and the contraction kernel's
+    average duration (HIP events), with the BT5 kernel's algorithmic bytes
+    per launch (packed bytes + int8 activations + scales + fp32 outputs)."""
+    packed5 = sum(B.packed5_bytes(m["N"], m["K"]) for m in mats)
+    out = {"format": "BT5-T32, five codes per byte (1.6 bits per weight)", "packed_bytes": packed5,
+           "points": []}
+    for M in Ms:
+        plan, probs = make_plan(B, torch, mats, M, dev, fmt=1)
+        ms5, k5 = time_plan(torch, plan, steps, warmup)
+        del plan, probs
+        plan, probs = make_plan(B, torch, mats, M, dev)
+        ms2, k2 = time_plan(torch, plan, steps, warmup)
+        del plan, probs
+        alg = packed5 + sum(M * B.q_stride5(m["K"]) + 8 * M + 4 * M * m["N"] for m in mats)
+        gbs = alg / (k5 * 1e-3) / 1e9
+        out["points"].append({
+            "M": M, "ms_per_step": round(ms5, 5), "kernel_ms": round(k5, 5),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 4), "bytes_per_launch": alg},
+            "bl2_ms_per_step": round(ms2, 5), "bl2_kernel_ms": round(k2, 5),
+            "kernel_speedup_vs_bl2": round(k2 / k5, 3)})
+        log(f"  BT5 M={M}: kernel {k5 * 1e3:.1f} us (2-bit {k2 * 1e3:.1f} us)")
+    torch.cuda.empty_cache()
+    return out
+
+
 def load_traffic(name):
     """HBM traffic of the dominant kernel from the committed rocprofv3 PMC
     summary, if it was taken on the current kernel sources."""
@@ -211,6 +245,7 @@ def main():
                     help="comma list of latency-vs-M curves to add: 3b (M 1,8,64,256), 70b (M 1,16,176); "
                          "'none' to skip")
     ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--no-bt5", action="store_true", help="skip the five-codes-per-byte comparison")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run only a plain device copy of known size (PMC calibration)")
     args = ap.parse_args()
@@ -238,7 +273,7 @@ def main():
     spec = synth.MODELS[args.model]
     layers = args.layers or spec["layers"]
     log(f"building {args.model} stack: {layers} layers")
-    mats = build_stack(B, torch, args.model, layers, dev)
+    mats = build_stack(B, torch, args.model, layers, dev, bt5=not args.no_bt5)
     packed = sum(m["N"] * m["K"] // 4 for m in mats)
     assert packed == sum(B.packed_bytes(m["N"], m["K"]) for m in mats)
 
@@ -280,6 +315,13 @@ def main():
                            "note": "the same step captured once in a HIP graph and replayed"}
     del plan, probs
     torch.cuda.empty_cache()
+
+    if not args.no_bt5:
+        log("timing BT5-T32 sweeps")
+        result["bt5"] = bt5_section(B, torch, mats, dev, [1, 8, 16], args.steps, args.warmup)
+        for m in mats:
+            m["P5"] = None
+        torch.cuda.empty_cache()
 
     if not args.no_prefill:
         PM = args.prefill_M

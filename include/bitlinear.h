@@ -54,6 +54,24 @@
  *   bytes, ready for a 4-way int8 dot product, and the four planes of one
  *   word are exactly the 16-byte int8 operand of one lane of the gfx950
  *   32x32x32 int8 matrix instruction.
+ *
+ * Packed weight format "BT5-T32" (five codes per byte, 1.6 bits per weight;
+ * bitlinear_pack5 writes it, the *5 calls read it; bitlinear_packed5_bytes
+ * (N, K) bytes).  The pages quote about 0.4 GB for the 2B model (BitNet
+ * b1.58 2B4T video transcript, yousumm.com, "Transcription"), which four
+ * codes per byte (0.52 GB) cannot reach and five per byte (0.42 GB) does:
+ *   the five codes of a byte, digit i = 0..4 (0 most significant), form
+ *   b = sum_i (code_i + 1) * 3^(4-i) in [0, 242]; the byte stores
+ *   s = ceil(256 b / 243) (five zero codes: 0x80).  Rows are grouped in
+ *   tiles of 32 (t = n / 32), K in units of 160 codes (u = k / 160), KU5 =
+ *   ceil(K / 160).  Tile t, unit u is a 1024-byte block at (t * KU5 + u) *
+ *   1024 made of 64 slots of 16 bytes; byte p of slot L holds row 32 t +
+ *   L % 32 and, as digit i, code k = 160 u + 32 i + 16 (L / 32) + p.  Rows
+ *   >= N and codes >= K are padding and hold zero codes.
+ *   Why: floor(s * 3^j / 256) is exactly the integer of the top j digits
+ *   (243 < 256), so a packed byte decodes with one multiply and one byte
+ *   select per digit plane, and a lane's 16-byte load is the B operand of
+ *   the 32x32x32 int8 matrix instruction for each of the five planes.
  */
 #ifndef BITLINEAR_H
 #define BITLINEAR_H
@@ -65,7 +83,7 @@
 extern "C" {
 #endif
 
-#define BITLINEAR_ABI_VERSION 1
+#define BITLINEAR_ABI_VERSION 2
 
 enum bitlinear_status {
     BITLINEAR_OK = 0,
@@ -81,7 +99,15 @@ enum bitlinear_status {
 enum bitlinear_ws_op {
     BITLINEAR_WS_QUANTIZE_WEIGHTS = 1,
     BITLINEAR_WS_MATMUL = 2,
-    BITLINEAR_WS_FORWARD = 3
+    BITLINEAR_WS_FORWARD = 3,
+    BITLINEAR_WS_MATMUL5 = 4,
+    BITLINEAR_WS_FORWARD5 = 5
+};
+
+/* Packed weight formats (bitlinear_problem.format). */
+enum bitlinear_format {
+    BITLINEAR_FORMAT_BL2 = 0, /* BL2-T64, four codes per byte */
+    BITLINEAR_FORMAT_BT5 = 1  /* BT5-T32, five codes per byte */
 };
 
 /* Library ABI version (BITLINEAR_ABI_VERSION of the build). */
@@ -101,6 +127,15 @@ size_t bitlinear_packed_bytes(int64_t N, int64_t K);
 /* Smallest row stride (bytes) of an int8 activation matrix that the matmul
  * calls accept: K rounded up to a multiple of 64. */
 int64_t bitlinear_q_stride(int64_t K);
+
+/* Bytes of the BT5-T32 buffer for an N x K matrix:
+ * ceil(N/32) * ceil(K/160) * 1024 (= N*K/5 when 32 divides N and 160 divides
+ * K).  Returns 0 for sizes out of range. */
+size_t bitlinear_packed5_bytes(int64_t N, int64_t K);
+
+/* Smallest row stride (bytes) of the int8 activations bitlinear_matmul5
+ * accepts: K rounded up to a multiple of 160. */
+int64_t bitlinear_q_stride5(int64_t K);
 
 /* Workspace bytes that `op` needs for these sizes (0 if none; SIZE_MAX if
  * the sizes are invalid).  M is ignored for BITLINEAR_WS_QUANTIZE_WEIGHTS. */
@@ -195,6 +230,43 @@ int bitlinear_matmul(const int8_t *Q, int64_t ldq, const float *absmax, const in
                      float *Y_out, int32_t *acc_out, void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * BT5-T32 packing of ternary codes (five per byte, format above).
+ *   T      [in]  N x K int8 codes (values outside {-1, 0, +1} are clamped).
+ *   P5_out [out] bitlinear_packed5_bytes(N, K) bytes; padding is written.
+ */
+int bitlinear_pack5(const int8_t *T, int64_t N, int64_t K, uint8_t *P5_out, void *stream);
+
+/* Inverse of bitlinear_pack5 (for checking): T_out receives N x K codes,
+ * decoded with the same digit planes the contraction uses. */
+int bitlinear_unpack5(const uint8_t *P5, int64_t N, int64_t K, int8_t *T_out, void *stream);
+
+/*
+ * bitlinear_matmul over BT5-T32 weights: the same results, bit for bit
+ * (acc exact, Y = float(acc) * ((gamma * a) / 127)).
+ *   Q       [in]  M rows of ldq bytes, ldq >= bitlinear_q_stride5(K), a
+ *                 multiple of 16 and <= 2^26; bytes k >= K of each row up to
+ *                 bitlinear_q_stride5(K) must be zero.
+ *   P5      [in]  BT5-T32 weights of an N x K matrix.
+ *   others  as for bitlinear_matmul; ws of bitlinear_workspace_bytes(
+ *           BITLINEAR_WS_MATMUL5, M, N, K) bytes (0 when K is not split).
+ * Any M is accepted; the kernel takes 16 tokens per pass over the weights,
+ * so it is meant for decode and small batches.
+ */
+int bitlinear_matmul5(const int8_t *Q, int64_t ldq, const float *absmax, const int32_t *rowsum,
+                      int64_t M, int64_t K, const uint8_t *P5, const float *gamma, int64_t N,
+                      float *Y_out, int32_t *acc_out, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * The whole BitLinear forward over BT5-T32 weights (quantize X, then
+ * bitlinear_matmul5).  ws: bitlinear_workspace_bytes(BITLINEAR_WS_FORWARD5,
+ * M, N, K) bytes; it receives Q (stride bitlinear_q_stride5(K)), a and the
+ * row sums.
+ */
+int bitlinear_forward5(const float *X, int64_t M, int64_t K, const uint8_t *P5,
+                       const float *gamma, int64_t N, float *Y_out, int32_t *acc_out,
+                       void *ws, size_t ws_bytes, void *stream);
+
+/*
  * The whole BitLinear forward: quantize X per token, contract with the
  * packed ternary weights, rescale.
  *   X       [in]  M x K fp32.          P, gamma as for bitlinear_matmul.
@@ -213,11 +285,13 @@ int bitlinear_forward(const float *X, int64_t M, int64_t K, const uint8_t *P,
 
 typedef struct bitlinear_problem {
     const float *X;     /* M x K fp32 activations (device)                  */
-    const uint8_t *P;   /* BL2-T64 weights of the N x K matrix (device)     */
+    const uint8_t *P;   /* packed weights of the N x K matrix (device)      */
     const float *gamma; /* one fp32 weight scale (device)                   */
     float *Y;           /* M x N fp32 output (device)                       */
     int32_t *acc;       /* M x N int32 accumulators (device, nullable)      */
     int64_t M, N, K;
+    int32_t format;     /* bitlinear_format of P (0 = BL2-T64)              */
+    int32_t reserved;   /* must be 0                                        */
 } bitlinear_problem;
 
 /* Host bytes of the plan table for these problems (0 on invalid input),

@@ -7,7 +7,8 @@ fallback: if the shared library is missing, importing works but the first
 call raises.
 
 Functions carry the C names without the ``bitlinear_`` prefix:
-quantize_weights, pack, unpack, quant_act, matmul, forward, plus the
+quantize_weights, pack, unpack, quant_act, matmul, forward, their BT5-T32
+(five codes per byte) twins pack5, unpack5, matmul5, forward5, plus the
 grouped forward (GroupPlan).
 """
 from __future__ import annotations
@@ -24,6 +25,10 @@ OK = 0
 WS_QUANTIZE_WEIGHTS = 1
 WS_MATMUL = 2
 WS_FORWARD = 3
+WS_MATMUL5 = 4
+WS_FORWARD5 = 5
+FORMAT_BL2 = 0
+FORMAT_BT5 = 1
 
 _vp = ctypes.c_void_p
 _i64 = ctypes.c_int64
@@ -34,7 +39,8 @@ _int = ctypes.c_int
 class Problem(ctypes.Structure):
     """ctypes mirror of struct bitlinear_problem."""
     _fields_ = [("X", _vp), ("P", _vp), ("gamma", _vp), ("Y", _vp), ("acc", _vp),
-                ("M", _i64), ("N", _i64), ("K", _i64)]
+                ("M", _i64), ("N", _i64), ("K", _i64), ("format", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
 
 
 _lib = None
@@ -54,6 +60,13 @@ def lib():
             "bitlinear_last_error": (ctypes.c_char_p, []),
             "bitlinear_packed_bytes": (_sz, [_i64, _i64]),
             "bitlinear_q_stride": (_i64, [_i64]),
+            "bitlinear_packed5_bytes": (_sz, [_i64, _i64]),
+            "bitlinear_q_stride5": (_i64, [_i64]),
+            "bitlinear_pack5": (_int, [_vp, _i64, _i64, _vp, _vp]),
+            "bitlinear_unpack5": (_int, [_vp, _i64, _i64, _vp, _vp]),
+            "bitlinear_matmul5": (_int, [_vp, _i64, _vp, _vp, _i64, _i64, _vp, _vp, _i64, _vp, _vp,
+                                         _vp, _sz, _vp]),
+            "bitlinear_forward5": (_int, [_vp, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _vp, _sz, _vp]),
             "bitlinear_workspace_bytes": (_sz, [_int, _i64, _i64, _i64]),
             "bitlinear_quantize_weights": (_int, [_vp, _i64, _i64, _vp, _vp, _vp, _vp, _sz, _vp]),
             "bitlinear_pack": (_int, [_vp, _i64, _i64, _vp, _vp]),
@@ -233,11 +246,70 @@ def forward(X, P, gamma, N: int, with_acc: bool = False, ws=None, out=None, stre
     return (Y, acc) if with_acc else Y
 
 
+def packed5_bytes(N: int, K: int) -> int:
+    return int(lib().bitlinear_packed5_bytes(N, K))
+
+
+def q_stride5(K: int) -> int:
+    return int(lib().bitlinear_q_stride5(K))
+
+
+def pack5(T, stream=None):
+    """BT5-T32 bytes (five codes per byte) of the N x K int8 codes T."""
+    _dev_tensor(T, torch.int8, "T")
+    N, K = T.shape
+    P = torch.empty(packed5_bytes(N, K), dtype=torch.uint8, device=T.device)
+    _check(lib().bitlinear_pack5(_ptr(T), N, K, _ptr(P), _stream(stream)), "pack5")
+    return P
+
+
+def unpack5(P, N: int, K: int, stream=None):
+    _dev_tensor(P, torch.uint8, "P")
+    T = torch.empty((N, K), dtype=torch.int8, device=P.device)
+    _check(lib().bitlinear_unpack5(_ptr(P), N, K, _ptr(T), _stream(stream)), "unpack5")
+    return T
+
+
+def matmul5(Q, absmax, rowsum, P, gamma, N: int, K: int, with_acc: bool = False, stream=None):
+    """matmul over BT5-T32 weights; Q rows have stride Q.shape[1] >=
+    q_stride5(K) and are zero beyond K."""
+    _dev_tensor(Q, torch.int8, "Q")
+    _dev_tensor(absmax, torch.float32, "absmax")
+    _dev_tensor(rowsum, torch.int32, "rowsum")
+    _dev_tensor(P, torch.uint8, "P")
+    _dev_tensor(gamma, torch.float32, "gamma")
+    M, ldq = Q.shape
+    Y = torch.empty((M, N), dtype=torch.float32, device=Q.device)
+    acc = torch.empty((M, N), dtype=torch.int32, device=Q.device) if with_acc else None
+    ws = _workspace(workspace_bytes(WS_MATMUL5, M, N, K), Q.device)
+    _check(lib().bitlinear_matmul5(_ptr(Q), ldq, _ptr(absmax), _ptr(rowsum), M, K, _ptr(P),
+                                   _ptr(gamma), N, _ptr(Y), _ptr(acc), _ptr(ws),
+                                   0 if ws is None else ws.numel(), _stream(stream)), "matmul5")
+    return (Y, acc) if with_acc else Y
+
+
+def forward5(X, P, gamma, N: int, with_acc: bool = False, ws=None, out=None, stream=None):
+    """BitLinear forward over BT5-T32 weights."""
+    _dev_tensor(X, torch.float32, "X")
+    _dev_tensor(P, torch.uint8, "P")
+    _dev_tensor(gamma, torch.float32, "gamma")
+    M, K = X.shape
+    Y = torch.empty((M, N), dtype=torch.float32, device=X.device) if out is None else out
+    acc = torch.empty((M, N), dtype=torch.int32, device=X.device) if with_acc else None
+    if ws is None:
+        ws = _workspace(workspace_bytes(WS_FORWARD5, M, N, K), X.device)
+    _check(lib().bitlinear_forward5(_ptr(X), M, K, _ptr(P), _ptr(gamma), N, _ptr(Y), _ptr(acc),
+                                    _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)),
+           "forward5")
+    return (Y, acc) if with_acc else Y
+
+
 class GroupPlan:
     """A grouped forward over independent BitLinear problems.
 
     problems: sequence of dicts with keys X, P, gamma, Y (torch CUDA
-    tensors), N, and optionally acc.  M and K come from X.  The plan binds
+    tensors), N, and optionally acc and format (FORMAT_BL2, the default, or
+    FORMAT_BT5 for pack5 weights).  M and K come from X.  The plan binds
     these tensors and its own workspace; run it with forward() (both stages)
     or quant_act() then matmul().
     """
@@ -256,7 +328,7 @@ class GroupPlan:
             _dev_tensor(Y, torch.float32, "Y")
             M, K = X.shape
             arr[i] = Problem(X.data_ptr(), P.data_ptr(), g.data_ptr(), Y.data_ptr(),
-                             _ptr(acc), M, int(p["N"]), K)
+                             _ptr(acc), M, int(p["N"]), K, int(p.get("format", FORMAT_BL2)), 0)
             keep.append((X, P, g, Y, acc))
         device = device or problems[0]["X"].device
         ws_bytes = L.bitlinear_group_workspace_bytes(arr, n)

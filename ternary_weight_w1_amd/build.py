@@ -15,8 +15,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libbitlinear.so")
-SOURCES = ["api.hip", "weight_quant.hip", "pack.hip", "act_quant.hip",
-           "gemv_stream.hip", "gemm_tile.hip"]
+SOURCES = ["api.hip", "weight_quant.hip", "pack.hip", "pack5.hip", "act_quant.hip",
+           "gemv_stream.hip", "gemm_tile.hip", "gemv5.hip"]
 ARCH = "gfx950"
 
 CFLAGS = [

@@ -254,7 +254,7 @@ __global__ __launch_bounds__(64 * WAVES) void quant_act_group_kernel(const Probl
     const Problem &p = probs[tok_map[tok]];
     const int64_t m = tok - p.tok_begin;
     if (m == 0 && p.tickets)
-        for (int i = threadIdx.x; i < p.NT; i += 64 * WAVES) p.tickets[i] = 0u;
+        for (int64_t i = threadIdx.x; i < ticket_count(p); i += 64 * WAVES) p.tickets[i] = 0u;
     const QDest dst{p.Q, p.ldq, m, p.KU, p.qtiled};
     quant_row<WAVES, kPlain>(p.X + m * p.K, p.K, dst, p.absmax + m, p.rowsum + m, nullptr, 0.0f);
 }

@@ -11,6 +11,7 @@
 #include <string>
 #include <vector>
 
+#include "bt5.hpp"
 #include "common.hpp"
 
 using bl::Problem;
@@ -144,11 +145,49 @@ void decompose(Problem &p, int64_t base_items, bool own_q, bool groups4 = false)
     }
 }
 
+// BT5-T32 weights always take the BT5 kernel, for any M: its work items are
+// (four 32-row tiles, 16 tokens, K split).  Splits are added while the
+// launch is short of workgroups, keeping at least four 160-code units each.
+int64_t bt5_items(int64_t M, int64_t N)
+{
+    const int64_t nt = (N + bl::kBt5TileRows - 1) / bl::kBt5TileRows;
+    return (nt + 3) / 4 * ((M + bl::kBt5Tokens - 1) / bl::kBt5Tokens);
+}
+void decompose5(Problem &p, int64_t base_items)
+{
+    p.fmt = 1;
+    p.kind = 2;
+    p.KU = (int32_t)((p.K + 63) / 64);
+    p.KU5 = (int32_t)((p.K + bl::kBt5UnitCodes - 1) / bl::kBt5UnitCodes);
+    p.NT = (int32_t)((p.N + bl::kBt5TileRows - 1) / bl::kBt5TileRows);
+    p.ntt = (p.NT + 3) / 4;
+    p.mt = (int32_t)((p.M + bl::kBt5Tokens - 1) / bl::kBt5Tokens);
+    p.mtile = p.qtiled = 0;
+    p.ks = 1;
+    p.upsplit = p.KU5;
+    const int64_t target = knobs().split_target;
+    if (base_items < target) {
+        int64_t ks = (target + base_items - 1) / base_items;
+        int64_t cap = p.KU5 / 4;
+        if (cap < 1) cap = 1;
+        if (ks > cap) ks = cap;
+        const int64_t upsplit = (p.KU5 + ks - 1) / ks;
+        p.upsplit = (int32_t)upsplit;
+        p.ks = (int32_t)((p.KU5 + upsplit - 1) / upsplit);
+    }
+}
+
 int64_t items_of(const Problem &p)
 {
     if (p.kind == 0) return (int64_t)(p.ntt > 0 ? p.ntt : p.NT) * p.ks;
+    if (p.kind == 2) return (int64_t)p.ntt * p.mt * p.ks;
     return (int64_t)p.mt * p.ntt;
 }
+
+// Row stride of the library's own int8 activations: whole 64-code units,
+// or whole 160-code units for BT5-T32 weights (the quantizer zero-fills the
+// row up to the stride, so every unit the kernels read is complete).
+int64_t own_ldq(const Problem &p) { return p.fmt ? 160 * (int64_t)p.KU5 : 64 * (int64_t)p.KU; }
 
 // Decomposition of a problem launched alone: the streaming MFMA kernel (more
 // tokens than the dot4 kernel takes) works on tile groups.
@@ -179,7 +218,7 @@ WsLayout ws_layout(const Problem &p, bool with_act)
 {
     WsLayout L;
     int64_t off = 0;
-    const int64_t ldq = 64 * (int64_t)p.KU;
+    const int64_t ldq = own_ldq(p);
     if (with_act) {
         L.q = off;
         off = up(off + (p.qtiled ? up(p.M, 32) : (int64_t)p.M) * ldq, 256);
@@ -188,11 +227,12 @@ WsLayout ws_layout(const Problem &p, bool with_act)
         L.rowsum = off;
         off = up(off + 4 * (int64_t)p.M, 256);
     }
-    if (p.kind == 0 && p.ks > 1) {
+    if (p.kind != 1 && p.ks > 1) {
+        const int64_t rows = (int64_t)p.NT * (p.kind == 2 ? bl::kBt5TileRows : 64);
         L.part = off;
-        off = up(off + 4 * (int64_t)p.ks * p.M * p.NT * 64, 256);
+        off = up(off + 4 * (int64_t)p.ks * p.M * rows, 256);
         L.tick = off;
-        off = up(off + 4 * (int64_t)p.NT, 256);
+        off = up(off + 4 * bl::ticket_count(p), 256);
     }
     L.total = off;
     return L;
@@ -218,6 +258,7 @@ Problem make_problem(int64_t M, int64_t N, int64_t K)
 
 hipError_t launch_contraction(const Problem &p, bool own_q, hipStream_t s)
 {
+    if (p.kind == 2) return bl::launch_bt5_single(p, s);
     if (p.kind == 0) return bl::launch_stream_single(p, stream_variant_for(p.M, p.upsplit), s);
     return bl::launch_tile_single(p, tile_variant(own_q), s);
 }
@@ -252,17 +293,30 @@ size_t bitlinear_packed_bytes(int64_t N, int64_t K)
 
 int64_t bitlinear_q_stride(int64_t K) { return (K < 1 || K > kMaxK) ? 0 : up(K, 64); }
 
+size_t bitlinear_packed5_bytes(int64_t N, int64_t K)
+{
+    if (N < 1 || N > kMaxMN || K < 1 || K > kMaxK) return 0;
+    return (size_t)((N + bl::kBt5TileRows - 1) / bl::kBt5TileRows) *
+           (size_t)((K + bl::kBt5UnitCodes - 1) / bl::kBt5UnitCodes) * 1024u;
+}
+
+int64_t bitlinear_q_stride5(int64_t K) { return (K < 1 || K > kMaxK) ? 0 : up(K, bl::kBt5UnitCodes); }
+
 size_t bitlinear_workspace_bytes(int op, int64_t M, int64_t N, int64_t K)
 {
     if (op == BITLINEAR_WS_QUANTIZE_WEIGHTS) {
         if (check_nk(N, K) != BITLINEAR_OK) return SIZE_MAX;
         return (size_t)quant_weight_blocks(N * K) * sizeof(double);
     }
-    if (op != BITLINEAR_WS_MATMUL && op != BITLINEAR_WS_FORWARD) return SIZE_MAX;
+    if (op < BITLINEAR_WS_MATMUL || op > BITLINEAR_WS_FORWARD5) return SIZE_MAX;
     if (check_mnk(M, N, K) != BITLINEAR_OK) return SIZE_MAX;
     Problem p = make_problem(M, N, K);
-    decompose_single(p, op == BITLINEAR_WS_FORWARD);
-    return (size_t)ws_layout(p, op == BITLINEAR_WS_FORWARD).total;
+    const bool with_act = op == BITLINEAR_WS_FORWARD || op == BITLINEAR_WS_FORWARD5;
+    if (op >= BITLINEAR_WS_MATMUL5)
+        decompose5(p, bt5_items(M, N));
+    else
+        decompose_single(p, with_act);
+    return (size_t)ws_layout(p, with_act).total;
 }
 
 int bitlinear_quantize_weights(const float *W, int64_t N, int64_t K, const float *gamma_in,
@@ -305,6 +359,24 @@ int bitlinear_unpack(const uint8_t *P, int64_t N, int64_t K, int8_t *T_out, void
     if (int st = check_nk(N, K)) return st;
     if (!a16(P) || !a16(T_out)) return fail(BITLINEAR_ERR_ALIGN, "unpack: buffers need 16-byte alignment");
     if (hipError_t e = bl::launch_unpack(P, N, K, T_out, static_cast<hipStream_t>(stream))) return hip_fail(e, "unpack");
+    return BITLINEAR_OK;
+}
+
+int bitlinear_pack5(const int8_t *T, int64_t N, int64_t K, uint8_t *P_out, void *stream)
+{
+    if (!T || !P_out) return fail(BITLINEAR_ERR_NULL, "pack5: T and P_out are required");
+    if (int st = check_nk(N, K)) return st;
+    if (!a16(T) || !a16(P_out)) return fail(BITLINEAR_ERR_ALIGN, "pack5: buffers need 16-byte alignment");
+    if (hipError_t e = bl::launch_pack5(T, N, K, P_out, static_cast<hipStream_t>(stream))) return hip_fail(e, "pack5");
+    return BITLINEAR_OK;
+}
+
+int bitlinear_unpack5(const uint8_t *P, int64_t N, int64_t K, int8_t *T_out, void *stream)
+{
+    if (!P || !T_out) return fail(BITLINEAR_ERR_NULL, "unpack5: P and T_out are required");
+    if (int st = check_nk(N, K)) return st;
+    if (!a16(P) || !a16(T_out)) return fail(BITLINEAR_ERR_ALIGN, "unpack5: buffers need 16-byte alignment");
+    if (hipError_t e = bl::launch_unpack5(P, N, K, T_out, static_cast<hipStream_t>(stream))) return hip_fail(e, "unpack5");
     return BITLINEAR_OK;
 }
 
@@ -439,6 +511,80 @@ int bitlinear_forward(const float *X, int64_t M, int64_t K, const uint8_t *P,
     return BITLINEAR_OK;
 }
 
+int bitlinear_matmul5(const int8_t *Q, int64_t ldq, const float *absmax, const int32_t *rowsum,
+                      int64_t M, int64_t K, const uint8_t *P5, const float *gamma, int64_t N,
+                      float *Y_out, int32_t *acc_out, void *ws, size_t ws_bytes, void *stream)
+{
+    if (!Q || !absmax || !rowsum || !P5 || !gamma || !Y_out)
+        return fail(BITLINEAR_ERR_NULL, "matmul5: Q, absmax, rowsum, P5, gamma and Y_out are required");
+    if (int st = check_mnk(M, N, K)) return st;
+    const int64_t k5 = up(K, bl::kBt5UnitCodes);
+    if (ldq < k5 || ldq % 16 != 0 || ldq > (int64_t(1) << 26))
+        return fail(BITLINEAR_ERR_SHAPE, "matmul5: ldq=%lld must be in [%lld, 2^26] and a multiple of 16",
+                    (long long)ldq, (long long)k5);
+    if (!a16(Q) || !a16(P5) || !a16(Y_out) || (acc_out && !a16(acc_out)) || !a4(absmax) || !a4(rowsum) || !a4(gamma))
+        return fail(BITLINEAR_ERR_ALIGN, "matmul5: arrays need 16-byte, scalars 4-byte alignment");
+    Problem p = make_problem(M, N, K);
+    decompose5(p, bt5_items(M, N));
+    const WsLayout L = ws_layout(p, false);
+    if (L.total > 0 && (!ws || ws_bytes < (size_t)L.total || !a16(ws)))
+        return fail(BITLINEAR_ERR_WORKSPACE, "matmul5: needs %lld workspace bytes (16-byte aligned)", (long long)L.total);
+    if (items_of(p) >= (int64_t(1) << 31)) return fail(BITLINEAR_ERR_SHAPE, "matmul5: grid too large");
+    p.Q = const_cast<int8_t *>(Q);
+    p.ldq = ldq;
+    p.absmax = const_cast<float *>(absmax);
+    p.rowsum = const_cast<int32_t *>(rowsum);
+    p.P = P5;
+    p.gamma = gamma;
+    p.Y = Y_out;
+    p.acc_out = acc_out;
+    char *base = static_cast<char *>(ws);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (p.ks > 1) {
+        p.acc_ws = reinterpret_cast<int32_t *>(base + L.part);
+        p.tickets = reinterpret_cast<uint32_t *>(base + L.tick);
+        if (hipError_t e = bl::launch_zero_words(p.tickets, bl::ticket_count(p), s)) return hip_fail(e, "zero tickets");
+    }
+    if (hipError_t e = launch_contraction(p, false, s)) return hip_fail(e, "matmul5");
+    return BITLINEAR_OK;
+}
+
+int bitlinear_forward5(const float *X, int64_t M, int64_t K, const uint8_t *P5,
+                       const float *gamma, int64_t N, float *Y_out, int32_t *acc_out,
+                       void *ws, size_t ws_bytes, void *stream)
+{
+    if (!X || !P5 || !gamma || !Y_out) return fail(BITLINEAR_ERR_NULL, "forward5: X, P5, gamma and Y_out are required");
+    if (int st = check_mnk(M, N, K)) return st;
+    if (!a16(X) || !a16(P5) || !a16(Y_out) || (acc_out && !a16(acc_out)) || !a4(gamma))
+        return fail(BITLINEAR_ERR_ALIGN, "forward5: arrays need 16-byte, gamma 4-byte alignment");
+    Problem p = make_problem(M, N, K);
+    decompose5(p, bt5_items(M, N));
+    const WsLayout L = ws_layout(p, true);
+    if (!ws || ws_bytes < (size_t)L.total || !a16(ws))
+        return fail(BITLINEAR_ERR_WORKSPACE, "forward5: needs %lld workspace bytes (16-byte aligned)", (long long)L.total);
+    if (items_of(p) >= (int64_t(1) << 31)) return fail(BITLINEAR_ERR_SHAPE, "forward5: grid too large");
+    char *base = static_cast<char *>(ws);
+    p.X = X;
+    p.P = P5;
+    p.gamma = gamma;
+    p.Y = Y_out;
+    p.acc_out = acc_out;
+    p.ldq = own_ldq(p);
+    p.Q = reinterpret_cast<int8_t *>(base + L.q);
+    p.absmax = reinterpret_cast<float *>(base + L.absmax);
+    p.rowsum = reinterpret_cast<int32_t *>(base + L.rowsum);
+    if (p.ks > 1) {
+        p.acc_ws = reinterpret_cast<int32_t *>(base + L.part);
+        p.tickets = reinterpret_cast<uint32_t *>(base + L.tick);
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (hipError_t e = bl::launch_quant_act(X, M, K, p.Q, p.ldq, 0, p.absmax, p.rowsum, p.tickets,
+                                            p.tickets ? (int)bl::ticket_count(p) : 0, s))
+        return hip_fail(e, "forward5: quant_act");
+    if (hipError_t e = launch_contraction(p, true, s)) return hip_fail(e, "forward5: matmul5");
+    return BITLINEAR_OK;
+}
+
 }  // extern "C"
 
 // --------------------------------------------------------------------------
@@ -449,7 +595,7 @@ namespace {
 struct GroupPlan {
     std::vector<Problem> probs;
     bl::GroupHeader h;
-    int64_t items_s = 0, items_t = 0;  // logical work items before XCD padding
+    int64_t items_s = 0, items_t = 0, items_5 = 0;  // logical work items before XCD padding
 };
 
 // Work-item map of one kernel: logical items in problem order; with
@@ -485,23 +631,32 @@ int build_group(const bitlinear_problem *in, int count, char *ws, GroupPlan &out
     if (count < 1 || count > (1 << 20)) return fail(BITLINEAR_ERR_SHAPE, "group: count=%d out of range", count);
     memset(&out.h, 0, sizeof out.h);
     out.probs.assign(count, make_problem(1, 1, 1));
-    int64_t base_items = 0;
+    int64_t base_items = 0, base5 = 0, max_m5 = 0;
     for (int i = 0; i < count; ++i) {
         const bitlinear_problem &q = in[i];
         if (!q.X || !q.P || !q.gamma || !q.Y) return fail(BITLINEAR_ERR_NULL, "group: problem %d lacks X, P, gamma or Y", i);
         if (int st = check_mnk(q.M, q.N, q.K)) return st;
         if (!a16(q.X) || !a16(q.P) || !a16(q.Y) || (q.acc && !a16(q.acc)) || !a4(q.gamma))
             return fail(BITLINEAR_ERR_ALIGN, "group: problem %d buffers misaligned", i);
-        if (q.M <= kStreamMaxM) base_items += (q.N + 63) / 64;
+        if ((q.format != BITLINEAR_FORMAT_BL2 && q.format != BITLINEAR_FORMAT_BT5) || q.reserved != 0)
+            return fail(BITLINEAR_ERR_ARG, "group: problem %d has unknown weight format %d (or reserved != 0)", i, q.format);
+        if (q.format == BITLINEAR_FORMAT_BT5) {
+            base5 += bt5_items(q.M, q.N);
+            max_m5 = q.M > max_m5 ? q.M : max_m5;
+        }
+        else if (q.M <= kStreamMaxM)
+            base_items += (q.N + 63) / 64;
     }
     if (base_items < 1) base_items = 1;
-    int64_t tokens = 0, items_s = 0, items_t = 0, off = 0;
+    if (base5 < 1) base5 = 1;
+    int64_t tokens = 0, items_s = 0, items_t = 0, items_5 = 0, off = 0;
     // streaming instantiation for the whole launch: LDS-staged dot4 when every
     // streaming problem has a single token (fused with the quantization when
     // none of them splits K), MFMA otherwise
     bool all_m1 = true, any_split = false;
     int64_t max_upsplit = 0;
     for (int i = 0; i < count; ++i) {
+        if (in[i].format == BITLINEAR_FORMAT_BT5) continue;
         Problem p = make_problem(in[i].M, in[i].N, in[i].K);
         decompose(p, base_items, true);
         if (p.kind != 0) continue;
@@ -516,27 +671,31 @@ int build_group(const bitlinear_problem *in, int count, char *ws, GroupPlan &out
         // the MFMA kernel's work items are tile groups
         base_items = 0;
         for (int i = 0; i < count; ++i)
-            if (in[i].M <= kStreamMaxM) base_items += ((in[i].N + 63) / 64 + kGroupTiles - 1) / kGroupTiles;
+            if (in[i].format != BITLINEAR_FORMAT_BT5 && in[i].M <= kStreamMaxM)
+                base_items += ((in[i].N + 63) / 64 + kGroupTiles - 1) / kGroupTiles;
         if (base_items < 1) base_items = 1;
     }
     for (int i = 0; i < count; ++i) {
         const bitlinear_problem &q = in[i];
         Problem &p = out.probs[i];
         p = make_problem(q.M, q.N, q.K);
-        decompose(p, base_items, true, groups4);
+        if (q.format == BITLINEAR_FORMAT_BT5)
+            decompose5(p, base5);
+        else
+            decompose(p, base_items, true, groups4);
         p.X = q.X;
         p.P = q.P;
         p.gamma = q.gamma;
         p.Y = q.Y;
         p.acc_out = q.acc;
-        p.ldq = 64 * (int64_t)p.KU;
+        p.ldq = own_ldq(p);
         const WsLayout L = ws_layout(p, true);
         if (ws) {
             char *b = ws + off;
             p.Q = reinterpret_cast<int8_t *>(b + L.q);
             p.absmax = reinterpret_cast<float *>(b + L.absmax);
             p.rowsum = reinterpret_cast<int32_t *>(b + L.rowsum);
-            if (p.kind == 0 && p.ks > 1) {
+            if (p.kind != 1 && p.ks > 1) {
                 p.acc_ws = reinterpret_cast<int32_t *>(b + L.part);
                 p.tickets = reinterpret_cast<uint32_t *>(b + L.tick);
             }
@@ -552,11 +711,15 @@ int build_group(const bitlinear_problem *in, int count, char *ws, GroupPlan &out
         if (p.kind == 0) {
             p.item_begin = (int32_t)items_s;
             items_s += items_of(p);
+        } else if (p.kind == 2) {
+            p.item_begin = (int32_t)items_5;
+            items_5 += items_of(p);
         } else {
             p.item_begin = (int32_t)items_t;
             items_t += items_of(p);
         }
-        if (tokens >= (int64_t(1) << 31) || items_s >= (int64_t(1) << 31) || items_t >= (int64_t(1) << 31))
+        if (tokens >= (int64_t(1) << 31) || items_s >= (int64_t(1) << 31) || items_t >= (int64_t(1) << 31) ||
+            items_5 >= (int64_t(1) << 31))
             return fail(BITLINEAR_ERR_SHAPE, "group: too many tokens or work items");
     }
     // every tile problem of a group takes the same tile variant (decompose
@@ -567,10 +730,14 @@ int build_group(const bitlinear_problem *in, int count, char *ws, GroupPlan &out
     h.n_tokens = (int32_t)tokens;
     out.items_s = items_s;
     out.items_t = items_t;
+    out.items_5 = items_5;
     if (knobs().xcd_order & 1) items_s = up(items_s, 8);
     if (knobs().xcd_order & 2) items_t = up(items_t, 8);
+    if (knobs().xcd_order & 1) items_5 = up(items_5, 8);
     h.n_items_stream = (int32_t)items_s;
     h.n_items_tile = (int32_t)items_t;
+    h.n_items_bt5 = (int32_t)items_5;
+    h.bt5_max_m = (int32_t)(max_m5 < bl::kBt5Tokens ? max_m5 : bl::kBt5Tokens);
     h.stream_variant = stream_variant;
     h.stream_lds = h.stream_variant >= 2 ? (int32_t)(64 * max_upsplit) : 0;
     h.tile_variant = tile_variant(true);
@@ -584,6 +751,8 @@ int build_group(const bitlinear_problem *in, int count, char *ws, GroupPlan &out
     t = up(t + 8 * items_s, 16);
     h.off_tile_map = t;
     t = up(t + 8 * items_t, 16);
+    h.off_bt5_map = t;
+    t = up(t + 8 * items_5, 16);
     h.total_bytes = t;
     return BITLINEAR_OK;
 }
@@ -641,6 +810,8 @@ int bitlinear_group_plan(const bitlinear_problem *probs, int count, void *ws, si
              reinterpret_cast<uint32_t *>(t + g.h.off_stream_map));
     fill_map(g.probs, 1, g.items_t, g.h.n_items_tile, (knobs().xcd_order & 2) != 0,
              reinterpret_cast<uint32_t *>(t + g.h.off_tile_map));
+    fill_map(g.probs, 2, g.items_5, g.h.n_items_bt5, knobs().xcd_order & 1,
+             reinterpret_cast<uint32_t *>(t + g.h.off_bt5_map));
     return BITLINEAR_OK;
 }
 
@@ -672,6 +843,10 @@ int bitlinear_group_matmul(const void *table_host, const void *table_dev, void *
         if (hipError_t e = bl::launch_tile_group(probs, reinterpret_cast<const uint2 *>(d + h.off_tile_map),
                                                  h.n_items_tile, h.tile_variant, s))
             return hip_fail(e, "group tile kernel");
+    if (h.n_items_bt5 > 0)
+        if (hipError_t e = bl::launch_bt5_group(probs, reinterpret_cast<const uint2 *>(d + h.off_bt5_map),
+                                                h.n_items_bt5, h.bt5_max_m, s))
+            return hip_fail(e, "group BT5 kernel");
     return BITLINEAR_OK;
 }
 

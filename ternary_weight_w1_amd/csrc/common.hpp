@@ -53,7 +53,7 @@ constexpr int kStreamFragTokens = 16;
 // an array of them in device memory (the plan table).
 struct Problem {
     const float *X;        // fp32 activations, M x K (quantization input)
-    const uint8_t *P;      // BL2-T64 packed weights
+    const uint8_t *P;      // packed weights (BL2-T64, or BT5-T32 when fmt == 1)
     const float *gamma;    // device scalar
     float *Y;              // M x N fp32 output
     int32_t *acc_out;      // optional M x N int32 accumulators
@@ -65,18 +65,27 @@ struct Problem {
     int64_t ldq;           // row stride of Q in bytes (>= 64*KU, % 16 == 0)
     int32_t M, N, K;
     int32_t KU;            // ceil(K/64)
-    int32_t NT;            // ceil(N/64)
+    int32_t NT;            // row tiles: ceil(N/64), or ceil(N/32) for BT5-T32
     int32_t ks;            // K splits of the streaming kernel (1 = none)
     int32_t upsplit;       // units per split (last split may be shorter)
-    int32_t kind;          // 0 = streaming kernel (small M), 1 = tile kernel
+    int32_t kind;          // 0 = streaming kernel (small M), 1 = tile kernel, 2 = BT5-T32 kernel
     int32_t mtile;         // rows of M per tile-kernel work item
     int32_t qtiled;        // 1: Q is stored in MFMA fragment order (see below)
-    int32_t mt;            // M tiles of the tile kernel
-    int32_t ntt;           // N tiles of the tile kernel
+    int32_t mt;            // M tiles of the tile kernel (token groups of the BT5 kernel)
+    int32_t ntt;           // N tiles of the tile kernel (four-tile groups of the BT5 kernel)
     int32_t tok_begin;     // first row of this problem in the grouped quant grid
     int32_t item_begin;    // first work item of this problem in its kernel's grid
+    int32_t fmt;           // 0: BL2-T64 weights, 1: BT5-T32 weights
+    int32_t KU5;           // ceil(K/160), the BT5-T32 units (0 for BL2-T64)
 };
-static_assert(sizeof(Problem) == 144, "Problem layout is shared by host and device");
+static_assert(sizeof(Problem) == 152, "Problem layout is shared by host and device");
+
+// Split-K arrival counters of a problem: one per N tile of the 2-bit
+// streaming kernels, one per (four-tile group, token group) of the BT5 kernel.
+__host__ __device__ inline int64_t ticket_count(const Problem &p)
+{
+    return p.kind == 2 ? (int64_t)p.ntt * p.mt : (int64_t)p.NT;
+}
 
 // Fragment order of the int8 activations ("QF32"), used by the tile kernel
 // so that each wave reads an MFMA A operand with one contiguous 1 KiB load:
@@ -103,15 +112,17 @@ struct GroupHeader {
     int32_t stream_variant; // streaming kernel instantiation (see api.hip)
     int32_t tile_variant;   // tile kernel instantiation
     int32_t stream_lds;     // dynamic LDS bytes of the streaming kernel
-    int32_t pad_[2];
+    int32_t n_items_bt5;    // work items of the BT5-T32 kernel
+    int32_t bt5_max_m;      // largest token count among the BT5-T32 problems
     int64_t ws_bytes;       // workspace the plan was built for
     int64_t off_probs;      // byte offsets inside the table
     int64_t off_tok_map;    // uint32 per token: problem index
     int64_t off_stream_map; // uint2 per workgroup: {problem, local item} ({~0u, 0} = idle)
     int64_t off_tile_map;   // uint2 per workgroup: {problem, local item}
+    int64_t off_bt5_map;    // uint2 per workgroup: {problem, local item}
     int64_t total_bytes;
 };
-constexpr uint32_t kGroupMagic = 0xB17E0001u;
+constexpr uint32_t kGroupMagic = 0xB17E0002u;
 
 // Kernel launchers (each defined next to its kernels).
 hipError_t launch_absmean_partial(const float *W, int64_t count, double *partial, int nblocks,
@@ -122,6 +133,8 @@ hipError_t launch_ternarize(const float *W, int64_t count, const float *gamma, i
                             hipStream_t s);
 hipError_t launch_pack(const int8_t *T, int64_t N, int64_t K, uint8_t *P, hipStream_t s);
 hipError_t launch_unpack(const uint8_t *P, int64_t N, int64_t K, int8_t *T, hipStream_t s);
+hipError_t launch_pack5(const int8_t *T, int64_t N, int64_t K, uint8_t *P, hipStream_t s);
+hipError_t launch_unpack5(const uint8_t *P, int64_t N, int64_t K, int8_t *T, hipStream_t s);
 hipError_t launch_quant_act(const float *X, int64_t M, int64_t K, int8_t *Q, int64_t ldq,
                             int qtiled, float *absmax, int32_t *rowsum, uint32_t *zero_ptr,
                             int zero_n, hipStream_t s);
@@ -139,5 +152,8 @@ hipError_t launch_stream_group(const Problem *probs, const uint2 *item_map, int 
 hipError_t launch_tile_single(const Problem &p, int variant, hipStream_t s);
 hipError_t launch_tile_group(const Problem *probs, const uint2 *item_map, int n_items,
                              int variant, hipStream_t s);
+hipError_t launch_bt5_single(const Problem &p, hipStream_t s);
+hipError_t launch_bt5_group(const Problem *probs, const uint2 *item_map, int n_items, int max_tokens,
+                            hipStream_t s);
 
 }  // namespace bl

@@ -29,7 +29,7 @@ def _declared():
 
 def test_every_declared_symbol_is_exported():
     names = _declared()
-    assert len(names) == 20, names
+    assert len(names) == 26, names
     out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r"\bT (bitlinear_\w+)", out))
@@ -49,7 +49,7 @@ def test_no_oracle_in_product():
 
 def test_version_and_strings():
     L = B.lib()
-    assert L.bitlinear_abi_version() == 1
+    assert L.bitlinear_abi_version() == 2
     for st in range(-6, 1):
         assert L.bitlinear_strerror(st)
     assert L.bitlinear_strerror(-99) == b"unknown status"
@@ -130,10 +130,10 @@ def test_pack_quant_matmul_forward_validation():
                FAKE, need - 1, None)[0] == -4
 
 
-def _problems(specs):
+def _problems(specs, fmt=0):
     arr = (B.Problem * len(specs))()
     for i, (M, N, K) in enumerate(specs):
-        arr[i] = B.Problem(FAKE, FAKE, FAKE, FAKE, None, M, N, K)
+        arr[i] = B.Problem(FAKE, FAKE, FAKE, FAKE, None, M, N, K, fmt, 0)
     return arr
 
 
@@ -148,7 +148,7 @@ def test_group_plan_table_on_host():
     st = L.bitlinear_group_plan(arr, len(specs), FAKE, wsb, host.ctypes.data, tb)
     assert st == 0, L.bitlinear_last_error()
     hdr = np.frombuffer(host[:48].tobytes(), np.int32)
-    assert hdr[0] == np.int32(np.uint32(0xB17E0001).astype(np.int32))
+    assert hdr[0] == np.int32(np.uint32(0xB17E0002).astype(np.int32))
     assert hdr[1] == 4            # problems
     assert hdr[2] in (0, 4)       # tokens quantized by the separate kernel (0 when fused)
     items = sum((N + 63) // 64 for _, N, _ in specs)
@@ -195,3 +195,71 @@ def test_group_calls_reject_foreign_tables():
     junk = np.zeros(256, np.uint8)
     assert L.bitlinear_group_forward(junk.ctypes.data, FAKE, None) == -6
     assert L.bitlinear_group_matmul(None, FAKE, None) == -1
+
+
+# ----------------------------------------------------- BT5-T32 (five per byte) --
+
+@pytest.mark.parametrize("N,K", [(1, 1), (32, 160), (33, 161), (2560, 2560), (2560, 6912),
+                                 (28672, 8192)])
+def test_packed5_bytes_matches_oracle(N, K):
+    import oracle
+    assert B.packed5_bytes(N, K) == oracle.packed5_bytes(N, K)
+
+
+def test_bt5_size_helpers():
+    assert B.packed5_bytes(0, 160) == 0 and B.packed5_bytes(32, 131073) == 0
+    assert B.q_stride5(100) == 160 and B.q_stride5(161) == 320 and B.q_stride5(0) == 0
+    smax = ctypes.c_size_t(-1).value
+    assert B.workspace_bytes(B.WS_FORWARD5, 0, 64, 64) == smax
+    assert B.workspace_bytes(6, 1, 64, 64) == smax
+    # forward5 holds Q at stride q_stride5(K), absmax and row sums
+    assert B.workspace_bytes(B.WS_FORWARD5, 4, 256, 256) >= 4 * 320 + 8
+    # many row tiles: no K split, no matmul5 workspace; one tile, long K: split
+    assert B.workspace_bytes(B.WS_MATMUL5, 1, 6912 * 40, 2560) == 0
+    assert B.workspace_bytes(B.WS_MATMUL5, 1, 32, 8192) > 0
+
+
+def test_bt5_validation():
+    assert _st("bitlinear_pack5", None, 4, 4, FAKE, None)[0] == -1
+    assert _st("bitlinear_pack5", FAKE, 4, 0, FAKE, None)[0] == -2
+    assert _st("bitlinear_pack5", FAKE, 4, 4, FAKE + 8, None)[0] == -3
+    assert _st("bitlinear_unpack5", FAKE, 4, 4, None, None)[0] == -1
+    # matmul5: ldq must cover K rounded up to 160 (128 does not for K = 100)
+    assert _st("bitlinear_matmul5", FAKE, 128, FAKE, FAKE, 2, 100, FAKE, FAKE, 64, FAKE, None,
+               None, 0, None)[0] == -2
+    assert _st("bitlinear_matmul5", FAKE, 168, FAKE, FAKE, 2, 100, FAKE, FAKE, 64, FAKE, None,
+               None, 0, None)[0] == -2  # not a multiple of 16
+    assert _st("bitlinear_matmul5", FAKE, 1 << 27, FAKE, FAKE, 2, 100, FAKE, FAKE, 64, FAKE,
+               None, None, 0, None)[0] == -2
+    assert _st("bitlinear_matmul5", None, 160, FAKE, FAKE, 2, 100, FAKE, FAKE, 64, FAKE, None,
+               None, 0, None)[0] == -1
+    assert _st("bitlinear_matmul5", FAKE, 160, FAKE, FAKE, 2, 100, FAKE + 4, FAKE, 64, FAKE,
+               None, None, 0, None)[0] == -3
+    need = B.workspace_bytes(B.WS_MATMUL5, 1, 32, 8192)
+    assert _st("bitlinear_matmul5", FAKE, 8320, FAKE, FAKE, 1, 8192, FAKE, FAKE, 32, FAKE, None,
+               FAKE, need - 1, None)[0] == -4
+    assert _st("bitlinear_forward5", FAKE, 1, 64, FAKE, FAKE, 64, FAKE, None, None, 0, None)[0] == -4
+    assert _st("bitlinear_forward5", FAKE, 1, 64, FAKE, FAKE, 0, FAKE, None, FAKE, 1 << 20,
+               None)[0] == -2
+
+
+def test_group_plan_bt5_items():
+    # BT5 problems go to the BT5 kernel's own item map: (four 32-row tiles,
+    # 16 tokens, K split) per item
+    L = B.lib()
+    specs = [(1, 2560, 2560), (1, 640, 2560), (1, 6912, 2560), (1, 2560, 6912)] * 30
+    arr = _problems(specs, fmt=1)
+    tb = L.bitlinear_group_table_bytes(arr, len(specs))
+    wsb = L.bitlinear_group_workspace_bytes(arr, len(specs))
+    host = np.zeros(tb, np.uint8)
+    assert L.bitlinear_group_plan(arr, len(specs), FAKE, max(wsb, 16), host.ctypes.data, tb) == 0
+    hdr = np.frombuffer(host[:48].tobytes(), np.int32)
+    items = sum(((N + 31) // 32 + 3) // 4 for _, N, _ in specs)
+    assert hdr[3] == 0 and hdr[4] == 0          # no 2-bit work
+    assert hdr[10] >= items and hdr[10] % 8 == 0  # BT5 items, padded for the XCD order
+    assert hdr[2] == len(specs)                  # every token quantized by the separate kernel
+    # unknown format or a nonzero reserved field rejects the plan
+    assert L.bitlinear_group_table_bytes(_problems([(1, 64, 64)], fmt=2), 1) == 0
+    bad = _problems([(1, 64, 64)], fmt=1)
+    bad[0].reserved = 1
+    assert L.bitlinear_group_table_bytes(bad, 1) == 0
