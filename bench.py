@@ -162,7 +162,7 @@ def curve(B, torch, model, Ms, dev, steps, warmup):
     return out
 
 
-def bt5_section(B, torch, mats, dev, Ms, steps, warmup):
+def bt5_section(B, torch, mats, dev, Ms, steps, warmup, model):
     """The stack in BT5-T32 (five codes per byte) against the 2-bit path at
     each M: step time (quantize + contract) and the contraction kernel's
     average duration (HIP events), with the BT5 kernel's algorithmic bytes
@@ -182,7 +182,8 @@ def bt5_section(B, torch, mats, dev, Ms, steps, warmup):
         out["points"].append({
             "M": M, "ms_per_step": round(ms5, 5), "kernel_ms": round(k5, 5),
             "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": round(gbs / HBM_PEAK_GBS, 4), "bytes_per_launch": alg},
+                         "frac": round(gbs / HBM_PEAK_GBS, 4), "bytes_per_launch": alg,
+                         "traffic": load_traffic(f"bt5_{model}_m{M}")},
             "bl2_ms_per_step": round(ms2, 5), "bl2_kernel_ms": round(k2, 5),
             "kernel_speedup_vs_bl2": round(k2 / k5, 3)})
         log(f"  BT5 M={M}: kernel {k5 * 1e3:.1f} us (2-bit {k2 * 1e3:.1f} us)")
@@ -307,7 +308,9 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
-                     "kernel": "stream contraction (grouped, one launch per step)",
+                     "kernel": "stream contraction (grouped, one launch per step)" +
+                               (f", BITLINEAR_DOT4_VARIANT={os.environ['BITLINEAR_DOT4_VARIANT']}"
+                                if os.environ.get("BITLINEAR_DOT4_VARIANT") else ""),
                      "kernel_ms_mean": round(kern_ms, 5), "bytes_per_launch": alg_bytes},
     }
     if gms is not None:
@@ -318,7 +321,7 @@ def main():
 
     if not args.no_bt5:
         log("timing BT5-T32 sweeps")
-        result["bt5"] = bt5_section(B, torch, mats, dev, [1, 8, 16], args.steps, args.warmup)
+        result["bt5"] = bt5_section(B, torch, mats, dev, [1, 8, 16], args.steps, args.warmup, args.model)
         for m in mats:
             m["P5"] = None
         torch.cuda.empty_cache()

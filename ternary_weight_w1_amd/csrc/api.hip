@@ -61,7 +61,7 @@ int check_mnk(int64_t M, int64_t N, int64_t K)
 // Tuning knobs, read once from the environment (immutable afterwards).
 struct Knobs {
     int dot4_max_m = 1;          // M <= this takes the packed-dot4 kernel
-    int dot4_variant = 3;        // 0: global activations, 2/3: LDS-staged (unroll 4/8)
+    int dot4_variant = 3;        // 0: global activations, 2/3: LDS-staged (unroll 4/8), 5: table lookup
     int fuse_quant = 0;          // single-token problems quantize in the dot4 prologue
     int split_target = 1024;     // aim for at least this many workgroups
     int xcd_order = 3;           // bit 0: streaming kernel, bit 1: tile kernel
@@ -73,7 +73,8 @@ const Knobs &knobs()
         Knobs v;
         if (const char *s = getenv("BITLINEAR_DOT4_MAX_M")) v.dot4_max_m = atoi(s) > 0 ? 1 : 0;
         if (const char *s = getenv("BITLINEAR_SPLIT_TARGET")) v.split_target = atoi(s) > 0 ? atoi(s) : 1;
-        if (const char *s = getenv("BITLINEAR_DOT4_VARIANT")) v.dot4_variant = (atoi(s) == 0 || atoi(s) == 2) ? atoi(s) : 3;
+        if (const char *s = getenv("BITLINEAR_DOT4_VARIANT"))
+            v.dot4_variant = (atoi(s) == 0 || atoi(s) == 2 || atoi(s) == 5) ? atoi(s) : 3;
         if (const char *s = getenv("BITLINEAR_FUSE_QUANT")) v.fuse_quant = atoi(s) != 0;
         if (const char *s = getenv("BITLINEAR_XCD_ORDER")) v.xcd_order = atoi(s) & 3;
         if (const char *s = getenv("BITLINEAR_TILE_VARIANT")) v.tile_variant = atoi(s);
@@ -103,6 +104,11 @@ int tile_variant(bool own_q)
 }
 int tile_bm(int variant) { return (variant == 0 || variant == 6 || variant == 19) ? 64 : 128; }
 bool tile_frag(int variant) { return variant >= 5 && variant <= 7; }
+
+// The table-lookup dot4 variant (knob value 5) runs single-token problems
+// with at most kLutMaxUnits units (64 KiB of table) per workgroup.
+constexpr int kLutMaxUnits = 64;
+bool lut_variant(int64_t M) { return knobs().dot4_variant == 5 && M <= knobs().dot4_max_m; }
 
 // Kernel kind and decomposition of one problem.  `base_items` is the number
 // of streaming work items the whole launch has without K splits; splits are
@@ -134,6 +140,11 @@ void decompose(Problem &p, int64_t base_items, bool own_q, bool groups4 = false)
             const int64_t upsplit = (p.KU + ks - 1) / ks;
             p.upsplit = (int32_t)upsplit;
             p.ks = (int32_t)((p.KU + upsplit - 1) / upsplit);
+        }
+        // the table-lookup variant holds 1 KiB of table per unit in LDS
+        if (lut_variant(p.M) && p.upsplit > kLutMaxUnits) {
+            p.upsplit = kLutMaxUnits;
+            p.ks = (p.KU + kLutMaxUnits - 1) / kLutMaxUnits;
         }
     } else {
         p.kind = 1;
@@ -205,6 +216,7 @@ int stream_variant_for(int64_t M, int64_t upsplit)
 {
     if (M > knobs().dot4_max_m) return 1;
     const int v = knobs().dot4_variant;
+    if (v == 5) return upsplit <= kLutMaxUnits ? 5 : 3;
     return (v != 0 && 64 * upsplit <= kStreamLdsMax) ? v : 0;
 }
 
@@ -739,7 +751,7 @@ int build_group(const bitlinear_problem *in, int count, char *ws, GroupPlan &out
     h.n_items_bt5 = (int32_t)items_5;
     h.bt5_max_m = (int32_t)(max_m5 < bl::kBt5Tokens ? max_m5 : bl::kBt5Tokens);
     h.stream_variant = stream_variant;
-    h.stream_lds = h.stream_variant >= 2 ? (int32_t)(64 * max_upsplit) : 0;
+    h.stream_lds = h.stream_variant >= 2 ? (int32_t)((h.stream_variant == 5 ? 1024 : 64) * max_upsplit) : 0;
     h.tile_variant = tile_variant(true);
     h.ws_bytes = off;
     int64_t t = up(sizeof(bl::GroupHeader), 16);

@@ -47,7 +47,11 @@ __device__ __forceinline__ Bt5Planes bt5_planes(unsigned w)
     r.h[2] = prefix(27u);
     r.h[3] = prefix(81u);
     const unsigned h5 = prefix(243u);
-    r.h[4] = h5 - (r.h[3] + (r.h[3] << 1));
+    // 3 H_4 as a shift-add kept apart from the subtraction (fused, the
+    // compiler picks a 64-bit multiply-add, a multi-pass instruction)
+    unsigned t3 = r.h[3] + (r.h[3] << 1);
+    asm volatile("" : "+v"(t3));
+    r.h[4] = h5 - t3;
     return r;
 }
 

@@ -18,8 +18,8 @@
 // off in the epilogue as for the 2-bit kernels.
 //
 // Work item: (group of four 32-row tiles, group of 16 tokens, K split); each
-// wave owns one tile and walks the split's 160-code units with three units in
-// flight.  Per unit a wave loads the packed block (16 bytes a lane) and the
+// wave owns one tile and walks the split's 160-code units with three or four
+// units in flight.  Per unit a wave loads the packed block (16 bytes a lane) and the
 // unit's activation rows -- ten 16-byte chunks per token, spread over the
 // lanes, NA = ceil(10 * tokens / 64) loads -- into a private LDS slot; the
 // five A operands are then LDS reads (rows of absent tokens and the zero
@@ -36,16 +36,21 @@ namespace bl {
 namespace {
 
 constexpr int kThreads = 256;  // four waves, one tile each
-constexpr int kRing = 3;       // units loaded ahead per wave
 
-// LDS of one wave: kRing slots of NA KiB (chunk i of a slot at 16 i) and a
-// 16-byte zero patch after them.
+// Units loaded ahead per wave: four, or three when three activation loads
+// per unit would push the wave past 128 VGPRs (four waves per SIMD).
 template <int NA>
-constexpr int wave_lds_bytes() { return kRing * NA * 1024 + 16; }
+constexpr int ring_of() { return NA >= 3 ? 3 : 4; }
+
+// LDS of one wave: the ring's slots of NA KiB (chunk i of a slot at 16 i) and
+// a 16-byte zero patch after them.
+template <int NA>
+constexpr int wave_lds_bytes() { return ring_of<NA>() * NA * 1024 + 16; }
 
 template <int NA>
 __device__ __forceinline__ void bt5_body(const Problem &p, int local)
 {
+    constexpr int kRing = ring_of<NA>();
     __shared__ __attribute__((aligned(16))) int8_t lds[4 * wave_lds_bytes<NA>()];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     // problem fields as wave-uniform values (they feed buffer resources and

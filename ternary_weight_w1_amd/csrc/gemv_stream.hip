@@ -111,14 +111,67 @@ __device__ void fused_quant_token(const Problem &p, int u0, int u1, float &absma
     rowsum = isum_l[0] + isum_l[1] + isum_l[2] + isum_l[3];
 }
 
+// Table-lookup variant, kept to compare against the dot4 stream: the pages
+// say the existing GPU path of the model uses lookup tables rather than
+// native tensor operations ("BitNet: Microsoft's AI Revolution Shows Why
+// Precision May be Overrated", promptinjection.net, "4. GPU Support: The
+// Fragile Boost").  Reading taken: for every pair of codes a nibble of the
+// packed word holds (two 2-bit fields f0, f1), the workgroup tabulates the
+// 16 possible partial sums f0 * q0 + f1 * q1 of the token's activations once;
+// the stream then replaces each nibble's multiply by one 16-bit LDS read.
+// Byte b of a word holds codes b, b + 4, b + 8, b + 12 of its 16 (bits 0, 2,
+// 4, 6), so nibble x of byte b pairs codes b + 8x and b + 8x + 4.
+// Table layout: for unit u of the range, word wi = 2 h + g of the unit and
+// pair pi = 2 b + x, the 16 int16 entries sit at byte
+// ((u - u0) * 32 + wi * 8 + pi) * 32 -- 1 KiB per 64-code unit.
+constexpr int kLutUnitBytes = 1024;
+
+__device__ inline int lut16(unsigned w, const int8_t *base)
+{
+    int s = 0;
+#pragma unroll
+    for (int pi = 0; pi < 8; ++pi) {
+        const unsigned v = (w >> (4 * pi)) & 0xFu;  // bit 8 b + 4 x = 4 pi
+        s += *reinterpret_cast<const int16_t *>(base + 32 * pi + 2 * v);
+    }
+    return s;
+}
+
+__device__ void build_lut(const Problem &p, int u0, int u1)
+{
+    const BL_GLOBAL int8_t *q = gload_ptr<int8_t>(p.Q);  // token 0, zero beyond K
+    for (int pg = threadIdx.x; pg < 32 * (u1 - u0); pg += kThreads) {
+        const int uu = pg >> 5, wi = (pg >> 3) & 3, pi = pg & 7;
+        const int k = 64 * (u0 + uu) + 32 * (wi >> 1) + 16 * (wi & 1) + (pi >> 1) + 8 * (pi & 1);
+        const int q0 = q[k], q1 = q[k + 4];
+        int e[16];
+#pragma unroll
+        for (int v = 0; v < 16; ++v) e[v] = (v & 3) * q0 + (v >> 2) * q1;
+        v4i lo, hi;
+        lo.x = (e[0] & 0xFFFF) | (e[1] << 16);
+        lo.y = (e[2] & 0xFFFF) | (e[3] << 16);
+        lo.z = (e[4] & 0xFFFF) | (e[5] << 16);
+        lo.w = (e[6] & 0xFFFF) | (e[7] << 16);
+        hi.x = (e[8] & 0xFFFF) | (e[9] << 16);
+        hi.y = (e[10] & 0xFFFF) | (e[11] << 16);
+        hi.z = (e[12] & 0xFFFF) | (e[13] << 16);
+        hi.w = (e[14] & 0xFFFF) | (e[15] << 16);
+        v4i *dst = reinterpret_cast<v4i *>(stream_q_lds + 32 * pg);
+        dst[0] = lo;
+        dst[1] = hi;
+    }
+}
+
 // QLDS: read the activations with broadcast LDS reads (2 distinct 16-byte
 // addresses per half wave) instead of two 16-byte global loads per lane per
 // unit, which would triple the vector-memory instructions of the stream.
 // FUSED: the activations are quantized in the prologue (implies QLDS).
-template <int UNROLL, bool QLDS, bool FUSED = false>
+// LUT: the table-lookup variant above instead of dot products.
+template <int UNROLL, bool QLDS, bool FUSED = false, bool LUT = false>
 __device__ void stream_dot4(const Problem &p, int local)
 {
     static_assert(!FUSED || QLDS, "the fused prologue writes the LDS activations");
+    static_assert(!LUT || (QLDS && !FUSED), "the table takes the LDS");
     __shared__ int red[kWaves][64];
     const int tile = local / p.ks, split = local - tile * p.ks;
     const int u0 = split * p.upsplit;
@@ -130,6 +183,9 @@ __device__ void stream_dot4(const Problem &p, int local)
     int tok_rowsum = 0;
     if constexpr (FUSED) {
         fused_quant_token(p, u0, u1, tok_absmax, tok_rowsum);
+    } else if constexpr (LUT) {
+        build_lut(p, u0, u1);
+        __syncthreads();
     } else if constexpr (QLDS) {
         const BL_GLOBAL v4i *src = gload_ptr<v4i>(p.Q + 64 * u0);
         v4i *dst = reinterpret_cast<v4i *>(stream_q_lds);
@@ -152,6 +208,28 @@ __device__ void stream_dot4(const Problem &p, int local)
 
     int acc0 = 0, acc1 = 0;  // rows r and 32 + r of the tile
     int u = u0 + wave;
+    if constexpr (LUT) {
+        // words (s, h): x = (0, 0), y = (0, 1), z = (1, 0), w = (1, 1); lane
+        // half g selects the table of code chunk g
+        for (; u + kWaves * (UNROLL - 1) < u1; u += kWaves * UNROLL) {
+            v4u w[UNROLL];
+#pragma unroll
+            for (int j = 0; j < UNROLL; ++j) w[j] = load_packed(blk + (int64_t)(u + kWaves * j) * 64);
+#pragma unroll
+            for (int j = 0; j < UNROLL; ++j) {
+                const int8_t *t0 = stream_q_lds + (u + kWaves * j - u0) * kLutUnitBytes + g * 256;
+                acc0 += lut16(w[j].x, t0) + lut16(w[j].y, t0 + 512);
+                acc1 += lut16(w[j].z, t0) + lut16(w[j].w, t0 + 512);
+            }
+        }
+        for (; u < u1; u += kWaves) {
+            const v4u w = load_packed(blk + (int64_t)u * 64);
+            const int8_t *t0 = stream_q_lds + (u - u0) * kLutUnitBytes + g * 256;
+            acc0 += lut16(w.x, t0) + lut16(w.y, t0 + 512);
+            acc1 += lut16(w.z, t0) + lut16(w.w, t0 + 512);
+        }
+        u = u1;  // the dot4 loops below have nothing left
+    }
     for (; u + kWaves * (UNROLL - 1) < u1; u += kWaves * UNROLL) {
         v4u w[UNROLL];
         v4i qa[UNROLL], qb[UNROLL];
@@ -344,7 +422,8 @@ __device__ void stream_mfma(const Problem &p, int local)
 // 0: dot4, activations from global; 1: MFMA (2..32 tokens, tile groups per
 // workgroup); 2: dot4 with
 // LDS-staged activations; 3: as 2 with 8 units in flight per wave; 4: as 3
-// with the activation quantization fused into the prologue.
+// with the activation quantization fused into the prologue; 5: the
+// table-lookup comparison variant (one token).
 template <int V>
 __device__ inline void stream_body(const Problem &p, int local)
 {
@@ -356,8 +435,10 @@ __device__ inline void stream_body(const Problem &p, int local)
         stream_dot4<4, true>(p, local);
     else if constexpr (V == 3)
         stream_dot4<8, true>(p, local);
-    else
+    else if constexpr (V == 4)
         stream_dot4<8, true, true>(p, local);
+    else
+        stream_dot4<8, true, false, true>(p, local);
 }
 
 template <int V>
@@ -382,12 +463,13 @@ hipError_t launch_stream_single(const Problem &p, int variant, hipStream_t s)
     // the MFMA variant's work items are tile groups (p.ntt of them)
     const int64_t tiles = variant == 1 ? (int64_t)p.ntt : (int64_t)p.NT;
     const dim3 grid((unsigned)(tiles * p.ks)), block(kThreads);
-    const unsigned lds = variant >= 2 ? 64u * (unsigned)p.upsplit : 0u;
+    const unsigned lds = variant >= 2 ? (variant == 5 ? kLutUnitBytes : 64u) * (unsigned)p.upsplit : 0u;
     switch (variant) {
     case 0: hipLaunchKernelGGL(stream_single_kernel<0>, grid, block, 0, s, p); break;
     case 1: hipLaunchKernelGGL(stream_single_kernel<1>, grid, block, 0, s, p); break;
     case 2: hipLaunchKernelGGL(stream_single_kernel<2>, grid, block, lds, s, p); break;
     case 3: hipLaunchKernelGGL(stream_single_kernel<3>, grid, block, lds, s, p); break;
+    case 5: hipLaunchKernelGGL(stream_single_kernel<5>, grid, block, lds, s, p); break;
     default: hipLaunchKernelGGL(stream_single_kernel<4>, grid, block, lds, s, p); break;
     }
     return hipGetLastError();
@@ -403,6 +485,7 @@ hipError_t launch_stream_group(const Problem *probs, const uint2 *item_map, int 
     case 1: hipLaunchKernelGGL(stream_group_kernel<1>, grid, block, 0, s, probs, item_map); break;
     case 2: hipLaunchKernelGGL(stream_group_kernel<2>, grid, block, lds, s, probs, item_map); break;
     case 3: hipLaunchKernelGGL(stream_group_kernel<3>, grid, block, lds, s, probs, item_map); break;
+    case 5: hipLaunchKernelGGL(stream_group_kernel<5>, grid, block, lds, s, probs, item_map); break;
     default: hipLaunchKernelGGL(stream_group_kernel<4>, grid, block, lds, s, probs, item_map); break;
     }
     return hipGetLastError();

@@ -498,6 +498,48 @@ def test_fused_quant_prologue_subprocess(B):
     assert r.returncode == 0 and "fused ok" in r.stdout, r.stdout + r.stderr
 
 
+LUT_SCRIPT = r"""
+import numpy as np, torch, sys
+sys.path.insert(0, ".")
+import oracle as O, synth, ternary_weight_w1_amd as B
+dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+def check(Y, acc, ref):
+    assert np.array_equal(acc, ref["acc"]) and np.array_equal(Y, ref["Y"])
+# single calls: short rows, a ragged K, K = 6912 (108 units: two 64-unit
+# table ranges) and a long K split over many workgroups
+for N, K in [(640, 512), (100, 37), (300, 130), (2560, 6912), (64, 28672)]:
+    T = synth.random_ternary(N, K, seed=N + K); X = synth.activations_np(1, K, seed=K, outlier_frac=0.01)
+    ref = O.forward(X, T, np.float32(0.031))
+    Y, acc = B.forward(dev(X), dev(O.pack(T)), dev(np.array([0.031], np.float32)), N, with_acc=True)
+    torch.cuda.synchronize(); check(Y.cpu().numpy(), acc.cpu().numpy(), ref)
+probs, refs = [], []
+for i, (N, K) in enumerate([(2560, 2560), (640, 2560), (6912, 2560), (2560, 6912), (4000, 37)]):
+    T = synth.random_ternary(N, K, seed=600 + i); X = synth.activations_np(1, K, seed=700 + i)
+    refs.append(O.forward(X, T, np.float32(0.02)))
+    probs.append(dict(X=dev(X), P=dev(O.pack(T)), gamma=dev(np.array([0.02], np.float32)),
+                      Y=torch.empty((1, N), device="cuda"), acc=torch.empty((1, N), dtype=torch.int32, device="cuda"), N=N))
+plan = B.GroupPlan(probs)
+assert int(np.frombuffer(plan.table_host.numpy()[:48].tobytes(), np.int32)[7]) == 5
+for rep in range(2):
+    plan.forward(); torch.cuda.synchronize()
+    for p, ref in zip(probs, refs):
+        check(p["Y"].cpu().numpy(), p["acc"].cpu().numpy(), ref)
+print("lut ok")
+"""
+
+
+def test_lut_variant_subprocess(B):
+    # the table-lookup comparison variant of the one-token stream
+    # (BITLINEAR_DOT4_VARIANT=5, a process-wide knob, hence one child process)
+    say("table-lookup dot4 variant (child process)")
+    import os
+    import subprocess
+    env = dict(os.environ, BITLINEAR_DOT4_VARIANT="5")
+    r = subprocess.run([sys.executable, "-c", LUT_SCRIPT], env=env, capture_output=True,
+                       text=True, timeout=110)
+    assert r.returncode == 0 and "lut ok" in r.stdout, r.stdout + r.stderr
+
+
 def test_group_mixed(B):
     say("group mixed")
     _group_run(B, [(1, 640, 2560), (4, 100, 200), (40, 257, 640), (130, 300, 700), (17, 64, 64)], 600)
