@@ -52,6 +52,8 @@ def lib():
         L.oracle_relu2_gate_quant_act.argtypes = [_vp, _vp, _i64, _i64, _vp, _vp, _vp, _vp]
         L.oracle_rmsnorm_quant_act.restype = None
         L.oracle_rmsnorm_quant_act.argtypes = [_vp, _i64, _i64, _vp, _f32, _vp, _vp, _vp, _vp, _vp]
+        L.oracle_add_rmsnorm_quant_act.restype = None
+        L.oracle_add_rmsnorm_quant_act.argtypes = [_vp, _vp, _i64, _i64, _vp, _f32, _vp, _vp, _vp, _vp, _vp, _vp]
         for name in ("oracle_matmul", "oracle_matmul_addsub"):
             f = getattr(L, name)
             f.restype = None
@@ -183,6 +185,25 @@ def rmsnorm_quant_act(X, g=None, eps=1e-5):
     lib().oracle_rmsnorm_quant_act(_p(X), M, K, None if gp is None else _p(gp), eps, _p(Xn),
                                    _p(inv), _p(Q), _p(a), _p(rs))
     return Q, a, rs, Xn, inv
+
+
+def add_rmsnorm_quant_act(X, R, g=None, eps=1e-5):
+    """S = X + R (fp32), then rmsnorm_quant_act on S:
+    (Q, absmax, rowsum, S, Xn, inv)."""
+    X = _c(X, np.float32)
+    R = _c(R, np.float32)
+    M, K = X.shape
+    assert R.shape == X.shape
+    gp = None if g is None else _c(g, np.float32)
+    Q = np.empty((M, K), np.int8)
+    a = np.empty(M, np.float32)
+    rs = np.empty(M, np.int32)
+    S = np.empty((M, K), np.float32)
+    Xn = np.empty((M, K), np.float32)
+    inv = np.empty(M, np.float32)
+    lib().oracle_add_rmsnorm_quant_act(_p(X), _p(R), M, K, None if gp is None else _p(gp), eps, _p(S),
+                                       _p(Xn), _p(inv), _p(Q), _p(a), _p(rs))
+    return Q, a, rs, S, Xn, inv
 
 
 def relu2_gate_quant_act(G, U):

@@ -38,6 +38,8 @@
  *      per-channel gain (oracle_rmsnorm_quant_act).
  *  R14 the squared-ReLU feed-forward is gated: h = relu(gate)^2 * up
  *      (oracle_relu2_gate_quant_act).
+ *  R17 blocks are pre-norm with an fp32 residual add before the next
+ *      sub-layer norm (oracle_add_rmsnorm_quant_act).
  *
  * Parity pins: every function below is pinned by tests/test_oracle_pins.py
  * against closed forms, hand-derived fixtures (tests/golden/), library
@@ -336,6 +338,17 @@ void oracle_rmsnorm_quant_act(const float *X, int64_t M, int64_t K, const float 
 /* value is h = relu(g)^2 * u from the gate and up projections' outputs,     */
 /* evaluated in fp32 as r = max(g, 0); h = (r * r) * u (two roundings in     */
 /* that order); then the absmax int8 cast of h (R3).  H (nullable) gets h.   */
+/* Residual add before the sub-layer norm (reading R17: pre-norm blocks,
+ * x_next = x + sublayer(norm(x)), with the addition in fp32): S = X + R,
+ * then oracle_rmsnorm_quant_act on S.                                       */
+void oracle_add_rmsnorm_quant_act(const float *X, const float *R, int64_t M, int64_t K,
+                                  const float *g, float eps, float *S, float *Xn, float *inv_out,
+                                  int8_t *Q, float *absmax, int32_t *rowsum)
+{
+    for (int64_t i = 0; i < M * K; ++i) S[i] = X[i] + R[i];
+    oracle_rmsnorm_quant_act(S, M, K, g, eps, Xn, inv_out, Q, absmax, rowsum);
+}
+
 /* ------------------------------------------------------------------------ */
 
 void oracle_relu2_gate_quant_act(const float *G, const float *U, int64_t M, int64_t N, float *H,

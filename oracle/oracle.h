@@ -28,6 +28,9 @@ void    oracle_quant_act(const float *X, int64_t M, int64_t K,
 void    oracle_rmsnorm_quant_act(const float *X, int64_t M, int64_t K, const float *g,
                                  float eps, float *Xn, float *inv_out, int8_t *Q,
                                  float *absmax, int32_t *rowsum);
+void    oracle_add_rmsnorm_quant_act(const float *X, const float *R, int64_t M, int64_t K,
+                                     const float *g, float eps, float *S, float *Xn, float *inv_out,
+                                     int8_t *Q, float *absmax, int32_t *rowsum);
 void    oracle_relu2_gate_quant_act(const float *G, const float *U, int64_t M, int64_t N,
                                     float *H, int8_t *Q, float *absmax, int32_t *rowsum);
 void    oracle_matmul(const int8_t *Q, const int8_t *T, int64_t M, int64_t N, int64_t K,

@@ -632,6 +632,33 @@ def test_rmsnorm_power_of_two_invariance():
     np.testing.assert_array_equal(a2, a * 2)
 
 
+def test_add_rmsnorm_residual_sum_and_reductions():
+    # R17: the residual sum is one fp32 addition per element (numpy's IEEE
+    # float32 add is the reference), and the cast is then exactly the RMSNorm
+    # cast of that sum; R = 0 reduces to the plain RMSNorm cast, R = -X to an
+    # all-zero row, and the hand fixture (3, 4) arrives as (1, 2) + (2, 2)
+    rng = np.random.default_rng(17)
+    for M, K in [(1, 5), (3, 37), (4, 2560)]:
+        X = rng.standard_normal((M, K)).astype(np.float32) * 3
+        R = rng.standard_normal((M, K)).astype(np.float32)
+        g = (rng.random(K) + 0.5).astype(np.float32)
+        Q, a, rs, S, Xn, inv = O.add_rmsnorm_quant_act(X, R, g, 1e-5)
+        np.testing.assert_array_equal(S, np.add(X, R, dtype=np.float32))
+        Q2, a2, rs2, Xn2, inv2 = O.rmsnorm_quant_act(np.add(X, R, dtype=np.float32), g, 1e-5)
+        np.testing.assert_array_equal(Q, Q2)
+        np.testing.assert_array_equal(a, a2)
+        np.testing.assert_array_equal(rs, rs2)
+        Q0, a0, rs0, S0, _, _ = O.add_rmsnorm_quant_act(X, np.zeros_like(X), g, 1e-5)
+        Q1, a1, rs1, _, _ = O.rmsnorm_quant_act(X, g, 1e-5)
+        np.testing.assert_array_equal(S0, X)
+        np.testing.assert_array_equal(Q0, Q1)
+        Qz, az, rsz, Sz, _, _ = O.add_rmsnorm_quant_act(X, -X, None, 1e-5)
+        assert not Sz.any() and not Qz.any() and not rsz.any()
+    Q, a, rs, S, _, _ = O.add_rmsnorm_quant_act(np.array([[1.0, 2.0]], np.float32),
+                                                np.array([[2.0, 2.0]], np.float32), None, 0.0)
+    assert S.tolist() == [[3.0, 4.0]] and Q[0].tolist() == [95, 127] and rs[0] == 222
+
+
 def test_rmsnorm_special_cases():
     # no gain == unit gain; a zero row stays zero (inv = 1/sqrt(eps), codes 0,
     # absmax at its floor); a constant row normalizes to +-1 -> +-127
