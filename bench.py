@@ -16,7 +16,9 @@ launch stream), against 8 TB/s.  prefill = the same 210 matrices at
 M = 512 (int8 TOP/s against 5.0 POP/s dense int8).  graph = the decode
 step captured once in a HIP graph and replayed.  curves = latency of a full
 sweep over the 3B-class stack at M in {1, 8, 64, 256} (and, on request, the
-70B-class stack at M in {1, 16, 176}).  bt5 = the same 2B stack packed
+70B-class stack at M in {1, 16, 176}); for 3B also the same stack chained as
+pre-norm blocks (residual adds, norms, the gated squared-ReLU, a single-key
+attention) at M in {1, 8, 64}, eager and as a replayed HIP graph.  bt5 = the same 2B stack packed
 five codes per byte (BT5-T32, 1.6 bits per weight) at M in {1, 8, 16},
 next to the 2-bit path at the same M.  cpu_baseline = the CPU oracle
 (single thread) on a bounded sample of the same workload.
@@ -157,6 +159,9 @@ def curve(B, torch, model, Ms, dev, steps, warmup):
                               "TOPs": round(ops / (ms * 1e-3) / 1e12, 1)})
         log(f"  {model} M={M}: {ms:.3f} ms per sweep")
         del plan, probs
+    if model == "3b":
+        log("timing the 3B stack chained as pre-norm blocks")
+        out["chained"] = stack_curve(B, torch, mats, dev, [1, 8, 64], steps, warmup)
     del mats
     torch.cuda.empty_cache()
     return out
@@ -187,6 +192,101 @@ def bt5_section(B, torch, mats, dev, Ms, steps, warmup, model):
             "bl2_ms_per_step": round(ms2, 5), "bl2_kernel_ms": round(k2, 5),
             "kernel_speedup_vs_bl2": round(k2 / k5, 3)})
         log(f"  BT5 M={M}: kernel {k5 * 1e3:.1f} us (2-bit {k2 * 1e3:.1f} us)")
+    torch.cuda.empty_cache()
+    return out
+
+
+def stack_curve(B, torch, mats, dev, Ms, steps, warmup):
+    """The stack chained as pre-norm blocks, one decode (or prefill) step of
+    M tokens through every layer, each step a library call on one stream:
+    residual add + RMSNorm + int8 cast, q/k/v contractions, the attention of
+    the first decode position (a single key, so its output is v), the cast
+    of v, the o contraction, residual add + RMSNorm + cast, gate/up, the
+    gated squared-ReLU cast, down; then the final residual add + norm.
+    Timed eagerly and as one HIP graph replayed (the step has hundreds of
+    short launches).  Buffers and workspace are allocated once."""
+    import ctypes
+    L = B.lib()
+    layers = {}
+    for m in mats:
+        layers.setdefault(m["layer"], {})[m["name"]] = m
+    dim = layers[0]["q"]["K"]
+    ffn = layers[0]["gate"]["N"]
+    out = {"layers": len(layers), "dim": dim, "ffn": ffn, "points": []}
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(5)
+    gains = [(torch.rand(dim, generator=gen, device=dev) + 0.5, torch.rand(dim, generator=gen, device=dev) + 0.5)
+             for _ in layers]
+    g_fin = torch.rand(dim, generator=gen, device=dev) + 0.5
+    for M in Ms:
+        x0 = synth.activations_torch(M, dim, 21, dev)
+        f32 = lambda n: torch.empty((M, n), dtype=torch.float32, device=dev)
+        x, q, k, v, o, gate, up, d = f32(dim), f32(dim), f32(dim), f32(dim), f32(dim), f32(ffn), f32(ffn), f32(dim)
+        ldd, ldf = B.q_stride(dim), B.q_stride(ffn)
+        Qd_, Qf_ = (torch.empty((M, ld), dtype=torch.int8, device=dev) for ld in (ldd, ldf))
+        a = torch.empty(M, dtype=torch.float32, device=dev)
+        rs = torch.empty(M, dtype=torch.int32, device=dev)
+        wsb = max(B.workspace_bytes(B.WS_MATMUL, M, N, K) for N, K in ((dim, dim), (ffn, dim), (dim, ffn)))
+        ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
+        P = lambda t: ctypes.c_void_p(t.data_ptr())
+
+        def check(st):
+            if st != 0:
+                raise RuntimeError(L.bitlinear_last_error().decode())
+
+        def lin(Q, ld, K, w, Y):
+            check(L.bitlinear_matmul(P(Q), ld, P(a), P(rs), M, K, P(w["P"]), P(w["gamma"]), w["N"], P(Y), None,
+                                     P(ws), ws.numel(), s))
+
+        def step():
+            for i, lay in sorted(layers.items()):
+                ga, gf = gains[i]
+                if i == 0:
+                    check(L.bitlinear_quant_act_rmsnorm(P(x0), M, dim, P(ga), 1e-5, P(Qd_), ldd, P(a), P(rs), s))
+                else:
+                    check(L.bitlinear_quant_act_add_rmsnorm(P(x), P(d), M, dim, P(ga), 1e-5, P(x), P(Qd_), ldd,
+                                                            P(a), P(rs), s))
+                lin(Qd_, ldd, dim, lay["q"], q)
+                lin(Qd_, ldd, dim, lay["k"], k)
+                lin(Qd_, ldd, dim, lay["v"], v)
+                check(L.bitlinear_quant_act(P(v), M, dim, P(Qd_), ldd, P(a), P(rs), s))
+                lin(Qd_, ldd, dim, lay["o"], o)
+                check(L.bitlinear_quant_act_add_rmsnorm(P(x0 if i == 0 else x), P(o), M, dim, P(gf), 1e-5, P(x),
+                                                        P(Qd_), ldd, P(a), P(rs), s))
+                lin(Qd_, ldd, dim, lay["gate"], gate)
+                lin(Qd_, ldd, dim, lay["up"], up)
+                check(L.bitlinear_quant_act_relu2_gate(P(gate), P(up), M, ffn, P(Qf_), ldf, P(a), P(rs), s))
+                lin(Qf_, ldf, ffn, lay["down"], d)
+            check(L.bitlinear_quant_act_add_rmsnorm(P(x), P(d), M, dim, P(g_fin), 1e-5, P(x), P(Qd_), ldd,
+                                                    P(a), P(rs), s))
+
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            s = ctypes.c_void_p(side.cuda_stream)
+            for _ in range(max(1, warmup)):
+                step()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(steps):
+                step()
+            torch.cuda.synchronize()
+            eager = (time.perf_counter() - t0) / steps * 1e3
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph, stream=side):
+                step()
+        torch.cuda.current_stream().wait_stream(side)
+        for _ in range(max(1, warmup)):
+            graph.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            graph.replay()
+        torch.cuda.synchronize()
+        gms = (time.perf_counter() - t0) / steps * 1e3
+        out["points"].append({"M": M, "eager_ms_per_step": round(eager, 4), "graph_ms_per_step": round(gms, 4)})
+        log(f"  stack M={M}: eager {eager:.3f} ms, graph {gms:.3f} ms per step")
+        del graph
     torch.cuda.empty_cache()
     return out
 

@@ -197,6 +197,26 @@ int bitlinear_quant_act_rmsnorm(const float *X, int64_t M, int64_t K, const floa
                                 int32_t *rowsum_out, void *stream);
 
 /*
+ * Residual add, then bitlinear_quant_act_rmsnorm, in one pass: the input of
+ * the next sub-layer of a stack of BitLinear blocks (the sub-layer norm of
+ * the BitNet b1.58 2B4T video transcript, yousumm.com, "Transcription",
+ * applied to the residual stream; the reading taken is the pre-norm block
+ * x_next = x + sublayer(norm(x))):
+ *   Xsum[m][k] = X[m][k] + R[m][k]   (fp32, one rounding; written out)
+ *   then exactly bitlinear_quant_act_rmsnorm on Xsum.
+ *   X, R      [in]  M x K fp32 (16-byte aligned): residual stream and the
+ *                   sub-layer output added to it.
+ *   Xsum_out  [out] M x K fp32 (16-byte aligned); it may be X or R itself
+ *                   (in-place update), but may not otherwise overlap X, R or
+ *                   Q_out (BITLINEAR_ERR_ARG).
+ *   Other arguments, layouts and errors as bitlinear_quant_act_rmsnorm.
+ */
+int bitlinear_quant_act_add_rmsnorm(const float *X, const float *R, int64_t M, int64_t K,
+                                    const float *norm_weight, float eps, float *Xsum_out,
+                                    int8_t *Q_out, int64_t ldq, float *absmax_out,
+                                    int32_t *rowsum_out, void *stream);
+
+/*
  * Gated squared-ReLU feed-forward activation, then the per-token absmax
  * int8 cast, in one pass: the input of a feed-forward block's down
  * projection (BitNet b1.58 2B4T video transcript, yousumm.com,

@@ -75,6 +75,8 @@ def lib():
             "bitlinear_quant_act_rmsnorm": (_int, [_vp, _i64, _i64, _vp, ctypes.c_float, _vp, _i64, _vp,
                                                    _vp, _vp]),
             "bitlinear_quant_act_relu2_gate": (_int, [_vp, _vp, _i64, _i64, _vp, _i64, _vp, _vp, _vp]),
+            "bitlinear_quant_act_add_rmsnorm": (_int, [_vp, _vp, _i64, _i64, _vp, ctypes.c_float, _vp, _vp,
+                                                       _i64, _vp, _vp, _vp]),
             "bitlinear_matmul": (_int, [_vp, _i64, _vp, _vp, _i64, _i64, _vp, _vp, _i64, _vp, _vp,
                                         _vp, _sz, _vp]),
             "bitlinear_forward": (_int, [_vp, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _vp, _sz, _vp]),
@@ -192,6 +194,28 @@ def quant_act_rmsnorm(X, norm_weight=None, eps: float = 1e-5, ldq: int | None = 
     _check(lib().bitlinear_quant_act_rmsnorm(_ptr(X), M, K, _ptr(norm_weight), float(eps), _ptr(Q), ldq,
                                              _ptr(a), _ptr(rs), _stream(stream)), "quant_act_rmsnorm")
     return Q, a, rs
+
+
+def quant_act_add_rmsnorm(X, R, norm_weight=None, eps: float = 1e-5, out=None, ldq: int | None = None,
+                          stream=None):
+    """(Q, absmax, rowsum, Xsum): Xsum = X + R (written to `out`, which may
+    be X or R for an in-place update), then the RMSNorm int8 cast of Xsum."""
+    _dev_tensor(X, torch.float32, "X")
+    _dev_tensor(R, torch.float32, "R")
+    if norm_weight is not None:
+        _dev_tensor(norm_weight, torch.float32, "norm_weight")
+    M, K = X.shape
+    if R.shape != X.shape:
+        raise ValueError("R must have the shape of X")
+    ldq = q_stride(K) if ldq is None else ldq
+    Xs = torch.empty_like(X) if out is None else _dev_tensor(out, torch.float32, "out")
+    Q = torch.empty((M, ldq), dtype=torch.int8, device=X.device)
+    a = torch.empty(M, dtype=torch.float32, device=X.device)
+    rs = torch.empty(M, dtype=torch.int32, device=X.device)
+    _check(lib().bitlinear_quant_act_add_rmsnorm(_ptr(X), _ptr(R), M, K, _ptr(norm_weight), float(eps), _ptr(Xs),
+                                                 _ptr(Q), ldq, _ptr(a), _ptr(rs), _stream(stream)),
+           "quant_act_add_rmsnorm")
+    return Q, a, rs, Xs
 
 
 def quant_act_relu2_gate(G, U, ldq: int | None = None, stream=None):

@@ -56,16 +56,21 @@ struct QDest {
 //              NULL = all ones).  The fp64 sum runs per thread, then across
 //              lanes, then across waves in a fixed order: deterministic;
 //   kRelu2Gate h = (r * r) * u with r = max(x, 0), x the gate projection's
-//              output and u the up projection's (aux = u).
+//              output and u the up projection's (aux = u);
+//   kAddRmsNorm the residual sum s = x + r (fp32, one rounding; r = res_)
+//              is written to xo_ and cast as kRmsNorm casts x.  Every element
+//              is read and written by one thread, load before store, so xo_
+//              may be x_ or res_ (an in-place residual update).
 constexpr int kRegF4 = 32;
 constexpr int kFewTokens = 2048;
-enum { kPlain = 0, kRmsNorm = 1, kRelu2Gate = 2 };
+enum { kPlain = 0, kRmsNorm = 1, kRelu2Gate = 2, kAddRmsNorm = 3 };
 
 template <int WAVES, int MODE>
 __device__ void quant_row(const float *x_, int K, const QDest &dst, float *absmax_, int32_t *rowsum_,
-                          const float *g_, float eps)
+                          const float *g_, float eps, const float *res_ = nullptr, float *xo_ = nullptr)
 {
-    constexpr bool NORM = MODE == kRmsNorm;
+    constexpr bool NORM = MODE == kRmsNorm || MODE == kAddRmsNorm;
+    constexpr bool ADD = MODE == kAddRmsNorm;
     constexpr int kThr = 64 * WAVES;
     constexpr int kRegs = kRegF4 / WAVES;
     __shared__ float red_a[WAVES];
@@ -77,12 +82,28 @@ __device__ void quant_row(const float *x_, int K, const QDest &dst, float *absma
     BL_GLOBAL int8_t *q = gstore_ptr<int8_t>(dst.Q);
     // float4 path: K a multiple of 4 and the rows (and gains) 16-byte aligned
     const bool vec = ((K & 3) == 0) && ((reinterpret_cast<uintptr_t>(x_) & 15) == 0) &&
-                     (MODE == kPlain || !g_ || (reinterpret_cast<uintptr_t>(g_) & 15) == 0);
+                     (MODE == kPlain || !g_ || (reinterpret_cast<uintptr_t>(g_) & 15) == 0) &&
+                     (!ADD || ((reinterpret_cast<uintptr_t>(res_) | reinterpret_cast<uintptr_t>(xo_)) & 15) == 0);
+    const BL_GLOBAL float *rs = gload_ptr<float>(res_);
+    BL_GLOBAL float *xo = gstore_ptr<float>(xo_);
+    const BL_GLOBAL v4f *r4 = reinterpret_cast<const BL_GLOBAL v4f *>(rs);
+    BL_GLOBAL v4f *xo4 = reinterpret_cast<BL_GLOBAL v4f *>(xo);
     const int nf = K >> 2;
     const BL_GLOBAL v4f *x4 = reinterpret_cast<const BL_GLOBAL v4f *>(x);
     const BL_GLOBAL v4f *g4 = reinterpret_cast<const BL_GLOBAL v4f *>(gw);
     const bool in_regs = vec && nf <= kRegs * kThr;
     const v4f zero4 = {0.f, 0.f, 0.f, 0.f};
+    // the row value before the norm: x, or x + r in the residual mode
+    auto ld4 = [&](int f) {
+        v4f u = x4[f];
+        if constexpr (ADD) u = u + r4[f];
+        return u;
+    };
+    auto ld1 = [&](int i) {
+        float u = x[i];
+        if constexpr (ADD) u = u + rs[i];
+        return u;
+    };
 
     auto relu2 = [](float gv, float uv) {
         const float r = gv > 0.0f ? gv : 0.0f;
@@ -104,6 +125,11 @@ __device__ void quant_row(const float *x_, int K, const QDest &dst, float *absma
             v[j] = f < nf ? __builtin_nontemporal_load(x4 + f) : zero4;
             if constexpr (MODE == kRelu2Gate)
                 if (f < nf) v[j] = relu2_4(v[j], __builtin_nontemporal_load(g4 + f));
+            if constexpr (ADD)
+                if (f < nf) {
+                    v[j] = v[j] + __builtin_nontemporal_load(r4 + f);
+                    xo4[f] = v[j];
+                }
         }
     }
 
@@ -121,9 +147,12 @@ __device__ void quant_row(const float *x_, int K, const QDest &dst, float *absma
 #pragma unroll
             for (int j = 0; j < kRegs; ++j) s2 += sq4(v[j]);
         } else if (vec) {
-            for (int f = t; f < nf; f += kThr) s2 += sq4(x4[f]);
+            for (int f = t; f < nf; f += kThr) s2 += sq4(ld4(f));
         } else {
-            for (int i = t; i < K; i += kThr) s2 += (double)x[i] * (double)x[i];
+            for (int i = t; i < K; i += kThr) {
+                const double u = (double)ld1(i);
+                s2 += u * u;
+            }
         }
         for (int off = 32; off > 0; off >>= 1) s2 += __shfl_xor(s2, off, 64);
         if constexpr (WAVES > 1) {
@@ -145,8 +174,8 @@ __device__ void quant_row(const float *x_, int K, const QDest &dst, float *absma
         }
         return u;
     };
-    auto norm1 = [&](int i) {
-        float u = x[i];
+    // the value cast for element i, given its pre-norm value u
+    auto norm1v = [&](float u, int i) {
         if constexpr (NORM) {
             u = u * inv;
             if (g_) u = u * gw[i];
@@ -155,6 +184,7 @@ __device__ void quant_row(const float *x_, int K, const QDest &dst, float *absma
         }
         return u;
     };
+    auto norm1 = [&](int i) { return norm1v(ld1(i), i); };
     if constexpr (NORM) {
         if (in_regs) {
 #pragma unroll
@@ -173,7 +203,7 @@ __device__ void quant_row(const float *x_, int K, const QDest &dst, float *absma
 #pragma unroll
         for (int j = 0; j < kRegs; ++j) a = fmaxf(a, amax4(v[j]));
     } else if (vec) {
-        for (int f = t; f < nf; f += kThr) a = fmaxf(a, amax4(norm4(x4[f], f)));
+        for (int f = t; f < nf; f += kThr) a = fmaxf(a, amax4(norm4(ld4(f), f)));
     } else {
         for (int i = t; i < K; i += kThr) a = fmaxf(a, fabsf(norm1(i)));
     }
@@ -204,10 +234,16 @@ __device__ void quant_row(const float *x_, int K, const QDest &dst, float *absma
             if (f < nf) put4(f, v[j]);
         }
     } else if (vec) {
-        for (int f = t; f < nf; f += kThr) put4(f, norm4(x4[f], f));
+        for (int f = t; f < nf; f += kThr) {
+            const v4f u = ld4(f);
+            if constexpr (ADD) xo4[f] = u;
+            put4(f, norm4(u, f));
+        }
     } else {
         for (int i = t; i < K; i += kThr) {
-            const int8_t c = quant_code(norm1(i), s);
+            const float u = ld1(i);  // read once: xo may alias x or r
+            if constexpr (ADD) xo[i] = u;
+            const int8_t c = quant_code(norm1v(u, i), s);
             sum += c;
             q[dst.at(i)] = c;
         }
@@ -235,7 +271,8 @@ __global__ __launch_bounds__(64 * WAVES) void quant_act_kernel(const float *__re
                                                                int32_t *__restrict__ rowsum,
                                                                uint32_t *__restrict__ zero_ptr,
                                                                int zero_n, const float *__restrict__ g,
-                                                               float eps)
+                                                               float eps, const float *res = nullptr,
+                                                               float *xo = nullptr)
 {
     const int64_t m = blockIdx.x;
     if (m == 0 && zero_ptr)
@@ -243,7 +280,11 @@ __global__ __launch_bounds__(64 * WAVES) void quant_act_kernel(const float *__re
     const QDest dst{Q, ldq, m, (K + 63) / 64, qtiled};
     // the gate/up mode reads a second M x K array (g) row by row
     const float *aux = MODE == kRelu2Gate ? g + m * K : g;
-    quant_row<WAVES, MODE>(X + m * K, K, dst, absmax + m, rowsum ? rowsum + m : nullptr, aux, eps);
+    if constexpr (MODE == kAddRmsNorm)
+        quant_row<WAVES, MODE>(X + m * K, K, dst, absmax + m, rowsum ? rowsum + m : nullptr, aux, eps,
+                               res + m * K, xo + m * K);
+    else
+        quant_row<WAVES, MODE>(X + m * K, K, dst, absmax + m, rowsum ? rowsum + m : nullptr, aux, eps);
 }
 
 template <int WAVES>
@@ -290,6 +331,19 @@ hipError_t launch_quant_act_rmsnorm(const float *X, int64_t M, int64_t K, const 
     else
         hipLaunchKernelGGL((quant_act_kernel<1, kRmsNorm>), dim3((unsigned)M), dim3(64), 0, s, X, (int)K, Q,
                            ldq, 0, absmax, rowsum, nullptr, 0, g, eps);
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_act_add_rmsnorm(const float *X, const float *R, int64_t M, int64_t K, const float *g,
+                                        float eps, float *Xsum, int8_t *Q, int64_t ldq, float *absmax,
+                                        int32_t *rowsum, hipStream_t s)
+{
+    if (M < kFewTokens)
+        hipLaunchKernelGGL((quant_act_kernel<4, kAddRmsNorm>), dim3((unsigned)M), dim3(256), 0, s, X, (int)K,
+                           Q, ldq, 0, absmax, rowsum, nullptr, 0, g, eps, R, Xsum);
+    else
+        hipLaunchKernelGGL((quant_act_kernel<1, kAddRmsNorm>), dim3((unsigned)M), dim3(64), 0, s, X, (int)K,
+                           Q, ldq, 0, absmax, rowsum, nullptr, 0, g, eps, R, Xsum);
     return hipGetLastError();
 }
 

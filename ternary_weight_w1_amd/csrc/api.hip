@@ -426,6 +426,35 @@ int bitlinear_quant_act_rmsnorm(const float *X, int64_t M, int64_t K, const floa
     return BITLINEAR_OK;
 }
 
+int bitlinear_quant_act_add_rmsnorm(const float *X, const float *R, int64_t M, int64_t K,
+                                    const float *norm_weight, float eps, float *Xsum_out, int8_t *Q_out,
+                                    int64_t ldq, float *absmax_out, int32_t *rowsum_out, void *stream)
+{
+    if (!X || !R || !Xsum_out || !Q_out || !absmax_out)
+        return fail(BITLINEAR_ERR_NULL, "quant_act_add_rmsnorm: X, R, Xsum_out, Q_out and absmax_out are required");
+    if (int st = check_mnk(M, 1, K)) return st;
+    if (ldq < K || ldq % 16 != 0)
+        return fail(BITLINEAR_ERR_SHAPE, "quant_act_add_rmsnorm: ldq=%lld must be >= K and a multiple of 16", (long long)ldq);
+    if (!(eps >= 0.0f) || !(eps <= 3.0e38f))
+        return fail(BITLINEAR_ERR_ARG, "quant_act_add_rmsnorm: eps must be finite and >= 0");
+    if (!a16(X) || !a16(R) || !a16(Xsum_out) || !a16(Q_out) || !a4(absmax_out) || (rowsum_out && !a4(rowsum_out)) ||
+        (norm_weight && !a4(norm_weight)))
+        return fail(BITLINEAR_ERR_ALIGN, "quant_act_add_rmsnorm: X/R/Xsum_out/Q_out need 16-byte, absmax/rowsum/norm_weight 4-byte alignment");
+    // Xsum_out may be X or R itself; any other overlap with X, R or Q is not allowed
+    auto overlaps = [](const void *a, int64_t na, const void *b, int64_t nb) {
+        const char *pa = static_cast<const char *>(a), *pb = static_cast<const char *>(b);
+        return pa < pb + nb && pb < pa + na;
+    };
+    const int64_t fb = 4 * M * K;
+    if ((Xsum_out != X && overlaps(Xsum_out, fb, X, fb)) || (Xsum_out != R && overlaps(Xsum_out, fb, R, fb)) ||
+        overlaps(Xsum_out, fb, Q_out, M * ldq))
+        return fail(BITLINEAR_ERR_ARG, "quant_act_add_rmsnorm: Xsum_out must be X, R or a separate buffer");
+    if (hipError_t e = bl::launch_quant_act_add_rmsnorm(X, R, M, K, norm_weight, eps, Xsum_out, Q_out, ldq, absmax_out,
+                                                        rowsum_out, static_cast<hipStream_t>(stream)))
+        return hip_fail(e, "quant_act_add_rmsnorm");
+    return BITLINEAR_OK;
+}
+
 int bitlinear_quant_act_relu2_gate(const float *G, const float *U, int64_t M, int64_t N, int8_t *Q_out,
                                    int64_t ldq, float *absmax_out, int32_t *rowsum_out, void *stream)
 {

@@ -141,6 +141,9 @@ hipError_t launch_quant_act(const float *X, int64_t M, int64_t K, int8_t *Q, int
 hipError_t launch_quant_act_rmsnorm(const float *X, int64_t M, int64_t K, const float *g, float eps,
                                     int8_t *Q, int64_t ldq, float *absmax, int32_t *rowsum,
                                     hipStream_t s);
+hipError_t launch_quant_act_add_rmsnorm(const float *X, const float *R, int64_t M, int64_t K, const float *g,
+                                        float eps, float *Xsum, int8_t *Q, int64_t ldq, float *absmax,
+                                        int32_t *rowsum, hipStream_t s);
 hipError_t launch_quant_act_relu2_gate(const float *G, const float *U, int64_t M, int64_t N, int8_t *Q,
                                        int64_t ldq, float *absmax, int32_t *rowsum, hipStream_t s);
 hipError_t launch_quant_act_group(const Problem *probs, const uint32_t *tok_map, int n_tokens,

@@ -160,13 +160,20 @@ __device__ __forceinline__ void bt5_body(const Problem &p, int local)
     }
     if (ks == 1) return;
     if (!arrive_last(p, rest)) return;
+    int64_t off[8];
+    bool ok[8];
 #pragma unroll
     for (int e = 0; e < 16; e += 2) {
         const int m = m0 + ((8 * (e >> 2) + 4 * c + (e & 3)) >> 1);
-        if (!tv || n >= p.N || m >= M) continue;
-        int32_t sum = 0;
-        for (int j = 0; j < ks; ++j) sum += get_partial(p.acc_ws + ((int64_t)j * M + m) * ldp + n);
-        finish_output(p, gamma, m, n, sum);
+        ok[e >> 1] = tv && n < p.N && m < M;
+        off[e >> 1] = (int64_t)m * ldp + n;
+    }
+    int32_t sums[8];
+    sum_partials<8>(p.acc_ws, off, ok, (int64_t)M * ldp, ks, sums);
+#pragma unroll
+    for (int e = 0; e < 16; e += 2) {
+        const int m = m0 + ((8 * (e >> 2) + 4 * c + (e & 3)) >> 1);
+        if (ok[e >> 1]) finish_output(p, gamma, m, n, sums[e >> 1]);
     }
 }
 

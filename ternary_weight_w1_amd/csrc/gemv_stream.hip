@@ -278,11 +278,11 @@ __device__ void stream_dot4(const Problem &p, int local)
     const int64_t ldp = (int64_t)p.NT * 64;  // partial row stride
     if (t < 64) put_partial(p.acc_ws + ((int64_t)split * p.M * ldp + n), total);
     if (!arrive_last(p, tile)) return;
-    if (t < 64 && n < p.N) {
-        int sum = 0;
-        for (int j = 0; j < p.ks; ++j) sum += get_partial(p.acc_ws + ((int64_t)j * p.M * ldp + n));
-        finish(n, sum, gamma);
-    }
+    const int64_t off[1] = {n};
+    const bool ok[1] = {t < 64 && n < p.N};
+    int32_t sum[1];
+    sum_partials<1>(p.acc_ws, off, ok, (int64_t)p.M * ldp, p.ks, sum);
+    if (ok[0]) finish(n, sum[0], gamma);
 }
 
 // 2..32 tokens: the same packed stream feeds v_mfma_i32_32x32x32_i8 with the
@@ -409,13 +409,24 @@ __device__ void stream_mfma(const Problem &p, int local)
     // split K: the last workgroup of the tile group sums its tiles
     constexpr int kRows = 256 * TPW;
     if (!arrive_last(p, 4 * TPW * grp)) return;
-    for (int idx = threadIdx.x; idx < p.M * kRows; idx += kThreads) {
-        const int m = idx / kRows;
-        const int n = kRows * grp + idx % kRows;
-        if (n >= p.N) continue;
-        int sum = 0;
-        for (int j = 0; j < p.ks; ++j) sum += get_partial(p.acc_ws + (((int64_t)j * p.M + m) * ldp + n));
-        finish_output(p, gamma, m, n, sum);
+    const int total = p.M * kRows;
+    for (int base = threadIdx.x; base < total; base += 4 * kThreads) {
+        int64_t off[4];
+        bool ok[4];
+        int mm[4], nn[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int idx = base + r * kThreads;
+            mm[r] = idx / kRows;
+            nn[r] = kRows * grp + idx % kRows;
+            ok[r] = idx < total && nn[r] < p.N;
+            off[r] = (int64_t)mm[r] * ldp + nn[r];
+        }
+        int32_t sums[4];
+        sum_partials<4>(p.acc_ws, off, ok, (int64_t)p.M * ldp, p.ks, sums);
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            if (ok[r]) finish_output_with(p, gamma, mm[r], nn[r], sums[r], s_rowsum[mm[r]], s_absmax[mm[r]]);
     }
 }
 

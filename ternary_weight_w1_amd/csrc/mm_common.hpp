@@ -63,7 +63,38 @@ __device__ inline void put_partial(int32_t *p, int32_t v)
 }
 __device__ inline int32_t get_partial(const int32_t *p)
 {
-    return __hip_atomic_load(const_cast<int32_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return __hip_atomic_load(const_cast<BL_GLOBAL int32_t *>(gload_ptr<int32_t>(p)), __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Split-K sums of R outputs at once: out[r] = sum_j part[off[r] + j * stride]
+// over the ks splits, for the outputs with ok[r].  The loads of four splits
+// of all R outputs are issued before any is added, so a thread waits once
+// per four splits instead of once per partial (each load crosses to the
+// device's coherence point).
+template <int R>
+__device__ inline void sum_partials(const int32_t *part, const int64_t (&off)[R], const bool (&ok)[R],
+                                    int64_t stride, int ks, int32_t (&out)[R])
+{
+#pragma unroll
+    for (int r = 0; r < R; ++r) out[r] = 0;
+    int j = 0;
+    for (; j + 4 <= ks; j += 4) {
+        int32_t v[R][4];
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[r][i] = ok[r] ? get_partial(part + off[r] + (j + i) * stride) : 0;
+#pragma unroll
+        for (int r = 0; r < R; ++r) out[r] += (v[r][0] + v[r][1]) + (v[r][2] + v[r][3]);
+    }
+    for (; j < ks; ++j) {
+        int32_t v[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) v[r] = ok[r] ? get_partial(part + off[r] + j * stride) : 0;
+#pragma unroll
+        for (int r = 0; r < R; ++r) out[r] += v[r];
+    }
 }
 
 // Split-K arrival: every workgroup of a tile publishes its partial sums

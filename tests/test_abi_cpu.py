@@ -29,7 +29,7 @@ def _declared():
 
 def test_every_declared_symbol_is_exported():
     names = _declared()
-    assert len(names) == 26, names
+    assert len(names) == 27, names
     out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r"\bT (bitlinear_\w+)", out))
@@ -108,6 +108,14 @@ def test_pack_quant_matmul_forward_validation():
     assert q(FAKE, 2, 100, None, -1.0, FAKE, 112, FAKE, FAKE, None) == -6
     assert q(FAKE, 2, 100, None, float("nan"), FAKE, 112, FAKE, FAKE, None) == -6
     assert q(FAKE, 2, 100, FAKE + 2, 1e-5, FAKE, 112, FAKE, FAKE, None) == -3
+    # residual add + RMSNorm + cast: the sum may be written over X or R only
+    ad = L.bitlinear_quant_act_add_rmsnorm
+    assert ad(FAKE, None, 2, 100, None, 1e-5, FAKE, FAKE, 112, FAKE, FAKE, None) == -1
+    assert ad(FAKE, FAKE + 4096, 2, 100, None, 1e-5, FAKE + 8192, FAKE + 12288, 104, FAKE, FAKE, None) == -2
+    assert ad(FAKE, FAKE + 4096, 2, 100, None, -1.0, FAKE + 8192, FAKE + 12288, 112, FAKE, FAKE, None) == -6
+    assert ad(FAKE, FAKE + 4096, 2, 100, None, 1e-5, FAKE + 8200, FAKE + 12288, 112, FAKE, FAKE, None) == -3
+    assert ad(FAKE, FAKE + 4096, 2, 100, None, 1e-5, FAKE + 16, FAKE + 12288, 112, FAKE, FAKE, None) == -6
+    assert ad(FAKE, FAKE + 4096, 2, 100, None, 1e-5, FAKE + 8192, FAKE + 8192, 112, FAKE, FAKE, None) == -6
     # gated squared-ReLU + cast
     r = L.bitlinear_quant_act_relu2_gate
     assert r(FAKE, None, 2, 100, FAKE, 112, FAKE, FAKE, None) == -1

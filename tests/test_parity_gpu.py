@@ -147,6 +147,121 @@ def test_rmsnorm_then_contraction(B):
     check_outputs(host(Y), host(acc), ref, 0.02, a, "rmsnorm -> matmul")
 
 
+@pytest.mark.parametrize("M,K", [(1, 3200), (3, 37), (4, 100), (7, 8640), (1, 28672), (2049, 2560),
+                                 (2050, 10004), (5, 64)])
+def test_quant_act_add_rmsnorm_parity(B, M, K):
+    # residual add + sub-layer norm + cast in one pass (register, re-read and
+    # scalar paths; 4-wave and 1-wave workgroups): the sum and the codes,
+    # scales and row sums bit-exact, with the sum written to a new buffer,
+    # over X and over R
+    say("quant_act_add_rmsnorm", M, K)
+    rng = np.random.default_rng(M * 7 + K)
+    X = (rng.standard_normal((M, K)) * 2).astype(np.float32)
+    R = rng.standard_normal((M, K)).astype(np.float32)
+    g = (rng.random(K) + 0.5).astype(np.float32)
+    Q, a, rs, S, _, _ = O.add_rmsnorm_quant_act(X, R, g, 1e-5)
+    for where in ("new", "x", "r"):
+        Xd, Rd = dev(X), dev(R)
+        out = None if where == "new" else (Xd if where == "x" else Rd)
+        Qg, ag, rsg, Sg = B.quant_act_add_rmsnorm(Xd, Rd, dev(g), 1e-5, out=out)
+        Qg = host(Qg)
+        np.testing.assert_array_equal(host(Sg), S, err_msg=where)
+        np.testing.assert_array_equal(Qg[:, :K], Q, err_msg=where)
+        assert not Qg[:, K:].any()
+        np.testing.assert_array_equal(host(ag), a, err_msg=where)
+        np.testing.assert_array_equal(host(rsg), rs, err_msg=where)
+
+
+def _stack_weights(dim, ffn, layers, seed):
+    shapes = [("q", dim, dim), ("k", dim, dim), ("v", dim, dim), ("o", dim, dim),
+              ("gate", dim, ffn), ("up", dim, ffn), ("down", ffn, dim)]
+    rng = np.random.default_rng(seed)
+    out = []
+    for layer in range(layers):
+        mats = {}
+        for j, (name, K, N) in enumerate(shapes):
+            W = synth.weights_np(N, K, 0.02, seed=seed + 10 * layer + j)
+            T, gam = O.quantize_weights(W)
+            mats[name] = (T, np.float32(gam), K, N)
+        mats["g_attn"] = (rng.random(dim) + 0.5).astype(np.float32)
+        mats["g_ffn"] = (rng.random(dim) + 0.5).astype(np.float32)
+        out.append(mats)
+    return out
+
+
+@pytest.mark.parametrize("M", [1, 5])
+def test_layer_stack_chain(B, M):
+    # Two pre-norm BitLinear blocks chained through the residual stream, then
+    # the final norm: residual add + norm + cast, q/k/v contractions, the
+    # attention of the first decode position (one key: the output is v),
+    # the o contraction, residual add + norm + cast, gate/up, the gated
+    # squared-ReLU cast, down.  Every intermediate bit-exact against the
+    # oracle's chain.
+    say("layer stack chain", M)
+    dim, ffn = 320, 864
+    layers = _stack_weights(dim, ffn, 2, 4242)
+    x0 = synth.activations_np(M, dim, seed=77)
+    g_fin = np.linspace(0.5, 1.5, dim).astype(np.float32)
+
+    def o_lin(Q, a, mats, name):
+        T, gam, K, N = mats[name]
+        return O.epilogue(O.matmul(Q, T), gam, a)
+
+    # oracle chain
+    x, d = x0.copy(), None
+    o_trace = []
+    for mats in layers:
+        if d is None:
+            Q, a, rs, _, _ = O.rmsnorm_quant_act(x, mats["g_attn"], 1e-5)
+        else:
+            Q, a, rs, x, _, _ = O.add_rmsnorm_quant_act(x, d, mats["g_attn"], 1e-5)
+        q, k, v = (o_lin(Q, a, mats, n) for n in ("q", "k", "v"))
+        Qo, ao, _ = O.quant_act(v)
+        o = o_lin(Qo, ao, mats, "o")
+        Qf, af, _, x, _, _ = O.add_rmsnorm_quant_act(x, o, mats["g_ffn"], 1e-5)
+        gate, up = o_lin(Qf, af, mats, "gate"), o_lin(Qf, af, mats, "up")
+        Qd, ad, _, _ = O.relu2_gate_quant_act(gate, up)
+        d = o_lin(Qd, ad, mats, "down")
+        o_trace.append((q, k, v, o, gate, up, d, x.copy()))
+    Qfin, afin, _, xfin, _, _ = O.add_rmsnorm_quant_act(x, d, g_fin, 1e-5)
+
+    # library chain (device weights packed by the library from the oracle codes)
+    dev_mats = []
+    for mats in layers:
+        dm = {}
+        for name in ("q", "k", "v", "o", "gate", "up", "down"):
+            T, gam, K, N = mats[name]
+            Pg = B.pack(dev(T))
+            dm[name] = (Pg, gamma_dev(float(gam)), K, N)
+        dm["g_attn"], dm["g_ffn"] = dev(mats["g_attn"]), dev(mats["g_ffn"])
+        dev_mats.append(dm)
+
+    def lin(Q, a, rs, dm, name):
+        P, gam, K, N = dm[name]
+        return B.matmul(Q, a, rs, P, gam, N, K)
+
+    xg, dg = dev(x0), None
+    for li, dm in enumerate(dev_mats):
+        if dg is None:
+            Q, a, rs = B.quant_act_rmsnorm(xg, dm["g_attn"], 1e-5)
+        else:
+            Q, a, rs, xg = B.quant_act_add_rmsnorm(xg, dg, dm["g_attn"], 1e-5, out=xg)
+        q, k, v = (lin(Q, a, rs, dm, n) for n in ("q", "k", "v"))
+        Qo, ao, rso = B.quant_act(v)
+        o = lin(Qo, ao, rso, dm, "o")
+        Qf, af, rsf, xg = B.quant_act_add_rmsnorm(xg, o, dm["g_ffn"], 1e-5, out=xg)
+        gate, up = lin(Qf, af, rsf, dm, "gate"), lin(Qf, af, rsf, dm, "up")
+        Qd, ad, rsd = B.quant_act_relu2_gate(gate, up)
+        dg = lin(Qd, ad, rsd, dm, "down")
+        for name, got, want in zip(("q", "k", "v", "o", "gate", "up", "down", "x"),
+                                   (q, k, v, o, gate, up, dg, xg), o_trace[li]):
+            np.testing.assert_array_equal(host(got), want, err_msg=f"layer {li} {name}")
+    Qg, ag, _, xg = B.quant_act_add_rmsnorm(xg, dg, dev(g_fin), 1e-5, out=xg)
+    np.testing.assert_array_equal(host(xg), xfin)
+    np.testing.assert_array_equal(host(Qg)[:, :dim], Qfin)
+    np.testing.assert_array_equal(host(ag), afin)
+
+
 @pytest.mark.parametrize("M,N", [(1, 6912), (3, 37), (7, 8640), (1, 28672), (2049, 6912), (2050, 10004),
                                  (2048, 37)])
 def test_quant_act_relu2_gate_parity(B, M, N):
