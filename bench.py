@@ -18,7 +18,8 @@ step captured once in a HIP graph and replayed.  curves = latency of a full
 sweep over the 3B-class stack at M in {1, 8, 64, 256} (and, on request, the
 70B-class stack at M in {1, 16, 176}); for 3B also the same stack chained as
 pre-norm blocks (residual adds, norms, the gated squared-ReLU, a single-key
-attention) at M in {1, 8, 64}, eager and as a replayed HIP graph.  bt5 = the same 2B stack packed
+attention; q|k|v and gate|up each one launch) at M in {1, 8, 64}, eager and
+as a replayed HIP graph.  bt5 = the same 2B stack packed
 five codes per byte (BT5-T32, 1.6 bits per weight) at M in {1, 8, 16},
 next to the 2-bit path at the same M.  cpu_baseline = the CPU oracle
 (single thread) on a bounded sample of the same workload.
@@ -199,12 +200,13 @@ def bt5_section(B, torch, mats, dev, Ms, steps, warmup, model):
 def stack_curve(B, torch, mats, dev, Ms, steps, warmup):
     """The stack chained as pre-norm blocks, one decode (or prefill) step of
     M tokens through every layer, each step a library call on one stream:
-    residual add + RMSNorm + int8 cast, q/k/v contractions, the attention of
-    the first decode position (a single key, so its output is v), the cast
-    of v, the o contraction, residual add + RMSNorm + cast, gate/up, the
-    gated squared-ReLU cast, down; then the final residual add + norm.
-    Timed eagerly and as one HIP graph replayed (the step has hundreds of
-    short launches).  Buffers and workspace are allocated once."""
+    residual add + RMSNorm + int8 cast, q|k|v in one launch (one input), the
+    attention of the first decode position (a single key, so its output is
+    v), the cast of v, o, residual add + RMSNorm + cast, gate|up in one
+    launch, the gated squared-ReLU cast, down; then the final residual add +
+    norm: 8 launches per layer.  Timed eagerly and as one HIP graph
+    replayed.  Buffers and workspaces are allocated once (workspaces
+    zero-filled once, as the multi-matrix call requires)."""
     import ctypes
     L = B.lib()
     layers = {}
@@ -212,12 +214,14 @@ def stack_curve(B, torch, mats, dev, Ms, steps, warmup):
         layers.setdefault(m["layer"], {})[m["name"]] = m
     dim = layers[0]["q"]["K"]
     ffn = layers[0]["gate"]["N"]
-    out = {"layers": len(layers), "dim": dim, "ffn": ffn, "points": []}
+    out = {"layers": len(layers), "dim": dim, "ffn": ffn, "launches_per_step": 8 * len(layers) + 1,
+           "points": []}
     gen = torch.Generator(device=dev)
     gen.manual_seed(5)
     gains = [(torch.rand(dim, generator=gen, device=dev) + 0.5, torch.rand(dim, generator=gen, device=dev) + 0.5)
              for _ in layers]
     g_fin = torch.rand(dim, generator=gen, device=dev) + 0.5
+    P = lambda t: ctypes.c_void_p(t.data_ptr())
     for M in Ms:
         x0 = synth.activations_torch(M, dim, 21, dev)
         f32 = lambda n: torch.empty((M, n), dtype=torch.float32, device=dev)
@@ -226,37 +230,48 @@ def stack_curve(B, torch, mats, dev, Ms, steps, warmup):
         Qd_, Qf_ = (torch.empty((M, ld), dtype=torch.int8, device=dev) for ld in (ldd, ldf))
         a = torch.empty(M, dtype=torch.float32, device=dev)
         rs = torch.empty(M, dtype=torch.int32, device=dev)
-        wsb = max(B.workspace_bytes(B.WS_MATMUL, M, N, K) for N, K in ((dim, dim), (ffn, dim), (dim, ffn)))
-        ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
-        P = lambda t: ctypes.c_void_p(t.data_ptr())
+
+        def warr(lay, names, outs):
+            arr = (B.Weight * len(names))()
+            for i, (nm, Y) in enumerate(zip(names, outs)):
+                arr[i] = B.Weight(lay[nm]["P"].data_ptr(), lay[nm]["gamma"].data_ptr(), Y.data_ptr(), None,
+                                  lay[nm]["N"], 0, 0)
+            return arr
+        sites = {}
+        for i, lay in layers.items():
+            sites[i] = dict(qkv=warr(lay, ("q", "k", "v"), (q, k, v)), o=warr(lay, ("o",), (o,)),
+                            gu=warr(lay, ("gate", "up"), (gate, up)), down=warr(lay, ("down",), (d,)))
+        wss = {}
+        for key, K in (("qkv", dim), ("o", dim), ("gu", dim), ("down", ffn)):
+            n = len(sites[0][key])
+            wsb = L.bitlinear_multi_workspace_bytes(sites[0][key], n, M, K)
+            wss[key] = torch.zeros(max(wsb, 16), dtype=torch.uint8, device=dev)
 
         def check(st):
             if st != 0:
                 raise RuntimeError(L.bitlinear_last_error().decode())
 
-        def lin(Q, ld, K, w, Y):
-            check(L.bitlinear_matmul(P(Q), ld, P(a), P(rs), M, K, P(w["P"]), P(w["gamma"]), w["N"], P(Y), None,
-                                     P(ws), ws.numel(), s))
+        def multi(Q, ld, K, arr, key):
+            check(L.bitlinear_matmul_multi(P(Q), ld, P(a), P(rs), M, K, arr, len(arr), P(wss[key]),
+                                           wss[key].numel(), s))
 
         def step():
             for i, lay in sorted(layers.items()):
                 ga, gf = gains[i]
+                site = sites[i]
                 if i == 0:
                     check(L.bitlinear_quant_act_rmsnorm(P(x0), M, dim, P(ga), 1e-5, P(Qd_), ldd, P(a), P(rs), s))
                 else:
                     check(L.bitlinear_quant_act_add_rmsnorm(P(x), P(d), M, dim, P(ga), 1e-5, P(x), P(Qd_), ldd,
                                                             P(a), P(rs), s))
-                lin(Qd_, ldd, dim, lay["q"], q)
-                lin(Qd_, ldd, dim, lay["k"], k)
-                lin(Qd_, ldd, dim, lay["v"], v)
+                multi(Qd_, ldd, dim, site["qkv"], "qkv")
                 check(L.bitlinear_quant_act(P(v), M, dim, P(Qd_), ldd, P(a), P(rs), s))
-                lin(Qd_, ldd, dim, lay["o"], o)
+                multi(Qd_, ldd, dim, site["o"], "o")
                 check(L.bitlinear_quant_act_add_rmsnorm(P(x0 if i == 0 else x), P(o), M, dim, P(gf), 1e-5, P(x),
                                                         P(Qd_), ldd, P(a), P(rs), s))
-                lin(Qd_, ldd, dim, lay["gate"], gate)
-                lin(Qd_, ldd, dim, lay["up"], up)
+                multi(Qd_, ldd, dim, site["gu"], "gu")
                 check(L.bitlinear_quant_act_relu2_gate(P(gate), P(up), M, ffn, P(Qf_), ldf, P(a), P(rs), s))
-                lin(Qf_, ldf, ffn, lay["down"], d)
+                multi(Qf_, ldf, ffn, site["down"], "down")
             check(L.bitlinear_quant_act_add_rmsnorm(P(x), P(d), M, dim, P(g_fin), 1e-5, P(x), P(Qd_), ldd,
                                                     P(a), P(rs), s))
 

@@ -299,6 +299,44 @@ int bitlinear_forward(const float *X, int64_t M, int64_t K, const uint8_t *P,
                       void *ws, size_t ws_bytes, void *stream);
 
 /* ---------------------------------------------------------------------- */
+/* Several weight matrices on one int8 input (q|k|v, gate|up): one launch.  */
+/* ---------------------------------------------------------------------- */
+
+typedef struct bitlinear_weight {
+    const uint8_t *P;   /* packed weights of an N x K matrix (device)        */
+    const float *gamma; /* one fp32 weight scale (device)                    */
+    float *Y;           /* M x N fp32 output (device)                        */
+    int32_t *acc;       /* M x N int32 accumulators (device, nullable)       */
+    int64_t N;
+    int32_t format;     /* bitlinear_format of P; the same for all weights   */
+    int32_t reserved;   /* must be 0                                         */
+} bitlinear_weight;
+
+/* Workspace bytes of bitlinear_matmul_multi for these weights (only N,
+ * format and reserved are read; SIZE_MAX on invalid input; 0 when no matrix
+ * splits K). */
+size_t bitlinear_multi_workspace_bytes(const bitlinear_weight *w, int count, int64_t M, int64_t K);
+
+/*
+ * bitlinear_matmul (or bitlinear_matmul5, by format) for 1..4 weight
+ * matrices that read the same activations, in one launch; each result is
+ * bit-identical to the single call's.
+ *   Q, ldq, absmax, rowsum, M, K  as bitlinear_matmul (bitlinear_matmul5
+ *                 for BITLINEAR_FORMAT_BT5: ldq >= bitlinear_q_stride5(K)).
+ *   w, count      the weight matrices (1 <= count <= 4).
+ *   ws            bitlinear_multi_workspace_bytes(w, count, M, K) bytes.  Its
+ *                 start holds split-K arrival counters: ZERO-FILL the
+ *                 workspace once before its first use.  Every completed call
+ *                 leaves the counters zero again, so later calls with the
+ *                 same weights and sizes reuse it without a clearing launch;
+ *                 calls with other sizes need their own zeroed workspace.
+ *                 Calls that share a workspace must not run concurrently.
+ */
+int bitlinear_matmul_multi(const int8_t *Q, int64_t ldq, const float *absmax, const int32_t *rowsum,
+                           int64_t M, int64_t K, const bitlinear_weight *w, int count, void *ws,
+                           size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------------- */
 /* Grouped forward: many independent BitLinear layers in one launch per    */
 /* stage (e.g. every weight matrix of a model, or q|k|v sharing an input). */
 /* ---------------------------------------------------------------------- */

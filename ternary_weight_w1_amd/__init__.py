@@ -36,6 +36,12 @@ _sz = ctypes.c_size_t
 _int = ctypes.c_int
 
 
+class Weight(ctypes.Structure):
+    """ctypes mirror of struct bitlinear_weight."""
+    _fields_ = [("P", _vp), ("gamma", _vp), ("Y", _vp), ("acc", _vp), ("N", _i64),
+                ("format", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
 class Problem(ctypes.Structure):
     """ctypes mirror of struct bitlinear_problem."""
     _fields_ = [("X", _vp), ("P", _vp), ("gamma", _vp), ("Y", _vp), ("acc", _vp),
@@ -80,6 +86,9 @@ def lib():
             "bitlinear_matmul": (_int, [_vp, _i64, _vp, _vp, _i64, _i64, _vp, _vp, _i64, _vp, _vp,
                                         _vp, _sz, _vp]),
             "bitlinear_forward": (_int, [_vp, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _vp, _sz, _vp]),
+            "bitlinear_multi_workspace_bytes": (_sz, [ctypes.POINTER(Weight), _int, _i64, _i64]),
+            "bitlinear_matmul_multi": (_int, [_vp, _i64, _vp, _vp, _i64, _i64, ctypes.POINTER(Weight), _int,
+                                              _vp, _sz, _vp]),
             "bitlinear_group_table_bytes": (_sz, [ctypes.POINTER(Problem), _int]),
             "bitlinear_group_workspace_bytes": (_sz, [ctypes.POINTER(Problem), _int]),
             "bitlinear_group_plan": (_int, [ctypes.POINTER(Problem), _int, _vp, _sz, _vp, _sz]),
@@ -326,6 +335,48 @@ def forward5(X, P, gamma, N: int, with_acc: bool = False, ws=None, out=None, str
                                     _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)),
            "forward5")
     return (Y, acc) if with_acc else Y
+
+
+class MultiMatmul:
+    """Several weight matrices that read the same int8 activations (q|k|v,
+    gate|up), contracted in one launch.  weights: sequence of dicts with P,
+    gamma (CUDA tensors), N and optionally format.  The object owns a
+    zero-filled workspace for its sizes (reused call after call)."""
+
+    def __init__(self, weights, M: int, K: int, device=None):
+        L = lib()
+        n = len(weights)
+        self.arr = (Weight * n)()
+        self.M, self.K, self.count = M, K, n
+        self.Ns = [int(w["N"]) for w in weights]
+        self.fmt = int(weights[0].get("format", FORMAT_BL2))
+        self._keep = []
+        device = device or weights[0]["P"].device
+        for i, w in enumerate(weights):
+            _dev_tensor(w["P"], torch.uint8, "P")
+            _dev_tensor(w["gamma"], torch.float32, "gamma")
+            self.arr[i] = Weight(w["P"].data_ptr(), w["gamma"].data_ptr(), None, None, self.Ns[i],
+                                 int(w.get("format", FORMAT_BL2)), 0)
+            self._keep.append(w)
+        wsb = L.bitlinear_multi_workspace_bytes(self.arr, n, M, K)
+        if wsb == ctypes.c_size_t(-1).value:
+            _check(-2, "multi_workspace_bytes")
+        self.ws = torch.zeros(max(wsb, 16), dtype=torch.uint8, device=device)
+
+    def __call__(self, Q, absmax, rowsum, outs=None, accs=None, stream=None):
+        """Y_i (M x N_i fp32) for every weight; outs/accs: optional tensors."""
+        _dev_tensor(Q, torch.int8, "Q")
+        M, ldq = Q.shape
+        if M != self.M:
+            raise ValueError("Q has the wrong number of rows")
+        outs = outs or [torch.empty((M, N), dtype=torch.float32, device=Q.device) for N in self.Ns]
+        for i in range(self.count):
+            self.arr[i].Y = outs[i].data_ptr()
+            self.arr[i].acc = None if accs is None else accs[i].data_ptr()
+        _check(lib().bitlinear_matmul_multi(_ptr(Q), ldq, _ptr(absmax), _ptr(rowsum), M, self.K, self.arr,
+                                            self.count, _ptr(self.ws), self.ws.numel(), _stream(stream)),
+               "matmul_multi")
+        return outs
 
 
 class GroupPlan:

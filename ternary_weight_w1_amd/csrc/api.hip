@@ -629,6 +629,138 @@ int bitlinear_forward5(const float *X, int64_t M, int64_t K, const uint8_t *P5,
 }  // extern "C"
 
 // --------------------------------------------------------------------------
+// Several weight matrices on one int8 input, one launch.
+// --------------------------------------------------------------------------
+namespace {
+
+struct MultiPlan {
+    bl::ProblemSet ps;
+    int kind = 0, variant = 0, lds = 0;
+    int64_t tick_bytes = 0, total_bytes = 0;  // workspace: all tickets first, then all partials
+    int64_t tick_off[bl::kMultiMax] = {}, part_off[bl::kMultiMax] = {};
+};
+
+// check_ptrs = false: sizing only (buffer pointers may still be unset)
+int multi_plan(const int8_t *Q, int64_t ldq, int64_t M, int64_t K, const bitlinear_weight *w, int count,
+               MultiPlan &mp, bool check_ptrs = true)
+{
+    if (!w) return fail(BITLINEAR_ERR_NULL, "matmul_multi: weight array is NULL");
+    if (count < 1 || count > bl::kMultiMax) return fail(BITLINEAR_ERR_SHAPE, "matmul_multi: count=%d not in [1, 4]", count);
+    const int fmt = w[0].format;
+    for (int i = 0; i < count; ++i) {
+        if (check_ptrs && (!w[i].P || !w[i].gamma || !w[i].Y))
+            return fail(BITLINEAR_ERR_NULL, "matmul_multi: weight %d lacks P, gamma or Y", i);
+        if (w[i].format != fmt || (fmt != BITLINEAR_FORMAT_BL2 && fmt != BITLINEAR_FORMAT_BT5) || w[i].reserved != 0)
+            return fail(BITLINEAR_ERR_ARG, "matmul_multi: weights need one known format and reserved == 0");
+        if (int st = check_mnk(M, w[i].N, K)) return st;
+        if (check_ptrs && (!a16(w[i].P) || !a16(w[i].Y) || (w[i].acc && !a16(w[i].acc)) || !a4(w[i].gamma)))
+            return fail(BITLINEAR_ERR_ALIGN, "matmul_multi: weight %d buffers misaligned", i);
+    }
+    const int64_t kq = fmt ? up(K, bl::kBt5UnitCodes) : up(K, 64);
+    if (ldq < kq || ldq % 16 != 0 || ldq > (int64_t(1) << 26))
+        return fail(BITLINEAR_ERR_SHAPE, "matmul_multi: ldq=%lld must be in [%lld, 2^26] and a multiple of 16",
+                    (long long)ldq, (long long)kq);
+    (void)Q;
+    memset(&mp.ps, 0, sizeof mp.ps);
+    // decomposition over the whole launch: K is split only while all the
+    // problems together are short of workgroups
+    const bool g4 = !fmt && M <= kStreamMaxM && M > knobs().dot4_max_m;
+    int64_t base = 0, max_upsplit = 0;
+    for (int i = 0; i < count; ++i) {
+        const int64_t nt = (w[i].N + 63) / 64;
+        base += fmt ? bt5_items(M, w[i].N) : (g4 ? (nt + kGroupTiles - 1) / kGroupTiles : nt);
+    }
+    if (base < 1) base = 1;
+    int64_t items = 0, tick = 0, part = 0;
+    for (int i = 0; i < count; ++i) {
+        Problem &p = mp.ps.p[i];
+        p = make_problem(M, w[i].N, K);
+        if (fmt)
+            decompose5(p, base);
+        else
+            decompose(p, base, false, g4);
+        mp.ps.begin[i] = (int32_t)items;
+        items += items_of(p);
+        max_upsplit = max_upsplit > p.upsplit ? max_upsplit : p.upsplit;
+        if (p.kind != 1 && p.ks > 1) {
+            const int64_t rows = (int64_t)p.NT * (p.kind == 2 ? bl::kBt5TileRows : 64);
+            mp.tick_off[i] = tick;
+            tick += 4 * bl::ticket_count(p);
+            mp.part_off[i] = part;
+            part = up(part + 4 * (int64_t)p.ks * p.M * rows, 256);
+        } else {
+            mp.tick_off[i] = mp.part_off[i] = -1;
+        }
+    }
+    if (items >= (int64_t(1) << 31)) return fail(BITLINEAR_ERR_SHAPE, "matmul_multi: grid too large");
+    mp.ps.begin[count] = (int32_t)items;
+    mp.ps.count = count;
+    mp.kind = mp.ps.p[0].kind;
+    if (mp.kind == 0) {
+        mp.variant = stream_variant_for(M, max_upsplit);
+        mp.lds = mp.variant >= 2 ? (int)((mp.variant == 5 ? 1024 : 64) * max_upsplit) : 0;
+    } else if (mp.kind == 1) {
+        mp.variant = tile_variant(false);
+    }
+    mp.tick_bytes = up(tick, 256);
+    mp.total_bytes = mp.tick_bytes + part;
+    return BITLINEAR_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t bitlinear_multi_workspace_bytes(const bitlinear_weight *w, int count, int64_t M, int64_t K)
+{
+    MultiPlan mp;
+    const int64_t ldq = (w && count >= 1 && w[0].format == BITLINEAR_FORMAT_BT5) ? up(K, bl::kBt5UnitCodes) : up(K, 64);
+    if (multi_plan(nullptr, ldq, M, K, w, count, mp, false) != BITLINEAR_OK) return SIZE_MAX;
+    return (size_t)mp.total_bytes;
+}
+
+int bitlinear_matmul_multi(const int8_t *Q, int64_t ldq, const float *absmax, const int32_t *rowsum,
+                           int64_t M, int64_t K, const bitlinear_weight *w, int count, void *ws,
+                           size_t ws_bytes, void *stream)
+{
+    if (!Q || !absmax || !rowsum) return fail(BITLINEAR_ERR_NULL, "matmul_multi: Q, absmax and rowsum are required");
+    if (!a16(Q) || !a4(absmax) || !a4(rowsum)) return fail(BITLINEAR_ERR_ALIGN, "matmul_multi: Q needs 16-byte, scales 4-byte alignment");
+    MultiPlan mp;
+    if (int st = multi_plan(Q, ldq, M, K, w, count, mp)) return st;
+    if (mp.total_bytes > 0 && (!ws || ws_bytes < (size_t)mp.total_bytes || !a16(ws)))
+        return fail(BITLINEAR_ERR_WORKSPACE, "matmul_multi: needs %lld workspace bytes (16-byte aligned)",
+                    (long long)mp.total_bytes);
+    char *base = static_cast<char *>(ws);
+    for (int i = 0; i < count; ++i) {
+        Problem &p = mp.ps.p[i];
+        p.Q = const_cast<int8_t *>(Q);
+        p.ldq = ldq;
+        p.absmax = const_cast<float *>(absmax);
+        p.rowsum = const_cast<int32_t *>(rowsum);
+        p.P = w[i].P;
+        p.gamma = w[i].gamma;
+        p.Y = w[i].Y;
+        p.acc_out = w[i].acc;
+        if (mp.tick_off[i] >= 0) {
+            p.tickets = reinterpret_cast<uint32_t *>(base + mp.tick_off[i]);
+            p.acc_ws = reinterpret_cast<int32_t *>(base + mp.tick_bytes + mp.part_off[i]);
+        }
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    if (mp.kind == 0)
+        e = bl::launch_stream_multi(mp.ps, mp.variant, mp.lds, s);
+    else if (mp.kind == 1)
+        e = bl::launch_tile_multi(mp.ps, mp.variant, s);
+    else
+        e = bl::launch_bt5_multi(mp.ps, (int)(M < bl::kBt5Tokens ? M : bl::kBt5Tokens), s);
+    if (e) return hip_fail(e, "matmul_multi");
+    return BITLINEAR_OK;
+}
+
+}  // extern "C"
+
+// --------------------------------------------------------------------------
 // Grouped forward: plan table construction.
 // --------------------------------------------------------------------------
 namespace {

@@ -87,6 +87,25 @@ __host__ __device__ inline int64_t ticket_count(const Problem &p)
     return p.kind == 2 ? (int64_t)p.ntt * p.mt : (int64_t)p.NT;
 }
 
+// Up to kMultiMax problems that read the same int8 activations, passed by
+// value to one launch (q|k|v, gate|up): workgroup b belongs to the last
+// problem i with begin[i] <= b, as its local item b - begin[i].
+constexpr int kMultiMax = 4;
+struct ProblemSet {
+    Problem p[kMultiMax];
+    int32_t begin[kMultiMax + 1];
+    int32_t count;
+    int32_t pad_;
+};
+__device__ inline int multi_index(const ProblemSet &ps, int b)
+{
+    int i = 0;
+#pragma unroll
+    for (int j = 1; j < kMultiMax; ++j)
+        if (j < ps.count && b >= ps.begin[j]) i = j;
+    return i;
+}
+
 // Fragment order of the int8 activations ("QF32"), used by the tile kernel
 // so that each wave reads an MFMA A operand with one contiguous 1 KiB load:
 // for 32-row block b = m / 32, 64-code unit u and half h, a 1 KiB block at
@@ -156,6 +175,9 @@ hipError_t launch_tile_single(const Problem &p, int variant, hipStream_t s);
 hipError_t launch_tile_group(const Problem *probs, const uint2 *item_map, int n_items,
                              int variant, hipStream_t s);
 hipError_t launch_bt5_single(const Problem &p, hipStream_t s);
+hipError_t launch_stream_multi(const ProblemSet &ps, int variant, int lds_bytes, hipStream_t s);
+hipError_t launch_tile_multi(const ProblemSet &ps, int variant, hipStream_t s);
+hipError_t launch_bt5_multi(const ProblemSet &ps, int max_tokens, hipStream_t s);
 hipError_t launch_bt5_group(const Problem *probs, const uint2 *item_map, int n_items, int max_tokens,
                             hipStream_t s);
 

@@ -507,6 +507,13 @@ __global__ __launch_bounds__(kThreads, 2) void tile_group_kernel(const Problem *
     if (it.x != 0xFFFFFFFFu) tile_dispatch<V>(probs[it.x], (int)it.y);
 }
 
+template <int V>
+__global__ __launch_bounds__(kThreads, 2) void tile_multi_kernel(ProblemSet ps)
+{
+    const int i = multi_index(ps, blockIdx.x);
+    tile_dispatch<V>(ps.p[i], (int)blockIdx.x - ps.begin[i]);
+}
+
 }  // namespace
 
 // one case per instantiation; unknown values take 18
@@ -539,6 +546,13 @@ hipError_t launch_tile_group(const Problem *probs, const uint2 *item_map, int n_
 {
     const dim3 grid((unsigned)n_items), block(kThreads);
     BL_TILE_CASES(tile_group_kernel, grid, block, 0, s, probs, item_map)
+    return hipGetLastError();
+}
+
+hipError_t launch_tile_multi(const ProblemSet &ps, int variant, hipStream_t s)
+{
+    const dim3 grid((unsigned)ps.begin[ps.count]), block(kThreads);
+    BL_TILE_CASES(tile_multi_kernel, grid, block, 0, s, ps)
     return hipGetLastError();
 }
 

@@ -191,6 +191,13 @@ __global__ __launch_bounds__(kThreads, 2) void bt5_group_kernel(const Problem *_
     if (it.x != 0xFFFFFFFFu) bt5_body<NA>(probs[it.x], (int)it.y);
 }
 
+template <int NA>
+__global__ __launch_bounds__(kThreads, 2) void bt5_multi_kernel(ProblemSet ps)
+{
+    const int i = multi_index(ps, blockIdx.x);
+    bt5_body<NA>(ps.p[i], (int)blockIdx.x - ps.begin[i]);
+}
+
 }  // namespace
 
 int bt5_chunk_loads(int max_tokens)
@@ -218,6 +225,17 @@ hipError_t launch_bt5_group(const Problem *probs, const uint2 *item_map, int n_i
     case 1: hipLaunchKernelGGL(bt5_group_kernel<1>, grid, block, 0, s, probs, item_map); break;
     case 2: hipLaunchKernelGGL(bt5_group_kernel<2>, grid, block, 0, s, probs, item_map); break;
     default: hipLaunchKernelGGL(bt5_group_kernel<3>, grid, block, 0, s, probs, item_map); break;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_bt5_multi(const ProblemSet &ps, int max_tokens, hipStream_t s)
+{
+    const dim3 grid((unsigned)ps.begin[ps.count]), block(kThreads);
+    switch (bt5_chunk_loads(max_tokens)) {
+    case 1: hipLaunchKernelGGL(bt5_multi_kernel<1>, grid, block, 0, s, ps); break;
+    case 2: hipLaunchKernelGGL(bt5_multi_kernel<2>, grid, block, 0, s, ps); break;
+    default: hipLaunchKernelGGL(bt5_multi_kernel<3>, grid, block, 0, s, ps); break;
     }
     return hipGetLastError();
 }

@@ -467,7 +467,28 @@ __global__ __launch_bounds__(kThreads) void stream_group_kernel(const Problem *_
     stream_body<V>(probs[it.x], (int)it.y);
 }
 
+template <int V>
+__global__ __launch_bounds__(kThreads) void stream_multi_kernel(ProblemSet ps)
+{
+    const int i = multi_index(ps, blockIdx.x);
+    stream_body<V>(ps.p[i], (int)blockIdx.x - ps.begin[i]);
+}
+
 }  // namespace
+
+hipError_t launch_stream_multi(const ProblemSet &ps, int variant, int lds_bytes, hipStream_t s)
+{
+    const dim3 grid((unsigned)ps.begin[ps.count]), block(kThreads);
+    const unsigned lds = variant >= 2 ? (unsigned)lds_bytes : 0u;
+    switch (variant) {
+    case 0: hipLaunchKernelGGL(stream_multi_kernel<0>, grid, block, 0, s, ps); break;
+    case 1: hipLaunchKernelGGL(stream_multi_kernel<1>, grid, block, 0, s, ps); break;
+    case 2: hipLaunchKernelGGL(stream_multi_kernel<2>, grid, block, lds, s, ps); break;
+    case 5: hipLaunchKernelGGL(stream_multi_kernel<5>, grid, block, lds, s, ps); break;
+    default: hipLaunchKernelGGL(stream_multi_kernel<3>, grid, block, lds, s, ps); break;
+    }
+    return hipGetLastError();
+}
 
 hipError_t launch_stream_single(const Problem &p, int variant, hipStream_t s)
 {

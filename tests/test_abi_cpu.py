@@ -29,7 +29,7 @@ def _declared():
 
 def test_every_declared_symbol_is_exported():
     names = _declared()
-    assert len(names) == 27, names
+    assert len(names) == 29, names
     out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r"\bT (bitlinear_\w+)", out))
@@ -271,3 +271,32 @@ def test_group_plan_bt5_items():
     bad = _problems([(1, 64, 64)], fmt=1)
     bad[0].reserved = 1
     assert L.bitlinear_group_table_bytes(bad, 1) == 0
+
+
+def _weights(Ns, fmt=0):
+    arr = (B.Weight * len(Ns))()
+    for i, N in enumerate(Ns):
+        arr[i] = B.Weight(FAKE, FAKE, FAKE, None, N, fmt, 0)
+    return arr
+
+
+def test_matmul_multi_validation():
+    L = B.lib()
+    w = _weights([640, 640, 2560])
+    smax = ctypes.c_size_t(-1).value
+    assert L.bitlinear_multi_workspace_bytes(w, 3, 1, 2560) != smax
+    assert L.bitlinear_multi_workspace_bytes(w, 0, 1, 2560) == smax
+    assert L.bitlinear_multi_workspace_bytes(_weights([64] * 5), 5, 1, 64) == smax
+    # one long-K small-N matrix splits K: counters and partials need workspace
+    assert L.bitlinear_multi_workspace_bytes(_weights([64]), 1, 1, 8192) > 0
+    mm = L.bitlinear_matmul_multi
+    assert mm(None, 2560, FAKE, FAKE, 1, 2560, w, 3, None, 0, None) == -1
+    assert mm(FAKE, 2496, FAKE, FAKE, 1, 2560, w, 3, None, 0, None) == -2      # ldq < K
+    assert mm(FAKE, 2560, FAKE, FAKE, 1, 2560, w, 5, None, 0, None) == -2      # count
+    mixed = _weights([640, 640])
+    mixed[1].format = 1
+    assert mm(FAKE, 2560, FAKE, FAKE, 1, 2560, mixed, 2, None, 0, None) == -6
+    bt5 = _weights([640], fmt=1)
+    assert mm(FAKE, 2560, FAKE, FAKE, 1, 2561, bt5, 1, None, 0, None) == -2   # BT5 needs ldq >= 2720 (160-code units)
+    need = L.bitlinear_multi_workspace_bytes(_weights([64]), 1, 1, 8192)
+    assert mm(FAKE, 8192, FAKE, FAKE, 1, 8192, _weights([64]), 1, FAKE, need - 1, None) == -4

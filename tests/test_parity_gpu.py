@@ -655,6 +655,35 @@ def test_lut_variant_subprocess(B):
     assert r.returncode == 0 and "lut ok" in r.stdout, r.stdout + r.stderr
 
 
+@pytest.mark.parametrize("M,K,Ns,fmt", [(1, 2560, (2560, 640, 640), 0), (1, 333, (100, 37, 257), 0),
+                                         (5, 640, (257, 100), 0), (40, 700, (300, 130, 64, 520), 0),
+                                         (100, 256, (256, 512), 0), (1, 8192, (64,), 0),
+                                         (1, 2560, (640, 2560, 100), 1), (9, 1000, (320, 64), 1),
+                                         (20, 8192, (64, 96), 1)])
+def test_matmul_multi_parity(B, M, K, Ns, fmt):
+    # several weight matrices on one int8 input in one launch: every output
+    # bit-exact against the oracle; a second call on the same (zero-filled
+    # once) workspace checks that the split-K counters come back to zero
+    say("matmul_multi", M, K, Ns, fmt)
+    X = synth.activations_np(M, K, seed=M + K, outlier_frac=0.01)
+    Q, a, rs = O.quant_act(X)
+    ldq = B.q_stride5(K) if fmt else B.q_stride(K)
+    Qp = np.zeros((M, ldq), np.int8)
+    Qp[:, :K] = Q
+    ws, refs = [], []
+    for i, N in enumerate(Ns):
+        T = synth.random_ternary(N, K, seed=31 * i + N + K)
+        g = np.float32(0.01 * (i + 1))
+        refs.append((O.matmul(Q, T), g))
+        ws.append(dict(P=dev(O.pack5(T) if fmt else O.pack(T)), gamma=gamma_dev(float(g)), N=N, format=fmt))
+    mm = B.MultiMatmul(ws, M, K)
+    for rep in range(2):
+        accs = [torch.empty((M, N), dtype=torch.int32, device="cuda") for N in Ns]
+        Ys = mm(dev(Qp), dev(a), dev(rs), accs=accs)
+        for Y, acc, (ref, g) in zip(Ys, accs, refs):
+            check_outputs(host(Y), host(acc), ref, float(g), a, f"multi rep {rep}")
+
+
 def test_group_mixed(B):
     say("group mixed")
     _group_run(B, [(1, 640, 2560), (4, 100, 200), (40, 257, 640), (130, 300, 700), (17, 64, 64)], 600)
