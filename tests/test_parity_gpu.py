@@ -684,6 +684,60 @@ def test_matmul_multi_parity(B, M, K, Ns, fmt):
             check_outputs(host(Y), host(acc), ref, float(g), a, f"multi rep {rep}")
 
 
+KNOB_SCRIPT = r"""
+import numpy as np, torch, sys
+sys.path.insert(0, ".")
+import oracle as O, synth, ternary_weight_w1_amd as B
+dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+g = np.float32(0.0173)
+gd = dev(np.array([g], np.float32))
+# forward (library-quantized activations) and matmul (caller activations):
+# one token, a few tokens, more than 32 (tile kernel), split K, ragged tails
+for M, N, K in [(1, 640, 2560), (1, 100, 200), (5, 257, 640), (17, 130, 1000), (33, 100, 200),
+                (96, 300, 700), (1, 64, 8192), (3, 130, 4000)]:
+    T = synth.random_ternary(N, K, seed=M + N + K); X = synth.activations_np(M, K, seed=K + M, outlier_frac=0.01)
+    ref = O.forward(X, T, g)
+    P = dev(O.pack(T))
+    Y, acc = B.forward(dev(X), P, gd, N, with_acc=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(acc.cpu().numpy(), ref["acc"]) and np.array_equal(Y.cpu().numpy(), ref["Y"]), ("forward", M, N, K)
+    Qp = np.zeros((M, B.q_stride(K)), np.int8); Qp[:, :K] = ref["Q"]
+    Y, acc = B.matmul(dev(Qp), dev(ref["absmax"]), dev(ref["rowsum"]), P, gd, N, K, with_acc=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(acc.cpu().numpy(), ref["acc"]) and np.array_equal(Y.cpu().numpy(), ref["Y"]), ("matmul", M, N, K)
+probs, refs = [], []
+for i, (M, N, K) in enumerate([(1, 640, 2560), (4, 100, 200), (40, 257, 640), (1, 64, 8192)]):
+    T = synth.random_ternary(N, K, seed=400 + i); X = synth.activations_np(M, K, seed=410 + i)
+    refs.append(O.forward(X, T, g))
+    probs.append(dict(X=dev(X), P=dev(O.pack(T)), gamma=gd, Y=torch.empty((M, N), device="cuda"),
+                      acc=torch.empty((M, N), dtype=torch.int32, device="cuda"), N=N))
+plan = B.GroupPlan(probs)
+plan.forward(); torch.cuda.synchronize()
+for p, ref in zip(probs, refs):
+    assert np.array_equal(p["acc"].cpu().numpy(), ref["acc"]) and np.array_equal(p["Y"].cpu().numpy(), ref["Y"]), "group"
+print("knob ok")
+"""
+
+KNOB_SETTINGS = [
+    ("BITLINEAR_DOT4_MAX_M", "0"), ("BITLINEAR_DOT4_VARIANT", "0"), ("BITLINEAR_DOT4_VARIANT", "2"),
+    ("BITLINEAR_SPLIT_TARGET", "1"), ("BITLINEAR_SPLIT_TARGET", "100000"), ("BITLINEAR_XCD_ORDER", "0"),
+] + [("BITLINEAR_TILE_VARIANT", str(v)) for v in (0, 1, 2, 5, 6, 7, 10, 11, 12, 18)]
+
+
+@pytest.mark.parametrize("knob,value", KNOB_SETTINGS)
+def test_knob_variants_subprocess(B, knob, value):
+    # every kernel variant a measurement knob can select gives the default
+    # path's results, bit for bit (knobs are read once per process, hence one
+    # child process per setting)
+    say("knob", knob, value)
+    import os
+    import subprocess
+    env = dict(os.environ, **{knob: value})
+    r = subprocess.run([sys.executable, "-c", KNOB_SCRIPT], env=env, capture_output=True, text=True,
+                       timeout=110)
+    assert r.returncode == 0 and "knob ok" in r.stdout, r.stdout + r.stderr
+
+
 def test_group_mixed(B):
     say("group mixed")
     _group_run(B, [(1, 640, 2560), (4, 100, 200), (40, 257, 640), (130, 300, 700), (17, 64, 64)], 600)
