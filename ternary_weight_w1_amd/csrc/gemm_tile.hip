@@ -457,7 +457,7 @@ __device__ __forceinline__ void tile_body_ups(const Problem &p, int local)
 //   18  as 11 with two 64-code units per LDS stage;
 //   19  as 18 with 64-token tiles (64 x 64 per wave; the default).
 template <int V>
-__device__ inline void tile_dispatch(const Problem &p, int local)
+__device__ __forceinline__ void tile_dispatch(const Problem &p, int local)
 {
     if constexpr (V == 0)
         tile_body<2, 1, 1, 0>(p, local);
