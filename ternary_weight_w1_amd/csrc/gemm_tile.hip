@@ -314,11 +314,6 @@ __device__ __forceinline__ void tile_body_ups(const Problem &p, int local)
     }
 
     __syncthreads();  // the previous work item of this workgroup may still read LDS
-    if (tid < BM) {
-        const int m = min(m0 + tid, p.M - 1);
-        cs[tid] = (*gload_ptr<float>(p.gamma) * gload_ptr<float>(p.absmax)[m]) / 127.0f;
-        rsum[tid] = gload_ptr<int32_t>(p.rowsum)[m];
-    }
 
     v4i ar[kD][UPS][CH];
     v4u br[kD][UPS];
@@ -340,6 +335,14 @@ __device__ __forceinline__ void tile_body_ups(const Problem &p, int local)
     };
 #pragma unroll
     for (int d = 0; d < kD; ++d) load_stage(d, d);
+    // the token scales (read by the epilogue only) are requested behind the
+    // first stages, so the two memory round trips overlap
+    __builtin_amdgcn_sched_barrier(0);
+    if (tid < BM) {
+        const int m = min(m0 + tid, p.M - 1);
+        cs[tid] = (*gload_ptr<float>(p.gamma) * gload_ptr<float>(p.absmax)[m]) / 127.0f;
+        rsum[tid] = gload_ptr<int32_t>(p.rowsum)[m];
+    }
     stage_lds(0, 0);
     __syncthreads();
 
