@@ -306,6 +306,80 @@ def stack_curve(B, torch, mats, dev, Ms, steps, warmup):
     return out
 
 
+def measured_peaks(B, torch, dev, seconds: float = 0.6):
+    """What this part sustains on the two roofline resources, from the
+    library's calibration probes (include/bitlinear_probe.h):
+    * HBM read: a plain 16-byte streaming read of a 2 GiB buffer (8x the
+      256 MB last-level cache), best of 256 KiB, 1 MiB and 4 MiB per
+      workgroup, 10 launches each;
+    * int8 matrix rate: chains of v_mfma_i32_32x32x32_i8 with no memory
+      traffic on every resident workgroup slot, launched back to back in
+      bursts for about `seconds`; the median of the later bursts (the clock
+      settles under sustained load).
+    Each probe's checksum is verified before its rate is reported."""
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    def xor_all(t):
+        t = t.clone()
+        n = t.numel()
+        while n > 1:
+            h = n // 2
+            if n % 2:
+                t[0] ^= t[n - 1]
+            t[:h] ^= t[h:2 * h]
+            n = h
+        return int(t[0]) & 0xFFFFFFFF
+
+    nbytes = 2 << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(0x5A)
+    buf[0] = 1
+    # 2^29 words: one is 0x5A5A5A01, an odd number of others are 0x5A5A5A5A
+    want = 0x5A5A5A01 ^ 0x5A5A5A5A
+    best = None
+    for chunk in (256 << 10, 1 << 20, 4 << 20):
+        sink = torch.empty(B.probe_read_sink_words(nbytes, chunk), dtype=torch.int32, device=dev)
+        for _ in range(2):
+            B.probe_read(buf, chunk, sink)
+        a, b = ev(), ev()
+        a.record()
+        for _ in range(10):
+            B.probe_read(buf, chunk, sink)
+        b.record()
+        torch.cuda.synchronize()
+        gbs = nbytes * 10 / (a.elapsed_time(b) * 1e-3) / 1e9
+        if xor_all(sink) != want:
+            raise RuntimeError("read probe checksum mismatch")
+        if best is None or gbs > best[0]:
+            best = (gbs, chunk)
+    del buf, sink
+    torch.cuda.empty_cache()
+    blocks = B.probe_mfma_blocks()
+    iters, burst = 4096, 10
+    ops = blocks * 4 * iters * 4 * 65536
+    sink = torch.empty(256 * blocks, dtype=torch.int32, device=dev)
+    rates = []
+    t_end = time.perf_counter() + seconds
+    while time.perf_counter() < t_end:
+        a, b = ev(), ev()
+        a.record()
+        for _ in range(burst):
+            B.probe_mfma(iters, 1, 1, blocks, sink)
+        b.record()
+        b.synchronize()
+        rates.append(ops * burst / (a.elapsed_time(b) * 1e-3) / 1e12)
+    if not bool((sink == 2048 * iters).all()):
+        raise RuntimeError("matrix-instruction probe checksum mismatch")
+    later = sorted(rates[len(rates) // 2:])
+    tops = later[len(later) // 2]
+    return {
+        "hbm_read": {"value": round(best[0], 1), "unit": "GB/s",
+                     "probe": f"16-byte non-temporal streaming read of 2 GiB, {best[1] >> 10} KiB per workgroup"},
+        "int8_mfma": {"value": round(tops, 1), "unit": "TOP/s",
+                      "probe": f"v_mfma_i32_32x32x32_i8 chains, {blocks} workgroups, no memory traffic, "
+                               f"median of {len(later)} sustained bursts"},
+    }
+
+
 def load_traffic(name):
     """HBM traffic of the dominant kernel from the committed rocprofv3 PMC
     summary, if it was taken on the current kernel sources."""
@@ -362,6 +436,7 @@ def main():
                          "'none' to skip")
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-bt5", action="store_true", help="skip the five-codes-per-byte comparison")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the measured-peak calibration probes")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run only a plain device copy of known size (PMC calibration)")
     args = ap.parse_args()
@@ -460,6 +535,21 @@ def main():
         }
         del plan, probs
         torch.cuda.empty_cache()
+
+    if not args.no_peaks:
+        log("measuring the sustained HBM-read and int8-matrix peaks")
+        peaks = measured_peaks(B, torch, dev)
+        result["measured_peaks"] = peaks
+        hbm, mfma = peaks["hbm_read"]["value"], peaks["int8_mfma"]["value"]
+        result["roofline"]["measured_peak"] = hbm
+        result["roofline"]["frac_of_measured"] = round(result["roofline"]["achieved"] / hbm, 4)
+        for pt in result.get("bt5", {}).get("points", []):
+            pt["roofline"]["measured_peak"] = hbm
+            pt["roofline"]["frac_of_measured"] = round(pt["roofline"]["achieved"] / hbm, 4)
+        if "prefill" in result:
+            pr = result["prefill"]["roofline"]
+            pr["measured_peak"] = mfma
+            pr["frac_of_measured"] = round(pr["achieved"] / mfma, 4)
 
     curves = [c for c in args.curves.split(",") if c and c != "none"]
     if curves:

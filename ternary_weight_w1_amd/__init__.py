@@ -95,6 +95,10 @@ def lib():
             "bitlinear_group_quant_act": (_int, [_vp, _vp, _vp]),
             "bitlinear_group_matmul": (_int, [_vp, _vp, _vp]),
             "bitlinear_group_forward": (_int, [_vp, _vp, _vp]),
+            "bitlinear_probe_read_sink_words": (_i64, [_i64, _i64]),
+            "bitlinear_probe_read": (_int, [_vp, _i64, _i64, _vp, _vp]),
+            "bitlinear_probe_mfma": (_int, [_i64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _vp, _vp]),
+            "bitlinear_probe_mfma_blocks": (_int, [ctypes.POINTER(ctypes.c_int32)]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -335,6 +339,40 @@ def forward5(X, P, gamma, N: int, with_acc: bool = False, ws=None, out=None, str
                                     _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)),
            "forward5")
     return (Y, acc) if with_acc else Y
+
+
+def probe_read_sink_words(nbytes: int, chunk_bytes: int) -> int:
+    return int(lib().bitlinear_probe_read_sink_words(nbytes, chunk_bytes))
+
+
+def probe_read(buf, chunk_bytes: int, sink=None, stream=None):
+    """Streaming-read calibration probe over the bytes of a contiguous CUDA
+    tensor; returns the uint32 sink (XOR of all sink words = XOR of all
+    32-bit words of the buffer)."""
+    if not (isinstance(buf, torch.Tensor) and buf.is_cuda and buf.is_contiguous()):
+        raise TypeError("buf must be a contiguous CUDA tensor")
+    nbytes = buf.numel() * buf.element_size()
+    words = probe_read_sink_words(nbytes, chunk_bytes)
+    if sink is None:
+        sink = torch.empty(max(words, 1), dtype=torch.int32, device=buf.device)
+    _check(lib().bitlinear_probe_read(buf.data_ptr(), nbytes, chunk_bytes, sink.data_ptr(), _stream(stream)),
+           "probe_read")
+    return sink
+
+
+def probe_mfma_blocks() -> int:
+    n = ctypes.c_int32(0)
+    _check(lib().bitlinear_probe_mfma_blocks(ctypes.byref(n)), "probe_mfma_blocks")
+    return int(n.value)
+
+
+def probe_mfma(iters: int, a: int, b: int, blocks: int, sink=None, device=None, stream=None):
+    """Int8 matrix-instruction calibration probe: blocks*4*iters*4*65536
+    int8 operations; every sink entry becomes 2048*a*b*iters."""
+    if sink is None:
+        sink = torch.empty(256 * blocks, dtype=torch.int32, device=device or "cuda")
+    _check(lib().bitlinear_probe_mfma(iters, a, b, blocks, sink.data_ptr(), _stream(stream)), "probe_mfma")
+    return sink
 
 
 class MultiMatmul:

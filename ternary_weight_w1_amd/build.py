@@ -20,7 +20,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libbitlinear.so")
 SOURCES = ["api.hip", "weight_quant.hip", "pack.hip", "pack5.hip", "act_quant.hip",
-           "gemv_stream.hip", "gemm_tile.hip", "gemv5.hip"]
+           "gemv_stream.hip", "gemm_tile.hip", "gemv5.hip", "probes.hip"]
 ARCH = "gfx950"
 
 CFLAGS = [

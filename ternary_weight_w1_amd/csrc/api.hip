@@ -3,6 +3,7 @@
 // allocates, frees, copies or synchronizes; validation happens before the
 // first launch, so a rejected call enqueues nothing.
 #include <bitlinear.h>
+#include <bitlinear_probe.h>
 
 #include <cstdarg>
 #include <cstdio>
@@ -13,6 +14,7 @@
 
 #include "bt5.hpp"
 #include "common.hpp"
+#include "probe.hpp"
 
 using bl::Problem;
 
@@ -1027,6 +1029,51 @@ int bitlinear_group_forward(const void *table_host, const void *table_dev, void 
 {
     if (int st = bitlinear_group_quant_act(table_host, table_dev, stream)) return st;
     return bitlinear_group_matmul(table_host, table_dev, stream);
+}
+
+
+// ---------------------------------------------------------------- probes
+
+int64_t bitlinear_probe_read_sink_words(int64_t bytes, int64_t chunk_bytes)
+{
+    if (bytes <= 0 || bytes % 16 != 0 || chunk_bytes <= 0 || chunk_bytes % 4096 != 0) return 0;
+    const int64_t chunks = (bytes + chunk_bytes - 1) / chunk_bytes;
+    return chunks > (int64_t(1) << 31) - 1 ? 0 : chunks * 256;
+}
+
+int bitlinear_probe_read(const void *buf, int64_t bytes, int64_t chunk_bytes, uint32_t *sink, void *stream)
+{
+    if (!buf || !sink) return fail(BITLINEAR_ERR_NULL, "probe_read: buf and sink are required");
+    if (!a16(buf) || !a4(sink)) return fail(BITLINEAR_ERR_ALIGN, "probe_read: buf must be 16-byte aligned");
+    if (bitlinear_probe_read_sink_words(bytes, chunk_bytes) == 0)
+        return fail(BITLINEAR_ERR_SHAPE, "probe_read: bytes=%lld (multiple of 16) chunk_bytes=%lld (multiple of 4096)",
+                    (long long)bytes, (long long)chunk_bytes);
+    const hipError_t e = bl::launch_probe_read(buf, bytes, chunk_bytes, sink, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? BITLINEAR_OK : hip_fail(e, "probe_read");
+}
+
+int bitlinear_probe_mfma(int64_t iters, int32_t a, int32_t b, int32_t blocks, int32_t *sink, void *stream)
+{
+    if (!sink) return fail(BITLINEAR_ERR_NULL, "probe_mfma: sink is required");
+    if (!a4(sink)) return fail(BITLINEAR_ERR_ALIGN, "probe_mfma: sink must be 4-byte aligned");
+    if (a < -128 || a > 127 || b < -128 || b > 127)
+        return fail(BITLINEAR_ERR_ARG, "probe_mfma: a=%d b=%d outside the int8 range", a, b);
+    const int64_t ab = (int64_t)(a < 0 ? -a : a) * (b < 0 ? -b : b);
+    if (iters < 1 || blocks < 1 || 2048 * ab * iters >= (int64_t(1) << 31))
+        return fail(BITLINEAR_ERR_SHAPE, "probe_mfma: iters=%lld blocks=%d (2048 |a b| iters must stay below 2^31)",
+                    (long long)iters, blocks);
+    const hipError_t e = bl::launch_probe_mfma(iters, a, b, blocks, sink, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? BITLINEAR_OK : hip_fail(e, "probe_mfma");
+}
+
+int bitlinear_probe_mfma_blocks(int32_t *blocks)
+{
+    if (!blocks) return fail(BITLINEAR_ERR_NULL, "probe_mfma_blocks: blocks is required");
+    int n = 0;
+    const hipError_t e = bl::probe_mfma_resident_blocks(&n);
+    if (e != hipSuccess) return hip_fail(e, "probe_mfma_blocks");
+    *blocks = n;
+    return BITLINEAR_OK;
 }
 
 }  // extern "C"

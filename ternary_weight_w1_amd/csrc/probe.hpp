@@ -1,0 +1,13 @@
+// Launchers of the calibration probes (defined in probes.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bl {
+
+hipError_t launch_probe_read(const void *buf, int64_t bytes, int64_t chunk_bytes, uint32_t *sink, hipStream_t s);
+hipError_t launch_probe_mfma(int64_t iters, int a, int b, int blocks, int32_t *sink, hipStream_t s);
+hipError_t probe_mfma_resident_blocks(int *blocks);
+
+}  // namespace bl

@@ -1,5 +1,6 @@
 """C-ABI checks that need no GPU: the library loads, exports every function
-include/bitlinear.h declares, sizes its buffers as documented, and rejects
+include/bitlinear.h and include/bitlinear_probe.h declare, sizes its buffers
+as documented, and rejects
 bad arguments before touching the HIP runtime (nothing is enqueued, so these
 calls never reach a device)."""
 import ctypes
@@ -13,7 +14,7 @@ import pytest
 import ternary_weight_w1_amd as B
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "bitlinear.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("bitlinear.h", "bitlinear_probe.h")]
 
 pytestmark = pytest.mark.skipif(not os.path.exists(B.LIB_PATH),
                                 reason="libbitlinear.so not built (run __graft_entry__.build())")
@@ -22,14 +23,21 @@ FAKE = 1 << 40  # a 16-byte aligned address that is never dereferenced
 
 
 def _declared():
-    src = open(HEADER).read()
-    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(bitlinear_\w+)\s*\(", src)))
+    names = set()
+    for h in HEADERS:
+        src = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(bitlinear_\w+)\s*\(", src))
+    return sorted(names)
+
+
+def test_every_header_is_checked():
+    inc = sorted(f for f in os.listdir(os.path.join(ROOT, "include")) if f.endswith(".h"))
+    assert inc == sorted(os.path.basename(h) for h in HEADERS)
 
 
 def test_every_declared_symbol_is_exported():
     names = _declared()
-    assert len(names) == 29, names
+    assert len(names) == 33, names
     out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r"\bT (bitlinear_\w+)", out))
@@ -300,3 +308,39 @@ def test_matmul_multi_validation():
     assert mm(FAKE, 2560, FAKE, FAKE, 1, 2561, bt5, 1, None, 0, None) == -2   # BT5 needs ldq >= 2720 (160-code units)
     need = L.bitlinear_multi_workspace_bytes(_weights([64]), 1, 1, 8192)
     assert mm(FAKE, 8192, FAKE, FAKE, 1, 8192, _weights([64]), 1, FAKE, need - 1, None) == -4
+
+
+# ---- calibration probes (include/bitlinear_probe.h): validation only
+
+
+def test_probe_read_sink_words():
+    L = B.lib()
+    assert L.bitlinear_probe_read_sink_words(1 << 20, 65536) == 16 * 256
+    assert L.bitlinear_probe_read_sink_words((1 << 20) + 16, 65536) == 17 * 256
+    assert L.bitlinear_probe_read_sink_words(16, 4096) == 256
+    for nbytes, chunk in [(0, 4096), (-16, 4096), (24, 4096), (4096, 0), (4096, 2048), (4096, 6000)]:
+        assert L.bitlinear_probe_read_sink_words(nbytes, chunk) == 0, (nbytes, chunk)
+
+
+def test_probe_read_rejects_bad_arguments():
+    L = B.lib()
+    assert L.bitlinear_probe_read(None, 4096, 4096, FAKE, None) == -1
+    assert L.bitlinear_probe_read(FAKE, 4096, 4096, None, None) == -1
+    assert L.bitlinear_probe_read(FAKE + 8, 4096, 4096, FAKE, None) == -3
+    assert L.bitlinear_probe_read(FAKE, 4100, 4096, FAKE, None) == -2
+    assert L.bitlinear_probe_read(FAKE, 4096, 1000, FAKE, None) == -2
+    assert L.bitlinear_probe_read(FAKE, 0, 4096, FAKE, None) == -2
+
+
+def test_probe_mfma_rejects_bad_arguments():
+    L = B.lib()
+    assert L.bitlinear_probe_mfma(10, 1, 1, 1, None, None) == -1
+    assert L.bitlinear_probe_mfma(10, 128, 1, 1, FAKE, None) == -6
+    assert L.bitlinear_probe_mfma(10, 1, -129, 1, FAKE, None) == -6
+    assert L.bitlinear_probe_mfma(0, 1, 1, 1, FAKE, None) == -2
+    assert L.bitlinear_probe_mfma(10, 1, 1, 0, FAKE, None) == -2
+    # 2048 |a b| iters must stay below 2^31: 2048 * 127 * 128 * 65 = 2,164,260,864
+    assert L.bitlinear_probe_mfma(65, 127, -128, 1, FAKE, None) == -2
+    assert L.bitlinear_probe_mfma((1 << 20), 1, 1, 1, FAKE, None) == -2
+    assert L.bitlinear_probe_mfma_blocks(None) == -1
+
