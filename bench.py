@@ -197,39 +197,48 @@ def bt5_section(B, torch, mats, dev, Ms, steps, warmup, model):
     return out
 
 
-def stack_curve(B, torch, mats, dev, Ms, steps, warmup):
-    """The stack chained as pre-norm blocks, one decode (or prefill) step of
-    M tokens through every layer, each step a library call on one stream:
-    residual add + RMSNorm + int8 cast, q|k|v in one launch (one input), the
-    attention of the first decode position (a single key, so its output is
-    v), the cast of v, o, residual add + RMSNorm + cast, gate|up in one
-    launch, the gated squared-ReLU cast, down; then the final residual add +
-    norm: 8 launches per layer.  Timed eagerly and as one HIP graph
-    replayed.  Buffers and workspaces are allocated once (workspaces
-    zero-filled once, as the multi-matrix call requires)."""
-    import ctypes
-    L = B.lib()
-    layers = {}
-    for m in mats:
-        layers.setdefault(m["layer"], {})[m["name"]] = m
-    dim = layers[0]["q"]["K"]
-    ffn = layers[0]["gate"]["N"]
-    out = {"layers": len(layers), "dim": dim, "ffn": ffn, "launches_per_step": 8 * len(layers) + 1,
-           "points": []}
+def stack_inputs(torch, dim, n_layers, M, dev):
+    """Seeded inputs of the chained stack: the first residual stream x0
+    (M x dim) and the RMSNorm gains, per layer (attention, feed-forward)
+    and final, drawn in (0.5, 1.5)."""
     gen = torch.Generator(device=dev)
     gen.manual_seed(5)
     gains = [(torch.rand(dim, generator=gen, device=dev) + 0.5, torch.rand(dim, generator=gen, device=dev) + 0.5)
-             for _ in layers]
+             for _ in range(n_layers)]
     g_fin = torch.rand(dim, generator=gen, device=dev) + 0.5
-    P = lambda t: ctypes.c_void_p(t.data_ptr())
-    for M in Ms:
-        x0 = synth.activations_torch(M, dim, 21, dev)
+    return synth.activations_torch(M, dim, 21, dev), gains, g_fin
+
+
+class ChainedStack:
+    """The stack chained as pre-norm blocks for M tokens, each stage a
+    library call on one stream: residual add + RMSNorm + int8 cast, q|k|v in
+    one launch (one input), the attention of the first decode position (a
+    single key, so its output is v), the cast of v, o, residual add + RMSNorm
+    + cast, gate|up in one launch, the gated squared-ReLU cast, down; then
+    the final residual add + norm + cast: 8 launches per layer.  Buffers and
+    workspaces are allocated once (workspaces zero-filled once, as the
+    multi-matrix call requires).  After step(), x holds the final residual
+    stream and (Q, a, rs) its final norm's int8 cast."""
+
+    def __init__(self, B, torch, mats, dev, M, x0, gains, g_fin):
+        import ctypes
+        self.L = L = B.lib()
+        self.layers = layers = {}
+        for m in mats:
+            layers.setdefault(m["layer"], {})[m["name"]] = m
+        self.M = M
+        self.dim = dim = layers[0]["q"]["K"]
+        self.ffn = ffn = layers[0]["gate"]["N"]
+        self.x0, self.gains, self.g_fin = x0, gains, g_fin
         f32 = lambda n: torch.empty((M, n), dtype=torch.float32, device=dev)
-        x, q, k, v, o, gate, up, d = f32(dim), f32(dim), f32(dim), f32(dim), f32(dim), f32(ffn), f32(ffn), f32(dim)
-        ldd, ldf = B.q_stride(dim), B.q_stride(ffn)
-        Qd_, Qf_ = (torch.empty((M, ld), dtype=torch.int8, device=dev) for ld in (ldd, ldf))
-        a = torch.empty(M, dtype=torch.float32, device=dev)
-        rs = torch.empty(M, dtype=torch.int32, device=dev)
+        self.x, self.q, self.k, self.v, self.o = f32(dim), f32(dim), f32(dim), f32(dim), f32(dim)
+        self.gate, self.up, self.d = f32(ffn), f32(ffn), f32(dim)
+        self.ldd, self.ldf = B.q_stride(dim), B.q_stride(ffn)
+        self.Q = torch.empty((M, self.ldd), dtype=torch.int8, device=dev)
+        self.Qf = torch.empty((M, self.ldf), dtype=torch.int8, device=dev)
+        self.a = torch.empty(M, dtype=torch.float32, device=dev)
+        self.rs = torch.empty(M, dtype=torch.int32, device=dev)
+        self.P = lambda t: ctypes.c_void_p(t.data_ptr())
 
         def warr(lay, names, outs):
             arr = (B.Weight * len(names))()
@@ -237,59 +246,78 @@ def stack_curve(B, torch, mats, dev, Ms, steps, warmup):
                 arr[i] = B.Weight(lay[nm]["P"].data_ptr(), lay[nm]["gamma"].data_ptr(), Y.data_ptr(), None,
                                   lay[nm]["N"], 0, 0)
             return arr
-        sites = {}
-        for i, lay in layers.items():
-            sites[i] = dict(qkv=warr(lay, ("q", "k", "v"), (q, k, v)), o=warr(lay, ("o",), (o,)),
-                            gu=warr(lay, ("gate", "up"), (gate, up)), down=warr(lay, ("down",), (d,)))
-        wss = {}
+        self.sites = {i: dict(qkv=warr(lay, ("q", "k", "v"), (self.q, self.k, self.v)),
+                              o=warr(lay, ("o",), (self.o,)),
+                              gu=warr(lay, ("gate", "up"), (self.gate, self.up)),
+                              down=warr(lay, ("down",), (self.d,)))
+                      for i, lay in layers.items()}
+        self.wss = {}
         for key, K in (("qkv", dim), ("o", dim), ("gu", dim), ("down", ffn)):
-            n = len(sites[0][key])
-            wsb = L.bitlinear_multi_workspace_bytes(sites[0][key], n, M, K)
-            wss[key] = torch.zeros(max(wsb, 16), dtype=torch.uint8, device=dev)
+            arr = self.sites[0][key]
+            wsb = L.bitlinear_multi_workspace_bytes(arr, len(arr), M, K)
+            self.wss[key] = torch.zeros(max(wsb, 16), dtype=torch.uint8, device=dev)
 
-        def check(st):
-            if st != 0:
-                raise RuntimeError(L.bitlinear_last_error().decode())
+    def _check(self, st):
+        if st != 0:
+            raise RuntimeError(self.L.bitlinear_last_error().decode())
 
-        def multi(Q, ld, K, arr, key):
-            check(L.bitlinear_matmul_multi(P(Q), ld, P(a), P(rs), M, K, arr, len(arr), P(wss[key]),
-                                           wss[key].numel(), s))
+    def step(self, s):
+        """Enqueue one pass over every layer on the raw stream handle s."""
+        L, P, M, dim, ffn, ldd, ldf = self.L, self.P, self.M, self.dim, self.ffn, self.ldd, self.ldf
+        x, a, rs, Q = self.x, self.a, self.rs, self.Q
 
-        def step():
-            for i, lay in sorted(layers.items()):
-                ga, gf = gains[i]
-                site = sites[i]
-                if i == 0:
-                    check(L.bitlinear_quant_act_rmsnorm(P(x0), M, dim, P(ga), 1e-5, P(Qd_), ldd, P(a), P(rs), s))
-                else:
-                    check(L.bitlinear_quant_act_add_rmsnorm(P(x), P(d), M, dim, P(ga), 1e-5, P(x), P(Qd_), ldd,
-                                                            P(a), P(rs), s))
-                multi(Qd_, ldd, dim, site["qkv"], "qkv")
-                check(L.bitlinear_quant_act(P(v), M, dim, P(Qd_), ldd, P(a), P(rs), s))
-                multi(Qd_, ldd, dim, site["o"], "o")
-                check(L.bitlinear_quant_act_add_rmsnorm(P(x0 if i == 0 else x), P(o), M, dim, P(gf), 1e-5, P(x),
-                                                        P(Qd_), ldd, P(a), P(rs), s))
-                multi(Qd_, ldd, dim, site["gu"], "gu")
-                check(L.bitlinear_quant_act_relu2_gate(P(gate), P(up), M, ffn, P(Qf_), ldf, P(a), P(rs), s))
-                multi(Qf_, ldf, ffn, site["down"], "down")
-            check(L.bitlinear_quant_act_add_rmsnorm(P(x), P(d), M, dim, P(g_fin), 1e-5, P(x), P(Qd_), ldd,
-                                                    P(a), P(rs), s))
+        def multi(Qin, ld, K, key, site):
+            arr = site[key]
+            self._check(L.bitlinear_matmul_multi(P(Qin), ld, P(a), P(rs), M, K, arr, len(arr), P(self.wss[key]),
+                                                 self.wss[key].numel(), s))
+        for i in sorted(self.layers):
+            ga, gf = self.gains[i]
+            site = self.sites[i]
+            if i == 0:
+                self._check(L.bitlinear_quant_act_rmsnorm(P(self.x0), M, dim, P(ga), 1e-5, P(Q), ldd, P(a),
+                                                          P(rs), s))
+            else:
+                self._check(L.bitlinear_quant_act_add_rmsnorm(P(x), P(self.d), M, dim, P(ga), 1e-5, P(x), P(Q),
+                                                              ldd, P(a), P(rs), s))
+            multi(Q, ldd, dim, "qkv", site)
+            self._check(L.bitlinear_quant_act(P(self.v), M, dim, P(Q), ldd, P(a), P(rs), s))
+            multi(Q, ldd, dim, "o", site)
+            self._check(L.bitlinear_quant_act_add_rmsnorm(P(self.x0 if i == 0 else x), P(self.o), M, dim, P(gf),
+                                                          1e-5, P(x), P(Q), ldd, P(a), P(rs), s))
+            multi(Q, ldd, dim, "gu", site)
+            self._check(L.bitlinear_quant_act_relu2_gate(P(self.gate), P(self.up), M, ffn, P(self.Qf), ldf, P(a),
+                                                         P(rs), s))
+            multi(self.Qf, ldf, ffn, "down", site)
+        self._check(L.bitlinear_quant_act_add_rmsnorm(P(x), P(self.d), M, dim, P(self.g_fin), 1e-5, P(x), P(Q),
+                                                      ldd, P(a), P(rs), s))
 
+
+def stack_curve(B, torch, mats, dev, Ms, steps, warmup):
+    """Latency of the stack chained as pre-norm blocks (ChainedStack), one
+    decode (or prefill) step of M tokens through every layer, timed eagerly
+    and as one HIP graph replayed."""
+    import ctypes
+    n_layers = len({m["layer"] for m in mats})
+    dim = next(m["K"] for m in mats if m["name"] == "q")
+    ffn = next(m["N"] for m in mats if m["name"] == "gate")
+    out = {"layers": n_layers, "dim": dim, "ffn": ffn, "launches_per_step": 8 * n_layers + 1, "points": []}
+    for M in Ms:
+        chain = ChainedStack(B, torch, mats, dev, M, *stack_inputs(torch, dim, n_layers, M, dev))
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
             s = ctypes.c_void_p(side.cuda_stream)
             for _ in range(max(1, warmup)):
-                step()
+                chain.step(s)
             torch.cuda.synchronize()
             t0 = time.perf_counter()
             for _ in range(steps):
-                step()
+                chain.step(s)
             torch.cuda.synchronize()
             eager = (time.perf_counter() - t0) / steps * 1e3
             graph = torch.cuda.CUDAGraph()
             with torch.cuda.graph(graph, stream=side):
-                step()
+                chain.step(s)
         torch.cuda.current_stream().wait_stream(side)
         for _ in range(max(1, warmup)):
             graph.replay()
@@ -301,7 +329,7 @@ def stack_curve(B, torch, mats, dev, Ms, steps, warmup):
         gms = (time.perf_counter() - t0) / steps * 1e3
         out["points"].append({"M": M, "eager_ms_per_step": round(eager, 4), "graph_ms_per_step": round(gms, 4)})
         log(f"  stack M={M}: eager {eager:.3f} ms, graph {gms:.3f} ms per step")
-        del graph
+        del graph, chain
     torch.cuda.empty_cache()
     return out
 
