@@ -1,21 +1,23 @@
 """Parity in the exact launch configurations bench.py times.
 
-1. The whole 2B-class stack (30 layers x q, k, v, o, gate, up, down = 210
-   matrices) in one grouped plan, built by bench.make_plan, stepped as the
-   benchmark steps it (grouped quantization, then the grouped contraction,
-   no int32 side output), at the decode (M = 1) and prefill (M = 512, 1%
-   outlier channels) sizes, and packed five codes per byte at M = 1, 8, 16.
+1. Whole stacks in one grouped plan, built by bench.make_plan and stepped as
+   the benchmark steps them (grouped quantization, then the grouped
+   contraction, no int32 side output): the 2B-class stack (30 layers x q, k,
+   v, o, gate, up, down = 210 matrices) at the decode (M = 1) and prefill
+   (M = 512, 1% outlier channels) sizes and packed five codes per byte at
+   M = 1, 8, 16; the 3B-class curve (182 matrices) at M = 1, 8, 64, 256; the
+   70B-class curve (560 matrices, 17 GB packed) at M = 1, 16, 176.
 2. The 3B-class stack chained as the benchmark chains it (bench.ChainedStack,
    26 layers), checked at its end against the oracle's chain.
 
-The oracle sees only the seeded inputs: for three sampled layers (21
-matrices) the fp32 weights drawn on the device are copied to the host and
-quantized and packed by the oracle; the GPU must reproduce the packed bytes
-exactly given the oracle's scale, and for 16 sampled output rows of each of
-those matrices (always including the last) every token's fp32 output must
-equal the oracle's, bit for bit, and be within 1e-5 relative of the fp64
-rescale.  The other 189 matrices run in the same launches with the GPU's
-own scales, as in the benchmark."""
+The oracle sees only the seeded inputs: for the sampled layers the fp32
+weights drawn on the device are copied to the host and quantized and packed
+by the oracle; the GPU must reproduce the packed bytes exactly given the
+oracle's scale, and for 16 sampled output rows of each sampled matrix
+(always including the last) every token's fp32 output must equal the
+oracle's, bit for bit, and be within 1e-5 relative of the fp64 rescale.  The
+other matrices run in the same launches with the GPU's own scales, as in the
+benchmark."""
 import numpy as np
 import pytest
 import torch
@@ -26,8 +28,10 @@ import synth
 
 pytestmark = pytest.mark.gpu
 
-SAMPLED_LAYERS = (0, 17, 29)
 ROWS = 16
+# sampled layers per model (the oracle quantizes these); None = every layer
+SAMPLED = {"2b": (0, 17, 29), "3b": None, "70b": (0, 79)}
+_STACKS = {}
 
 
 def host(t):
@@ -38,38 +42,59 @@ def gamma_dev(g):
     return torch.tensor([g], dtype=torch.float32, device="cuda")
 
 
-@pytest.fixture(scope="module")
-def stack():
+def _stack(model):
+    """The model's whole stack packed on the device as bench.build_stack packs
+    it (also five codes per byte for 2B), the sampled layers from the
+    oracle's codes and scales; cached for the module."""
+    if model in _STACKS:
+        return _STACKS[model]
     import ternary_weight_w1_amd as B
-    spec = synth.MODELS["2b"]
-    mats, ref = [], {}
+    spec = synth.MODELS[model]
+    layers = SAMPLED[model]
+    bt5 = model == "2b"
+    mats, ref, codes = [], {}, {}
     for layer in range(spec["layers"]):
+        sampled = layers is None or layer in layers
         for j, (name, K, N) in enumerate(spec["shapes"]):
             W = synth.weights_torch(N, K, spec["sigma"], synth.matrix_seed(layer, j), "cuda")
-            sampled = layer in SAMPLED_LAYERS
             if sampled:
                 T, g = O.quantize_weights(host(W))
-                P, P5 = O.pack(T), O.pack5(T)
-                del T
                 Tg, gg = B.quantize_weights(W, gamma_in=gamma_dev(g))
             else:
                 Tg, gg = B.quantize_weights(W)
             del W
-            Pg, P5g = B.pack(Tg), B.pack5(Tg)
+            Pg = B.pack(Tg)
+            P5g = B.pack5(Tg) if bt5 else None
             del Tg
             if sampled:
-                np.testing.assert_array_equal(host(Pg), P, err_msg=f"packed bytes layer {layer} {name}")
-                np.testing.assert_array_equal(host(P5g), P5, err_msg=f"BT5 bytes layer {layer} {name}")
+                P = O.pack(T)
+                np.testing.assert_array_equal(host(Pg), P, err_msg=f"{model} packed bytes layer {layer} {name}")
+                P5 = None
+                if bt5:
+                    P5 = O.pack5(T)
+                    np.testing.assert_array_equal(host(P5g), P5, err_msg=f"{model} BT5 bytes layer {layer} {name}")
                 ref[len(mats)] = (name, P, P5, g)
+                if model == "3b":
+                    codes[(layer, name)] = (T, np.float32(g))
+                del T
             mats.append(dict(layer=layer, name=name, K=K, N=N, P=Pg, P5=P5g, gamma=gg))
     torch.cuda.synchronize()
-    assert len(mats) == 210
-    return B, mats, ref
+    _STACKS[model] = (B, mats, ref, codes)
+    return _STACKS[model]
 
 
-def _check_sampled(mats, ref, probs, M, fmt):
+@pytest.fixture(scope="module", autouse=True)
+def _release_stacks():
+    yield
+    _STACKS.clear()
+    torch.cuda.empty_cache()
+
+
+def _check_sampled(mats, ref, probs, M, fmt, every=1):
     rng = np.random.default_rng(M + 1000 * fmt)
-    for i, (name, P, P5, g) in ref.items():
+    for idx, (i, (name, P, P5, g)) in enumerate(sorted(ref.items())):
+        if idx % every:
+            continue
         N, K = mats[i]["N"], mats[i]["K"]
         Q, a, rs = O.quant_act(host(probs[i]["X"]))
         rows = np.sort(rng.choice(N, size=ROWS, replace=False))
@@ -87,24 +112,27 @@ def _check_sampled(mats, ref, probs, M, fmt):
         assert rel.size == 0 or rel.max() <= 1e-5, what
 
 
-@pytest.mark.parametrize("M,outliers", [(1, 0.0), (512, 0.01)])
-def test_bench_launch_configuration_sampled(stack, M, outliers):
-    B, mats, ref = stack
-    print(f"bench configuration: 210 matrices, M={M}", flush=True)
+@pytest.mark.parametrize("model,M,outliers", [("2b", 1, 0.0), ("2b", 512, 0.01), ("3b", 1, 0.0), ("3b", 8, 0.0),
+                                              ("3b", 64, 0.0), ("3b", 256, 0.0), ("70b", 1, 0.0), ("70b", 16, 0.0),
+                                              ("70b", 176, 0.0)])
+def test_bench_launch_configuration_sampled(model, M, outliers):
+    B, mats, ref, _ = _stack(model)
+    print(f"bench configuration: {model}, {len(mats)} matrices, M={M}", flush=True)
     plan, probs = bench.make_plan(B, torch, mats, M, torch.device("cuda:0"), outliers=outliers)
     plan.quant_act()
     plan.matmul()
     torch.cuda.synchronize()
-    _check_sampled(mats, ref, probs, M, 0)
+    # every layer of the 3B stack has oracle codes; check every fourth matrix
+    _check_sampled(mats, ref, probs, M, 0, every=4 if model == "3b" else 1)
     del plan, probs
     torch.cuda.empty_cache()
 
 
 @pytest.mark.parametrize("M", [1, 8, 16])
-def test_bench_bt5_configuration_sampled(stack, M):
+def test_bench_bt5_configuration_sampled(M):
     # the benchmark's five-codes-per-byte sweeps: the same 210 matrices in
     # BT5-T32, one grouped plan per token count
-    B, mats, ref = stack
+    B, mats, ref, _ = _stack("2b")
     print(f"bench BT5 configuration: 210 matrices, M={M}", flush=True)
     plan, probs = bench.make_plan(B, torch, mats, M, torch.device("cuda:0"), fmt=1)
     plan.quant_act()
@@ -117,37 +145,15 @@ def test_bench_bt5_configuration_sampled(stack, M):
 
 # ------------------------------------------- the chained 3B stack, full depth --
 
-@pytest.fixture(scope="module")
-def stack_3b():
-    """Every 3B-class matrix (26 layers) quantized by the oracle from the
-    seeded device-drawn weights; the GPU packs the same codes (bytes checked)
-    and the oracle keeps its codes for the reference chain."""
-    import ternary_weight_w1_amd as B
-    spec = synth.MODELS["3b"]
-    mats, codes = [], {}
-    for layer in range(spec["layers"]):
-        for j, (name, K, N) in enumerate(spec["shapes"]):
-            W = synth.weights_torch(N, K, spec["sigma"], synth.matrix_seed(layer, j), "cuda")
-            T, g = O.quantize_weights(host(W))
-            Tg, gg = B.quantize_weights(W, gamma_in=gamma_dev(g))
-            del W
-            Pg = B.pack(Tg)
-            del Tg
-            np.testing.assert_array_equal(host(Pg), O.pack(T), err_msg=f"packed bytes layer {layer} {name}")
-            codes[(layer, name)] = (T, np.float32(g))
-            mats.append(dict(layer=layer, name=name, K=K, N=N, P=Pg, P5=None, gamma=gg))
-    torch.cuda.synchronize()
-    return B, mats, codes, spec["layers"]
-
-
 @pytest.mark.parametrize("M", [1, 8])
-def test_bench_chained_3b_stack(stack_3b, M):
+def test_bench_chained_3b_stack(M):
     # bench.py's chained stack (the latency curve it reports): 26 pre-norm
     # blocks, q|k|v and gate|up each in one multi-matrix launch, every
     # workspace reused by all 26 layers; the final residual stream and its
     # final norm's int8 cast must equal the oracle's chain bit for bit.
     import ctypes
-    B, mats, codes, n_layers = stack_3b
+    B, mats, _, codes = _stack("3b")
+    n_layers = synth.MODELS["3b"]["layers"]
     print(f"chained 3B stack, {n_layers} layers, M={M}", flush=True)
     dim = next(m["K"] for m in mats if m["name"] == "q")
     x0, gains, g_fin = bench.stack_inputs(torch, dim, n_layers, M, torch.device("cuda:0"))
