@@ -62,7 +62,7 @@ int check_mnk(int64_t M, int64_t N, int64_t K)
 
 // Tuning knobs, read once from the environment (immutable afterwards).
 struct Knobs {
-    int dot4_max_m = 1;          // M <= this takes the packed-dot4 kernel
+    int dot4_max_m = 2;          // M <= this takes a packed-dot4 kernel (knob: 0..4)
     int dot4_variant = 3;        // 0: global activations, 2/3: LDS-staged (unroll 4/8), 5: table lookup
     int fuse_quant = 0;          // single-token problems quantize in the dot4 prologue
     int split_target = 1024;     // aim for at least this many workgroups
@@ -73,7 +73,8 @@ const Knobs &knobs()
 {
     static const Knobs k = [] {
         Knobs v;
-        if (const char *s = getenv("BITLINEAR_DOT4_MAX_M")) v.dot4_max_m = atoi(s) > 0 ? 1 : 0;
+        if (const char *s = getenv("BITLINEAR_DOT4_MAX_M"))
+            v.dot4_max_m = atoi(s) < 0 ? 0 : (atoi(s) > bl::kDot4MaxTokens ? bl::kDot4MaxTokens : atoi(s));
         if (const char *s = getenv("BITLINEAR_SPLIT_TARGET")) v.split_target = atoi(s) > 0 ? atoi(s) : 1;
         if (const char *s = getenv("BITLINEAR_DOT4_VARIANT"))
             v.dot4_variant = (atoi(s) == 0 || atoi(s) == 2 || atoi(s) == 5) ? atoi(s) : 3;
@@ -110,7 +111,11 @@ bool tile_frag(int variant) { return variant >= 5 && variant <= 7; }
 // The table-lookup dot4 variant (knob value 5) runs single-token problems
 // with at most kLutMaxUnits units (64 KiB of table) per workgroup.
 constexpr int kLutMaxUnits = 64;
-bool lut_variant(int64_t M) { return knobs().dot4_variant == 5 && M <= knobs().dot4_max_m; }
+bool lut_variant(int64_t M) { return knobs().dot4_variant == 5 && M == 1 && knobs().dot4_max_m >= 1; }
+// The dot4 kernel for 2..4 tokens stages 64 bytes per token slot per unit:
+// at most kDot4TokMaxUnits units (64 KiB) per workgroup.
+constexpr int kDot4TokMaxUnits = 64 * 1024 / (64 * bl::kDot4MaxTokens);
+bool dot4_tokens(int64_t M) { return M >= 2 && M <= knobs().dot4_max_m; }
 
 // Kernel kind and decomposition of one problem.  `base_items` is the number
 // of streaming work items the whole launch has without K splits; splits are
@@ -143,10 +148,15 @@ void decompose(Problem &p, int64_t base_items, bool own_q, bool groups4 = false)
             p.upsplit = (int32_t)upsplit;
             p.ks = (int32_t)((p.KU + upsplit - 1) / upsplit);
         }
-        // the table-lookup variant holds 1 KiB of table per unit in LDS
+        // the table-lookup variant holds 1 KiB of table per unit in LDS, the
+        // 2..4-token dot4 kernel 256 bytes of activations
         if (lut_variant(p.M) && p.upsplit > kLutMaxUnits) {
             p.upsplit = kLutMaxUnits;
             p.ks = (p.KU + kLutMaxUnits - 1) / kLutMaxUnits;
+        }
+        if (dot4_tokens(p.M) && p.upsplit > kDot4TokMaxUnits) {
+            p.upsplit = kDot4TokMaxUnits;
+            p.ks = (p.KU + kDot4TokMaxUnits - 1) / kDot4TokMaxUnits;
         }
     } else {
         p.kind = 1;
@@ -217,11 +227,23 @@ constexpr int kStreamLdsMax = 64 * 1024;
 int stream_variant_for(int64_t M, int64_t upsplit)
 {
     if (M > knobs().dot4_max_m) return 1;
+    if (M >= 2) return (int)(4 + M);  // 6, 7, 8; decompose keeps upsplit <= kDot4TokMaxUnits
     const int v = knobs().dot4_variant;
     if (v == 5) return upsplit <= kLutMaxUnits ? 5 : 3;
     return (v != 0 && 64 * upsplit <= kStreamLdsMax) ? v : 0;
 }
 
+
+// Dynamic LDS of a streaming-kernel launch whose workgroups take at most
+// max_upsplit units: activations (64 bytes per unit, per token slot for
+// variants 6..8, which have variant - 4 slots) or the lookup table (1 KiB per
+// unit); none for 0 and 1.
+int stream_lds_bytes(int variant, int64_t max_upsplit)
+{
+    if (variant < 2) return 0;
+    const int64_t per_unit = variant == 5 ? 1024 : variant >= 6 ? 64 * (int64_t)(variant - 4) : 64;
+    return (int)(per_unit * max_upsplit);
+}
 
 // Workspace layout of one problem: [Q][absmax][rowsum][partials][tickets],
 // each region 256-byte aligned.  with_act = false leaves out the first three.
@@ -700,7 +722,7 @@ int multi_plan(const int8_t *Q, int64_t ldq, int64_t M, int64_t K, const bitline
     mp.kind = mp.ps.p[0].kind;
     if (mp.kind == 0) {
         mp.variant = stream_variant_for(M, max_upsplit);
-        mp.lds = mp.variant >= 2 ? (int)((mp.variant == 5 ? 1024 : 64) * max_upsplit) : 0;
+        mp.lds = stream_lds_bytes(mp.variant, max_upsplit);
     } else if (mp.kind == 1) {
         mp.variant = tile_variant(false);
     }
@@ -826,20 +848,32 @@ int build_group(const bitlinear_problem *in, int count, char *ws, GroupPlan &out
     if (base5 < 1) base5 = 1;
     int64_t tokens = 0, items_s = 0, items_t = 0, items_5 = 0, off = 0;
     // streaming instantiation for the whole launch: LDS-staged dot4 when every
-    // streaming problem has a single token (fused with the quantization when
-    // none of them splits K), MFMA otherwise
-    bool all_m1 = true, any_split = false;
-    int64_t max_upsplit = 0;
+    // streaming problem has at most dot4_max_m tokens (the one-token kernel,
+    // fused with the quantization when none of them splits K, if all have
+    // one), MFMA otherwise
+    bool any_split = false;
+    int64_t max_upsplit = 0, max_m = 1, tok_units = 0, one_units = 0;
     for (int i = 0; i < count; ++i) {
         if (in[i].format == BITLINEAR_FORMAT_BT5) continue;
         Problem p = make_problem(in[i].M, in[i].N, in[i].K);
         decompose(p, base_items, true);
         if (p.kind != 0) continue;
-        all_m1 = all_m1 && p.M <= knobs().dot4_max_m;
+        max_m = max_m > p.M ? max_m : p.M;
         any_split = any_split || p.ks > 1;
         max_upsplit = max_upsplit > p.upsplit ? max_upsplit : p.upsplit;
+        // the token-loop variants stage every problem's K range with as
+        // many slots per unit as the launch's largest token count (a
+        // one-token problem keeps one slot; its upsplit is not capped)
+        tok_units = tok_units > (p.M >= 2 ? p.upsplit : 0) ? tok_units : (p.M >= 2 ? p.upsplit : 0);
+        one_units = one_units > (p.M == 1 ? p.upsplit : 0) ? one_units : (p.M == 1 ? p.upsplit : 0);
     }
-    int stream_variant = all_m1 ? stream_variant_for(1, max_upsplit) : 1;
+    int stream_variant = stream_variant_for(max_m, max_upsplit);
+    int64_t lds6 = 0;
+    if (stream_variant >= 6) {
+        const int64_t a = stream_lds_bytes(stream_variant, tok_units), b = 64 * one_units;
+        lds6 = a > b ? a : b;
+        if (lds6 > kStreamLdsMax) stream_variant = 1;
+    }
     if (stream_variant == 3 && knobs().fuse_quant && !any_split) stream_variant = 4;
     const bool groups4 = stream_variant == 1;
     if (groups4) {
@@ -914,7 +948,7 @@ int build_group(const bitlinear_problem *in, int count, char *ws, GroupPlan &out
     h.n_items_bt5 = (int32_t)items_5;
     h.bt5_max_m = (int32_t)(max_m5 < bl::kBt5Tokens ? max_m5 : bl::kBt5Tokens);
     h.stream_variant = stream_variant;
-    h.stream_lds = h.stream_variant >= 2 ? (int32_t)((h.stream_variant == 5 ? 1024 : 64) * max_upsplit) : 0;
+    h.stream_lds = h.stream_variant >= 6 ? (int32_t)lds6 : stream_lds_bytes(h.stream_variant, max_upsplit);
     h.tile_variant = tile_variant(true);
     h.ws_bytes = off;
     int64_t t = up(sizeof(bl::GroupHeader), 16);

@@ -47,6 +47,9 @@ constexpr int kStreamMaxTokens = 32;
 constexpr int kStreamMfmaTiles = 2;
 // token counts above which that kernel reads fragment-ordered activations
 constexpr int kStreamFragTokens = 16;
+// most tokens the packed-dot4 streaming kernel takes (64 LDS bytes per token
+// per unit of the workgroup's K range)
+constexpr int kDot4MaxTokens = 4;
 
 // Everything the contraction kernels need to know about one BitLinear
 // problem.  Single calls pass one of these by value; the grouped path keeps

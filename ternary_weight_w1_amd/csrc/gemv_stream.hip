@@ -285,6 +285,104 @@ __device__ void stream_dot4(const Problem &p, int local)
     if (ok[0]) finish(n, sum[0], gamma);
 }
 
+// 1..4 tokens (dot4): the four planes of a packed word are unpacked once
+// and serve every token, so each token costs 4 dot products per 16 codes on
+// top of the 7 shared bit operations.  The K range's activations are staged
+// once per workgroup in LDS, unit by unit and token by token within a unit
+// (64 bytes per token per unit: ((u - u0) * MT + m) * 64), so the reads of
+// one unit are broadcast reads as in the one-token kernel.  Split K, the
+// cross-wave sum and the epilogue work as there, with one row of partials
+// per token; workgroup thread t finishes token t / 64, row t % 64.
+template <int UNROLL, int MT>
+__device__ __forceinline__ void stream_dot4_tokens(const Problem &p, int local)
+{
+    static_assert(MT >= 1 && MT * 64 <= kThreads, "one epilogue thread per (token, row)");
+    __shared__ int red[kWaves][MT][64];
+    const int tile = local / p.ks, split = local - tile * p.ks;
+    const int u0 = split * p.upsplit;
+    const int u1 = min(p.KU, u0 + p.upsplit);
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 5;
+    const BL_GLOBAL v4u *blk = gload_ptr<v4u>(p.P + (int64_t)tile * p.KU * kBlockBytes) + lane;
+    {
+        // 16-byte chunk i of the staged range: chunk c = i % 4 of token
+        // m = (i / 4) % MT in unit u0 + i / (4 MT); rows p.M .. MT-1 are zero
+        const BL_GLOBAL int8_t *q = gload_ptr<int8_t>(p.Q);
+        v4i *dst = reinterpret_cast<v4i *>(stream_q_lds);
+        const v4i zero = {0, 0, 0, 0};
+        for (int i = threadIdx.x; i < 4 * MT * (u1 - u0); i += kThreads) {
+            const int c = i & 3, m = (i >> 2) % MT, uu = (i >> 2) / MT;
+            dst[i] = m < p.M ? *reinterpret_cast<const BL_GLOBAL v4i *>(q + (int64_t)m * p.ldq + 64 * (u0 + uu) + 16 * c)
+                             : zero;
+        }
+        __syncthreads();
+    }
+    int acc0[MT], acc1[MT];  // rows r and 32 + r of the tile, per token
+#pragma unroll
+    for (int m = 0; m < MT; ++m) acc0[m] = acc1[m] = 0;
+    auto dot4x4 = [](v4i pl, v4i q, int acc) {
+        acc = __builtin_amdgcn_sdot4(pl.x, q.x, acc, false);
+        acc = __builtin_amdgcn_sdot4(pl.y, q.y, acc, false);
+        acc = __builtin_amdgcn_sdot4(pl.z, q.z, acc, false);
+        acc = __builtin_amdgcn_sdot4(pl.w, q.w, acc, false);
+        return acc;
+    };
+    // words (s, h): x = (0, 0), y = (0, 1), z = (1, 0), w = (1, 1)
+    auto unit = [&](v4u w, int u) {
+        const v4i px = planes(w.x), py = planes(w.y), pz = planes(w.z), pw = planes(w.w);
+        const int8_t *qu = stream_q_lds + (u - u0) * MT * 64 + 16 * g;
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            const v4i qa = *reinterpret_cast<const v4i *>(qu + 64 * m);
+            const v4i qb = *reinterpret_cast<const v4i *>(qu + 64 * m + 32);
+            acc0[m] = dot4x4(py, qb, dot4x4(px, qa, acc0[m]));
+            acc1[m] = dot4x4(pw, qb, dot4x4(pz, qa, acc1[m]));
+        }
+    };
+    int u = u0 + wave;
+    for (; u + kWaves * (UNROLL - 1) < u1; u += kWaves * UNROLL) {
+        v4u w[UNROLL];
+#pragma unroll
+        for (int j = 0; j < UNROLL; ++j) w[j] = load_packed(blk + (int64_t)(u + kWaves * j) * 64);
+#pragma unroll
+        for (int j = 0; j < UNROLL; ++j) unit(w[j], u + kWaves * j);
+    }
+    for (; u < u1; u += kWaves) unit(load_packed(blk + (int64_t)u * 64), u);
+    // lanes r and r + 32 hold the two code chunks of the same rows
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+        acc0[m] += __shfl_xor(acc0[m], 32, 64);
+        acc1[m] += __shfl_xor(acc1[m], 32, 64);
+    }
+    if (lane < 32) {
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            red[wave][m][lane] = acc0[m];
+            red[wave][m][32 + lane] = acc1[m];
+        }
+    }
+    __syncthreads();
+
+    const int t = threadIdx.x;
+    const int m = t >> 6, row = t & 63;
+    const int n = 64 * tile + row;
+    const bool mine = t < 64 * MT && m < p.M;
+    const float gamma = *p.gamma;
+    int total = 0;
+    if (mine) total = red[0][m][row] + red[1][m][row] + red[2][m][row] + red[3][m][row];
+    if (p.ks == 1) {
+        if (mine && n < p.N) finish_output(p, gamma, m, n, total);
+        return;
+    }
+    const int64_t ldp = (int64_t)p.NT * 64;  // partial row stride
+    if (mine) put_partial(p.acc_ws + (((int64_t)split * p.M + m) * ldp + n), total);
+    if (!arrive_last(p, tile)) return;
+    const int64_t off[1] = {(int64_t)m * ldp + n};
+    const bool ok[1] = {mine && n < p.N};
+    int32_t sum[1];
+    sum_partials<1>(p.acc_ws, off, ok, (int64_t)p.M * ldp, p.ks, sum);
+    if (ok[0]) finish_output(p, gamma, m, n, sum[0]);
+}
+
 // 2..32 tokens: the same packed stream feeds v_mfma_i32_32x32x32_i8 with the
 // token rows as the A operand.  A workgroup covers 4 * kStreamMfmaTiles
 // 64-row tiles over one K range: each wave owns kStreamMfmaTiles tiles and
@@ -434,11 +532,19 @@ __device__ void stream_mfma(const Problem &p, int local)
 // workgroup); 2: dot4 with
 // LDS-staged activations; 3: as 2 with 8 units in flight per wave; 4: as 3
 // with the activation quantization fused into the prologue; 5: the
-// table-lookup comparison variant (one token).
+// table-lookup comparison variant (one token); 6, 7, 8: the dot4 token-loop
+// kernel with V - 4 token slots per unit, for launches whose problems have
+// at most V - 4 tokens (one-token problems take the one-slot loop, whose
+// LDS layout and stream are those of 3).
 template <int V>
 __device__ inline void stream_body(const Problem &p, int local)
 {
-    if constexpr (V == 0)
+    if constexpr (V >= 6 && V <= 8) {
+        if (p.M == 1)
+            stream_dot4_tokens<8, 1>(p, local);
+        else
+            stream_dot4_tokens<8, V - 4>(p, local);
+    } else if constexpr (V == 0)
         stream_dot4<4, false>(p, local);
     else if constexpr (V == 1)
         stream_mfma<2>(p, local);
@@ -485,6 +591,9 @@ hipError_t launch_stream_multi(const ProblemSet &ps, int variant, int lds_bytes,
     case 1: hipLaunchKernelGGL(stream_multi_kernel<1>, grid, block, 0, s, ps); break;
     case 2: hipLaunchKernelGGL(stream_multi_kernel<2>, grid, block, lds, s, ps); break;
     case 5: hipLaunchKernelGGL(stream_multi_kernel<5>, grid, block, lds, s, ps); break;
+    case 6: hipLaunchKernelGGL(stream_multi_kernel<6>, grid, block, lds, s, ps); break;
+    case 7: hipLaunchKernelGGL(stream_multi_kernel<7>, grid, block, lds, s, ps); break;
+    case 8: hipLaunchKernelGGL(stream_multi_kernel<8>, grid, block, lds, s, ps); break;
     default: hipLaunchKernelGGL(stream_multi_kernel<3>, grid, block, lds, s, ps); break;
     }
     return hipGetLastError();
@@ -495,13 +604,17 @@ hipError_t launch_stream_single(const Problem &p, int variant, hipStream_t s)
     // the MFMA variant's work items are tile groups (p.ntt of them)
     const int64_t tiles = variant == 1 ? (int64_t)p.ntt : (int64_t)p.NT;
     const dim3 grid((unsigned)(tiles * p.ks)), block(kThreads);
-    const unsigned lds = variant >= 2 ? (variant == 5 ? kLutUnitBytes : 64u) * (unsigned)p.upsplit : 0u;
+    const unsigned slot = variant >= 6 ? 64u * (unsigned)(variant - 4) : 64u;
+    const unsigned lds = variant >= 2 ? (variant == 5 ? kLutUnitBytes : slot) * (unsigned)p.upsplit : 0u;
     switch (variant) {
     case 0: hipLaunchKernelGGL(stream_single_kernel<0>, grid, block, 0, s, p); break;
     case 1: hipLaunchKernelGGL(stream_single_kernel<1>, grid, block, 0, s, p); break;
     case 2: hipLaunchKernelGGL(stream_single_kernel<2>, grid, block, lds, s, p); break;
     case 3: hipLaunchKernelGGL(stream_single_kernel<3>, grid, block, lds, s, p); break;
     case 5: hipLaunchKernelGGL(stream_single_kernel<5>, grid, block, lds, s, p); break;
+    case 6: hipLaunchKernelGGL(stream_single_kernel<6>, grid, block, lds, s, p); break;
+    case 7: hipLaunchKernelGGL(stream_single_kernel<7>, grid, block, lds, s, p); break;
+    case 8: hipLaunchKernelGGL(stream_single_kernel<8>, grid, block, lds, s, p); break;
     default: hipLaunchKernelGGL(stream_single_kernel<4>, grid, block, lds, s, p); break;
     }
     return hipGetLastError();
@@ -518,6 +631,9 @@ hipError_t launch_stream_group(const Problem *probs, const uint2 *item_map, int 
     case 2: hipLaunchKernelGGL(stream_group_kernel<2>, grid, block, lds, s, probs, item_map); break;
     case 3: hipLaunchKernelGGL(stream_group_kernel<3>, grid, block, lds, s, probs, item_map); break;
     case 5: hipLaunchKernelGGL(stream_group_kernel<5>, grid, block, lds, s, probs, item_map); break;
+    case 6: hipLaunchKernelGGL(stream_group_kernel<6>, grid, block, lds, s, probs, item_map); break;
+    case 7: hipLaunchKernelGGL(stream_group_kernel<7>, grid, block, lds, s, probs, item_map); break;
+    case 8: hipLaunchKernelGGL(stream_group_kernel<8>, grid, block, lds, s, probs, item_map); break;
     default: hipLaunchKernelGGL(stream_group_kernel<4>, grid, block, lds, s, probs, item_map); break;
     }
     return hipGetLastError();

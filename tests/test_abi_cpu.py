@@ -185,7 +185,10 @@ def test_group_plan_single_token_quantization():
     # token goes to the quantization kernel and the dot4 kernel reads LDS-
     # staged activations (3), or -- with BITLINEAR_FUSE_QUANT=1 -- the dot4
     # kernel quantizes in its prologue (4) and no token is left over; a
-    # 2-token problem switches the streaming kernel to MFMA (1)
+    # 2-token problem switches the streaming kernel to the two-slot dot4
+    # token-loop kernel (6), whose LDS holds 64 bytes per unit for one-token
+    # problems and 128 for two-token ones; a 5-token problem switches it to
+    # MFMA (1)
     L = B.lib()
     fused = os.environ.get("BITLINEAR_FUSE_QUANT", "0") not in ("", "0")
     specs = [(1, 4096, 256)] * 16
@@ -203,7 +206,24 @@ def test_group_plan_single_token_quantization():
     wsb2 = L.bitlinear_group_workspace_bytes(arr2, 17)
     assert L.bitlinear_group_plan(arr2, 17, FAKE, wsb2, host2.ctypes.data, tb2) == 0
     hdr2 = np.frombuffer(host2[:48].tobytes(), np.int32)
-    assert hdr2[2] == 18 and hdr2[7] == 1
+    assert hdr2[2] == 18 and hdr2[7] == 6
+    assert hdr2[9] == max(64 * 4, 128 * 1)  # K = 256: 4 units; K = 64: 1 unit
+    arr3 = _problems(specs + [(5, 64, 64)])
+    tb3 = L.bitlinear_group_table_bytes(arr3, 17)
+    host3 = np.zeros(tb3, np.uint8)
+    wsb3 = L.bitlinear_group_workspace_bytes(arr3, 17)
+    assert L.bitlinear_group_plan(arr3, 17, FAKE, wsb3, host3.ctypes.data, tb3) == 0
+    hdr3 = np.frombuffer(host3[:48].tobytes(), np.int32)
+    assert hdr3[2] == 21 and hdr3[7] == 1 and hdr3[9] == 0
+    # a one-token problem whose unsplit K range (1250 units) needs more than
+    # 64 KiB of staged activations keeps a 2-token launch off variant 6
+    arr4 = _problems(specs + [(1, 64, 80000), (2, 64, 64)])
+    tb4 = L.bitlinear_group_table_bytes(arr4, 18)
+    host4 = np.zeros(tb4, np.uint8)
+    wsb4 = L.bitlinear_group_workspace_bytes(arr4, 18)
+    assert L.bitlinear_group_plan(arr4, 18, FAKE, wsb4, host4.ctypes.data, tb4) == 0
+    hdr4 = np.frombuffer(host4[:48].tobytes(), np.int32)
+    assert hdr4[7] == 1 and hdr4[9] == 0
 
 
 def test_group_calls_reject_foreign_tables():

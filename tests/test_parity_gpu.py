@@ -383,10 +383,11 @@ def test_pack_golden_single_codes(B):
 # ---------------------------------------------------------- contraction ------
 
 MM_CASES = [
-    # (M, N, K): dot4 (M=1), streaming MFMA (2..32), tile MFMA (33 and up);
-    # ragged N and K tails throughout
+    # (M, N, K): dot4 (M = 1, and 2 with the token loop), streaming MFMA
+    # (3..32), tile MFMA (33 and up); ragged N and K tails throughout
     (1, 64, 64), (1, 100, 200), (1, 257, 640), (1, 640, 2560),
-    (2, 64, 64), (3, 100, 200), (8, 257, 640), (17, 640, 2560), (32, 130, 1000),
+    (2, 64, 64), (3, 100, 200), (2, 640, 2560), (3, 257, 6912), (4, 130, 1000), (4, 6912, 2560),
+    (5, 100, 200), (8, 257, 640), (17, 640, 2560), (32, 130, 1000),
     (33, 64, 64), (40, 100, 200), (64, 257, 640), (65, 130, 1000), (128, 640, 2560),
     (176, 300, 700), (200, 513, 129), (512, 256, 256),
 ]
@@ -719,7 +720,8 @@ print("knob ok")
 """
 
 KNOB_SETTINGS = [
-    ("BITLINEAR_DOT4_MAX_M", "0"), ("BITLINEAR_DOT4_VARIANT", "0"), ("BITLINEAR_DOT4_VARIANT", "2"),
+    ("BITLINEAR_DOT4_MAX_M", "0"), ("BITLINEAR_DOT4_MAX_M", "1"), ("BITLINEAR_DOT4_MAX_M", "4"),
+    ("BITLINEAR_DOT4_VARIANT", "0"), ("BITLINEAR_DOT4_VARIANT", "2"),
     ("BITLINEAR_SPLIT_TARGET", "1"), ("BITLINEAR_SPLIT_TARGET", "100000"), ("BITLINEAR_XCD_ORDER", "0"),
 ] + [("BITLINEAR_TILE_VARIANT", str(v)) for v in (0, 1, 2, 5, 6, 7, 10, 11, 12, 18)]
 
@@ -736,6 +738,13 @@ def test_knob_variants_subprocess(B, knob, value):
     r = subprocess.run([sys.executable, "-c", KNOB_SCRIPT], env=env, capture_output=True, text=True,
                        timeout=110)
     assert r.returncode == 0 and "knob ok" in r.stdout, r.stdout + r.stderr
+
+
+def test_group_dot4_token_counts(B):
+    # one and two tokens per problem: the whole launch takes the two-slot dot4
+    # token-loop kernel (variant 6), K split for the short problems
+    say("group M=1..2")
+    _group_run(B, [(1, 640, 2560), (2, 100, 200), (2, 2560, 640), (1, 64, 64), (2, 130, 6912), (2, 257, 37)], 700)
 
 
 def test_group_mixed(B):
