@@ -116,6 +116,9 @@ bool lut_variant(int64_t M) { return knobs().dot4_variant == 5 && M == 1 && knob
 // at most kDot4TokMaxUnits units (64 KiB) per workgroup.
 constexpr int kDot4TokMaxUnits = 64 * 1024 / (64 * bl::kDot4MaxTokens);
 bool dot4_tokens(int64_t M) { return M >= 2 && M <= knobs().dot4_max_m; }
+// Token counts the 32x32x32 MFMA stream takes (its work items are groups of
+// kGroupTiles row tiles; the dot4 kernels work per tile).
+bool mfma32_stream(int64_t M) { return M <= kStreamMaxM && M > knobs().dot4_max_m; }
 
 // Kernel kind and decomposition of one problem.  `base_items` is the number
 // of streaming work items the whole launch has without K splits; splits are
@@ -217,7 +220,7 @@ int64_t own_ldq(const Problem &p) { return p.fmt ? 160 * (int64_t)p.KU5 : 64 * (
 void decompose_single(Problem &p, bool own_q)
 {
     const int64_t nt = (p.N + 63) / 64;
-    const bool g4 = p.M <= kStreamMaxM && p.M > knobs().dot4_max_m;
+    const bool g4 = mfma32_stream(p.M);
     decompose(p, g4 ? (nt + kGroupTiles - 1) / kGroupTiles : nt, own_q, g4);
 }
 
@@ -234,15 +237,18 @@ int stream_variant_for(int64_t M, int64_t upsplit)
 }
 
 
-// Dynamic LDS of a streaming-kernel launch whose workgroups take at most
-// max_upsplit units: activations (64 bytes per unit, per token slot for
-// variants 6..8, which have variant - 4 slots) or the lookup table (1 KiB per
-// unit); none for 0 and 1.
-int stream_lds_bytes(int variant, int64_t max_upsplit)
+// Dynamic LDS a problem of M tokens whose workgroups take upsplit units
+// needs under a streaming-kernel variant: activations, 64 bytes per token
+// slot per unit (one slot for 2..4; variant - 4 slots for 6..8, whose
+// one-token problems take one), or the lookup table (1 KiB per unit, 5);
+// none for 0 and 1.
+int64_t stream_lds_need(int variant, int64_t M, int64_t upsplit)
 {
+    int64_t slots = 1;
     if (variant < 2) return 0;
-    const int64_t per_unit = variant == 5 ? 1024 : variant >= 6 ? 64 * (int64_t)(variant - 4) : 64;
-    return (int)(per_unit * max_upsplit);
+    if (variant == 5) return 1024 * upsplit;
+    if (variant >= 6 && variant <= 8) slots = M == 1 ? 1 : variant - 4;
+    return 64 * slots * upsplit;
 }
 
 // Workspace layout of one problem: [Q][absmax][rowsum][partials][tickets],
@@ -688,7 +694,7 @@ int multi_plan(const int8_t *Q, int64_t ldq, int64_t M, int64_t K, const bitline
     memset(&mp.ps, 0, sizeof mp.ps);
     // decomposition over the whole launch: K is split only while all the
     // problems together are short of workgroups
-    const bool g4 = !fmt && M <= kStreamMaxM && M > knobs().dot4_max_m;
+    const bool g4 = !fmt && mfma32_stream(M);
     int64_t base = 0, max_upsplit = 0;
     for (int i = 0; i < count; ++i) {
         const int64_t nt = (w[i].N + 63) / 64;
@@ -722,7 +728,7 @@ int multi_plan(const int8_t *Q, int64_t ldq, int64_t M, int64_t K, const bitline
     mp.kind = mp.ps.p[0].kind;
     if (mp.kind == 0) {
         mp.variant = stream_variant_for(M, max_upsplit);
-        mp.lds = stream_lds_bytes(mp.variant, max_upsplit);
+        mp.lds = (int)stream_lds_need(mp.variant, M, max_upsplit);
     } else if (mp.kind == 1) {
         mp.variant = tile_variant(false);
     }
@@ -852,7 +858,8 @@ int build_group(const bitlinear_problem *in, int count, char *ws, GroupPlan &out
     // fused with the quantization when none of them splits K, if all have
     // one), MFMA otherwise
     bool any_split = false;
-    int64_t max_upsplit = 0, max_m = 1, tok_units = 0, one_units = 0;
+    int64_t max_upsplit = 0, max_m = 1;
+    std::vector<std::pair<int64_t, int64_t>> mu;  // (M, upsplit) of the streaming problems
     for (int i = 0; i < count; ++i) {
         if (in[i].format == BITLINEAR_FORMAT_BT5) continue;
         Problem p = make_problem(in[i].M, in[i].N, in[i].K);
@@ -861,18 +868,20 @@ int build_group(const bitlinear_problem *in, int count, char *ws, GroupPlan &out
         max_m = max_m > p.M ? max_m : p.M;
         any_split = any_split || p.ks > 1;
         max_upsplit = max_upsplit > p.upsplit ? max_upsplit : p.upsplit;
-        // the token-loop variants stage every problem's K range with as
-        // many slots per unit as the launch's largest token count (a
-        // one-token problem keeps one slot; its upsplit is not capped)
-        tok_units = tok_units > (p.M >= 2 ? p.upsplit : 0) ? tok_units : (p.M >= 2 ? p.upsplit : 0);
-        one_units = one_units > (p.M == 1 ? p.upsplit : 0) ? one_units : (p.M == 1 ? p.upsplit : 0);
+        mu.emplace_back(p.M, p.upsplit);
     }
+    // one instantiation for the launch, from its largest token count; the
+    // staged-activation variants size their LDS for every problem (a
+    // one-token problem's K range is not capped) and give way to the MFMA
+    // stream when that exceeds 64 KiB
     int stream_variant = stream_variant_for(max_m, max_upsplit);
-    int64_t lds6 = 0;
+    int64_t lds_tok = 0;
     if (stream_variant >= 6) {
-        const int64_t a = stream_lds_bytes(stream_variant, tok_units), b = 64 * one_units;
-        lds6 = a > b ? a : b;
-        if (lds6 > kStreamLdsMax) stream_variant = 1;
+        for (const auto &x : mu) {
+            const int64_t b = stream_lds_need(stream_variant, x.first, x.second);
+            lds_tok = lds_tok > b ? lds_tok : b;
+        }
+        if (lds_tok > kStreamLdsMax) stream_variant = 1;
     }
     if (stream_variant == 3 && knobs().fuse_quant && !any_split) stream_variant = 4;
     const bool groups4 = stream_variant == 1;
@@ -948,7 +957,7 @@ int build_group(const bitlinear_problem *in, int count, char *ws, GroupPlan &out
     h.n_items_bt5 = (int32_t)items_5;
     h.bt5_max_m = (int32_t)(max_m5 < bl::kBt5Tokens ? max_m5 : bl::kBt5Tokens);
     h.stream_variant = stream_variant;
-    h.stream_lds = h.stream_variant >= 6 ? (int32_t)lds6 : stream_lds_bytes(h.stream_variant, max_upsplit);
+    h.stream_lds = h.stream_variant >= 6 ? (int32_t)lds_tok : (int32_t)stream_lds_need(h.stream_variant, 1, max_upsplit);
     h.tile_variant = tile_variant(true);
     h.ws_bytes = off;
     int64_t t = up(sizeof(bl::GroupHeader), 16);

@@ -52,6 +52,52 @@ __device__ inline int dot16(unsigned w, v4i q, int acc)
 // the dot4 kernel runs with QLDS (dynamic LDS, 64 bytes per unit).
 extern __shared__ __attribute__((aligned(16))) int8_t stream_q_lds[];
 
+// Copies n 16-byte chunks into the staged activations, chunk i from src(i):
+// each thread issues up to eight loads before its first LDS store, so a
+// workgroup's staging costs one memory round trip per 8 * 256 chunks
+// rather than one per 256.
+template <typename Src>
+__device__ __forceinline__ void stage_chunks(int n, Src src)
+{
+    v4i *dst = reinterpret_cast<v4i *>(stream_q_lds);
+    for (int base = threadIdx.x; base < n; base += 8 * kThreads) {
+        v4i v[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            if (base + k * kThreads < n) v[k] = src(base + k * kThreads);
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            if (base + k * kThreads < n) dst[base + k * kThreads] = v[k];
+    }
+}
+
+// Stages units [u0, u1) of the first M token rows of Q (row stride ldq) with
+// MT slots per unit: slot m of unit u0 + uu at byte (uu * MT + m) * 64,
+// slots M .. MT-1 zero.  Thread t always copies chunk t % 4 of slot
+// (t / 4) % MT, for every (256 / (4 MT))-th unit, with up to eight loads in
+// flight before its first LDS store.
+template <int MT>
+__device__ __forceinline__ void stage_token_slots(const Problem &p, int u0, int u1)
+{
+    static_assert(MT >= 1 && 4 * MT <= kThreads, "one pass covers at least one unit");
+    constexpr int kPer = kThreads / (4 * MT);  // units per pass
+    const int t = threadIdx.x, ch = t & 3, m = (t >> 2) % MT, uo = t / (4 * MT);
+    const bool live = m < p.M && uo < kPer;
+    const BL_GLOBAL int8_t *src = gload_ptr<int8_t>(p.Q) + (int64_t)(m < p.M ? m : 0) * p.ldq + 64 * u0 + 16 * ch;
+    v4i *dst = reinterpret_cast<v4i *>(stream_q_lds) + m * 4 + ch;
+    const v4i zero = {0, 0, 0, 0};
+    const int nu = u1 - u0;
+    for (int ub = uo; ub < nu; ub += 8 * kPer) {
+        v4i v[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            if (ub + k * kPer < nu) v[k] = live ? *reinterpret_cast<const BL_GLOBAL v4i *>(src + 64 * (ub + k * kPer)) : zero;
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            if (ub + k * kPer < nu && uo < kPer) dst[(ub + k * kPer) * MT * 4] = v[k];
+    }
+}
+
 // Fused prologue (decode, one token): quantize the token's fp32 activations
 // straight into LDS -- absmax over the whole row (block reduction), then
 // the same per-element code as the quantization kernel -- keeping the codes
@@ -188,8 +234,7 @@ __device__ void stream_dot4(const Problem &p, int local)
         __syncthreads();
     } else if constexpr (QLDS) {
         const BL_GLOBAL v4i *src = gload_ptr<v4i>(p.Q + 64 * u0);
-        v4i *dst = reinterpret_cast<v4i *>(stream_q_lds);
-        for (int i = threadIdx.x; i < 4 * (u1 - u0); i += kThreads) dst[i] = src[i];
+        stage_chunks(4 * (u1 - u0), [&](int i) { return src[i]; });
         __syncthreads();
     }
     auto finish = [&](int n, int32_t fields, float gamma) {
@@ -303,19 +348,8 @@ __device__ __forceinline__ void stream_dot4_tokens(const Problem &p, int local)
     const int u1 = min(p.KU, u0 + p.upsplit);
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 5;
     const BL_GLOBAL v4u *blk = gload_ptr<v4u>(p.P + (int64_t)tile * p.KU * kBlockBytes) + lane;
-    {
-        // 16-byte chunk i of the staged range: chunk c = i % 4 of token
-        // m = (i / 4) % MT in unit u0 + i / (4 MT); rows p.M .. MT-1 are zero
-        const BL_GLOBAL int8_t *q = gload_ptr<int8_t>(p.Q);
-        v4i *dst = reinterpret_cast<v4i *>(stream_q_lds);
-        const v4i zero = {0, 0, 0, 0};
-        for (int i = threadIdx.x; i < 4 * MT * (u1 - u0); i += kThreads) {
-            const int c = i & 3, m = (i >> 2) % MT, uu = (i >> 2) / MT;
-            dst[i] = m < p.M ? *reinterpret_cast<const BL_GLOBAL v4i *>(q + (int64_t)m * p.ldq + 64 * (u0 + uu) + 16 * c)
-                             : zero;
-        }
-        __syncthreads();
-    }
+    stage_token_slots<MT>(p, u0, u1);
+    __syncthreads();
     int acc0[MT], acc1[MT];  // rows r and 32 + r of the tile, per token
 #pragma unroll
     for (int m = 0; m < MT; ++m) acc0[m] = acc1[m] = 0;
@@ -346,7 +380,16 @@ __device__ __forceinline__ void stream_dot4_tokens(const Problem &p, int local)
 #pragma unroll
         for (int j = 0; j < UNROLL; ++j) unit(w[j], u + kWaves * j);
     }
-    for (; u < u1; u += kWaves) unit(load_packed(blk + (int64_t)u * 64), u);
+    if (u < u1) {
+        // the last (fewer than UNROLL) units of this wave, loaded together
+        v4u w[UNROLL - 1];
+#pragma unroll
+        for (int j = 0; j < UNROLL - 1; ++j)
+            if (u + kWaves * j < u1) w[j] = load_packed(blk + (int64_t)(u + kWaves * j) * 64);
+#pragma unroll
+        for (int j = 0; j < UNROLL - 1; ++j)
+            if (u + kWaves * j < u1) unit(w[j], u + kWaves * j);
+    }
     // lanes r and r + 32 hold the two code chunks of the same rows
 #pragma unroll
     for (int m = 0; m < MT; ++m) {

@@ -387,7 +387,7 @@ MM_CASES = [
     # (3..32), tile MFMA (33 and up); ragged N and K tails throughout
     (1, 64, 64), (1, 100, 200), (1, 257, 640), (1, 640, 2560),
     (2, 64, 64), (3, 100, 200), (2, 640, 2560), (3, 257, 6912), (4, 130, 1000), (4, 6912, 2560),
-    (5, 100, 200), (8, 257, 640), (17, 640, 2560), (32, 130, 1000),
+    (5, 100, 200), (8, 257, 640), (6, 640, 8640), (9, 100, 200), (17, 640, 2560), (32, 130, 1000),
     (33, 64, 64), (40, 100, 200), (64, 257, 640), (65, 130, 1000), (128, 640, 2560),
     (176, 300, 700), (200, 513, 129), (512, 256, 256),
 ]
@@ -745,6 +745,15 @@ def test_group_dot4_token_counts(B):
     # token-loop kernel (variant 6), K split for the short problems
     say("group M=1..2")
     _group_run(B, [(1, 640, 2560), (2, 100, 200), (2, 2560, 640), (1, 64, 64), (2, 130, 6912), (2, 257, 37)], 700)
+
+
+def test_group_decode_token_counts(B):
+    # one to eight tokens per problem: the launch takes the 32x32x32 MFMA
+    # stream for every problem (its largest token count is past the dot4
+    # kernels); short K ranges split
+    say("group M=1..8")
+    _group_run(B, [(1, 640, 2560), (3, 100, 200), (8, 2560, 640), (5, 64, 64), (2, 130, 6912), (7, 257, 3200),
+                   (4, 64, 37)], 800)
 
 
 def test_group_mixed(B):
