@@ -1,5 +1,6 @@
-// Streaming contraction for small token counts (decode): M = 1 with packed
-// int8 dot products, 2 <= M <= 32 with int8 matrix instructions.
+// Streaming contraction for small token counts (decode): M = 1 and 2 with
+// packed int8 dot products, 3 <= M <= 32 with int8 matrix instructions (the
+// split point is a host-side setting; the dot4 kernels take up to 4 tokens).
 //
 // The pages describe the decode kernel as: weights packed four codes per
 // byte are streamed across the GPU and unpacked next to the math units,
@@ -22,7 +23,8 @@
 //                 with v_dot4c_i32_i8: per 16 codes 7 bit operations + 4
 //                 dot products.  The (t+1) fields make the sum exceed the
 //                 ternary dot product by the activation row sum, which the
-//                 epilogue subtracts once.
+//                 epilogue subtracts once.  With 2..4 tokens the planes are
+//                 unpacked once and serve every token.
 // M <= 32 (mfma): the four planes of a word are exactly one lane's B operand
 //                 of v_mfma_i32_32x32x32_i8 (A = 32 token rows of int8
 //                 activations, zero beyond M), so per 1 KiB unit a wave
@@ -426,8 +428,9 @@ __device__ __forceinline__ void stream_dot4_tokens(const Problem &p, int local)
     if (ok[0]) finish_output(p, gamma, m, n, sum[0]);
 }
 
-// 2..32 tokens: the same packed stream feeds v_mfma_i32_32x32x32_i8 with the
-// token rows as the A operand.  A workgroup covers 4 * kStreamMfmaTiles
+// 3..32 tokens (2..32 when the dot4 kernels are limited to one): the same
+// packed stream feeds v_mfma_i32_32x32x32_i8 with the token rows as the A
+// operand.  A workgroup covers 4 * kStreamMfmaTiles
 // 64-row tiles over one K range: each wave owns kStreamMfmaTiles tiles and
 // every wave walks the same units in the same order, so a wave streams its
 // tiles' blocks contiguously, one activation fragment serves all its tiles,
