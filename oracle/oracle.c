@@ -20,7 +20,7 @@
  *        (michaelmallari.bitbucket.io), "From High-Precision Bloat to Elegant
  *        Bit-Level Efficiency".
  *
- * Readings taken where the pages are silent (each is listed in the design doc):
+ * Readings taken where the pages are silent, numbered R1 .. R17:
  *  R1  absmean scale = mean of |W| over the whole matrix (one scale per
  *      tensor), accumulated in fp64, divided by N*K in fp64, rounded once to
  *      fp32, then floored at 1e-5.
