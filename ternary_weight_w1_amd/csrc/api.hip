@@ -67,6 +67,7 @@ struct Knobs {
     int fuse_quant = 0;          // single-token problems quantize in the dot4 prologue
     int split_target = 1024;     // aim for at least this many workgroups
     int xcd_order = 3;           // bit 0: streaming kernel, bit 1: tile kernel
+    int mfma_tiles = 0;          // tiles per wave of the streaming MFMA kernel: 0 = by launch size, 1, 2
     int tile_variant = -1;       // force a tile-kernel instantiation (see tile_variant())
 };
 const Knobs &knobs()
@@ -80,6 +81,7 @@ const Knobs &knobs()
             v.dot4_variant = (atoi(s) == 0 || atoi(s) == 2 || atoi(s) == 5) ? atoi(s) : 3;
         if (const char *s = getenv("BITLINEAR_FUSE_QUANT")) v.fuse_quant = atoi(s) != 0;
         if (const char *s = getenv("BITLINEAR_XCD_ORDER")) v.xcd_order = atoi(s) & 3;
+        if (const char *s = getenv("BITLINEAR_MFMA_TILES")) v.mfma_tiles = (atoi(s) == 1 || atoi(s) == 2) ? atoi(s) : 0;
         if (const char *s = getenv("BITLINEAR_TILE_VARIANT")) v.tile_variant = atoi(s);
         return v;
     }();
@@ -117,26 +119,35 @@ bool lut_variant(int64_t M) { return knobs().dot4_variant == 5 && M == 1 && knob
 constexpr int kDot4TokMaxUnits = 64 * 1024 / (64 * bl::kDot4MaxTokens);
 bool dot4_tokens(int64_t M) { return M >= 2 && M <= knobs().dot4_max_m; }
 // Token counts the 32x32x32 MFMA stream takes (its work items are groups of
-// kGroupTiles row tiles; the dot4 kernels work per tile).
+// 4 * tiles-per-wave row tiles; the dot4 kernels work per tile).
 bool mfma32_stream(int64_t M) { return M <= kStreamMaxM && M > knobs().dot4_max_m; }
+// Tiles per wave of that stream for a launch with `groups` kGroupTiles-tile
+// groups: two when the groups alone fill the part (the split target), else
+// one, which doubles the workgroups without more split-K reductions.
+int mfma_tiles_for(int64_t groups)
+{
+    if (knobs().mfma_tiles) return knobs().mfma_tiles;
+    return groups < knobs().split_target ? 1 : bl::kStreamMfmaTiles;
+}
 
 // Kernel kind and decomposition of one problem.  `base_items` is the number
 // of streaming work items the whole launch has without K splits; splits are
 // added only while the launch is short of workgroups.  own_q: the library
 // quantizes the activations itself and may choose their layout.  groups4:
 // the launch runs the streaming MFMA kernel, whose work items are groups of
-// kGroupTiles 64-row tiles (p.ntt of them).
-void decompose(Problem &p, int64_t base_items, bool own_q, bool groups4 = false)
+// 4 * tpw 64-row tiles (p.ntt of them).
+void decompose(Problem &p, int64_t base_items, bool own_q, bool groups4 = false, int tpw = bl::kStreamMfmaTiles)
 {
     p.KU = (int32_t)((p.K + 63) / 64);
     p.NT = (int32_t)((p.N + 63) / 64);
     p.ks = 1;
     p.upsplit = p.KU;
-    p.mt = p.ntt = p.mtile = p.qtiled = 0;
+    p.mt = p.ntt = p.mtile = p.qtiled = p.stiles = 0;
     if (p.M <= kStreamMaxM) {
         p.kind = 0;
         if (groups4) {
-            p.ntt = (p.NT + kGroupTiles - 1) / kGroupTiles;
+            p.stiles = tpw;
+            p.ntt = (p.NT + 4 * tpw - 1) / (4 * tpw);
             // past 16 tokens the MFMA kernel reads each A operand as one
             // 1 KiB block when the library lays the activations out itself
             p.qtiled = own_q && p.M > bl::kStreamFragTokens ? 1 : 0;
@@ -221,7 +232,8 @@ void decompose_single(Problem &p, bool own_q)
 {
     const int64_t nt = (p.N + 63) / 64;
     const bool g4 = mfma32_stream(p.M);
-    decompose(p, g4 ? (nt + kGroupTiles - 1) / kGroupTiles : nt, own_q, g4);
+    const int tpw = g4 ? mfma_tiles_for((nt + kGroupTiles - 1) / kGroupTiles) : bl::kStreamMfmaTiles;
+    decompose(p, g4 ? (nt + 4 * tpw - 1) / (4 * tpw) : nt, own_q, g4, tpw);
 }
 
 // The LDS-staged dot4 variants hold 64 bytes of activations per unit of
@@ -245,7 +257,7 @@ int stream_variant_for(int64_t M, int64_t upsplit)
 int64_t stream_lds_need(int variant, int64_t M, int64_t upsplit)
 {
     int64_t slots = 1;
-    if (variant < 2) return 0;
+    if (variant < 2 || variant == 9) return 0;
     if (variant == 5) return 1024 * upsplit;
     if (variant >= 6 && variant <= 8) slots = M == 1 ? 1 : variant - 4;
     return 64 * slots * upsplit;
@@ -301,7 +313,10 @@ Problem make_problem(int64_t M, int64_t N, int64_t K)
 hipError_t launch_contraction(const Problem &p, bool own_q, hipStream_t s)
 {
     if (p.kind == 2) return bl::launch_bt5_single(p, s);
-    if (p.kind == 0) return bl::launch_stream_single(p, stream_variant_for(p.M, p.upsplit), s);
+    if (p.kind == 0) {
+        const int v = stream_variant_for(p.M, p.upsplit);
+        return bl::launch_stream_single(p, v == 1 && p.stiles == 1 ? 9 : v, s);
+    }
     return bl::launch_tile_single(p, tile_variant(own_q), s);
 }
 
@@ -696,11 +711,18 @@ int multi_plan(const int8_t *Q, int64_t ldq, int64_t M, int64_t K, const bitline
     // problems together are short of workgroups
     const bool g4 = !fmt && mfma32_stream(M);
     int64_t base = 0, max_upsplit = 0;
-    for (int i = 0; i < count; ++i) {
-        const int64_t nt = (w[i].N + 63) / 64;
-        base += fmt ? bt5_items(M, w[i].N) : (g4 ? (nt + kGroupTiles - 1) / kGroupTiles : nt);
+    int tpw = bl::kStreamMfmaTiles;
+    for (int pass = 0; pass < (g4 ? 2 : 1); ++pass) {
+        // the MFMA stream's groups: kGroupTiles tiles first, then as many
+        // tiles as the tiles-per-wave choice gives
+        if (pass == 1) tpw = mfma_tiles_for(base);
+        base = 0;
+        for (int i = 0; i < count; ++i) {
+            const int64_t nt = (w[i].N + 63) / 64;
+            base += fmt ? bt5_items(M, w[i].N) : (g4 ? (nt + 4 * tpw - 1) / (4 * tpw) : nt);
+        }
+        if (base < 1) base = 1;
     }
-    if (base < 1) base = 1;
     int64_t items = 0, tick = 0, part = 0;
     for (int i = 0; i < count; ++i) {
         Problem &p = mp.ps.p[i];
@@ -708,7 +730,7 @@ int multi_plan(const int8_t *Q, int64_t ldq, int64_t M, int64_t K, const bitline
         if (fmt)
             decompose5(p, base);
         else
-            decompose(p, base, false, g4);
+            decompose(p, base, false, g4, tpw);
         mp.ps.begin[i] = (int32_t)items;
         items += items_of(p);
         max_upsplit = max_upsplit > p.upsplit ? max_upsplit : p.upsplit;
@@ -728,6 +750,7 @@ int multi_plan(const int8_t *Q, int64_t ldq, int64_t M, int64_t K, const bitline
     mp.kind = mp.ps.p[0].kind;
     if (mp.kind == 0) {
         mp.variant = stream_variant_for(M, max_upsplit);
+        if (mp.variant == 1 && tpw == 1) mp.variant = 9;
         mp.lds = (int)stream_lds_need(mp.variant, M, max_upsplit);
     } else if (mp.kind == 1) {
         mp.variant = tile_variant(false);
@@ -876,7 +899,7 @@ int build_group(const bitlinear_problem *in, int count, char *ws, GroupPlan &out
     // stream when that exceeds 64 KiB
     int stream_variant = stream_variant_for(max_m, max_upsplit);
     int64_t lds_tok = 0;
-    if (stream_variant >= 6) {
+    if (stream_variant >= 6 && stream_variant <= 8) {
         for (const auto &x : mu) {
             const int64_t b = stream_lds_need(stream_variant, x.first, x.second);
             lds_tok = lds_tok > b ? lds_tok : b;
@@ -885,13 +908,19 @@ int build_group(const bitlinear_problem *in, int count, char *ws, GroupPlan &out
     }
     if (stream_variant == 3 && knobs().fuse_quant && !any_split) stream_variant = 4;
     const bool groups4 = stream_variant == 1;
+    int tpw = bl::kStreamMfmaTiles;
     if (groups4) {
-        // the MFMA kernel's work items are tile groups
-        base_items = 0;
-        for (int i = 0; i < count; ++i)
-            if (in[i].format != BITLINEAR_FORMAT_BT5 && in[i].M <= kStreamMaxM)
-                base_items += ((in[i].N + 63) / 64 + kGroupTiles - 1) / kGroupTiles;
-        if (base_items < 1) base_items = 1;
+        // the MFMA kernel's work items are tile groups: kGroupTiles tiles,
+        // or 4 when the launch is too small for two tiles per wave
+        for (int pass = 0; pass < 2; ++pass) {
+            if (pass == 1) tpw = mfma_tiles_for(base_items);
+            base_items = 0;
+            for (int i = 0; i < count; ++i)
+                if (in[i].format != BITLINEAR_FORMAT_BT5 && in[i].M <= kStreamMaxM)
+                    base_items += ((in[i].N + 63) / 64 + 4 * tpw - 1) / (4 * tpw);
+            if (base_items < 1) base_items = 1;
+        }
+        if (tpw == 1) stream_variant = 9;
     }
     for (int i = 0; i < count; ++i) {
         const bitlinear_problem &q = in[i];
@@ -900,7 +929,7 @@ int build_group(const bitlinear_problem *in, int count, char *ws, GroupPlan &out
         if (q.format == BITLINEAR_FORMAT_BT5)
             decompose5(p, base5);
         else
-            decompose(p, base_items, true, groups4);
+            decompose(p, base_items, true, groups4, tpw);
         p.X = q.X;
         p.P = q.P;
         p.gamma = q.gamma;
@@ -957,7 +986,8 @@ int build_group(const bitlinear_problem *in, int count, char *ws, GroupPlan &out
     h.n_items_bt5 = (int32_t)items_5;
     h.bt5_max_m = (int32_t)(max_m5 < bl::kBt5Tokens ? max_m5 : bl::kBt5Tokens);
     h.stream_variant = stream_variant;
-    h.stream_lds = h.stream_variant >= 6 ? (int32_t)lds_tok : (int32_t)stream_lds_need(h.stream_variant, 1, max_upsplit);
+    h.stream_lds = (h.stream_variant >= 6 && h.stream_variant <= 8) ? (int32_t)lds_tok
+                                                                     : (int32_t)stream_lds_need(h.stream_variant, 1, max_upsplit);
     h.tile_variant = tile_variant(true);
     h.ws_bytes = off;
     int64_t t = up(sizeof(bl::GroupHeader), 16);

@@ -44,6 +44,8 @@ constexpr int kBlockBytes = 1024;
 // token counts the streaming kernels take; larger ones take the tile kernel
 constexpr int kStreamMaxTokens = 32;
 // 64-row tiles per wave of the streaming MFMA kernel (a workgroup takes 4x)
+// in launches with enough tile groups to fill the part; smaller launches
+// take one per wave, twice as many workgroups
 constexpr int kStreamMfmaTiles = 2;
 // token counts above which that kernel reads fragment-ordered activations
 constexpr int kStreamFragTokens = 16;
@@ -75,13 +77,16 @@ struct Problem {
     int32_t mtile;         // rows of M per tile-kernel work item
     int32_t qtiled;        // 1: Q is stored in MFMA fragment order (see below)
     int32_t mt;            // M tiles of the tile kernel (token groups of the BT5 kernel)
-    int32_t ntt;           // N tiles of the tile kernel (four-tile groups of the BT5 kernel)
+    int32_t ntt;           // N tiles of the tile kernel; tile groups of the streaming MFMA
+                           // kernel (4 * stiles tiles each); four-tile groups of the BT5 kernel
     int32_t tok_begin;     // first row of this problem in the grouped quant grid
     int32_t item_begin;    // first work item of this problem in its kernel's grid
     int32_t fmt;           // 0: BL2-T64 weights, 1: BT5-T32 weights
     int32_t KU5;           // ceil(K/160), the BT5-T32 units (0 for BL2-T64)
+    int32_t stiles;        // 64-row tiles per wave of the streaming MFMA kernel (1 or 2; else 0)
+    int32_t pad_;
 };
-static_assert(sizeof(Problem) == 152, "Problem layout is shared by host and device");
+static_assert(sizeof(Problem) == 160, "Problem layout is shared by host and device");
 
 // Split-K arrival counters of a problem: one per N tile of the 2-bit
 // streaming kernels, one per (four-tile group, token group) of the BT5 kernel.

@@ -430,8 +430,8 @@ __device__ __forceinline__ void stream_dot4_tokens(const Problem &p, int local)
 
 // 3..32 tokens (2..32 when the dot4 kernels are limited to one): the same
 // packed stream feeds v_mfma_i32_32x32x32_i8 with the token rows as the A
-// operand.  A workgroup covers 4 * kStreamMfmaTiles
-// 64-row tiles over one K range: each wave owns kStreamMfmaTiles tiles and
+// operand.  A workgroup covers 4 * TPW
+// 64-row tiles over one K range: each wave owns TPW tiles and
 // every wave walks the same units in the same order, so a wave streams its
 // tiles' blocks contiguously, one activation fragment serves all its tiles,
 // the four waves fetch that fragment at about the same time (one L2 read,
@@ -440,10 +440,9 @@ __device__ __forceinline__ void stream_dot4_tokens(const Problem &p, int local)
 // of the MFMAs through a two-slot register ring (branch-free: unit indices
 // clamp to the range end and surplus units get zero weights, which add
 // nothing).
-template <int UNROLL>
+template <int UNROLL, int TPW>
 __device__ void stream_mfma(const Problem &p, int local)
 {
-    constexpr int TPW = kStreamMfmaTiles;
     const int grp = local / p.ks, split = local - grp * p.ks;
     const int u0 = split * p.upsplit;
     const int u1 = min(p.KU, u0 + p.upsplit);
@@ -581,7 +580,7 @@ __device__ void stream_mfma(const Problem &p, int local)
 // table-lookup comparison variant (one token); 6, 7, 8: the dot4 token-loop
 // kernel with V - 4 token slots per unit, for launches whose problems have
 // at most V - 4 tokens (one-token problems take the one-slot loop, whose
-// LDS layout and stream are those of 3).
+// LDS layout and stream are those of 3); 9: as 1 with one tile per wave.
 template <int V>
 __device__ inline void stream_body(const Problem &p, int local)
 {
@@ -593,7 +592,9 @@ __device__ inline void stream_body(const Problem &p, int local)
     } else if constexpr (V == 0)
         stream_dot4<4, false>(p, local);
     else if constexpr (V == 1)
-        stream_mfma<2>(p, local);
+        stream_mfma<2, kStreamMfmaTiles>(p, local);
+    else if constexpr (V == 9)
+        stream_mfma<2, 1>(p, local);
     else if constexpr (V == 2)
         stream_dot4<4, true>(p, local);
     else if constexpr (V == 3)
@@ -631,10 +632,11 @@ __global__ __launch_bounds__(kThreads) void stream_multi_kernel(ProblemSet ps)
 hipError_t launch_stream_multi(const ProblemSet &ps, int variant, int lds_bytes, hipStream_t s)
 {
     const dim3 grid((unsigned)ps.begin[ps.count]), block(kThreads);
-    const unsigned lds = variant >= 2 ? (unsigned)lds_bytes : 0u;
+    const unsigned lds = (variant >= 2 && variant <= 8) ? (unsigned)lds_bytes : 0u;
     switch (variant) {
     case 0: hipLaunchKernelGGL(stream_multi_kernel<0>, grid, block, 0, s, ps); break;
     case 1: hipLaunchKernelGGL(stream_multi_kernel<1>, grid, block, 0, s, ps); break;
+    case 9: hipLaunchKernelGGL(stream_multi_kernel<9>, grid, block, 0, s, ps); break;
     case 2: hipLaunchKernelGGL(stream_multi_kernel<2>, grid, block, lds, s, ps); break;
     case 5: hipLaunchKernelGGL(stream_multi_kernel<5>, grid, block, lds, s, ps); break;
     case 6: hipLaunchKernelGGL(stream_multi_kernel<6>, grid, block, lds, s, ps); break;
@@ -647,14 +649,16 @@ hipError_t launch_stream_multi(const ProblemSet &ps, int variant, int lds_bytes,
 
 hipError_t launch_stream_single(const Problem &p, int variant, hipStream_t s)
 {
-    // the MFMA variant's work items are tile groups (p.ntt of them)
-    const int64_t tiles = variant == 1 ? (int64_t)p.ntt : (int64_t)p.NT;
+    // the MFMA variants' work items are tile groups (p.ntt of them)
+    const int64_t tiles = (variant == 1 || variant == 9) ? (int64_t)p.ntt : (int64_t)p.NT;
     const dim3 grid((unsigned)(tiles * p.ks)), block(kThreads);
     const unsigned slot = variant >= 6 ? 64u * (unsigned)(variant - 4) : 64u;
-    const unsigned lds = variant >= 2 ? (variant == 5 ? kLutUnitBytes : slot) * (unsigned)p.upsplit : 0u;
+    const unsigned lds =
+        (variant >= 2 && variant <= 8) ? (variant == 5 ? kLutUnitBytes : slot) * (unsigned)p.upsplit : 0u;
     switch (variant) {
     case 0: hipLaunchKernelGGL(stream_single_kernel<0>, grid, block, 0, s, p); break;
     case 1: hipLaunchKernelGGL(stream_single_kernel<1>, grid, block, 0, s, p); break;
+    case 9: hipLaunchKernelGGL(stream_single_kernel<9>, grid, block, 0, s, p); break;
     case 2: hipLaunchKernelGGL(stream_single_kernel<2>, grid, block, lds, s, p); break;
     case 3: hipLaunchKernelGGL(stream_single_kernel<3>, grid, block, lds, s, p); break;
     case 5: hipLaunchKernelGGL(stream_single_kernel<5>, grid, block, lds, s, p); break;
@@ -670,10 +674,11 @@ hipError_t launch_stream_group(const Problem *probs, const uint2 *item_map, int 
                                int variant, int lds_bytes, hipStream_t s)
 {
     const dim3 grid((unsigned)n_items), block(kThreads);
-    const unsigned lds = variant >= 2 ? (unsigned)lds_bytes : 0u;
+    const unsigned lds = (variant >= 2 && variant <= 8) ? (unsigned)lds_bytes : 0u;
     switch (variant) {
     case 0: hipLaunchKernelGGL(stream_group_kernel<0>, grid, block, 0, s, probs, item_map); break;
     case 1: hipLaunchKernelGGL(stream_group_kernel<1>, grid, block, 0, s, probs, item_map); break;
+    case 9: hipLaunchKernelGGL(stream_group_kernel<9>, grid, block, 0, s, probs, item_map); break;
     case 2: hipLaunchKernelGGL(stream_group_kernel<2>, grid, block, lds, s, probs, item_map); break;
     case 3: hipLaunchKernelGGL(stream_group_kernel<3>, grid, block, lds, s, probs, item_map); break;
     case 5: hipLaunchKernelGGL(stream_group_kernel<5>, grid, block, lds, s, probs, item_map); break;

@@ -188,7 +188,8 @@ def test_group_plan_single_token_quantization():
     # 2-token problem switches the streaming kernel to the two-slot dot4
     # token-loop kernel (6), whose LDS holds 64 bytes per unit for one-token
     # problems and 128 for two-token ones; a 5-token problem switches it to
-    # MFMA (1)
+    # the MFMA stream, which takes one tile per wave (9) in a launch this small
+    # (129 eight-tile groups, fewer than the 1024-workgroup split target)
     L = B.lib()
     fused = os.environ.get("BITLINEAR_FUSE_QUANT", "0") not in ("", "0")
     specs = [(1, 4096, 256)] * 16
@@ -214,16 +215,26 @@ def test_group_plan_single_token_quantization():
     wsb3 = L.bitlinear_group_workspace_bytes(arr3, 17)
     assert L.bitlinear_group_plan(arr3, 17, FAKE, wsb3, host3.ctypes.data, tb3) == 0
     hdr3 = np.frombuffer(host3[:48].tobytes(), np.int32)
-    assert hdr3[2] == 21 and hdr3[7] == 1 and hdr3[9] == 0
+    assert hdr3[2] == 21 and hdr3[7] == 9 and hdr3[9] == 0
     # a one-token problem whose unsplit K range (1250 units) needs more than
-    # 64 KiB of staged activations keeps a 2-token launch off variant 6
+    # 64 KiB of staged activations keeps a 2-token launch off variant 6 (the
+    # MFMA stream takes it, one tile per wave)
     arr4 = _problems(specs + [(1, 64, 80000), (2, 64, 64)])
     tb4 = L.bitlinear_group_table_bytes(arr4, 18)
     host4 = np.zeros(tb4, np.uint8)
     wsb4 = L.bitlinear_group_workspace_bytes(arr4, 18)
     assert L.bitlinear_group_plan(arr4, 18, FAKE, wsb4, host4.ctypes.data, tb4) == 0
     hdr4 = np.frombuffer(host4[:48].tobytes(), np.int32)
-    assert hdr4[7] == 1 and hdr4[9] == 0
+    assert hdr4[7] == 9 and hdr4[9] == 0
+    # a launch whose eight-tile groups fill the split target keeps two tiles
+    # per wave (1): 130 problems of 64 tiles at M = 5
+    arr6 = _problems([(5, 4096, 256)] * 130)
+    tb6 = L.bitlinear_group_table_bytes(arr6, 130)
+    host6 = np.zeros(tb6, np.uint8)
+    wsb6 = L.bitlinear_group_workspace_bytes(arr6, 130)
+    assert L.bitlinear_group_plan(arr6, 130, FAKE, wsb6, host6.ctypes.data, tb6) == 0
+    hdr6 = np.frombuffer(host6[:48].tobytes(), np.int32)
+    assert hdr6[7] == 1 and hdr6[3] == 130 * 8
 
 
 def test_group_calls_reject_foreign_tables():

@@ -721,6 +721,7 @@ print("knob ok")
 
 KNOB_SETTINGS = [
     ("BITLINEAR_DOT4_MAX_M", "0"), ("BITLINEAR_DOT4_MAX_M", "1"), ("BITLINEAR_DOT4_MAX_M", "4"),
+    ("BITLINEAR_MFMA_TILES", "1"), ("BITLINEAR_MFMA_TILES", "2"),
     ("BITLINEAR_DOT4_VARIANT", "0"), ("BITLINEAR_DOT4_VARIANT", "2"),
     ("BITLINEAR_SPLIT_TARGET", "1"), ("BITLINEAR_SPLIT_TARGET", "100000"), ("BITLINEAR_XCD_ORDER", "0"),
 ] + [("BITLINEAR_TILE_VARIANT", str(v)) for v in (0, 1, 2, 5, 6, 7, 10, 11, 12, 18)]
