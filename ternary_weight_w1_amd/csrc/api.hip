@@ -130,13 +130,19 @@ int mfma_tiles_for(int64_t groups)
     return groups < knobs().split_target ? 1 : bl::kStreamMfmaTiles;
 }
 
+// Most K splits of a tile-kernel problem (measured on the chained 3B step at
+// M = 64: 3.16 ms unsplit, 2.70 at two, 2.74 at four, 3.06 at eight, 3.33 at
+// up to sixteen).
+constexpr int64_t kTileMaxSplits = 2;
+
 // Kernel kind and decomposition of one problem.  `base_items` is the number
 // of streaming work items the whole launch has without K splits; splits are
 // added only while the launch is short of workgroups.  own_q: the library
 // quantizes the activations itself and may choose their layout.  groups4:
 // the launch runs the streaming MFMA kernel, whose work items are groups of
 // 4 * tpw 64-row tiles (p.ntt of them).
-void decompose(Problem &p, int64_t base_items, bool own_q, bool groups4 = false, int tpw = bl::kStreamMfmaTiles)
+void decompose(Problem &p, int64_t base_items, bool own_q, bool groups4 = false, int tpw = bl::kStreamMfmaTiles,
+               int64_t tile_base = 0)
 {
     p.KU = (int32_t)((p.K + 63) / 64);
     p.NT = (int32_t)((p.N + 63) / 64);
@@ -179,6 +185,23 @@ void decompose(Problem &p, int64_t base_items, bool own_q, bool groups4 = false,
         p.qtiled = tile_frag(v) ? 1 : 0;
         p.mt = (int32_t)((p.M + p.mtile - 1) / p.mtile);
         p.ntt = (p.NT + 3) / 4;
+        // K splits for the default instantiation while the launch's work
+        // items (tile_base, or this problem's alone) are short of the
+        // target: at most kTileMaxSplits, keeping >= 8 units (4 stages) per
+        // split.  Each split's partials are 64 KiB per item, read back by
+        // the item's last split, so more splits cost more than they gain.
+        const int64_t items = tile_base > 0 ? tile_base : (int64_t)p.mt * p.ntt;
+        const int64_t target = knobs().split_target;
+        if (v == 19 && items < target) {
+            int64_t ks = (target + items - 1) / items;
+            int64_t cap = p.KU / 8;
+            if (cap > kTileMaxSplits) cap = kTileMaxSplits;
+            if (cap < 1) cap = 1;
+            if (ks > cap) ks = cap;
+            const int64_t upsplit = (p.KU + ks - 1) / ks;
+            p.upsplit = (int32_t)upsplit;
+            p.ks = (int32_t)((p.KU + upsplit - 1) / upsplit);
+        }
     }
 }
 
@@ -217,8 +240,7 @@ void decompose5(Problem &p, int64_t base_items)
 int64_t items_of(const Problem &p)
 {
     if (p.kind == 0) return (int64_t)(p.ntt > 0 ? p.ntt : p.NT) * p.ks;
-    if (p.kind == 2) return (int64_t)p.ntt * p.mt * p.ks;
-    return (int64_t)p.mt * p.ntt;
+    return (int64_t)p.ntt * p.mt * p.ks;
 }
 
 // Row stride of the library's own int8 activations: whole 64-code units,
@@ -281,10 +303,9 @@ WsLayout ws_layout(const Problem &p, bool with_act)
         L.rowsum = off;
         off = up(off + 4 * (int64_t)p.M, 256);
     }
-    if (p.kind != 1 && p.ks > 1) {
-        const int64_t rows = (int64_t)p.NT * (p.kind == 2 ? bl::kBt5TileRows : 64);
+    if (p.ks > 1) {
         L.part = off;
-        off = up(off + 4 * (int64_t)p.ks * p.M * rows, 256);
+        off = up(off + 4 * bl::partial_words(p), 256);
         L.tick = off;
         off = up(off + 4 * bl::ticket_count(p), 256);
     }
@@ -532,7 +553,7 @@ int bitlinear_matmul(const int8_t *Q, int64_t ldq, const float *absmax, const in
     const WsLayout L = ws_layout(p, false);
     if (L.total > 0 && (!ws || ws_bytes < (size_t)L.total || !a16(ws)))
         return fail(BITLINEAR_ERR_WORKSPACE, "matmul: needs %lld workspace bytes (16-byte aligned)", (long long)L.total);
-    if (p.kind == 1 && (int64_t)p.mt * p.ntt >= (int64_t(1) << 31))
+    if (p.kind == 1 && items_of(p) >= (int64_t(1) << 31))
         return fail(BITLINEAR_ERR_SHAPE, "matmul: grid too large");
     p.Q = const_cast<int8_t *>(Q);
     p.ldq = ldq;
@@ -544,10 +565,10 @@ int bitlinear_matmul(const int8_t *Q, int64_t ldq, const float *absmax, const in
     p.acc_out = acc_out;
     char *base = static_cast<char *>(ws);
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (p.kind == 0 && p.ks > 1) {
+    if (p.ks > 1) {
         p.acc_ws = reinterpret_cast<int32_t *>(base + L.part);
         p.tickets = reinterpret_cast<uint32_t *>(base + L.tick);
-        if (hipError_t e = bl::launch_zero_words(p.tickets, p.NT, s)) return hip_fail(e, "zero tickets");
+        if (hipError_t e = bl::launch_zero_words(p.tickets, bl::ticket_count(p), s)) return hip_fail(e, "zero tickets");
     }
     if (hipError_t e = launch_contraction(p, false, s)) return hip_fail(e, "matmul");
     return BITLINEAR_OK;
@@ -566,7 +587,7 @@ int bitlinear_forward(const float *X, int64_t M, int64_t K, const uint8_t *P,
     const WsLayout L = ws_layout(p, true);
     if (!ws || ws_bytes < (size_t)L.total || !a16(ws))
         return fail(BITLINEAR_ERR_WORKSPACE, "forward: needs %lld workspace bytes (16-byte aligned)", (long long)L.total);
-    if (p.kind == 1 && (int64_t)p.mt * p.ntt >= (int64_t(1) << 31))
+    if (p.kind == 1 && items_of(p) >= (int64_t(1) << 31))
         return fail(BITLINEAR_ERR_SHAPE, "forward: grid too large");
     char *base = static_cast<char *>(ws);
     p.X = X;
@@ -578,7 +599,7 @@ int bitlinear_forward(const float *X, int64_t M, int64_t K, const uint8_t *P,
     p.Q = reinterpret_cast<int8_t *>(base + L.q);
     p.absmax = reinterpret_cast<float *>(base + L.absmax);
     p.rowsum = reinterpret_cast<int32_t *>(base + L.rowsum);
-    if (p.kind == 0 && p.ks > 1) {
+    if (p.ks > 1) {
         p.acc_ws = reinterpret_cast<int32_t *>(base + L.part);
         p.tickets = reinterpret_cast<uint32_t *>(base + L.tick);
     }
@@ -591,7 +612,7 @@ int bitlinear_forward(const float *X, int64_t M, int64_t K, const uint8_t *P,
         return BITLINEAR_OK;
     }
     if (hipError_t e = bl::launch_quant_act(X, M, K, p.Q, p.ldq, p.qtiled, p.absmax, p.rowsum,
-                                            p.tickets, p.tickets ? p.NT : 0, s))
+                                            p.tickets, p.tickets ? (int)bl::ticket_count(p) : 0, s))
         return hip_fail(e, "forward: quant_act");
     if (hipError_t e = launch_contraction(p, true, s)) return hip_fail(e, "forward: matmul");
     return BITLINEAR_OK;
@@ -723,6 +744,12 @@ int multi_plan(const int8_t *Q, int64_t ldq, int64_t M, int64_t K, const bitline
         }
         if (base < 1) base = 1;
     }
+    // the tile kernel's work items over the whole launch (M > 32)
+    int64_t tile_base = 0;
+    if (!fmt && M > kStreamMaxM) {
+        const int64_t bm = tile_bm(tile_variant(false));
+        for (int i = 0; i < count; ++i) tile_base += (M + bm - 1) / bm * (((w[i].N + 63) / 64 + 3) / 4);
+    }
     int64_t items = 0, tick = 0, part = 0;
     for (int i = 0; i < count; ++i) {
         Problem &p = mp.ps.p[i];
@@ -730,16 +757,15 @@ int multi_plan(const int8_t *Q, int64_t ldq, int64_t M, int64_t K, const bitline
         if (fmt)
             decompose5(p, base);
         else
-            decompose(p, base, false, g4, tpw);
+            decompose(p, base, false, g4, tpw, tile_base);
         mp.ps.begin[i] = (int32_t)items;
         items += items_of(p);
         max_upsplit = max_upsplit > p.upsplit ? max_upsplit : p.upsplit;
-        if (p.kind != 1 && p.ks > 1) {
-            const int64_t rows = (int64_t)p.NT * (p.kind == 2 ? bl::kBt5TileRows : 64);
+        if (p.ks > 1) {
             mp.tick_off[i] = tick;
             tick += 4 * bl::ticket_count(p);
             mp.part_off[i] = part;
-            part = up(part + 4 * (int64_t)p.ks * p.M * rows, 256);
+            part = up(part + 4 * bl::partial_words(p), 256);
         } else {
             mp.tick_off[i] = mp.part_off[i] = -1;
         }
@@ -875,6 +901,14 @@ int build_group(const bitlinear_problem *in, int count, char *ws, GroupPlan &out
     }
     if (base_items < 1) base_items = 1;
     if (base5 < 1) base5 = 1;
+    // the tile kernel's work items over the whole launch
+    int64_t tile_base = 0;
+    {
+        const int64_t bm = tile_bm(tile_variant(true));
+        for (int i = 0; i < count; ++i)
+            if (in[i].format != BITLINEAR_FORMAT_BT5 && in[i].M > kStreamMaxM)
+                tile_base += (in[i].M + bm - 1) / bm * (((in[i].N + 63) / 64 + 3) / 4);
+    }
     int64_t tokens = 0, items_s = 0, items_t = 0, items_5 = 0, off = 0;
     // streaming instantiation for the whole launch: LDS-staged dot4 when every
     // streaming problem has at most dot4_max_m tokens (the one-token kernel,
@@ -886,7 +920,7 @@ int build_group(const bitlinear_problem *in, int count, char *ws, GroupPlan &out
     for (int i = 0; i < count; ++i) {
         if (in[i].format == BITLINEAR_FORMAT_BT5) continue;
         Problem p = make_problem(in[i].M, in[i].N, in[i].K);
-        decompose(p, base_items, true);
+        decompose(p, base_items, true, false, bl::kStreamMfmaTiles, tile_base);
         if (p.kind != 0) continue;
         max_m = max_m > p.M ? max_m : p.M;
         any_split = any_split || p.ks > 1;
@@ -929,7 +963,7 @@ int build_group(const bitlinear_problem *in, int count, char *ws, GroupPlan &out
         if (q.format == BITLINEAR_FORMAT_BT5)
             decompose5(p, base5);
         else
-            decompose(p, base_items, true, groups4, tpw);
+            decompose(p, base_items, true, groups4, tpw, tile_base);
         p.X = q.X;
         p.P = q.P;
         p.gamma = q.gamma;
@@ -942,7 +976,7 @@ int build_group(const bitlinear_problem *in, int count, char *ws, GroupPlan &out
             p.Q = reinterpret_cast<int8_t *>(b + L.q);
             p.absmax = reinterpret_cast<float *>(b + L.absmax);
             p.rowsum = reinterpret_cast<int32_t *>(b + L.rowsum);
-            if (p.kind != 1 && p.ks > 1) {
+            if (p.ks > 1) {
                 p.acc_ws = reinterpret_cast<int32_t *>(b + L.part);
                 p.tickets = reinterpret_cast<uint32_t *>(b + L.tick);
             }

@@ -89,10 +89,21 @@ struct Problem {
 static_assert(sizeof(Problem) == 160, "Problem layout is shared by host and device");
 
 // Split-K arrival counters of a problem: one per N tile of the 2-bit
-// streaming kernels, one per (four-tile group, token group) of the BT5 kernel.
+// streaming kernels, one per (four-tile group, token group) of the BT5
+// kernel, one per (M tile, four N tiles) item of the tile kernel.
 __host__ __device__ inline int64_t ticket_count(const Problem &p)
 {
-    return p.kind == 2 ? (int64_t)p.ntt * p.mt : (int64_t)p.NT;
+    return p.kind == 0 ? (int64_t)p.NT : (int64_t)p.ntt * p.mt;
+}
+
+// int32 words of a problem's split-K partial sums (ks > 1): one row of N
+// tiles per split and token for the streaming kernels (64 or 32 rows per
+// tile), mtile accumulators per thread of every (item, split) for the tile
+// kernel.
+__host__ __device__ inline int64_t partial_words(const Problem &p)
+{
+    if (p.kind == 1) return (int64_t)p.ks * p.mt * p.ntt * p.mtile * 256;
+    return (int64_t)p.ks * p.M * p.NT * (p.kind == 2 ? 32 : 64);
 }
 
 // Up to kMultiMax problems that read the same int8 activations, passed by

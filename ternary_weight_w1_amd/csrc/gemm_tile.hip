@@ -272,9 +272,18 @@ __device__ __forceinline__ void tile_body(const Problem &p, int local)
 // WMS*32-token x 64-row-per-wave tile (as tile_body<WMS, 1, 1, 0, true>) with
 // UPS units of K per LDS stage and barrier: the fixed cost of a barrier
 // round (the wait itself and the LDS read latency before the first MFMA)
-// is paid once per UPS units.  A stage's unit past KU gets an all-zero
-// packed word -- zero fields add nothing -- so odd unit counts need no
-// branch; its activation chunk re-reads unit KU-1 (valid memory).
+// is paid once per UPS units.  A stage's unit past the K range gets an
+// all-zero packed word -- zero fields add nothing -- so odd unit counts need
+// no branch; its activation chunk re-reads the range's last unit (valid
+// memory).
+//
+// K split (launches with few work items): work item = (item, split), item =
+// (M tile, four N tiles); split j covers units [j upsplit, (j + 1) upsplit).
+// Each split publishes its 32 WMS accumulators per thread as device-scope
+// stores, [item][split][accumulator][thread], takes the item's ticket, and
+// the last one adds the other splits into its registers and runs the
+// epilogue.  Integer addition is associative: the bits do not depend on the
+// order.
 constexpr int kLda2 = 144;  // 128 bytes + 16 of padding: 8 lanes on distinct banks
 
 template <int UPS, int WMS>
@@ -292,13 +301,17 @@ __device__ __forceinline__ void tile_body_ups(const Problem &p, int local)
     __shared__ float cs[BM];
     __shared__ int rsum[BM];
 
-    const int mtile = local % p.mt;
-    const int nt = local / p.mt;
+    const int split = local % p.ks;
+    const int item = local / p.ks;
+    const int mtile = item % p.mt;
+    const int nt = item / p.mt;
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63, g = lane >> 5, r = lane & 31;
     const int m0 = mtile * BM;
     const int KU = p.KU;
-    const int KS = (KU + UPS - 1) / UPS;
+    const int ub = split * p.upsplit;           // first unit of the split
+    const int nu = min(KU, ub + p.upsplit) - ub;  // its units
+    const int KS = (nu + UPS - 1) / UPS;
     const int tile = 4 * nt + wave;
     const bool tv = tile < p.NT;
     const BL_GLOBAL v4u *blk = gload_ptr<v4u>(p.P + (int64_t)min(tile, p.NT - 1) * KU * kBlockBytes) + lane;
@@ -321,7 +334,7 @@ __device__ __forceinline__ void tile_body_ups(const Problem &p, int local)
 #pragma unroll
         for (int h = 0; h < UPS; ++h) {
             const int u = st * UPS + h;
-            const int uc = min(u, KU - 1);
+            const int uc = ub + min(u, nu - 1);
 #pragma unroll
             for (int i = 0; i < CH; ++i) ar[slot][h][i] = *reinterpret_cast<const BL_GLOBAL v4i *>(asrc[i] + 64 * uc);
             br[slot][h] = blk[(int64_t)uc * 64];
@@ -356,7 +369,7 @@ __device__ __forceinline__ void tile_body_ups(const Problem &p, int local)
         v4u w[UPS];
         const v4u z = {0u, 0u, 0u, 0u};
 #pragma unroll
-        for (int h = 0; h < UPS; ++h) w[h] = st * UPS + h < KU ? br[s][h] : z;
+        for (int h = 0; h < UPS; ++h) w[h] = st * UPS + h < nu ? br[s][h] : z;
         const int8_t *abase = &As[buf][r * kRow + 16 * g];
 #pragma unroll
         for (int h = 0; h < UPS; ++h) {
@@ -395,6 +408,36 @@ __device__ __forceinline__ void tile_body_ups(const Problem &p, int local)
 #pragma unroll
     for (int s = 0; s < kD - 1; ++s)
         if (s0 + s < KS) step(s, s0 + s);
+
+    if constexpr (WMS == 2) {  // the host splits K for the 64-token instantiation only
+        if (p.ks > 1) {
+            constexpr int kAcc = 32 * WMS;  // accumulators per thread
+            int32_t *part = p.acc_ws + (int64_t)item * p.ks * (kAcc * kThreads);
+#pragma unroll
+            for (int i = 0; i < WMS; ++i)
+#pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e)
+                        put_partial(part + ((int64_t)split * kAcc + (i * 2 + s2) * 16 + e) * kThreads + tid,
+                                    acc[i][s2][e]);
+            if (!arrive_last(p, item)) return;
+            for (int j = 0; j < p.ks; ++j) {
+                if (j == split) continue;
+#pragma unroll
+                for (int i = 0; i < WMS; ++i)
+#pragma unroll
+                    for (int s2 = 0; s2 < 2; ++s2) {
+                        int32_t v[16];
+#pragma unroll
+                        for (int e = 0; e < 16; ++e)
+                            v[e] = get_partial(part + ((int64_t)j * kAcc + (i * 2 + s2) * 16 + e) * kThreads + tid);
+#pragma unroll
+                        for (int e = 0; e < 16; ++e) acc[i][s2][e] += v[e];
+                    }
+            }
+        }
+    }
 
     // epilogue: rescale, transpose through LDS, 16-byte non-temporal stores
     __syncthreads();  // every wave is done with the activation stages
@@ -537,7 +580,7 @@ __global__ __launch_bounds__(kThreads, 2) void tile_multi_kernel(ProblemSet ps)
 
 hipError_t launch_tile_single(const Problem &p, int variant, hipStream_t s)
 {
-    const int items = p.mt * p.ntt;
+    const int items = p.mt * p.ntt * p.ks;
     const int per = (items + 7) / 8;
     const dim3 grid((unsigned)(8 * per)), block(kThreads);
     BL_TILE_CASES(tile_single_kernel, grid, block, 0, s, p, items, per)

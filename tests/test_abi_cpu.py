@@ -79,8 +79,12 @@ def test_size_helpers_reject_bad_sizes():
     assert B.workspace_bytes(99, 1, 64, 64) == smax
     # forward workspace holds at least Q, absmax and the row sums
     assert B.workspace_bytes(B.WS_FORWARD, 4, 256, 256) >= 4 * 256 + 8
-    # a matmul without K splits needs no workspace
-    assert B.workspace_bytes(B.WS_MATMUL, 512, 2560, 2560) == 0
+    # a matmul without K splits needs no workspace: the tile kernel on enough
+    # work items (M = 2048: 32 x 40 = 1280, the split target is 1024) ...
+    assert B.workspace_bytes(B.WS_MATMUL, 2048, 10240, 2560) == 0
+    # ... while 80 items (M = 512, N = 2560) split K in two: 64 KiB of int32
+    # partials per item and split, one 4-byte ticket per item (256-aligned)
+    assert B.workspace_bytes(B.WS_MATMUL, 512, 2560, 2560) == 2 * 80 * 65536 + 512
 
 
 def _st(f, *args):

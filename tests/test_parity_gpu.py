@@ -189,7 +189,7 @@ def _stack_weights(dim, ffn, layers, seed):
     return out
 
 
-@pytest.mark.parametrize("M", [1, 5])
+@pytest.mark.parametrize("M", [1, 5, 70])
 def test_layer_stack_chain(B, M):
     # Two pre-norm BitLinear blocks chained through the residual stream, then
     # the final norm: residual add + norm + cast, q/k/v contractions, the
@@ -428,11 +428,13 @@ def test_matmul_split_k(B, M, N, K):
         check_outputs(host(Y), host(acc), ref, 0.5, a, "split-K")
 
 
-@pytest.mark.parametrize("M,N,K", [(24, 64, 8192), (32, 520, 4000), (17, 64, 131072), (2, 64, 131072)])
+@pytest.mark.parametrize("M,N,K", [(24, 64, 8192), (32, 520, 4000), (17, 64, 131072), (2, 64, 131072),
+                                   (96, 300, 8192), (40, 64, 131072), (200, 1000, 3000)])
 def test_forward_split_k(B, M, N, K):
     # the forward call quantizes itself: above 16 tokens the streaming MFMA
     # kernel reads fragment-ordered activations; few tile groups and a long K
-    # split it over workgroups (partial sums + arrival tickets); twice, so the
+    # split it over workgroups (partial sums + arrival tickets), and so do
+    # few tile-kernel items above 32 tokens (two splits); twice, so the
     # tickets must come back to zero
     say("forward split-K", M, N, K)
     T = synth.random_ternary(N, K, seed=N + K)
