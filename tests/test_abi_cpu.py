@@ -379,3 +379,27 @@ def test_probe_mfma_rejects_bad_arguments():
     assert L.bitlinear_probe_mfma((1 << 20), 1, 1, 1, FAKE, None) == -2
     assert L.bitlinear_probe_mfma_blocks(None) == -1
 
+
+
+def test_group_plan_tile_split():
+    # tile-kernel problems (M > 32) in a launch with 7 work items, short of
+    # the 1024-workgroup split target: each splits K in two (14 items, padded
+    # to whole XCD slices of 8), and the workspace holds 64 KiB of partials
+    # per item and split; with enough items (1040) nothing splits
+    L = B.lib()
+    specs = [(64, 640, 2560), (100, 300, 4000)]
+    arr = _problems(specs)
+    tb = L.bitlinear_group_table_bytes(arr, 2)
+    host = np.zeros(tb, np.uint8)
+    wsb = L.bitlinear_group_workspace_bytes(arr, 2)
+    assert L.bitlinear_group_plan(arr, 2, FAKE, wsb, host.ctypes.data, tb) == 0
+    hdr = np.frombuffer(host[:48].tobytes(), np.int32)
+    assert hdr[4] == 16
+    assert wsb >= 2 * 7 * 65536
+    big = _problems([(64, 4096 * 4, 2560)] * 65)  # 65 x 64 items of 256 rows
+    tb2 = L.bitlinear_group_table_bytes(big, 65)
+    host2 = np.zeros(tb2, np.uint8)
+    wsb2 = L.bitlinear_group_workspace_bytes(big, 65)
+    assert L.bitlinear_group_plan(big, 65, FAKE, wsb2, host2.ctypes.data, tb2) == 0
+    hdr2 = np.frombuffer(host2[:48].tobytes(), np.int32)
+    assert hdr2[4] == 65 * 64

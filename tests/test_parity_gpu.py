@@ -660,6 +660,7 @@ def test_lut_variant_subprocess(B):
 
 @pytest.mark.parametrize("M,K,Ns,fmt", [(1, 2560, (2560, 640, 640), 0), (1, 333, (100, 37, 257), 0),
                                          (5, 640, (257, 100), 0), (40, 700, (300, 130, 64, 520), 0),
+                                         (48, 2560, (640, 1000), 0),
                                          (100, 256, (256, 512), 0), (1, 8192, (64,), 0),
                                          (1, 2560, (640, 2560, 100), 1), (9, 1000, (320, 64), 1),
                                          (20, 8192, (64, 96), 1)])
@@ -757,6 +758,13 @@ def test_group_decode_token_counts(B):
     say("group M=1..8")
     _group_run(B, [(1, 640, 2560), (3, 100, 200), (8, 2560, 640), (5, 64, 64), (2, 130, 6912), (7, 257, 3200),
                    (4, 64, 37)], 800)
+
+
+def test_group_tile_split(B):
+    # tile-kernel problems (more than 32 tokens) in a launch with few work
+    # items: K split in two, partials handed over through the tickets
+    say("group tile split")
+    _group_run(B, [(64, 640, 2560), (100, 300, 4000), (1, 640, 2560)], 900)
 
 
 def test_group_mixed(B):
