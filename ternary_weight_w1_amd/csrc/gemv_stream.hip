@@ -295,14 +295,23 @@ __device__ void stream_dot4(const Problem &p, int local)
             acc1 = dot16(w[j].w, qb[j], acc1);
         }
     }
-    for (; u < u1; u += kWaves) {
-        const v4u w = load_packed(blk + (int64_t)u * 64);
-        const v4i qa = qload(u, 0);
-        const v4i qb = qload(u, 32);
-        acc0 = dot16(w.x, qa, acc0);
-        acc0 = dot16(w.y, qb, acc0);
-        acc1 = dot16(w.z, qa, acc1);
-        acc1 = dot16(w.w, qb, acc1);
+    if (u < u1) {
+        // the last (fewer than UNROLL) units of this wave, loaded together:
+        // with K split finely (small launches) they are all a wave has
+        v4u w[UNROLL - 1];
+#pragma unroll
+        for (int j = 0; j < UNROLL - 1; ++j)
+            if (u + kWaves * j < u1) w[j] = load_packed(blk + (int64_t)(u + kWaves * j) * 64);
+#pragma unroll
+        for (int j = 0; j < UNROLL - 1; ++j)
+            if (u + kWaves * j < u1) {
+                const v4i qa = qload(u + kWaves * j, 0);
+                const v4i qb = qload(u + kWaves * j, 32);
+                acc0 = dot16(w[j].x, qa, acc0);
+                acc0 = dot16(w[j].y, qb, acc0);
+                acc1 = dot16(w[j].z, qa, acc1);
+                acc1 = dot16(w[j].w, qb, acc1);
+            }
     }
     // lanes r and r + 32 hold the two code chunks of the same rows
     acc0 += __shfl_xor(acc0, 32, 64);
