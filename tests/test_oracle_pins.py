@@ -18,6 +18,7 @@ import pytest
 
 import oracle as O
 import synth
+from fp_exact import fl32, fp32_margin, inv_rms_exact, rint_half_even, rms_fp64_error_bound
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
@@ -346,7 +347,7 @@ def test_absmean_scale_matches_exact_mean():
 
 def test_activation_quantizer_golden():
     acts = [ln for ln in _golden("quant_fixtures.txt") if ln.startswith("act ")]
-    assert len(acts) == 3
+    assert len(acts) == 4
     for ln in acts:
         x, q, tail = ln[4:].split("|")
         X = np.array([float(v) for v in x.split()], np.float32).reshape(1, -1)
@@ -381,6 +382,45 @@ def test_epilogue_golden():
         acc = np.array([int(v) for v in acc.split()], np.int32).reshape(1, -1)
         Y = O.epilogue(acc, gamma, np.array([amax], np.float32))
         np.testing.assert_array_equal(Y.ravel(), np.array([float(v) for v in y.split()], np.float32))
+
+
+def test_activation_scale_order_fixture_discriminates():
+    # R3 fixes the order s = fl(127/a), then q = rint(fl(x*s)); the pages fix
+    # none.  The fixture row a = 19/16, x = a/2 makes the exact product the
+    # tie 63.5: derived here in exact rationals with fp32 rounding modelled,
+    # the stated order gives 63, both other orders 64.  A consistent swap of
+    # the order in the oracle (and the kernels) fails this pin.
+    line = [ln for ln in _golden("quant_fixtures.txt") if ln.startswith("act 1.1875")][0]
+    x, q, _ = line[4:].split("|")
+    xs = [Fraction(float(v)) for v in x.split()]
+    a = max(abs(v) for v in xs)
+    s = fl32(Fraction(127) / a)
+    stated = [max(-127, min(127, rint_half_even(fl32(v * s)))) for v in xs]
+    mul_first = [rint_half_even(fl32(fl32(v * 127) / a)) for v in xs]
+    div_scale = [rint_half_even(fl32(v / fl32(a / 127))) for v in xs]
+    assert stated == [int(v) for v in q.split()]
+    assert stated[1] == 63 and mul_first[1] == 64 and div_scale[1] == 64
+    assert stated[2] == -63 and mul_first[2] == -64 and div_scale[2] == -64
+    Q, am, rs = O.quant_act(np.array([[float(v) for v in x.split()]], np.float32))
+    assert list(Q.ravel()) == stated and rs[0] == sum(stated)
+
+
+def test_epilogue_scale_order_fixture_discriminates():
+    # R4 fixes c = fl(fl(gamma*a)/127), y = fl(float(acc)*c).  The fixture's
+    # gamma = 3/256, a = 69/64 round the other two orders one ulp lower.
+    line = [ln for ln in _golden("quant_fixtures.txt") if ln.startswith("epi 0.01171875")][0]
+    head, acc, y = line[4:].split("|")
+    g, a = (Fraction(float(v)) for v in head.split())
+    accs = [int(v) for v in acc.split()]
+    c = fl32(fl32(g * a) / 127)
+    c_alt1 = fl32(g * fl32(a / 127))
+    c_alt2 = fl32(fl32(g / 127) * a)
+    assert c != c_alt1 and c != c_alt2
+    stated = [fl32(v * c) for v in accs]
+    assert stated == [Fraction(float(v)) for v in y.split()]
+    assert all(fl32(v * c_alt1) != t for v, t in zip(accs, stated))
+    Y = O.epilogue(np.array([accs], np.int32), float(g), np.array([float(a)], np.float32))
+    assert [Fraction(float(v)) for v in Y.ravel()] == stated
 
 
 # ------------------------------------------ P-C identity and library check --
@@ -611,6 +651,39 @@ def test_rmsnorm_matches_float64_definition():
         np.testing.assert_array_equal(Q, Q2)
         np.testing.assert_array_equal(a, a2)
         np.testing.assert_array_equal(rs, rs2)
+
+
+def test_fp32_margin_helper():
+    # the switch points of fp32 rounding around 1 are 1 - 2^-25 and 1 + 2^-24
+    assert fp32_margin(Fraction(1)) == 2.0 ** -25
+    assert fp32_margin(Fraction(1) + Fraction(1, 2 ** 24)) == 0.0
+    assert fl32(Fraction(1) + Fraction(1, 2 ** 24)) == 1  # the tie goes to even
+    assert inv_rms_exact([4.0], 0.0) == Fraction(1, 4)
+    assert inv_rms_exact([3.0, 4.0], 0.0) ** 2 <= Fraction(2, 25) < (inv_rms_exact([3.0, 4.0], 0.0)
+                                                                    + Fraction(1, 2 ** 100)) ** 2
+
+
+def test_rmsnorm_factor_is_correctly_rounded_when_decided():
+    # R13 computes inv in fp64 and rounds it to fp32 once.  Whenever the
+    # exact factor sits farther from an fp32 switch point than fp64 can err,
+    # any correct fp64 order -- the oracle's sequential sum, the kernel's
+    # tree -- must give fl32(exact), which pins the oracle's factor to the
+    # definition itself (a sum in fp32, eps outside the root, or a missing
+    # 1/K fail here).  Rows too close to call are counted, not compared.
+    rng = np.random.default_rng(23)
+    checked = undecided = 0
+    for K, eps in [(3, 1e-5), (37, 1e-5), (1000, 0.0), (4096, 1e-6), (300, 10.0)]:
+        X = (rng.standard_normal((40, K)) * rng.uniform(0.01, 100)).astype(np.float32)
+        _, _, _, _, inv = O.rmsnorm_quant_act(X, None, eps)
+        bound = rms_fp64_error_bound(K) + 2.0 ** -60
+        for m in range(X.shape[0]):
+            exact = inv_rms_exact(X[m], eps)
+            if fp32_margin(exact) <= bound:
+                undecided += 1
+                continue
+            assert Fraction(float(inv[m])) == fl32(exact), (K, m)
+            checked += 1
+    assert checked >= 195 and undecided <= 5
 
 
 def test_rmsnorm_power_of_two_invariance():
