@@ -64,6 +64,8 @@ def lib():
         L.oracle_epilogue.argtypes = [_vp, _i64, _i64, _f32, _vp, _vp]
         L.oracle_epilogue_f64.restype = None
         L.oracle_epilogue_f64.argtypes = [_vp, _i64, _i64, _f32, _vp, _vp]
+        L.oracle_threads.restype = ctypes.c_int
+        L.oracle_threads.argtypes = []
         L.oracle_forward_packed.restype = _i64
         L.oracle_forward_packed.argtypes = [_vp, _i64, _i64, _vp, _f32, _i64, _vp,
                                             _vp, _vp, _vp, _vp, _vp]
@@ -281,6 +283,12 @@ def forward(X, T, gamma):
     Y = epilogue(acc, gamma, a)
     return {"Q": Q, "absmax": a, "rowsum": rs, "acc": acc, "Y": Y,
             "Y64": epilogue_f64(acc, gamma, a)}
+
+
+def threads() -> int:
+    """Threads the oracle's OpenMP loops use (OMP_NUM_THREADS, else every
+    core)."""
+    return int(lib().oracle_threads())
 
 
 def forward_packed(X, P, gamma, N):

@@ -10,7 +10,11 @@
  * Style: plain scalar C, one obvious loop per definition, no SIMD, no
  * blocking, no fusion.  Built with -O2 -fno-fast-math -ffp-contract=off so
  * that every fp32 operation is a single IEEE-754 rounding in the default
- * round-to-nearest-even mode.
+ * round-to-nearest-even mode.  The loops over independent outputs (rows of
+ * the contraction, tokens of the activation cast, rows of the unpack) carry
+ * an OpenMP work-sharing pragma, so the CPU-baseline leg of the benchmark
+ * can use every host core: each output is still produced by one thread in
+ * one sequential loop, so no result depends on the thread count.
  *
  * Sources (page title, section):
  *  [AN]  anthology note-168 on arXiv 2402.17764 (dmarx.github.io),
@@ -48,6 +52,7 @@
  * that is "parity unpinned" beyond a 1e-6 relative bound.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -144,6 +149,7 @@ int64_t oracle_unpack(const uint8_t *P, int64_t N, int64_t K, int8_t *T)
 {
     int64_t bad = 0;
     int64_t tiles = (N + 63) / 64, units = (K + 63) / 64;
+#pragma omp parallel for schedule(static) reduction(+ : bad) if (N * K >= (1 << 20))
     for (int64_t n = 0; n < tiles * 64; ++n) {
         for (int64_t k = 0; k < units * 64; ++k) {
             int64_t b; int sh;
@@ -276,6 +282,7 @@ void oracle_matmul_packed5_rows(const int8_t *Q, const uint8_t *P, int64_t M, in
 void oracle_quant_act(const float *X, int64_t M, int64_t K,
                       int8_t *Q, float *absmax, int32_t *rowsum)
 {
+#pragma omp parallel for schedule(static) if (M > 1 && M * K >= (1 << 20))
     for (int64_t m = 0; m < M; ++m) {
         float a = 0.0f;
         for (int64_t k = 0; k < K; ++k) {
@@ -376,6 +383,7 @@ void oracle_relu2_gate_quant_act(const float *G, const float *U, int64_t M, int6
 void oracle_matmul(const int8_t *Q, const int8_t *T, int64_t M, int64_t N, int64_t K,
                    int32_t *acc)
 {
+#pragma omp parallel for collapse(2) schedule(static) if (M * N * K >= (1 << 20))
     for (int64_t m = 0; m < M; ++m)
         for (int64_t n = 0; n < N; ++n) {
             int32_t s = 0;
@@ -409,6 +417,7 @@ void oracle_matmul_packed_rows(const int8_t *Q, const uint8_t *P, int64_t M, int
                                int64_t K, const int64_t *rows, int64_t nrows, int32_t *acc)
 {
     (void)N;
+#pragma omp parallel for schedule(static) if (nrows * M * K >= (1 << 20))
     for (int64_t i = 0; i < nrows; ++i) {
         int64_t n = rows[i];
         for (int64_t m = 0; m < M; ++m) {
@@ -466,3 +475,6 @@ int64_t oracle_forward_packed(const float *X, int64_t M, int64_t K, const uint8_
     oracle_epilogue(acc, M, N, gamma, absmax, Y);
     return bad;
 }
+
+/* Threads the OpenMP loops above use (the CPU-baseline leg reports it). */
+int oracle_threads(void) { return omp_get_max_threads(); }

@@ -44,6 +44,7 @@ void    oracle_epilogue(const int32_t *acc, int64_t M, int64_t N, float gamma,
                         const float *absmax, float *Y);
 void    oracle_epilogue_f64(const int32_t *acc, int64_t M, int64_t N, float gamma,
                             const float *absmax, double *Y);
+int     oracle_threads(void);
 int64_t oracle_forward_packed(const float *X, int64_t M, int64_t K, const uint8_t *P,
                               float gamma, int64_t N, float *Y,
                               int8_t *Q, float *absmax, int32_t *rowsum,

@@ -95,7 +95,7 @@ const Knobs &knobs()
 // stacks).  5..7 read fragment-ordered activations that only the library's
 // own quantizer writes, so caller-supplied activations map them to their
 // row-major twins 2, 0, 1.
-bool tile_variant_known(int v) { return v == 0 || v == 1 || v == 2 || (v >= 5 && v <= 7) || (v >= 10 && v <= 12) || v == 18 || v == 19; }
+bool tile_variant_known(int v) { return v == 0 || v == 1 || v == 2 || (v >= 5 && v <= 7) || (v >= 10 && v <= 12) || (v >= 18 && v <= 28 && v != 22 && v != 25 && v != 26); }
 int tile_variant(bool own_q)
 {
     int v = knobs().tile_variant;
@@ -107,8 +107,11 @@ int tile_variant(bool own_q)
     }
     return v;
 }
-int tile_bm(int variant) { return (variant == 0 || variant == 6 || variant == 19) ? 64 : 128; }
-bool tile_frag(int variant) { return variant >= 5 && variant <= 7; }
+int tile_bm(int variant) { return (variant == 0 || variant == 6 || variant == 19 || variant == 20 || variant == 21 || variant == 24 || variant >= 27) ? 64 : 128; }
+// weight rows per tile-kernel work item
+int tile_rows(int variant) { return variant == 24 ? 512 : 256; }
+// 20, 21 read either layout; the library's own activations are fragment-ordered
+bool tile_frag(int variant, bool own_q) { return (variant >= 5 && variant <= 7) || (own_q && variant >= 20 && !getenv("BITLINEAR_TILE_ROWMAJOR")); }
 
 // The table-lookup dot4 variant (knob value 5) runs single-token problems
 // with at most kLutMaxUnits units (64 KiB of table) per workgroup.
@@ -182,9 +185,9 @@ void decompose(Problem &p, int64_t base_items, bool own_q, bool groups4 = false,
         p.kind = 1;
         const int v = tile_variant(own_q);
         p.mtile = tile_bm(v);
-        p.qtiled = tile_frag(v) ? 1 : 0;
+        p.qtiled = tile_frag(v, own_q) ? 1 : 0;
         p.mt = (int32_t)((p.M + p.mtile - 1) / p.mtile);
-        p.ntt = (p.NT + 3) / 4;
+        p.ntt = (p.NT + tile_rows(v) / 64 - 1) / (tile_rows(v) / 64);
         // K splits for the default instantiation while the launch's work
         // items (tile_base, or this problem's alone) are short of the
         // target: at most kTileMaxSplits, keeping >= 8 units (4 stages) per
@@ -192,7 +195,7 @@ void decompose(Problem &p, int64_t base_items, bool own_q, bool groups4 = false,
         // the item's last split, so more splits cost more than they gain.
         const int64_t items = tile_base > 0 ? tile_base : (int64_t)p.mt * p.ntt;
         const int64_t target = knobs().split_target;
-        if (v == 19 && items < target) {
+        if (v >= 19 && items < target) {
             int64_t ks = (target + items - 1) / items;
             int64_t cap = p.KU / 8;
             if (cap > kTileMaxSplits) cap = kTileMaxSplits;
@@ -747,8 +750,9 @@ int multi_plan(const int8_t *Q, int64_t ldq, int64_t M, int64_t K, const bitline
     // the tile kernel's work items over the whole launch (M > 32)
     int64_t tile_base = 0;
     if (!fmt && M > kStreamMaxM) {
-        const int64_t bm = tile_bm(tile_variant(false));
-        for (int i = 0; i < count; ++i) tile_base += (M + bm - 1) / bm * (((w[i].N + 63) / 64 + 3) / 4);
+        const int v = tile_variant(false);
+        const int64_t bm = tile_bm(v), tn = tile_rows(v) / 64;
+        for (int i = 0; i < count; ++i) tile_base += (M + bm - 1) / bm * (((w[i].N + 63) / 64 + tn - 1) / tn);
     }
     int64_t items = 0, tick = 0, part = 0;
     for (int i = 0; i < count; ++i) {
@@ -904,10 +908,11 @@ int build_group(const bitlinear_problem *in, int count, char *ws, GroupPlan &out
     // the tile kernel's work items over the whole launch
     int64_t tile_base = 0;
     {
-        const int64_t bm = tile_bm(tile_variant(true));
+        const int v = tile_variant(true);
+        const int64_t bm = tile_bm(v), tn = tile_rows(v) / 64;
         for (int i = 0; i < count; ++i)
             if (in[i].format != BITLINEAR_FORMAT_BT5 && in[i].M > kStreamMaxM)
-                tile_base += (in[i].M + bm - 1) / bm * (((in[i].N + 63) / 64 + 3) / 4);
+                tile_base += (in[i].M + bm - 1) / bm * (((in[i].N + 63) / 64 + tn - 1) / tn);
     }
     int64_t tokens = 0, items_s = 0, items_t = 0, items_5 = 0, off = 0;
     // streaming instantiation for the whole launch: LDS-staged dot4 when every

@@ -491,6 +491,297 @@ __device__ __forceinline__ void tile_body_ups(const Problem &p, int local)
     }
 }
 
+// 64-token x 256-row tile with the activation tile moved by the buffer
+// unit straight into LDS (buffer_load ... lds) instead of through a
+// register ring and ds_write: no VGPRs hold in-flight activations, the LDS
+// stages are laid out in MFMA fragment order (each wave instruction fills
+// one 1 KiB fragment, lane l's 16 bytes at 16 l, and each operand read is
+// the same linear 1 KiB: no bank conflicts, no padding), and NB stages sit
+// in LDS, D of them in flight.  Weights come through buffer loads too; every
+// address of the loop is scalar: the buffer resource of unit u starts at
+// unit u, and units past the K range get a record count of zero, so their
+// loads return zeros -- zero fields add nothing -- with no per-lane select.
+// Waits are placed by hand: the DMA's LDS writes are not tracked by the
+// compiler, so every stage waits until at most the loads of the stages
+// after it are outstanding (loads complete in order), then meets the
+// other waves at a barrier.
+__device__ inline __amdgpu_buffer_rsrc_t unit_rsrc(const void *base, int64_t off, bool live, uint32_t bytes)
+{
+    // CDNA buffer resource: 32-bit data format, no stride, raw addressing
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(static_cast<const char *>(base)) + off, 0,
+                                             live ? bytes : 0u, 0x00020000);
+}
+
+template <int WMS, int WNT, int NB, int D, int UPS = 2, bool PRIO = false>
+__device__ __forceinline__ void tile_body_dma(const Problem &p, int local)
+{
+    // WMS 32-token blocks x WNT 64-row weight tiles per wave; the four waves
+    // share the tokens and take consecutive weight tiles
+    constexpr int BM = 32 * WMS;
+    constexpr int kFrags = 2 * WMS;                 // 1 KiB fragments per unit (block, half)
+    constexpr int kFragsPerWave = kFrags / 4;       // moved by each wave per unit
+    static_assert(kFrags % 4 == 0, "every wave moves whole fragments");
+    constexpr int kUnitBytes = kFrags * 1024;
+    constexpr int kStageBytes = UPS * kUnitBytes;
+    constexpr int kEpiBytes = 4 * 32 * kEpiStride * 4;
+    constexpr int kSmem = NB * kStageBytes > kEpiBytes ? NB * kStageBytes : kEpiBytes;
+    static_assert(NB >= D + 1, "a stage's LDS buffer is refilled only after every wave has read it");
+    __shared__ __attribute__((aligned(1024))) int8_t smem[kSmem];
+    __shared__ float cs[BM];
+    __shared__ int rsum[BM];
+
+    const int split = local % p.ks;
+    const int item = local / p.ks;
+    const int mtile = item % p.mt;
+    const int nt = item / p.mt;
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, g = lane >> 5, r = lane & 31;
+    const int m0 = mtile * BM;
+    const int KU = p.KU;
+    const int ub = split * p.upsplit;             // first unit of the split
+    const int nu = min(KU, ub + p.upsplit) - ub;  // its units
+    const int KS = (nu + UPS - 1) / UPS;
+    int tile[WNT];
+    bool tv[WNT];
+    const uint8_t *bbase[WNT];
+#pragma unroll
+    for (int j = 0; j < WNT; ++j) {
+        tile[j] = 4 * WNT * nt + WNT * wave + j;
+        tv[j] = tile[j] < p.NT;
+        bbase[j] = p.P + (int64_t)min(tile[j], p.NT - 1) * KU * kBlockBytes;
+    }
+
+    // the token scales (read by the epilogue only), requested first so that
+    // every later wait covers them; kept in registers until the epilogue
+    float cs_r = 0.0f;
+    int rs_r = 0;
+    if (tid < BM) {
+        const int m = min(m0 + tid, p.M - 1);
+        cs_r = (*gload_ptr<float>(p.gamma) * gload_ptr<float>(p.absmax)[m]) / 127.0f;
+        rs_r = gload_ptr<int32_t>(p.rowsum)[m];
+    }
+
+    // fragment f = 2 b + h of a unit: 32-token block b, code half h; lane l
+    // brings token 32 b + l % 32, codes 32 h + 16 (l / 32) .. + 15.  Wave w
+    // moves fragments w * kFragsPerWave + i.  Row-major activations: 16
+    // bytes of the token's row (rows past M re-read row M - 1, never
+    // stored); fragment-ordered ones: the 1 KiB block of (32-row block,
+    // unit, half).
+    const int8_t *abase[kFragsPerWave];
+    int64_t astride;
+    uint32_t avoff[kFragsPerWave], abytes;
+#pragma unroll
+    for (int i = 0; i < kFragsPerWave; ++i) {
+        const int f = wave * kFragsPerWave + i, fb = f >> 1, fh = f & 1;
+        if (p.qtiled) {
+            // 32-row blocks past the last one re-read the last
+            const int64_t blk = min(m0 / 32 + fb, (p.M + 31) / 32 - 1);
+            abase[i] = p.Q + ((blk * KU) * 2 + fh) * 1024;
+            avoff[i] = 16u * (uint32_t)lane;
+        } else {
+            const int m = min(m0 + 32 * fb + r, p.M - 1);
+            abase[i] = p.Q + (int64_t)m0 * p.ldq + 32 * fh;
+            avoff[i] = (uint32_t)((m - m0) * p.ldq + 16 * g);
+        }
+    }
+    astride = p.qtiled ? 2048 : 64;
+    abytes = p.qtiled ? 1024u : (uint32_t)(BM * p.ldq);
+    // LDS: stage buffer b holds UPS units of kFrags fragments; fragment f of
+    // unit h lands at b * kStageBytes + h * kUnitBytes + f * 1024
+    auto issue_a = [&](int st) {
+        const int buf = st % NB;
+#pragma unroll
+        for (int h = 0; h < UPS; ++h) {
+            const int u = st * UPS + h;
+#pragma unroll
+            for (int i = 0; i < kFragsPerWave; ++i) {
+                const int f = wave * kFragsPerWave + i;
+                const __amdgpu_buffer_rsrc_t rs = unit_rsrc(abase[i], astride * (ub + u), u < nu, abytes);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rs, (__attribute__((address_space(3))) void *)(smem + buf * kStageBytes + h * kUnitBytes + f * 1024),
+                    16, avoff[i], 0, 0, 0);
+            }
+        }
+    };
+    v4u br[D][UPS][WNT];
+    auto issue_b = [&](int slot, int st) {
+#pragma unroll
+        for (int h = 0; h < UPS; ++h) {
+            const int u = st * UPS + h;
+#pragma unroll
+            for (int j = 0; j < WNT; ++j) {
+                const __amdgpu_buffer_rsrc_t rs =
+                    unit_rsrc(bbase[j], (int64_t)(ub + u) * kBlockBytes, u < nu, kBlockBytes);
+                br[slot][h][j] =
+                    __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rs, 16u * (uint32_t)lane, 0, 0));
+            }
+        }
+    };
+
+    __syncthreads();  // the previous work item of this workgroup may still read LDS
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+        issue_a(d);
+        issue_b(d, d);
+    }
+
+    v16i acc[WMS][2 * WNT];
+#pragma unroll
+    for (int i = 0; i < WMS; ++i)
+#pragma unroll
+        for (int j = 0; j < 2 * WNT; ++j) acc[i][j] = (v16i){};
+
+    // s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding:
+    // vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
+    constexpr int kAfter = (D - 1) * UPS * (kFragsPerWave + WNT);  // loads of the later stages
+    constexpr int kWaitLater = 0x0F70 | (kAfter & 15) | ((kAfter >> 4) << 14);
+    static_assert(kAfter < 64, "wait count fits the counter");
+    auto step = [&](int s, int st) {
+        if constexpr (PRIO) __builtin_amdgcn_s_setprio(1);
+        __builtin_amdgcn_s_waitcnt(kWaitLater);
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        issue_a(st + D);
+        const int8_t *sb = smem + (st % NB) * kStageBytes + 16 * lane;
+        v4i b[UPS][WNT][4];
+#pragma unroll
+        for (int h = 0; h < UPS; ++h)
+#pragma unroll
+            for (int j = 0; j < WNT; ++j) {
+                const v4u w = br[s][h][j];
+                b[h][j][0] = planes(w.x);
+                b[h][j][1] = planes(w.y);
+                b[h][j][2] = planes(w.z);
+                b[h][j][3] = planes(w.w);
+            }
+        __builtin_amdgcn_sched_barrier(0);
+        issue_b(s, st + D);
+        if constexpr (PRIO) __builtin_amdgcn_s_setprio(0);
+#pragma unroll
+        for (int h = 0; h < UPS; ++h) {
+#pragma unroll
+            for (int kh = 0; kh < 2; ++kh) {
+                v4i a[WMS];
+#pragma unroll
+                for (int i = 0; i < WMS; ++i)
+                    a[i] = *reinterpret_cast<const v4i *>(sb + h * kUnitBytes + (2 * i + kh) * 1024);
+#pragma unroll
+                for (int i = 0; i < WMS; ++i)
+#pragma unroll
+                    for (int j = 0; j < WNT; ++j) {
+                        // word (s, kh) of the slot: rows 32 s of the tile, code half kh
+                        acc[i][2 * j] = mfma_i8(a[i], b[h][j][kh], acc[i][2 * j]);
+                        acc[i][2 * j + 1] = mfma_i8(a[i], b[h][j][2 + kh], acc[i][2 * j + 1]);
+                    }
+            }
+        }
+    };
+    int s0 = 0;
+    for (; s0 + D <= KS; s0 += D) {
+#pragma unroll
+        for (int s = 0; s < D; ++s) step(s, s0 + s);
+    }
+#pragma unroll
+    for (int s = 0; s < D - 1; ++s)
+        if (s0 + s < KS) step(s, s0 + s);
+
+    // the surplus stages' loads (zeros) must land before LDS is reused
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    if (tid < BM) {
+        cs[tid] = cs_r;
+        rsum[tid] = rs_r;
+    }
+
+    if (p.ks > 1) {
+        constexpr int kAcc = 32 * WMS * WNT;  // accumulators per thread
+        int32_t *part = p.acc_ws + (int64_t)item * p.ks * (kAcc * kThreads);
+#pragma unroll
+        for (int i = 0; i < WMS; ++i)
+#pragma unroll
+            for (int s2 = 0; s2 < 2 * WNT; ++s2)
+#pragma unroll
+                for (int e = 0; e < 16; ++e)
+                    put_partial(part + ((int64_t)split * kAcc + (i * 2 * WNT + s2) * 16 + e) * kThreads + tid,
+                                acc[i][s2][e]);
+        if (!arrive_last(p, item)) return;
+        for (int jj = 0; jj < p.ks; ++jj) {
+            if (jj == split) continue;
+#pragma unroll
+            for (int i = 0; i < WMS; ++i)
+#pragma unroll
+                for (int s2 = 0; s2 < 2 * WNT; ++s2) {
+                    int32_t v[16];
+#pragma unroll
+                    for (int e = 0; e < 16; ++e)
+                        v[e] = get_partial(part + ((int64_t)jj * kAcc + (i * 2 * WNT + s2) * 16 + e) * kThreads + tid);
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) acc[i][s2][e] += v[e];
+                }
+        }
+    }
+
+    // epilogue: rescale, transpose through LDS (32 token rows x 64 weight
+    // rows per wave at a time), 16-byte non-temporal stores
+    __syncthreads();  // every wave is done with the activation stages; scales visible
+    float *ep = reinterpret_cast<float *>(smem) + wave * (32 * kEpiStride);
+    const bool vec_ok = (p.N & 3) == 0;
+    BL_GLOBAL float *Y = gstore_ptr<float>(p.Y);
+#pragma unroll
+    for (int j = 0; j < WNT; ++j)
+#pragma unroll
+        for (int i = 0; i < WMS; ++i) {
+            __builtin_amdgcn_wave_barrier();
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int row = 8 * (e >> 2) + 4 * g + (e & 3);
+                    const int rr = 32 * i + row;
+                    ep[row * kEpiStride + 32 * s2 + r] = (float)(acc[i][2 * j + s2][e] - rsum[rr]) * cs[rr];
+                }
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const int row = (lane >> 4) + 4 * k;
+                const int c4 = 4 * (lane & 15);
+                const int m = m0 + 32 * i + row;
+                const int n = 64 * tile[j] + c4;
+                const v4f_t v = *reinterpret_cast<const v4f_t *>(&ep[row * kEpiStride + c4]);
+                if (tv[j] && m < p.M) {
+                    const int64_t o = (int64_t)m * p.N + n;
+                    if (vec_ok && n + 3 < p.N) {
+                        __builtin_nontemporal_store(v, reinterpret_cast<BL_GLOBAL v4f_t *>(Y + o));
+                    } else {
+                        if (n < p.N) __builtin_nontemporal_store(v.x, Y + o);
+                        if (n + 1 < p.N) __builtin_nontemporal_store(v.y, Y + o + 1);
+                        if (n + 2 < p.N) __builtin_nontemporal_store(v.z, Y + o + 2);
+                        if (n + 3 < p.N) __builtin_nontemporal_store(v.w, Y + o + 3);
+                    }
+                }
+            }
+        }
+    if (p.acc_out) {
+#pragma unroll
+        for (int j = 0; j < WNT; ++j) {
+            if (!tv[j]) continue;
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) {
+                const int n = 64 * tile[j] + 32 * s2 + r;
+                if (n >= p.N) continue;
+#pragma unroll
+                for (int i = 0; i < WMS; ++i)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        const int row = 32 * i + 8 * (e >> 2) + 4 * g + (e & 3);
+                        const int m = m0 + row;
+                        if (m < p.M)
+                            gstore_ptr<int32_t>(p.acc_out)[(int64_t)m * p.N + n] = acc[i][2 * j + s2][e] - rsum[row];
+                    }
+            }
+        }
+    }
+}
+
 // Instantiations (the value of the tile-variant knob):
 //   0  64 tokens x 256 rows, each wave 64 x 64 (four waves along N);
 //   1  128 tokens x 256 rows, each wave 64 x 128 (2 x 2 waves): half the LDS
@@ -525,6 +816,18 @@ __device__ __forceinline__ void tile_dispatch(const Problem &p, int local)
         tile_body<4, 1, 1, 2, false>(p, local);
     else if constexpr (V == 19)
         tile_body_ups<2, 2>(p, local);
+    else if constexpr (V == 20)
+        tile_body_dma<2, 1, 3, 2>(p, local);
+    else if constexpr (V == 21)
+        tile_body_dma<2, 1, 4, 3>(p, local);
+    else if constexpr (V == 23)
+        tile_body_dma<4, 1, 3, 2>(p, local);
+    else if constexpr (V == 24)
+        tile_body_dma<2, 2, 3, 2>(p, local);
+    else if constexpr (V == 27)
+        tile_body_dma<2, 1, 3, 2, 2, true>(p, local);
+    else if constexpr (V == 28)
+        tile_body_dma<2, 1, 2, 1, 4>(p, local);
     else
         tile_body_ups<2, 4>(p, local);
 }
@@ -538,15 +841,26 @@ __device__ inline int xcd_logical(int b, int per)
     return (b & 7) * per + (b >> 3);
 }
 
+// Waves per SIMD each instantiation is compiled for (the register budget):
+// the DMA-staged 64 x 64-per-wave tile fits 128 VGPRs (four waves), the
+// larger per-wave tiles hold 128 or 256 accumulators.
 template <int V>
-__global__ __launch_bounds__(kThreads, 2) void tile_single_kernel(Problem p, int items, int per)
+struct TileWaves {
+    static constexpr int lo = (V == 19 || V == 20 || V == 27) ? 4 : (V == 21 || V == 28) ? 3 : 2;
+    static constexpr int hi = (V == 19 || V == 20 || V == 27) ? 4 : (V == 21 || V == 28) ? 3 : (V >= 23) ? 2 : 8;
+};
+
+template <int V>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(TileWaves<V>::lo, TileWaves<V>::hi)))
+void tile_single_kernel(Problem p, int items, int per)
 {
     const int j = xcd_logical(blockIdx.x, per);
     if (j < items) tile_dispatch<V>(p, j);
 }
 
 template <int V>
-__global__ __launch_bounds__(kThreads, 2) void tile_group_kernel(const Problem *__restrict__ probs,
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(TileWaves<V>::lo, TileWaves<V>::hi)))
+void tile_group_kernel(const Problem *__restrict__ probs,
                                                                  const uint2 *__restrict__ item_map)
 {
     const uint2 it = item_map[blockIdx.x];
@@ -554,7 +868,8 @@ __global__ __launch_bounds__(kThreads, 2) void tile_group_kernel(const Problem *
 }
 
 template <int V>
-__global__ __launch_bounds__(kThreads, 2) void tile_multi_kernel(ProblemSet ps)
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(TileWaves<V>::lo, TileWaves<V>::hi)))
+void tile_multi_kernel(ProblemSet ps)
 {
     const int i = multi_index(ps, blockIdx.x);
     tile_dispatch<V>(ps.p[i], (int)blockIdx.x - ps.begin[i]);
@@ -575,6 +890,12 @@ __global__ __launch_bounds__(kThreads, 2) void tile_multi_kernel(ProblemSet ps)
     case 11: hipLaunchKernelGGL(KERNEL<11>, __VA_ARGS__); break;                           \
     case 12: hipLaunchKernelGGL(KERNEL<12>, __VA_ARGS__); break;                           \
     case 19: hipLaunchKernelGGL(KERNEL<19>, __VA_ARGS__); break;                           \
+    case 20: hipLaunchKernelGGL(KERNEL<20>, __VA_ARGS__); break;                           \
+    case 21: hipLaunchKernelGGL(KERNEL<21>, __VA_ARGS__); break;                           \
+    case 23: hipLaunchKernelGGL(KERNEL<23>, __VA_ARGS__); break;                           \
+    case 24: hipLaunchKernelGGL(KERNEL<24>, __VA_ARGS__); break;                           \
+    case 27: hipLaunchKernelGGL(KERNEL<27>, __VA_ARGS__); break;                           \
+    case 28: hipLaunchKernelGGL(KERNEL<28>, __VA_ARGS__); break;                           \
     default: hipLaunchKernelGGL(KERNEL<18>, __VA_ARGS__); break;                           \
     }
 

@@ -801,3 +801,27 @@ def test_relu2_gate_special_cases():
     np.testing.assert_array_equal(Qb, -Qa)
     np.testing.assert_array_equal(ab, aa)
     np.testing.assert_array_equal(rsb, -rsa)
+
+
+def test_oracle_results_do_not_depend_on_thread_count(tmp_path):
+    # the OpenMP pragmas only split independent outputs across threads: the
+    # same inputs give the same bytes with one thread as with four (sizes
+    # above the pragmas' thresholds, so every parallel loop runs parallel)
+    import sys
+    script = (
+        "import numpy as np, sys; sys.path.insert(0, %r)\n"
+        "import oracle as O, synth\n"
+        "T = synth.random_ternary(1030, 1100, seed=5); X = synth.activations_np(1000, 1100, seed=6)\n"
+        "Q, a, rs = O.quant_act(X); P = O.pack(T); T2, bad = O.unpack(P, 1030, 1100); assert bad == 0\n"
+        "acc = O.matmul(Q[:9], T2); Y, _ = O.forward_packed(X[:9], P, 0.02, 1030)\n"
+        "rows = np.array([0, 64, 1029]); ap = O.matmul_packed_rows(Q, P, 1030, 1100, rows)\n"
+        "np.savez(sys.argv[1], Q=Q, a=a, rs=rs, T2=T2, acc=acc, Y=Y, ap=ap, n=O.threads())\n" % ROOT)
+    outs = []
+    for threads in ("1", "4"):
+        f = tmp_path / f"t{threads}.npz"
+        env = dict(os.environ, OMP_NUM_THREADS=threads)
+        subprocess.run([sys.executable, "-c", script, str(f)], env=env, check=True)
+        outs.append(np.load(f))
+    assert int(outs[0]["n"]) == 1 and int(outs[1]["n"]) == 4
+    for key in ("Q", "a", "rs", "T2", "acc", "Y", "ap"):
+        np.testing.assert_array_equal(outs[0][key], outs[1][key], err_msg=key)
