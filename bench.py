@@ -12,17 +12,18 @@ timing, like loading an inference-ready checkpoint.
 Printed: one JSON line.  value = packed weight bytes per step / step time.
 roofline = the contraction kernel's algorithmic bytes (packed weights + int8
 activations + fp32 outputs) over its average duration (HIP events on the
-launch stream), against 8 TB/s.  prefill = the same 210 matrices at
-M = 512 (int8 TOP/s against 5.0 POP/s dense int8).  graph = the decode
-step captured once in a HIP graph and replayed.  curves = latency of a full
-sweep over the 3B-class stack at M in {1, 8, 64, 256} (and, on request, the
-70B-class stack at M in {1, 16, 176}); for 3B also the same stack chained as
-pre-norm blocks (residual adds, norms, the gated squared-ReLU, a single-key
-attention; q|k|v and gate|up each one launch) at M in {1, 8, 64}, eager and
-as a replayed HIP graph.  bt5 = the same 2B stack packed
-five codes per byte (BT5-T32, 1.6 bits per weight) at M in {1, 8, 16},
-next to the 2-bit path at the same M.  cpu_baseline = the CPU oracle
-(single thread) on a bounded sample of the same workload.
+launch stream; the median of 7 windows, with min and max), against 8 TB/s.
+prefill = the same 210 matrices at M = 512 (int8 TOP/s against 5.0 POP/s
+dense int8).  graph = the decode step captured once in a HIP graph and
+replayed.  curves = latency of a full sweep over the 3B-class stack at M in
+{1, 8, 64, 256} and the 70B-class stack (17 GB resident) at M in {1, 16,
+176}; for 3B also the same stack chained as pre-norm blocks (residual adds,
+norms, the gated squared-ReLU, a single-key attention; q|k|v and gate|up
+each one launch) at M in {1, 8, 64, 256}, eager and as a replayed HIP
+graph.  bt5 = the same 2B stack packed five codes per byte (BT5-T32, 1.6
+bits per weight) at M in {1, 8, 16}, next to the 2-bit path at the same M.
+cpu_baseline = the CPU oracle on the host's cores on a bounded sample of
+the same workload (decode, and one prefill layer extrapolated).
 
 Inputs are synthetic: weights ~ N(0, 0.02) drawn on the device per matrix,
 activations ~ N(0, 1) (prefill: 1% of channels x20), seeded.
@@ -94,11 +95,14 @@ def make_plan(B, torch, mats, M, dev, outliers=0.0, seed0=7, fmt=0):
     return plan, probs
 
 
-def time_plan(torch, plan, steps, warmup):
+def time_plan(torch, plan, steps, warmup, windows=7):
     """Wall time per step over `steps` steps (quantize + contract), then the
-    contraction kernel alone: `steps` back-to-back launches between one pair
-    of HIP events on the launch stream (torch's current stream), giving its
-    average launch duration without per-launch event overhead."""
+    contraction kernel alone: `windows` event windows, each `steps`
+    back-to-back launches between one pair of HIP events on the launch
+    stream (torch's current stream), giving the average launch duration
+    without per-launch event overhead.  Returns (ms per step, median kernel
+    ms, {min, median, max} over the windows): the median keeps one window
+    taken while the clock settles from deciding the figure."""
     for _ in range(warmup):
         plan.quant_act()
         plan.matmul()
@@ -109,13 +113,20 @@ def time_plan(torch, plan, steps, warmup):
         plan.matmul()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record()
-    for _ in range(steps):
-        plan.matmul()
-    b.record()
-    torch.cuda.synchronize()
-    return wall / steps * 1e3, a.elapsed_time(b) / steps
+    per = []
+    for _ in range(windows):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(steps):
+            plan.matmul()
+        b.record()
+        torch.cuda.synchronize()
+        per.append(a.elapsed_time(b) / steps)
+    per.sort()
+    med = per[len(per) // 2]
+    spread = {"min": round(per[0], 5), "median": round(med, 5), "max": round(per[-1], 5), "windows": windows,
+              "launches_per_window": steps}
+    return wall / steps * 1e3, med, spread
 
 
 def time_graph(torch, plan, steps, warmup):
@@ -153,16 +164,19 @@ def curve(B, torch, model, Ms, dev, steps, warmup):
     out = {"matrices": len(mats), "packed_bytes": packed, "points": []}
     for M in Ms:
         plan, probs = make_plan(B, torch, mats, M, dev)
-        ms, kern = time_plan(torch, plan, steps, warmup)
+        ms, kern, _ = time_plan(torch, plan, steps, warmup, windows=5)
         ops = sum(2 * M * m["N"] * m["K"] for m in mats)
+        alg = packed + sum(M * B.q_stride(m["K"]) + 8 * M + 4 * M * m["N"] for m in mats)
         out["points"].append({"M": M, "ms_per_sweep": round(ms, 4), "contraction_ms": round(kern, 4),
                               "packed_GBps": round(packed / (ms * 1e-3) / 1e9, 1),
-                              "TOPs": round(ops / (ms * 1e-3) / 1e12, 1)})
+                              "TOPs": round(ops / (ms * 1e-3) / 1e12, 1),
+                              "contraction_hbm_frac": round(alg / (kern * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                              "contraction_mfma_frac": round(ops / (kern * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4)})
         log(f"  {model} M={M}: {ms:.3f} ms per sweep")
         del plan, probs
     if model == "3b":
         log("timing the 3B stack chained as pre-norm blocks")
-        out["chained"] = stack_curve(B, torch, mats, dev, [1, 8, 64], steps, warmup)
+        out["chained"] = stack_curve(B, torch, mats, dev, [1, 8, 64, 256], steps, warmup)
     del mats
     torch.cuda.empty_cache()
     return out
@@ -178,10 +192,10 @@ def bt5_section(B, torch, mats, dev, Ms, steps, warmup, model):
            "points": []}
     for M in Ms:
         plan, probs = make_plan(B, torch, mats, M, dev, fmt=1)
-        ms5, k5 = time_plan(torch, plan, steps, warmup)
+        ms5, k5, spread5 = time_plan(torch, plan, steps, warmup)
         del plan, probs
         plan, probs = make_plan(B, torch, mats, M, dev)
-        ms2, k2 = time_plan(torch, plan, steps, warmup)
+        ms2, k2, _ = time_plan(torch, plan, steps, warmup)
         del plan, probs
         alg = packed5 + sum(M * B.q_stride5(m["K"]) + 8 * M + 4 * M * m["N"] for m in mats)
         gbs = alg / (k5 * 1e-3) / 1e9
@@ -189,7 +203,7 @@ def bt5_section(B, torch, mats, dev, Ms, steps, warmup, model):
             "M": M, "ms_per_step": round(ms5, 5), "kernel_ms": round(k5, 5),
             "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(gbs / HBM_PEAK_GBS, 4), "bytes_per_launch": alg,
-                         "traffic": load_traffic(f"bt5_{model}_m{M}")},
+                         "traffic": load_traffic(f"bt5_{model}_m{M}"), "kernel_ms_spread": spread5},
             "bl2_ms_per_step": round(ms2, 5), "bl2_kernel_ms": round(k2, 5),
             "kernel_speedup_vs_bl2": round(k2 / k5, 3)})
         log(f"  BT5 M={M}: kernel {k5 * 1e3:.1f} us (2-bit {k2 * 1e3:.1f} us)")
@@ -423,29 +437,65 @@ def load_traffic(name):
     return e.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(model: str, seconds: float = 10.0):
-    """The oracle, untuned, single thread: unpack + activation quantization +
-    triple-loop contraction + rescale on one layer of the stack (7 matrices,
-    M = 1), repeated until about `seconds` of CPU time."""
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(model: str, seconds: float = 10.0, prefill_M: int = 512, prefill_seconds: float = 6.0):
+    """The oracle, untuned, on the host's cores (its OpenMP loops split the
+    independent outputs over OMP_NUM_THREADS threads, every core by
+    default): unpack + activation quantization + triple-loop contraction +
+    rescale, on layer 0 of the stack (7 matrices).  Decode (M = 1) is
+    repeated until about `seconds` of wall time; the prefill leg (M =
+    prefill_M, 1% outlier channels) runs the layer until about
+    `prefill_seconds` and is extrapolated to the whole stack, labelled so."""
     import oracle as O
     spec = synth.MODELS[model]
     work = []
     for j, (name, K, N) in enumerate(spec["shapes"]):
         W = synth.weights_np(N, K, spec["sigma"], synth.matrix_seed(0, j))
         T, g = O.quantize_weights(W)
-        work.append((synth.activations_np(1, K, 7 + j), O.pack(T), g, N, N * K // 4))
+        work.append((K, N, O.pack(T), g))
         del W, T
+    threads = O.threads()
     reps, t, nbytes = 0, 0.0, 0
+    xs = [synth.activations_np(1, K, 7 + j) for j, (K, N, P, g) in enumerate(work)]
     while t < seconds:
         t0 = time.perf_counter()
-        for X, P, g, N, b in work:
+        for X, (K, N, P, g) in zip(xs, work):
             O.forward_packed(X, P, g, N)
-            nbytes += b
+            nbytes += N * K // 4
         t += time.perf_counter() - t0
         reps += 1
-    return {"value": nbytes / t / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"layer 0 of the {model.upper()} stack (7 matrices, M=1) x {reps} passes, "
-                      f"{t:.1f} s single-thread: unpack + act quant + int32 triple loop + rescale"}
+    out = {"value": nbytes / t / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+           "sample": f"layer 0 of the {model.upper()} stack (7 matrices, M=1) x {reps} passes, {t:.1f} s on "
+                     f"{threads} threads: unpack + act quant + int32 triple loop + rescale",
+           "cpu_model": _cpu_model(), "host_cpus": os.cpu_count()}
+    if prefill_M:
+        xs = [synth.activations_np(prefill_M, K, 70 + j, outlier_frac=0.01) for j, (K, N, P, g) in enumerate(work)]
+        passes, tp = 0, 0.0
+        while tp < prefill_seconds or passes == 0:
+            t0 = time.perf_counter()
+            for X, (K, N, P, g) in zip(xs, work):
+                O.forward_packed(X, P, g, N)
+            tp += time.perf_counter() - t0
+            passes += 1
+        ops = sum(2 * prefill_M * N * K for K, N, P, g in work) * passes
+        per_layer = tp / passes
+        out["prefill"] = {"M": prefill_M, "value": round(ops / tp / 1e12, 4), "unit": "TOP/s",
+                          "layer_s": round(per_layer, 3),
+                          "sweep_s_extrapolated": round(per_layer * spec["layers"], 2),
+                          "sample": f"layer 0 (7 matrices) at M={prefill_M} x {passes} passes, {tp:.1f} s on "
+                                    f"{threads} threads; the {spec['layers']}-layer sweep time is that layer's "
+                                    f"time x {spec['layers']} (extrapolated)"}
+    return out
 
 
 def main():
@@ -459,8 +509,8 @@ def main():
     ap.add_argument("--prefill-M", type=int, default=512)
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--curves", default="3b",
-                    help="comma list of latency-vs-M curves to add: 3b (M 1,8,64,256), 70b (M 1,16,176); "
+    ap.add_argument("--curves", default="3b,70b",
+                    help="comma list of latency-vs-M curves: 3b (M 1,8,64,256, and chained), 70b (M 1,16,176); "
                          "'none' to skip")
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-bt5", action="store_true", help="skip the five-codes-per-byte comparison")
@@ -499,7 +549,7 @@ def main():
     M = args.M
     plan, probs = make_plan(B, torch, mats, M, dev)
     log(f"timing decode sweep: {len(mats)} matrices, M={M}, {packed / 1e6:.1f} MB packed")
-    ms, kern_ms = time_plan(torch, plan, args.steps, args.warmup)
+    ms, kern_ms, spread = time_plan(torch, plan, args.steps, args.warmup)
     value = packed / (ms * 1e-3) / 1e9
     act_bytes = sum(M * B.q_stride(m["K"]) + 8 * M for m in mats)
     out_bytes = sum(4 * M * m["N"] for m in mats)
@@ -529,7 +579,8 @@ def main():
                      "kernel": "stream contraction (grouped, one launch per step)" +
                                (f", BITLINEAR_DOT4_VARIANT={os.environ['BITLINEAR_DOT4_VARIANT']}"
                                 if os.environ.get("BITLINEAR_DOT4_VARIANT") else ""),
-                     "kernel_ms_mean": round(kern_ms, 5), "bytes_per_launch": alg_bytes},
+                     "kernel_ms_mean": round(kern_ms, 5), "kernel_ms_spread": spread,
+                     "bytes_per_launch": alg_bytes},
     }
     if gms is not None:
         result["graph"] = {"ms_per_step": round(gms, 5), "GBps": round(packed / (gms * 1e-3) / 1e9, 2),
@@ -537,19 +588,12 @@ def main():
     del plan, probs
     torch.cuda.empty_cache()
 
-    if not args.no_bt5:
-        log("timing BT5-T32 sweeps")
-        result["bt5"] = bt5_section(B, torch, mats, dev, [1, 8, 16], args.steps, args.warmup, args.model)
-        for m in mats:
-            m["P5"] = None
-        torch.cuda.empty_cache()
-
     if not args.no_prefill:
         PM = args.prefill_M
         plan, probs = make_plan(B, torch, mats, PM, dev, outliers=0.01)
         log(f"timing prefill sweep: M={PM}")
-        steps = max(3, args.steps // 5)
-        pms, pkern = time_plan(torch, plan, steps, max(1, args.warmup // 2))
+        steps = max(20, args.steps)
+        pms, pkern, pspread = time_plan(torch, plan, steps, max(5, args.warmup))
         ops = sum(2 * PM * m["N"] * m["K"] for m in mats)
         result["prefill"] = {
             "M": PM, "ms_per_step": round(pms, 4), "value": round(ops / (pms * 1e-3) / 1e12, 2),
@@ -559,9 +603,16 @@ def main():
                          "frac": round(ops / (pkern * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4),
                          "traffic": load_traffic(f"tile_{args.model}_m{PM}"),
                          "kernel": "tile contraction (grouped)", "kernel_ms_mean": round(pkern, 4),
-                         "ops_per_launch": ops},
+                         "kernel_ms_spread": pspread, "ops_per_launch": ops},
         }
         del plan, probs
+        torch.cuda.empty_cache()
+
+    if not args.no_bt5:
+        log("timing BT5-T32 sweeps")
+        result["bt5"] = bt5_section(B, torch, mats, dev, [1, 8, 16], args.steps, args.warmup, args.model)
+        for m in mats:
+            m["P5"] = None
         torch.cuda.empty_cache()
 
     if not args.no_peaks:

@@ -60,70 +60,47 @@ int check_mnk(int64_t M, int64_t N, int64_t K)
     return check_nk(N, K);
 }
 
-// Tuning knobs, read once from the environment (immutable afterwards).
+// Measurement knobs, read once from the environment (immutable afterwards).
 struct Knobs {
-    int dot4_max_m = 2;          // M <= this takes a packed-dot4 kernel (knob: 0..4)
-    int dot4_variant = 3;        // 0: global activations, 2/3: LDS-staged (unroll 4/8), 5: table lookup
-    int fuse_quant = 0;          // single-token problems quantize in the dot4 prologue
+    int lut = 0;                 // one-token problems take the table-lookup comparison kernel
     int split_target = 1024;     // aim for at least this many workgroups
     int xcd_order = 3;           // bit 0: streaming kernel, bit 1: tile kernel
     int mfma_tiles = 0;          // tiles per wave of the streaming MFMA kernel: 0 = by launch size, 1, 2
-    int tile_variant = -1;       // force a tile-kernel instantiation (see tile_variant())
 };
 const Knobs &knobs()
 {
     static const Knobs k = [] {
         Knobs v;
-        if (const char *s = getenv("BITLINEAR_DOT4_MAX_M"))
-            v.dot4_max_m = atoi(s) < 0 ? 0 : (atoi(s) > bl::kDot4MaxTokens ? bl::kDot4MaxTokens : atoi(s));
         if (const char *s = getenv("BITLINEAR_SPLIT_TARGET")) v.split_target = atoi(s) > 0 ? atoi(s) : 1;
-        if (const char *s = getenv("BITLINEAR_DOT4_VARIANT"))
-            v.dot4_variant = (atoi(s) == 0 || atoi(s) == 2 || atoi(s) == 5) ? atoi(s) : 3;
-        if (const char *s = getenv("BITLINEAR_FUSE_QUANT")) v.fuse_quant = atoi(s) != 0;
+        if (const char *s = getenv("BITLINEAR_DOT4_VARIANT")) v.lut = atoi(s) == 5;
         if (const char *s = getenv("BITLINEAR_XCD_ORDER")) v.xcd_order = atoi(s) & 3;
         if (const char *s = getenv("BITLINEAR_MFMA_TILES")) v.mfma_tiles = (atoi(s) == 1 || atoi(s) == 2) ? atoi(s) : 0;
-        if (const char *s = getenv("BITLINEAR_TILE_VARIANT")) v.tile_variant = atoi(s);
         return v;
     }();
     return k;
 }
 
-// Tile-kernel instantiation (the list is next to the tile kernels): 19 (64
-// token rows per tile, two units per stage) unless the knob picks another.
-// Against the 128-token tile it is as fast at M = 256 and 512 and pads
-// less elsewhere (M = 64: 0.27 vs 0.40 ms; 176: 0.40 vs 0.49 ms on 3B/2B
-// stacks).  5..7 read fragment-ordered activations that only the library's
-// own quantizer writes, so caller-supplied activations map them to their
-// row-major twins 2, 0, 1.
-bool tile_variant_known(int v) { return v == 0 || v == 1 || v == 2 || (v >= 5 && v <= 7) || (v >= 10 && v <= 12) || (v >= 18 && v <= 28 && v != 22 && v != 25 && v != 26); }
-int tile_variant(bool own_q)
-{
-    int v = knobs().tile_variant;
-    if (!tile_variant_known(v)) return 19;
-    if (!own_q) {  // caller-supplied activations are row-major
-        if (v == 5) return 2;
-        if (v == 6) return 0;
-        if (v == 7) return 1;
-    }
-    return v;
-}
-int tile_bm(int variant) { return (variant == 0 || variant == 6 || variant == 19 || variant == 20 || variant == 21 || variant == 24 || variant >= 27) ? 64 : 128; }
-// weight rows per tile-kernel work item
-int tile_rows(int variant) { return variant == 24 ? 512 : 256; }
-// 20, 21 read either layout; the library's own activations are fragment-ordered
-bool tile_frag(int variant, bool own_q) { return (variant >= 5 && variant <= 7) || (own_q && variant >= 20 && !getenv("BITLINEAR_TILE_ROWMAJOR")); }
+// Token rows per tile-kernel work item (64-token tiles, two units per stage:
+// against a 128-token tile it is as fast at M = 256 and 512 and pads less
+// elsewhere -- M = 64: 0.27 vs 0.40 ms; 176: 0.40 vs 0.49 ms on 3B/2B stacks)
+// and weight rows per item (four 64-row tiles, one per wave).
+constexpr int kTileTokens = 64;
+constexpr int kTileRowTiles = 4;
 
+// The dot4 kernels hold 64 bytes of activations per token slot per unit of
+// the workgroup's K range (decompose caps the range to fit 64 KiB).
+constexpr int kStreamLdsMax = 64 * 1024;
 // The table-lookup dot4 variant (knob value 5) runs single-token problems
 // with at most kLutMaxUnits units (64 KiB of table) per workgroup.
 constexpr int kLutMaxUnits = 64;
-bool lut_variant(int64_t M) { return knobs().dot4_variant == 5 && M == 1 && knobs().dot4_max_m >= 1; }
-// The dot4 kernel for 2..4 tokens stages 64 bytes per token slot per unit:
+bool lut_variant(int64_t M) { return knobs().lut && M == 1; }
+// The dot4 kernel for two tokens stages 64 bytes per token slot per unit:
 // at most kDot4TokMaxUnits units (64 KiB) per workgroup.
 constexpr int kDot4TokMaxUnits = 64 * 1024 / (64 * bl::kDot4MaxTokens);
-bool dot4_tokens(int64_t M) { return M >= 2 && M <= knobs().dot4_max_m; }
+bool dot4_tokens(int64_t M) { return M >= 2 && M <= bl::kDot4MaxTokens; }
 // Token counts the 32x32x32 MFMA stream takes (its work items are groups of
 // 4 * tiles-per-wave row tiles; the dot4 kernels work per tile).
-bool mfma32_stream(int64_t M) { return M <= kStreamMaxM && M > knobs().dot4_max_m; }
+bool mfma32_stream(int64_t M) { return M <= kStreamMaxM && M > bl::kDot4MaxTokens; }
 // Tiles per wave of that stream for a launch with `groups` kGroupTiles-tile
 // groups: two when the groups alone fill the part (the split target), else
 // one, which doubles the workgroups without more split-K reductions.
@@ -181,21 +158,25 @@ void decompose(Problem &p, int64_t base_items, bool own_q, bool groups4 = false,
             p.upsplit = kDot4TokMaxUnits;
             p.ks = (p.KU + kDot4TokMaxUnits - 1) / kDot4TokMaxUnits;
         }
+        // the one-token kernel stages 64 bytes per unit: longer ranges are
+        // split into equal parts that fit 64 KiB
+        if (p.M == 1 && p.upsplit > kStreamLdsMax / 64) {
+            const int32_t ks = (p.KU + kStreamLdsMax / 64 - 1) / (kStreamLdsMax / 64);
+            p.upsplit = (p.KU + ks - 1) / ks;
+            p.ks = (p.KU + p.upsplit - 1) / p.upsplit;
+        }
     } else {
         p.kind = 1;
-        const int v = tile_variant(own_q);
-        p.mtile = tile_bm(v);
-        p.qtiled = tile_frag(v, own_q) ? 1 : 0;
+        p.mtile = kTileTokens;
         p.mt = (int32_t)((p.M + p.mtile - 1) / p.mtile);
-        p.ntt = (p.NT + tile_rows(v) / 64 - 1) / (tile_rows(v) / 64);
-        // K splits for the default instantiation while the launch's work
-        // items (tile_base, or this problem's alone) are short of the
-        // target: at most kTileMaxSplits, keeping >= 8 units (4 stages) per
+        p.ntt = (p.NT + kTileRowTiles - 1) / kTileRowTiles;
+        // K splits while the launch's work items (tile_base, or this
+        // problem's alone) are short of the target: at most kTileMaxSplits, keeping >= 8 units (4 stages) per
         // split.  Each split's partials are 64 KiB per item, read back by
         // the item's last split, so more splits cost more than they gain.
         const int64_t items = tile_base > 0 ? tile_base : (int64_t)p.mt * p.ntt;
         const int64_t target = knobs().split_target;
-        if (v >= 19 && items < target) {
+        if (items < target) {
             int64_t ks = (target + items - 1) / items;
             int64_t cap = p.KU / 8;
             if (cap > kTileMaxSplits) cap = kTileMaxSplits;
@@ -261,30 +242,24 @@ void decompose_single(Problem &p, bool own_q)
     decompose(p, g4 ? (nt + 4 * tpw - 1) / (4 * tpw) : nt, own_q, g4, tpw);
 }
 
-// The LDS-staged dot4 variants hold 64 bytes of activations per unit of
-// the workgroup's K range; longer ranges fall back to global activations.
-constexpr int kStreamLdsMax = 64 * 1024;
 int stream_variant_for(int64_t M, int64_t upsplit)
 {
-    if (M > knobs().dot4_max_m) return 1;
-    if (M >= 2) return (int)(4 + M);  // 6, 7, 8; decompose keeps upsplit <= kDot4TokMaxUnits
-    const int v = knobs().dot4_variant;
-    if (v == 5) return upsplit <= kLutMaxUnits ? 5 : 3;
-    return (v != 0 && 64 * upsplit <= kStreamLdsMax) ? v : 0;
+    if (M > bl::kDot4MaxTokens) return 1;
+    if (M >= 2) return 6;  // decompose keeps upsplit <= kDot4TokMaxUnits
+    if (knobs().lut && upsplit <= kLutMaxUnits) return 5;
+    return 3;
 }
 
 
 // Dynamic LDS a problem of M tokens whose workgroups take upsplit units
 // needs under a streaming-kernel variant: activations, 64 bytes per token
-// slot per unit (one slot for 2..4; variant - 4 slots for 6..8, whose
-// one-token problems take one), or the lookup table (1 KiB per unit, 5);
-// none for 0 and 1.
+// slot per unit (one slot for 3; two for 6 except one-token problems), or
+// the lookup table (1 KiB per unit, 5); none for the MFMA stream (1, 9).
 int64_t stream_lds_need(int variant, int64_t M, int64_t upsplit)
 {
-    int64_t slots = 1;
-    if (variant < 2 || variant == 9) return 0;
+    if (variant == 1 || variant == 9) return 0;
     if (variant == 5) return 1024 * upsplit;
-    if (variant >= 6 && variant <= 8) slots = M == 1 ? 1 : variant - 4;
+    const int64_t slots = (variant == 6 && M > 1) ? bl::kDot4MaxTokens : 1;
     return 64 * slots * upsplit;
 }
 
@@ -341,7 +316,8 @@ hipError_t launch_contraction(const Problem &p, bool own_q, hipStream_t s)
         const int v = stream_variant_for(p.M, p.upsplit);
         return bl::launch_stream_single(p, v == 1 && p.stiles == 1 ? 9 : v, s);
     }
-    return bl::launch_tile_single(p, tile_variant(own_q), s);
+    (void)own_q;
+    return bl::launch_tile_single(p, s);
 }
 
 }  // namespace
@@ -607,13 +583,6 @@ int bitlinear_forward(const float *X, int64_t M, int64_t K, const uint8_t *P,
         p.tickets = reinterpret_cast<uint32_t *>(base + L.tick);
     }
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (p.kind == 0 && knobs().fuse_quant && stream_variant_for(p.M, p.upsplit) == 3) {
-        // one token: the dot4 kernel quantizes it in its prologue
-        if (p.tickets)
-            if (hipError_t e = bl::launch_zero_words(p.tickets, p.NT, s)) return hip_fail(e, "forward: zero tickets");
-        if (hipError_t e = bl::launch_stream_single(p, 4, s)) return hip_fail(e, "forward: fused matmul");
-        return BITLINEAR_OK;
-    }
     if (hipError_t e = bl::launch_quant_act(X, M, K, p.Q, p.ldq, p.qtiled, p.absmax, p.rowsum,
                                             p.tickets, p.tickets ? (int)bl::ticket_count(p) : 0, s))
         return hip_fail(e, "forward: quant_act");
@@ -750,9 +719,8 @@ int multi_plan(const int8_t *Q, int64_t ldq, int64_t M, int64_t K, const bitline
     // the tile kernel's work items over the whole launch (M > 32)
     int64_t tile_base = 0;
     if (!fmt && M > kStreamMaxM) {
-        const int v = tile_variant(false);
-        const int64_t bm = tile_bm(v), tn = tile_rows(v) / 64;
-        for (int i = 0; i < count; ++i) tile_base += (M + bm - 1) / bm * (((w[i].N + 63) / 64 + tn - 1) / tn);
+        for (int i = 0; i < count; ++i)
+            tile_base += (M + kTileTokens - 1) / kTileTokens * (((w[i].N + 63) / 64 + kTileRowTiles - 1) / kTileRowTiles);
     }
     int64_t items = 0, tick = 0, part = 0;
     for (int i = 0; i < count; ++i) {
@@ -782,8 +750,6 @@ int multi_plan(const int8_t *Q, int64_t ldq, int64_t M, int64_t K, const bitline
         mp.variant = stream_variant_for(M, max_upsplit);
         if (mp.variant == 1 && tpw == 1) mp.variant = 9;
         mp.lds = (int)stream_lds_need(mp.variant, M, max_upsplit);
-    } else if (mp.kind == 1) {
-        mp.variant = tile_variant(false);
     }
     mp.tick_bytes = up(tick, 256);
     mp.total_bytes = mp.tick_bytes + part;
@@ -834,7 +800,7 @@ int bitlinear_matmul_multi(const int8_t *Q, int64_t ldq, const float *absmax, co
     if (mp.kind == 0)
         e = bl::launch_stream_multi(mp.ps, mp.variant, mp.lds, s);
     else if (mp.kind == 1)
-        e = bl::launch_tile_multi(mp.ps, mp.variant, s);
+        e = bl::launch_tile_multi(mp.ps, s);
     else
         e = bl::launch_bt5_multi(mp.ps, (int)(M < bl::kBt5Tokens ? M : bl::kBt5Tokens), s);
     if (e) return hip_fail(e, "matmul_multi");
@@ -907,19 +873,14 @@ int build_group(const bitlinear_problem *in, int count, char *ws, GroupPlan &out
     if (base5 < 1) base5 = 1;
     // the tile kernel's work items over the whole launch
     int64_t tile_base = 0;
-    {
-        const int v = tile_variant(true);
-        const int64_t bm = tile_bm(v), tn = tile_rows(v) / 64;
-        for (int i = 0; i < count; ++i)
-            if (in[i].format != BITLINEAR_FORMAT_BT5 && in[i].M > kStreamMaxM)
-                tile_base += (in[i].M + bm - 1) / bm * (((in[i].N + 63) / 64 + tn - 1) / tn);
-    }
+    for (int i = 0; i < count; ++i)
+        if (in[i].format != BITLINEAR_FORMAT_BT5 && in[i].M > kStreamMaxM)
+            tile_base += (in[i].M + kTileTokens - 1) / kTileTokens *
+                         (((in[i].N + 63) / 64 + kTileRowTiles - 1) / kTileRowTiles);
     int64_t tokens = 0, items_s = 0, items_t = 0, items_5 = 0, off = 0;
     // streaming instantiation for the whole launch: LDS-staged dot4 when every
-    // streaming problem has at most dot4_max_m tokens (the one-token kernel,
-    // fused with the quantization when none of them splits K, if all have
-    // one), MFMA otherwise
-    bool any_split = false;
+    // streaming problem has at most two tokens (the one-token kernel if all
+    // have one), MFMA otherwise
     int64_t max_upsplit = 0, max_m = 1;
     std::vector<std::pair<int64_t, int64_t>> mu;  // (M, upsplit) of the streaming problems
     for (int i = 0; i < count; ++i) {
@@ -928,7 +889,6 @@ int build_group(const bitlinear_problem *in, int count, char *ws, GroupPlan &out
         decompose(p, base_items, true, false, bl::kStreamMfmaTiles, tile_base);
         if (p.kind != 0) continue;
         max_m = max_m > p.M ? max_m : p.M;
-        any_split = any_split || p.ks > 1;
         max_upsplit = max_upsplit > p.upsplit ? max_upsplit : p.upsplit;
         mu.emplace_back(p.M, p.upsplit);
     }
@@ -938,14 +898,13 @@ int build_group(const bitlinear_problem *in, int count, char *ws, GroupPlan &out
     // stream when that exceeds 64 KiB
     int stream_variant = stream_variant_for(max_m, max_upsplit);
     int64_t lds_tok = 0;
-    if (stream_variant >= 6 && stream_variant <= 8) {
+    if (stream_variant == 6) {
         for (const auto &x : mu) {
             const int64_t b = stream_lds_need(stream_variant, x.first, x.second);
             lds_tok = lds_tok > b ? lds_tok : b;
         }
         if (lds_tok > kStreamLdsMax) stream_variant = 1;
     }
-    if (stream_variant == 3 && knobs().fuse_quant && !any_split) stream_variant = 4;
     const bool groups4 = stream_variant == 1;
     int tpw = bl::kStreamMfmaTiles;
     if (groups4) {
@@ -987,13 +946,8 @@ int build_group(const bitlinear_problem *in, int count, char *ws, GroupPlan &out
             }
         }
         off += L.total;
-        // rows quantized by the separate kernel (fused problems do it inline)
-        if (!(p.kind == 0 && stream_variant == 4)) {
-            p.tok_begin = (int32_t)tokens;
-            tokens += p.M;
-        } else {
-            p.tok_begin = -1;
-        }
+        p.tok_begin = (int32_t)tokens;
+        tokens += p.M;
         if (p.kind == 0) {
             p.item_begin = (int32_t)items_s;
             items_s += items_of(p);
@@ -1008,8 +962,6 @@ int build_group(const bitlinear_problem *in, int count, char *ws, GroupPlan &out
             items_5 >= (int64_t(1) << 31))
             return fail(BITLINEAR_ERR_SHAPE, "group: too many tokens or work items");
     }
-    // every tile problem of a group takes the same tile variant (decompose
-    // picks it from the knobs alone)
     bl::GroupHeader &h = out.h;
     h.magic = bl::kGroupMagic;
     h.count = count;
@@ -1025,9 +977,8 @@ int build_group(const bitlinear_problem *in, int count, char *ws, GroupPlan &out
     h.n_items_bt5 = (int32_t)items_5;
     h.bt5_max_m = (int32_t)(max_m5 < bl::kBt5Tokens ? max_m5 : bl::kBt5Tokens);
     h.stream_variant = stream_variant;
-    h.stream_lds = (h.stream_variant >= 6 && h.stream_variant <= 8) ? (int32_t)lds_tok
-                                                                     : (int32_t)stream_lds_need(h.stream_variant, 1, max_upsplit);
-    h.tile_variant = tile_variant(true);
+    h.stream_lds = h.stream_variant == 6 ? (int32_t)lds_tok
+                                         : (int32_t)stream_lds_need(h.stream_variant, 1, max_upsplit);
     h.ws_bytes = off;
     int64_t t = up(sizeof(bl::GroupHeader), 16);
     h.off_probs = t;
@@ -1128,7 +1079,7 @@ int bitlinear_group_matmul(const void *table_host, const void *table_dev, void *
             return hip_fail(e, "group stream kernel");
     if (h.n_items_tile > 0)
         if (hipError_t e = bl::launch_tile_group(probs, reinterpret_cast<const uint2 *>(d + h.off_tile_map),
-                                                 h.n_items_tile, h.tile_variant, s))
+                                                 h.n_items_tile, s))
             return hip_fail(e, "group tile kernel");
     if (h.n_items_bt5 > 0)
         if (hipError_t e = bl::launch_bt5_group(probs, reinterpret_cast<const uint2 *>(d + h.off_bt5_map),

@@ -49,9 +49,10 @@ constexpr int kStreamMaxTokens = 32;
 constexpr int kStreamMfmaTiles = 2;
 // token counts above which that kernel reads fragment-ordered activations
 constexpr int kStreamFragTokens = 16;
-// most tokens the packed-dot4 streaming kernel takes (64 LDS bytes per token
-// per unit of the workgroup's K range)
-constexpr int kDot4MaxTokens = 4;
+// most tokens the packed-dot4 streaming kernels take (64 LDS bytes per token
+// per unit of the workgroup's K range): one, and two in the token loop;
+// from three tokens on the matrix-instruction stream is faster
+constexpr int kDot4MaxTokens = 2;
 
 // Everything the contraction kernels need to know about one BitLinear
 // problem.  Single calls pass one of these by value; the grouped path keeps
@@ -125,8 +126,9 @@ __device__ inline int multi_index(const ProblemSet &ps, int b)
     return i;
 }
 
-// Fragment order of the int8 activations ("QF32"), used by the tile kernel
-// so that each wave reads an MFMA A operand with one contiguous 1 KiB load:
+// Fragment order of the int8 activations ("QF32"), used by the streaming
+// MFMA kernel above 16 tokens so that each wave reads an A operand with one
+// contiguous 1 KiB load:
 // for 32-row block b = m / 32, 64-code unit u and half h, a 1 KiB block at
 // ((b * KU + u) * 2 + h) * 1024 holds, at byte 16 * l + c (lane l = 0..63,
 // c = 0..15), Q[32 b + l % 32][64 u + 32 h + 16 (l / 32) + c].  Rows past M
@@ -148,7 +150,7 @@ struct GroupHeader {
     int32_t n_zero;         // problems whose split-K scratch must be zeroed
     int32_t dot4_items;     // unused by the kernels (diagnostics)
     int32_t stream_variant; // streaming kernel instantiation (see api.hip)
-    int32_t tile_variant;   // tile kernel instantiation
+    int32_t reserved_;      // unused
     int32_t stream_lds;     // dynamic LDS bytes of the streaming kernel
     int32_t n_items_bt5;    // work items of the BT5-T32 kernel
     int32_t bt5_max_m;      // largest token count among the BT5-T32 problems
@@ -190,12 +192,11 @@ hipError_t launch_zero_words(uint32_t *p, int64_t n, hipStream_t s);
 hipError_t launch_stream_single(const Problem &p, int variant, hipStream_t s);
 hipError_t launch_stream_group(const Problem *probs, const uint2 *item_map, int n_items,
                                int variant, int lds_bytes, hipStream_t s);
-hipError_t launch_tile_single(const Problem &p, int variant, hipStream_t s);
-hipError_t launch_tile_group(const Problem *probs, const uint2 *item_map, int n_items,
-                             int variant, hipStream_t s);
+hipError_t launch_tile_single(const Problem &p, hipStream_t s);
+hipError_t launch_tile_group(const Problem *probs, const uint2 *item_map, int n_items, hipStream_t s);
 hipError_t launch_bt5_single(const Problem &p, hipStream_t s);
 hipError_t launch_stream_multi(const ProblemSet &ps, int variant, int lds_bytes, hipStream_t s);
-hipError_t launch_tile_multi(const ProblemSet &ps, int variant, hipStream_t s);
+hipError_t launch_tile_multi(const ProblemSet &ps, hipStream_t s);
 hipError_t launch_bt5_multi(const ProblemSet &ps, int max_tokens, hipStream_t s);
 hipError_t launch_bt5_group(const Problem *probs, const uint2 *item_map, int n_items, int max_tokens,
                             hipStream_t s);

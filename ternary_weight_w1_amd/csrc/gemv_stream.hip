@@ -51,7 +51,7 @@ __device__ inline int dot16(unsigned w, v4i q, int acc)
 }
 
 // Activations of the workgroup's K range, staged once per workgroup when
-// the dot4 kernel runs with QLDS (dynamic LDS, 64 bytes per unit).
+// the dot4 kernels run (dynamic LDS, 64 bytes per token slot per unit).
 extern __shared__ __attribute__((aligned(16))) int8_t stream_q_lds[];
 
 // Copies n 16-byte chunks into the staged activations, chunk i from src(i):
@@ -98,65 +98,6 @@ __device__ __forceinline__ void stage_token_slots(const Problem &p, int u0, int 
         for (int k = 0; k < 8; ++k)
             if (ub + k * kPer < nu && uo < kPer) dst[(ub + k * kPer) * MT * 4] = v[k];
     }
-}
-
-// Fused prologue (decode, one token): quantize the token's fp32 activations
-// straight into LDS -- absmax over the whole row (block reduction), then
-// the same per-element code as the quantization kernel -- keeping the codes
-// of units [u0, u1) and the row sum of all of them.  Replaces a separate
-// quantization launch; the row is re-read from L1/L2 in the second pass.
-__device__ void fused_quant_token(const Problem &p, int u0, int u1, float &absmax, int &rowsum)
-{
-    __shared__ float fmax_l[kWaves];
-    __shared__ int isum_l[kWaves];
-    const int tid = threadIdx.x, K = p.K;
-    const BL_GLOBAL float *x = gload_ptr<float>(p.X);
-    typedef float v4f __attribute__((ext_vector_type(4)));
-    const bool vec = ((K & 3) == 0) && ((reinterpret_cast<uintptr_t>(p.X) & 15) == 0);
-    const BL_GLOBAL v4f *x4 = reinterpret_cast<const BL_GLOBAL v4f *>(x);
-    float a = 0.0f;
-    if (vec) {
-        for (int i = tid; i < (K >> 2); i += kThreads) {
-            const v4f w = x4[i];
-            a = fmaxf(a, fmaxf(fmaxf(fabsf(w.x), fabsf(w.y)), fmaxf(fabsf(w.z), fabsf(w.w))));
-        }
-    } else {
-        for (int i = tid; i < K; i += kThreads) a = fmaxf(a, fabsf(x[i]));
-    }
-    for (int off = 32; off > 0; off >>= 1) a = fmaxf(a, __shfl_xor(a, off, 64));
-    if ((tid & 63) == 0) fmax_l[tid >> 6] = a;
-    __syncthreads();
-    a = fmaxf(fmaxf(fmax_l[0], fmax_l[1]), fmaxf(fmax_l[2], fmax_l[3]));
-    if (!(a >= 1e-5f)) a = 1e-5f;
-    const float s = 127.0f / a;
-
-    const int k0 = 64 * u0, k1 = 64 * u1;  // LDS holds codes k0 .. k1-1
-    int sum = 0;
-    if (vec) {
-        for (int i = tid; i < (K >> 2); i += kThreads) {
-            const v4f w = x4[i];
-            const int8_t c0 = quant_code(w.x, s), c1 = quant_code(w.y, s);
-            const int8_t c2 = quant_code(w.z, s), c3 = quant_code(w.w, s);
-            sum += (int)c0 + (int)c1 + (int)c2 + (int)c3;
-            const int k = 4 * i;
-            if (k >= k0 && k < k1)
-                *reinterpret_cast<uint32_t *>(stream_q_lds + (k - k0)) =
-                    (uint32_t)(uint8_t)c0 | ((uint32_t)(uint8_t)c1 << 8) |
-                    ((uint32_t)(uint8_t)c2 << 16) | ((uint32_t)(uint8_t)c3 << 24);
-        }
-    } else {
-        for (int k = tid; k < K; k += kThreads) {
-            const int8_t c = quant_code(x[k], s);
-            sum += c;
-            if (k >= k0 && k < k1) stream_q_lds[k - k0] = c;
-        }
-    }
-    for (int k = (K > k0 ? K : k0) + tid; k < k1; k += kThreads) stream_q_lds[k - k0] = 0;
-    for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off, 64);
-    if ((tid & 63) == 0) isum_l[tid >> 6] = sum;
-    __syncthreads();
-    absmax = a;
-    rowsum = isum_l[0] + isum_l[1] + isum_l[2] + isum_l[3];
 }
 
 // Table-lookup variant, kept to compare against the dot4 stream: the pages
@@ -210,47 +151,31 @@ __device__ void build_lut(const Problem &p, int u0, int u1)
     }
 }
 
-// QLDS: read the activations with broadcast LDS reads (2 distinct 16-byte
-// addresses per half wave) instead of two 16-byte global loads per lane per
-// unit, which would triple the vector-memory instructions of the stream.
-// FUSED: the activations are quantized in the prologue (implies QLDS).
+// The activations of the workgroup's K range are staged once in LDS and
+// read with broadcast LDS reads (2 distinct 16-byte addresses per half
+// wave) instead of two 16-byte global loads per lane per unit, which would
+// triple the vector-memory instructions of the stream.
 // LUT: the table-lookup variant above instead of dot products.
-template <int UNROLL, bool QLDS, bool FUSED = false, bool LUT = false>
+template <int UNROLL, bool LUT = false>
 __device__ void stream_dot4(const Problem &p, int local)
 {
-    static_assert(!FUSED || QLDS, "the fused prologue writes the LDS activations");
-    static_assert(!LUT || (QLDS && !FUSED), "the table takes the LDS");
     __shared__ int red[kWaves][64];
     const int tile = local / p.ks, split = local - tile * p.ks;
     const int u0 = split * p.upsplit;
     const int u1 = min(p.KU, u0 + p.upsplit);
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 5;
     const BL_GLOBAL v4u *blk = gload_ptr<v4u>(p.P + (int64_t)tile * p.KU * kBlockBytes) + lane;
-    const BL_GLOBAL int8_t *qg = gload_ptr<int8_t>(p.Q) + 16 * g;  // token 0; chunk g of each 32-code half
-    float tok_absmax = 0.0f;
-    int tok_rowsum = 0;
-    if constexpr (FUSED) {
-        fused_quant_token(p, u0, u1, tok_absmax, tok_rowsum);
-    } else if constexpr (LUT) {
+    if constexpr (LUT) {
         build_lut(p, u0, u1);
-        __syncthreads();
-    } else if constexpr (QLDS) {
+    } else {
         const BL_GLOBAL v4i *src = gload_ptr<v4i>(p.Q + 64 * u0);
         stage_chunks(4 * (u1 - u0), [&](int i) { return src[i]; });
-        __syncthreads();
     }
-    auto finish = [&](int n, int32_t fields, float gamma) {
-        if constexpr (FUSED)
-            finish_output_with(p, gamma, 0, n, fields, tok_rowsum, tok_absmax);
-        else
-            finish_output(p, gamma, 0, n, fields);
-    };
+    __syncthreads();
+    auto finish = [&](int n, int32_t fields, float gamma) { finish_output(p, gamma, 0, n, fields); };
     // activation bytes 64*u + 16*g (+32 for the second half) of unit u
     auto qload = [&](int u, int off) -> v4i {
-        if constexpr (QLDS)
-            return *reinterpret_cast<const v4i *>(stream_q_lds + 64 * (u - u0) + 16 * g + off);
-        else
-            return *reinterpret_cast<const BL_GLOBAL v4i *>(qg + 64 * u + off);
+        return *reinterpret_cast<const v4i *>(stream_q_lds + 64 * (u - u0) + 16 * g + off);
     };
 
     int acc0 = 0, acc1 = 0;  // rows r and 32 + r of the tile
@@ -582,36 +507,28 @@ __device__ void stream_mfma(const Problem &p, int local)
     }
 }
 
-// 0: dot4, activations from global; 1: MFMA (2..32 tokens, tile groups per
-// workgroup); 2: dot4 with
-// LDS-staged activations; 3: as 2 with 8 units in flight per wave; 4: as 3
-// with the activation quantization fused into the prologue; 5: the
-// table-lookup comparison variant (one token); 6, 7, 8: the dot4 token-loop
-// kernel with V - 4 token slots per unit, for launches whose problems have
-// at most V - 4 tokens (one-token problems take the one-slot loop, whose
-// LDS layout and stream are those of 3); 9: as 1 with one tile per wave.
+// Instantiations: 1: MFMA stream (3..32 tokens; two tiles per wave); 3: dot4
+// with LDS-staged activations, 8 units in flight per wave (one token); 5:
+// the table-lookup comparison variant (one token); 6: the dot4 token loop
+// for launches whose problems have at most two tokens (one-token problems
+// take the one-slot loop, whose LDS layout and stream are those of 3); 9:
+// as 1 with one tile per wave.
 template <int V>
 __device__ inline void stream_body(const Problem &p, int local)
 {
-    if constexpr (V >= 6 && V <= 8) {
+    if constexpr (V == 6) {
         if (p.M == 1)
             stream_dot4_tokens<8, 1>(p, local);
         else
-            stream_dot4_tokens<8, V - 4>(p, local);
-    } else if constexpr (V == 0)
-        stream_dot4<4, false>(p, local);
-    else if constexpr (V == 1)
+            stream_dot4_tokens<8, kDot4MaxTokens>(p, local);
+    } else if constexpr (V == 1)
         stream_mfma<2, kStreamMfmaTiles>(p, local);
     else if constexpr (V == 9)
         stream_mfma<2, 1>(p, local);
-    else if constexpr (V == 2)
-        stream_dot4<4, true>(p, local);
-    else if constexpr (V == 3)
+    else if constexpr (V == 5)
         stream_dot4<8, true>(p, local);
-    else if constexpr (V == 4)
-        stream_dot4<8, true, true>(p, local);
     else
-        stream_dot4<8, true, false, true>(p, local);
+        stream_dot4<8>(p, local);
 }
 
 template <int V>
@@ -638,21 +555,20 @@ __global__ __launch_bounds__(kThreads) void stream_multi_kernel(ProblemSet ps)
 
 }  // namespace
 
+// one case per instantiation; unknown values take 3
+#define BL_STREAM_CASES(KERNEL, LDS, ...)                                                   \
+    switch (variant) {                                                                     \
+    case 1: hipLaunchKernelGGL(KERNEL<1>, grid, block, 0, s, __VA_ARGS__); break;          \
+    case 9: hipLaunchKernelGGL(KERNEL<9>, grid, block, 0, s, __VA_ARGS__); break;          \
+    case 5: hipLaunchKernelGGL(KERNEL<5>, grid, block, LDS, s, __VA_ARGS__); break;        \
+    case 6: hipLaunchKernelGGL(KERNEL<6>, grid, block, LDS, s, __VA_ARGS__); break;        \
+    default: hipLaunchKernelGGL(KERNEL<3>, grid, block, LDS, s, __VA_ARGS__); break;       \
+    }
+
 hipError_t launch_stream_multi(const ProblemSet &ps, int variant, int lds_bytes, hipStream_t s)
 {
     const dim3 grid((unsigned)ps.begin[ps.count]), block(kThreads);
-    const unsigned lds = (variant >= 2 && variant <= 8) ? (unsigned)lds_bytes : 0u;
-    switch (variant) {
-    case 0: hipLaunchKernelGGL(stream_multi_kernel<0>, grid, block, 0, s, ps); break;
-    case 1: hipLaunchKernelGGL(stream_multi_kernel<1>, grid, block, 0, s, ps); break;
-    case 9: hipLaunchKernelGGL(stream_multi_kernel<9>, grid, block, 0, s, ps); break;
-    case 2: hipLaunchKernelGGL(stream_multi_kernel<2>, grid, block, lds, s, ps); break;
-    case 5: hipLaunchKernelGGL(stream_multi_kernel<5>, grid, block, lds, s, ps); break;
-    case 6: hipLaunchKernelGGL(stream_multi_kernel<6>, grid, block, lds, s, ps); break;
-    case 7: hipLaunchKernelGGL(stream_multi_kernel<7>, grid, block, lds, s, ps); break;
-    case 8: hipLaunchKernelGGL(stream_multi_kernel<8>, grid, block, lds, s, ps); break;
-    default: hipLaunchKernelGGL(stream_multi_kernel<3>, grid, block, lds, s, ps); break;
-    }
+    BL_STREAM_CASES(stream_multi_kernel, (unsigned)lds_bytes, ps)
     return hipGetLastError();
 }
 
@@ -661,21 +577,9 @@ hipError_t launch_stream_single(const Problem &p, int variant, hipStream_t s)
     // the MFMA variants' work items are tile groups (p.ntt of them)
     const int64_t tiles = (variant == 1 || variant == 9) ? (int64_t)p.ntt : (int64_t)p.NT;
     const dim3 grid((unsigned)(tiles * p.ks)), block(kThreads);
-    const unsigned slot = variant >= 6 ? 64u * (unsigned)(variant - 4) : 64u;
-    const unsigned lds =
-        (variant >= 2 && variant <= 8) ? (variant == 5 ? kLutUnitBytes : slot) * (unsigned)p.upsplit : 0u;
-    switch (variant) {
-    case 0: hipLaunchKernelGGL(stream_single_kernel<0>, grid, block, 0, s, p); break;
-    case 1: hipLaunchKernelGGL(stream_single_kernel<1>, grid, block, 0, s, p); break;
-    case 9: hipLaunchKernelGGL(stream_single_kernel<9>, grid, block, 0, s, p); break;
-    case 2: hipLaunchKernelGGL(stream_single_kernel<2>, grid, block, lds, s, p); break;
-    case 3: hipLaunchKernelGGL(stream_single_kernel<3>, grid, block, lds, s, p); break;
-    case 5: hipLaunchKernelGGL(stream_single_kernel<5>, grid, block, lds, s, p); break;
-    case 6: hipLaunchKernelGGL(stream_single_kernel<6>, grid, block, lds, s, p); break;
-    case 7: hipLaunchKernelGGL(stream_single_kernel<7>, grid, block, lds, s, p); break;
-    case 8: hipLaunchKernelGGL(stream_single_kernel<8>, grid, block, lds, s, p); break;
-    default: hipLaunchKernelGGL(stream_single_kernel<4>, grid, block, lds, s, p); break;
-    }
+    const unsigned slot = variant == 6 ? 64u * kDot4MaxTokens : 64u;
+    const unsigned lds = (variant == 5 ? kLutUnitBytes : slot) * (unsigned)p.upsplit;
+    BL_STREAM_CASES(stream_single_kernel, lds, p)
     return hipGetLastError();
 }
 
@@ -683,20 +587,10 @@ hipError_t launch_stream_group(const Problem *probs, const uint2 *item_map, int 
                                int variant, int lds_bytes, hipStream_t s)
 {
     const dim3 grid((unsigned)n_items), block(kThreads);
-    const unsigned lds = (variant >= 2 && variant <= 8) ? (unsigned)lds_bytes : 0u;
-    switch (variant) {
-    case 0: hipLaunchKernelGGL(stream_group_kernel<0>, grid, block, 0, s, probs, item_map); break;
-    case 1: hipLaunchKernelGGL(stream_group_kernel<1>, grid, block, 0, s, probs, item_map); break;
-    case 9: hipLaunchKernelGGL(stream_group_kernel<9>, grid, block, 0, s, probs, item_map); break;
-    case 2: hipLaunchKernelGGL(stream_group_kernel<2>, grid, block, lds, s, probs, item_map); break;
-    case 3: hipLaunchKernelGGL(stream_group_kernel<3>, grid, block, lds, s, probs, item_map); break;
-    case 5: hipLaunchKernelGGL(stream_group_kernel<5>, grid, block, lds, s, probs, item_map); break;
-    case 6: hipLaunchKernelGGL(stream_group_kernel<6>, grid, block, lds, s, probs, item_map); break;
-    case 7: hipLaunchKernelGGL(stream_group_kernel<7>, grid, block, lds, s, probs, item_map); break;
-    case 8: hipLaunchKernelGGL(stream_group_kernel<8>, grid, block, lds, s, probs, item_map); break;
-    default: hipLaunchKernelGGL(stream_group_kernel<4>, grid, block, lds, s, probs, item_map); break;
-    }
+    BL_STREAM_CASES(stream_group_kernel, (unsigned)lds_bytes, probs, item_map)
     return hipGetLastError();
 }
+
+#undef BL_STREAM_CASES
 
 }  // namespace bl

@@ -103,6 +103,8 @@ def rms_undecided_rows(X, eps: float):
     for m in range(M):
         s = Fraction(math.fsum(sq[m]))  # correctly rounded sum of exact squares
         v = s / K + Fraction(float(eps))
+        if v == 0:
+            continue  # 1/sqrt(0) is +inf in any order: nothing to round
         scaled = (Fraction(4) ** 100) / v
         inv = Fraction(math.isqrt(scaled.numerator // scaled.denominator), 2 ** 100)
         margin = fp32_margin(inv)

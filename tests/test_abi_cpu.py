@@ -170,7 +170,7 @@ def test_group_plan_table_on_host():
     hdr = np.frombuffer(host[:48].tobytes(), np.int32)
     assert hdr[0] == np.int32(np.uint32(0xB17E0002).astype(np.int32))
     assert hdr[1] == 4            # problems
-    assert hdr[2] in (0, 4)       # tokens quantized by the separate kernel (0 when fused)
+    assert hdr[2] == 4            # tokens quantized by the quantization kernel
     items = sum((N + 63) // 64 for _, N, _ in specs)
     assert hdr[3] >= items        # streaming work items (K splits may add more)
     assert hdr[4] == 0            # no tile-kernel items at M = 1
@@ -187,15 +187,12 @@ def test_group_plan_table_on_host():
 def test_group_plan_single_token_quantization():
     # 16 single-token problems with 64 row tiles each (no K split): every
     # token goes to the quantization kernel and the dot4 kernel reads LDS-
-    # staged activations (3), or -- with BITLINEAR_FUSE_QUANT=1 -- the dot4
-    # kernel quantizes in its prologue (4) and no token is left over; a
-    # 2-token problem switches the streaming kernel to the two-slot dot4
+    # staged activations (3); a 2-token problem switches the streaming kernel to the two-slot dot4
     # token-loop kernel (6), whose LDS holds 64 bytes per unit for one-token
     # problems and 128 for two-token ones; a 5-token problem switches it to
     # the MFMA stream, which takes one tile per wave (9) in a launch this small
     # (129 eight-tile groups, fewer than the 1024-workgroup split target)
     L = B.lib()
-    fused = os.environ.get("BITLINEAR_FUSE_QUANT", "0") not in ("", "0")
     specs = [(1, 4096, 256)] * 16
     arr = _problems(specs)
     tb = L.bitlinear_group_table_bytes(arr, 16)
@@ -204,7 +201,7 @@ def test_group_plan_single_token_quantization():
     assert L.bitlinear_group_plan(arr, 16, FAKE, wsb, host.ctypes.data, tb) == 0
     hdr = np.frombuffer(host[:48].tobytes(), np.int32)
     assert hdr[3] == 16 * 64
-    assert (hdr[2], hdr[7]) == ((0, 4) if fused else (16, 3))
+    assert (hdr[2], hdr[7]) == (16, 3)
     arr2 = _problems(specs + [(2, 64, 64)])
     tb2 = L.bitlinear_group_table_bytes(arr2, 17)
     host2 = np.zeros(tb2, np.uint8)
@@ -220,16 +217,16 @@ def test_group_plan_single_token_quantization():
     assert L.bitlinear_group_plan(arr3, 17, FAKE, wsb3, host3.ctypes.data, tb3) == 0
     hdr3 = np.frombuffer(host3[:48].tobytes(), np.int32)
     assert hdr3[2] == 21 and hdr3[7] == 9 and hdr3[9] == 0
-    # a one-token problem whose unsplit K range (1250 units) needs more than
-    # 64 KiB of staged activations keeps a 2-token launch off variant 6 (the
-    # MFMA stream takes it, one tile per wave)
+    # a one-token problem whose K range (1250 units) would need more than
+    # 64 KiB of staged activations is split in two (625 units, 40000 bytes),
+    # so a 2-token launch still takes the token loop (6)
     arr4 = _problems(specs + [(1, 64, 80000), (2, 64, 64)])
     tb4 = L.bitlinear_group_table_bytes(arr4, 18)
     host4 = np.zeros(tb4, np.uint8)
     wsb4 = L.bitlinear_group_workspace_bytes(arr4, 18)
     assert L.bitlinear_group_plan(arr4, 18, FAKE, wsb4, host4.ctypes.data, tb4) == 0
     hdr4 = np.frombuffer(host4[:48].tobytes(), np.int32)
-    assert hdr4[7] == 9 and hdr4[9] == 0
+    assert hdr4[7] == 6 and hdr4[9] == 64 * 625
     # a launch whose eight-tile groups fill the split target keeps two tiles
     # per wave (1): 130 problems of 64 tiles at M = 5
     arr6 = _problems([(5, 4096, 256)] * 130)
