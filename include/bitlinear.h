@@ -36,8 +36,9 @@
  *     in range is accepted (no multiple-of-64 requirement); internally K
  *     is padded to a multiple of 64 with zero codes / zero activations.
  *   - NaN or infinite inputs give unspecified (but memory-safe) results.
- *   - Calls are reentrant; the library holds no mutable global state.  Two
- *     calls that share a workspace must not run concurrently.
+ *   - Calls are reentrant; the library holds no mutable global state beyond
+ *     the scratch array of bitlinear_forward_noalloc.  Two calls that share
+ *     a workspace must not run concurrently.
  *
  * Packed weight format "BL2-T64" (the buffer bitlinear_pack writes and the
  * matmul calls read; bitlinear_packed_bytes(N, K) bytes):
@@ -297,6 +298,32 @@ int bitlinear_forward5(const float *X, int64_t M, int64_t K, const uint8_t *P5,
 int bitlinear_forward(const float *X, int64_t M, int64_t K, const uint8_t *P,
                       const float *gamma, int64_t N, float *Y_out, int32_t *acc_out,
                       void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * bitlinear_forward for callers that cannot allocate: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  Results
+ * are bit-identical to bitlinear_forward.  The workspace (int8 activations,
+ * scales, row sums, split-K partial sums and arrival counters) is a fixed
+ * device array inside the library, bitlinear_noalloc_scratch_bytes() bytes
+ * (16 MiB) on each GPU, held until the process ends; its device address is
+ * looked up once per device on the first call.  The call allocates and
+ * frees nothing; the arrival counters it needs are cleared by its own
+ * kernels.
+ *   X, M, K, P, gamma, N, Y_out, acc_out  as bitlinear_forward.
+ *   stream  must belong to the current device (else BITLINEAR_ERR_ARG).
+ *   Sizes whose bitlinear_workspace_bytes(BITLINEAR_WS_FORWARD, M, N, K)
+ *   exceed the array are rejected with BITLINEAR_ERR_WORKSPACE before
+ *   anything is enqueued.
+ * Every call on a GPU uses that GPU's one array: calls that can overlap on
+ * one GPU (other streams, other host threads) race and must be serialized
+ * by the caller.
+ */
+int bitlinear_forward_noalloc(const float *X, int64_t M, int64_t K, const uint8_t *P,
+                              const float *gamma, int64_t N, float *Y_out, int32_t *acc_out,
+                              void *stream);
+
+/* Bytes of the scratch array bitlinear_forward_noalloc works in. */
+size_t bitlinear_noalloc_scratch_bytes(void);
 
 /* ---------------------------------------------------------------------- */
 /* Several weight matrices on one int8 input (q|k|v, gate|up): one launch.  */

@@ -86,6 +86,8 @@ def lib():
             "bitlinear_matmul": (_int, [_vp, _i64, _vp, _vp, _i64, _i64, _vp, _vp, _i64, _vp, _vp,
                                         _vp, _sz, _vp]),
             "bitlinear_forward": (_int, [_vp, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _vp, _sz, _vp]),
+            "bitlinear_forward_noalloc": (_int, [_vp, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _vp]),
+            "bitlinear_noalloc_scratch_bytes": (_sz, []),
             "bitlinear_multi_workspace_bytes": (_sz, [ctypes.POINTER(Weight), _int, _i64, _i64]),
             "bitlinear_matmul_multi": (_int, [_vp, _i64, _vp, _vp, _i64, _i64, ctypes.POINTER(Weight), _int,
                                               _vp, _sz, _vp]),
@@ -281,6 +283,26 @@ def forward(X, P, gamma, N: int, with_acc: bool = False, ws=None, out=None, stre
                                    _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)),
            "forward")
     return (Y, acc) if with_acc else Y
+
+
+def forward_noalloc(X, P, gamma, N: int, with_acc: bool = False, out=None, acc=None, stream=None):
+    """BitLinear forward in the library's own scratch array (no workspace):
+    bit-identical to forward().  Calls on one GPU share that array and must
+    not overlap."""
+    _dev_tensor(X, torch.float32, "X")
+    _dev_tensor(P, torch.uint8, "P")
+    _dev_tensor(gamma, torch.float32, "gamma")
+    M, K = X.shape
+    Y = torch.empty((M, N), dtype=torch.float32, device=X.device) if out is None else out
+    if with_acc and acc is None:
+        acc = torch.empty((M, N), dtype=torch.int32, device=X.device)
+    _check(lib().bitlinear_forward_noalloc(_ptr(X), M, K, _ptr(P), _ptr(gamma), N, _ptr(Y), _ptr(acc),
+                                           _stream(stream)), "forward_noalloc")
+    return (Y, acc) if with_acc else Y
+
+
+def noalloc_scratch_bytes() -> int:
+    return int(lib().bitlinear_noalloc_scratch_bytes())
 
 
 def packed5_bytes(N: int, K: int) -> int:

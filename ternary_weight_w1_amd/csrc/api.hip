@@ -9,6 +9,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -320,6 +321,52 @@ hipError_t launch_contraction(const Problem &p, bool own_q, hipStream_t s)
     return bl::launch_tile_single(p, s);
 }
 
+// Validation shared by the forward calls (nothing is enqueued on failure).
+int forward_check(const char *who, const float *X, int64_t M, int64_t K, const uint8_t *P, const float *gamma,
+                  int64_t N, float *Y_out, int32_t *acc_out)
+{
+    if (!X || !P || !gamma || !Y_out) return fail(BITLINEAR_ERR_NULL, "%s: X, P, gamma and Y_out are required", who);
+    if (int st = check_mnk(M, N, K)) return st;
+    if (!a16(X) || !a16(P) || !a16(Y_out) || (acc_out && !a16(acc_out)) || !a4(gamma))
+        return fail(BITLINEAR_ERR_ALIGN, "%s: arrays need 16-byte, gamma 4-byte alignment", who);
+    return BITLINEAR_OK;
+}
+
+// bitlinear_forward on the workspace ws (the caller's, or the library's
+// scratch for bitlinear_forward_noalloc).
+int forward_impl(const char *who, const float *X, int64_t M, int64_t K, const uint8_t *P, const float *gamma,
+                 int64_t N, float *Y_out, int32_t *acc_out, void *ws, size_t ws_bytes, void *stream)
+{
+    if (int st = forward_check(who, X, M, K, P, gamma, N, Y_out, acc_out)) return st;
+    Problem p = make_problem(M, N, K);
+    decompose_single(p, true);
+    const WsLayout L = ws_layout(p, true);
+    if (!ws || ws_bytes < (size_t)L.total || !a16(ws))
+        return fail(BITLINEAR_ERR_WORKSPACE, "%s: needs %lld workspace bytes (16-byte aligned)", who, (long long)L.total);
+    if (p.kind == 1 && items_of(p) >= (int64_t(1) << 31))
+        return fail(BITLINEAR_ERR_SHAPE, "%s: grid too large", who);
+    char *base = static_cast<char *>(ws);
+    p.X = X;
+    p.P = P;
+    p.gamma = gamma;
+    p.Y = Y_out;
+    p.acc_out = acc_out;
+    p.ldq = 64 * (int64_t)p.KU;
+    p.Q = reinterpret_cast<int8_t *>(base + L.q);
+    p.absmax = reinterpret_cast<float *>(base + L.absmax);
+    p.rowsum = reinterpret_cast<int32_t *>(base + L.rowsum);
+    if (p.ks > 1) {
+        p.acc_ws = reinterpret_cast<int32_t *>(base + L.part);
+        p.tickets = reinterpret_cast<uint32_t *>(base + L.tick);
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (hipError_t e = bl::launch_quant_act(X, M, K, p.Q, p.ldq, p.qtiled, p.absmax, p.rowsum,
+                                            p.tickets, p.tickets ? (int)bl::ticket_count(p) : 0, s))
+        return hip_fail(e, who);
+    if (hipError_t e = launch_contraction(p, true, s)) return hip_fail(e, who);
+    return BITLINEAR_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -557,37 +604,7 @@ int bitlinear_forward(const float *X, int64_t M, int64_t K, const uint8_t *P,
                       const float *gamma, int64_t N, float *Y_out, int32_t *acc_out,
                       void *ws, size_t ws_bytes, void *stream)
 {
-    if (!X || !P || !gamma || !Y_out) return fail(BITLINEAR_ERR_NULL, "forward: X, P, gamma and Y_out are required");
-    if (int st = check_mnk(M, N, K)) return st;
-    if (!a16(X) || !a16(P) || !a16(Y_out) || (acc_out && !a16(acc_out)) || !a4(gamma))
-        return fail(BITLINEAR_ERR_ALIGN, "forward: arrays need 16-byte, gamma 4-byte alignment");
-    Problem p = make_problem(M, N, K);
-    decompose_single(p, true);
-    const WsLayout L = ws_layout(p, true);
-    if (!ws || ws_bytes < (size_t)L.total || !a16(ws))
-        return fail(BITLINEAR_ERR_WORKSPACE, "forward: needs %lld workspace bytes (16-byte aligned)", (long long)L.total);
-    if (p.kind == 1 && items_of(p) >= (int64_t(1) << 31))
-        return fail(BITLINEAR_ERR_SHAPE, "forward: grid too large");
-    char *base = static_cast<char *>(ws);
-    p.X = X;
-    p.P = P;
-    p.gamma = gamma;
-    p.Y = Y_out;
-    p.acc_out = acc_out;
-    p.ldq = 64 * (int64_t)p.KU;
-    p.Q = reinterpret_cast<int8_t *>(base + L.q);
-    p.absmax = reinterpret_cast<float *>(base + L.absmax);
-    p.rowsum = reinterpret_cast<int32_t *>(base + L.rowsum);
-    if (p.ks > 1) {
-        p.acc_ws = reinterpret_cast<int32_t *>(base + L.part);
-        p.tickets = reinterpret_cast<uint32_t *>(base + L.tick);
-    }
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    if (hipError_t e = bl::launch_quant_act(X, M, K, p.Q, p.ldq, p.qtiled, p.absmax, p.rowsum,
-                                            p.tickets, p.tickets ? (int)bl::ticket_count(p) : 0, s))
-        return hip_fail(e, "forward: quant_act");
-    if (hipError_t e = launch_contraction(p, true, s)) return hip_fail(e, "forward: matmul");
-    return BITLINEAR_OK;
+    return forward_impl("forward", X, M, K, P, gamma, N, Y_out, acc_out, ws, ws_bytes, stream);
 }
 
 int bitlinear_matmul5(const int8_t *Q, int64_t ldq, const float *absmax, const int32_t *rowsum,
@@ -1137,6 +1154,79 @@ int bitlinear_probe_mfma_blocks(int32_t *blocks)
     if (e != hipSuccess) return hip_fail(e, "probe_mfma_blocks");
     *blocks = n;
     return BITLINEAR_OK;
+}
+
+}  // extern "C"
+
+// --------------------------------------------------------------------------
+// The forward for callers that cannot allocate (code under HIP graph
+// capture, tight serving loops, harnesses that forbid hipMalloc): the
+// workspace of bitlinear_forward -- int8 activations, scales, row sums,
+// split-K partial sums and arrival tickets -- lives in a fixed device array
+// of the library instead of a caller buffer.
+// --------------------------------------------------------------------------
+namespace {
+constexpr size_t kScratchBytes = size_t(16) << 20;
+constexpr int kScratchDevices = 64;
+}  // namespace
+
+// One copy per GPU, alive until the process ends.  In host code this name is
+// only a handle for hipGetSymbolAddress: its device address comes from
+// scratch_on_current_device() and is the only thing ever passed to kernels.
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+namespace {
+
+std::mutex g_scratch_mu;
+void *g_scratch_addr[kScratchDevices];  // device address of `scratch`, per device
+
+// The device address of `scratch` on the current device, looked up once per
+// device (with that device current) and cached.
+int scratch_on_current_device(const char *who, void *stream, void **out)
+{
+    int dev = -1;
+    if (hipError_t e = hipGetDevice(&dev)) return hip_fail(e, who);
+    if (stream) {
+        int sdev = -1;
+        if (hipError_t e = hipStreamGetDevice(static_cast<hipStream_t>(stream), &sdev)) return hip_fail(e, who);
+        if (sdev != dev)
+            return fail(BITLINEAR_ERR_ARG, "%s: the stream belongs to device %d, the current device is %d", who,
+                        sdev, dev);
+    }
+    if (dev < 0 || dev >= kScratchDevices)
+        return fail(BITLINEAR_ERR_ARG, "%s: device %d is beyond the %d the library serves", who, dev,
+                    kScratchDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_addr[dev]) {
+        void *p = nullptr;
+        if (hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch))) return hip_fail(e, who);
+        if (!p || !a16(p)) return fail(BITLINEAR_ERR_HIP, "%s: no usable device address for the scratch array", who);
+        g_scratch_addr[dev] = p;
+    }
+    *out = g_scratch_addr[dev];
+    return BITLINEAR_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t bitlinear_noalloc_scratch_bytes(void) { return kScratchBytes; }
+
+int bitlinear_forward_noalloc(const float *X, int64_t M, int64_t K, const uint8_t *P, const float *gamma,
+                              int64_t N, float *Y_out, int32_t *acc_out, void *stream)
+{
+    const char *who = "forward_noalloc";
+    if (int st = forward_check(who, X, M, K, P, gamma, N, Y_out, acc_out)) return st;
+    const size_t need = bitlinear_workspace_bytes(BITLINEAR_WS_FORWARD, M, N, K);
+    if (need > kScratchBytes)
+        return fail(BITLINEAR_ERR_WORKSPACE,
+                    "%s: M=%lld N=%lld K=%lld need %zu bytes of scratch, more than the %zu the library holds "
+                    "(use bitlinear_forward with a workspace)",
+                    who, (long long)M, (long long)N, (long long)K, need, kScratchBytes);
+    void *ws = nullptr;
+    if (int st = scratch_on_current_device(who, stream, &ws)) return st;
+    return forward_impl(who, X, M, K, P, gamma, N, Y_out, acc_out, ws, kScratchBytes, stream);
 }
 
 }  // extern "C"

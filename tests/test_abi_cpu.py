@@ -37,7 +37,7 @@ def test_every_header_is_checked():
 
 def test_every_declared_symbol_is_exported():
     names = _declared()
-    assert len(names) == 33, names
+    assert len(names) == 35, names
     out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r"\bT (bitlinear_\w+)", out))
@@ -400,3 +400,18 @@ def test_group_plan_tile_split():
     assert L.bitlinear_group_plan(big, 65, FAKE, wsb2, host2.ctypes.data, tb2) == 0
     hdr2 = np.frombuffer(host2[:48].tobytes(), np.int32)
     assert hdr2[4] == 65 * 64
+
+
+def test_noalloc_forward_rejects_before_touching_the_device():
+    # the no-allocation forward validates first: bad pointers and sizes whose
+    # workspace exceeds the library's 16 MiB scratch array are refused before
+    # any HIP call (FAKE addresses are never dereferenced)
+    L = B.lib()
+    assert L.bitlinear_noalloc_scratch_bytes() == 16 << 20
+    assert L.bitlinear_forward_noalloc(None, 1, 64, FAKE, FAKE, 64, FAKE, None, None) == -1
+    assert L.bitlinear_forward_noalloc(FAKE, 0, 64, FAKE, FAKE, 64, FAKE, None, None) == -2
+    assert L.bitlinear_forward_noalloc(FAKE + 4, 1, 64, FAKE, FAKE, 64, FAKE, None, None) == -3
+    M, N, K = 4096, 2560, 2560
+    assert L.bitlinear_workspace_bytes(3, M, N, K) > 16 << 20
+    assert L.bitlinear_forward_noalloc(FAKE, M, K, FAKE, FAKE, N, FAKE, None, None) == -4
+    assert b"scratch" in L.bitlinear_last_error()
