@@ -14,6 +14,7 @@ grouped forward (GroupPlan).
 from __future__ import annotations
 
 import ctypes
+import functools
 import os
 
 import torch
@@ -123,6 +124,29 @@ def _stream(stream):
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
 
 
+def _torch_stream(stream):
+    """The torch stream object a call enqueues on: the current stream for
+    None, the object itself, or an ExternalStream around a raw hipStream_t."""
+    if stream is None:
+        return torch.cuda.current_stream()
+    if isinstance(stream, torch.cuda.Stream):
+        return stream
+    return torch.cuda.ExternalStream(int(stream))
+
+
+def _on_stream(fn):
+    """Run a call with its launch stream current, so that the outputs and
+    temporary workspaces it allocates belong to that stream in torch's
+    caching allocator: their memory is not handed to other streams' work
+    while the library's kernels may still use it."""
+    @functools.wraps(fn)
+    def wrapper(*args, stream=None, **kw):
+        s = _torch_stream(stream)
+        with torch.cuda.stream(s):
+            return fn(*args, stream=s, **kw)
+    return wrapper
+
+
 def _ptr(t):
     return None if t is None else t.data_ptr()
 
@@ -151,6 +175,7 @@ def _workspace(nbytes, device):
     return torch.empty(nbytes, dtype=torch.uint8, device=device)
 
 
+@_on_stream
 def quantize_weights(W, gamma_in=None, stream=None):
     """(T int8 N x K, gamma fp32 [1]) for fp32 N x K weights."""
     _dev_tensor(W, torch.float32, "W")
@@ -164,6 +189,7 @@ def quantize_weights(W, gamma_in=None, stream=None):
     return T, gamma
 
 
+@_on_stream
 def pack(T, stream=None):
     """BL2-T64 packed bytes (uint8, packed_bytes(N, K)) of int8 codes."""
     _dev_tensor(T, torch.int8, "T")
@@ -173,6 +199,7 @@ def pack(T, stream=None):
     return P
 
 
+@_on_stream
 def unpack(P, N: int, K: int, stream=None):
     _dev_tensor(P, torch.uint8, "P")
     T = torch.empty((N, K), dtype=torch.int8, device=P.device)
@@ -180,6 +207,7 @@ def unpack(P, N: int, K: int, stream=None):
     return T
 
 
+@_on_stream
 def quant_act(X, ldq: int | None = None, stream=None):
     """(Q int8 M x ldq, absmax fp32 [M], rowsum int32 [M]); ldq defaults to
     q_stride(K), the stride the matmul call accepts."""
@@ -194,6 +222,7 @@ def quant_act(X, ldq: int | None = None, stream=None):
     return Q, a, rs
 
 
+@_on_stream
 def quant_act_rmsnorm(X, norm_weight=None, eps: float = 1e-5, ldq: int | None = None, stream=None):
     """RMSNorm (gain norm_weight, all ones when None) then the absmax int8
     cast: (Q int8 M x ldq, absmax fp32 [M] of the normalized rows, rowsum
@@ -211,6 +240,7 @@ def quant_act_rmsnorm(X, norm_weight=None, eps: float = 1e-5, ldq: int | None = 
     return Q, a, rs
 
 
+@_on_stream
 def quant_act_add_rmsnorm(X, R, norm_weight=None, eps: float = 1e-5, out=None, ldq: int | None = None,
                           stream=None):
     """(Q, absmax, rowsum, Xsum): Xsum = X + R (written to `out`, which may
@@ -233,6 +263,7 @@ def quant_act_add_rmsnorm(X, R, norm_weight=None, eps: float = 1e-5, out=None, l
     return Q, a, rs, Xs
 
 
+@_on_stream
 def quant_act_relu2_gate(G, U, ldq: int | None = None, stream=None):
     """Gated squared-ReLU H = relu(G)^2 * U of the gate and up projections'
     outputs (M x N fp32 each), then the absmax int8 cast: (Q int8 M x ldq,
@@ -251,6 +282,7 @@ def quant_act_relu2_gate(G, U, ldq: int | None = None, stream=None):
     return Q, a, rs
 
 
+@_on_stream
 def matmul(Q, absmax, rowsum, P, gamma, N: int, K: int, with_acc: bool = False, stream=None):
     """Y (and acc) from already-quantized activations Q (M rows, stride
     Q.shape[1] >= q_stride(K), zero beyond K)."""
@@ -269,6 +301,7 @@ def matmul(Q, absmax, rowsum, P, gamma, N: int, K: int, with_acc: bool = False, 
     return (Y, acc) if with_acc else Y
 
 
+@_on_stream
 def forward(X, P, gamma, N: int, with_acc: bool = False, ws=None, out=None, stream=None):
     """BitLinear forward: Y = rescale(ternary(P) x int8(X)), M x N fp32."""
     _dev_tensor(X, torch.float32, "X")
@@ -285,6 +318,7 @@ def forward(X, P, gamma, N: int, with_acc: bool = False, ws=None, out=None, stre
     return (Y, acc) if with_acc else Y
 
 
+@_on_stream
 def forward_noalloc(X, P, gamma, N: int, with_acc: bool = False, out=None, acc=None, stream=None):
     """BitLinear forward in the library's own scratch array (no workspace):
     bit-identical to forward().  Calls on one GPU share that array and must
@@ -313,6 +347,7 @@ def q_stride5(K: int) -> int:
     return int(lib().bitlinear_q_stride5(K))
 
 
+@_on_stream
 def pack5(T, stream=None):
     """BT5-T32 bytes (five codes per byte) of the N x K int8 codes T."""
     _dev_tensor(T, torch.int8, "T")
@@ -322,6 +357,7 @@ def pack5(T, stream=None):
     return P
 
 
+@_on_stream
 def unpack5(P, N: int, K: int, stream=None):
     _dev_tensor(P, torch.uint8, "P")
     T = torch.empty((N, K), dtype=torch.int8, device=P.device)
@@ -329,6 +365,7 @@ def unpack5(P, N: int, K: int, stream=None):
     return T
 
 
+@_on_stream
 def matmul5(Q, absmax, rowsum, P, gamma, N: int, K: int, with_acc: bool = False, stream=None):
     """matmul over BT5-T32 weights; Q rows have stride Q.shape[1] >=
     q_stride5(K) and are zero beyond K."""
@@ -347,6 +384,7 @@ def matmul5(Q, absmax, rowsum, P, gamma, N: int, K: int, with_acc: bool = False,
     return (Y, acc) if with_acc else Y
 
 
+@_on_stream
 def forward5(X, P, gamma, N: int, with_acc: bool = False, ws=None, out=None, stream=None):
     """BitLinear forward over BT5-T32 weights."""
     _dev_tensor(X, torch.float32, "X")
@@ -367,6 +405,7 @@ def probe_read_sink_words(nbytes: int, chunk_bytes: int) -> int:
     return int(lib().bitlinear_probe_read_sink_words(nbytes, chunk_bytes))
 
 
+@_on_stream
 def probe_read(buf, chunk_bytes: int, sink=None, stream=None):
     """Streaming-read calibration probe over the bytes of a contiguous CUDA
     tensor; returns the uint32 sink (XOR of all sink words = XOR of all
@@ -388,6 +427,7 @@ def probe_mfma_blocks() -> int:
     return int(n.value)
 
 
+@_on_stream
 def probe_mfma(iters: int, a: int, b: int, blocks: int, sink=None, device=None, stream=None):
     """Int8 matrix-instruction calibration probe: blocks*4*iters*4*65536
     int8 operations; every sink entry becomes 2048*a*b*iters."""
@@ -423,6 +463,7 @@ class MultiMatmul:
             _check(-2, "multi_workspace_bytes")
         self.ws = torch.zeros(max(wsb, 16), dtype=torch.uint8, device=device)
 
+    @_on_stream
     def __call__(self, Q, absmax, rowsum, outs=None, accs=None, stream=None):
         """Y_i (M x N_i fp32) for every weight; outs/accs: optional tensors."""
         _dev_tensor(Q, torch.int8, "Q")

@@ -66,7 +66,7 @@ struct Knobs {
     int lut = 0;                 // one-token problems take the table-lookup comparison kernel
     int split_target = 1024;     // aim for at least this many workgroups
     int xcd_order = 3;           // bit 0: streaming kernel, bit 1: tile kernel
-    int mfma_tiles = 0;          // tiles per wave of the streaming MFMA kernel: 0 = by launch size, 1, 2
+    int mfma_tiles = 0;          // tiles per wave of the streaming MFMA kernel above 16 tokens: 0 = by launch size, 1, 2
 };
 const Knobs &knobs()
 {
@@ -102,6 +102,14 @@ bool dot4_tokens(int64_t M) { return M >= 2 && M <= bl::kDot4MaxTokens; }
 // Token counts the 32x32x32 MFMA stream takes (its work items are groups of
 // 4 * tiles-per-wave row tiles; the dot4 kernels work per tile).
 bool mfma32_stream(int64_t M) { return M <= kStreamMaxM && M > bl::kDot4MaxTokens; }
+// Up to 16 tokens the MFMA stream stages the workgroup's activations in LDS
+// (row-major, 80 bytes per token per unit of the K range) and takes one
+// tile per wave (variant 10); beyond, it reads fragment-ordered activations
+// from memory.  Staging cut the 2B sweeps 8-10% (M = 8: 128.5 -> 117.6 us;
+// M = 16: 145.4 -> 131.6 us) and the 3B sweep at M = 8 12% (186.9 -> 164.5).
+constexpr int kAldsMaxTokens = 16;
+bool alds_for(int64_t maxM) { return maxM > bl::kDot4MaxTokens && maxM <= kAldsMaxTokens; }
+int64_t alds_max_units(int64_t M) { return (kStreamLdsMax - 16) / (80 * M); }
 // Tiles per wave of that stream for a launch with `groups` kGroupTiles-tile
 // groups: two when the groups alone fill the part (the split target), else
 // one, which doubles the workgroups without more split-K reductions.
@@ -123,7 +131,7 @@ constexpr int64_t kTileMaxSplits = 2;
 // the launch runs the streaming MFMA kernel, whose work items are groups of
 // 4 * tpw 64-row tiles (p.ntt of them).
 void decompose(Problem &p, int64_t base_items, bool own_q, bool groups4 = false, int tpw = bl::kStreamMfmaTiles,
-               int64_t tile_base = 0)
+               int64_t tile_base = 0, bool alds = false)
 {
     p.KU = (int32_t)((p.K + 63) / 64);
     p.NT = (int32_t)((p.N + 63) / 64);
@@ -159,9 +167,16 @@ void decompose(Problem &p, int64_t base_items, bool own_q, bool groups4 = false,
             p.upsplit = kDot4TokMaxUnits;
             p.ks = (p.KU + kDot4TokMaxUnits - 1) / kDot4TokMaxUnits;
         }
+        // the MFMA stream with staged activations: 80 bytes per token per unit
+        if (groups4 && alds && p.upsplit > alds_max_units(p.M)) {
+            const int64_t cap = alds_max_units(p.M);
+            const int32_t ks = (int32_t)((p.KU + cap - 1) / cap);
+            p.upsplit = (p.KU + ks - 1) / ks;
+            p.ks = (p.KU + p.upsplit - 1) / p.upsplit;
+        }
         // the one-token kernel stages 64 bytes per unit: longer ranges are
         // split into equal parts that fit 64 KiB
-        if (p.M == 1 && p.upsplit > kStreamLdsMax / 64) {
+        if (p.M == 1 && !groups4 && p.upsplit > kStreamLdsMax / 64) {
             const int32_t ks = (p.KU + kStreamLdsMax / 64 - 1) / (kStreamLdsMax / 64);
             p.upsplit = (p.KU + ks - 1) / ks;
             p.ks = (p.KU + p.upsplit - 1) / p.upsplit;
@@ -239,8 +254,9 @@ void decompose_single(Problem &p, bool own_q)
 {
     const int64_t nt = (p.N + 63) / 64;
     const bool g4 = mfma32_stream(p.M);
-    const int tpw = g4 ? mfma_tiles_for((nt + kGroupTiles - 1) / kGroupTiles) : bl::kStreamMfmaTiles;
-    decompose(p, g4 ? (nt + 4 * tpw - 1) / (4 * tpw) : nt, own_q, g4, tpw);
+    const bool alds = g4 && alds_for(p.M);
+    const int tpw = alds ? 1 : g4 ? mfma_tiles_for((nt + kGroupTiles - 1) / kGroupTiles) : bl::kStreamMfmaTiles;
+    decompose(p, g4 ? (nt + 4 * tpw - 1) / (4 * tpw) : nt, own_q, g4, tpw, 0, alds);
 }
 
 int stream_variant_for(int64_t M, int64_t upsplit)
@@ -259,6 +275,7 @@ int stream_variant_for(int64_t M, int64_t upsplit)
 int64_t stream_lds_need(int variant, int64_t M, int64_t upsplit)
 {
     if (variant == 1 || variant == 9) return 0;
+    if (variant >= 10) return 80 * M * upsplit + 16;
     if (variant == 5) return 1024 * upsplit;
     const int64_t slots = (variant == 6 && M > 1) ? bl::kDot4MaxTokens : 1;
     return 64 * slots * upsplit;
@@ -315,7 +332,8 @@ hipError_t launch_contraction(const Problem &p, bool own_q, hipStream_t s)
     if (p.kind == 2) return bl::launch_bt5_single(p, s);
     if (p.kind == 0) {
         const int v = stream_variant_for(p.M, p.upsplit);
-        return bl::launch_stream_single(p, v == 1 && p.stiles == 1 ? 9 : v, s);
+        const int sv = v != 1 ? v : alds_for(p.M) ? 10 : p.stiles == 1 ? 9 : 1;
+        return bl::launch_stream_single(p, sv, s);
     }
     (void)own_q;
     return bl::launch_tile_single(p, s);
@@ -725,7 +743,7 @@ int multi_plan(const int8_t *Q, int64_t ldq, int64_t M, int64_t K, const bitline
     for (int pass = 0; pass < (g4 ? 2 : 1); ++pass) {
         // the MFMA stream's groups: kGroupTiles tiles first, then as many
         // tiles as the tiles-per-wave choice gives
-        if (pass == 1) tpw = mfma_tiles_for(base);
+        if (pass == 1) tpw = alds_for(M) ? 1 : mfma_tiles_for(base);
         base = 0;
         for (int i = 0; i < count; ++i) {
             const int64_t nt = (w[i].N + 63) / 64;
@@ -746,7 +764,7 @@ int multi_plan(const int8_t *Q, int64_t ldq, int64_t M, int64_t K, const bitline
         if (fmt)
             decompose5(p, base);
         else
-            decompose(p, base, false, g4, tpw, tile_base);
+            decompose(p, base, false, g4, tpw, tile_base, g4 && alds_for(M));
         mp.ps.begin[i] = (int32_t)items;
         items += items_of(p);
         max_upsplit = max_upsplit > p.upsplit ? max_upsplit : p.upsplit;
@@ -765,7 +783,7 @@ int multi_plan(const int8_t *Q, int64_t ldq, int64_t M, int64_t K, const bitline
     mp.kind = mp.ps.p[0].kind;
     if (mp.kind == 0) {
         mp.variant = stream_variant_for(M, max_upsplit);
-        if (mp.variant == 1 && tpw == 1) mp.variant = 9;
+        if (mp.variant == 1) mp.variant = alds_for(M) ? 10 : tpw == 1 ? 9 : 1;
         mp.lds = (int)stream_lds_need(mp.variant, M, max_upsplit);
     }
     mp.tick_bytes = up(tick, 256);
@@ -928,7 +946,7 @@ int build_group(const bitlinear_problem *in, int count, char *ws, GroupPlan &out
         // the MFMA kernel's work items are tile groups: kGroupTiles tiles,
         // or 4 when the launch is too small for two tiles per wave
         for (int pass = 0; pass < 2; ++pass) {
-            if (pass == 1) tpw = mfma_tiles_for(base_items);
+            if (pass == 1) tpw = alds_for(max_m) ? 1 : mfma_tiles_for(base_items);
             base_items = 0;
             for (int i = 0; i < count; ++i)
                 if (in[i].format != BITLINEAR_FORMAT_BT5 && in[i].M <= kStreamMaxM)
@@ -937,6 +955,9 @@ int build_group(const bitlinear_problem *in, int count, char *ws, GroupPlan &out
         }
         if (tpw == 1) stream_variant = 9;
     }
+    const bool alds = groups4 && alds_for(max_m);
+    if (alds) stream_variant = 10;
+    int64_t lds_alds = 0;
     for (int i = 0; i < count; ++i) {
         const bitlinear_problem &q = in[i];
         Problem &p = out.probs[i];
@@ -944,7 +965,11 @@ int build_group(const bitlinear_problem *in, int count, char *ws, GroupPlan &out
         if (q.format == BITLINEAR_FORMAT_BT5)
             decompose5(p, base5);
         else
-            decompose(p, base_items, true, groups4, tpw, tile_base);
+            decompose(p, base_items, true, groups4, tpw, tile_base, alds);
+        if (alds && p.kind == 0) {
+            const int64_t b = stream_lds_need(stream_variant, p.M, p.upsplit);
+            lds_alds = lds_alds > b ? lds_alds : b;
+        }
         p.X = q.X;
         p.P = q.P;
         p.gamma = q.gamma;
@@ -995,7 +1020,7 @@ int build_group(const bitlinear_problem *in, int count, char *ws, GroupPlan &out
     h.bt5_max_m = (int32_t)(max_m5 < bl::kBt5Tokens ? max_m5 : bl::kBt5Tokens);
     h.stream_variant = stream_variant;
     h.stream_lds = h.stream_variant == 6 ? (int32_t)lds_tok
-                                         : (int32_t)stream_lds_need(h.stream_variant, 1, max_upsplit);
+                   : alds ? (int32_t)lds_alds : (int32_t)stream_lds_need(h.stream_variant, 1, max_upsplit);
     h.ws_bytes = off;
     int64_t t = up(sizeof(bl::GroupHeader), 16);
     h.off_probs = t;

@@ -374,7 +374,13 @@ __device__ __forceinline__ void stream_dot4_tokens(const Problem &p, int local)
 // of the MFMAs through a two-slot register ring (branch-free: unit indices
 // clamp to the range end and surplus units get zero weights, which add
 // nothing).
-template <int UNROLL, int TPW>
+// ALDS: the activations of the workgroup's K range are staged once in LDS
+// (row-major, at most 16 tokens): token m's 64 bytes of unit u at byte
+// ((u - u0) * M + m) * kTokStride, 16 zero bytes after the last; each wave
+// reads its A operands with ds_read_b128 (lanes of rows past M read the zero
+// chunk) instead of two global loads per unit.
+constexpr int kTokStride = 80;  // 64 bytes + 16: 16 rows at one column hit distinct bank groups
+template <int UNROLL, int TPW, bool ALDS = false>
 __device__ void stream_mfma(const Problem &p, int local)
 {
     const int grp = local / p.ks, split = local - grp * p.ks;
@@ -416,6 +422,34 @@ __device__ void stream_mfma(const Problem &p, int local)
 
     const int n_units = u1 - u0;
     const int groups = (n_units + UNROLL - 1) / UNROLL;
+    int a_lane = 0;  // this lane's byte offset within a staged unit (ALDS)
+    if constexpr (ALDS) {
+        const int M = p.M, nch = n_units * M * 4;
+        const BL_GLOBAL int8_t *q = gload_ptr<int8_t>(p.Q) + 64 * u0;
+        for (int base = threadIdx.x; base < nch; base += 8 * kThreads) {
+            v4i v[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const int c = base + k * kThreads;  // chunk c: unit c / (4 M), token (c / 4) % M, part c % 4
+                if (c < nch) {
+                    const int uu = c / (4 * M), rem = c - uu * 4 * M;
+                    v[k] = *reinterpret_cast<const BL_GLOBAL v4i *>(q + (int64_t)(rem >> 2) * p.ldq + 64 * uu +
+                                                                   16 * (rem & 3));
+                }
+            }
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const int c = base + k * kThreads;
+                if (c < nch) {
+                    const int uu = c / (4 * M), rem = c - uu * 4 * M;
+                    *reinterpret_cast<v4i *>(stream_q_lds + (uu * M + (rem >> 2)) * kTokStride + 16 * (rem & 3)) = v[k];
+                }
+            }
+        }
+        if (threadIdx.x == 0) *reinterpret_cast<v4i *>(stream_q_lds + n_units * M * kTokStride) = zero;
+        a_lane = r < M ? r * kTokStride + 16 * g : n_units * M * kTokStride;
+        __syncthreads();
+    }
     v4u w[2][UNROLL][TPW];
     v4i qa[2][UNROLL], qb[2][UNROLL];
     auto load_group = [&](int slot, int i) {
@@ -424,9 +458,11 @@ __device__ void stream_mfma(const Problem &p, int local)
             const int u = min(u0 + UNROLL * i + j, u1 - 1);
 #pragma unroll
             for (int t = 0; t < TPW; ++t) w[slot][j][t] = load_packed(blk[t] + (int64_t)u * 64);
-            const BL_GLOBAL int8_t *qu = qbase + ustride * u;
-            qa[slot][j] = rv ? *reinterpret_cast<const BL_GLOBAL v4i *>(qu) : zero;
-            qb[slot][j] = rv ? *reinterpret_cast<const BL_GLOBAL v4i *>(qu + hoff) : zero;
+            if constexpr (!ALDS) {
+                const BL_GLOBAL int8_t *qu = qbase + ustride * u;
+                qa[slot][j] = rv ? *reinterpret_cast<const BL_GLOBAL v4i *>(qu) : zero;
+                qb[slot][j] = rv ? *reinterpret_cast<const BL_GLOBAL v4i *>(qu + hoff) : zero;
+            }
         }
     };
     v16i acc[TPW][2];
@@ -441,7 +477,15 @@ __device__ void stream_mfma(const Problem &p, int local)
 #pragma unroll
             for (int j = 0; j < UNROLL; ++j) {
                 const bool live = UNROLL * i + j < n_units;
-                const v4i a = h ? qb[slot][j] : qa[slot][j];
+                v4i a;
+                if constexpr (ALDS) {
+                    // units past the range read any staged unit: their weights are zero
+                    const int uu = min(UNROLL * i + j, n_units - 1);
+                    const int off = r < p.M ? a_lane + uu * p.M * kTokStride + 32 * h : a_lane;
+                    a = *reinterpret_cast<const v4i *>(stream_q_lds + off);
+                } else {
+                    a = h ? qb[slot][j] : qa[slot][j];
+                }
 #pragma unroll
                 for (int t = 0; t < TPW; ++t) {
                     const v4u wj = live ? w[slot][j][t] : zw;
@@ -507,12 +551,14 @@ __device__ void stream_mfma(const Problem &p, int local)
     }
 }
 
-// Instantiations: 1: MFMA stream (3..32 tokens; two tiles per wave); 3: dot4
-// with LDS-staged activations, 8 units in flight per wave (one token); 5:
-// the table-lookup comparison variant (one token); 6: the dot4 token loop
-// for launches whose problems have at most two tokens (one-token problems
-// take the one-slot loop, whose LDS layout and stream are those of 3); 9:
-// as 1 with one tile per wave.
+// Instantiations: 1: MFMA stream (17..32 tokens; two tiles per wave); 3:
+// dot4 with LDS-staged activations, 8 units in flight per wave (one token);
+// 5: the table-lookup comparison variant (one token); 6: the dot4 token
+// loop for launches whose problems have at most two tokens (one-token
+// problems take the one-slot loop, whose LDS layout and stream are those
+// of 3); 9: as 1 with one tile per wave; 10: the MFMA stream for 3..16
+// tokens with LDS-staged activations, one tile per wave, loads four units
+// ahead.
 template <int V>
 __device__ inline void stream_body(const Problem &p, int local)
 {
@@ -525,6 +571,8 @@ __device__ inline void stream_body(const Problem &p, int local)
         stream_mfma<2, kStreamMfmaTiles>(p, local);
     else if constexpr (V == 9)
         stream_mfma<2, 1>(p, local);
+    else if constexpr (V == 10)
+        stream_mfma<4, 1, true>(p, local);
     else if constexpr (V == 5)
         stream_dot4<8, true>(p, local);
     else
@@ -560,6 +608,7 @@ __global__ __launch_bounds__(kThreads) void stream_multi_kernel(ProblemSet ps)
     switch (variant) {                                                                     \
     case 1: hipLaunchKernelGGL(KERNEL<1>, grid, block, 0, s, __VA_ARGS__); break;          \
     case 9: hipLaunchKernelGGL(KERNEL<9>, grid, block, 0, s, __VA_ARGS__); break;          \
+    case 10: hipLaunchKernelGGL(KERNEL<10>, grid, block, LDS, s, __VA_ARGS__); break;      \
     case 5: hipLaunchKernelGGL(KERNEL<5>, grid, block, LDS, s, __VA_ARGS__); break;        \
     case 6: hipLaunchKernelGGL(KERNEL<6>, grid, block, LDS, s, __VA_ARGS__); break;        \
     default: hipLaunchKernelGGL(KERNEL<3>, grid, block, LDS, s, __VA_ARGS__); break;       \
@@ -575,10 +624,11 @@ hipError_t launch_stream_multi(const ProblemSet &ps, int variant, int lds_bytes,
 hipError_t launch_stream_single(const Problem &p, int variant, hipStream_t s)
 {
     // the MFMA variants' work items are tile groups (p.ntt of them)
-    const int64_t tiles = (variant == 1 || variant == 9) ? (int64_t)p.ntt : (int64_t)p.NT;
+    const int64_t tiles = (variant == 1 || variant >= 9) ? (int64_t)p.ntt : (int64_t)p.NT;
     const dim3 grid((unsigned)(tiles * p.ks)), block(kThreads);
     const unsigned slot = variant == 6 ? 64u * kDot4MaxTokens : 64u;
-    const unsigned lds = (variant == 5 ? kLutUnitBytes : slot) * (unsigned)p.upsplit;
+    const unsigned lds = variant >= 10 ? (unsigned)(kTokStride * p.M * p.upsplit + 16)
+                                       : (variant == 5 ? kLutUnitBytes : slot) * (unsigned)p.upsplit;
     BL_STREAM_CASES(stream_single_kernel, lds, p)
     return hipGetLastError();
 }

@@ -190,8 +190,8 @@ def test_group_plan_single_token_quantization():
     # staged activations (3); a 2-token problem switches the streaming kernel to the two-slot dot4
     # token-loop kernel (6), whose LDS holds 64 bytes per unit for one-token
     # problems and 128 for two-token ones; a 5-token problem switches it to
-    # the MFMA stream, which takes one tile per wave (9) in a launch this small
-    # (129 eight-tile groups, fewer than the 1024-workgroup split target)
+    # the MFMA stream with activations staged in LDS (10: 80 bytes per token
+    # per unit, one tile per wave)
     L = B.lib()
     specs = [(1, 4096, 256)] * 16
     arr = _problems(specs)
@@ -216,7 +216,7 @@ def test_group_plan_single_token_quantization():
     wsb3 = L.bitlinear_group_workspace_bytes(arr3, 17)
     assert L.bitlinear_group_plan(arr3, 17, FAKE, wsb3, host3.ctypes.data, tb3) == 0
     hdr3 = np.frombuffer(host3[:48].tobytes(), np.int32)
-    assert hdr3[2] == 21 and hdr3[7] == 9 and hdr3[9] == 0
+    assert hdr3[2] == 21 and hdr3[7] == 10 and hdr3[9] == max(80 * 1 * 4, 80 * 5 * 1) + 16
     # a one-token problem whose K range (1250 units) would need more than
     # 64 KiB of staged activations is split in two (625 units, 40000 bytes),
     # so a 2-token launch still takes the token loop (6)
@@ -228,8 +228,16 @@ def test_group_plan_single_token_quantization():
     hdr4 = np.frombuffer(host4[:48].tobytes(), np.int32)
     assert hdr4[7] == 6 and hdr4[9] == 64 * 625
     # a launch whose eight-tile groups fill the split target keeps two tiles
-    # per wave (1): 130 problems of 64 tiles at M = 5
-    arr6 = _problems([(5, 4096, 256)] * 130)
+    # per wave (1) above 16 tokens: 130 problems of 64 tiles at M = 17; at
+    # M = 5 the staged-activation stream takes one tile per wave (10)
+    arr5 = _problems([(5, 4096, 256)] * 130)
+    tb5 = L.bitlinear_group_table_bytes(arr5, 130)
+    host5 = np.zeros(tb5, np.uint8)
+    wsb5 = L.bitlinear_group_workspace_bytes(arr5, 130)
+    assert L.bitlinear_group_plan(arr5, 130, FAKE, wsb5, host5.ctypes.data, tb5) == 0
+    hdr5 = np.frombuffer(host5[:48].tobytes(), np.int32)
+    assert hdr5[7] == 10 and hdr5[3] == 130 * 16
+    arr6 = _problems([(17, 4096, 256)] * 130)
     tb6 = L.bitlinear_group_table_bytes(arr6, 130)
     host6 = np.zeros(tb6, np.uint8)
     wsb6 = L.bitlinear_group_workspace_bytes(arr6, 130)

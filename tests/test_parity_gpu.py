@@ -455,6 +455,35 @@ def test_forward_split_k(B, M, N, K):
         check_outputs(host(Y), host(acc), ref["acc"], 0.03, ref["absmax"], "forward split-K")
 
 
+def test_calls_on_a_side_stream(B):
+    # matmul and forward at M > 32 (tile kernel, K split: its temporary
+    # workspace holds partial sums) enqueued on a side stream, as a torch
+    # stream object and as a raw handle, while the current stream keeps
+    # allocating and filling memory: the binding allocates its outputs and
+    # workspaces on the launch stream, so none is recycled under the kernels
+    say("side-stream matmul / forward")
+    M, N, K = 96, 640, 2560
+    T = synth.random_ternary(N, K, seed=91)
+    X = synth.activations_np(M, K, seed=92, outlier_frac=0.01)
+    ref = O.forward(X, T, np.float32(0.019))
+    Qp = np.zeros((M, B.q_stride(K)), np.int8)
+    Qp[:, :K] = ref["Q"]
+    Qd, ad, rsd = dev(Qp), dev(ref["absmax"]), dev(ref["rowsum"])
+    P, gd, Xd = dev(O.pack(T)), gamma_dev(0.019), dev(X)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    outs = []
+    for i in range(4):
+        st = side if i % 2 == 0 else side.cuda_stream
+        outs.append(B.matmul(Qd, ad, rsd, P, gd, N, K, with_acc=True, stream=st))
+        outs.append(B.forward(Xd, P, gd, N, with_acc=True, stream=st))
+        junk = torch.full((M * N * 3,), -1.0, device="cuda")  # current-stream churn
+        del junk
+    torch.cuda.synchronize()
+    for Y, acc in outs:
+        check_outputs(host(Y), host(acc), ref["acc"], 0.019, ref["absmax"], "side stream")
+
+
 def test_extreme_values_exact(B):
     # |acc| = 127*K: every code +1 against every activation 127, and the
     # mirrored case; exercises the int32 path at its bound for this K
