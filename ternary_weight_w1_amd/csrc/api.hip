@@ -107,9 +107,19 @@ bool mfma32_stream(int64_t M) { return M <= kStreamMaxM && M > bl::kDot4MaxToken
 // tile per wave (variant 10); beyond, it reads fragment-ordered activations
 // from memory.  Staging cut the 2B sweeps 8-10% (M = 8: 128.5 -> 117.6 us;
 // M = 16: 145.4 -> 131.6 us) and the 3B sweep at M = 8 12% (186.9 -> 164.5).
+// A K range longer than the staging holds is split; problems that would
+// need more than three such splits (the 70B class at 16 tokens: 448 units)
+// keep the launch on the global-load stream, whose larger tiles per wave
+// win there (70B M = 16: 3.69 ms, against 3.97 ms staged).
 constexpr int kAldsMaxTokens = 16;
-bool alds_for(int64_t maxM) { return maxM > bl::kDot4MaxTokens && maxM <= kAldsMaxTokens; }
+constexpr int64_t kAldsMaxSplits = 3;
 int64_t alds_max_units(int64_t M) { return (kStreamLdsMax - 16) / (80 * M); }
+bool alds_for(int64_t maxM) { return maxM > bl::kDot4MaxTokens && maxM <= kAldsMaxTokens; }
+bool alds_fits(int64_t M, int64_t K)
+{
+    const int64_t ku = (K + 63) / 64, cap = alds_max_units(M);
+    return (ku + cap - 1) / cap <= kAldsMaxSplits;
+}
 // Tiles per wave of that stream for a launch with `groups` kGroupTiles-tile
 // groups: two when the groups alone fill the part (the split target), else
 // one, which doubles the workgroups without more split-K reductions.
@@ -254,7 +264,7 @@ void decompose_single(Problem &p, bool own_q)
 {
     const int64_t nt = (p.N + 63) / 64;
     const bool g4 = mfma32_stream(p.M);
-    const bool alds = g4 && alds_for(p.M);
+    const bool alds = g4 && alds_for(p.M) && alds_fits(p.M, p.K);
     const int tpw = alds ? 1 : g4 ? mfma_tiles_for((nt + kGroupTiles - 1) / kGroupTiles) : bl::kStreamMfmaTiles;
     decompose(p, g4 ? (nt + 4 * tpw - 1) / (4 * tpw) : nt, own_q, g4, tpw, 0, alds);
 }
@@ -332,7 +342,7 @@ hipError_t launch_contraction(const Problem &p, bool own_q, hipStream_t s)
     if (p.kind == 2) return bl::launch_bt5_single(p, s);
     if (p.kind == 0) {
         const int v = stream_variant_for(p.M, p.upsplit);
-        const int sv = v != 1 ? v : alds_for(p.M) ? 10 : p.stiles == 1 ? 9 : 1;
+        const int sv = v != 1 ? v : (alds_for(p.M) && alds_fits(p.M, p.K)) ? 10 : p.stiles == 1 ? 9 : 1;
         return bl::launch_stream_single(p, sv, s);
     }
     (void)own_q;
@@ -743,7 +753,7 @@ int multi_plan(const int8_t *Q, int64_t ldq, int64_t M, int64_t K, const bitline
     for (int pass = 0; pass < (g4 ? 2 : 1); ++pass) {
         // the MFMA stream's groups: kGroupTiles tiles first, then as many
         // tiles as the tiles-per-wave choice gives
-        if (pass == 1) tpw = alds_for(M) ? 1 : mfma_tiles_for(base);
+        if (pass == 1) tpw = (alds_for(M) && alds_fits(M, K)) ? 1 : mfma_tiles_for(base);
         base = 0;
         for (int i = 0; i < count; ++i) {
             const int64_t nt = (w[i].N + 63) / 64;
@@ -764,7 +774,7 @@ int multi_plan(const int8_t *Q, int64_t ldq, int64_t M, int64_t K, const bitline
         if (fmt)
             decompose5(p, base);
         else
-            decompose(p, base, false, g4, tpw, tile_base, g4 && alds_for(M));
+            decompose(p, base, false, g4, tpw, tile_base, g4 && alds_for(M) && alds_fits(M, K));
         mp.ps.begin[i] = (int32_t)items;
         items += items_of(p);
         max_upsplit = max_upsplit > p.upsplit ? max_upsplit : p.upsplit;
@@ -783,7 +793,7 @@ int multi_plan(const int8_t *Q, int64_t ldq, int64_t M, int64_t K, const bitline
     mp.kind = mp.ps.p[0].kind;
     if (mp.kind == 0) {
         mp.variant = stream_variant_for(M, max_upsplit);
-        if (mp.variant == 1) mp.variant = alds_for(M) ? 10 : tpw == 1 ? 9 : 1;
+        if (mp.variant == 1) mp.variant = (alds_for(M) && alds_fits(M, K)) ? 10 : tpw == 1 ? 9 : 1;
         mp.lds = (int)stream_lds_need(mp.variant, M, max_upsplit);
     }
     mp.tick_bytes = up(tick, 256);
@@ -941,12 +951,17 @@ int build_group(const bitlinear_problem *in, int count, char *ws, GroupPlan &out
         if (lds_tok > kStreamLdsMax) stream_variant = 1;
     }
     const bool groups4 = stream_variant == 1;
+    // staged activations for the whole launch: every streaming problem fits
+    bool alds_ok = groups4 && alds_for(max_m);
+    for (int i = 0; i < count && alds_ok; ++i)
+        if (in[i].format != BITLINEAR_FORMAT_BT5 && in[i].M <= kStreamMaxM && !alds_fits(max_m, in[i].K))
+            alds_ok = false;
     int tpw = bl::kStreamMfmaTiles;
     if (groups4) {
         // the MFMA kernel's work items are tile groups: kGroupTiles tiles,
         // or 4 when the launch is too small for two tiles per wave
         for (int pass = 0; pass < 2; ++pass) {
-            if (pass == 1) tpw = alds_for(max_m) ? 1 : mfma_tiles_for(base_items);
+            if (pass == 1) tpw = alds_ok ? 1 : mfma_tiles_for(base_items);
             base_items = 0;
             for (int i = 0; i < count; ++i)
                 if (in[i].format != BITLINEAR_FORMAT_BT5 && in[i].M <= kStreamMaxM)
@@ -955,7 +970,7 @@ int build_group(const bitlinear_problem *in, int count, char *ws, GroupPlan &out
         }
         if (tpw == 1) stream_variant = 9;
     }
-    const bool alds = groups4 && alds_for(max_m);
+    const bool alds = alds_ok;
     if (alds) stream_variant = 10;
     int64_t lds_alds = 0;
     for (int i = 0; i < count; ++i) {

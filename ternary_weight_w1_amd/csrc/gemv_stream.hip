@@ -423,6 +423,24 @@ __device__ void stream_mfma(const Problem &p, int local)
     const int n_units = u1 - u0;
     const int groups = (n_units + UNROLL - 1) / UNROLL;
     int a_lane = 0;  // this lane's byte offset within a staged unit (ALDS)
+    v4u w[2][UNROLL][TPW];
+    v4i qa[2][UNROLL], qb[2][UNROLL];
+    auto load_group = [&](int slot, int i) {
+#pragma unroll
+        for (int j = 0; j < UNROLL; ++j) {
+            const int u = min(u0 + UNROLL * i + j, u1 - 1);
+#pragma unroll
+            for (int t = 0; t < TPW; ++t) w[slot][j][t] = load_packed(blk[t] + (int64_t)u * 64);
+            if constexpr (!ALDS) {
+                const BL_GLOBAL int8_t *qu = qbase + ustride * u;
+                qa[slot][j] = rv ? *reinterpret_cast<const BL_GLOBAL v4i *>(qu) : zero;
+                qb[slot][j] = rv ? *reinterpret_cast<const BL_GLOBAL v4i *>(qu + hoff) : zero;
+            }
+        }
+    };
+    // the first group's packed weights are requested before the activations
+    // are staged (they do not depend on them): the two round trips overlap
+    if constexpr (ALDS) load_group(0, 0);
     if constexpr (ALDS) {
         const int M = p.M, nch = n_units * M * 4;
         const BL_GLOBAL int8_t *q = gload_ptr<int8_t>(p.Q) + 64 * u0;
@@ -450,21 +468,6 @@ __device__ void stream_mfma(const Problem &p, int local)
         a_lane = r < M ? r * kTokStride + 16 * g : n_units * M * kTokStride;
         __syncthreads();
     }
-    v4u w[2][UNROLL][TPW];
-    v4i qa[2][UNROLL], qb[2][UNROLL];
-    auto load_group = [&](int slot, int i) {
-#pragma unroll
-        for (int j = 0; j < UNROLL; ++j) {
-            const int u = min(u0 + UNROLL * i + j, u1 - 1);
-#pragma unroll
-            for (int t = 0; t < TPW; ++t) w[slot][j][t] = load_packed(blk[t] + (int64_t)u * 64);
-            if constexpr (!ALDS) {
-                const BL_GLOBAL int8_t *qu = qbase + ustride * u;
-                qa[slot][j] = rv ? *reinterpret_cast<const BL_GLOBAL v4i *>(qu) : zero;
-                qb[slot][j] = rv ? *reinterpret_cast<const BL_GLOBAL v4i *>(qu + hoff) : zero;
-            }
-        }
-    };
     v16i acc[TPW][2];
 #pragma unroll
     for (int t = 0; t < TPW; ++t) acc[t][0] = acc[t][1] = (v16i){};
@@ -494,7 +497,7 @@ __device__ void stream_mfma(const Problem &p, int local)
                 }
             }
     };
-    load_group(0, 0);
+    if constexpr (!ALDS) load_group(0, 0);
     int i = 0;
     for (; i + 2 <= groups; i += 2) {
         load_group(1, i + 1);
