@@ -63,6 +63,7 @@ struct QDest {
 //              may be x_ or res_ (an in-place residual update).
 constexpr int kRegF4 = 32;
 constexpr int kFewTokens = 2048;
+constexpr int kSingleTokens = 16;  // fewer rows: sixteen waves per row
 enum { kPlain = 0, kRmsNorm = 1, kRelu2Gate = 2, kAddRmsNorm = 3 };
 
 template <int WAVES, int MODE>
@@ -72,7 +73,9 @@ __device__ void quant_row(const float *x_, int K, const QDest &dst, float *absma
     constexpr bool NORM = MODE == kRmsNorm || MODE == kAddRmsNorm;
     constexpr bool ADD = MODE == kAddRmsNorm;
     constexpr int kThr = 64 * WAVES;
-    constexpr int kRegs = kRegF4 / WAVES;
+    // float4 groups per thread kept in registers: 32 with one wave, 8 with
+    // four, 3 with sixteen (rows up to 8192, 8192 and 12288 values)
+    constexpr int kRegs = WAVES == 1 ? kRegF4 : WAVES == 4 ? kRegF4 / 4 : 3;
     __shared__ float red_a[WAVES];
     __shared__ int red_s[WAVES];
     __shared__ double red_d[WAVES];
@@ -118,11 +121,16 @@ __device__ void quant_row(const float *x_, int K, const QDest &dst, float *absma
         return h;
     };
     v4f v[kRegs];
+    // sixteen waves serve single tokens (decode chains), where every memory
+    // round trip is on the critical path: the norm's gains come with the row
+    constexpr bool kGainRegs = NORM && WAVES == 16;
+    v4f gv[kGainRegs ? kRegs : 1];
     if (in_regs) {
 #pragma unroll
         for (int j = 0; j < kRegs; ++j) {
             const int f = t + kThr * j;
             v[j] = f < nf ? __builtin_nontemporal_load(x4 + f) : zero4;
+            if constexpr (kGainRegs) gv[j] = (g_ && f < nf) ? g4[f] : zero4;
             if constexpr (MODE == kRelu2Gate)
                 if (f < nf) v[j] = relu2_4(v[j], __builtin_nontemporal_load(g4 + f));
             if constexpr (ADD)
@@ -190,7 +198,15 @@ __device__ void quant_row(const float *x_, int K, const QDest &dst, float *absma
 #pragma unroll
             for (int j = 0; j < kRegs; ++j) {
                 const int f = t + kThr * j;
-                if (f < nf) v[j] = norm4(v[j], f);
+                if constexpr (kGainRegs) {
+                    // (x * inv) * g: the same two roundings as norm4
+                    if (f < nf) {
+                        v[j] = v[j] * inv;
+                        if (g_) v[j] = v[j] * gv[j];
+                    }
+                } else {
+                    if (f < nf) v[j] = norm4(v[j], f);
+                }
             }
         }
     }
@@ -312,7 +328,10 @@ hipError_t launch_quant_act(const float *X, int64_t M, int64_t K, int8_t *Q, int
                             int qtiled, float *absmax, int32_t *rowsum, uint32_t *zero_ptr,
                             int zero_n, hipStream_t s)
 {
-    if (M < kFewTokens)
+    if (M < kSingleTokens)
+        hipLaunchKernelGGL((quant_act_kernel<16, kPlain>), dim3((unsigned)M), dim3(1024), 0, s, X, (int)K, Q,
+                           ldq, qtiled, absmax, rowsum, zero_ptr, zero_n, nullptr, 0.0f);
+    else if (M < kFewTokens)
         hipLaunchKernelGGL((quant_act_kernel<4, kPlain>), dim3((unsigned)M), dim3(256), 0, s, X, (int)K, Q,
                            ldq, qtiled, absmax, rowsum, zero_ptr, zero_n, nullptr, 0.0f);
     else
@@ -325,7 +344,10 @@ hipError_t launch_quant_act_rmsnorm(const float *X, int64_t M, int64_t K, const 
                                     int8_t *Q, int64_t ldq, float *absmax, int32_t *rowsum,
                                     hipStream_t s)
 {
-    if (M < kFewTokens)
+    if (M < kSingleTokens)
+        hipLaunchKernelGGL((quant_act_kernel<16, kRmsNorm>), dim3((unsigned)M), dim3(1024), 0, s, X, (int)K, Q,
+                           ldq, 0, absmax, rowsum, nullptr, 0, g, eps);
+    else if (M < kFewTokens)
         hipLaunchKernelGGL((quant_act_kernel<4, kRmsNorm>), dim3((unsigned)M), dim3(256), 0, s, X, (int)K, Q,
                            ldq, 0, absmax, rowsum, nullptr, 0, g, eps);
     else
@@ -338,7 +360,10 @@ hipError_t launch_quant_act_add_rmsnorm(const float *X, const float *R, int64_t 
                                         float eps, float *Xsum, int8_t *Q, int64_t ldq, float *absmax,
                                         int32_t *rowsum, hipStream_t s)
 {
-    if (M < kFewTokens)
+    if (M < kSingleTokens)
+        hipLaunchKernelGGL((quant_act_kernel<16, kAddRmsNorm>), dim3((unsigned)M), dim3(1024), 0, s, X, (int)K,
+                           Q, ldq, 0, absmax, rowsum, nullptr, 0, g, eps, R, Xsum);
+    else if (M < kFewTokens)
         hipLaunchKernelGGL((quant_act_kernel<4, kAddRmsNorm>), dim3((unsigned)M), dim3(256), 0, s, X, (int)K,
                            Q, ldq, 0, absmax, rowsum, nullptr, 0, g, eps, R, Xsum);
     else
@@ -350,7 +375,10 @@ hipError_t launch_quant_act_add_rmsnorm(const float *X, const float *R, int64_t 
 hipError_t launch_quant_act_relu2_gate(const float *G, const float *U, int64_t M, int64_t N, int8_t *Q,
                                        int64_t ldq, float *absmax, int32_t *rowsum, hipStream_t s)
 {
-    if (M < kFewTokens)
+    if (M < kSingleTokens)
+        hipLaunchKernelGGL((quant_act_kernel<16, kRelu2Gate>), dim3((unsigned)M), dim3(1024), 0, s, G, (int)N,
+                           Q, ldq, 0, absmax, rowsum, nullptr, 0, U, 0.0f);
+    else if (M < kFewTokens)
         hipLaunchKernelGGL((quant_act_kernel<4, kRelu2Gate>), dim3((unsigned)M), dim3(256), 0, s, G, (int)N,
                            Q, ldq, 0, absmax, rowsum, nullptr, 0, U, 0.0f);
     else
