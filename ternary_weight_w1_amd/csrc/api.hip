@@ -67,6 +67,7 @@ struct Knobs {
     int split_target = 1024;     // aim for at least this many workgroups
     int xcd_order = 3;           // bit 0: streaming kernel, bit 1: tile kernel
     int mfma_tiles = 0;          // tiles per wave of the streaming MFMA kernel above 16 tokens: 0 = by launch size, 1, 2
+    int wide = 1;                // one-token launches over few tiles take the wide kernel
 };
 const Knobs &knobs()
 {
@@ -76,6 +77,7 @@ const Knobs &knobs()
         if (const char *s = getenv("BITLINEAR_DOT4_VARIANT")) v.lut = atoi(s) == 5;
         if (const char *s = getenv("BITLINEAR_XCD_ORDER")) v.xcd_order = atoi(s) & 3;
         if (const char *s = getenv("BITLINEAR_MFMA_TILES")) v.mfma_tiles = (atoi(s) == 1 || atoi(s) == 2) ? atoi(s) : 0;
+        if (const char *s = getenv("BITLINEAR_WIDE")) v.wide = atoi(s) != 0;
         return v;
     }();
     return k;
@@ -129,6 +131,34 @@ int mfma_tiles_for(int64_t groups)
     return groups < knobs().split_target ? 1 : bl::kStreamMfmaTiles;
 }
 
+// One-token launches of at most one workgroup per compute unit (256 of 16
+// waves, or 512 of 8) take the wide kernel: a workgroup's W waves share one
+// 64-row tile and K range, so the launch is one memory round trip per
+// workgroup and, where W * kWideUnits units cover K, needs no K split.
+// Returns W for a launch of `tiles` row tiles with KU units each, or 0.
+constexpr int64_t kWideSlots16 = 256, kWideSlots8 = 512;
+int64_t wide_splits(int64_t KU, int W) { return (KU + (int64_t)W * bl::kWideUnits - 1) / ((int64_t)W * bl::kWideUnits); }
+int wide_waves(int64_t M, int64_t tiles, int64_t KU)
+{
+    if (M != 1 || !knobs().wide || knobs().lut) return 0;
+    if (tiles * wide_splits(KU, 16) <= kWideSlots16) return 16;
+    if (tiles * wide_splits(KU, 8) <= kWideSlots8) return 8;
+    return 0;
+}
+// Decomposition of a one-token problem for the wide kernel with W waves.
+void decompose_wide(Problem &p, int W)
+{
+    p.kind = 0;
+    p.KU = (int32_t)((p.K + 63) / 64);
+    p.NT = (int32_t)((p.N + 63) / 64);
+    p.mt = p.ntt = p.mtile = p.qtiled = p.stiles = 0;
+    p.wide = W;
+    p.ks = (int32_t)wide_splits(p.KU, W);
+    p.upsplit = (p.KU + p.ks - 1) / p.ks;
+    p.ks = (p.KU + p.upsplit - 1) / p.upsplit;
+}
+int wide_variant(int W) { return W == 16 ? 12 : 13; }
+
 // Most K splits of a tile-kernel problem (measured on the chained 3B step at
 // M = 64: 3.16 ms unsplit, 2.70 at two, 2.74 at four, 3.06 at eight, 3.33 at
 // up to sixteen).
@@ -147,7 +177,7 @@ void decompose(Problem &p, int64_t base_items, bool own_q, bool groups4 = false,
     p.NT = (int32_t)((p.N + 63) / 64);
     p.ks = 1;
     p.upsplit = p.KU;
-    p.mt = p.ntt = p.mtile = p.qtiled = p.stiles = 0;
+    p.mt = p.ntt = p.mtile = p.qtiled = p.stiles = p.wide = 0;
     if (p.M <= kStreamMaxM) {
         p.kind = 0;
         if (groups4) {
@@ -263,6 +293,10 @@ int64_t own_ldq(const Problem &p) { return p.fmt ? 160 * (int64_t)p.KU5 : 64 * (
 void decompose_single(Problem &p, bool own_q)
 {
     const int64_t nt = (p.N + 63) / 64;
+    if (const int W = wide_waves(p.M, nt, (p.K + 63) / 64)) {
+        decompose_wide(p, W);
+        return;
+    }
     const bool g4 = mfma32_stream(p.M);
     const bool alds = g4 && alds_for(p.M) && alds_fits(p.M, p.K);
     const int tpw = alds ? 1 : g4 ? mfma_tiles_for((nt + kGroupTiles - 1) / kGroupTiles) : bl::kStreamMfmaTiles;
@@ -285,7 +319,7 @@ int stream_variant_for(int64_t M, int64_t upsplit)
 int64_t stream_lds_need(int variant, int64_t M, int64_t upsplit)
 {
     if (variant == 1 || variant == 9) return 0;
-    if (variant >= 10) return 80 * M * upsplit + 16;
+    if (variant == 10) return 80 * M * upsplit + 16;
     if (variant == 5) return 1024 * upsplit;
     const int64_t slots = (variant == 6 && M > 1) ? bl::kDot4MaxTokens : 1;
     return 64 * slots * upsplit;
@@ -341,6 +375,7 @@ hipError_t launch_contraction(const Problem &p, bool own_q, hipStream_t s)
 {
     if (p.kind == 2) return bl::launch_bt5_single(p, s);
     if (p.kind == 0) {
+        if (p.wide) return bl::launch_stream_single(p, wide_variant(p.wide), s);
         const int v = stream_variant_for(p.M, p.upsplit);
         const int sv = v != 1 ? v : (alds_for(p.M) && alds_fits(p.M, p.K)) ? 10 : p.stiles == 1 ? 9 : 1;
         return bl::launch_stream_single(p, sv, s);
@@ -767,12 +802,17 @@ int multi_plan(const int8_t *Q, int64_t ldq, int64_t M, int64_t K, const bitline
         for (int i = 0; i < count; ++i)
             tile_base += (M + kTileTokens - 1) / kTileTokens * (((w[i].N + 63) / 64 + kTileRowTiles - 1) / kTileRowTiles);
     }
+    int64_t all_tiles = 0;
+    for (int i = 0; i < count; ++i) all_tiles += (w[i].N + 63) / 64;
+    const int W = fmt ? 0 : wide_waves(M, all_tiles, (K + 63) / 64);
     int64_t items = 0, tick = 0, part = 0;
     for (int i = 0; i < count; ++i) {
         Problem &p = mp.ps.p[i];
         p = make_problem(M, w[i].N, K);
         if (fmt)
             decompose5(p, base);
+        else if (W)
+            decompose_wide(p, W);
         else
             decompose(p, base, false, g4, tpw, tile_base, g4 && alds_for(M) && alds_fits(M, K));
         mp.ps.begin[i] = (int32_t)items;
@@ -791,7 +831,10 @@ int multi_plan(const int8_t *Q, int64_t ldq, int64_t M, int64_t K, const bitline
     mp.ps.begin[count] = (int32_t)items;
     mp.ps.count = count;
     mp.kind = mp.ps.p[0].kind;
-    if (mp.kind == 0) {
+    if (mp.kind == 0 && W) {
+        mp.variant = wide_variant(W);
+        mp.lds = (int)stream_lds_need(mp.variant, M, max_upsplit);
+    } else if (mp.kind == 0) {
         mp.variant = stream_variant_for(M, max_upsplit);
         if (mp.variant == 1) mp.variant = (alds_for(M) && alds_fits(M, K)) ? 10 : tpw == 1 ? 9 : 1;
         mp.lds = (int)stream_lds_need(mp.variant, M, max_upsplit);

@@ -49,6 +49,9 @@ constexpr int kStreamMaxTokens = 32;
 constexpr int kStreamMfmaTiles = 2;
 // token counts above which that kernel reads fragment-ordered activations
 constexpr int kStreamFragTokens = 16;
+// one-token launches over few tiles take the wide kernel: 8 or 16 waves per
+// 64-row tile, each wave holding up to kWideUnits 64-code units in flight
+constexpr int kWideUnits = 12;
 // most tokens the packed-dot4 streaming kernels take (64 LDS bytes per token
 // per unit of the workgroup's K range): one, and two in the token loop;
 // from three tokens on the matrix-instruction stream is faster
@@ -85,7 +88,7 @@ struct Problem {
     int32_t fmt;           // 0: BL2-T64 weights, 1: BT5-T32 weights
     int32_t KU5;           // ceil(K/160), the BT5-T32 units (0 for BL2-T64)
     int32_t stiles;        // 64-row tiles per wave of the streaming MFMA kernel (1 or 2; else 0)
-    int32_t pad_;
+    int32_t wide;          // waves per workgroup of the one-token wide kernel (8 or 16; else 0)
 };
 static_assert(sizeof(Problem) == 160, "Problem layout is shared by host and device");
 

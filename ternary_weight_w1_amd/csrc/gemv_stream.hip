@@ -266,6 +266,82 @@ __device__ void stream_dot4(const Problem &p, int local)
     if (ok[0]) finish(n, sum[0], gamma);
 }
 
+// One token over few tiles (the matrices of one decode layer, launched on
+// their own): the launch is too small to be bound by bandwidth, and its time
+// is the chain of memory round trips of one workgroup.  W waves (8 or 16)
+// share one 64-row tile and K range; wave w takes units u0 + w, u0 + w + W,
+// ... (at most kWideUnits) and requests all of them before the activations
+// are staged, so the weight and activation round trips overlap and nothing
+// waits on memory after the barrier.  The waves' sums meet in LDS; where
+// W * kWideUnits units cover K there is no K split and no hand-off through
+// memory, otherwise splits work as in the other streaming kernels.
+template <int W>
+__device__ void stream_dot4_wide(const Problem &p, int local)
+{
+    constexpr int kThr = 64 * W;
+    __shared__ int red[W][64];
+    const int tile = local / p.ks, split = local - tile * p.ks;
+    const int u0 = split * p.upsplit;
+    const int u1 = min(p.KU, u0 + p.upsplit);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63, g = lane >> 5;
+    const BL_GLOBAL v4u *blk = gload_ptr<v4u>(p.P + (int64_t)tile * p.KU * kBlockBytes) + lane;
+    // units of this wave (the host keeps the split within W * kWideUnits)
+    const int nu = u1 - u0 > wave ? (u1 - u0 - wave + W - 1) / W : 0;
+    v4u w[kWideUnits];
+#pragma unroll
+    for (int j = 0; j < kWideUnits; ++j)
+        if (j < nu) w[j] = load_packed(blk + (int64_t)(u0 + wave + W * j) * 64);
+    {
+        const int n = 4 * (u1 - u0);  // 16-byte chunks of the range
+        const BL_GLOBAL v4i *src = gload_ptr<v4i>(p.Q + 64 * u0);
+        v4i *dst = reinterpret_cast<v4i *>(stream_q_lds);
+        for (int i = threadIdx.x; i < n; i += kThr) dst[i] = src[i];
+    }
+    __syncthreads();
+    int acc0 = 0, acc1 = 0;  // rows r and 32 + r of the tile
+#pragma unroll
+    for (int j = 0; j < kWideUnits; ++j)
+        if (j < nu) {
+            const int8_t *q = stream_q_lds + 64 * (wave + W * j) + 16 * g;
+            const v4i qa = *reinterpret_cast<const v4i *>(q);
+            const v4i qb = *reinterpret_cast<const v4i *>(q + 32);
+            acc0 = dot16(w[j].x, qa, acc0);
+            acc0 = dot16(w[j].y, qb, acc0);
+            acc1 = dot16(w[j].z, qa, acc1);
+            acc1 = dot16(w[j].w, qb, acc1);
+        }
+    // lanes r and r + 32 hold the two code chunks of the same rows
+    acc0 += __shfl_xor(acc0, 32, 64);
+    acc1 += __shfl_xor(acc1, 32, 64);
+    if (lane < 32) {
+        red[wave][lane] = acc0;
+        red[wave][32 + lane] = acc1;
+    }
+    __syncthreads();
+
+    const int t = threadIdx.x;
+    const int n = 64 * tile + t;
+    const float gamma = *p.gamma;
+    int total = 0;
+    if (t < 64) {
+#pragma unroll
+        for (int i = 0; i < W; ++i) total += red[i][t];
+    }
+    if (p.ks == 1) {
+        if (t < 64 && n < p.N) finish_output(p, gamma, 0, n, total);
+        return;
+    }
+    const int64_t ldp = (int64_t)p.NT * 64;  // partial row stride
+    if (t < 64) put_partial(p.acc_ws + ((int64_t)split * p.M * ldp + n), total);
+    if (!arrive_last(p, tile)) return;
+    const int64_t off[1] = {n};
+    const bool ok[1] = {t < 64 && n < p.N};
+    int32_t sum[1];
+    sum_partials<1>(p.acc_ws, off, ok, (int64_t)p.M * ldp, p.ks, sum);
+    if (ok[0]) finish_output(p, gamma, 0, n, sum[0]);
+}
+
 // 1..4 tokens (dot4): the four planes of a packed word are unpacked once
 // and serve every token, so each token costs 4 dot products per 16 codes on
 // top of the 7 shared bit operations.  The K range's activations are staged
@@ -561,7 +637,7 @@ __device__ void stream_mfma(const Problem &p, int local)
 // problems take the one-slot loop, whose LDS layout and stream are those
 // of 3); 9: as 1 with one tile per wave; 10: the MFMA stream for 3..16
 // tokens with LDS-staged activations, one tile per wave, loads four units
-// ahead.
+// ahead; 12 and 13: the one-token wide kernel with 16 and 8 waves.
 template <int V>
 __device__ inline void stream_body(const Problem &p, int local)
 {
@@ -576,20 +652,27 @@ __device__ inline void stream_body(const Problem &p, int local)
         stream_mfma<2, 1>(p, local);
     else if constexpr (V == 10)
         stream_mfma<4, 1, true>(p, local);
+    else if constexpr (V == 12)
+        stream_dot4_wide<16>(p, local);
+    else if constexpr (V == 13)
+        stream_dot4_wide<8>(p, local);
     else if constexpr (V == 5)
         stream_dot4<8, true>(p, local);
     else
         stream_dot4<8>(p, local);
 }
 
+// threads per workgroup of variant V
+__host__ __device__ constexpr int stream_threads(int V) { return V == 12 ? 1024 : V == 13 ? 512 : kThreads; }
+
 template <int V>
-__global__ __launch_bounds__(kThreads) void stream_single_kernel(Problem p)
+__global__ __launch_bounds__(stream_threads(V)) void stream_single_kernel(Problem p)
 {
     stream_body<V>(p, blockIdx.x);
 }
 
 template <int V>
-__global__ __launch_bounds__(kThreads) void stream_group_kernel(const Problem *__restrict__ probs,
+__global__ __launch_bounds__(stream_threads(V)) void stream_group_kernel(const Problem *__restrict__ probs,
                                                                 const uint2 *__restrict__ item_map)
 {
     const uint2 it = item_map[blockIdx.x];
@@ -598,7 +681,7 @@ __global__ __launch_bounds__(kThreads) void stream_group_kernel(const Problem *_
 }
 
 template <int V>
-__global__ __launch_bounds__(kThreads) void stream_multi_kernel(ProblemSet ps)
+__global__ __launch_bounds__(stream_threads(V)) void stream_multi_kernel(ProblemSet ps)
 {
     const int i = multi_index(ps, blockIdx.x);
     stream_body<V>(ps.p[i], (int)blockIdx.x - ps.begin[i]);
@@ -614,12 +697,14 @@ __global__ __launch_bounds__(kThreads) void stream_multi_kernel(ProblemSet ps)
     case 10: hipLaunchKernelGGL(KERNEL<10>, grid, block, LDS, s, __VA_ARGS__); break;      \
     case 5: hipLaunchKernelGGL(KERNEL<5>, grid, block, LDS, s, __VA_ARGS__); break;        \
     case 6: hipLaunchKernelGGL(KERNEL<6>, grid, block, LDS, s, __VA_ARGS__); break;        \
+    case 12: hipLaunchKernelGGL(KERNEL<12>, grid, block, LDS, s, __VA_ARGS__); break;      \
+    case 13: hipLaunchKernelGGL(KERNEL<13>, grid, block, LDS, s, __VA_ARGS__); break;      \
     default: hipLaunchKernelGGL(KERNEL<3>, grid, block, LDS, s, __VA_ARGS__); break;       \
     }
 
 hipError_t launch_stream_multi(const ProblemSet &ps, int variant, int lds_bytes, hipStream_t s)
 {
-    const dim3 grid((unsigned)ps.begin[ps.count]), block(kThreads);
+    const dim3 grid((unsigned)ps.begin[ps.count]), block(stream_threads(variant));
     BL_STREAM_CASES(stream_multi_kernel, (unsigned)lds_bytes, ps)
     return hipGetLastError();
 }
@@ -627,10 +712,10 @@ hipError_t launch_stream_multi(const ProblemSet &ps, int variant, int lds_bytes,
 hipError_t launch_stream_single(const Problem &p, int variant, hipStream_t s)
 {
     // the MFMA variants' work items are tile groups (p.ntt of them)
-    const int64_t tiles = (variant == 1 || variant >= 9) ? (int64_t)p.ntt : (int64_t)p.NT;
-    const dim3 grid((unsigned)(tiles * p.ks)), block(kThreads);
+    const int64_t tiles = (variant == 1 || variant == 9 || variant == 10) ? (int64_t)p.ntt : (int64_t)p.NT;
+    const dim3 grid((unsigned)(tiles * p.ks)), block(stream_threads(variant));
     const unsigned slot = variant == 6 ? 64u * kDot4MaxTokens : 64u;
-    const unsigned lds = variant >= 10 ? (unsigned)(kTokStride * p.M * p.upsplit + 16)
+    const unsigned lds = variant == 10 ? (unsigned)(kTokStride * p.M * p.upsplit + 16)
                                        : (variant == 5 ? kLutUnitBytes : slot) * (unsigned)p.upsplit;
     BL_STREAM_CASES(stream_single_kernel, lds, p)
     return hipGetLastError();
@@ -639,7 +724,7 @@ hipError_t launch_stream_single(const Problem &p, int variant, hipStream_t s)
 hipError_t launch_stream_group(const Problem *probs, const uint2 *item_map, int n_items,
                                int variant, int lds_bytes, hipStream_t s)
 {
-    const dim3 grid((unsigned)n_items), block(kThreads);
+    const dim3 grid((unsigned)n_items), block(stream_threads(variant));
     BL_STREAM_CASES(stream_group_kernel, (unsigned)lds_bytes, probs, item_map)
     return hipGetLastError();
 }

@@ -143,10 +143,12 @@ def test_pack_quant_matmul_forward_validation():
     assert _st("bitlinear_forward", FAKE, 1, 64, FAKE, FAKE, 64, FAKE, None, None, 0, None)[0] == -4
     assert _st("bitlinear_forward", FAKE, 1, 64, FAKE, FAKE, 64, FAKE + 4, None, FAKE, 1 << 20,
                None)[0] == -3
-    # split-K matmul (one row tile, long K) needs a workspace too
-    need = B.workspace_bytes(B.WS_MATMUL, 1, 64, 8192)
+    # one token, one row tile: a wide workgroup (16 waves x 12 units) covers
+    # K = 8192 without a split and needs no workspace; K = 16384 is split
+    assert B.workspace_bytes(B.WS_MATMUL, 1, 64, 8192) == 0
+    need = B.workspace_bytes(B.WS_MATMUL, 1, 64, 16384)
     assert need > 0
-    assert _st("bitlinear_matmul", FAKE, 8192, FAKE, FAKE, 1, 8192, FAKE, FAKE, 64, FAKE, None,
+    assert _st("bitlinear_matmul", FAKE, 16384, FAKE, FAKE, 1, 16384, FAKE, FAKE, 64, FAKE, None,
                FAKE, need - 1, None)[0] == -4
 
 
@@ -335,8 +337,10 @@ def test_matmul_multi_validation():
     assert L.bitlinear_multi_workspace_bytes(w, 3, 1, 2560) != smax
     assert L.bitlinear_multi_workspace_bytes(w, 0, 1, 2560) == smax
     assert L.bitlinear_multi_workspace_bytes(_weights([64] * 5), 5, 1, 64) == smax
-    # one long-K small-N matrix splits K: counters and partials need workspace
-    assert L.bitlinear_multi_workspace_bytes(_weights([64]), 1, 1, 8192) > 0
+    # one long-K small-N matrix splits K beyond what one wide workgroup
+    # covers: counters and partials need workspace
+    assert L.bitlinear_multi_workspace_bytes(_weights([64]), 1, 1, 8192) == 0
+    assert L.bitlinear_multi_workspace_bytes(_weights([64]), 1, 1, 16384) > 0
     mm = L.bitlinear_matmul_multi
     assert mm(None, 2560, FAKE, FAKE, 1, 2560, w, 3, None, 0, None) == -1
     assert mm(FAKE, 2496, FAKE, FAKE, 1, 2560, w, 3, None, 0, None) == -2      # ldq < K
@@ -346,8 +350,8 @@ def test_matmul_multi_validation():
     assert mm(FAKE, 2560, FAKE, FAKE, 1, 2560, mixed, 2, None, 0, None) == -6
     bt5 = _weights([640], fmt=1)
     assert mm(FAKE, 2560, FAKE, FAKE, 1, 2561, bt5, 1, None, 0, None) == -2   # BT5 needs ldq >= 2720 (160-code units)
-    need = L.bitlinear_multi_workspace_bytes(_weights([64]), 1, 1, 8192)
-    assert mm(FAKE, 8192, FAKE, FAKE, 1, 8192, _weights([64]), 1, FAKE, need - 1, None) == -4
+    need = L.bitlinear_multi_workspace_bytes(_weights([64]), 1, 1, 16384)
+    assert mm(FAKE, 16384, FAKE, FAKE, 1, 16384, _weights([64]), 1, FAKE, need - 1, None) == -4
 
 
 # ---- calibration probes (include/bitlinear_probe.h): validation only

@@ -417,10 +417,12 @@ def test_matmul_parity_injected_scales(B, M, N, K):
     check_outputs(host(Y), host(acc), ref, g, a, f"M={M} N={N} K={K}")
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 64, 8192), (5, 64, 8192), (1, 200, 4000), (3, 130, 131072)])
+@pytest.mark.parametrize("M,N,K", [(1, 64, 16384), (5, 64, 8192), (1, 200, 40000), (3, 130, 131072),
+                                   (1, 64, 131072)])
 def test_matmul_split_k(B, M, N, K):
     # few row tiles and a long K: the streaming kernel splits K over
-    # workgroups and the last one to arrive adds the partial sums
+    # workgroups and the last one to arrive adds the partial sums (one
+    # token: K beyond the 192 units one wide workgroup covers)
     say("matmul split-K", M, N, K)
     assert B.workspace_bytes(B.WS_MATMUL, M, N, K) > 0
     T = synth.random_ternary(N, K, seed=K)
@@ -453,6 +455,23 @@ def test_forward_split_k(B, M, N, K):
     for _ in range(2):
         Y, acc = B.forward(Xd, Pd, gamma_dev(0.03), N, with_acc=True)
         check_outputs(host(Y), host(acc), ref["acc"], 0.03, ref["absmax"], "forward split-K")
+
+
+@pytest.mark.parametrize("N,K", [(1, 1), (100, 12288), (100, 12289), (130, 3200), (64, 8640),
+                                 (17000, 3000), (16400, 12000)])
+def test_forward_wide_one_token(B, N, K):
+    # one token over at most 256 row tiles (512 with 8 waves) takes the wide
+    # kernel: 192 units (96 with 8 waves) per workgroup without a split, one
+    # unit more splits K in two; 17000 rows take 8 waves; 16400 rows at
+    # K = 12000 would need 514 workgroups and take the default stream
+    say("forward wide", N, K)
+    T = synth.random_ternary(N, K, seed=N + 5 * K)
+    X = synth.activations_np(1, K, seed=N + K, outlier_frac=0.01)
+    ref = O.forward(X, T, np.float32(0.021))
+    Xd, Pd = dev(X), dev(O.pack(T))
+    for _ in range(2):
+        Y, acc = B.forward(Xd, Pd, gamma_dev(0.021), N, with_acc=True)
+        check_outputs(host(Y), host(acc), ref["acc"], 0.021, ref["absmax"], "forward wide")
 
 
 def test_calls_on_a_side_stream(B):
@@ -661,6 +680,7 @@ def test_lut_variant_subprocess(B):
                                          (5, 640, (257, 100), 0), (40, 700, (300, 130, 64, 520), 0),
                                          (48, 2560, (640, 1000), 0),
                                          (100, 256, (256, 512), 0), (1, 8192, (64,), 0),
+                                         (1, 16384, (64, 100), 0), (1, 3200, (8640, 8640), 0),
                                          (1, 2560, (640, 2560, 100), 1), (9, 1000, (320, 64), 1),
                                          (20, 8192, (64, 96), 1)])
 def test_matmul_multi_parity(B, M, K, Ns, fmt):
@@ -724,6 +744,7 @@ print("knob ok")
 KNOB_SETTINGS = [
     ("BITLINEAR_MFMA_TILES", "1"), ("BITLINEAR_MFMA_TILES", "2"),
     ("BITLINEAR_SPLIT_TARGET", "1"), ("BITLINEAR_SPLIT_TARGET", "100000"), ("BITLINEAR_XCD_ORDER", "0"),
+    ("BITLINEAR_WIDE", "0"),
 ]
 
 
