@@ -5,6 +5,7 @@
 #include <bitlinear.h>
 #include <bitlinear_probe.h>
 
+#include <algorithm>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
@@ -131,18 +132,29 @@ int mfma_tiles_for(int64_t groups)
     return groups < knobs().split_target ? 1 : bl::kStreamMfmaTiles;
 }
 
-// One-token launches of at most one workgroup per compute unit (256 of 16
-// waves, or 512 of 8) take the wide kernel: a workgroup's W waves share one
-// 64-row tile and K range, so the launch is one memory round trip per
-// workgroup and, where W * kWideUnits units cover K, needs no K split.
-// Returns W for a launch of `tiles` row tiles with KU units each, or 0.
+// Launches of 1..16 tokens with at most one workgroup per compute unit (256
+// of 16 waves, or 512 of 8) take the wide kernels: a workgroup's W waves
+// share one 64-row tile and K range, so the launch is one memory round trip
+// per workgroup and, where one split covers K, needs no hand-off through
+// memory.  wide_waves returns W for a launch of `tiles` row tiles with KU
+// units each, or 0.
 constexpr int64_t kWideSlots16 = 256, kWideSlots8 = 512;
-int64_t wide_splits(int64_t KU, int W) { return (KU + (int64_t)W * bl::kWideUnits - 1) / ((int64_t)W * bl::kWideUnits); }
+// With 2..16 tokens (the MFMA stream) a split also holds at most what fits
+// 64 KiB of LDS with the kernel's own 512 bytes: staged activations (80
+// bytes per token per unit and a 16-byte zero chunk); the waves' sums
+// (8 * M * 256 bytes) reuse that space.
+constexpr int64_t kWideMaxTokens = 16;
+int64_t wide_units(int64_t M, int W)
+{
+    const int64_t u = (int64_t)W * bl::kWideUnits;
+    return M == 1 ? u : std::min<int64_t>(u, (65536 - 512 - 16) / (80 * M));
+}
+int64_t wide_splits(int64_t M, int64_t KU, int W) { return (KU + wide_units(M, W) - 1) / wide_units(M, W); }
 int wide_waves(int64_t M, int64_t tiles, int64_t KU)
 {
-    if (M != 1 || !knobs().wide || knobs().lut) return 0;
-    if (tiles * wide_splits(KU, 16) <= kWideSlots16) return 16;
-    if (tiles * wide_splits(KU, 8) <= kWideSlots8) return 8;
+    if (M < 1 || M > kWideMaxTokens || !knobs().wide || (M == 1 && knobs().lut)) return 0;
+    if (tiles * wide_splits(M, KU, 16) <= kWideSlots16) return 16;
+    if (tiles * wide_splits(M, KU, 8) <= kWideSlots8) return 8;
     return 0;
 }
 // Decomposition of a one-token problem for the wide kernel with W waves.
@@ -153,11 +165,11 @@ void decompose_wide(Problem &p, int W)
     p.NT = (int32_t)((p.N + 63) / 64);
     p.mt = p.ntt = p.mtile = p.qtiled = p.stiles = 0;
     p.wide = W;
-    p.ks = (int32_t)wide_splits(p.KU, W);
+    p.ks = (int32_t)wide_splits(p.M, p.KU, W);
     p.upsplit = (p.KU + p.ks - 1) / p.ks;
     p.ks = (p.KU + p.upsplit - 1) / p.upsplit;
 }
-int wide_variant(int W) { return W == 16 ? 12 : 13; }
+int wide_variant(int64_t M, int W) { return M == 1 ? (W == 16 ? 12 : 13) : (W == 16 ? 14 : 15); }
 
 // Most K splits of a tile-kernel problem (measured on the chained 3B step at
 // M = 64: 3.16 ms unsplit, 2.70 at two, 2.74 at four, 3.06 at eight, 3.33 at
@@ -320,6 +332,7 @@ int64_t stream_lds_need(int variant, int64_t M, int64_t upsplit)
 {
     if (variant == 1 || variant == 9) return 0;
     if (variant == 10) return 80 * M * upsplit + 16;
+    if (variant == 14 || variant == 15) return std::max<int64_t>(80 * M * upsplit + 16, 8 * M * 256);
     if (variant == 5) return 1024 * upsplit;
     const int64_t slots = (variant == 6 && M > 1) ? bl::kDot4MaxTokens : 1;
     return 64 * slots * upsplit;
@@ -375,7 +388,7 @@ hipError_t launch_contraction(const Problem &p, bool own_q, hipStream_t s)
 {
     if (p.kind == 2) return bl::launch_bt5_single(p, s);
     if (p.kind == 0) {
-        if (p.wide) return bl::launch_stream_single(p, wide_variant(p.wide), s);
+        if (p.wide) return bl::launch_stream_single(p, wide_variant(p.M, p.wide), s);
         const int v = stream_variant_for(p.M, p.upsplit);
         const int sv = v != 1 ? v : (alds_for(p.M) && alds_fits(p.M, p.K)) ? 10 : p.stiles == 1 ? 9 : 1;
         return bl::launch_stream_single(p, sv, s);
@@ -832,7 +845,7 @@ int multi_plan(const int8_t *Q, int64_t ldq, int64_t M, int64_t K, const bitline
     mp.ps.count = count;
     mp.kind = mp.ps.p[0].kind;
     if (mp.kind == 0 && W) {
-        mp.variant = wide_variant(W);
+        mp.variant = wide_variant(M, W);
         mp.lds = (int)stream_lds_need(mp.variant, M, max_upsplit);
     } else if (mp.kind == 0) {
         mp.variant = stream_variant_for(M, max_upsplit);

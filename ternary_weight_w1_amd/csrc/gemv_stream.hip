@@ -630,6 +630,146 @@ __device__ void stream_mfma(const Problem &p, int local)
     }
 }
 
+// 2..16 tokens over few tiles: the wide kernel's decomposition (W waves per
+// 64-row tile and K range, every wave's units requested before the staging)
+// with the matrix-instruction stream.  The activations of the range are
+// staged row-major as in variant 10 (token m's 64 bytes of unit u at
+// ((u - u0) * M + m) * kTokStride, a zero chunk after the last); each wave
+// accumulates its units into two 32 x 32 tiles (rows 0..31 and 32..63 of
+// the weight tile), and the waves' sums meet in LDS, in the space the
+// staged activations held: eight slots, word (slot * M + m) * 64 + row for
+// token m.
+template <int W>
+__device__ void stream_mfma_wide(const Problem &p, int local)
+{
+    constexpr int kThr = 64 * W;
+    const int tile = local / p.ks, split = local - tile * p.ks;
+    const int u0 = split * p.upsplit;
+    const int u1 = min(p.KU, u0 + p.upsplit);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63, g = lane >> 5, r = lane & 31;
+    const int M = p.M;
+    const BL_GLOBAL v4u *blk = gload_ptr<v4u>(p.P + (int64_t)tile * p.KU * kBlockBytes) + lane;
+    const int nu = u1 - u0 > wave ? (u1 - u0 - wave + W - 1) / W : 0;
+    v4u w[kWideUnits];
+#pragma unroll
+    for (int j = 0; j < kWideUnits; ++j)
+        if (j < nu) w[j] = load_packed(blk + (int64_t)(u0 + wave + W * j) * 64);
+    __shared__ int s_rowsum[kStreamMaxTokens];
+    __shared__ float s_absmax[kStreamMaxTokens];
+    if (threadIdx.x < M) {
+        s_rowsum[threadIdx.x] = gload_ptr<int32_t>(p.rowsum)[threadIdx.x];
+        s_absmax[threadIdx.x] = gload_ptr<float>(p.absmax)[threadIdx.x];
+    }
+    const int n_units = u1 - u0;
+    {
+        const int nch = n_units * M * 4;  // chunk c: unit c / (4 M), token (c / 4) % M, part c % 4
+        const BL_GLOBAL int8_t *q = gload_ptr<int8_t>(p.Q) + 64 * u0;
+        for (int base = threadIdx.x; base < nch; base += 4 * kThr) {
+            v4i v[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int c = base + k * kThr;
+                if (c < nch) {
+                    const int uu = c / (4 * M), rem = c - uu * 4 * M;
+                    v[k] = *reinterpret_cast<const BL_GLOBAL v4i *>(q + (int64_t)(rem >> 2) * p.ldq + 64 * uu +
+                                                                   16 * (rem & 3));
+                }
+            }
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int c = base + k * kThr;
+                if (c < nch) {
+                    const int uu = c / (4 * M), rem = c - uu * 4 * M;
+                    *reinterpret_cast<v4i *>(stream_q_lds + (uu * M + (rem >> 2)) * kTokStride + 16 * (rem & 3)) = v[k];
+                }
+            }
+        }
+        if (threadIdx.x == 0) *reinterpret_cast<v4i *>(stream_q_lds + n_units * M * kTokStride) = (v4i){0, 0, 0, 0};
+    }
+    __syncthreads();
+    // lanes of rows past M read the zero chunk
+    const int a_lane = r < M ? r * kTokStride + 16 * g : n_units * M * kTokStride;
+    const int a_step = r < M ? M * kTokStride : 0, a_half = r < M ? 32 : 0;
+    v16i acc0 = (v16i){}, acc1 = (v16i){};
+#pragma unroll
+    for (int j = 0; j < kWideUnits; ++j)
+        if (j < nu) {
+            const int8_t *a = stream_q_lds + a_lane + (wave + W * j) * a_step;
+            const v4i a0 = *reinterpret_cast<const v4i *>(a);
+            const v4i a1 = *reinterpret_cast<const v4i *>(a + a_half);
+            acc0 = mfma_i8(a0, planes(w[j].x), acc0);
+            acc1 = mfma_i8(a0, planes(w[j].z), acc1);
+            acc0 = mfma_i8(a1, planes(w[j].y), acc0);
+            acc1 = mfma_i8(a1, planes(w[j].w), acc1);
+        }
+    __syncthreads();  // the staged activations are no longer read
+    // element e of lane l is token 8*(e/4) + 4*(l/32) + e%4, row 32*s + l%32;
+    // at most 16 tokens: elements 0..7.  Eight slots of M * 64 sums: waves
+    // 0..7 store theirs, then waves 8..15 (when W = 16) add theirs to slot
+    // wave - 8, each lane to the words it stored itself.
+    int *red = reinterpret_cast<int *>(stream_q_lds);
+    constexpr int kSlots = 8;
+    auto put = [&](bool add) {
+        const int slot = wave % kSlots;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int m = 8 * (e >> 2) + 4 * g + (e & 3);
+            if (m < M) {
+                int *d = red + (slot * M + m) * 64 + r;
+                d[0] = add ? d[0] + acc0[e] : acc0[e];
+                d[32] = add ? d[32] + acc1[e] : acc1[e];
+            }
+        }
+    };
+    if (wave < kSlots) put(false);
+    if constexpr (W > kSlots) {
+        __syncthreads();
+        if (wave >= kSlots) put(true);
+    }
+    __syncthreads();
+    // thread t finishes outputs t + kThr * i: token (t + kThr * i) / 64, row % 64
+    constexpr int kR = (16 * 64 + kThr - 1) / kThr;
+    int mm[kR], nn[kR], tot[kR];
+    bool mine[kR];
+#pragma unroll
+    for (int i = 0; i < kR; ++i) {
+        const int idx = threadIdx.x + kThr * i;
+        mm[i] = idx >> 6;
+        nn[i] = 64 * tile + (idx & 63);
+        mine[i] = mm[i] < M;
+        tot[i] = 0;
+        if (mine[i]) {
+#pragma unroll
+            for (int v = 0; v < kSlots; ++v) tot[i] += red[(v * M + mm[i]) * 64 + (idx & 63)];
+        }
+    }
+    const float gamma = *p.gamma;
+    if (p.ks == 1) {
+#pragma unroll
+        for (int i = 0; i < kR; ++i)
+            if (mine[i] && nn[i] < p.N) finish_output_with(p, gamma, mm[i], nn[i], tot[i], s_rowsum[mm[i]], s_absmax[mm[i]]);
+        return;
+    }
+    const int64_t ldp = (int64_t)p.NT * 64;  // partial row stride
+#pragma unroll
+    for (int i = 0; i < kR; ++i)
+        if (mine[i]) put_partial(p.acc_ws + (((int64_t)split * M + mm[i]) * ldp + nn[i]), tot[i]);
+    if (!arrive_last(p, tile)) return;
+    int64_t off[kR];
+    bool ok[kR];
+#pragma unroll
+    for (int i = 0; i < kR; ++i) {
+        off[i] = (int64_t)mm[i] * ldp + nn[i];
+        ok[i] = mine[i] && nn[i] < p.N;
+    }
+    int32_t sum[kR];
+    sum_partials<kR>(p.acc_ws, off, ok, (int64_t)M * ldp, p.ks, sum);
+#pragma unroll
+    for (int i = 0; i < kR; ++i)
+        if (ok[i]) finish_output_with(p, gamma, mm[i], nn[i], sum[i], s_rowsum[mm[i]], s_absmax[mm[i]]);
+}
+
 // Instantiations: 1: MFMA stream (17..32 tokens; two tiles per wave); 3:
 // dot4 with LDS-staged activations, 8 units in flight per wave (one token);
 // 5: the table-lookup comparison variant (one token); 6: the dot4 token
@@ -637,7 +777,8 @@ __device__ void stream_mfma(const Problem &p, int local)
 // problems take the one-slot loop, whose LDS layout and stream are those
 // of 3); 9: as 1 with one tile per wave; 10: the MFMA stream for 3..16
 // tokens with LDS-staged activations, one tile per wave, loads four units
-// ahead; 12 and 13: the one-token wide kernel with 16 and 8 waves.
+// ahead; 12 and 13: the one-token wide kernel with 16 and 8 waves; 14 and
+// 15: the wide kernel's MFMA stream for 2..16 tokens, 16 and 8 waves.
 template <int V>
 __device__ inline void stream_body(const Problem &p, int local)
 {
@@ -656,6 +797,10 @@ __device__ inline void stream_body(const Problem &p, int local)
         stream_dot4_wide<16>(p, local);
     else if constexpr (V == 13)
         stream_dot4_wide<8>(p, local);
+    else if constexpr (V == 14)
+        stream_mfma_wide<16>(p, local);
+    else if constexpr (V == 15)
+        stream_mfma_wide<8>(p, local);
     else if constexpr (V == 5)
         stream_dot4<8, true>(p, local);
     else
@@ -663,7 +808,10 @@ __device__ inline void stream_body(const Problem &p, int local)
 }
 
 // threads per workgroup of variant V
-__host__ __device__ constexpr int stream_threads(int V) { return V == 12 ? 1024 : V == 13 ? 512 : kThreads; }
+__host__ __device__ constexpr int stream_threads(int V)
+{
+    return (V == 12 || V == 14) ? 1024 : (V == 13 || V == 15) ? 512 : kThreads;
+}
 
 template <int V>
 __global__ __launch_bounds__(stream_threads(V)) void stream_single_kernel(Problem p)
@@ -699,6 +847,8 @@ __global__ __launch_bounds__(stream_threads(V)) void stream_multi_kernel(Problem
     case 6: hipLaunchKernelGGL(KERNEL<6>, grid, block, LDS, s, __VA_ARGS__); break;        \
     case 12: hipLaunchKernelGGL(KERNEL<12>, grid, block, LDS, s, __VA_ARGS__); break;      \
     case 13: hipLaunchKernelGGL(KERNEL<13>, grid, block, LDS, s, __VA_ARGS__); break;      \
+    case 14: hipLaunchKernelGGL(KERNEL<14>, grid, block, LDS, s, __VA_ARGS__); break;      \
+    case 15: hipLaunchKernelGGL(KERNEL<15>, grid, block, LDS, s, __VA_ARGS__); break;      \
     default: hipLaunchKernelGGL(KERNEL<3>, grid, block, LDS, s, __VA_ARGS__); break;       \
     }
 
@@ -715,8 +865,14 @@ hipError_t launch_stream_single(const Problem &p, int variant, hipStream_t s)
     const int64_t tiles = (variant == 1 || variant == 9 || variant == 10) ? (int64_t)p.ntt : (int64_t)p.NT;
     const dim3 grid((unsigned)(tiles * p.ks)), block(stream_threads(variant));
     const unsigned slot = variant == 6 ? 64u * kDot4MaxTokens : 64u;
-    const unsigned lds = variant == 10 ? (unsigned)(kTokStride * p.M * p.upsplit + 16)
-                                       : (variant == 5 ? kLutUnitBytes : slot) * (unsigned)p.upsplit;
+    unsigned lds = variant == 10 ? (unsigned)(kTokStride * p.M * p.upsplit + 16)
+                                 : (variant == 5 ? kLutUnitBytes : slot) * (unsigned)p.upsplit;
+    if (variant == 14 || variant == 15) {
+        // staged activations, then the waves' sums (eight slots) in the same space
+        const unsigned red = (unsigned)(8 * p.M * 256);
+        lds = (unsigned)(kTokStride * p.M * p.upsplit + 16);
+        lds = lds > red ? lds : red;
+    }
     BL_STREAM_CASES(stream_single_kernel, lds, p)
     return hipGetLastError();
 }

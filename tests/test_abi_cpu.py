@@ -146,6 +146,12 @@ def test_pack_quant_matmul_forward_validation():
     # one token, one row tile: a wide workgroup (16 waves x 12 units) covers
     # K = 8192 without a split and needs no workspace; K = 16384 is split
     assert B.workspace_bytes(B.WS_MATMUL, 1, 64, 8192) == 0
+    # 2..16 tokens: a split holds what 64 KiB of staged activations take
+    # (80 bytes per token per unit): 50 units at 16 tokens, 101 at 8
+    assert B.workspace_bytes(B.WS_MATMUL, 16, 64, 3200) == 0
+    assert B.workspace_bytes(B.WS_MATMUL, 16, 64, 3264) > 0
+    assert B.workspace_bytes(B.WS_MATMUL, 8, 64, 101 * 64) == 0
+    assert B.workspace_bytes(B.WS_MATMUL, 8, 64, 102 * 64) > 0
     need = B.workspace_bytes(B.WS_MATMUL, 1, 64, 16384)
     assert need > 0
     assert _st("bitlinear_matmul", FAKE, 16384, FAKE, FAKE, 1, 16384, FAKE, FAKE, 64, FAKE, None,

@@ -417,12 +417,12 @@ def test_matmul_parity_injected_scales(B, M, N, K):
     check_outputs(host(Y), host(acc), ref, g, a, f"M={M} N={N} K={K}")
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 64, 16384), (5, 64, 8192), (1, 200, 40000), (3, 130, 131072),
-                                   (1, 64, 131072)])
+@pytest.mark.parametrize("M,N,K", [(1, 64, 16384), (5, 64, 16384), (1, 200, 40000), (3, 130, 131072),
+                                   (1, 64, 131072), (16, 100, 8192)])
 def test_matmul_split_k(B, M, N, K):
     # few row tiles and a long K: the streaming kernel splits K over
-    # workgroups and the last one to arrive adds the partial sums (one
-    # token: K beyond the 192 units one wide workgroup covers)
+    # workgroups and the last one to arrive adds the partial sums (up to 16
+    # tokens: K beyond the units one wide workgroup covers)
     say("matmul split-K", M, N, K)
     assert B.workspace_bytes(B.WS_MATMUL, M, N, K) > 0
     T = synth.random_ternary(N, K, seed=K)
@@ -472,6 +472,23 @@ def test_forward_wide_one_token(B, N, K):
     for _ in range(2):
         Y, acc = B.forward(Xd, Pd, gamma_dev(0.021), N, with_acc=True)
         check_outputs(host(Y), host(acc), ref["acc"], 0.021, ref["absmax"], "forward wide")
+
+
+@pytest.mark.parametrize("M,N,K", [(2, 130, 3200), (5, 100, 12289), (8, 64, 8640), (8, 8640, 3200),
+                                   (16, 100, 3200), (16, 17000, 3000), (12, 300, 777), (3, 1, 1)])
+def test_forward_wide_tokens(B, M, N, K):
+    # 2..16 tokens over few row tiles: the wide kernel's matrix-instruction
+    # stream (activations staged per workgroup, the waves' sums meeting in
+    # LDS); 8640 and 17000 rows take 8 waves (two outputs per thread at 16
+    # tokens); K = 12289 and 8640 at 8 tokens split K
+    say("forward wide", M, N, K)
+    T = synth.random_ternary(N, K, seed=M + N + 3 * K)
+    X = synth.activations_np(M, K, seed=M * 7 + K, outlier_frac=0.01)
+    ref = O.forward(X, T, np.float32(0.017))
+    Xd, Pd = dev(X), dev(O.pack(T))
+    for _ in range(2):
+        Y, acc = B.forward(Xd, Pd, gamma_dev(0.017), N, with_acc=True)
+        check_outputs(host(Y), host(acc), ref["acc"], 0.017, ref["absmax"], "forward wide tokens")
 
 
 def test_calls_on_a_side_stream(B):
@@ -681,6 +698,8 @@ def test_lut_variant_subprocess(B):
                                          (48, 2560, (640, 1000), 0),
                                          (100, 256, (256, 512), 0), (1, 8192, (64,), 0),
                                          (1, 16384, (64, 100), 0), (1, 3200, (8640, 8640), 0),
+                                         (8, 3200, (8640, 8640), 0), (16, 3200, (3200, 3200, 3200), 0),
+                                         (8, 8640, (3200,), 0),
                                          (1, 2560, (640, 2560, 100), 1), (9, 1000, (320, 64), 1),
                                          (20, 8192, (64, 96), 1)])
 def test_matmul_multi_parity(B, M, K, Ns, fmt):
