@@ -225,18 +225,23 @@ def stack_inputs(torch, dim, n_layers, M, dev):
 
 class ChainedStack:
     """The stack chained as pre-norm blocks for M tokens, each stage a
-    library call on one stream: residual add + RMSNorm + int8 cast, q|k|v in
-    one launch (one input), the attention of the first decode position (a
-    single key, so its output is v), the cast of v, o, residual add + RMSNorm
-    + cast, gate|up in one launch, the gated squared-ReLU cast, down; then
-    the final residual add + norm + cast: 8 launches per layer.  Buffers and
-    workspaces are allocated once (workspaces zero-filled once, as the
-    multi-matrix call requires).  After step(), x holds the final residual
-    stream and (Q, a, rs) its final norm's int8 cast."""
+    library call on one stream: residual add + RMSNorm + int8 cast and q|k|v
+    (one input, one call), the attention of the first decode position (a
+    single key, so its output is v), the cast of v and o, residual add +
+    RMSNorm + cast and gate|up, the gated squared-ReLU cast and down; then
+    the final residual add + norm + cast.  Each cast + contraction pair is
+    one bitlinear_cast_matmul_multi call: a single launch at one token (the
+    contraction's workgroups cast their own input), two otherwise.  The
+    residual stream alternates between two buffers (a call's X_out may not
+    be its X).  Buffers and workspaces are allocated once (workspaces
+    zero-filled once, as the multi-matrix calls require).  After step(), x
+    holds the final residual stream and (Q, a, rs) its final norm's int8
+    cast."""
 
     def __init__(self, B, torch, mats, dev, M, x0, gains, g_fin):
         import ctypes
         self.L = L = B.lib()
+        self.B = B
         self.layers = layers = {}
         for m in mats:
             layers.setdefault(m["layer"], {})[m["name"]] = m
@@ -245,14 +250,14 @@ class ChainedStack:
         self.ffn = ffn = layers[0]["gate"]["N"]
         self.x0, self.gains, self.g_fin = x0, gains, g_fin
         f32 = lambda n: torch.empty((M, n), dtype=torch.float32, device=dev)
-        self.x, self.q, self.k, self.v, self.o = f32(dim), f32(dim), f32(dim), f32(dim), f32(dim)
+        self.x, self.xb = f32(dim), f32(dim)
+        self.q, self.k, self.v, self.o = f32(dim), f32(dim), f32(dim), f32(dim)
         self.gate, self.up, self.d = f32(ffn), f32(ffn), f32(dim)
-        self.ldd, self.ldf = B.q_stride(dim), B.q_stride(ffn)
+        self.ldd = B.q_stride(dim)
         self.Q = torch.empty((M, self.ldd), dtype=torch.int8, device=dev)
-        self.Qf = torch.empty((M, self.ldf), dtype=torch.int8, device=dev)
         self.a = torch.empty(M, dtype=torch.float32, device=dev)
         self.rs = torch.empty(M, dtype=torch.int32, device=dev)
-        self.P = lambda t: ctypes.c_void_p(t.data_ptr())
+        self.P = lambda t: ctypes.c_void_p(t.data_ptr()) if t is not None else None
 
         def warr(lay, names, outs):
             arr = (B.Weight * len(names))()
@@ -265,10 +270,13 @@ class ChainedStack:
                               gu=warr(lay, ("gate", "up"), (self.gate, self.up)),
                               down=warr(lay, ("down",), (self.d,)))
                       for i, lay in layers.items()}
+        # the largest workspace over the modes a site is called in (q|k|v: the
+        # norm at layer 0, the residual add + norm after)
         self.wss = {}
-        for key, K in (("qkv", dim), ("o", dim), ("gu", dim), ("down", ffn)):
+        for key, K, modes in (("qkv", dim, (B.CAST_RMSNORM, B.CAST_ADD_RMSNORM)), ("o", dim, (B.CAST_PLAIN,)),
+                              ("gu", dim, (B.CAST_ADD_RMSNORM,)), ("down", ffn, (B.CAST_RELU2_GATE,))):
             arr = self.sites[0][key]
-            wsb = L.bitlinear_multi_workspace_bytes(arr, len(arr), M, K)
+            wsb = max(L.bitlinear_cast_multi_workspace_bytes(md, arr, len(arr), M, K) for md in modes)
             self.wss[key] = torch.zeros(max(wsb, 16), dtype=torch.uint8, device=dev)
 
     def _check(self, st):
@@ -277,33 +285,25 @@ class ChainedStack:
 
     def step(self, s):
         """Enqueue one pass over every layer on the raw stream handle s."""
-        L, P, M, dim, ffn, ldd, ldf = self.L, self.P, self.M, self.dim, self.ffn, self.ldd, self.ldf
-        x, a, rs, Q = self.x, self.a, self.rs, self.Q
+        L, P, B, M, dim, ffn = self.L, self.P, self.B, self.M, self.dim, self.ffn
+        xa, xb = self.x, self.xb
 
-        def multi(Qin, ld, K, key, site):
+        def call(key, site, mode, X, K, aux=None, R=None, X_out=None):
             arr = site[key]
-            self._check(L.bitlinear_matmul_multi(P(Qin), ld, P(a), P(rs), M, K, arr, len(arr), P(self.wss[key]),
-                                                 self.wss[key].numel(), s))
+            self._check(L.bitlinear_cast_matmul_multi(mode, P(X), P(aux), P(R), 1e-5, P(X_out), M, K, arr,
+                                                      len(arr), P(self.wss[key]), self.wss[key].numel(), s))
         for i in sorted(self.layers):
             ga, gf = self.gains[i]
             site = self.sites[i]
             if i == 0:
-                self._check(L.bitlinear_quant_act_rmsnorm(P(self.x0), M, dim, P(ga), 1e-5, P(Q), ldd, P(a),
-                                                          P(rs), s))
+                call("qkv", site, B.CAST_RMSNORM, self.x0, dim, aux=ga)
             else:
-                self._check(L.bitlinear_quant_act_add_rmsnorm(P(x), P(self.d), M, dim, P(ga), 1e-5, P(x), P(Q),
-                                                              ldd, P(a), P(rs), s))
-            multi(Q, ldd, dim, "qkv", site)
-            self._check(L.bitlinear_quant_act(P(self.v), M, dim, P(Q), ldd, P(a), P(rs), s))
-            multi(Q, ldd, dim, "o", site)
-            self._check(L.bitlinear_quant_act_add_rmsnorm(P(self.x0 if i == 0 else x), P(self.o), M, dim, P(gf),
-                                                          1e-5, P(x), P(Q), ldd, P(a), P(rs), s))
-            multi(Q, ldd, dim, "gu", site)
-            self._check(L.bitlinear_quant_act_relu2_gate(P(self.gate), P(self.up), M, ffn, P(self.Qf), ldf, P(a),
-                                                         P(rs), s))
-            multi(self.Qf, ldf, ffn, "down", site)
-        self._check(L.bitlinear_quant_act_add_rmsnorm(P(x), P(self.d), M, dim, P(self.g_fin), 1e-5, P(x), P(Q),
-                                                      ldd, P(a), P(rs), s))
+                call("qkv", site, B.CAST_ADD_RMSNORM, xa, dim, aux=ga, R=self.d, X_out=xb)
+            call("o", site, B.CAST_PLAIN, self.v, dim)
+            call("gu", site, B.CAST_ADD_RMSNORM, self.x0 if i == 0 else xb, dim, aux=gf, R=self.o, X_out=xa)
+            call("down", site, B.CAST_RELU2_GATE, self.gate, ffn, aux=self.up)
+        self._check(L.bitlinear_quant_act_add_rmsnorm(P(xa), P(self.d), M, dim, P(self.g_fin), 1e-5, P(xa),
+                                                      P(self.Q), self.ldd, P(self.a), P(self.rs), s))
 
 
 def stack_curve(B, torch, mats, dev, Ms, steps, warmup):
@@ -314,7 +314,8 @@ def stack_curve(B, torch, mats, dev, Ms, steps, warmup):
     n_layers = len({m["layer"] for m in mats})
     dim = next(m["K"] for m in mats if m["name"] == "q")
     ffn = next(m["N"] for m in mats if m["name"] == "gate")
-    out = {"layers": n_layers, "dim": dim, "ffn": ffn, "launches_per_step": 8 * n_layers + 1, "points": []}
+    out = {"layers": n_layers, "dim": dim, "ffn": ffn,
+           "launches_per_step": {"M=1": 4 * n_layers + 1, "M>1": 8 * n_layers + 1}, "points": []}
     for M in Ms:
         chain = ChainedStack(B, torch, mats, dev, M, *stack_inputs(torch, dim, n_layers, M, dev))
         side = torch.cuda.Stream()

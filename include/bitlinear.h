@@ -363,6 +363,59 @@ int bitlinear_matmul_multi(const int8_t *Q, int64_t ldq, const float *absmax, co
                            int64_t M, int64_t K, const bitlinear_weight *w, int count, void *ws,
                            size_t ws_bytes, void *stream);
 
+/* What bitlinear_cast_matmul_multi casts to int8 (the activation casts
+ * above: quant_act, quant_act_rmsnorm, quant_act_relu2_gate,
+ * quant_act_add_rmsnorm). */
+enum bitlinear_cast_mode {
+    BITLINEAR_CAST_PLAIN = 0,      /* X                                      */
+    BITLINEAR_CAST_RMSNORM = 1,    /* RMSNorm(X) with gains aux (NULL: ones) */
+    BITLINEAR_CAST_RELU2_GATE = 2, /* relu(X)^2 * aux (X gate, aux up)       */
+    BITLINEAR_CAST_ADD_RMSNORM = 3 /* RMSNorm(X + R), X + R to X_out         */
+};
+
+/* Workspace bytes of bitlinear_cast_matmul_multi in `mode` (only N, format
+ * and reserved of w are read; SIZE_MAX on invalid input). */
+size_t bitlinear_cast_multi_workspace_bytes(int mode, const bitlinear_weight *w, int count, int64_t M, int64_t K);
+
+/*
+ * The activation cast of `mode` followed by bitlinear_matmul_multi on its
+ * int8 codes: a decode layer's sub-layer norm (or gated squared ReLU) and
+ * the BitLinear matrices that read it, as the pages describe a BitNet block
+ * (BitNet b1.58 2B4T video transcript, yousumm.com, "Transcription": a
+ * norm before each BitLinear, squared ReLU in the feed-forward part; the
+ * int8 cast: anthology note-168 on arXiv 2402.17764, "What it does").
+ * Every Y (and acc) equals that of the cast call followed by
+ * bitlinear_matmul_multi, bit for bit, and X_out that of the add mode's
+ * cast -- except that with 8 waves per workgroup (launches of 257..512 row
+ * tiles) the norm modes add the fp64 squares in another order, which moves
+ * the fp32 norm factor only where the exact value lies within that rounding
+ * of an fp32 rounding boundary.
+ * One token whose weights take the wide one-token kernel (BL2-T64, few row
+ * tiles, K <= 65536) in at most one workgroup per compute unit, each
+ * reading fewer cast-input bytes than packed weights, is cast inside every
+ * workgroup of the contraction launch, so the call is one launch; otherwise
+ * the cast runs as its own kernel into the workspace.
+ *   mode   a bitlinear_cast_mode.
+ *   X      M x K fp32 rows (device; the gate projection's output for
+ *          BITLINEAR_CAST_RELU2_GATE), 16-byte aligned.
+ *   aux    RMSNorm gains [K] (nullable, 4-byte aligned) for the norm modes;
+ *          the up projection's output (M x K, 16-byte aligned, required)
+ *          for the gate; ignored for BITLINEAR_CAST_PLAIN.
+ *   R      the addend of the residual sum (M x K, add mode only).
+ *   eps    RMSNorm epsilon (finite, >= 0; norm modes only).
+ *   X_out  receives X + R (add mode only); must not overlap X or R, which
+ *          every workgroup reads while one writes X_out.
+ *   M, K, w, count  as bitlinear_matmul_multi (K is the cast rows' length).
+ *   ws     bitlinear_cast_multi_workspace_bytes(mode, w, count, M, K) bytes,
+ *          ZERO-FILLED once before first use as for bitlinear_matmul_multi
+ *          (the same reuse rules; calls sharing it must not overlap).
+ * Errors: NULL (missing X, aux, R or X_out), SHAPE, ALIGN, ARG (mode, eps,
+ * overlap, weights), WORKSPACE; nothing is enqueued on an error.
+ */
+int bitlinear_cast_matmul_multi(int mode, const float *X, const float *aux, const float *R, float eps,
+                                float *X_out, int64_t M, int64_t K, const bitlinear_weight *w, int count,
+                                void *ws, size_t ws_bytes, void *stream);
+
 /* ---------------------------------------------------------------------- */
 /* Grouped forward: many independent BitLinear layers in one launch per    */
 /* stage (e.g. every weight matrix of a model, or q|k|v sharing an input). */

@@ -30,6 +30,10 @@ WS_MATMUL5 = 4
 WS_FORWARD5 = 5
 FORMAT_BL2 = 0
 FORMAT_BT5 = 1
+CAST_PLAIN = 0
+CAST_RMSNORM = 1
+CAST_RELU2_GATE = 2
+CAST_ADD_RMSNORM = 3
 
 _vp = ctypes.c_void_p
 _i64 = ctypes.c_int64
@@ -92,6 +96,9 @@ def lib():
             "bitlinear_multi_workspace_bytes": (_sz, [ctypes.POINTER(Weight), _int, _i64, _i64]),
             "bitlinear_matmul_multi": (_int, [_vp, _i64, _vp, _vp, _i64, _i64, ctypes.POINTER(Weight), _int,
                                               _vp, _sz, _vp]),
+            "bitlinear_cast_multi_workspace_bytes": (_sz, [_int, ctypes.POINTER(Weight), _int, _i64, _i64]),
+            "bitlinear_cast_matmul_multi": (_int, [_int, _vp, _vp, _vp, ctypes.c_float, _vp, _i64, _i64,
+                                                   ctypes.POINTER(Weight), _int, _vp, _sz, _vp]),
             "bitlinear_group_table_bytes": (_sz, [ctypes.POINTER(Problem), _int]),
             "bitlinear_group_workspace_bytes": (_sz, [ctypes.POINTER(Problem), _int]),
             "bitlinear_group_plan": (_int, [ctypes.POINTER(Problem), _int, _vp, _sz, _vp, _sz]),
@@ -477,6 +484,38 @@ class MultiMatmul:
         _check(lib().bitlinear_matmul_multi(_ptr(Q), ldq, _ptr(absmax), _ptr(rowsum), M, self.K, self.arr,
                                             self.count, _ptr(self.ws), self.ws.numel(), _stream(stream)),
                "matmul_multi")
+        return outs
+
+
+class CastMultiMatmul(MultiMatmul):
+    """An activation cast (mode CAST_PLAIN, CAST_RMSNORM, CAST_RELU2_GATE or
+    CAST_ADD_RMSNORM) and the weight matrices that read its int8 codes, in
+    one call (bitlinear_cast_matmul_multi); weights as MultiMatmul.  The
+    object owns a zero-filled workspace for its mode and sizes."""
+
+    def __init__(self, mode, weights, M: int, K: int, device=None):
+        super().__init__(weights, M, K, device)
+        self.mode = int(mode)
+        wsb = lib().bitlinear_cast_multi_workspace_bytes(self.mode, self.arr, self.count, M, K)
+        if wsb == ctypes.c_size_t(-1).value:
+            _check(-2, "cast_multi_workspace_bytes")
+        self.ws = torch.zeros(max(wsb, 16), dtype=torch.uint8, device=self.ws.device)
+
+    @_on_stream
+    def __call__(self, X, aux=None, R=None, eps=0.0, X_out=None, outs=None, accs=None, stream=None):
+        """Y_i (M x N_i fp32) for every weight of the cast of X (aux: norm
+        gains or the up projection's output; R, X_out: the residual sum)."""
+        _dev_tensor(X, torch.float32, "X")
+        if tuple(X.shape) != (self.M, self.K):
+            raise ValueError("X must be M x K")
+        outs = outs or [torch.empty((self.M, N), dtype=torch.float32, device=X.device) for N in self.Ns]
+        for i in range(self.count):
+            self.arr[i].Y = outs[i].data_ptr()
+            self.arr[i].acc = None if accs is None else accs[i].data_ptr()
+        _check(lib().bitlinear_cast_matmul_multi(self.mode, _ptr(X), _ptr(aux), _ptr(R), float(eps), _ptr(X_out),
+                                                 self.M, self.K, self.arr, self.count, _ptr(self.ws),
+                                                 self.ws.numel(), _stream(stream)),
+               "cast_matmul_multi")
         return outs
 
 

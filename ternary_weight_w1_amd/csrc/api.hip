@@ -68,7 +68,8 @@ struct Knobs {
     int split_target = 1024;     // aim for at least this many workgroups
     int xcd_order = 3;           // bit 0: streaming kernel, bit 1: tile kernel
     int mfma_tiles = 0;          // tiles per wave of the streaming MFMA kernel above 16 tokens: 0 = by launch size, 1, 2
-    int wide = 1;                // one-token launches over few tiles take the wide kernel
+    int wide = 1;                // launches of 1..16 tokens over few tiles take the wide kernels
+    int cast_fuse = 1;           // one-token cast + contraction calls cast inside the contraction
 };
 const Knobs &knobs()
 {
@@ -79,6 +80,7 @@ const Knobs &knobs()
         if (const char *s = getenv("BITLINEAR_XCD_ORDER")) v.xcd_order = atoi(s) & 3;
         if (const char *s = getenv("BITLINEAR_MFMA_TILES")) v.mfma_tiles = (atoi(s) == 1 || atoi(s) == 2) ? atoi(s) : 0;
         if (const char *s = getenv("BITLINEAR_WIDE")) v.wide = atoi(s) != 0;
+        if (const char *s = getenv("BITLINEAR_CAST_FUSE")) v.cast_fuse = atoi(s) != 0;
         return v;
     }();
     return k;
@@ -132,44 +134,52 @@ int mfma_tiles_for(int64_t groups)
     return groups < knobs().split_target ? 1 : bl::kStreamMfmaTiles;
 }
 
-// Launches of 1..16 tokens with at most one workgroup per compute unit (256
-// of 16 waves, or 512 of 8) take the wide kernels: a workgroup's W waves
-// share one 64-row tile and K range, so the launch is one memory round trip
-// per workgroup and, where one split covers K, needs no hand-off through
-// memory.  wide_waves returns W for a launch of `tiles` row tiles with KU
-// units each, or 0.
-constexpr int64_t kWideSlots16 = 256, kWideSlots8 = 512;
+// Launches of 1..16 tokens of at most two workgroups per compute unit take
+// the wide kernels: a workgroup's kWideWaves waves share one 64-row tile and
+// K range, so the launch is one memory round trip per workgroup and, where
+// one split covers K, needs no hand-off through memory.  Eight waves beat
+// sixteen on every decode-layer shape measured (one token: q|k|v 3.95 vs
+// 4.21 us, o 3.79 vs 4.02, gate|up 5.66 vs 5.78; eight tokens: q|k|v 4.92
+// vs 5.41, o 4.74 vs 5.16).
+constexpr int64_t kWideSlots = 512;
 // With 2..16 tokens (the MFMA stream) a split also holds at most what fits
 // 64 KiB of LDS with the kernel's own 512 bytes: staged activations (80
 // bytes per token per unit and a 16-byte zero chunk); the waves' sums
 // (8 * M * 256 bytes) reuse that space.
 constexpr int64_t kWideMaxTokens = 16;
-int64_t wide_units(int64_t M, int W)
+int64_t wide_units(int64_t M)
 {
-    const int64_t u = (int64_t)W * bl::kWideUnits;
+    const int64_t u = (int64_t)bl::kWideWaves * bl::kWideUnits;
     return M == 1 ? u : std::min<int64_t>(u, (65536 - 512 - 16) / (80 * M));
 }
-int64_t wide_splits(int64_t M, int64_t KU, int W) { return (KU + wide_units(M, W) - 1) / wide_units(M, W); }
-int wide_waves(int64_t M, int64_t tiles, int64_t KU)
+// A K range longer than a workgroup holds is split into parts of about
+// kWideSplitUnits units: a split costs a hand-off through memory (about
+// 2 us), so it pays only where it takes the per-workgroup stream well below
+// that (3200 x 8640 at one token: 7.5 us unsplit with 16 waves, 6.5 in three
+// parts, 5.8 in five; at eight tokens 8.1 in two parts, 7.4 in three).
+constexpr int64_t kWideSplitUnits = 28;
+int64_t wide_splits(int64_t M, int64_t KU)
 {
-    if (M < 1 || M > kWideMaxTokens || !knobs().wide || (M == 1 && knobs().lut)) return 0;
-    if (tiles * wide_splits(M, KU, 16) <= kWideSlots16) return 16;
-    if (tiles * wide_splits(M, KU, 8) <= kWideSlots8) return 8;
-    return 0;
+    return KU <= wide_units(M) ? 1 : (KU + kWideSplitUnits - 1) / kWideSplitUnits;
 }
-// Decomposition of a one-token problem for the wide kernel with W waves.
-void decompose_wide(Problem &p, int W)
+bool wide_for(int64_t M, int64_t tiles, int64_t KU)
+{
+    if (M < 1 || M > kWideMaxTokens || !knobs().wide || (M == 1 && knobs().lut)) return false;
+    return tiles * wide_splits(M, KU) <= kWideSlots;
+}
+// Decomposition of a problem for the wide kernels.
+void decompose_wide(Problem &p)
 {
     p.kind = 0;
     p.KU = (int32_t)((p.K + 63) / 64);
     p.NT = (int32_t)((p.N + 63) / 64);
     p.mt = p.ntt = p.mtile = p.qtiled = p.stiles = 0;
-    p.wide = W;
-    p.ks = (int32_t)wide_splits(p.M, p.KU, W);
+    p.wide = 1;
+    p.ks = (int32_t)wide_splits(p.M, p.KU);
     p.upsplit = (p.KU + p.ks - 1) / p.ks;
     p.ks = (p.KU + p.upsplit - 1) / p.upsplit;
 }
-int wide_variant(int64_t M, int W) { return M == 1 ? (W == 16 ? 12 : 13) : (W == 16 ? 14 : 15); }
+int wide_variant(int64_t M) { return M == 1 ? 12 : 13; }
 
 // Most K splits of a tile-kernel problem (measured on the chained 3B step at
 // M = 64: 3.16 ms unsplit, 2.70 at two, 2.74 at four, 3.06 at eight, 3.33 at
@@ -305,8 +315,8 @@ int64_t own_ldq(const Problem &p) { return p.fmt ? 160 * (int64_t)p.KU5 : 64 * (
 void decompose_single(Problem &p, bool own_q)
 {
     const int64_t nt = (p.N + 63) / 64;
-    if (const int W = wide_waves(p.M, nt, (p.K + 63) / 64)) {
-        decompose_wide(p, W);
+    if (wide_for(p.M, nt, (p.K + 63) / 64)) {
+        decompose_wide(p);
         return;
     }
     const bool g4 = mfma32_stream(p.M);
@@ -332,7 +342,7 @@ int64_t stream_lds_need(int variant, int64_t M, int64_t upsplit)
 {
     if (variant == 1 || variant == 9) return 0;
     if (variant == 10) return 80 * M * upsplit + 16;
-    if (variant == 14 || variant == 15) return std::max<int64_t>(80 * M * upsplit + 16, 8 * M * 256);
+    if (variant == 13) return std::max<int64_t>(80 * M * upsplit + 16, 8 * M * 256);
     if (variant == 5) return 1024 * upsplit;
     const int64_t slots = (variant == 6 && M > 1) ? bl::kDot4MaxTokens : 1;
     return 64 * slots * upsplit;
@@ -388,7 +398,7 @@ hipError_t launch_contraction(const Problem &p, bool own_q, hipStream_t s)
 {
     if (p.kind == 2) return bl::launch_bt5_single(p, s);
     if (p.kind == 0) {
-        if (p.wide) return bl::launch_stream_single(p, wide_variant(p.M, p.wide), s);
+        if (p.wide) return bl::launch_stream_single(p, wide_variant(p.M), s);
         const int v = stream_variant_for(p.M, p.upsplit);
         const int sv = v != 1 ? v : (alds_for(p.M) && alds_fits(p.M, p.K)) ? 10 : p.stiles == 1 ? 9 : 1;
         return bl::launch_stream_single(p, sv, s);
@@ -817,7 +827,7 @@ int multi_plan(const int8_t *Q, int64_t ldq, int64_t M, int64_t K, const bitline
     }
     int64_t all_tiles = 0;
     for (int i = 0; i < count; ++i) all_tiles += (w[i].N + 63) / 64;
-    const int W = fmt ? 0 : wide_waves(M, all_tiles, (K + 63) / 64);
+    const bool W = !fmt && wide_for(M, all_tiles, (K + 63) / 64);
     int64_t items = 0, tick = 0, part = 0;
     for (int i = 0; i < count; ++i) {
         Problem &p = mp.ps.p[i];
@@ -825,7 +835,7 @@ int multi_plan(const int8_t *Q, int64_t ldq, int64_t M, int64_t K, const bitline
         if (fmt)
             decompose5(p, base);
         else if (W)
-            decompose_wide(p, W);
+            decompose_wide(p);
         else
             decompose(p, base, false, g4, tpw, tile_base, g4 && alds_for(M) && alds_fits(M, K));
         mp.ps.begin[i] = (int32_t)items;
@@ -845,7 +855,7 @@ int multi_plan(const int8_t *Q, int64_t ldq, int64_t M, int64_t K, const bitline
     mp.ps.count = count;
     mp.kind = mp.ps.p[0].kind;
     if (mp.kind == 0 && W) {
-        mp.variant = wide_variant(M, W);
+        mp.variant = wide_variant(M);
         mp.lds = (int)stream_lds_need(mp.variant, M, max_upsplit);
     } else if (mp.kind == 0) {
         mp.variant = stream_variant_for(M, max_upsplit);
@@ -905,6 +915,141 @@ int bitlinear_matmul_multi(const int8_t *Q, int64_t ldq, const float *absmax, co
     else
         e = bl::launch_bt5_multi(mp.ps, (int)(M < bl::kBt5Tokens ? M : bl::kBt5Tokens), s);
     if (e) return hip_fail(e, "matmul_multi");
+    return BITLINEAR_OK;
+}
+
+}  // extern "C"
+
+// --------------------------------------------------------------------------
+// Cast + multi-matrix contraction.
+// --------------------------------------------------------------------------
+namespace {
+
+// One token whose launch takes the wide kernel (BL2-T64 weights) casts its
+// row inside every workgroup: the whole row's codes sit in LDS (64 KiB
+// cap).  Otherwise the cast runs as its own kernel into the workspace,
+// which then holds [multi-matrix workspace][Q][absmax][rowsum].
+constexpr int64_t kCastMaxK = 65536, kCastMaxItems = 256;
+struct CastPlan {
+    MultiPlan mp;
+    bool fused = false;
+    int64_t ldq = 0, q_off = 0, a_off = 0, rs_off = 0, total = 0;
+};
+int cast_plan(int mode, int64_t M, int64_t K, const bitlinear_weight *w, int count, CastPlan &cp, bool check_ptrs)
+{
+    const bool bt5 = w && count >= 1 && w[0].format == BITLINEAR_FORMAT_BT5;
+    cp.ldq = bt5 ? up(K, bl::kBt5UnitCodes) : up(K, 64);
+    if (int st = multi_plan(nullptr, cp.ldq, M, K, w, count, cp.mp, check_ptrs)) return st;
+    // casting in every workgroup pays where each workgroup reads fewer cast
+    // input bytes than packed weights and the launch has at most one
+    // workgroup per compute unit (measured per decode-layer call: q|k|v after
+    // the residual add + norm 7.9 us against 4.7 + 4.2 in two launches, o
+    // 5.4 against 3.1 + 3.8; gate|up, 270 workgroups, 11.1 against
+    // 4.7 + 5.7; down after the gated squared ReLU, 69 KiB of input per
+    // workgroup, 9.9 against 3.8 + 5.8)
+    int64_t items = 0, upsplit = 0;
+    for (int i = 0; i < count; ++i) {
+        items += items_of(cp.mp.ps.p[i]);
+        upsplit = std::max<int64_t>(upsplit, cp.mp.ps.p[i].upsplit);
+    }
+    const int64_t arrays = (mode == BITLINEAR_CAST_ADD_RMSNORM) ? 3 : (mode == BITLINEAR_CAST_PLAIN) ? 1 : 2;
+    cp.fused = knobs().cast_fuse && !bt5 && M == 1 && cp.mp.kind == 0 && cp.mp.variant == 12 && K <= kCastMaxK &&
+               items <= kCastMaxItems && arrays * 4 * K <= 1024 * upsplit;
+    if (cp.fused) {
+        cp.total = cp.mp.total_bytes;
+        return BITLINEAR_OK;
+    }
+    cp.q_off = up(cp.mp.total_bytes, 256);
+    cp.a_off = cp.q_off + up(M * cp.ldq, 256);
+    cp.rs_off = cp.a_off + up(4 * M, 256);
+    cp.total = cp.rs_off + up(4 * M, 256);
+    return BITLINEAR_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t bitlinear_cast_multi_workspace_bytes(int mode, const bitlinear_weight *w, int count, int64_t M, int64_t K)
+{
+    CastPlan cp;
+    if (mode < BITLINEAR_CAST_PLAIN || mode > BITLINEAR_CAST_ADD_RMSNORM) return SIZE_MAX;
+    if (cast_plan(mode, M, K, w, count, cp, false) != BITLINEAR_OK) return SIZE_MAX;
+    return (size_t)cp.total;
+}
+
+int bitlinear_cast_matmul_multi(int mode, const float *X, const float *aux, const float *R, float eps,
+                                float *X_out, int64_t M, int64_t K, const bitlinear_weight *w, int count,
+                                void *ws, size_t ws_bytes, void *stream)
+{
+    const char *who = "cast_matmul_multi";
+    if (mode < BITLINEAR_CAST_PLAIN || mode > BITLINEAR_CAST_ADD_RMSNORM)
+        return fail(BITLINEAR_ERR_ARG, "%s: unknown cast mode %d", who, mode);
+    const bool norm = mode == BITLINEAR_CAST_RMSNORM || mode == BITLINEAR_CAST_ADD_RMSNORM;
+    const bool add = mode == BITLINEAR_CAST_ADD_RMSNORM, gate = mode == BITLINEAR_CAST_RELU2_GATE;
+    if (!X || (gate && !aux) || (add && (!R || !X_out)))
+        return fail(BITLINEAR_ERR_NULL, "%s: X (and U for the gate, R and X_out for the residual sum) are required", who);
+    if (int st = check_mnk(M, 1, K)) return st;
+    if (norm && (!(eps >= 0.0f) || !(eps <= 3.0e38f))) return fail(BITLINEAR_ERR_ARG, "%s: eps must be finite and >= 0", who);
+    if (!a16(X) || (gate && !a16(aux)) || (norm && aux && !a4(aux)) || (add && (!a16(R) || !a16(X_out))))
+        return fail(BITLINEAR_ERR_ALIGN, "%s: X, U, R and X_out need 16-byte, norm weights 4-byte alignment", who);
+    if (add) {
+        auto overlaps = [](const void *a, int64_t na, const void *b, int64_t nb) {
+            const char *pa = static_cast<const char *>(a), *pb = static_cast<const char *>(b);
+            return pa < pb + nb && pb < pa + na;
+        };
+        const int64_t fb = 4 * M * K;
+        if (overlaps(X_out, fb, X, fb) || overlaps(X_out, fb, R, fb))
+            return fail(BITLINEAR_ERR_ARG, "%s: X_out must not overlap X or R", who);
+    }
+    CastPlan cp;
+    if (int st = cast_plan(mode, M, K, w, count, cp, true)) return st;
+    if (cp.total > 0 && (!ws || ws_bytes < (size_t)cp.total || !a16(ws)))
+        return fail(BITLINEAR_ERR_WORKSPACE, "%s: needs %lld workspace bytes (16-byte aligned)", who, (long long)cp.total);
+    char *base = static_cast<char *>(ws);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    int8_t *Q = cp.fused ? nullptr : reinterpret_cast<int8_t *>(base + cp.q_off);
+    float *absmax = cp.fused ? nullptr : reinterpret_cast<float *>(base + cp.a_off);
+    int32_t *rowsum = cp.fused ? nullptr : reinterpret_cast<int32_t *>(base + cp.rs_off);
+    MultiPlan &mp = cp.mp;
+    for (int i = 0; i < count; ++i) {
+        Problem &p = mp.ps.p[i];
+        p.Q = Q;
+        p.ldq = cp.ldq;
+        p.absmax = absmax;
+        p.rowsum = rowsum;
+        p.P = w[i].P;
+        p.gamma = w[i].gamma;
+        p.Y = w[i].Y;
+        p.acc_out = w[i].acc;
+        if (mp.tick_off[i] >= 0) {
+            p.tickets = reinterpret_cast<uint32_t *>(base + mp.tick_off[i]);
+            p.acc_ws = reinterpret_cast<int32_t *>(base + mp.tick_bytes + mp.part_off[i]);
+        }
+    }
+    hipError_t e;
+    if (cp.fused) {
+        bl::CastIn ci{X, aux, add ? R : nullptr, add ? X_out : nullptr, eps, (int32_t)K};
+        e = bl::launch_stream_cast_multi(mp.ps, ci, mode, s);
+        if (e) return hip_fail(e, who);
+        return BITLINEAR_OK;
+    }
+    switch (mode) {
+    case BITLINEAR_CAST_RMSNORM: e = bl::launch_quant_act_rmsnorm(X, M, K, aux, eps, Q, cp.ldq, absmax, rowsum, s); break;
+    case BITLINEAR_CAST_ADD_RMSNORM:
+        e = bl::launch_quant_act_add_rmsnorm(X, R, M, K, aux, eps, X_out, Q, cp.ldq, absmax, rowsum, s);
+        break;
+    case BITLINEAR_CAST_RELU2_GATE: e = bl::launch_quant_act_relu2_gate(X, aux, M, K, Q, cp.ldq, absmax, rowsum, s); break;
+    default: e = bl::launch_quant_act(X, M, K, Q, cp.ldq, 0, absmax, rowsum, nullptr, 0, s); break;
+    }
+    if (e) return hip_fail(e, who);
+    if (mp.kind == 0)
+        e = bl::launch_stream_multi(mp.ps, mp.variant, mp.lds, s);
+    else if (mp.kind == 1)
+        e = bl::launch_tile_multi(mp.ps, s);
+    else
+        e = bl::launch_bt5_multi(mp.ps, (int)(M < bl::kBt5Tokens ? M : bl::kBt5Tokens), s);
+    if (e) return hip_fail(e, who);
     return BITLINEAR_OK;
 }
 

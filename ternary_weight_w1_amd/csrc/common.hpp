@@ -49,8 +49,9 @@ constexpr int kStreamMaxTokens = 32;
 constexpr int kStreamMfmaTiles = 2;
 // token counts above which that kernel reads fragment-ordered activations
 constexpr int kStreamFragTokens = 16;
-// one-token launches over few tiles take the wide kernel: 8 or 16 waves per
-// 64-row tile, each wave holding up to kWideUnits 64-code units in flight
+// launches of 1..16 tokens over few tiles take the wide kernels: kWideWaves
+// waves per 64-row tile, each holding up to kWideUnits 64-code units in flight
+constexpr int kWideWaves = 8;
 constexpr int kWideUnits = 12;
 // most tokens the packed-dot4 streaming kernels take (64 LDS bytes per token
 // per unit of the workgroup's K range): one, and two in the token loop;
@@ -88,7 +89,7 @@ struct Problem {
     int32_t fmt;           // 0: BL2-T64 weights, 1: BT5-T32 weights
     int32_t KU5;           // ceil(K/160), the BT5-T32 units (0 for BL2-T64)
     int32_t stiles;        // 64-row tiles per wave of the streaming MFMA kernel (1 or 2; else 0)
-    int32_t wide;          // waves per workgroup of the one-token wide kernel (8 or 16; else 0)
+    int32_t wide;          // 1: the wide kernels (kWideWaves waves per tile); else 0
 };
 static_assert(sizeof(Problem) == 160, "Problem layout is shared by host and device");
 
@@ -128,6 +129,18 @@ __device__ inline int multi_index(const ProblemSet &ps, int b)
         if (j < ps.count && b >= ps.begin[j]) i = j;
     return i;
 }
+
+// Input of a one-token contraction launch whose workgroups cast the
+// activations themselves (quant_row.hpp modes): every workgroup casts the
+// whole row into LDS and keeps its absmax and code sum.
+struct CastIn {
+    const float *x;    // the row (the gate projection's output for the gated squared ReLU)
+    const float *aux;  // RMSNorm gains (NULL: ones), or the up projection's output
+    const float *res;  // the addend of the residual sum, or NULL
+    float *xo;         // the residual sum, written by workgroup 0, or NULL
+    float eps;
+    int32_t K;
+};
 
 // Fragment order of the int8 activations ("QF32"), used by the streaming
 // MFMA kernel above 16 tokens so that each wave reads an A operand with one
@@ -199,6 +212,7 @@ hipError_t launch_tile_single(const Problem &p, hipStream_t s);
 hipError_t launch_tile_group(const Problem *probs, const uint2 *item_map, int n_items, hipStream_t s);
 hipError_t launch_bt5_single(const Problem &p, hipStream_t s);
 hipError_t launch_stream_multi(const ProblemSet &ps, int variant, int lds_bytes, hipStream_t s);
+hipError_t launch_stream_cast_multi(const ProblemSet &ps, const CastIn &ci, int mode, hipStream_t s);
 hipError_t launch_tile_multi(const ProblemSet &ps, hipStream_t s);
 hipError_t launch_bt5_multi(const ProblemSet &ps, int max_tokens, hipStream_t s);
 hipError_t launch_bt5_group(const Problem *probs, const uint2 *item_map, int n_items, int max_tokens,

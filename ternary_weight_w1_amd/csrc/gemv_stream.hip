@@ -34,6 +34,7 @@
 // workgroups the last one to arrive (atomic ticket) adds the splits.
 // Integer addition is associative, so every order gives the same bits.
 #include "mm_common.hpp"
+#include "quant_row.hpp"
 
 namespace bl {
 namespace {
@@ -268,15 +269,19 @@ __device__ void stream_dot4(const Problem &p, int local)
 
 // One token over few tiles (the matrices of one decode layer, launched on
 // their own): the launch is too small to be bound by bandwidth, and its time
-// is the chain of memory round trips of one workgroup.  W waves (8 or 16)
-// share one 64-row tile and K range; wave w takes units u0 + w, u0 + w + W,
+// is the chain of memory round trips of one workgroup.  W waves
+// (kWideWaves) share one 64-row tile and K range; wave w takes units u0 + w, u0 + w + W,
 // ... (at most kWideUnits) and requests all of them before the activations
 // are staged, so the weight and activation round trips overlap and nothing
 // waits on memory after the barrier.  The waves' sums meet in LDS; where
 // W * kWideUnits units cover K there is no K split and no hand-off through
 // memory, otherwise splits work as in the other streaming kernels.
-template <int W>
-__device__ void stream_dot4_wide(const Problem &p, int local)
+// CAST >= 0: the workgroup casts the token row itself (quant_row.hpp mode
+// CAST, input ci) into LDS, the whole row (byte k = code k), after its
+// weight loads are requested; the epilogue takes the row's absmax and code
+// sum from that cast.
+template <int W, int CAST = -1>
+__device__ void stream_dot4_wide(const Problem &p, int local, const CastIn *ci = nullptr)
 {
     constexpr int kThr = 64 * W;
     __shared__ int red[W][64];
@@ -292,7 +297,13 @@ __device__ void stream_dot4_wide(const Problem &p, int local)
 #pragma unroll
     for (int j = 0; j < kWideUnits; ++j)
         if (j < nu) w[j] = load_packed(blk + (int64_t)(u0 + wave + W * j) * 64);
-    {
+    RowScale rsc{0.0f, 0};
+    int lds_u0 = u0;  // unit staged at LDS byte 0
+    if constexpr (CAST >= 0) {
+        const LdsDest dst{stream_q_lds, p.KU};
+        rsc = quant_row<W, CAST>(ci->x, ci->K, dst, ci->aux, ci->eps, ci->res, blockIdx.x == 0 ? ci->xo : nullptr);
+        lds_u0 = 0;
+    } else {
         const int n = 4 * (u1 - u0);  // 16-byte chunks of the range
         const BL_GLOBAL v4i *src = gload_ptr<v4i>(p.Q + 64 * u0);
         v4i *dst = reinterpret_cast<v4i *>(stream_q_lds);
@@ -303,7 +314,7 @@ __device__ void stream_dot4_wide(const Problem &p, int local)
 #pragma unroll
     for (int j = 0; j < kWideUnits; ++j)
         if (j < nu) {
-            const int8_t *q = stream_q_lds + 64 * (wave + W * j) + 16 * g;
+            const int8_t *q = stream_q_lds + 64 * (u0 - lds_u0 + wave + W * j) + 16 * g;
             const v4i qa = *reinterpret_cast<const v4i *>(q);
             const v4i qb = *reinterpret_cast<const v4i *>(q + 32);
             acc0 = dot16(w[j].x, qa, acc0);
@@ -323,13 +334,19 @@ __device__ void stream_dot4_wide(const Problem &p, int local)
     const int t = threadIdx.x;
     const int n = 64 * tile + t;
     const float gamma = *p.gamma;
+    auto finish = [&](int32_t fields) {
+        if constexpr (CAST >= 0)
+            finish_output_with(p, gamma, 0, n, fields, rsc.sum, rsc.a);
+        else
+            finish_output(p, gamma, 0, n, fields);
+    };
     int total = 0;
     if (t < 64) {
 #pragma unroll
         for (int i = 0; i < W; ++i) total += red[i][t];
     }
     if (p.ks == 1) {
-        if (t < 64 && n < p.N) finish_output(p, gamma, 0, n, total);
+        if (t < 64 && n < p.N) finish(total);
         return;
     }
     const int64_t ldp = (int64_t)p.NT * 64;  // partial row stride
@@ -339,7 +356,7 @@ __device__ void stream_dot4_wide(const Problem &p, int local)
     const bool ok[1] = {t < 64 && n < p.N};
     int32_t sum[1];
     sum_partials<1>(p.acc_ws, off, ok, (int64_t)p.M * ldp, p.ks, sum);
-    if (ok[0]) finish_output(p, gamma, 0, n, sum[0]);
+    if (ok[0]) finish(sum[0]);
 }
 
 // 1..4 tokens (dot4): the four planes of a packed word are unpacked once
@@ -777,8 +794,8 @@ __device__ void stream_mfma_wide(const Problem &p, int local)
 // problems take the one-slot loop, whose LDS layout and stream are those
 // of 3); 9: as 1 with one tile per wave; 10: the MFMA stream for 3..16
 // tokens with LDS-staged activations, one tile per wave, loads four units
-// ahead; 12 and 13: the one-token wide kernel with 16 and 8 waves; 14 and
-// 15: the wide kernel's MFMA stream for 2..16 tokens, 16 and 8 waves.
+// ahead; 12: the one-token wide kernel; 13: the wide kernel's MFMA stream
+// for 2..16 tokens (kWideWaves waves per workgroup, both).
 template <int V>
 __device__ inline void stream_body(const Problem &p, int local)
 {
@@ -794,13 +811,9 @@ __device__ inline void stream_body(const Problem &p, int local)
     else if constexpr (V == 10)
         stream_mfma<4, 1, true>(p, local);
     else if constexpr (V == 12)
-        stream_dot4_wide<16>(p, local);
+        stream_dot4_wide<kWideWaves>(p, local);
     else if constexpr (V == 13)
-        stream_dot4_wide<8>(p, local);
-    else if constexpr (V == 14)
-        stream_mfma_wide<16>(p, local);
-    else if constexpr (V == 15)
-        stream_mfma_wide<8>(p, local);
+        stream_mfma_wide<kWideWaves>(p, local);
     else if constexpr (V == 5)
         stream_dot4<8, true>(p, local);
     else
@@ -808,10 +821,7 @@ __device__ inline void stream_body(const Problem &p, int local)
 }
 
 // threads per workgroup of variant V
-__host__ __device__ constexpr int stream_threads(int V)
-{
-    return (V == 12 || V == 14) ? 1024 : (V == 13 || V == 15) ? 512 : kThreads;
-}
+__host__ __device__ constexpr int stream_threads(int V) { return (V == 12 || V == 13) ? 64 * kWideWaves : kThreads; }
 
 template <int V>
 __global__ __launch_bounds__(stream_threads(V)) void stream_single_kernel(Problem p)
@@ -835,7 +845,29 @@ __global__ __launch_bounds__(stream_threads(V)) void stream_multi_kernel(Problem
     stream_body<V>(ps.p[i], (int)blockIdx.x - ps.begin[i]);
 }
 
+// One-token launches that cast their own input: W waves, cast mode MODE.
+template <int W, int MODE>
+__global__ __launch_bounds__(64 * W) void stream_cast_multi_kernel(ProblemSet ps, CastIn ci)
+{
+    const int i = multi_index(ps, blockIdx.x);
+    stream_dot4_wide<W, MODE>(ps.p[i], (int)blockIdx.x - ps.begin[i], &ci);
+}
+
 }  // namespace
+
+hipError_t launch_stream_cast_multi(const ProblemSet &ps, const CastIn &ci, int mode, hipStream_t s)
+{
+    const dim3 grid((unsigned)ps.begin[ps.count]), block(64 * kWideWaves);
+    const unsigned lds = 64u * (unsigned)ps.p[0].KU;  // the whole row's codes
+    constexpr int W = kWideWaves;
+    switch (mode) {
+    case kRmsNorm: hipLaunchKernelGGL((stream_cast_multi_kernel<W, kRmsNorm>), grid, block, lds, s, ps, ci); break;
+    case kRelu2Gate: hipLaunchKernelGGL((stream_cast_multi_kernel<W, kRelu2Gate>), grid, block, lds, s, ps, ci); break;
+    case kAddRmsNorm: hipLaunchKernelGGL((stream_cast_multi_kernel<W, kAddRmsNorm>), grid, block, lds, s, ps, ci); break;
+    default: hipLaunchKernelGGL((stream_cast_multi_kernel<W, kPlain>), grid, block, lds, s, ps, ci); break;
+    }
+    return hipGetLastError();
+}
 
 // one case per instantiation; unknown values take 3
 #define BL_STREAM_CASES(KERNEL, LDS, ...)                                                   \
@@ -847,8 +879,6 @@ __global__ __launch_bounds__(stream_threads(V)) void stream_multi_kernel(Problem
     case 6: hipLaunchKernelGGL(KERNEL<6>, grid, block, LDS, s, __VA_ARGS__); break;        \
     case 12: hipLaunchKernelGGL(KERNEL<12>, grid, block, LDS, s, __VA_ARGS__); break;      \
     case 13: hipLaunchKernelGGL(KERNEL<13>, grid, block, LDS, s, __VA_ARGS__); break;      \
-    case 14: hipLaunchKernelGGL(KERNEL<14>, grid, block, LDS, s, __VA_ARGS__); break;      \
-    case 15: hipLaunchKernelGGL(KERNEL<15>, grid, block, LDS, s, __VA_ARGS__); break;      \
     default: hipLaunchKernelGGL(KERNEL<3>, grid, block, LDS, s, __VA_ARGS__); break;       \
     }
 
@@ -867,7 +897,7 @@ hipError_t launch_stream_single(const Problem &p, int variant, hipStream_t s)
     const unsigned slot = variant == 6 ? 64u * kDot4MaxTokens : 64u;
     unsigned lds = variant == 10 ? (unsigned)(kTokStride * p.M * p.upsplit + 16)
                                  : (variant == 5 ? kLutUnitBytes : slot) * (unsigned)p.upsplit;
-    if (variant == 14 || variant == 15) {
+    if (variant == 13) {
         // staged activations, then the waves' sums (eight slots) in the same space
         const unsigned red = (unsigned)(8 * p.M * 256);
         lds = (unsigned)(kTokStride * p.M * p.upsplit + 16);

@@ -37,7 +37,7 @@ def test_every_header_is_checked():
 
 def test_every_declared_symbol_is_exported():
     names = _declared()
-    assert len(names) == 35, names
+    assert len(names) == 37, names
     out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r"\bT (bitlinear_\w+)", out))
@@ -143,15 +143,17 @@ def test_pack_quant_matmul_forward_validation():
     assert _st("bitlinear_forward", FAKE, 1, 64, FAKE, FAKE, 64, FAKE, None, None, 0, None)[0] == -4
     assert _st("bitlinear_forward", FAKE, 1, 64, FAKE, FAKE, 64, FAKE + 4, None, FAKE, 1 << 20,
                None)[0] == -3
-    # one token, one row tile: a wide workgroup (16 waves x 12 units) covers
-    # K = 8192 without a split and needs no workspace; K = 16384 is split
-    assert B.workspace_bytes(B.WS_MATMUL, 1, 64, 8192) == 0
-    # 2..16 tokens: a split holds what 64 KiB of staged activations take
-    # (80 bytes per token per unit): 50 units at 16 tokens, 101 at 8
+    # one token, one row tile: a wide workgroup (8 waves x 12 units) covers
+    # K = 6144 without a split and needs no workspace; longer K is split
+    assert B.workspace_bytes(B.WS_MATMUL, 1, 64, 6144) == 0
+    assert B.workspace_bytes(B.WS_MATMUL, 1, 64, 6145) > 0
+    # 2..16 tokens: a split holds at most what 64 KiB of staged activations
+    # take (80 bytes per token per unit): 50 units at 16 tokens; at 8 tokens
+    # the 96 units eight waves hold
     assert B.workspace_bytes(B.WS_MATMUL, 16, 64, 3200) == 0
     assert B.workspace_bytes(B.WS_MATMUL, 16, 64, 3264) > 0
-    assert B.workspace_bytes(B.WS_MATMUL, 8, 64, 101 * 64) == 0
-    assert B.workspace_bytes(B.WS_MATMUL, 8, 64, 102 * 64) > 0
+    assert B.workspace_bytes(B.WS_MATMUL, 8, 64, 96 * 64) == 0
+    assert B.workspace_bytes(B.WS_MATMUL, 8, 64, 97 * 64) > 0
     need = B.workspace_bytes(B.WS_MATMUL, 1, 64, 16384)
     assert need > 0
     assert _st("bitlinear_matmul", FAKE, 16384, FAKE, FAKE, 1, 16384, FAKE, FAKE, 64, FAKE, None,
@@ -345,8 +347,8 @@ def test_matmul_multi_validation():
     assert L.bitlinear_multi_workspace_bytes(_weights([64] * 5), 5, 1, 64) == smax
     # one long-K small-N matrix splits K beyond what one wide workgroup
     # covers: counters and partials need workspace
-    assert L.bitlinear_multi_workspace_bytes(_weights([64]), 1, 1, 8192) == 0
-    assert L.bitlinear_multi_workspace_bytes(_weights([64]), 1, 1, 16384) > 0
+    assert L.bitlinear_multi_workspace_bytes(_weights([64]), 1, 1, 6144) == 0
+    assert L.bitlinear_multi_workspace_bytes(_weights([64]), 1, 1, 8192) > 0
     mm = L.bitlinear_matmul_multi
     assert mm(None, 2560, FAKE, FAKE, 1, 2560, w, 3, None, 0, None) == -1
     assert mm(FAKE, 2496, FAKE, FAKE, 1, 2560, w, 3, None, 0, None) == -2      # ldq < K
@@ -358,6 +360,45 @@ def test_matmul_multi_validation():
     assert mm(FAKE, 2560, FAKE, FAKE, 1, 2561, bt5, 1, None, 0, None) == -2   # BT5 needs ldq >= 2720 (160-code units)
     need = L.bitlinear_multi_workspace_bytes(_weights([64]), 1, 1, 16384)
     assert mm(FAKE, 16384, FAKE, FAKE, 1, 16384, _weights([64]), 1, FAKE, need - 1, None) == -4
+
+
+def test_cast_matmul_multi_validation():
+    # every rejection happens on the host, before anything is enqueued
+    L = B.lib()
+    smax = ctypes.c_size_t(-1).value
+    w = _weights([3200, 3200, 3200])
+    # one token, 150 row tiles: the contraction casts its own input (no
+    # workspace beyond the multi-matrix one); eight tokens cast into the
+    # workspace first (Q, absmax and row sums on top)
+    assert L.bitlinear_cast_multi_workspace_bytes(3, w, 3, 1, 3200) == L.bitlinear_multi_workspace_bytes(w, 3, 1, 3200)
+    assert (L.bitlinear_cast_multi_workspace_bytes(3, w, 3, 8, 3200)
+            >= L.bitlinear_multi_workspace_bytes(w, 3, 8, 3200) + 8 * 3200 + 64)
+    # gate|up (270 row tiles) and the down projection after the gated
+    # squared ReLU (more input bytes than weight bytes per workgroup) cast in
+    # a launch of their own
+    gu, down = _weights([8640, 8640]), _weights([3200])
+    assert L.bitlinear_cast_multi_workspace_bytes(3, gu, 2, 1, 3200) > L.bitlinear_multi_workspace_bytes(gu, 2, 1, 3200)
+    assert L.bitlinear_cast_multi_workspace_bytes(2, down, 1, 1, 8640) > L.bitlinear_multi_workspace_bytes(down, 1, 1, 8640)
+    assert L.bitlinear_cast_multi_workspace_bytes(0, w, 0, 1, 3200) == smax
+    assert L.bitlinear_cast_multi_workspace_bytes(4, w, 3, 1, 3200) == smax
+    cm = L.bitlinear_cast_matmul_multi
+    X, R, Xo = FAKE, FAKE + (1 << 20), FAKE + (2 << 20)
+    assert cm(4, X, None, None, 0.0, None, 1, 3200, w, 3, None, 0, None) == -6            # mode
+    assert cm(-1, X, None, None, 0.0, None, 1, 3200, w, 3, None, 0, None) == -6
+    assert cm(0, None, None, None, 0.0, None, 1, 3200, w, 3, None, 0, None) == -1         # X
+    assert cm(2, X, None, None, 0.0, None, 1, 3200, w, 3, None, 0, None) == -1            # gate needs U
+    assert cm(3, X, None, None, 1e-5, Xo, 1, 3200, w, 3, None, 0, None) == -1             # add needs R
+    assert cm(3, X, None, R, 1e-5, None, 1, 3200, w, 3, None, 0, None) == -1              # and X_out
+    assert cm(1, X, None, None, -1.0, None, 1, 3200, w, 3, None, 0, None) == -6           # eps
+    assert cm(1, X, None, None, float("nan"), None, 1, 3200, w, 3, None, 0, None) == -6
+    assert cm(0, X + 4, None, None, 0.0, None, 1, 3200, w, 3, None, 0, None) == -3        # alignment
+    assert cm(2, X, X + 8, None, 0.0, None, 1, 3200, w, 3, None, 0, None) == -3
+    assert cm(3, X, None, R, 1e-5, X, 1, 3200, w, 3, None, 0, None) == -6                 # X_out = X
+    assert cm(3, X, None, R, 1e-5, R + 16, 1, 3200, w, 3, None, 0, None) == -6            # overlaps R
+    assert cm(0, X, None, None, 0.0, None, 0, 3200, w, 3, None, 0, None) == -2            # M
+    assert cm(0, X, None, None, 0.0, None, 1, 3200, w, 5, None, 0, None) == -2            # count
+    need = L.bitlinear_cast_multi_workspace_bytes(0, w, 3, 8, 3200)
+    assert cm(0, X, None, None, 0.0, None, 8, 3200, w, 3, FAKE, need - 1, None) == -4     # workspace
 
 
 # ---- calibration probes (include/bitlinear_probe.h): validation only

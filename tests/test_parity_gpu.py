@@ -457,13 +457,13 @@ def test_forward_split_k(B, M, N, K):
         check_outputs(host(Y), host(acc), ref["acc"], 0.03, ref["absmax"], "forward split-K")
 
 
-@pytest.mark.parametrize("N,K", [(1, 1), (100, 12288), (100, 12289), (130, 3200), (64, 8640),
+@pytest.mark.parametrize("N,K", [(1, 1), (100, 6144), (100, 6145), (130, 3200), (64, 8640),
                                  (17000, 3000), (16400, 12000)])
 def test_forward_wide_one_token(B, N, K):
-    # one token over at most 256 row tiles (512 with 8 waves) takes the wide
-    # kernel: 192 units (96 with 8 waves) per workgroup without a split, one
-    # unit more splits K in two; 17000 rows take 8 waves; 16400 rows at
-    # K = 12000 would need 514 workgroups and take the default stream
+    # one token over at most 512 workgroups takes the wide kernel (8 waves):
+    # 96 units per workgroup without a split, one unit more splits K into
+    # parts of about 28 units (8640: five); 16400 rows at K = 12000 would
+    # need 257 x 7 workgroups and take the default stream
     say("forward wide", N, K)
     T = synth.random_ternary(N, K, seed=N + 5 * K)
     X = synth.activations_np(1, K, seed=N + K, outlier_frac=0.01)
@@ -479,8 +479,8 @@ def test_forward_wide_one_token(B, N, K):
 def test_forward_wide_tokens(B, M, N, K):
     # 2..16 tokens over few row tiles: the wide kernel's matrix-instruction
     # stream (activations staged per workgroup, the waves' sums meeting in
-    # LDS); 8640 and 17000 rows take 8 waves (two outputs per thread at 16
-    # tokens); K = 12289 and 8640 at 8 tokens split K
+    # LDS; two outputs per thread at 16 tokens); K = 12289 at 5 tokens and
+    # 8640 at 8 split K
     say("forward wide", M, N, K)
     T = synth.random_ternary(N, K, seed=M + N + 3 * K)
     X = synth.activations_np(M, K, seed=M * 7 + K, outlier_frac=0.01)
@@ -724,6 +724,58 @@ def test_matmul_multi_parity(B, M, K, Ns, fmt):
         Ys = mm(dev(Qp), dev(a), dev(rs), accs=accs)
         for Y, acc, (ref, g) in zip(Ys, accs, refs):
             check_outputs(host(Y), host(acc), ref, float(g), a, f"multi rep {rep}")
+
+
+@pytest.mark.parametrize("mode,M,K,Ns", [
+    (0, 1, 3200, (3200,)), (1, 1, 3200, (3200, 3200, 3200)), (3, 1, 3200, (8640, 8640)),
+    (2, 1, 8640, (3200,)), (2, 1, 20000, (64, 100)), (1, 1, 333, (100, 37)), (3, 1, 3200, (3200,)),
+    (3, 8, 3200, (3200, 640)), (0, 40, 777, (300,)), (2, 5, 1000, (257,)), (3, 1, 70000, (64,))])
+def test_cast_matmul_multi_parity(B, mode, M, K, Ns):
+    # the activation cast (plain, RMSNorm, gated squared ReLU, residual add +
+    # RMSNorm) and the matrices that read it in one call: at one token over
+    # few row tiles every contraction workgroup casts its own input (q|k|v
+    # and o shapes; K = 333 takes the scalar cast path); 270 row tiles, a
+    # cast input larger than a workgroup's weights (the gate's two rows, K =
+    # 20000), more tokens, or K > 65536 cast in a launch of their own.
+    # Outputs, accumulators and the residual sum against the oracle's cast +
+    # contraction, twice on one zero-filled-once workspace.
+    say("cast_matmul_multi", mode, M, K, Ns)
+    X = synth.activations_np(M, K, seed=3 * M + K + mode, outlier_frac=0.01)
+    aux = R = None
+    if mode == 1 or mode == 3:
+        aux = (1.0 + 0.1 * synth.activations_np(1, K, seed=K + 5)[0]).astype(np.float32)
+    if mode == 2:
+        aux = synth.activations_np(M, K, seed=K + 9)
+    if mode == 3:
+        R = synth.activations_np(M, K, seed=K + 11)
+    if mode == 0:
+        Q, a, rs = O.quant_act(X)
+    elif mode == 1:
+        decided_or_skip(X, 1e-5, "cast input")
+        Q, a, rs, _, _ = O.rmsnorm_quant_act(X, aux, 1e-5)
+    elif mode == 2:
+        Q, a, rs, _ = O.relu2_gate_quant_act(X, aux)
+    else:
+        Q, a, rs, S, _, _ = O.add_rmsnorm_quant_act(X, R, aux, 1e-5)
+        decided_or_skip(S, 1e-5, "cast input")
+    ws, refs = [], []
+    for i, N in enumerate(Ns):
+        T = synth.random_ternary(N, K, seed=17 * i + N + K)
+        g = np.float32(0.013 * (i + 1))
+        refs.append((O.matmul(Q, T), g))
+        ws.append(dict(P=dev(O.pack(T)), gamma=gamma_dev(float(g)), N=N))
+    cm = B.CastMultiMatmul(mode, ws, M, K)
+    Xd = dev(X)
+    auxd = None if aux is None else dev(aux)
+    Rd = None if R is None else dev(R)
+    for rep in range(2):
+        Xo = torch.full((M, K), float("nan"), device="cuda") if mode == 3 else None
+        accs = [torch.empty((M, N), dtype=torch.int32, device="cuda") for N in Ns]
+        Ys = cm(Xd, aux=auxd, R=Rd, eps=1e-5, X_out=Xo, accs=accs)
+        for Y, acc, (ref, g) in zip(Ys, accs, refs):
+            check_outputs(host(Y), host(acc), ref, float(g), a, f"cast multi rep {rep}")
+        if mode == 3:
+            np.testing.assert_array_equal(host(Xo), S, err_msg="residual sum")
 
 
 KNOB_SCRIPT = r"""
