@@ -50,7 +50,8 @@ HBM_PEAK_GBS = 8000.0
 INT8_PEAK_TOPS = 5000.0
 KERNEL_SOURCES = ["ternary_weight_w1_amd/csrc/gemv_stream.hip", "ternary_weight_w1_amd/csrc/gemm_tile.hip",
                   "ternary_weight_w1_amd/csrc/mm_common.hpp", "ternary_weight_w1_amd/csrc/common.hpp",
-                  "ternary_weight_w1_amd/csrc/gemv5.hip", "ternary_weight_w1_amd/csrc/bt5.hpp"]
+                  "ternary_weight_w1_amd/csrc/gemv5.hip", "ternary_weight_w1_amd/csrc/bt5.hpp",
+                  "ternary_weight_w1_amd/csrc/quant_row.hpp"]
 
 
 def log(*a):
@@ -156,7 +157,11 @@ def time_graph(torch, plan, steps, warmup):
 
 def curve(B, torch, model, Ms, dev, steps, warmup):
     """Latency of one full sweep over a model's BitLinear stack at each token
-    count M (quantize + contract every matrix, grouped launches)."""
+    count M (quantize + contract every matrix, grouped launches); "3b" adds
+    the chained stack, "3b-chained" runs only that."""
+    chained_only = model == "3b-chained"
+    if chained_only:
+        model = "3b"
     spec = synth.MODELS[model]
     log(f"building {model} stack: {spec['layers']} layers")
     mats = build_stack(B, torch, model, spec["layers"], dev)
@@ -174,6 +179,8 @@ def curve(B, torch, model, Ms, dev, steps, warmup):
                               "contraction_mfma_frac": round(ops / (kern * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4)})
         log(f"  {model} M={M}: {ms:.3f} ms per sweep")
         del plan, probs
+    if chained_only:
+        del out["points"]
     if model == "3b":
         log("timing the 3B stack chained as pre-norm blocks")
         out["chained"] = stack_curve(B, torch, mats, dev, [1, 8, 64, 256], steps, warmup)
@@ -511,8 +518,8 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--curves", default="3b,70b",
-                    help="comma list of latency-vs-M curves: 3b (M 1,8,64,256, and chained), 70b (M 1,16,176); "
-                         "'none' to skip")
+                    help="comma list of latency-vs-M curves: 3b (M 1,8,64,256, and chained), 70b (M 1,16,176), "
+                         "3b-chained (the chained 3B stack only); 'none' to skip")
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-bt5", action="store_true", help="skip the five-codes-per-byte comparison")
     ap.add_argument("--no-peaks", action="store_true", help="skip the measured-peak calibration probes")
@@ -635,7 +642,7 @@ def main():
     if curves:
         del mats
         torch.cuda.empty_cache()
-        points = {"3b": [1, 8, 64, 256], "70b": [1, 16, 176]}
+        points = {"3b": [1, 8, 64, 256], "70b": [1, 16, 176], "3b-chained": []}
         result["curves"] = {c: curve(B, torch, c, points[c], dev, max(5, args.steps // 5),
                                      max(1, args.warmup // 2)) for c in curves}
 
