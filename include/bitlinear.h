@@ -19,6 +19,25 @@
  *   acc[m,n] = sum_k T[n,k] * Q[m,k]           exact int32
  *   Y[m,n] = float(acc[m,n]) * ((gamma * a[m]) / 127)
  *
+ * The hot path and where each step lives (every other call is an extension
+ * built from the same kernels):
+ *   bitlinear_quantize_weights  absmean scale + ternarize (once per weight)
+ *   bitlinear_pack              four codes per byte, BL2-T64 (once per weight)
+ *   bitlinear_quant_act         per-token absmax + int8 cast + row sums
+ *   bitlinear_forward           quant_act + ternary x int8 contraction
+ *                               (exact int32) + fp32 rescale, per call
+ *   bitlinear_workspace_bytes, bitlinear_strerror, bitlinear_last_error,
+ *   bitlinear_abi_version       helpers of those four
+ * Extensions: bitlinear_matmul (the contraction on caller-quantized
+ * activations), the cast variants (_rmsnorm, _add_rmsnorm, _relu2_gate),
+ * multi-matrix and cast + multi-matrix launches, grouped plans, BT5-T32
+ * (five codes per byte), bitlinear_forward_noalloc, and the calibration
+ * probes of bitlinear_probe.h.
+ * Two deliberate differences from a minimal contract: every call takes
+ * `void *stream`, which is a hipStream_t (void * keeps HIP headers out of
+ * this file), and bitlinear_quant_act takes a row stride ldq so that the
+ * codes land directly in the padded rows the contraction reads.
+ *
  * Conventions for every call
  *   - Matrices are row-major.  W and T are N x K (N = out features, K = in
  *     features); X and Q are M x K (M tokens); Y and acc are M x N.
@@ -143,7 +162,11 @@ int64_t bitlinear_q_stride5(int64_t K);
 size_t bitlinear_workspace_bytes(int op, int64_t M, int64_t N, int64_t K);
 
 /*
- * Weight quantization (absmean -> ternary), once per weight matrix.
+ * Weight quantization (absmean -> ternary), once per weight matrix: one
+ * absmean scale per matrix, codes in {-1, 0, +1} (anthology note-168 on
+ * arXiv 2402.17764, "What it does"; the scale is quantized once, ahead of
+ * inference: BitNet b1.58 2B4T video transcript, yousumm.com,
+ * "Transcription").
  *   W         [in]  N x K fp32.
  *   gamma_in  [in]  NULL: compute gamma = absmean of W (deterministic fp64
  *                   two-stage reduction, rounded once to fp32).  Non-NULL:
@@ -158,7 +181,9 @@ int bitlinear_quantize_weights(const float *W, int64_t N, int64_t K, const float
                                void *stream);
 
 /*
- * Pack ternary codes into BL2-T64 (four codes per byte).
+ * Pack ternary codes into BL2-T64, four codes per byte (BitNet b1.58 2B4T
+ * video transcript, yousumm.com, "Transcription": four codes are packed
+ * into one byte and unpacked next to the math units).
  *   T      [in]  N x K int8 codes; values outside {-1, 0, +1} are clamped.
  *   P_out  [out] bitlinear_packed_bytes(N, K) bytes; padding is written too.
  */
@@ -171,7 +196,9 @@ int bitlinear_pack(const int8_t *T, int64_t N, int64_t K, uint8_t *P_out, void *
 int bitlinear_unpack(const uint8_t *P, int64_t N, int64_t K, int8_t *T_out, void *stream);
 
 /*
- * Per-token absmax int8 activation quantization.
+ * Per-token absmax int8 activation quantization (anthology note-168 on
+ * arXiv 2402.17764, "What it does": the activations are 8-bit; per-token
+ * absmax scaling is the reading taken).
  *   X          [in]  M x K fp32.
  *   Q_out      [out] M rows of ldq bytes: K int8 codes, then zeros up to ldq.
  *   ldq        row stride of Q_out in bytes, ldq >= K, ldq % 16 == 0.
@@ -289,7 +316,10 @@ int bitlinear_forward5(const float *X, int64_t M, int64_t K, const uint8_t *P5,
 
 /*
  * The whole BitLinear forward: quantize X per token, contract with the
- * packed ternary weights, rescale.
+ * packed ternary weights, rescale -- BitLinear in place of nn.Linear
+ * (anthology note-168 on arXiv 2402.17764, "What it does"), the product
+ * exact in integers (same note, "The part that is a bet rather than a
+ * measurement").
  *   X       [in]  M x K fp32.          P, gamma as for bitlinear_matmul.
  *   Y_out   [out] M x N fp32.          acc_out as for bitlinear_matmul.
  *   ws      bitlinear_workspace_bytes(BITLINEAR_WS_FORWARD, M, N, K) bytes;
