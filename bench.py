@@ -356,6 +356,99 @@ def stack_curve(B, torch, mats, dev, Ms, steps, warmup):
     return out
 
 
+def layer_calls(B, torch, dev, M, reps=20, rounds=20):
+    """Latency of each library call of one 3B-class decode layer at M tokens
+    (the chained stack's calls, on synthetic weights): every call captured
+    reps times back to back in a HIP graph, replayed rounds times; us per
+    call.  cast_*: the activation casts; mm_*: the multi-matrix contractions
+    on int8 input; cast_mm_*: the cast + contraction calls the chained stack
+    makes (at one token a single launch where the contraction casts its own
+    input)."""
+    import ctypes
+    L = B.lib()
+    dim, ffn = 3200, 8640
+    P = lambda t: ctypes.c_void_p(t.data_ptr()) if t is not None else None
+    g = torch.Generator(device=dev).manual_seed(1)
+    rnd = lambda *sh: torch.randn(*sh, device=dev, generator=g)
+    gam = torch.full((1,), 0.01, device=dev)
+    keep = []
+
+    def weights(Ns, K):
+        arr = (B.Weight * len(Ns))()
+        for i, N in enumerate(Ns):
+            Pk = B.pack(torch.randint(-1, 2, (N, K), dtype=torch.int8, device=dev, generator=g))
+            Y = torch.empty((M, N), device=dev)
+            keep.extend([Pk, Y])
+            arr[i] = B.Weight(Pk.data_ptr(), gam.data_ptr(), Y.data_ptr(), None, N, 0, 0)
+        return arr
+    sites = {"qkv": ((dim,) * 3, dim), "o": ((dim,), dim), "gu": ((ffn, ffn), dim), "down": ((dim,), ffn)}
+    W = {k: weights(Ns, K) for k, (Ns, K) in sites.items()}
+    x, r = rnd(M, dim), rnd(M, dim)
+    xo, gains = torch.empty_like(x), 1 + 0.1 * rnd(dim)
+    gt, up = rnd(M, ffn), rnd(M, ffn)
+    Qd = torch.zeros((M, B.q_stride(dim)), dtype=torch.int8, device=dev)
+    Qf = torch.zeros((M, B.q_stride(ffn)), dtype=torch.int8, device=dev)
+    a, rs = torch.ones(M, device=dev), torch.zeros(M, dtype=torch.int32, device=dev)
+    ws = {}
+    for k, (Ns, K) in sites.items():
+        n = max([L.bitlinear_multi_workspace_bytes(W[k], len(Ns), M, K)] +
+                [L.bitlinear_cast_multi_workspace_bytes(md, W[k], len(Ns), M, K) for md in range(4)])
+        ws[k] = torch.zeros(max(n, 16), dtype=torch.uint8, device=dev)
+
+    def chk(st):
+        if st:
+            raise RuntimeError(L.bitlinear_last_error().decode())
+
+    def mm(k, Q, K):
+        return lambda s: chk(L.bitlinear_matmul_multi(P(Q), Q.shape[1], P(a), P(rs), M, K, W[k], len(sites[k][0]),
+                                                      P(ws[k]), ws[k].numel(), s))
+
+    def cmm(k, mode, X, aux, R, Xo, K):
+        return lambda s: chk(L.bitlinear_cast_matmul_multi(mode, P(X), P(aux), P(R), 1e-5, P(Xo), M, K, W[k],
+                                                           len(sites[k][0]), P(ws[k]), ws[k].numel(), s))
+    calls = {
+        "cast_add_rmsnorm_3200": lambda s: chk(L.bitlinear_quant_act_add_rmsnorm(
+            P(x), P(r), M, dim, P(gains), 1e-5, P(xo), P(Qd), Qd.shape[1], P(a), P(rs), s)),
+        "cast_plain_3200": lambda s: chk(L.bitlinear_quant_act(P(x), M, dim, P(Qd), Qd.shape[1], P(a), P(rs), s)),
+        "cast_relu2_gate_8640": lambda s: chk(L.bitlinear_quant_act_relu2_gate(
+            P(gt), P(up), M, ffn, P(Qf), Qf.shape[1], P(a), P(rs), s)),
+        "mm_qkv": mm("qkv", Qd, dim), "mm_o": mm("o", Qd, dim), "mm_gate_up": mm("gu", Qd, dim),
+        "mm_down": mm("down", Qf, ffn),
+        "cast_mm_qkv": cmm("qkv", B.CAST_ADD_RMSNORM, x, gains, r, xo, dim),
+        "cast_mm_o": cmm("o", B.CAST_PLAIN, x, None, None, None, dim),
+        "cast_mm_gate_up": cmm("gu", B.CAST_ADD_RMSNORM, x, gains, r, xo, dim),
+        "cast_mm_down": cmm("down", B.CAST_RELU2_GATE, gt, up, None, None, ffn),
+    }
+    out = {}
+    side = torch.cuda.Stream()
+    for name, fn in calls.items():
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            s = ctypes.c_void_p(side.cuda_stream)
+            for _ in range(3):
+                fn(s)
+            torch.cuda.synchronize()
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr, stream=side):
+                for _ in range(reps):
+                    fn(s)
+        torch.cuda.current_stream().wait_stream(side)
+        for _ in range(3):
+            gr.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(rounds):
+            gr.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        out[name] = round(e0.elapsed_time(e1) * 1e3 / (reps * rounds), 2)
+        del gr
+    del keep
+    torch.cuda.empty_cache()
+    return out
+
+
 def measured_peaks(B, torch, dev, seconds: float = 0.6):
     """What this part sustains on the two roofline resources, from the
     library's calibration probes (include/bitlinear_probe.h):
@@ -525,6 +618,9 @@ def main():
     ap.add_argument("--no-peaks", action="store_true", help="skip the measured-peak calibration probes")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run only a plain device copy of known size (PMC calibration)")
+    ap.add_argument("--layer-calls", default=None,
+                    help="comma list of token counts: print only the per-call latency of one 3B-class decode "
+                         "layer's library calls at each (JSON line)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -545,6 +641,12 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         log(f"copy probe: 3 x {n} bytes")
+        return
+
+    if args.layer_calls:
+        res = {f"M={M}": layer_calls(B, torch, dev, int(M)) for M in args.layer_calls.split(",")}
+        print(json.dumps({"layer_calls_us": res, "workload": "one 3B-class decode layer (dim 3200, ffn 8640)"}),
+              flush=True)
         return
 
     spec = synth.MODELS[args.model]
