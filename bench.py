@@ -514,9 +514,31 @@ def measured_peaks(B, torch, dev, seconds: float = 0.6):
         raise RuntimeError("matrix-instruction probe checksum mismatch")
     later = sorted(rates[len(rates) // 2:])
     tops = later[len(later) // 2]
+    # grid-wide barrier with one word exchanged per workgroup, one workgroup
+    # per compute unit: (time of R rounds - time of 1 round) / (R - 1)
+    cus = B.probe_compute_units()
+
+    def barrier_ms(rounds):
+        best = None
+        for _ in range(5):
+            state = torch.zeros(2 + 2 * cus, dtype=torch.int32, device=dev)
+            a, b = ev(), ev()
+            a.record()
+            state, _ = B.probe_barrier(rounds, cus, state=state)
+            b.record()
+            b.synchronize()
+            if int(state[1]) != 0 or int(state[0]) != rounds * cus:
+                raise RuntimeError("barrier probe gave up or miscounted")
+            best = a.elapsed_time(b) if best is None else min(best, a.elapsed_time(b))
+        return best
+    barrier_us = (barrier_ms(2001) - barrier_ms(1)) / 2000 * 1e3
     return {
         "hbm_read": {"value": round(best[0], 1), "unit": "GB/s",
                      "probe": f"16-byte non-temporal streaming read of 2 GiB, {best[1] >> 10} KiB per workgroup"},
+        "grid_barrier": {"value": round(barrier_us, 3), "unit": "us",
+                         "probe": f"device-scope store + wait + atomic arrival + polling, one word exchanged per "
+                                  f"workgroup, {cus} workgroups (one per compute unit), best of 5 runs of 2001 "
+                                  f"rounds less 1 round"},
         "int8_mfma": {"value": round(tops, 1), "unit": "TOP/s",
                       "probe": f"v_mfma_i32_32x32x32_i8 chains, {blocks} workgroups, no memory traffic, "
                                f"median of {len(later)} sustained bursts"},

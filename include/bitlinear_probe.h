@@ -3,9 +3,11 @@
  *
  * The contraction kernels are reported against the part's published peaks
  * (8 TB/s HBM, 5.0 POP/s dense int8) and also against what this part
- * sustains on the same two resources, measured by these two probes.  They
- * compute nothing of the BitLinear layer; each leaves a checksum so that its
- * work cannot be elided and its result can be checked on the host.
+ * sustains on the same two resources, measured by the first two probes; the
+ * third measures a grid-wide barrier, the cost per dependent stage of a
+ * persistent kernel.  They compute nothing of the BitLinear layer; each
+ * leaves a checksum so that its work cannot be elided and its result can be
+ * checked on the host.
  *
  * Conventions are those of bitlinear.h: device pointers owned by the
  * caller, 16-byte aligned; calls only enqueue work on `stream` (a
@@ -59,6 +61,32 @@ int bitlinear_probe_mfma(int64_t iters, int32_t a, int32_t b, int32_t blocks, in
  * device at once (compute units times workgroups per unit), into *blocks.
  * Queries the HIP runtime: BITLINEAR_ERR_HIP if it fails. */
 int bitlinear_probe_mfma_blocks(int32_t *blocks);
+
+/*
+ * `rounds` grid-wide barriers among `blocks` workgroups of 256 threads: at
+ * each, every workgroup publishes one word (round * blocks + its index) with
+ * a device-scope store, waits for it to complete, increments a device-scope
+ * counter and polls it until every workgroup has arrived, then reads all
+ * words of that round with device-scope loads and adds them to its sum.
+ * The poll is bounded: a workgroup that polls spin_limit times (each poll
+ * about 64 clocks apart) without seeing everyone records a give-up and stops.
+ *   rounds      >= 1                              (BITLINEAR_ERR_SHAPE)
+ *   blocks      1 .. the device's compute units, so that all are resident
+ *               at once                            (BITLINEAR_ERR_SHAPE)
+ *   spin_limit  >= 1                              (BITLINEAR_ERR_ARG)
+ *   state       uint32[2 + 2 * blocks], ZERO-FILLED by the caller; after the
+ *               call state[0] = rounds * blocks and state[1] = 0 (give-ups)
+ *               unless a workgroup gave up.
+ *   sink        uint32[256 * blocks]; the 256 words of workgroup b add up
+ *               (mod 2^32) to the sum over rounds r and workgroups i of
+ *               r * blocks + i.
+ */
+int bitlinear_probe_barrier(int32_t rounds, int32_t blocks, int32_t spin_limit, uint32_t *state, uint32_t *sink,
+                            void *stream);
+
+/* Compute units of the current device, into *cus (the most workgroups
+ * bitlinear_probe_barrier takes).  BITLINEAR_ERR_HIP if the query fails. */
+int bitlinear_probe_compute_units(int32_t *cus);
 
 #ifdef __cplusplus
 }

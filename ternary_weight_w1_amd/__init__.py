@@ -109,6 +109,8 @@ def lib():
             "bitlinear_probe_read": (_int, [_vp, _i64, _i64, _vp, _vp]),
             "bitlinear_probe_mfma": (_int, [_i64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _vp, _vp]),
             "bitlinear_probe_mfma_blocks": (_int, [ctypes.POINTER(ctypes.c_int32)]),
+            "bitlinear_probe_barrier": (_int, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _vp, _vp, _vp]),
+            "bitlinear_probe_compute_units": (_int, [ctypes.POINTER(ctypes.c_int32)]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -442,6 +444,30 @@ def probe_mfma(iters: int, a: int, b: int, blocks: int, sink=None, device=None, 
         sink = torch.empty(256 * blocks, dtype=torch.int32, device=device or "cuda")
     _check(lib().bitlinear_probe_mfma(iters, a, b, blocks, sink.data_ptr(), _stream(stream)), "probe_mfma")
     return sink
+
+
+def probe_compute_units() -> int:
+    n = ctypes.c_int32(0)
+    _check(lib().bitlinear_probe_compute_units(ctypes.byref(n)), "probe_compute_units")
+    return int(n.value)
+
+
+@_on_stream
+def probe_barrier(rounds: int, blocks: int, spin_limit: int = 1 << 20, state=None, sink=None, device=None,
+                  stream=None):
+    """Grid-barrier calibration probe: `rounds` barriers among `blocks`
+    workgroups with a word exchanged per workgroup per barrier; returns
+    (state, sink).  state[0] ends at rounds * blocks, state[1] counts
+    give-ups; each workgroup's 256 sink words add up to the sum over rounds r
+    and workgroups i of r * blocks + i (mod 2^32)."""
+    device = device or "cuda"
+    if state is None:
+        state = torch.zeros(2 + 2 * blocks, dtype=torch.int32, device=device)
+    if sink is None:
+        sink = torch.empty(256 * blocks, dtype=torch.int32, device=device)
+    _check(lib().bitlinear_probe_barrier(rounds, blocks, spin_limit, state.data_ptr(), sink.data_ptr(),
+                                         _stream(stream)), "probe_barrier")
+    return state, sink
 
 
 class MultiMatmul:

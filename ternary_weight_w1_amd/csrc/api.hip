@@ -69,7 +69,8 @@ struct Knobs {
     int xcd_order = 3;           // bit 0: streaming kernel, bit 1: tile kernel
     int mfma_tiles = 0;          // tiles per wave of the streaming MFMA kernel above 16 tokens: 0 = by launch size, 1, 2
     int wide = 1;                // launches of 1..16 tokens over few tiles take the wide kernels
-    int cast_fuse = 1;           // one-token cast + contraction calls cast inside the contraction
+    int cast_fuse = 1;           // one-token cast + contraction calls cast inside the contraction:
+                                 // 0 never, 1 where it pays (the default rule), 2 wherever it can
 };
 const Knobs &knobs()
 {
@@ -80,7 +81,7 @@ const Knobs &knobs()
         if (const char *s = getenv("BITLINEAR_XCD_ORDER")) v.xcd_order = atoi(s) & 3;
         if (const char *s = getenv("BITLINEAR_MFMA_TILES")) v.mfma_tiles = (atoi(s) == 1 || atoi(s) == 2) ? atoi(s) : 0;
         if (const char *s = getenv("BITLINEAR_WIDE")) v.wide = atoi(s) != 0;
-        if (const char *s = getenv("BITLINEAR_CAST_FUSE")) v.cast_fuse = atoi(s) != 0;
+        if (const char *s = getenv("BITLINEAR_CAST_FUSE")) v.cast_fuse = (atoi(s) >= 0 && atoi(s) <= 2) ? atoi(s) : 1;
         return v;
     }();
     return k;
@@ -954,7 +955,7 @@ int cast_plan(int mode, int64_t M, int64_t K, const bitlinear_weight *w, int cou
     }
     const int64_t arrays = (mode == BITLINEAR_CAST_ADD_RMSNORM) ? 3 : (mode == BITLINEAR_CAST_PLAIN) ? 1 : 2;
     cp.fused = knobs().cast_fuse && !bt5 && M == 1 && cp.mp.kind == 0 && cp.mp.variant == 12 && K <= kCastMaxK &&
-               items <= kCastMaxItems && arrays * 4 * K <= 1024 * upsplit;
+               (knobs().cast_fuse == 2 || (items <= kCastMaxItems && arrays * 4 * K <= 1024 * upsplit));
     if (cp.fused) {
         cp.total = cp.mp.total_bytes;
         return BITLINEAR_OK;
@@ -1385,6 +1386,30 @@ int bitlinear_probe_mfma(int64_t iters, int32_t a, int32_t b, int32_t blocks, in
                     (long long)iters, blocks);
     const hipError_t e = bl::launch_probe_mfma(iters, a, b, blocks, sink, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? BITLINEAR_OK : hip_fail(e, "probe_mfma");
+}
+
+int bitlinear_probe_compute_units(int32_t *cus)
+{
+    if (!cus) return fail(BITLINEAR_ERR_NULL, "probe_compute_units: cus is required");
+    int n = 0;
+    if (hipError_t e = bl::probe_compute_units(&n)) return hip_fail(e, "probe_compute_units");
+    *cus = n;
+    return BITLINEAR_OK;
+}
+
+int bitlinear_probe_barrier(int32_t rounds, int32_t blocks, int32_t spin_limit, uint32_t *state, uint32_t *sink,
+                            void *stream)
+{
+    if (!state || !sink) return fail(BITLINEAR_ERR_NULL, "probe_barrier: state and sink are required");
+    if (!a4(state) || !a4(sink)) return fail(BITLINEAR_ERR_ALIGN, "probe_barrier: state and sink must be 4-byte aligned");
+    if (rounds < 1) return fail(BITLINEAR_ERR_SHAPE, "probe_barrier: rounds=%d must be >= 1", rounds);
+    if (spin_limit < 1) return fail(BITLINEAR_ERR_ARG, "probe_barrier: spin_limit=%d must be >= 1", spin_limit);
+    int cus = 0;
+    if (hipError_t e = bl::probe_compute_units(&cus)) return hip_fail(e, "probe_barrier");
+    if (blocks < 1 || blocks > cus)
+        return fail(BITLINEAR_ERR_SHAPE, "probe_barrier: blocks=%d must be in [1, %d] (one per compute unit)", blocks, cus);
+    const hipError_t e = bl::launch_probe_barrier(rounds, blocks, spin_limit, state, sink, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? BITLINEAR_OK : hip_fail(e, "probe_barrier");
 }
 
 int bitlinear_probe_mfma_blocks(int32_t *blocks)

@@ -2,8 +2,10 @@
 // kernels are reported against: a plain streaming read of a device buffer
 // (the HBM bound of the one-token sweep) and a chain of int8 matrix
 // instructions with no memory traffic at all (the bound of the prefill
-// contraction).  Neither does any of the layer's arithmetic; each leaves a
-// checksum so that its work cannot be dropped and its result can be checked.
+// contraction); and the cost of a grid-wide barrier with data exchange,
+// the price a persistent kernel would pay per dependent stage.  None does
+// any of the layer's arithmetic; each leaves a checksum so that its work
+// cannot be dropped and its result can be checked.
 #include "mm_common.hpp"
 #include "probe.hpp"
 
@@ -60,7 +62,67 @@ __global__ __launch_bounds__(kProbeThreads) void probe_mfma_kernel(int64_t iters
     gstore_ptr<int32_t>(sink)[(int64_t)blockIdx.x * kProbeThreads + threadIdx.x] = s;
 }
 
+// `rounds` grid-wide barriers among the launch's workgroups (at most one per
+// compute unit, so all are resident at once).  At barrier r every workgroup
+// publishes one word (r * G + b) with a device-scope store, waits until the
+// store has completed, increments the device-scope arrival counter and polls
+// it until all G have arrived; then it reads every workgroup's word of round
+// r with device-scope loads and adds them up.  Words alternate between two
+// slot sets by round parity: a workgroup can overwrite its round-r slot (in
+// round r + 2) only after the barrier of round r + 1, which every reader of
+// round r has passed.  The poll is bounded: a workgroup that polls
+// spin_limit times without seeing everyone counts a give-up and stops, so
+// every wave exits whatever the others do.
+// state: [0] arrival counter, [1] give-ups, [2 + (r & 1) * G + b] the words.
+__global__ __launch_bounds__(kProbeThreads) void probe_barrier_kernel(int rounds, int spin_limit,
+                                                                      uint32_t *__restrict__ state,
+                                                                      uint32_t *__restrict__ sink)
+{
+    const int b = blockIdx.x, G = gridDim.x, t = threadIdx.x;
+    __shared__ int s_ok;
+    uint32_t sum = 0;
+    for (int r = 0; r < rounds; ++r) {
+        uint32_t *words = state + 2 + (r & 1) * G;
+        if (t == 0) __hip_atomic_store(&words[b], (uint32_t)r * G + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __builtin_amdgcn_s_waitcnt(0);  // the word is at the coherence point
+        __syncthreads();
+        if (t == 0) {
+            __hip_atomic_fetch_add(&state[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const uint32_t target = (uint32_t)(r + 1) * G;
+            int spins = 0;
+            while (__hip_atomic_load(&state[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target &&
+                   spins < spin_limit) {
+                __builtin_amdgcn_s_sleep(1);
+                ++spins;
+            }
+            s_ok = spins < spin_limit;
+            if (!s_ok) __hip_atomic_fetch_add(&state[1], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        __syncthreads();
+        if (!s_ok) break;
+        for (int i = t; i < G; i += kProbeThreads)
+            sum += __hip_atomic_load(&words[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    gstore_ptr<uint32_t>(sink)[(int64_t)b * kProbeThreads + t] = sum;
+}
+
 }  // namespace
+
+hipError_t launch_probe_barrier(int rounds, int blocks, int spin_limit, uint32_t *state, uint32_t *sink,
+                                hipStream_t s)
+{
+    hipLaunchKernelGGL(probe_barrier_kernel, dim3((unsigned)blocks), dim3(kProbeThreads), 0, s, rounds, spin_limit,
+                       state, sink);
+    return hipGetLastError();
+}
+
+hipError_t probe_compute_units(int *cus)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(cus, hipDeviceAttributeMultiprocessorCount, dev);
+    return e;
+}
 
 hipError_t launch_probe_read(const void *buf, int64_t bytes, int64_t chunk_bytes, uint32_t *sink, hipStream_t s)
 {

@@ -37,7 +37,7 @@ def test_every_header_is_checked():
 
 def test_every_declared_symbol_is_exported():
     names = _declared()
-    assert len(names) == 37, names
+    assert len(names) == 39, names
     out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r"\bT (bitlinear_\w+)", out))
@@ -421,6 +421,15 @@ def test_probe_read_rejects_bad_arguments():
     assert L.bitlinear_probe_read(FAKE, 4100, 4096, FAKE, None) == -2
     assert L.bitlinear_probe_read(FAKE, 4096, 1000, FAKE, None) == -2
     assert L.bitlinear_probe_read(FAKE, 0, 4096, FAKE, None) == -2
+
+
+def test_probe_barrier_rejects_bad_arguments():
+    L = B.lib()
+    assert L.bitlinear_probe_barrier(10, 4, 100, None, FAKE, None) == -1
+    assert L.bitlinear_probe_barrier(10, 4, 100, FAKE, None, None) == -1
+    assert L.bitlinear_probe_barrier(10, 4, 100, FAKE + 2, FAKE, None) == -3
+    assert L.bitlinear_probe_barrier(0, 4, 100, FAKE, FAKE, None) == -2
+    assert L.bitlinear_probe_barrier(10, 4, 0, FAKE, FAKE, None) == -6
 
 
 def test_probe_mfma_rejects_bad_arguments():

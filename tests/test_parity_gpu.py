@@ -809,13 +809,37 @@ plan = B.GroupPlan(probs)
 plan.forward(); torch.cuda.synchronize()
 for p, ref in zip(probs, refs):
     assert np.array_equal(p["acc"].cpu().numpy(), ref["acc"]) and np.array_equal(p["Y"].cpu().numpy(), ref["Y"]), "group"
+# cast + multi-matrix calls at one token (plain and residual add + RMSNorm,
+# 270 row tiles and one) and at five tokens
+for M, K, Ns, mode in [(1, 3200, (8640, 8640), 3), (1, 640, (100,), 0), (5, 640, (257, 64), 3)]:
+    X = synth.activations_np(M, K, seed=500 + K); R = synth.activations_np(M, K, seed=501 + K)
+    if mode == 3:
+        Q, a, rs, S, _, _ = O.add_rmsnorm_quant_act(X, R, None, 1e-5)
+        sys.path.insert(0, "tests")
+        from fp_exact import rms_undecided_rows
+        if rms_undecided_rows(S, 1e-5):
+            print("undecided RMSNorm factor, case skipped", M, K)
+            continue
+    else:
+        Q, a, rs = O.quant_act(X)
+    ws, refs = [], []
+    for i, N in enumerate(Ns):
+        T = synth.random_ternary(N, K, seed=510 + i + N)
+        refs.append(O.epilogue(O.matmul(Q, T), g, a))
+        ws.append(dict(P=dev(O.pack(T)), gamma=gd, N=N))
+    cm = B.CastMultiMatmul(mode, ws, M, K)
+    Xo = torch.empty((M, K), device="cuda") if mode == 3 else None
+    Ys = cm(dev(X), R=dev(R) if mode == 3 else None, eps=1e-5, X_out=Xo)
+    torch.cuda.synchronize()
+    for Y, ref in zip(Ys, refs):
+        assert np.array_equal(Y.cpu().numpy(), ref), ("cast multi", M, K, mode)
 print("knob ok")
 """
 
 KNOB_SETTINGS = [
     ("BITLINEAR_MFMA_TILES", "1"), ("BITLINEAR_MFMA_TILES", "2"),
     ("BITLINEAR_SPLIT_TARGET", "1"), ("BITLINEAR_SPLIT_TARGET", "100000"), ("BITLINEAR_XCD_ORDER", "0"),
-    ("BITLINEAR_WIDE", "0"),
+    ("BITLINEAR_WIDE", "0"), ("BITLINEAR_CAST_FUSE", "0"), ("BITLINEAR_CAST_FUSE", "2"),
 ]
 
 

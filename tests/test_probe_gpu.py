@@ -45,3 +45,21 @@ def test_probe_mfma_blocks_fill_the_device():
     n = B.probe_mfma_blocks()
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     assert n >= cus and n % cus == 0
+
+
+@pytest.mark.parametrize("rounds,blocks", [(1, 1), (5, 3), (64, 256), (1000, 256)])
+def test_probe_barrier_exchange(rounds, blocks):
+    # every barrier completes (no give-up), the counter ends at rounds x
+    # blocks, and every workgroup saw every other workgroup's word of every
+    # round: its sum is the closed form
+    cus = B.probe_compute_units()
+    blocks = min(blocks, cus)
+    print(f"probe_barrier rounds={rounds} blocks={blocks}", flush=True)
+    state, sink = B.probe_barrier(rounds, blocks, spin_limit=1 << 20)
+    torch.cuda.synchronize()
+    st = state.cpu().numpy().view(np.uint32)
+    assert int(st[1]) == 0, "a workgroup gave up waiting"
+    assert int(st[0]) == rounds * blocks
+    want = sum(r * blocks + i for r in range(rounds) for i in range(blocks)) % (1 << 32)
+    per = sink.cpu().numpy().view(np.uint32).reshape(blocks, 256).astype(np.uint64).sum(1) % (1 << 32)
+    assert (per == want).all()
