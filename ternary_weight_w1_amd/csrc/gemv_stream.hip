@@ -1,6 +1,8 @@
 // Streaming contraction for small token counts (decode): M = 1 and 2 with
 // packed int8 dot products, 3 <= M <= 32 with int8 matrix instructions (the
-// split point is a host-side setting; the dot4 kernels take up to 4 tokens).
+// split point is a host-side setting), and, for launches of few tiles (the
+// matrices of one decode layer), wide workgroups of eight waves per tile
+// that may also cast their own input row.
 //
 // The pages describe the decode kernel as: weights packed four codes per
 // byte are streamed across the GPU and unpacked next to the math units,
@@ -13,9 +15,10 @@
 // few VALU operations per code as possible.
 //
 // Work item = (problem, 64-row weight tile, K split).  A 256-thread
-// workgroup owns one item; its four waves take every fourth 64-code unit of
-// the split, so together they stream 4 KiB of contiguous packed weights per
-// step.  Each lane loads one 16-byte slot of the unit's 1 KiB block: words
+// workgroup owns one item (the dot4 kernels; the MFMA stream takes groups of
+// tiles, the wide kernels 512 threads per item); its four waves take every
+// fourth 64-code unit of the split, so together they stream 4 KiB of
+// contiguous packed weights per step.  Each lane loads one 16-byte slot of the unit's 1 KiB block: words
 // (s, h) hold 16 codes of rows r and 32 + r (r = lane % 32) for code chunk
 // lane / 32 of half h.
 //
