@@ -476,6 +476,32 @@ __device__ __forceinline__ void stream_dot4_tokens(const Problem &p, int local)
 // reads its A operands with ds_read_b128 (lanes of rows past M read the zero
 // chunk) instead of two global loads per unit.
 constexpr int kTokStride = 80;  // 64 bytes + 16: 16 rows at one column hit distinct bank groups
+
+// Stages units [0, n_units) of the K range at q (the first M token rows,
+// row stride ldq) row-major into LDS: token m's 64 bytes of unit uu at
+// (uu * M + m) * kTokStride.  Thread t always copies part t % 4 of token
+// (t / 4) % M, for every (THR / (4 M))-th unit from t / (4 M) on -- so no
+// thread divides per chunk -- with up to UNR loads in flight before its
+// first LDS store; threads past the last whole pass of 4 M copy nothing.
+template <int THR, int UNR>
+__device__ __forceinline__ void stage_rows(const BL_GLOBAL int8_t *q, int64_t ldq, int M, int n_units)
+{
+    const int cpu = 4 * M, per = THR / cpu;
+    const int slot = threadIdx.x % cpu, uo = threadIdx.x / cpu;
+    if (uo >= per) return;
+    const BL_GLOBAL int8_t *src = q + (int64_t)(slot >> 2) * ldq + 16 * (slot & 3);
+    int8_t *dst = stream_q_lds + (slot >> 2) * kTokStride + 16 * (slot & 3);
+    const int ustride = M * kTokStride;
+    for (int ub = uo; ub < n_units; ub += UNR * per) {
+        v4i v[UNR];
+#pragma unroll
+        for (int k = 0; k < UNR; ++k)
+            if (ub + k * per < n_units) v[k] = *reinterpret_cast<const BL_GLOBAL v4i *>(src + 64 * (ub + k * per));
+#pragma unroll
+        for (int k = 0; k < UNR; ++k)
+            if (ub + k * per < n_units) *reinterpret_cast<v4i *>(dst + (ub + k * per) * ustride) = v[k];
+    }
+}
 template <int UNROLL, int TPW, bool ALDS = false>
 __device__ void stream_mfma(const Problem &p, int local)
 {
@@ -507,13 +533,13 @@ __device__ void stream_mfma(const Problem &p, int local)
     }
     const v4i zero = {0, 0, 0, 0};
     const v4u zw = {0u, 0u, 0u, 0u};
-    // the tokens' row sums and absmax, fetched now so that their latency
-    // hides under the stream (read per output element at the end)
+    // the tokens' row sums and rescale factors, fetched now so that their
+    // latency hides under the stream (read per output element at the end)
     __shared__ int s_rowsum[kStreamMaxTokens];
-    __shared__ float s_absmax[kStreamMaxTokens];
+    __shared__ float s_scale[kStreamMaxTokens];
     if (threadIdx.x < p.M) {
         s_rowsum[threadIdx.x] = gload_ptr<int32_t>(p.rowsum)[threadIdx.x];
-        s_absmax[threadIdx.x] = gload_ptr<float>(p.absmax)[threadIdx.x];
+        s_scale[threadIdx.x] = token_scale(*p.gamma, gload_ptr<float>(p.absmax)[threadIdx.x]);
     }
 
     const int n_units = u1 - u0;
@@ -538,28 +564,8 @@ __device__ void stream_mfma(const Problem &p, int local)
     // are staged (they do not depend on them): the two round trips overlap
     if constexpr (ALDS) load_group(0, 0);
     if constexpr (ALDS) {
-        const int M = p.M, nch = n_units * M * 4;
-        const BL_GLOBAL int8_t *q = gload_ptr<int8_t>(p.Q) + 64 * u0;
-        for (int base = threadIdx.x; base < nch; base += 8 * kThreads) {
-            v4i v[8];
-#pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                const int c = base + k * kThreads;  // chunk c: unit c / (4 M), token (c / 4) % M, part c % 4
-                if (c < nch) {
-                    const int uu = c / (4 * M), rem = c - uu * 4 * M;
-                    v[k] = *reinterpret_cast<const BL_GLOBAL v4i *>(q + (int64_t)(rem >> 2) * p.ldq + 64 * uu +
-                                                                   16 * (rem & 3));
-                }
-            }
-#pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                const int c = base + k * kThreads;
-                if (c < nch) {
-                    const int uu = c / (4 * M), rem = c - uu * 4 * M;
-                    *reinterpret_cast<v4i *>(stream_q_lds + (uu * M + (rem >> 2)) * kTokStride + 16 * (rem & 3)) = v[k];
-                }
-            }
-        }
+        const int M = p.M;
+        stage_rows<kThreads, 8>(gload_ptr<int8_t>(p.Q) + 64 * u0, p.ldq, M, n_units);
         if (threadIdx.x == 0) *reinterpret_cast<v4i *>(stream_q_lds + n_units * M * kTokStride) = zero;
         a_lane = r < M ? r * kTokStride + 16 * g : n_units * M * kTokStride;
         __syncthreads();
@@ -604,7 +610,6 @@ __device__ void stream_mfma(const Problem &p, int local)
     if (i < groups) run_group(0, i);
 
     // element e of lane l is token 8*(e/4) + 4*(l/32) + e%4, row 32*s + l%32
-    const float gamma = *p.gamma;
     const int64_t ldp = (int64_t)p.NT * 64;
     __syncthreads();  // the token scales are in LDS
 #pragma unroll
@@ -618,7 +623,7 @@ __device__ void stream_mfma(const Problem &p, int local)
                 const int m = 8 * (e >> 2) + 4 * g + (e & 3);
                 if (m < p.M && n < p.N) {
                     if (p.ks == 1)
-                        finish_output_with(p, gamma, m, n, acc[t][s2][e], s_rowsum[m], s_absmax[m]);
+                        finish_output_scaled(p, m, n, acc[t][s2][e], s_rowsum[m], s_scale[m]);
                     else
                         put_partial(p.acc_ws + (((int64_t)split * p.M + m) * ldp + n), acc[t][s2][e]);
                 }
@@ -646,7 +651,7 @@ __device__ void stream_mfma(const Problem &p, int local)
         sum_partials<4>(p.acc_ws, off, ok, (int64_t)p.M * ldp, p.ks, sums);
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-            if (ok[r]) finish_output_with(p, gamma, mm[r], nn[r], sums[r], s_rowsum[mm[r]], s_absmax[mm[r]]);
+            if (ok[r]) finish_output_scaled(p, mm[r], nn[r], sums[r], s_rowsum[mm[r]], s_scale[mm[r]]);
     }
 }
 
@@ -676,35 +681,14 @@ __device__ void stream_mfma_wide(const Problem &p, int local)
     for (int j = 0; j < kWideUnits; ++j)
         if (j < nu) w[j] = load_packed(blk + (int64_t)(u0 + wave + W * j) * 64);
     __shared__ int s_rowsum[kStreamMaxTokens];
-    __shared__ float s_absmax[kStreamMaxTokens];
+    __shared__ float s_scale[kStreamMaxTokens];
     if (threadIdx.x < M) {
         s_rowsum[threadIdx.x] = gload_ptr<int32_t>(p.rowsum)[threadIdx.x];
-        s_absmax[threadIdx.x] = gload_ptr<float>(p.absmax)[threadIdx.x];
+        s_scale[threadIdx.x] = token_scale(*p.gamma, gload_ptr<float>(p.absmax)[threadIdx.x]);
     }
     const int n_units = u1 - u0;
     {
-        const int nch = n_units * M * 4;  // chunk c: unit c / (4 M), token (c / 4) % M, part c % 4
-        const BL_GLOBAL int8_t *q = gload_ptr<int8_t>(p.Q) + 64 * u0;
-        for (int base = threadIdx.x; base < nch; base += 4 * kThr) {
-            v4i v[4];
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const int c = base + k * kThr;
-                if (c < nch) {
-                    const int uu = c / (4 * M), rem = c - uu * 4 * M;
-                    v[k] = *reinterpret_cast<const BL_GLOBAL v4i *>(q + (int64_t)(rem >> 2) * p.ldq + 64 * uu +
-                                                                   16 * (rem & 3));
-                }
-            }
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const int c = base + k * kThr;
-                if (c < nch) {
-                    const int uu = c / (4 * M), rem = c - uu * 4 * M;
-                    *reinterpret_cast<v4i *>(stream_q_lds + (uu * M + (rem >> 2)) * kTokStride + 16 * (rem & 3)) = v[k];
-                }
-            }
-        }
+        stage_rows<kThr, 4>(gload_ptr<int8_t>(p.Q) + 64 * u0, p.ldq, M, n_units);
         if (threadIdx.x == 0) *reinterpret_cast<v4i *>(stream_q_lds + n_units * M * kTokStride) = (v4i){0, 0, 0, 0};
     }
     __syncthreads();
@@ -764,11 +748,10 @@ __device__ void stream_mfma_wide(const Problem &p, int local)
             for (int v = 0; v < kSlots; ++v) tot[i] += red[(v * M + mm[i]) * 64 + (idx & 63)];
         }
     }
-    const float gamma = *p.gamma;
     if (p.ks == 1) {
 #pragma unroll
         for (int i = 0; i < kR; ++i)
-            if (mine[i] && nn[i] < p.N) finish_output_with(p, gamma, mm[i], nn[i], tot[i], s_rowsum[mm[i]], s_absmax[mm[i]]);
+            if (mine[i] && nn[i] < p.N) finish_output_scaled(p, mm[i], nn[i], tot[i], s_rowsum[mm[i]], s_scale[mm[i]]);
         return;
     }
     const int64_t ldp = (int64_t)p.NT * 64;  // partial row stride
@@ -787,7 +770,7 @@ __device__ void stream_mfma_wide(const Problem &p, int local)
     sum_partials<kR>(p.acc_ws, off, ok, (int64_t)M * ldp, p.ks, sum);
 #pragma unroll
     for (int i = 0; i < kR; ++i)
-        if (ok[i]) finish_output_with(p, gamma, mm[i], nn[i], sum[i], s_rowsum[mm[i]], s_absmax[mm[i]]);
+        if (ok[i]) finish_output_scaled(p, mm[i], nn[i], sum[i], s_rowsum[mm[i]], s_scale[mm[i]]);
 }
 
 // Instantiations: 1: MFMA stream (17..32 tokens; two tiles per wave); 3:

@@ -36,11 +36,22 @@ __device__ inline v16i mfma_i8(v4i a, v4i b, v16i c)
 // the layer replaces nn.Linear, so it returns real values).  The kernels
 // accumulate sum_k (t+1) q = acc + rowsum; the exact integer acc is
 // recovered here, then y = float(acc) * ((gamma * a) / 127) in fp32.
+__device__ inline float token_scale(float gamma, float absmax) { return (gamma * absmax) / 127.0f; }
 __device__ inline void finish_output_with(const Problem &p, float gamma, int m, int n, int32_t fields,
                                           int32_t rowsum, float absmax)
 {
     const int32_t acc = fields - rowsum;
-    const float c = (gamma * absmax) / 127.0f;
+    const float c = token_scale(gamma, absmax);
+    const int64_t o = (int64_t)m * p.N + n;
+    gstore_ptr<float>(p.Y)[o] = (float)acc * c;
+    if (p.acc_out) gstore_ptr<int32_t>(p.acc_out)[o] = acc;
+}
+
+// The same with the token's factor c = token_scale(gamma, a) computed once
+// per token by the caller (kernels that finish many outputs per token).
+__device__ inline void finish_output_scaled(const Problem &p, int m, int n, int32_t fields, int32_t rowsum, float c)
+{
+    const int32_t acc = fields - rowsum;
     const int64_t o = (int64_t)m * p.N + n;
     gstore_ptr<float>(p.Y)[o] = (float)acc * c;
     if (p.acc_out) gstore_ptr<int32_t>(p.acc_out)[o] = acc;
