@@ -158,7 +158,9 @@ __device__ __forceinline__ void tile_body(const Problem &p, int local)
                 a[i][0] = *reinterpret_cast<const v4i *>(arow);
                 a[i][1] = *reinterpret_cast<const v4i *>(arow + 32);
             }
-            const v4i b0 = planes(w[h].x), b1 = planes(w[h].y), b2 = planes(w[h].z), b3 = planes(w[h].w);
+            v4i b0, b1;
+            planes2(w[h].x, w[h].y, b0, b1);
+            const v4i b2 = planes(w[h].z), b3 = planes(w[h].w);
             if (h == UPS - 1) {
                 // every word of slot s has become planes: refill it
                 __builtin_amdgcn_sched_barrier(0);

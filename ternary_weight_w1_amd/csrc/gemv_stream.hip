@@ -594,8 +594,10 @@ __device__ void stream_mfma(const Problem &p, int local)
 #pragma unroll
                 for (int t = 0; t < TPW; ++t) {
                     const v4u wj = live ? w[slot][j][t] : zw;
-                    acc[t][0] = mfma_i8(a, planes(h ? wj.y : wj.x), acc[t][0]);
-                    acc[t][1] = mfma_i8(a, planes(h ? wj.w : wj.z), acc[t][1]);
+                    v4i b0, b1;
+                    planes2(h ? wj.y : wj.x, h ? wj.w : wj.z, b0, b1);
+                    acc[t][0] = mfma_i8(a, b0, acc[t][0]);
+                    acc[t][1] = mfma_i8(a, b1, acc[t][1]);
                 }
             }
     };

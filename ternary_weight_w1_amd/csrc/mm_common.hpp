@@ -23,6 +23,24 @@ __device__ inline v4i planes(unsigned w)
     return r;
 }
 
+// The planes of two words at once: one 64-bit shift serves both (the bits a
+// word receives from its neighbour land above bit 25 of its top byte, which
+// the mask clears), 11 operations instead of 14.
+__device__ inline void planes2(unsigned a, unsigned b, v4i &pa, v4i &pb)
+{
+    const uint64_t ab = ((uint64_t)b << 32) | a;
+    const uint64_t m = 0x0303030303030303ull;
+    const uint64_t s1 = (ab >> 2) & m, s2 = (ab >> 4) & m, s3 = (ab >> 6) & m;
+    pa.x = (int)(a & 0x03030303u);
+    pb.x = (int)(b & 0x03030303u);
+    pa.y = (int)(uint32_t)s1;
+    pb.y = (int)(uint32_t)(s1 >> 32);
+    pa.z = (int)(uint32_t)s2;
+    pb.z = (int)(uint32_t)(s2 >> 32);
+    pa.w = (int)(uint32_t)s3;
+    pb.w = (int)(uint32_t)(s3 >> 32);
+}
+
 // Streaming read of one 16-byte slot of the packed weights (read once, so
 // marked non-temporal).
 __device__ inline v4u load_packed(const BL_GLOBAL v4u *p) { return __builtin_nontemporal_load(p); }
