@@ -237,8 +237,9 @@ class ChainedStack:
     single key, so its output is v), the cast of v and o, residual add +
     RMSNorm + cast and gate|up, the gated squared-ReLU cast and down; then
     the final residual add + norm + cast.  Each cast + contraction pair is
-    one bitlinear_cast_matmul_multi call: a single launch at one token (the
-    contraction's workgroups cast their own input), two otherwise.  The
+    one bitlinear_cast_matmul_multi call: a single launch where the
+    contraction's workgroups cast their own input (q|k|v and o at one
+    token), two otherwise (`launches` counts them per step).  The
     residual stream alternates between two buffers (a call's X_out may not
     be its X).  Buffers and workspaces are allocated once (workspaces
     zero-filled once, as the multi-matrix calls require).  After step(), x
@@ -285,6 +286,13 @@ class ChainedStack:
             arr = self.sites[0][key]
             wsb = max(L.bitlinear_cast_multi_workspace_bytes(md, arr, len(arr), M, K) for md in modes)
             self.wss[key] = torch.zeros(max(wsb, 16), dtype=torch.uint8, device=dev)
+        # kernels one step enqueues, as the library's policy decides them
+        # (layer 0's q|k|v cast has no residual add), plus the final cast
+        def n(key, K, md):
+            return L.bitlinear_cast_multi_launches(md, self.sites[0][key], len(self.sites[0][key]), M, K)
+        rest = n("o", dim, B.CAST_PLAIN) + n("gu", dim, B.CAST_ADD_RMSNORM) + n("down", ffn, B.CAST_RELU2_GATE)
+        self.launches = (1 + n("qkv", dim, B.CAST_RMSNORM) + (len(layers) - 1) * n("qkv", dim, B.CAST_ADD_RMSNORM)
+                         + len(layers) * rest)
 
     def _check(self, st):
         if st != 0:
@@ -321,8 +329,7 @@ def stack_curve(B, torch, mats, dev, Ms, steps, warmup):
     n_layers = len({m["layer"] for m in mats})
     dim = next(m["K"] for m in mats if m["name"] == "q")
     ffn = next(m["N"] for m in mats if m["name"] == "gate")
-    out = {"layers": n_layers, "dim": dim, "ffn": ffn,
-           "launches_per_step": {"M=1": 4 * n_layers + 1, "M>1": 8 * n_layers + 1}, "points": []}
+    out = {"layers": n_layers, "dim": dim, "ffn": ffn, "points": []}
     for M in Ms:
         chain = ChainedStack(B, torch, mats, dev, M, *stack_inputs(torch, dim, n_layers, M, dev))
         side = torch.cuda.Stream()
@@ -349,7 +356,8 @@ def stack_curve(B, torch, mats, dev, Ms, steps, warmup):
             graph.replay()
         torch.cuda.synchronize()
         gms = (time.perf_counter() - t0) / steps * 1e3
-        out["points"].append({"M": M, "eager_ms_per_step": round(eager, 4), "graph_ms_per_step": round(gms, 4)})
+        out["points"].append({"M": M, "launches_per_step": chain.launches, "eager_ms_per_step": round(eager, 4),
+                              "graph_ms_per_step": round(gms, 4)})
         log(f"  stack M={M}: eager {eager:.3f} ms, graph {gms:.3f} ms per step")
         del graph, chain
     torch.cuda.empty_cache()

@@ -408,6 +408,16 @@ enum bitlinear_cast_mode {
 size_t bitlinear_cast_multi_workspace_bytes(int mode, const bitlinear_weight *w, int count, int64_t M, int64_t K);
 
 /*
+ * How many kernels bitlinear_cast_matmul_multi enqueues for these arguments:
+ * 1 when the contraction's workgroups cast the row themselves, 2 when the
+ * cast runs as its own kernel first (the rule is stated at that call).  Host
+ * only: nothing is enqueued and no device memory is read.  Returns -1 where
+ * bitlinear_cast_multi_workspace_bytes returns SIZE_MAX (bad mode, shapes
+ * or weights).
+ */
+int bitlinear_cast_multi_launches(int mode, const bitlinear_weight *w, int count, int64_t M, int64_t K);
+
+/*
  * The activation cast of `mode` followed by bitlinear_matmul_multi on its
  * int8 codes: a decode layer's sub-layer norm (or gated squared ReLU) and
  * the BitLinear matrices that read it, as the pages describe a BitNet block

@@ -97,6 +97,7 @@ def lib():
             "bitlinear_matmul_multi": (_int, [_vp, _i64, _vp, _vp, _i64, _i64, ctypes.POINTER(Weight), _int,
                                               _vp, _sz, _vp]),
             "bitlinear_cast_multi_workspace_bytes": (_sz, [_int, ctypes.POINTER(Weight), _int, _i64, _i64]),
+            "bitlinear_cast_multi_launches": (_int, [_int, ctypes.POINTER(Weight), _int, _i64, _i64]),
             "bitlinear_cast_matmul_multi": (_int, [_int, _vp, _vp, _vp, ctypes.c_float, _vp, _i64, _i64,
                                                    ctypes.POINTER(Weight), _int, _vp, _sz, _vp]),
             "bitlinear_group_table_bytes": (_sz, [ctypes.POINTER(Problem), _int]),

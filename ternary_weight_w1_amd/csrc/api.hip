@@ -943,11 +943,11 @@ int cast_plan(int mode, int64_t M, int64_t K, const bitlinear_weight *w, int cou
     if (int st = multi_plan(nullptr, cp.ldq, M, K, w, count, cp.mp, check_ptrs)) return st;
     // casting in every workgroup pays where each workgroup reads fewer cast
     // input bytes than packed weights and the launch has at most one
-    // workgroup per compute unit (measured per decode-layer call: q|k|v after
-    // the residual add + norm 7.9 us against 4.7 + 4.2 in two launches, o
-    // 5.4 against 3.1 + 3.8; gate|up, 270 workgroups, 11.1 against
-    // 4.7 + 5.7; down after the gated squared ReLU, 69 KiB of input per
-    // workgroup, 9.9 against 3.8 + 5.8)
+    // workgroup per compute unit (measured per 3B-class decode-layer call,
+    // graph replay: q|k|v after the residual add + norm 7.25 us against
+    // 4.31 + 3.93 in two launches, o 5.22 against 2.77 + 3.81; gate|up, 270
+    // workgroups, 10.39 against 4.31 + 5.66; down after the gated squared
+    // ReLU, 69 KiB of input per workgroup, 10.14 against 3.49 + 5.85)
     int64_t items = 0, upsplit = 0;
     for (int i = 0; i < count; ++i) {
         items += items_of(cp.mp.ps.p[i]);
@@ -977,6 +977,14 @@ size_t bitlinear_cast_multi_workspace_bytes(int mode, const bitlinear_weight *w,
     if (mode < BITLINEAR_CAST_PLAIN || mode > BITLINEAR_CAST_ADD_RMSNORM) return SIZE_MAX;
     if (cast_plan(mode, M, K, w, count, cp, false) != BITLINEAR_OK) return SIZE_MAX;
     return (size_t)cp.total;
+}
+
+int bitlinear_cast_multi_launches(int mode, const bitlinear_weight *w, int count, int64_t M, int64_t K)
+{
+    CastPlan cp;
+    if (mode < BITLINEAR_CAST_PLAIN || mode > BITLINEAR_CAST_ADD_RMSNORM) return -1;
+    if (cast_plan(mode, M, K, w, count, cp, false) != BITLINEAR_OK) return -1;
+    return cp.fused ? 1 : 2;
 }
 
 int bitlinear_cast_matmul_multi(int mode, const float *X, const float *aux, const float *R, float eps,

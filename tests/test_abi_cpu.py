@@ -37,7 +37,7 @@ def test_every_header_is_checked():
 
 def test_every_declared_symbol_is_exported():
     names = _declared()
-    assert len(names) == 39, names
+    assert len(names) == 40, names
     out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r"\bT (bitlinear_\w+)", out))
@@ -381,6 +381,11 @@ def test_cast_matmul_multi_validation():
     assert L.bitlinear_cast_multi_workspace_bytes(2, down, 1, 1, 8640) > L.bitlinear_multi_workspace_bytes(down, 1, 1, 8640)
     assert L.bitlinear_cast_multi_workspace_bytes(0, w, 0, 1, 3200) == smax
     assert L.bitlinear_cast_multi_workspace_bytes(4, w, 3, 1, 3200) == smax
+    # the launch count follows the same rule
+    n = L.bitlinear_cast_multi_launches
+    assert (n(3, w, 3, 1, 3200), n(0, _weights([3200]), 1, 1, 3200), n(3, w, 3, 8, 3200)) == (1, 1, 2)
+    assert (n(3, gu, 2, 1, 3200), n(2, down, 1, 1, 8640)) == (2, 2)
+    assert (n(0, w, 0, 1, 3200), n(4, w, 3, 1, 3200), n(0, w, 3, 0, 3200)) == (-1, -1, -1)
     cm = L.bitlinear_cast_matmul_multi
     X, R, Xo = FAKE, FAKE + (1 << 20), FAKE + (2 << 20)
     assert cm(4, X, None, None, 0.0, None, 1, 3200, w, 3, None, 0, None) == -6            # mode
