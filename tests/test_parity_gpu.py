@@ -810,8 +810,10 @@ plan.forward(); torch.cuda.synchronize()
 for p, ref in zip(probs, refs):
     assert np.array_equal(p["acc"].cpu().numpy(), ref["acc"]) and np.array_equal(p["Y"].cpu().numpy(), ref["Y"]), "group"
 # cast + multi-matrix calls at one token (plain and residual add + RMSNorm,
-# 270 row tiles and one) and at five tokens
-for M, K, Ns, mode in [(1, 3200, (8640, 8640), 3), (1, 640, (100,), 0), (5, 640, (257, 64), 3)]:
+# 270 row tiles and one; K = 8192 splits K, cast inside the contraction only
+# when every workgroup casts regardless) and at five tokens
+for M, K, Ns, mode in [(1, 3200, (8640, 8640), 3), (1, 640, (100,), 0), (5, 640, (257, 64), 3),
+                       (1, 8192, (64,), 0)]:
     X = synth.activations_np(M, K, seed=500 + K); R = synth.activations_np(M, K, seed=501 + K)
     if mode == 3:
         Q, a, rs, S, _, _ = O.add_rmsnorm_quant_act(X, R, None, 1e-5)
