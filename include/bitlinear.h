@@ -263,7 +263,7 @@ int bitlinear_quant_act_relu2_gate(const float *G, const float *U, int64_t M, in
 /*
  * Ternary x int8 contraction and rescale from already-quantized activations
  * (lets a caller supply Q, a and the row sums itself).
- *   Q       [in]  M rows of ldq bytes, ldq >= bitlinear_q_stride(K),
+ *   Q       [in]  M rows of ldq bytes, bitlinear_q_stride(K) <= ldq <= 2^26,
  *                 ldq % 16 == 0; bytes K..ldq-1 of each row must be 0.
  *   absmax  [in]  M fp32 activation scales.
  *   rowsum  [in]  M int32, rowsum[m] = sum_k Q[m,k].

@@ -657,8 +657,9 @@ int bitlinear_matmul(const int8_t *Q, int64_t ldq, const float *absmax, const in
     if (!Q || !absmax || !rowsum || !P || !gamma || !Y_out)
         return fail(BITLINEAR_ERR_NULL, "matmul: Q, absmax, rowsum, P, gamma and Y_out are required");
     if (int st = check_mnk(M, N, K)) return st;
-    if (ldq < up(K, 64) || ldq % 16 != 0)
-        return fail(BITLINEAR_ERR_SHAPE, "matmul: ldq=%lld must be >= %lld and a multiple of 16", (long long)ldq, (long long)up(K, 64));
+    if (ldq < up(K, 64) || ldq % 16 != 0 || ldq > (int64_t(1) << 26))
+        return fail(BITLINEAR_ERR_SHAPE, "matmul: ldq=%lld must be in [%lld, 2^26] and a multiple of 16", (long long)ldq,
+                    (long long)up(K, 64));
     if (!a16(Q) || !a16(P) || !a16(Y_out) || (acc_out && !a16(acc_out)) || !a4(absmax) || !a4(rowsum) || !a4(gamma))
         return fail(BITLINEAR_ERR_ALIGN, "matmul: arrays need 16-byte, scalars 4-byte alignment");
     Problem p = make_problem(M, N, K);

@@ -55,23 +55,4 @@ __device__ __forceinline__ Bt5Planes bt5_planes(unsigned w)
     return r;
 }
 
-// Wave-uniform copy of a value every lane holds (problem fields read from
-// the plan table arrive in vector registers); buffer resources and scalar
-// offsets must live in scalar registers.
-__device__ __forceinline__ int bt5_uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
-__device__ __forceinline__ const void *bt5_uni(const void *p)
-{
-    const uint64_t a = reinterpret_cast<uint64_t>(p);
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
-    return reinterpret_cast<const void *>(((uint64_t)hi << 32) | lo);
-}
-
-// Buffer resource over `bytes` bytes at p (both wave-uniform): raw
-// (unstrided) loads whose per-lane offset reaches past `bytes` return zeros.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t bt5_rsrc(const void *p, int bytes)
-{
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, bytes, 0x00020000);
-}
-
 }  // namespace bl

@@ -24,6 +24,28 @@ __device__ inline BL_GLOBAL T *gstore_ptr(void *p)
     return (BL_GLOBAL T *)p;
 }
 
+// Wave-uniform copy of a value every lane holds (problem fields read from
+// a plan table can arrive in vector registers); buffer resources and scalar
+// offsets must live in scalar registers.
+__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+template <typename T>
+__device__ __forceinline__ T *uni(T *p)
+{
+    const uint64_t a = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
+    return reinterpret_cast<T *>(((uint64_t)hi << 32) | lo);
+}
+
+// Buffer resource over `bytes` bytes at p (both wave-uniform; 32-bit data
+// format, unstrided).  A raw access whose lane offset reaches past `bytes`
+// reads zeros (a store is dropped); bytes = 0 makes every access miss, and
+// -1 admits every offset below 2^32.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *p, int bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, bytes, 0x00020000);
+}
+
 // int8 code of one activation: clamp(rint(x * s), -127, 127) with s = 127 / a
 // computed once per token (anthology note-168 on arXiv 2402.17764, "What it
 // does": 8-bit activations; per-token absmax scaling is the reading taken).

@@ -20,6 +20,8 @@
 // Global loads run two stages ahead of the MFMAs through register rings.
 // Four workgroups share a CU (126 VGPRs, about 37 KiB of LDS each), so
 // while one stages or stores, three keep the matrix cores busy.
+#include <type_traits>
+
 #include "mm_common.hpp"
 
 namespace bl {
@@ -27,6 +29,8 @@ namespace {
 
 constexpr int kThreads = 256;
 typedef float v4f_t __attribute__((ext_vector_type(4)));
+// cache-policy operand of a buffer access that marks it non-temporal (nt)
+constexpr int kNonTemporal = 2;
 // floats per LDS row of the epilogue transpose: the rescaled outputs go
 // through LDS, 32 rows at a time per wave, so that Y is written with
 // 16-byte stores covering whole 256-byte row pieces.  Output stores are
@@ -71,36 +75,47 @@ __device__ __forceinline__ void tile_body(const Problem &p, int local)
     __shared__ __attribute__((aligned(16))) int8_t smem[kSmem];
     int8_t (*As)[kStageBytes] = reinterpret_cast<int8_t (*)[kStageBytes]>(smem);
     __shared__ float cs[BM];
-    __shared__ int rsum[BM];
+    __shared__ __attribute__((aligned(16))) int nrsum[BM];
 
-    const int split = local % p.ks;
-    const int item = local / p.ks;
-    const int mtile = item % p.mt;
-    const int nt = item / p.mt;
+    const int ks = uni(p.ks), mt = uni(p.mt), NT = uni(p.NT), M = uni(p.M), N = uni(p.N);
+    const int ldq = uni((int)p.ldq);  // at most 2^26: 64 rows stay below 2^32 bytes
+    const int split = local % ks;
+    const int item = local / ks;
+    const int mtile = item % mt;
+    const int nt = item / mt;
     const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63, g = lane >> 5, r = lane & 31;
+    const int wave = uni(tid >> 6), lane = tid & 63, g = lane >> 5, r = lane & 31;
     const int m0 = mtile * BM;
-    const int KU = p.KU;
-    const int ub = split * p.upsplit;           // first unit of the split
-    const int nu = min(KU, ub + p.upsplit) - ub;  // its units
+    const int KU = uni(p.KU);
+    const int ub = split * uni(p.upsplit);           // first unit of the split
+    const int nu = min(KU, ub + uni(p.upsplit)) - ub;  // its units
     const int KS = (nu + UPS - 1) / UPS;
     const int tile = 4 * nt + wave;
-    const bool tv = tile < p.NT;
-    const BL_GLOBAL v4u *blk = gload_ptr<v4u>(p.P + (int64_t)min(tile, p.NT - 1) * KU * kBlockBytes) + lane;
+    const bool tv = tile < NT;
+    // this wave's 64-row tile over the split's units, read through a buffer
+    // resource of exactly those bytes; a unit past them is read through a
+    // resource of none, which returns the all-zero word (zero fields add
+    // nothing), so odd unit counts and the loads run ahead of the last
+    // stage need no selects
+    const uint8_t *wp = uni(p.P) + ((int64_t)min(tile, NT - 1) * KU + ub) * kBlockBytes;
+    const __amdgpu_buffer_rsrc_t rw = buffer_rsrc(wp, nu * kBlockBytes), rz = buffer_rsrc(wp, 0);
+    const int woff = 16 * lane;
+    // the work item's activation rows; every offset stays in them (rows past
+    // M re-read row M-1, units past the split re-read its last unit)
+    const __amdgpu_buffer_rsrc_t rq = buffer_rsrc(uni(p.Q) + (int64_t)m0 * ldq, -1);
 
     // 16-byte chunk c of a unit: column c % 4 of token row ((c / 16) % 4) +
     // 4 ((c / 4) % 4) + 16 (c / 64): four consecutive lanes read one
     // contiguous 64-byte row piece, a wave reads 16 whole row pieces, and
     // each 16-lane group of the LDS writes covers rows r, r+4, r+8, r+12
     // (rows past M re-read row M-1; their results are never stored)
-    const BL_GLOBAL int8_t *asrc[CH];
+    int aoff[CH];
     int adst[CH];
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
         const int c = tid + kThreads * i;
         const int row = ((c >> 4) & 3) + 4 * ((c >> 2) & 3) + 16 * (c >> 6), col = c & 3;
-        const int m = min(m0 + row, p.M - 1);
-        asrc[i] = gload_ptr<int8_t>(p.Q + (int64_t)m * p.ldq + 16 * col);
+        aoff[i] = (min(m0 + row, M - 1) - m0) * ldq + 16 * col;
         adst[i] = row * kRow + 16 * col;
     }
 
@@ -114,8 +129,9 @@ __device__ __forceinline__ void tile_body(const Problem &p, int local)
             const int u = st * UPS + h;
             const int uc = ub + min(u, nu - 1);
 #pragma unroll
-            for (int i = 0; i < CH; ++i) ar[slot][h][i] = *reinterpret_cast<const BL_GLOBAL v4i *>(asrc[i] + 64 * uc);
-            br[slot][h] = blk[(int64_t)uc * 64];
+            for (int i = 0; i < CH; ++i)
+                ar[slot][h][i] = (v4i)__builtin_amdgcn_raw_buffer_load_b128(rq, aoff[i], 64 * uc, 0);
+            br[slot][h] = __builtin_amdgcn_raw_buffer_load_b128(u < nu ? rw : rz, woff, u * kBlockBytes, 0);
         }
     };
     auto stage_lds = [&](int buf, int slot) {
@@ -130,24 +146,35 @@ __device__ __forceinline__ void tile_body(const Problem &p, int local)
     // first stages, so the two memory round trips overlap
     __builtin_amdgcn_sched_barrier(0);
     if (tid < BM) {
-        const int m = min(m0 + tid, p.M - 1);
-        cs[tid] = (*gload_ptr<float>(p.gamma) * gload_ptr<float>(p.absmax)[m]) / 127.0f;
-        rsum[tid] = gload_ptr<int32_t>(p.rowsum)[m];
+        const int m = min(m0 + tid, M - 1);
+        cs[tid] = token_scale(*gload_ptr<float>(p.gamma), gload_ptr<float>(p.absmax)[m]);
+        nrsum[tid] = -gload_ptr<int32_t>(p.rowsum)[m];
     }
     stage_lds(0, 0);
     __syncthreads();
 
+    // the accumulators start at minus the token's row sum (in the first K
+    // split only), so they end as sum (t + 1) q - sum q = sum t q
     v16i acc[WMS][2];
 #pragma unroll
     for (int i = 0; i < WMS; ++i) acc[i][0] = acc[i][1] = (v16i){};
+    if (split == 0) {
+#pragma unroll
+        for (int i = 0; i < WMS; ++i)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const v4i n4 = *reinterpret_cast<const v4i *>(&nrsum[32 * i + 8 * q + 4 * g]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[i][0][4 * q + e] = acc[i][1][4 * q + e] = n4[e];
+            }
+    }
 
     auto step = [&](int s, int st) {
         __builtin_amdgcn_sched_barrier(0);
         const int buf = st & 1;
         v4u w[UPS];
-        const v4u z = {0u, 0u, 0u, 0u};
 #pragma unroll
-        for (int h = 0; h < UPS; ++h) w[h] = st * UPS + h < nu ? br[s][h] : z;
+        for (int h = 0; h < UPS; ++h) w[h] = br[s][h];
         const int8_t *abase = &As[buf][r * kRow + 16 * g];
 #pragma unroll
         for (int h = 0; h < UPS; ++h) {
@@ -158,9 +185,9 @@ __device__ __forceinline__ void tile_body(const Problem &p, int local)
                 a[i][0] = *reinterpret_cast<const v4i *>(arow);
                 a[i][1] = *reinterpret_cast<const v4i *>(arow + 32);
             }
-            v4i b0, b1;
+            v4i b0, b1, b2, b3;
             planes2(w[h].x, w[h].y, b0, b1);
-            const v4i b2 = planes(w[h].z), b3 = planes(w[h].w);
+            planes2(w[h].z, w[h].w, b2, b3);
             if (h == UPS - 1) {
                 // every word of slot s has become planes: refill it
                 __builtin_amdgcn_sched_barrier(0);
@@ -190,9 +217,9 @@ __device__ __forceinline__ void tile_body(const Problem &p, int local)
         if (s0 + s < KS) step(s, s0 + s);
 
     {
-        if (p.ks > 1) {
+        if (ks > 1) {
             constexpr int kAcc = 32 * WMS;  // accumulators per thread
-            int32_t *part = p.acc_ws + (int64_t)item * p.ks * (kAcc * kThreads);
+            int32_t *part = p.acc_ws + (int64_t)item * ks * (kAcc * kThreads);
 #pragma unroll
             for (int i = 0; i < WMS; ++i)
 #pragma unroll
@@ -202,7 +229,7 @@ __device__ __forceinline__ void tile_body(const Problem &p, int local)
                         put_partial(part + ((int64_t)split * kAcc + (i * 2 + s2) * 16 + e) * kThreads + tid,
                                     acc[i][s2][e]);
             if (!arrive_last(p, item)) return;
-            for (int j = 0; j < p.ks; ++j) {
+            for (int j = 0; j < ks; ++j) {
                 if (j == split) continue;
 #pragma unroll
                 for (int i = 0; i < WMS; ++i)
@@ -219,53 +246,70 @@ __device__ __forceinline__ void tile_body(const Problem &p, int local)
         }
     }
 
-    // epilogue: rescale, transpose through LDS, 16-byte non-temporal stores
+    // epilogue: rescale, transpose through LDS, 16-byte non-temporal stores.
+    // A wave whose 64 x 64 block lies wholly inside Y (N a multiple of 4)
+    // stores through a buffer resource at scalar row offsets: no per-row
+    // bounds tests or address arithmetic in vector registers
     __syncthreads();  // every wave is done with the activation stages
     float *ep = reinterpret_cast<float *>(smem) + wave * (32 * kEpiStride);
-    const bool vec_ok = (p.N & 3) == 0;
+    const bool vec_ok = (N & 3) == 0;
+    const bool interior = tv && vec_ok && m0 + BM <= M && 64 * tile + 64 <= N && N <= (1 << 23);
     BL_GLOBAL float *Y = gstore_ptr<float>(p.Y);
+    float *yp = uni(p.Y) + (int64_t)m0 * N;
+    const __amdgpu_buffer_rsrc_t ry = buffer_rsrc(yp, -1);
+    const int yoff = 4 * ((lane >> 4) * N + 64 * tile + 4 * (lane & 15));
+    auto epilogue = [&](auto whole) {
 #pragma unroll
-    for (int i = 0; i < WMS; ++i) {
+        for (int i = 0; i < WMS; ++i) {
 #pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2)
+            for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int row = 8 * (e >> 2) + 4 * g + (e & 3);
-                const int rr = 32 * i + row;
-                ep[row * kEpiStride + 32 * s2 + r] = (float)(acc[i][s2][e] - rsum[rr]) * cs[rr];
-            }
+                for (int e = 0; e < 16; ++e) {
+                    const int row = 8 * (e >> 2) + 4 * g + (e & 3);
+                    ep[row * kEpiStride + 32 * s2 + r] = (float)acc[i][s2][e] * cs[32 * i + row];
+                }
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            const int row = (lane >> 4) + 4 * k;
-            const int c4 = 4 * (lane & 15);
-            const int m = m0 + 32 * i + row;
-            const int n = 64 * tile + c4;
-            const v4f_t v = *reinterpret_cast<const v4f_t *>(&ep[row * kEpiStride + c4]);
-            if (tv && m < p.M) {
-                const int64_t o = (int64_t)m * p.N + n;
-                if (vec_ok && n + 3 < p.N) {
-                    __builtin_nontemporal_store(v, reinterpret_cast<BL_GLOBAL v4f_t *>(Y + o));
+            for (int k = 0; k < 8; ++k) {
+                const int row = (lane >> 4) + 4 * k;
+                const int c4 = 4 * (lane & 15);
+                const v4f_t v = *reinterpret_cast<const v4f_t *>(&ep[row * kEpiStride + c4]);
+                if constexpr (decltype(whole)::value) {
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, v), ry, yoff,
+                                                           4 * (32 * i + 4 * k) * N, kNonTemporal);
                 } else {
-                    if (n < p.N) __builtin_nontemporal_store(v.x, Y + o);
-                    if (n + 1 < p.N) __builtin_nontemporal_store(v.y, Y + o + 1);
-                    if (n + 2 < p.N) __builtin_nontemporal_store(v.z, Y + o + 2);
-                    if (n + 3 < p.N) __builtin_nontemporal_store(v.w, Y + o + 3);
+                    const int m = m0 + 32 * i + row;
+                    const int n = 64 * tile + c4;
+                    if (tv && m < M) {
+                        const int64_t o = (int64_t)m * N + n;
+                        if (vec_ok && n + 3 < N) {
+                            __builtin_nontemporal_store(v, reinterpret_cast<BL_GLOBAL v4f_t *>(Y + o));
+                        } else {
+                            if (n < N) __builtin_nontemporal_store(v.x, Y + o);
+                            if (n + 1 < N) __builtin_nontemporal_store(v.y, Y + o + 1);
+                            if (n + 2 < N) __builtin_nontemporal_store(v.z, Y + o + 2);
+                            if (n + 3 < N) __builtin_nontemporal_store(v.w, Y + o + 3);
+                        }
+                    }
                 }
             }
         }
-    }
+    };
+    if (interior)
+        epilogue(std::true_type{});
+    else
+        epilogue(std::false_type{});
     if (p.acc_out && tv) {
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
             const int n = 64 * tile + 32 * s2 + r;
-            if (n >= p.N) continue;
+            if (n >= N) continue;
 #pragma unroll
             for (int i = 0; i < WMS; ++i)
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
                     const int row = 32 * i + 8 * (e >> 2) + 4 * g + (e & 3);
                     const int m = m0 + row;
-                    if (m < p.M) gstore_ptr<int32_t>(p.acc_out)[(int64_t)m * p.N + n] = acc[i][s2][e] - rsum[row];
+                    if (m < M) gstore_ptr<int32_t>(p.acc_out)[(int64_t)m * N + n] = acc[i][s2][e];
                 }
         }
     }

@@ -55,18 +55,18 @@ __device__ __forceinline__ void bt5_body(const Problem &p, int local)
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     // problem fields as wave-uniform values (they feed buffer resources and
     // scalar offsets)
-    const int ks = bt5_uni(p.ks), ntt = bt5_uni(p.ntt), NT = bt5_uni(p.NT), KU5 = bt5_uni(p.KU5);
-    const int M = bt5_uni(p.M), ldq = bt5_uni((int)p.ldq);
-    const int split = bt5_uni(local % ks);
-    const int rest = bt5_uni(local / ks);
+    const int ks = uni(p.ks), ntt = uni(p.ntt), NT = uni(p.NT), KU5 = uni(p.KU5);
+    const int M = uni(p.M), ldq = uni((int)p.ldq);
+    const int split = uni(local % ks);
+    const int rest = uni(local / ks);
     const int grp = rest % ntt;
     const int tg = rest / ntt;
-    const int tile = bt5_uni(4 * grp + wave);
+    const int tile = uni(4 * grp + wave);
     const bool tv = tile < NT;
-    const int u0 = bt5_uni(split * p.upsplit);
-    const int u1 = bt5_uni(min(KU5, u0 + p.upsplit));
+    const int u0 = uni(split * p.upsplit);
+    const int u1 = uni(min(KU5, u0 + p.upsplit));
     const int m0 = tg * kBt5Tokens;
-    const int mg = bt5_uni(min(kBt5Tokens, M - m0));
+    const int mg = uni(min(kBt5Tokens, M - m0));
     const int c = lane >> 5;
 
     v16i acc;
@@ -78,11 +78,11 @@ __device__ __forceinline__ void bt5_body(const Problem &p, int local)
         constexpr int kZero = kRing * NA * 1024;
         if (lane == 0) *reinterpret_cast<v4i *>(wl + kZero) = (v4i){0, 0, 0, 0};
         const int bbytes = KU5 * kBlockBytes;
-        const uint8_t *wp = static_cast<const uint8_t *>(bt5_uni(p.P));
-        const int8_t *qp = static_cast<const int8_t *>(bt5_uni(p.Q));
-        const __amdgpu_buffer_rsrc_t rb = bt5_rsrc(wp + (int64_t)tile * KU5 * kBlockBytes, bbytes);
+        const uint8_t *wp = static_cast<const uint8_t *>(uni(p.P));
+        const int8_t *qp = static_cast<const int8_t *>(uni(p.Q));
+        const __amdgpu_buffer_rsrc_t rb = buffer_rsrc(wp + (int64_t)tile * KU5 * kBlockBytes, bbytes);
         const int qbytes = mg * ldq;
-        const __amdgpu_buffer_rsrc_t rq = bt5_rsrc(qp + (int64_t)m0 * ldq, qbytes);
+        const __amdgpu_buffer_rsrc_t rq = buffer_rsrc(qp + (int64_t)m0 * ldq, qbytes);
         // chunk i = 10 m + q (token m, 16-byte chunk q of its 160-byte unit
         // row) is loaded by lane i % 64 in load i / 64
         int coff[NA];

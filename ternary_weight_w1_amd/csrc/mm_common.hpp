@@ -88,7 +88,7 @@ __device__ inline void finish_output(const Problem &p, float gamma, int m, int n
 // writes back and invalidates the whole local L2 in every workgroup.
 __device__ inline void put_partial(int32_t *p, int32_t v)
 {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(gstore_ptr<int32_t>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ inline int32_t get_partial(const int32_t *p)
 {
@@ -138,10 +138,10 @@ __device__ inline bool arrive_last(const Problem &p, int tile)
     __builtin_amdgcn_s_waitcnt(0);  // this thread's partial stores are complete
     __syncthreads();
     if (threadIdx.x == 0) {
-        const unsigned old =
-            __hip_atomic_fetch_add(&p.tickets[tile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        BL_GLOBAL uint32_t *t = gstore_ptr<uint32_t>(p.tickets) + tile;
+        const unsigned old = __hip_atomic_fetch_add(t, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         const bool last = old == (unsigned)(p.ks - 1);
-        if (last) __hip_atomic_store(&p.tickets[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (last) __hip_atomic_store(t, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         s_last = last ? 1 : 0;
     }
     __syncthreads();

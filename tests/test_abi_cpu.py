@@ -134,8 +134,10 @@ def test_pack_quant_matmul_forward_validation():
     assert r(FAKE, FAKE, 2, 0, FAKE, 112, FAKE, FAKE, None) == -2
     assert r(FAKE, FAKE, 2, 100, FAKE, 104, FAKE, FAKE, None) == -2
     assert r(FAKE, FAKE + 4, 2, 100, FAKE, 112, FAKE, FAKE, None) == -3
-    # matmul: ldq must cover K rounded up to 64
+    # matmul: ldq must cover K rounded up to 64, and stay within 2^26
     assert _st("bitlinear_matmul", FAKE, 112, FAKE, FAKE, 2, 100, FAKE, FAKE, 64, FAKE, None,
+               None, 0, None)[0] == -2
+    assert _st("bitlinear_matmul", FAKE, (1 << 26) + 16, FAKE, FAKE, 2, 100, FAKE, FAKE, 64, FAKE, None,
                None, 0, None)[0] == -2
     assert _st("bitlinear_matmul", None, 128, FAKE, FAKE, 2, 100, FAKE, FAKE, 64, FAKE, None,
                None, 0, None)[0] == -1
