@@ -119,7 +119,7 @@ bool mfma32_stream(int64_t M) { return M <= kStreamMaxM && M > bl::kDot4MaxToken
 // win there (70B M = 16: 3.69 ms, against 3.97 ms staged).
 constexpr int kAldsMaxTokens = 16;
 constexpr int64_t kAldsMaxSplits = 3;
-int64_t alds_max_units(int64_t M) { return (kStreamLdsMax - 16) / (80 * M); }
+int64_t alds_max_units(int64_t M) { return kStreamLdsMax / (80 * M); }
 bool alds_for(int64_t maxM) { return maxM > bl::kDot4MaxTokens && maxM <= kAldsMaxTokens; }
 bool alds_fits(int64_t M, int64_t K)
 {
@@ -145,13 +145,13 @@ int mfma_tiles_for(int64_t groups)
 constexpr int64_t kWideSlots = 512;
 // With 2..16 tokens (the MFMA stream) a split also holds at most what fits
 // 64 KiB of LDS with the kernel's own 512 bytes: staged activations (80
-// bytes per token per unit and a 16-byte zero chunk); the waves' sums
-// (8 * M * 256 bytes) reuse that space.
+// bytes per token per unit); the waves' sums (8 * M * 256 bytes) reuse
+// that space.
 constexpr int64_t kWideMaxTokens = 16;
 int64_t wide_units(int64_t M)
 {
     const int64_t u = (int64_t)bl::kWideWaves * bl::kWideUnits;
-    return M == 1 ? u : std::min<int64_t>(u, (65536 - 512 - 16) / (80 * M));
+    return M == 1 ? u : std::min<int64_t>(u, (65536 - 512) / (80 * M));
 }
 // A K range longer than a workgroup holds is split into parts of about
 // kWideSplitUnits units: a split costs a hand-off through memory (about
@@ -342,8 +342,8 @@ int stream_variant_for(int64_t M, int64_t upsplit)
 int64_t stream_lds_need(int variant, int64_t M, int64_t upsplit)
 {
     if (variant == 1 || variant == 9) return 0;
-    if (variant == 10) return 80 * M * upsplit + 16;
-    if (variant == 13) return std::max<int64_t>(80 * M * upsplit + 16, 8 * M * 256);
+    if (variant == 10) return 80 * M * upsplit;
+    if (variant == 13) return std::max<int64_t>(80 * M * upsplit, 8 * M * 256);
     if (variant == 5) return 1024 * upsplit;
     const int64_t slots = (variant == 6 && M > 1) ? bl::kDot4MaxTokens : 1;
     return 64 * slots * upsplit;
@@ -1076,28 +1076,47 @@ struct GroupPlan {
     int64_t items_s = 0, items_t = 0, items_5 = 0;  // logical work items before XCD padding
 };
 
+// Units of K that work item j of problem p streams (every kernel numbers
+// the K splits of an item consecutively: split = j % ks).
+int64_t item_units(const Problem &p, int64_t j)
+{
+    const int64_t ku = p.kind == 2 ? p.KU5 : p.KU, split = j % p.ks;
+    return std::min<int64_t>(ku, (split + 1) * p.upsplit) - split * p.upsplit;
+}
+
 // Work-item map of one kernel: logical items in problem order; with
 // xcd = true, workgroup b takes logical item (b % 8) * per + b / 8, so each
-// of the eight XCDs walks a contiguous slice of the list.
+// of the eight XCDs walks a contiguous slice of the list.  With
+// longest_first, items run longest first within a slice (the whole list
+// without xcd), stably: a slice that ended on its longest items (a stack's
+// down projections, K 2.7 times the others') would leave its compute units
+// idle while the last of them ran.  The streaming kernels take it (few
+// rounds of workgroups: the 2B decode sweep at one token 85.8 -> 83.3 us,
+// at eight tokens 110.6 -> 103.4); the tile kernel does not (some 24
+// rounds, and the 2B prefill sweep 0.917 -> 0.934 ms with it).
 void fill_map(const std::vector<Problem> &probs, int kind, int64_t logical, int64_t slots,
-              bool xcd, uint32_t *map)
+              bool xcd, bool longest_first, uint32_t *map)
 {
-    std::vector<uint32_t> pi, li;
-    pi.reserve(logical);
-    li.reserve(logical);
+    struct It {
+        uint32_t p, j;
+        int64_t units;
+    };
+    std::vector<It> it;
+    it.reserve(logical);
     for (size_t i = 0; i < probs.size(); ++i) {
         if (probs[i].kind != kind) continue;
         const int64_t n = items_of(probs[i]);
-        for (int64_t j = 0; j < n; ++j) {
-            pi.push_back((uint32_t)i);
-            li.push_back((uint32_t)j);
-        }
+        for (int64_t j = 0; j < n; ++j) it.push_back({(uint32_t)i, (uint32_t)j, item_units(probs[i], j)});
     }
     const int64_t per = xcd ? slots / 8 : slots;
+    for (int64_t b0 = 0; longest_first && b0 < logical; b0 += per) {
+        const int64_t b1 = std::min<int64_t>(logical, b0 + per);
+        std::stable_sort(it.begin() + b0, it.begin() + b1, [](const It &a, const It &b) { return a.units > b.units; });
+    }
     for (int64_t b = 0; b < slots; ++b) {
         const int64_t j = xcd ? (b % 8) * per + b / 8 : b;
-        map[2 * b] = j < logical ? pi[j] : 0xFFFFFFFFu;
-        map[2 * b + 1] = j < logical ? li[j] : 0u;
+        map[2 * b] = j < logical ? it[j].p : 0xFFFFFFFFu;
+        map[2 * b + 1] = j < logical ? it[j].j : 0u;
     }
 }
 
@@ -1312,11 +1331,11 @@ int bitlinear_group_plan(const bitlinear_problem *probs, int count, void *ws, si
         if (p.tok_begin >= 0)
             for (int m = 0; m < p.M; ++m) tok[p.tok_begin + m] = (uint32_t)i;
     }
-    fill_map(g.probs, 0, g.items_s, g.h.n_items_stream, knobs().xcd_order & 1,
+    fill_map(g.probs, 0, g.items_s, g.h.n_items_stream, knobs().xcd_order & 1, true,
              reinterpret_cast<uint32_t *>(t + g.h.off_stream_map));
-    fill_map(g.probs, 1, g.items_t, g.h.n_items_tile, (knobs().xcd_order & 2) != 0,
+    fill_map(g.probs, 1, g.items_t, g.h.n_items_tile, (knobs().xcd_order & 2) != 0, false,
              reinterpret_cast<uint32_t *>(t + g.h.off_tile_map));
-    fill_map(g.probs, 2, g.items_5, g.h.n_items_bt5, knobs().xcd_order & 1,
+    fill_map(g.probs, 2, g.items_5, g.h.n_items_bt5, knobs().xcd_order & 1, true,
              reinterpret_cast<uint32_t *>(t + g.h.off_bt5_map));
     return BITLINEAR_OK;
 }

@@ -37,6 +37,9 @@ __device__ __forceinline__ T *uni(T *p)
     return reinterpret_cast<T *>(((uint64_t)hi << 32) | lo);
 }
 
+// cache-policy operand of a buffer access that marks it non-temporal (nt)
+constexpr int kNonTemporal = 2;
+
 // Buffer resource over `bytes` bytes at p (both wave-uniform; 32-bit data
 // format, unstrided).  A raw access whose lane offset reaches past `bytes`
 // reads zeros (a store is dropped); bytes = 0 makes every access miss, and

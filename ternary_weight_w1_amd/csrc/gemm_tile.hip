@@ -29,8 +29,6 @@ namespace {
 
 constexpr int kThreads = 256;
 typedef float v4f_t __attribute__((ext_vector_type(4)));
-// cache-policy operand of a buffer access that marks it non-temporal (nt)
-constexpr int kNonTemporal = 2;
 // floats per LDS row of the epilogue transpose: the rescaled outputs go
 // through LDS, 32 rows at a time per wave, so that Y is written with
 // 16-byte stores covering whole 256-byte row pieces.  Output stores are

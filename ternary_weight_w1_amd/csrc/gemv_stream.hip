@@ -467,14 +467,14 @@ __device__ __forceinline__ void stream_dot4_tokens(const Problem &p, int local)
 // the four waves fetch that fragment at about the same time (one L2 read,
 // three L1 hits), and each wave ends with complete sums -- no cross-wave
 // reduction, no LDS, no barrier.  Loads run one group of UNROLL units ahead
-// of the MFMAs through a two-slot register ring (branch-free: unit indices
-// clamp to the range end and surplus units get zero weights, which add
-// nothing).
+// of the MFMAs through a two-slot register ring (branch-free: activation
+// unit indices clamp to the range end, and surplus units read zero weights
+// through an empty buffer resource, which add nothing).
 // ALDS: the activations of the workgroup's K range are staged once in LDS
 // (row-major, at most 16 tokens): token m's 64 bytes of unit u at byte
-// ((u - u0) * M + m) * kTokStride, 16 zero bytes after the last; each wave
-// reads its A operands with ds_read_b128 (lanes of rows past M read the zero
-// chunk) instead of two global loads per unit.
+// ((u - u0) * M + m) * kTokStride; each wave reads its A operands with
+// ds_read_b128 (lanes of rows past M read row M-1, whose sums in those
+// rows are never stored) instead of two global loads per unit.
 constexpr int kTokStride = 80;  // 64 bytes + 16: 16 rows at one column hit distinct bank groups
 
 // Stages units [0, n_units) of the K range at q (the first M token rows,
@@ -505,44 +505,43 @@ __device__ __forceinline__ void stage_rows(const BL_GLOBAL int8_t *q, int64_t ld
 template <int UNROLL, int TPW, bool ALDS = false>
 __device__ void stream_mfma(const Problem &p, int local)
 {
-    const int grp = local / p.ks, split = local - grp * p.ks;
-    const int u0 = split * p.upsplit;
-    const int u1 = min(p.KU, u0 + p.upsplit);
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int ks = uni(p.ks), KU = uni(p.KU), NT = uni(p.NT), M = uni(p.M);
+    const int grp = local / ks, split = local - grp * ks;
+    const int u0 = split * uni(p.upsplit);
+    const int u1 = min(KU, u0 + uni(p.upsplit));
+    const int n_units = u1 - u0;
+    const int wave = uni(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63, g = lane >> 5, r = lane & 31;
     const int tile0 = 4 * TPW * grp + TPW * wave;
-    // tiles past NT stream tile NT-1 (valid memory); their sums are dropped
-    const BL_GLOBAL v4u *blk[TPW];
+    // Each tile's units of the range are read through a buffer resource of
+    // exactly those bytes, and a unit past the range through a resource of
+    // none, which returns the all-zero word: zero fields add nothing, so the
+    // loop needs no selects.  Tiles past NT stream tile NT-1 (valid memory);
+    // their sums are dropped.
+    __amdgpu_buffer_rsrc_t rw[TPW];
+    const __amdgpu_buffer_rsrc_t rz = buffer_rsrc(uni(p.P), 0);
 #pragma unroll
     for (int t = 0; t < TPW; ++t)
-        blk[t] = gload_ptr<v4u>(p.P + (int64_t)min(tile0 + t, p.NT - 1) * p.KU * kBlockBytes) + lane;
+        rw[t] = buffer_rsrc(uni(p.P) + ((int64_t)min(tile0 + t, NT - 1) * KU + u0) * kBlockBytes, n_units * kBlockBytes);
+    const int woff = 16 * lane;
     // A operand of unit u, half h: fragment-ordered activations hold it as one
     // contiguous 1 KiB block (16 bytes per lane); row-major activations give
-    // each lane 16 bytes of its token row (lanes of rows past M load nothing).
-    const bool rv = p.qtiled || r < p.M;
-    const BL_GLOBAL int8_t *qbase;
-    int64_t ustride, hoff;
-    if (p.qtiled) {
-        qbase = gload_ptr<int8_t>(p.Q) + 16 * lane;
-        ustride = 2048;
-        hoff = 1024;
-    } else {
-        qbase = gload_ptr<int8_t>(p.Q) + (int64_t)min(r, p.M - 1) * p.ldq + 16 * g;
-        ustride = 64;
-        hoff = 32;
-    }
-    const v4i zero = {0, 0, 0, 0};
-    const v4u zw = {0u, 0u, 0u, 0u};
+    // each lane 16 bytes of its token row.  Lanes of rows past M read row
+    // M-1: an A row only feeds the same output row, which is never stored.
+    const __amdgpu_buffer_rsrc_t rq = buffer_rsrc(uni(p.Q), -1);
+    const int qtiled = uni(p.qtiled);
+    const int ldq = uni((int)p.ldq);
+    const int qlane = qtiled ? 16 * lane : min(r, M - 1) * ldq + 16 * g;
+    const int ustride = qtiled ? 2048 : 64, hoff = qtiled ? 1024 : 32;
     // the tokens' row sums and rescale factors, fetched now so that their
     // latency hides under the stream (read per output element at the end)
     __shared__ int s_rowsum[kStreamMaxTokens];
     __shared__ float s_scale[kStreamMaxTokens];
-    if (threadIdx.x < p.M) {
+    if (threadIdx.x < M) {
         s_rowsum[threadIdx.x] = gload_ptr<int32_t>(p.rowsum)[threadIdx.x];
         s_scale[threadIdx.x] = token_scale(*p.gamma, gload_ptr<float>(p.absmax)[threadIdx.x]);
     }
 
-    const int n_units = u1 - u0;
     const int groups = (n_units + UNROLL - 1) / UNROLL;
     int a_lane = 0;  // this lane's byte offset within a staged unit (ALDS)
     v4u w[2][UNROLL][TPW];
@@ -550,13 +549,15 @@ __device__ void stream_mfma(const Problem &p, int local)
     auto load_group = [&](int slot, int i) {
 #pragma unroll
         for (int j = 0; j < UNROLL; ++j) {
-            const int u = min(u0 + UNROLL * i + j, u1 - 1);
+            const int ur = UNROLL * i + j;  // unit within the range
 #pragma unroll
-            for (int t = 0; t < TPW; ++t) w[slot][j][t] = load_packed(blk[t] + (int64_t)u * 64);
+            for (int t = 0; t < TPW; ++t)
+                w[slot][j][t] = __builtin_amdgcn_raw_buffer_load_b128(ur < n_units ? rw[t] : rz, woff,
+                                                                      ur * kBlockBytes, kNonTemporal);
             if constexpr (!ALDS) {
-                const BL_GLOBAL int8_t *qu = qbase + ustride * u;
-                qa[slot][j] = rv ? *reinterpret_cast<const BL_GLOBAL v4i *>(qu) : zero;
-                qb[slot][j] = rv ? *reinterpret_cast<const BL_GLOBAL v4i *>(qu + hoff) : zero;
+                const int uoff = ustride * (u0 + min(ur, n_units - 1));
+                qa[slot][j] = (v4i)__builtin_amdgcn_raw_buffer_load_b128(rq, qlane, uoff, 0);
+                qb[slot][j] = (v4i)__builtin_amdgcn_raw_buffer_load_b128(rq, qlane + hoff, uoff, 0);
             }
         }
     };
@@ -564,50 +565,59 @@ __device__ void stream_mfma(const Problem &p, int local)
     // are staged (they do not depend on them): the two round trips overlap
     if constexpr (ALDS) load_group(0, 0);
     if constexpr (ALDS) {
-        const int M = p.M;
         stage_rows<kThreads, 8>(gload_ptr<int8_t>(p.Q) + 64 * u0, p.ldq, M, n_units);
-        if (threadIdx.x == 0) *reinterpret_cast<v4i *>(stream_q_lds + n_units * M * kTokStride) = zero;
-        a_lane = r < M ? r * kTokStride + 16 * g : n_units * M * kTokStride;
+        a_lane = min(r, M - 1) * kTokStride + 16 * g;
         __syncthreads();
     }
     v16i acc[TPW][2];
 #pragma unroll
     for (int t = 0; t < TPW; ++t) acc[t][0] = acc[t][1] = (v16i){};
-    // Both halves of every unit of the group, first half first: consecutive
-    // updates of one accumulator are 2 * TPW MFMAs apart, so the matrix pipe
+    // Word x of a lane's slot holds rows 0..31 of the unit's first half of
+    // codes, y the same rows' second half, z and w rows 32..63; the pairs
+    // (x, y) and (z, w) share the unpack's 64-bit shifts.  Consecutive
+    // updates of one accumulator are two MFMAs apart, so the matrix pipe
     // never waits on its own previous result.
     auto run_group = [&](int slot, int i) {
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-            for (int j = 0; j < UNROLL; ++j) {
-                const bool live = UNROLL * i + j < n_units;
-                v4i a;
-                if constexpr (ALDS) {
-                    // units past the range read any staged unit: their weights are zero
-                    const int uu = min(UNROLL * i + j, n_units - 1);
-                    const int off = r < p.M ? a_lane + uu * p.M * kTokStride + 32 * h : a_lane;
-                    a = *reinterpret_cast<const v4i *>(stream_q_lds + off);
-                } else {
-                    a = h ? qb[slot][j] : qa[slot][j];
-                }
-#pragma unroll
-                for (int t = 0; t < TPW; ++t) {
-                    const v4u wj = live ? w[slot][j][t] : zw;
-                    v4i b0, b1;
-                    planes2(h ? wj.y : wj.x, h ? wj.w : wj.z, b0, b1);
-                    acc[t][0] = mfma_i8(a, b0, acc[t][0]);
-                    acc[t][1] = mfma_i8(a, b1, acc[t][1]);
-                }
+        for (int j = 0; j < UNROLL; ++j) {
+            v4i a0, a1;
+            if constexpr (ALDS) {
+                // units past the range read any staged unit: their weights are zero
+                const int uu = min(UNROLL * i + j, n_units - 1);
+                const int8_t *q = stream_q_lds + a_lane + uu * M * kTokStride;
+                a0 = *reinterpret_cast<const v4i *>(q);
+                a1 = *reinterpret_cast<const v4i *>(q + 32);
+            } else {
+                a0 = qa[slot][j];
+                a1 = qb[slot][j];
             }
+#pragma unroll
+            for (int t = 0; t < TPW; ++t) {
+                const v4u wj = w[slot][j][t];
+                v4i bx, by, bz, bw;
+                planes2(wj.x, wj.y, bx, by);
+                planes2(wj.z, wj.w, bz, bw);
+                acc[t][0] = mfma_i8(a0, bx, acc[t][0]);
+                acc[t][1] = mfma_i8(a0, bz, acc[t][1]);
+                acc[t][0] = mfma_i8(a1, by, acc[t][0]);
+                acc[t][1] = mfma_i8(a1, bw, acc[t][1]);
+            }
+        }
     };
     if constexpr (!ALDS) load_group(0, 0);
+    // each group's loads are issued before the previous group's MFMAs (the
+    // barriers keep the scheduler from sinking them behind the MFMAs, which
+    // would shorten the stream's lookahead)
     int i = 0;
     for (; i + 2 <= groups; i += 2) {
         load_group(1, i + 1);
+        __builtin_amdgcn_sched_barrier(0);
         run_group(0, i);
+        __builtin_amdgcn_sched_barrier(0);
         load_group(0, i + 2);
+        __builtin_amdgcn_sched_barrier(0);
         run_group(1, i + 1);
+        __builtin_amdgcn_sched_barrier(0);
     }
     if (i < groups) run_group(0, i);
 
@@ -661,7 +671,7 @@ __device__ void stream_mfma(const Problem &p, int local)
 // 64-row tile and K range, every wave's units requested before the staging)
 // with the matrix-instruction stream.  The activations of the range are
 // staged row-major as in variant 10 (token m's 64 bytes of unit u at
-// ((u - u0) * M + m) * kTokStride, a zero chunk after the last); each wave
+// ((u - u0) * M + m) * kTokStride); each wave
 // accumulates its units into two 32 x 32 tiles (rows 0..31 and 32..63 of
 // the weight tile), and the waves' sums meet in LDS, in the space the
 // staged activations held: eight slots, word (slot * M + m) * 64 + row for
@@ -689,25 +699,25 @@ __device__ void stream_mfma_wide(const Problem &p, int local)
         s_scale[threadIdx.x] = token_scale(*p.gamma, gload_ptr<float>(p.absmax)[threadIdx.x]);
     }
     const int n_units = u1 - u0;
-    {
-        stage_rows<kThr, 4>(gload_ptr<int8_t>(p.Q) + 64 * u0, p.ldq, M, n_units);
-        if (threadIdx.x == 0) *reinterpret_cast<v4i *>(stream_q_lds + n_units * M * kTokStride) = (v4i){0, 0, 0, 0};
-    }
+    stage_rows<kThr, 4>(gload_ptr<int8_t>(p.Q) + 64 * u0, p.ldq, M, n_units);
     __syncthreads();
-    // lanes of rows past M read the zero chunk
-    const int a_lane = r < M ? r * kTokStride + 16 * g : n_units * M * kTokStride;
-    const int a_step = r < M ? M * kTokStride : 0, a_half = r < M ? 32 : 0;
+    // lanes of rows past M read row M-1: an A row only feeds the same output
+    // row, which is never stored
+    const int a_lane = min(r, M - 1) * kTokStride + 16 * g;
     v16i acc0 = (v16i){}, acc1 = (v16i){};
 #pragma unroll
     for (int j = 0; j < kWideUnits; ++j)
         if (j < nu) {
-            const int8_t *a = stream_q_lds + a_lane + (wave + W * j) * a_step;
+            const int8_t *a = stream_q_lds + a_lane + (wave + W * j) * M * kTokStride;
             const v4i a0 = *reinterpret_cast<const v4i *>(a);
-            const v4i a1 = *reinterpret_cast<const v4i *>(a + a_half);
-            acc0 = mfma_i8(a0, planes(w[j].x), acc0);
-            acc1 = mfma_i8(a0, planes(w[j].z), acc1);
-            acc0 = mfma_i8(a1, planes(w[j].y), acc0);
-            acc1 = mfma_i8(a1, planes(w[j].w), acc1);
+            const v4i a1 = *reinterpret_cast<const v4i *>(a + 32);
+            v4i bx, by, bz, bw;
+            planes2(w[j].x, w[j].y, bx, by);
+            planes2(w[j].z, w[j].w, bz, bw);
+            acc0 = mfma_i8(a0, bx, acc0);
+            acc1 = mfma_i8(a0, bz, acc1);
+            acc0 = mfma_i8(a1, by, acc0);
+            acc1 = mfma_i8(a1, bw, acc1);
         }
     __syncthreads();  // the staged activations are no longer read
     // element e of lane l is token 8*(e/4) + 4*(l/32) + e%4, row 32*s + l%32;

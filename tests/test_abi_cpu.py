@@ -228,7 +228,7 @@ def test_group_plan_single_token_quantization():
     wsb3 = L.bitlinear_group_workspace_bytes(arr3, 17)
     assert L.bitlinear_group_plan(arr3, 17, FAKE, wsb3, host3.ctypes.data, tb3) == 0
     hdr3 = np.frombuffer(host3[:48].tobytes(), np.int32)
-    assert hdr3[2] == 21 and hdr3[7] == 10 and hdr3[9] == max(80 * 1 * 4, 80 * 5 * 1) + 16
+    assert hdr3[2] == 21 and hdr3[7] == 10 and hdr3[9] == max(80 * 1 * 4, 80 * 5 * 1)
     # a one-token problem whose K range (1250 units) would need more than
     # 64 KiB of staged activations is split in two (625 units, 40000 bytes),
     # so a 2-token launch still takes the token loop (6)
