@@ -9,6 +9,11 @@ activations per matrix.  A step quantizes every activation vector per token
 kernel for all 210 problems).  Weights are quantized and packed once, before
 timing, like loading an inference-ready checkpoint.
 
+Timing: each measured step first runs back to back for --settle seconds
+(default 0.1, reported as clock_settle_s) so that the clock governor has
+reached this load's sustained state, then --warmup untimed steps, then
+exactly --steps timed steps between synchronizations.
+
 Printed: one JSON line.  value = packed weight bytes per step / step time.
 roofline = the contraction kernel's algorithmic bytes (packed weights + int8
 activations + fp32 outputs) over its average duration (HIP events on the
@@ -96,14 +101,32 @@ def make_plan(B, torch, mats, M, dev, outliers=0.0, seed0=7, fmt=0):
     return plan, probs
 
 
-def time_plan(torch, plan, steps, warmup, windows=7):
+def settle(torch, fn, seconds):
+    """Run fn back to back (synchronizing every 20 calls) for about
+    `seconds`, so that the clock governor reaches the sustained state of
+    this load before anything is timed: the step's clock ramps for tens of
+    milliseconds (the 2B decode step measures 88 us in its first 17 ms and
+    82 us after)."""
+    t_end = time.perf_counter() + seconds
+    while time.perf_counter() < t_end:
+        for _ in range(20):
+            fn()
+        torch.cuda.synchronize()
+
+
+SETTLE_S = 0.0  # seconds of clock settling before each timed measurement (set from --settle)
+
+
+def time_plan(torch, plan, steps, warmup, windows=7, settle_s=None):
     """Wall time per step over `steps` steps (quantize + contract), then the
     contraction kernel alone: `windows` event windows, each `steps`
     back-to-back launches between one pair of HIP events on the launch
     stream (torch's current stream), giving the average launch duration
-    without per-launch event overhead.  Returns (ms per step, median kernel
-    ms, {min, median, max} over the windows): the median keeps one window
-    taken while the clock settles from deciding the figure."""
+    without per-launch event overhead.  Before the `warmup` steps the step
+    runs for settle_s seconds (see settle).  Returns (ms per step, median
+    kernel ms, {min, median, max} over the windows): the median keeps one
+    window taken while the clock settles from deciding the figure."""
+    settle(torch, lambda: (plan.quant_act(), plan.matmul()), SETTLE_S if settle_s is None else settle_s)
     for _ in range(warmup):
         plan.quant_act()
         plan.matmul()
@@ -145,6 +168,7 @@ def time_graph(torch, plan, steps, warmup):
     with torch.cuda.graph(graph):
         plan.quant_act()
         plan.matmul()
+    settle(torch, graph.replay, SETTLE_S)
     for _ in range(warmup):
         graph.replay()
     torch.cuda.synchronize()
@@ -336,6 +360,7 @@ def stack_curve(B, torch, mats, dev, Ms, steps, warmup):
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
             s = ctypes.c_void_p(side.cuda_stream)
+            settle(torch, lambda: chain.step(s), SETTLE_S)
             for _ in range(max(1, warmup)):
                 chain.step(s)
             torch.cuda.synchronize()
@@ -348,6 +373,7 @@ def stack_curve(B, torch, mats, dev, Ms, steps, warmup):
             with torch.cuda.graph(graph, stream=side):
                 chain.step(s)
         torch.cuda.current_stream().wait_stream(side)
+        settle(torch, graph.replay, SETTLE_S)
         for _ in range(max(1, warmup)):
             graph.replay()
         torch.cuda.synchronize()
@@ -634,6 +660,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--settle", type=float, default=0.1,
+                    help="seconds the step runs before the warm-up steps, so that the clock has settled")
     ap.add_argument("--model", default="2b", choices=sorted(synth.MODELS))
     ap.add_argument("--layers", type=int, default=None)
     ap.add_argument("--M", type=int, default=1)
@@ -652,6 +680,8 @@ def main():
                     help="comma list of token counts: print only the per-call latency of one 3B-class decode "
                          "layer's library calls at each (JSON line)")
     args = ap.parse_args()
+    global SETTLE_S
+    SETTLE_S = max(0.0, args.settle)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path "
@@ -704,6 +734,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "clock_settle_s": args.settle,
         "ms_per_step": round(ms, 5),
         "higher_is_better": True,
         "scaling": "weak",
