@@ -29,9 +29,10 @@ namespace {
 
 constexpr int kThreads = 256;
 typedef float v4f_t __attribute__((ext_vector_type(4)));
-// floats per LDS row of the epilogue transpose: the rescaled outputs go
-// through LDS, 32 rows at a time per wave, so that Y is written with
-// 16-byte stores covering whole 256-byte row pieces.  Output stores are
+// floats per LDS row of the epilogue transpose of blocks at the edge of Y:
+// their rescaled outputs go through LDS, 32 rows at a time per wave, so
+// that Y is written with 16-byte stores covering whole 256-byte row pieces
+// (interior blocks store straight from the accumulators).  Output stores are
 // non-temporal: the fp32 result (M*N*4 bytes, the largest stream of the
 // kernel) is written once and must not evict the activation and weight
 // tiles that other workgroups still reuse from L2.
@@ -244,10 +245,11 @@ __device__ __forceinline__ void tile_body(const Problem &p, int local)
         }
     }
 
-    // epilogue: rescale, transpose through LDS, 16-byte non-temporal stores.
-    // A wave whose 64 x 64 block lies wholly inside Y (N a multiple of 4)
-    // stores through a buffer resource at scalar row offsets: no per-row
-    // bounds tests or address arithmetic in vector registers
+    // epilogue: rescale and store, non-temporal.  A wave whose 64 x 64 block
+    // lies wholly inside Y (N a multiple of 4) stores straight from its
+    // accumulators through a buffer resource at scalar row offsets: no LDS,
+    // no per-row bounds tests, no address arithmetic in vector registers.
+    // Other waves transpose through LDS for 16-byte stores with tests.
     __syncthreads();  // every wave is done with the activation stages
     float *ep = reinterpret_cast<float *>(smem) + wave * (32 * kEpiStride);
     const bool vec_ok = (N & 3) == 0;
@@ -292,10 +294,25 @@ __device__ __forceinline__ void tile_body(const Problem &p, int local)
             }
         }
     };
-    if (interior)
-        epilogue(std::true_type{});
-    else
+    if (interior) {
+        // straight from the accumulators: element e of lane l is token
+        // 8 (e / 4) + 4 (l / 32) + e % 4 of the half, row 32 s2 + l % 32, so
+        // one 4-byte store of the wave writes two whole 128-byte row pieces
+        const int doff = 4 * (4 * g * N + 64 * tile + r);
+#pragma unroll
+        for (int i = 0; i < WMS; ++i)
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int row = 8 * (e >> 2) + 4 * g + (e & 3);
+                    const float v = (float)acc[i][s2][e] * cs[32 * i + row];
+                    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), ry, doff + 128 * s2,
+                                                          4 * (32 * i + 8 * (e >> 2) + (e & 3)) * N, kNonTemporal);
+                }
+    } else {
         epilogue(std::false_type{});
+    }
     if (p.acc_out && tv) {
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
