@@ -196,6 +196,73 @@ def test_group_plan_table_on_host():
     assert L.bitlinear_group_plan(bad, 5, FAKE, wsb, host.ctypes.data, tb) == -2
 
 
+def _plan_tables(specs):
+    """Host plan table of `specs`: (header ints, header offsets, problem
+    fields by name, map entries of each kernel as (problem, local) pairs)."""
+    L = B.lib()
+    arr = _problems(specs)
+    tb = L.bitlinear_group_table_bytes(arr, len(specs))
+    wsb = L.bitlinear_group_workspace_bytes(arr, len(specs))
+    host = np.zeros(tb, np.uint8)
+    assert L.bitlinear_group_plan(arr, len(specs), FAKE, wsb, host.ctypes.data, tb) == 0, L.bitlinear_last_error()
+    hdr = np.frombuffer(host[:48].tobytes(), np.int32)
+    off = np.frombuffer(host[48:104].tobytes(), np.int64)  # ws_bytes, probs, tok, stream, tile, bt5, total
+    # Problem: ten pointers and ldq (88 bytes), then int32 fields from M on
+    names = ["M", "N", "K", "KU", "NT", "ks", "upsplit", "kind", "mtile", "qtiled", "mt", "ntt"]
+    size = 160
+    probs = []
+    for i in range(len(specs)):
+        f = np.frombuffer(host[off[1] + i * size + 88: off[1] + i * size + 88 + 4 * len(names)].tobytes(), np.int32)
+        probs.append(dict(zip(names, (int(v) for v in f))))
+    maps = {}
+    for key, n, o in (("stream", hdr[3], off[3]), ("tile", hdr[4], off[4])):
+        maps[key] = np.frombuffer(host[o: o + 8 * n].tobytes(), np.uint32).reshape(-1, 2)
+    return hdr, off, probs, maps
+
+
+def _slices(entries):
+    """The eight XCD slices of a map: workgroup b runs on XCD b % 8 and takes
+    logical item (b % 8) * per + b / 8, so slice x is entries x, x + 8, ..."""
+    return [entries[x::8] for x in range(8)]
+
+
+def test_group_plan_item_order():
+    # streaming items run longest first within each XCD slice (a slice must
+    # not end on its long down projections); the tile kernel keeps problem
+    # order, so consecutive items share activation and weight tiles
+    specs = [(1, 2560, 2560), (1, 2560, 6912), (1, 6912, 2560), (1, 2560, 2560), (1, 640, 13824)] * 3
+    _, _, probs, maps = _plan_tables(specs)
+    st = maps["stream"]
+    assert all(p["kind"] == 0 for p in probs) and len(st) > 0 and len(st) % 8 == 0
+
+    def units(e):
+        p = probs[e[0]]
+        split = int(e[1]) % p["ks"]
+        return min(p["KU"], (split + 1) * p["upsplit"]) - split * p["upsplit"]
+    lengths = set()
+    for sl in _slices(st):
+        u = [units(e) for e in sl if e[0] != 0xFFFFFFFF]
+        lengths |= set(u)
+        assert u == sorted(u, reverse=True), u
+        idle = [e[0] == 0xFFFFFFFF for e in sl]
+        assert idle == sorted(idle)  # idle entries only at a slice's end
+    assert len(lengths) > 1  # the case mixes item lengths
+    # every item of every problem appears exactly once
+    seen = sorted((int(a), int(b)) for a, b in st if a != 0xFFFFFFFF)
+    want = sorted((i, j) for i, p in enumerate(probs) if p["kind"] == 0
+                  for j in range((p["ntt"] if p["ntt"] > 0 else p["NT"]) * p["ks"]))
+    assert seen == want
+
+    tspecs = [(512, 2560, 2560), (512, 6912, 2560), (512, 2560, 6912)] * 2
+    _, _, tprobs, tmaps = _plan_tables(tspecs)
+    tl = tmaps["tile"]
+    assert all(p["kind"] == 1 for p in tprobs) and len(tl) > 0 and len(tl) % 8 == 0
+    per = len(tl) // 8
+    logical = [tl[8 * j + x] for x in range(8) for j in range(per)]
+    order = [(int(a), int(b)) for a, b in logical if a != 0xFFFFFFFF]
+    assert order == sorted(order)  # problem order, then local item order
+
+
 def test_group_plan_single_token_quantization():
     # 16 single-token problems with 64 row tiles each (no K split): every
     # token goes to the quantization kernel and the dot4 kernel reads LDS-
