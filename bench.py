@@ -548,6 +548,56 @@ def measured_peaks(B, torch, dev, seconds: float = 0.6):
         raise RuntimeError("matrix-instruction probe checksum mismatch")
     later = sorted(rates[len(rates) // 2:])
     tops = later[len(later) // 2]
+    # the same chains on operands from memory, which toggle as many bits as a
+    # real contraction: (a) this workload's own operands, int8 codes of the
+    # prefill activations (N(0, 1), 1% of channels x20, cast by the library)
+    # against ternary fields of N(0, 0.02) weights (quantized by the
+    # library); (b) uniform random int8 against uniform random fields.  The
+    # probe's clock counters give the shader clock each load sustains.
+    def frags(T):  # [32 rows, 128 codes] -> four 64-lane x 16-byte fragments
+        return T.reshape(32, 4, 2, 16).permute(1, 2, 0, 3).reshape(4, 64, 16)
+
+    Xw = synth.activations_torch(32, 2560, 777, dev, outlier_frac=0.01)
+    Qw = B.quant_act(Xw)[0][:, :128]
+    Tw, _ = B.quantize_weights(synth.weights_torch(32, 2560, 0.02, 778, dev))
+    workload_ops = torch.stack([frags(Qw), frags((Tw[:, :128] + 1).to(torch.int8))], 1)
+    rng = np.random.default_rng(12345)
+    uniform_ops = np.empty((4, 2, 64, 16), np.int8)
+    uniform_ops[:, 0] = rng.integers(-127, 128, (4, 64, 16))
+    uniform_ops[:, 1] = rng.integers(0, 3, (4, 64, 16))
+    clocks = torch.empty(3 * blocks, dtype=torch.int64, device=dev)
+
+    def data_probe(dops):
+        drates, ghz = [], []
+        t_end = time.perf_counter() + seconds / 2
+        while time.perf_counter() < t_end:
+            a, b = ev(), ev()
+            a.record()
+            for _ in range(burst - 1):
+                B.probe_mfma_data(iters, dops, blocks, sink, clocks)
+            c = ev()
+            c.record()
+            B.probe_mfma_data(iters, dops, blocks, sink, clocks)
+            b.record()
+            b.synchronize()
+            drates.append(ops * burst / (a.elapsed_time(b) * 1e-3) / 1e12)
+            ck = clocks.cpu().numpy().reshape(blocks, 3).astype(np.float64)
+            # reference-counter rate: the span of all workgroups' loops over
+            # the last launch's event time (the loops fill nearly all of it)
+            ref_hz = (ck[:, 2].max() - ck[:, 1].min()) / (c.elapsed_time(b) * 1e-3)
+            ghz.append(float(np.median(ck[:, 0] / (ck[:, 2] - ck[:, 1]))) * ref_hz / 1e9)
+        o64 = dops.cpu().numpy().reshape(4, 2, 64, 16).astype(np.int64)
+        per_set = int((o64[:, 0].reshape(4, 2, 32, 16).sum(2) * o64[:, 1].reshape(4, 2, 32, 16).sum(2)).sum())
+        want = (4 * iters * per_set) % (1 << 32)
+        per = sink.cpu().numpy().view(np.uint32).reshape(blocks, 256).astype(np.uint64).sum(1) % (1 << 32)
+        if not bool((per == want).all()):
+            raise RuntimeError("matrix-instruction data probe checksum mismatch")
+        half = len(drates) // 2
+        return (sorted(drates[half:])[len(drates[half:]) // 2], sorted(ghz[half:])[len(ghz[half:]) // 2],
+                len(drates) - half)
+
+    data_runs = {"workload": data_probe(workload_ops.reshape(-1).contiguous()),
+                 "uniform": data_probe(torch.from_numpy(uniform_ops.reshape(-1)).to(dev))}
     # grid-wide barrier with one word exchanged per workgroup, one workgroup
     # per compute unit: (time of R rounds - time of 1 round) / (R - 1)
     cus = B.probe_compute_units()
@@ -575,7 +625,16 @@ def measured_peaks(B, torch, dev, seconds: float = 0.6):
                                   f"rounds less 1 round"},
         "int8_mfma": {"value": round(tops, 1), "unit": "TOP/s",
                       "probe": f"v_mfma_i32_32x32x32_i8 chains, {blocks} workgroups, no memory traffic, "
-                               f"median of {len(later)} sustained bursts"},
+                               f"every operand byte 1, median of {len(later)} sustained bursts"},
+        **{f"int8_mfma_{k}_operands": {
+            "value": round(v[0], 1), "unit": "TOP/s", "clock_ghz": round(v[1], 3),
+            "probe": f"the same chains on four sets of A and B fragments held in registers ("
+                     + ("int8 codes of N(0,1) activations with 1% of channels x20 against ternary fields of "
+                        "N(0,0.02) weights, both quantized by the library" if k == "workload" else
+                        "uniform random int8 against uniform random ternary fields")
+                     + f"), median of {v[2]} sustained bursts; clock = shader-clock count over reference-"
+                       f"counter span of each workgroup's loop, the reference rate from the launch's event time"}
+           for k, v in data_runs.items()},
     }
 
 
@@ -800,6 +859,9 @@ def main():
             pr = result["prefill"]["roofline"]
             pr["measured_peak"] = mfma
             pr["frac_of_measured"] = round(pr["achieved"] / mfma, 4)
+            wl = peaks["int8_mfma_workload_operands"]["value"]
+            pr["measured_peak_workload_operands"] = wl
+            pr["frac_of_measured_workload_operands"] = round(pr["achieved"] / wl, 4)
 
     curves = [c for c in args.curves.split(",") if c and c != "none"]
     if curves:

@@ -57,6 +57,29 @@ int bitlinear_probe_read(const void *buf, int64_t bytes, int64_t chunk_bytes, ui
  */
 int bitlinear_probe_mfma(int64_t iters, int32_t a, int32_t b, int32_t blocks, int32_t *sink, void *stream);
 
+/*
+ * The chains of bitlinear_probe_mfma with operands from memory, so that the
+ * matrix instructions toggle as many bits as a contraction over real data
+ * does: `operands` holds four sets of an A and a B fragment, int8
+ * [4][2][64 lanes][16 bytes] (set j's A at [j][0], its B at [j][1]); every
+ * wave loads them once and chain j multiplies set j for `iters` rounds.
+ * It performs blocks * 4 * iters * 4 * 65536 int8 operations.
+ *   iters     >= 1, blocks >= 1                     (BITLINEAR_ERR_SHAPE)
+ *   sink      int32[256 * blocks]; thread t of workgroup b writes the sum,
+ *             wrapped to 32 bits, of its 64 accumulator elements.  Byte i
+ *             of lane l of an A fragment and byte i of lane l' of a B
+ *             fragment meet in a product exactly when l / 32 = l' / 32, so
+ *             the 256 words of a workgroup add up (mod 2^32) to
+ *             4 iters sum_j sum_{h<2, i<16} (sum_{r<32} A_j[32h+r][i])
+ *             (sum_{r<32} B_j[32h+r][i]).
+ *   clocks    uint64[3 * blocks]: per workgroup, read by thread 0, the
+ *             shader-clock count (s_memtime) elapsed over its loop, then the
+ *             constant-rate reference counter (s_memrealtime) at the loop's
+ *             start and at its end.
+ */
+int bitlinear_probe_mfma_data(int64_t iters, const void *operands, int32_t blocks, int32_t *sink, uint64_t *clocks,
+                              void *stream);
+
 /* Workgroups of bitlinear_probe_mfma that are resident on the current
  * device at once (compute units times workgroups per unit), into *blocks.
  * Queries the HIP runtime: BITLINEAR_ERR_HIP if it fails. */

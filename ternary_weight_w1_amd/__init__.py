@@ -109,6 +109,7 @@ def lib():
             "bitlinear_probe_read_sink_words": (_i64, [_i64, _i64]),
             "bitlinear_probe_read": (_int, [_vp, _i64, _i64, _vp, _vp]),
             "bitlinear_probe_mfma": (_int, [_i64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _vp, _vp]),
+            "bitlinear_probe_mfma_data": (_int, [_i64, _vp, ctypes.c_int32, _vp, _vp, _vp]),
             "bitlinear_probe_mfma_blocks": (_int, [ctypes.POINTER(ctypes.c_int32)]),
             "bitlinear_probe_barrier": (_int, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _vp, _vp, _vp]),
             "bitlinear_probe_compute_units": (_int, [ctypes.POINTER(ctypes.c_int32)]),
@@ -445,6 +446,27 @@ def probe_mfma(iters: int, a: int, b: int, blocks: int, sink=None, device=None, 
         sink = torch.empty(256 * blocks, dtype=torch.int32, device=device or "cuda")
     _check(lib().bitlinear_probe_mfma(iters, a, b, blocks, sink.data_ptr(), _stream(stream)), "probe_mfma")
     return sink
+
+
+@_on_stream
+def probe_mfma_data(iters: int, operands, blocks: int, sink=None, clocks=None, device=None, stream=None):
+    """Int8 matrix-instruction probe on operands from memory (an int8 CUDA
+    tensor of 8192 bytes: four (A, B) fragment sets of 64 lanes x 16
+    bytes): blocks*4*iters*4*65536 int8 operations.  Returns (sink, clocks):
+    int32[256*blocks] accumulator sums and int64[3*blocks]: per workgroup
+    the shader-clock count over its loop and the reference counter at the
+    loop's start and end."""
+    _dev_tensor(operands, torch.int8, "operands")
+    if operands.numel() != 8192:
+        raise ValueError("operands must hold 4 x 2 x 64 x 16 bytes")
+    dev = operands.device
+    if sink is None:
+        sink = torch.empty(256 * blocks, dtype=torch.int32, device=dev)
+    if clocks is None:
+        clocks = torch.empty(3 * blocks, dtype=torch.int64, device=dev)
+    _check(lib().bitlinear_probe_mfma_data(iters, operands.data_ptr(), blocks, sink.data_ptr(), clocks.data_ptr(),
+                                           _stream(stream)), "probe_mfma_data")
+    return sink, clocks
 
 
 def probe_compute_units() -> int:

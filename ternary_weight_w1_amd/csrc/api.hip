@@ -1416,6 +1416,20 @@ int bitlinear_probe_mfma(int64_t iters, int32_t a, int32_t b, int32_t blocks, in
     return e == hipSuccess ? BITLINEAR_OK : hip_fail(e, "probe_mfma");
 }
 
+int bitlinear_probe_mfma_data(int64_t iters, const void *operands, int32_t blocks, int32_t *sink, uint64_t *clocks,
+                              void *stream)
+{
+    if (!operands || !sink || !clocks)
+        return fail(BITLINEAR_ERR_NULL, "probe_mfma_data: operands, sink and clocks are required");
+    if (!a16(operands) || !a4(sink) || (reinterpret_cast<uintptr_t>(clocks) & 7) != 0)
+        return fail(BITLINEAR_ERR_ALIGN, "probe_mfma_data: operands 16-byte, sink 4-byte, clocks 8-byte aligned");
+    if (iters < 1 || blocks < 1)
+        return fail(BITLINEAR_ERR_SHAPE, "probe_mfma_data: iters=%lld blocks=%d must be >= 1", (long long)iters, blocks);
+    const hipError_t e =
+        bl::launch_probe_mfma_data(iters, operands, blocks, sink, clocks, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? BITLINEAR_OK : hip_fail(e, "probe_mfma_data");
+}
+
 int bitlinear_probe_compute_units(int32_t *cus)
 {
     if (!cus) return fail(BITLINEAR_ERR_NULL, "probe_compute_units: cus is required");

@@ -62,6 +62,48 @@ __global__ __launch_bounds__(kProbeThreads) void probe_mfma_kernel(int64_t iters
     gstore_ptr<int32_t>(sink)[(int64_t)blockIdx.x * kProbeThreads + threadIdx.x] = s;
 }
 
+// The same four chains with operands taken from memory: kProbeSets pairs of
+// (A, B) fragments, 16 bytes per lane each, loaded once into registers; chain
+// j multiplies set j, so consecutive matrix instructions take different
+// operand bits, as they do in a contraction over real data (the constant
+// operands above toggle almost nothing).  Thread 0 of each workgroup records
+// the shader-clock count over its loop and the reference-clock counter at
+// its start and end, so the clock the part sustains under this load can be
+// read off.
+constexpr int kProbeSets = 4;
+__global__ __launch_bounds__(kProbeThreads) void probe_mfma_data_kernel(int64_t iters, const v4i *__restrict__ ops,
+                                                                        int32_t *__restrict__ sink,
+                                                                        uint64_t *__restrict__ clocks)
+{
+    const int lane = threadIdx.x & 63;
+    v4i av[kProbeSets], bv[kProbeSets];
+#pragma unroll
+    for (int j = 0; j < kProbeSets; ++j) {
+        av[j] = gload_ptr<v4i>(ops)[(2 * j) * 64 + lane];
+        bv[j] = gload_ptr<v4i>(ops)[(2 * j + 1) * 64 + lane];
+    }
+    v16i acc[kProbeSets];
+#pragma unroll
+    for (int j = 0; j < kProbeSets; ++j) acc[j] = (v16i){};
+    const uint64_t t0 = __builtin_amdgcn_s_memtime(), r0 = __builtin_amdgcn_s_memrealtime();
+    for (int64_t i = 0; i < iters; ++i) {
+#pragma unroll
+        for (int j = 0; j < kProbeSets; ++j) acc[j] = mfma_i8(av[j], bv[j], acc[j]);
+    }
+    int32_t s = 0;
+#pragma unroll
+    for (int j = 0; j < kProbeSets; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) s += acc[j][e];
+    const uint64_t t1 = __builtin_amdgcn_s_memtime(), r1 = __builtin_amdgcn_s_memrealtime();
+    gstore_ptr<int32_t>(sink)[(int64_t)blockIdx.x * kProbeThreads + threadIdx.x] = s;
+    if (threadIdx.x == 0) {
+        gstore_ptr<uint64_t>(clocks)[3 * blockIdx.x] = t1 - t0;
+        gstore_ptr<uint64_t>(clocks)[3 * blockIdx.x + 1] = r0;
+        gstore_ptr<uint64_t>(clocks)[3 * blockIdx.x + 2] = r1;
+    }
+}
+
 // `rounds` grid-wide barriers among the launch's workgroups (at most one per
 // compute unit, so all are resident at once).  At barrier r every workgroup
 // publishes one word (r * G + b) with a device-scope store, waits until the
@@ -135,6 +177,14 @@ hipError_t launch_probe_read(const void *buf, int64_t bytes, int64_t chunk_bytes
 hipError_t launch_probe_mfma(int64_t iters, int a, int b, int blocks, int32_t *sink, hipStream_t s)
 {
     hipLaunchKernelGGL(probe_mfma_kernel, dim3((unsigned)blocks), dim3(kProbeThreads), 0, s, iters, a, b, sink);
+    return hipGetLastError();
+}
+
+hipError_t launch_probe_mfma_data(int64_t iters, const void *ops, int blocks, int32_t *sink, uint64_t *clocks,
+                                  hipStream_t s)
+{
+    hipLaunchKernelGGL(probe_mfma_data_kernel, dim3((unsigned)blocks), dim3(kProbeThreads), 0, s, iters,
+                       static_cast<const v4i *>(ops), sink, clocks);
     return hipGetLastError();
 }
 

@@ -37,7 +37,7 @@ def test_every_header_is_checked():
 
 def test_every_declared_symbol_is_exported():
     names = _declared()
-    assert len(names) == 40, names
+    assert len(names) == 41, names
     out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r"\bT (bitlinear_\w+)", out))
@@ -517,6 +517,17 @@ def test_probe_mfma_rejects_bad_arguments():
     assert L.bitlinear_probe_mfma(65, 127, -128, 1, FAKE, None) == -2
     assert L.bitlinear_probe_mfma((1 << 20), 1, 1, 1, FAKE, None) == -2
     assert L.bitlinear_probe_mfma_blocks(None) == -1
+
+
+def test_probe_mfma_data_rejects_bad_arguments():
+    L = B.lib()
+    assert L.bitlinear_probe_mfma_data(10, None, 1, FAKE, FAKE, None) == -1
+    assert L.bitlinear_probe_mfma_data(10, FAKE, 1, None, FAKE, None) == -1
+    assert L.bitlinear_probe_mfma_data(10, FAKE, 1, FAKE, None, None) == -1
+    assert L.bitlinear_probe_mfma_data(10, FAKE + 4, 1, FAKE, FAKE, None) == -3
+    assert L.bitlinear_probe_mfma_data(10, FAKE, 1, FAKE, FAKE + 4, None) == -3
+    assert L.bitlinear_probe_mfma_data(0, FAKE, 1, FAKE, FAKE, None) == -2
+    assert L.bitlinear_probe_mfma_data(10, FAKE, 0, FAKE, FAKE, None) == -2
 
 
 

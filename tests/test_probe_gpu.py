@@ -41,6 +41,34 @@ def test_probe_mfma_closed_form(iters, a, b, blocks):
     assert bool((sink == 2048 * a * b * iters).all())
 
 
+def probe_operands(seed):
+    """Four (A, B) fragment sets: A random int8 in [-127, 127], B random
+    ternary fields {0, 1, 2}, as the contraction kernels feed them."""
+    rng = np.random.default_rng(seed)
+    ops = np.empty((4, 2, 64, 16), np.int8)
+    ops[:, 0] = rng.integers(-127, 128, (4, 64, 16))
+    ops[:, 1] = rng.integers(0, 3, (4, 64, 16))
+    return ops
+
+
+@pytest.mark.parametrize("iters,blocks", [(1, 1), (9, 3), (2048, 2)])
+def test_probe_mfma_data_checksum(iters, blocks):
+    # byte i of A lane l meets byte i of B lane l' exactly when the lanes
+    # hold the same K half (l // 32 == l' // 32): the sum over all outputs
+    # of A B is sum_k colsum_A[k] rowsum_B[k]
+    print(f"probe_mfma_data iters={iters} blocks={blocks}", flush=True)
+    ops = probe_operands(iters)
+    sink, clocks = B.probe_mfma_data(iters, torch.from_numpy(ops.reshape(-1)).to("cuda"), blocks)
+    torch.cuda.synchronize()
+    o = ops.astype(np.int64)
+    per_set = (o[:, 0].reshape(4, 2, 32, 16).sum(2) * o[:, 1].reshape(4, 2, 32, 16).sum(2)).sum()
+    want = (4 * iters * per_set) % (1 << 32)
+    per = sink.cpu().numpy().view(np.uint32).reshape(blocks, 256).astype(np.uint64).sum(1) % (1 << 32)
+    assert (per == want).all()
+    ck = clocks.cpu().numpy().reshape(blocks, 3)
+    assert (ck[:, 0] > 0).all() and (ck[:, 2] >= ck[:, 1]).all()
+
+
 def test_probe_mfma_blocks_fill_the_device():
     n = B.probe_mfma_blocks()
     cus = torch.cuda.get_device_properties(0).multi_processor_count
