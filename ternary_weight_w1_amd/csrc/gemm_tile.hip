@@ -203,8 +203,10 @@ __device__ __forceinline__ void tile_body(const Problem &p, int local)
                 acc[i][1] = mfma_i8(a[i][1], b3, acc[i][1]);
             }
         }
-        stage_lds(buf ^ 1, (s + 1) % kD);
-        __syncthreads();
+        if (st + 1 < KS) {  // the last stage has no successor to stage
+            stage_lds(buf ^ 1, (s + 1) % kD);
+            __syncthreads();
+        }
     };
     int s0 = 0;
     for (; s0 + kD <= KS; s0 += kD) {
@@ -250,10 +252,13 @@ __device__ __forceinline__ void tile_body(const Problem &p, int local)
     // accumulators through a buffer resource at scalar row offsets: no LDS,
     // no per-row bounds tests, no address arithmetic in vector registers.
     // Other waves transpose through LDS for 16-byte stores with tests.
-    __syncthreads();  // every wave is done with the activation stages
     float *ep = reinterpret_cast<float *>(smem) + wave * (32 * kEpiStride);
     const bool vec_ok = (N & 3) == 0;
     const bool interior = tv && vec_ok && m0 + BM <= M && 64 * tile + 64 <= N && N <= (1 << 23);
+    // only blocks at the edge of Y reuse the stage buffers (for the
+    // transpose): where every wave's block is interior, no wave waits
+    if (!(vec_ok && m0 + BM <= M && 64 * (4 * nt + 3) + 64 <= N && N <= (1 << 23)))
+        __syncthreads();  // every wave is done with the activation stages
     BL_GLOBAL float *Y = gstore_ptr<float>(p.Y);
     float *yp = uni(p.Y) + (int64_t)m0 * N;
     const __amdgpu_buffer_rsrc_t ry = buffer_rsrc(yp, -1);
