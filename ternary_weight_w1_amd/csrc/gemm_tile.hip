@@ -118,8 +118,6 @@ __device__ __forceinline__ void tile_body(const Problem &p, int local)
         adst[i] = row * kRow + 16 * col;
     }
 
-    __syncthreads();  // the previous work item of this workgroup may still read LDS
-
     v4i ar[kD][UPS][CH];
     v4u br[kD][UPS];
     auto load_stage = [&](int slot, int st) {
