@@ -137,15 +137,26 @@ __device__ __forceinline__ void tile_body(const Problem &p, int local)
 #pragma unroll
             for (int i = 0; i < CH; ++i) *reinterpret_cast<v4i *>(&As[buf][adst[i] + 64 * h]) = ar[slot][h][i];
     };
-#pragma unroll
-    for (int d = 0; d < kD; ++d) load_stage(d, d);
-    // the token scales (read by the epilogue only) are requested behind the
-    // first stages, so the two memory round trips overlap
+    // stage 0 is requested first, then the token scales and row sums (the
+    // row sums start the accumulators), then stage 1: the round trips
+    // overlap, and the wait for the scales leaves stage 1's loads in flight
+    load_stage(0, 0);
     __builtin_amdgcn_sched_barrier(0);
+    float s_gamma = 0.0f, s_absmax = 0.0f;
+    int32_t s_rowsum = 0;
     if (tid < BM) {
         const int m = min(m0 + tid, M - 1);
-        cs[tid] = token_scale(*gload_ptr<float>(p.gamma), gload_ptr<float>(p.absmax)[m]);
-        nrsum[tid] = -gload_ptr<int32_t>(p.rowsum)[m];
+        s_gamma = *gload_ptr<float>(p.gamma);
+        s_absmax = gload_ptr<float>(p.absmax)[m];
+        s_rowsum = gload_ptr<int32_t>(p.rowsum)[m];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    static_assert(kD == 2, "two stages of lookahead");
+    load_stage(1, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    if (tid < BM) {
+        cs[tid] = token_scale(s_gamma, s_absmax);
+        nrsum[tid] = -s_rowsum;
     }
     stage_lds(0, 0);
     __syncthreads();
