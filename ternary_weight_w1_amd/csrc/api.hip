@@ -126,6 +126,11 @@ bool alds_fits(int64_t M, int64_t K)
     const int64_t ku = (K + 63) / 64, cap = alds_max_units(M);
     return (ku + cap - 1) / cap <= kAldsMaxSplits;
 }
+// Its instantiation for a launch whose workgroups stage `lds` bytes: held to
+// 128 VGPRs (11, four waves per SIMD) where four such workgroups fit in a
+// compute unit's 160 KiB of LDS, else 10 (136 VGPRs, three per SIMD).
+constexpr int64_t kAlds4Lds = 160 * 1024 / 4 - 512;
+int alds_variant(int64_t lds) { return lds <= kAlds4Lds ? 11 : 10; }
 // Tiles per wave of that stream for a launch with `groups` kGroupTiles-tile
 // groups: two when the groups alone fill the part (the split target), else
 // one, which doubles the workgroups without more split-K reductions.
@@ -342,7 +347,7 @@ int stream_variant_for(int64_t M, int64_t upsplit)
 int64_t stream_lds_need(int variant, int64_t M, int64_t upsplit)
 {
     if (variant == 1 || variant == 9) return 0;
-    if (variant == 10) return 80 * M * upsplit;
+    if (variant == 10 || variant == 11) return 80 * M * upsplit;
     if (variant == 13) return std::max<int64_t>(80 * M * upsplit, 8 * M * 256);
     if (variant == 5) return 1024 * upsplit;
     const int64_t slots = (variant == 6 && M > 1) ? bl::kDot4MaxTokens : 1;
@@ -401,7 +406,10 @@ hipError_t launch_contraction(const Problem &p, bool own_q, hipStream_t s)
     if (p.kind == 0) {
         if (p.wide) return bl::launch_stream_single(p, wide_variant(p.M), s);
         const int v = stream_variant_for(p.M, p.upsplit);
-        const int sv = v != 1 ? v : (alds_for(p.M) && alds_fits(p.M, p.K)) ? 10 : p.stiles == 1 ? 9 : 1;
+        const int sv = v != 1                                     ? v
+                       : (alds_for(p.M) && alds_fits(p.M, p.K)) ? alds_variant(80 * p.M * p.upsplit)
+                       : p.stiles == 1                          ? 9
+                                                                : 1;
         return bl::launch_stream_single(p, sv, s);
     }
     (void)own_q;
@@ -863,6 +871,7 @@ int multi_plan(const int8_t *Q, int64_t ldq, int64_t M, int64_t K, const bitline
         mp.variant = stream_variant_for(M, max_upsplit);
         if (mp.variant == 1) mp.variant = (alds_for(M) && alds_fits(M, K)) ? 10 : tpw == 1 ? 9 : 1;
         mp.lds = (int)stream_lds_need(mp.variant, M, max_upsplit);
+        if (mp.variant == 10) mp.variant = alds_variant(mp.lds);
     }
     mp.tick_bytes = up(tick, 256);
     mp.total_bytes = mp.tick_bytes + part;
@@ -1263,6 +1272,7 @@ int build_group(const bitlinear_problem *in, int count, char *ws, GroupPlan &out
     h.n_items_tile = (int32_t)items_t;
     h.n_items_bt5 = (int32_t)items_5;
     h.bt5_max_m = (int32_t)(max_m5 < bl::kBt5Tokens ? max_m5 : bl::kBt5Tokens);
+    if (alds) stream_variant = alds_variant(lds_alds);
     h.stream_variant = stream_variant;
     h.stream_lds = h.stream_variant == 6 ? (int32_t)lds_tok
                    : alds ? (int32_t)lds_alds : (int32_t)stream_lds_need(h.stream_variant, 1, max_upsplit);

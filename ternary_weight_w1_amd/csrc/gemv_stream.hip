@@ -503,7 +503,7 @@ __device__ __forceinline__ void stage_rows(const BL_GLOBAL int8_t *q, int64_t ld
     }
 }
 template <int UNROLL, int TPW, bool ALDS = false>
-__device__ void stream_mfma(const Problem &p, int local)
+__device__ __forceinline__ void stream_mfma(const Problem &p, int local)
 {
     const int ks = uni(p.ks), KU = uni(p.KU), NT = uni(p.NT), M = uni(p.M);
     const int grp = local / ks, split = local - grp * ks;
@@ -795,7 +795,7 @@ __device__ void stream_mfma_wide(const Problem &p, int local)
 // ahead; 12: the one-token wide kernel; 13: the wide kernel's MFMA stream
 // for 2..16 tokens (kWideWaves waves per workgroup, both).
 template <int V>
-__device__ inline void stream_body(const Problem &p, int local)
+__device__ __forceinline__ void stream_body(const Problem &p, int local)
 {
     if constexpr (V == 6) {
         if (p.M == 1)
@@ -806,7 +806,7 @@ __device__ inline void stream_body(const Problem &p, int local)
         stream_mfma<2, kStreamMfmaTiles>(p, local);
     else if constexpr (V == 9)
         stream_mfma<2, 1>(p, local);
-    else if constexpr (V == 10)
+    else if constexpr (V == 10 || V == 11)
         stream_mfma<4, 1, true>(p, local);
     else if constexpr (V == 12)
         stream_dot4_wide<kWideWaves>(p, local);
@@ -843,6 +843,26 @@ __global__ __launch_bounds__(stream_threads(V)) void stream_multi_kernel(Problem
     stream_body<V>(ps.p[i], (int)blockIdx.x - ps.begin[i]);
 }
 
+// Variant 11: the body of 10 held to 128 VGPRs (four waves per SIMD), so that
+// four workgroups share a compute unit where their staged activations fit
+// (10 takes 136, three waves per SIMD).
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))) void stream_single_kernel_w4(Problem p)
+{
+    stream_body<11>(p, blockIdx.x);
+}
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))) void stream_group_kernel_w4(
+    const Problem *__restrict__ probs, const uint2 *__restrict__ item_map)
+{
+    const uint2 it = item_map[blockIdx.x];
+    if (it.x == 0xFFFFFFFFu) return;
+    stream_body<11>(probs[it.x], (int)it.y);
+}
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))) void stream_multi_kernel_w4(ProblemSet ps)
+{
+    const int i = multi_index(ps, blockIdx.x);
+    stream_body<11>(ps.p[i], (int)blockIdx.x - ps.begin[i]);
+}
+
 // One-token launches that cast their own input: W waves, cast mode MODE.
 template <int W, int MODE>
 __global__ __launch_bounds__(64 * W) void stream_cast_multi_kernel(ProblemSet ps, CastIn ci)
@@ -873,6 +893,7 @@ hipError_t launch_stream_cast_multi(const ProblemSet &ps, const CastIn &ci, int 
     case 1: hipLaunchKernelGGL(KERNEL<1>, grid, block, 0, s, __VA_ARGS__); break;          \
     case 9: hipLaunchKernelGGL(KERNEL<9>, grid, block, 0, s, __VA_ARGS__); break;          \
     case 10: hipLaunchKernelGGL(KERNEL<10>, grid, block, LDS, s, __VA_ARGS__); break;      \
+    case 11: hipLaunchKernelGGL(KERNEL##_w4, grid, block, LDS, s, __VA_ARGS__); break;     \
     case 5: hipLaunchKernelGGL(KERNEL<5>, grid, block, LDS, s, __VA_ARGS__); break;        \
     case 6: hipLaunchKernelGGL(KERNEL<6>, grid, block, LDS, s, __VA_ARGS__); break;        \
     case 12: hipLaunchKernelGGL(KERNEL<12>, grid, block, LDS, s, __VA_ARGS__); break;      \
@@ -890,10 +911,10 @@ hipError_t launch_stream_multi(const ProblemSet &ps, int variant, int lds_bytes,
 hipError_t launch_stream_single(const Problem &p, int variant, hipStream_t s)
 {
     // the MFMA variants' work items are tile groups (p.ntt of them)
-    const int64_t tiles = (variant == 1 || variant == 9 || variant == 10) ? (int64_t)p.ntt : (int64_t)p.NT;
+    const int64_t tiles = (variant == 1 || variant == 9 || variant == 10 || variant == 11) ? (int64_t)p.ntt : (int64_t)p.NT;
     const dim3 grid((unsigned)(tiles * p.ks)), block(stream_threads(variant));
     const unsigned slot = variant == 6 ? 64u * kDot4MaxTokens : 64u;
-    unsigned lds = variant == 10 ? (unsigned)(kTokStride * p.M * p.upsplit + 16)
+    unsigned lds = (variant == 10 || variant == 11) ? (unsigned)(kTokStride * p.M * p.upsplit + 16)
                                  : (variant == 5 ? kLutUnitBytes : slot) * (unsigned)p.upsplit;
     if (variant == 13) {
         // staged activations, then the waves' sums (eight slots) in the same space

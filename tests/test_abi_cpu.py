@@ -269,8 +269,9 @@ def test_group_plan_single_token_quantization():
     # staged activations (3); a 2-token problem switches the streaming kernel to the two-slot dot4
     # token-loop kernel (6), whose LDS holds 64 bytes per unit for one-token
     # problems and 128 for two-token ones; a 5-token problem switches it to
-    # the MFMA stream with activations staged in LDS (10: 80 bytes per token
-    # per unit, one tile per wave)
+    # the MFMA stream with activations staged in LDS (80 bytes per token per
+    # unit, one tile per wave; 11, held to four waves per SIMD, while four
+    # workgroups' staging fits a compute unit's LDS, else 10)
     L = B.lib()
     specs = [(1, 4096, 256)] * 16
     arr = _problems(specs)
@@ -295,7 +296,7 @@ def test_group_plan_single_token_quantization():
     wsb3 = L.bitlinear_group_workspace_bytes(arr3, 17)
     assert L.bitlinear_group_plan(arr3, 17, FAKE, wsb3, host3.ctypes.data, tb3) == 0
     hdr3 = np.frombuffer(host3[:48].tobytes(), np.int32)
-    assert hdr3[2] == 21 and hdr3[7] == 10 and hdr3[9] == max(80 * 1 * 4, 80 * 5 * 1)
+    assert hdr3[2] == 21 and hdr3[7] == 11 and hdr3[9] == max(80 * 1 * 4, 80 * 5 * 1)
     # a one-token problem whose K range (1250 units) would need more than
     # 64 KiB of staged activations is split in two (625 units, 40000 bytes),
     # so a 2-token launch still takes the token loop (6)
@@ -308,14 +309,32 @@ def test_group_plan_single_token_quantization():
     assert hdr4[7] == 6 and hdr4[9] == 64 * 625
     # a launch whose eight-tile groups fill the split target keeps two tiles
     # per wave (1) above 16 tokens: 130 problems of 64 tiles at M = 17; at
-    # M = 5 the staged-activation stream takes one tile per wave (10)
+    # M = 5 the staged-activation stream takes one tile per wave (11)
     arr5 = _problems([(5, 4096, 256)] * 130)
     tb5 = L.bitlinear_group_table_bytes(arr5, 130)
     host5 = np.zeros(tb5, np.uint8)
     wsb5 = L.bitlinear_group_workspace_bytes(arr5, 130)
     assert L.bitlinear_group_plan(arr5, 130, FAKE, wsb5, host5.ctypes.data, tb5) == 0
     hdr5 = np.frombuffer(host5[:48].tobytes(), np.int32)
-    assert hdr5[7] == 10 and hdr5[3] == 130 * 16
+    assert hdr5[7] == 11 and hdr5[3] == 130 * 16
+    # 16 tokens over K = 2560 stage 40 units x 16 x 80 = 51200 bytes per
+    # workgroup (120 problems of 10 tile groups: enough work items that K is
+    # not split): more than a quarter of the LDS, so three waves per SIMD (10)
+    arr7 = _problems([(16, 2560, 2560)] * 120)
+    tb7 = L.bitlinear_group_table_bytes(arr7, 120)
+    host7 = np.zeros(tb7, np.uint8)
+    wsb7 = L.bitlinear_group_workspace_bytes(arr7, 120)
+    assert L.bitlinear_group_plan(arr7, 120, FAKE, wsb7, host7.ctypes.data, tb7) == 0
+    hdr7 = np.frombuffer(host7[:48].tobytes(), np.int32)
+    assert hdr7[7] == 10 and hdr7[9] == 80 * 16 * 40
+    # the same at 8 tokens stages 25600 bytes: four per compute unit fit (11)
+    arr8 = _problems([(8, 2560, 2560)] * 120)
+    tb8 = L.bitlinear_group_table_bytes(arr8, 120)
+    host8 = np.zeros(tb8, np.uint8)
+    wsb8 = L.bitlinear_group_workspace_bytes(arr8, 120)
+    assert L.bitlinear_group_plan(arr8, 120, FAKE, wsb8, host8.ctypes.data, tb8) == 0
+    hdr8 = np.frombuffer(host8[:48].tobytes(), np.int32)
+    assert hdr8[7] == 11 and hdr8[9] == 80 * 8 * 40
     arr6 = _problems([(17, 4096, 256)] * 130)
     tb6 = L.bitlinear_group_table_bytes(arr6, 130)
     host6 = np.zeros(tb6, np.uint8)
