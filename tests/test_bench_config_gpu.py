@@ -3,7 +3,8 @@
 1. Whole stacks in one grouped plan, built by bench.make_plan and stepped as
    the benchmark steps them (grouped quantization, then the grouped
    contraction, no int32 side output): the 2B-class stack (30 layers x q, k,
-   v, o, gate, up, down = 210 matrices) at the decode (M = 1) and prefill
+   v, o, gate, up, down = 210 matrices) at the decode (M = 1), batched
+   decode (M = 8, 16: the 2-bit sweeps of the BT5 comparison) and prefill
    (M = 512, 1% outlier channels) sizes and packed five codes per byte at
    M = 1, 8, 16; the 3B-class curve (182 matrices) at M = 1, 8, 64, 256; the
    70B-class curve (560 matrices, 17 GB packed) at M = 1, 16, 176.
@@ -114,7 +115,8 @@ def _check_sampled(mats, ref, probs, M, fmt, every=1):
         assert rel.size == 0 or rel.max() <= 1e-5, what
 
 
-@pytest.mark.parametrize("model,M,outliers", [("2b", 1, 0.0), ("2b", 512, 0.01), ("3b", 1, 0.0), ("3b", 8, 0.0),
+@pytest.mark.parametrize("model,M,outliers", [("2b", 1, 0.0), ("2b", 8, 0.0), ("2b", 16, 0.0), ("2b", 512, 0.01),
+                                              ("3b", 1, 0.0), ("3b", 8, 0.0),
                                               ("3b", 64, 0.0), ("3b", 256, 0.0), ("70b", 1, 0.0), ("70b", 16, 0.0),
                                               ("70b", 176, 0.0)])
 def test_bench_launch_configuration_sampled(model, M, outliers):
