@@ -1,9 +1,9 @@
 // Per-token absmax int8 activation quantization for gfx950 (the row cast
 // itself, its readings of the pages and its citations are in quant_row.hpp).
 //
-// One workgroup per token: one wave when there are many tokens, four for
-// few, sixteen for fewer than 16 (decode chains, where each cast is a
-// single-workgroup latency problem).  Variants cast the RMSNorm of the row
+// One workgroup per token: one wave when there are many tokens (2048 or
+// more), four for 512..2047, sixteen for fewer than 512 (decode and short
+// prefill chains, where each cast is a few workgroups' latency problem).  Variants cast the RMSNorm of the row
 // (the sub-layer norm before a BitLinear), the residual sum and its RMSNorm,
 // or the gated squared-ReLU of two rows (the feed-forward hidden value
 // before the down projection), computed in the same pass over the inputs.
@@ -14,7 +14,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kFewTokens = 2048;
-constexpr int kSingleTokens = 16;  // fewer rows: sixteen waves per row
+constexpr int kSingleTokens = 512;  // fewer rows: sixteen waves per row
 
 // One workgroup per token.
 template <int WAVES, int MODE>
