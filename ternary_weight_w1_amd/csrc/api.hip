@@ -188,9 +188,14 @@ void decompose_wide(Problem &p)
 int wide_variant(int64_t M) { return M == 1 ? 12 : 13; }
 
 // Most K splits of a tile-kernel problem (measured on the chained 3B step at
-// M = 64: 3.16 ms unsplit, 2.70 at two, 2.74 at four, 3.06 at eight, 3.33 at
-// up to sixteen).
-constexpr int64_t kTileMaxSplits = 2;
+// M = 64 with one split count for every launch: 3.16 ms unsplit, 2.70 at
+// two, 2.74 at four, 3.06 at eight, 3.33 at up to sixteen).  Two, except in
+// launches of at most kTileFewItems items (a layer's o or down at 64 tokens:
+// 13 items), which take up to four of at least 16 units (chained 3B step at
+// M = 64: 2.353 -> 2.280 ms; four splits for launches of up to ~50 items
+// made M = 256 3% slower).
+constexpr int64_t kTileMaxSplits = 4;
+constexpr int64_t kTileFewItems = 32;
 
 // Kernel kind and decomposition of one problem.  `base_items` is the number
 // of streaming work items the whole launch has without K splits; splits are
@@ -255,15 +260,20 @@ void decompose(Problem &p, int64_t base_items, bool own_q, bool groups4 = false,
         p.mt = (int32_t)((p.M + p.mtile - 1) / p.mtile);
         p.ntt = (p.NT + kTileRowTiles - 1) / kTileRowTiles;
         // K splits while the launch's work items (tile_base, or this
-        // problem's alone) are short of the target: at most kTileMaxSplits, keeping >= 8 units (4 stages) per
-        // split.  Each split's partials are 64 KiB per item, read back by
-        // the item's last split, so more splits cost more than they gain.
+        // problem's alone) are short of the target (see kTileMaxSplits).
+        // Each split's partials are 64 KiB per item, read back by the
+        // item's last split, so more splits cost more than they gain.
         const int64_t items = tile_base > 0 ? tile_base : (int64_t)p.mt * p.ntt;
         const int64_t target = knobs().split_target;
         if (items < target) {
             int64_t ks = (target + items - 1) / items;
-            int64_t cap = p.KU / 8;
-            if (cap > kTileMaxSplits) cap = kTileMaxSplits;
+            // launches of very few items (a single layer's o or down at 64
+            // tokens) split up to four ways, at least 16 units each; others
+            // in two, at least 8 units each
+            const bool few = items <= kTileFewItems;
+            int64_t cap = few ? p.KU / 16 : p.KU / 8;
+            const int64_t max_splits = few ? kTileMaxSplits : 2;
+            if (cap > max_splits) cap = max_splits;
             if (cap < 1) cap = 1;
             if (ks > cap) ks = cap;
             const int64_t upsplit = (p.KU + ks - 1) / ks;

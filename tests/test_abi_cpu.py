@@ -552,9 +552,11 @@ def test_probe_mfma_data_rejects_bad_arguments():
 
 def test_group_plan_tile_split():
     # tile-kernel problems (M > 32) in a launch with 7 work items, short of
-    # the 1024-workgroup split target: each splits K in two (14 items, padded
-    # to whole XCD slices of 8), and the workspace holds 64 KiB of partials
-    # per item and split; with enough items (1040) nothing splits
+    # the 1024-workgroup split target and at most 32 items: K splits up to
+    # four ways keeping at least 16 units each -- 40 units in two (3 items ->
+    # 6), 63 units in three (4 items -> 12): 18 items, padded to whole XCD
+    # slices of 8 -- and the workspace holds 64 KiB of partials per item and
+    # split; with enough items (1040) nothing splits
     L = B.lib()
     specs = [(64, 640, 2560), (100, 300, 4000)]
     arr = _problems(specs)
@@ -563,8 +565,8 @@ def test_group_plan_tile_split():
     wsb = L.bitlinear_group_workspace_bytes(arr, 2)
     assert L.bitlinear_group_plan(arr, 2, FAKE, wsb, host.ctypes.data, tb) == 0
     hdr = np.frombuffer(host[:48].tobytes(), np.int32)
-    assert hdr[4] == 16
-    assert wsb >= 2 * 7 * 65536
+    assert hdr[4] == 24
+    assert wsb >= (3 * 2 + 4 * 3) * 65536
     big = _problems([(64, 4096 * 4, 2560)] * 65)  # 65 x 64 items of 256 rows
     tb2 = L.bitlinear_group_table_bytes(big, 65)
     host2 = np.zeros(tb2, np.uint8)
